@@ -1,0 +1,137 @@
+/*
+ * prism.h -- C ABI of the PRISM layer hot path on AMD MI355X (gfx950).
+ *
+ * The layer is the one described by the web summary "Technical Summary: PRISM
+ * (Parallel Residual Iterative Sequence Model)" (gist.science, paper
+ * 2602.10796), sections cited as §n below:
+ *
+ *   Stage 1 (§2.2): u_t = sum_{j=0..3} conv[h, :, j] * v_{t-j}      (ShortConv anchor)
+ *   Stage 2 (§2.2): r^(1) = v_t - u_t; for l = 1..L:
+ *                   k^(l) = W_k^(l) u_t, p^(l) = W_p^(l) u_t,
+ *                   beta^(l) = sigmoid(w_beta^(l) . u_t),
+ *                   delta^(l) = GELU(p^(l) * r^(l)), r^(l+1) = r^(l) - delta^(l)
+ *   Write   (§2.2): B_t = beta_t v_t k_t^T + sum_l beta^(l) delta^(l) k^(l)^T
+ *   Forget  (§2.1): A_t = alpha_t (I - beta_t k_t k_t^T)   (Gated-DeltaNet form)
+ *   Update  (§2.1): S_t = S_{t-1} A_t + B_t
+ *   Readout        : o_t = S_t q_t
+ * With L = 0 the layer is Gated DeltaNet (§3, item 3).  GELU is the exact erf
+ * form.  The base term beta_t v_t k_t^T of the write, r^(1) = v - u, the conv
+ * over v of width 4 (tap j multiplies v_{t-j}), the gate beta^(l) as a
+ * sigmoid of w_beta^(l) . u and the readout are readings of passages the
+ * summary leaves open; the library implements exactly the formulas above.
+ *
+ * Conventions common to every entry point
+ * ---------------------------------------
+ * - All tensor pointers are DEVICE pointers, contiguous, row-major, 16-byte
+ *   aligned.  The caller owns every buffer, including the workspace.  The
+ *   library allocates no device memory and keeps no pointer after a call.
+ * - Work is enqueued asynchronously on `stream`; nothing synchronises the
+ *   host.  Buffers must stay alive until the stream has finished the work.
+ * - Every argument is validated on the host before any HIP call; a failed
+ *   check returns a non-zero status and enqueues nothing.
+ *   prism_last_error() then returns a message naming the argument.
+ * - NaN / Inf inputs are not checked; they propagate.
+ * - Results are deterministic: the same inputs and descriptor give bitwise
+ *   identical outputs (no atomics; all reductions in a fixed order).
+ * - Functions are thread-safe except while kernel timing is enabled
+ *   (prism_timing_begin .. prism_timing_end).
+ */
+#ifndef PRISM_H_
+#define PRISM_H_
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PRISM_OK = 0,
+  PRISM_ERR_NULL = 1,        /* a required pointer is NULL                      */
+  PRISM_ERR_SHAPE = 2,       /* a size is out of range (B, T, H < 1, ...)       */
+  PRISM_ERR_UNSUPPORTED = 3, /* valid but outside the compiled envelope         */
+  PRISM_ERR_ALIGN = 4,       /* a pointer is not 16-byte aligned                */
+  PRISM_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required         */
+  PRISM_ERR_HIP = 6          /* a HIP launch failed; see prism_last_error()     */
+} prism_status;
+
+typedef enum {
+  PRISM_F32 = 0,  /* q, k, v, o, weights, taps, dO, dq, dk, dv in float32  */
+  PRISM_BF16 = 1  /* the same tensors in bfloat16 (round-to-nearest-even)  */
+} prism_dtype;
+
+/* Problem descriptor.
+ *   B, T, H    batch, sequence length, heads            (each >= 1)
+ *   dk, dv     key / value head dimension; must be equal, in {16, 32, 64, 128}
+ *              for PRISM_BF16 and {16, 32, 64} for PRISM_F32
+ *   L          refinement steps, 0 <= L <= 8
+ *   chunk      tokens per chunk of the parallel scan, in {16, 32, 64};
+ *              any T >= 1 is accepted (the last chunk may be partial)
+ *   conv_width ShortConv width; must be 4
+ *   dtype      storage type of the dtype-typed tensors (see prism_dtype)   */
+typedef struct {
+  int B, T, H, dk, dv, L, chunk, conv_width;
+  prism_dtype dtype;
+} prism_desc;
+
+/* Tensor layouts (element type "dt" = desc->dtype; f32 = float32):
+ *   q, k        [B, T, H, dk]  dt      v, o, dO   [B, T, H, dv]  dt
+ *   alpha, beta [B, T, H]      f32     alpha in (0, 1], beta in [0, 1]
+ *   Wk          [H, L, dk, dv] dt      k^(l) = Wk[h, l] u   (row i . u)
+ *   Wp          [H, L, dv, dv] dt      p^(l) = Wp[h, l] u
+ *   wbeta       [H, L, dv]     dt      beta^(l) = sigmoid(wbeta[h, l] . u)
+ *   conv        [H, dv, 4]     dt      tap j multiplies v_{t-j} (j = 0: current token)
+ *   S0, ST      [B, H, dv, dk] f32     state entering / leaving the sequence
+ *   dST, dS0    [B, H, dv, dk] f32
+ *   dq, dk, dv  as q, k, v     dt
+ *   dalpha, dbeta [B, T, H]    f32
+ *   dWk, dWp, dwbeta, dconv    f32, layouts of Wk, Wp, wbeta, conv
+ * q and k are used as given (callers normalise them if they wish).  With
+ * L = 0, Wk, Wp, wbeta, conv (and their gradients) may be NULL. */
+
+/* Workspace sizes in bytes for a descriptor; *bytes = 0 on error. */
+prism_status prism_forward_workspace(const prism_desc* desc, size_t* bytes);
+prism_status prism_backward_workspace(const prism_desc* desc, size_t* bytes);
+
+/* Forward pass: o = readout of S_1..S_T, ST = S_T (ST may be NULL).
+ * S0 may be NULL (zero initial state). */
+prism_status prism_forward(const prism_desc* desc, const void* q, const void* k, const void* v,
+                           const float* alpha, const float* beta, const void* Wk, const void* Wp,
+                           const void* wbeta, const void* conv, const float* S0, void* o,
+                           float* ST, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
+
+/* Backward pass: gradients of <dO, o> + <dST, S_T> with respect to every
+ * input.  Stateless: recomputes what it needs from the forward inputs.
+ * dST may be NULL (zero).  dS0 may be NULL; it is written when given.
+ * Every other gradient pointer is required (weight / tap gradients only
+ * when L > 0).  Gradients are written, not accumulated. */
+prism_status prism_backward(const prism_desc* desc, const void* q, const void* k, const void* v,
+                            const float* alpha, const float* beta, const void* Wk, const void* Wp,
+                            const void* wbeta, const void* conv, const float* S0, const void* dO,
+                            const float* dST, void* dq, void* dk, void* dv, float* dalpha,
+                            float* dbeta, float* dWk, float* dWp, float* dwbeta, float* dconv,
+                            float* dS0, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
+
+/* Human-readable name of a status code (static string). */
+const char* prism_status_string(prism_status status);
+
+/* Detail of the last failure on the calling thread ("" if none). */
+const char* prism_last_error(void);
+
+/* Kernel timing.  Between prism_timing_begin() and prism_timing_end(), every
+ * kernel the library enqueues is bracketed by two HIP events recorded on the
+ * stream it runs on.  prism_timing_end() waits for those events and fills up
+ * to `capacity` entries: names[i] (static strings), total_ms[i] (sum of the
+ * event-measured durations) and launches[i]; it returns the number of
+ * distinct kernels.  Not thread-safe; meant for benchmarks. */
+void prism_timing_begin(void);
+int prism_timing_end(const char** names, double* total_ms, int* launches, int capacity);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PRISM_H_ */

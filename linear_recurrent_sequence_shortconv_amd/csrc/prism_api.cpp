@@ -1,0 +1,319 @@
+// C ABI of the PRISM layer: argument validation, workspace carving and the
+// launch sequence.  The launch sequence of the forward pass is
+//   refine_fwd  (ShortConv anchor + L refinement steps, summary §2.2)
+//   chunk_fwd   (chunk-local affine maps of S_t = S_{t-1} A_t + B_t, §2.1)
+//   state_fwd   (sequential pass over chunks, fp32 state)
+//   out_fwd     (readout o_t = S_t q_t)
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "../../include/prism.h"
+#include "prism_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+prism_status fail(prism_status st, const std::string& msg) {
+  g_err = msg;
+  return st;
+}
+
+// ---------------------------------------------------------------- timing
+struct TimedLaunch {
+  const char* name;
+  hipEvent_t a, b;
+};
+bool g_timing = false;
+std::vector<TimedLaunch> g_launches;
+std::vector<hipEvent_t> g_pool;
+
+hipEvent_t pool_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <typename F>
+hipError_t timed(const char* name, hipStream_t s, F&& f) {
+  if (!g_timing) return f();
+  hipEvent_t a = pool_event(), b = pool_event();
+  if (a) (void)hipEventRecord(a, s);
+  hipError_t err = f();
+  if (b) (void)hipEventRecord(b, s);
+  if (a && b) g_launches.push_back({name, a, b});
+  return err;
+}
+
+// ---------------------------------------------------------------- layout
+size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+struct Carve {
+  size_t off = 0;
+  char* base = nullptr;
+  template <typename P>
+  P* take(size_t bytes) {
+    P* p = base ? reinterpret_cast<P*>(base + off) : nullptr;
+    off += align256(bytes);
+    return p;
+  }
+};
+
+template <typename E>
+struct FwdWs {
+  E *Kl, *Wl, *Mt, *Qt, *Sc;
+  float *HT, *Oloc, *gC, *ST;
+};
+
+template <typename E>
+FwdWs<E> carve_fwd(const prism::Dims& d, Carve& cv) {
+  const size_t bh = (size_t)d.B * d.H;
+  const size_t es = sizeof(E);
+  FwdWs<E> w;
+  w.Kl = cv.take<E>(bh * d.L * d.Tp * d.D * es);
+  w.Wl = cv.take<E>(bh * d.L * d.Tp * d.D * es);
+  w.Mt = cv.take<E>(bh * d.NC * d.D * d.D * es);
+  w.HT = cv.take<float>(bh * d.NC * d.D * d.D * 4);
+  w.Qt = cv.take<E>(bh * d.NC * d.C * d.D * es);
+  w.Oloc = cv.take<float>(bh * d.NC * d.C * d.D * 4);
+  w.gC = cv.take<float>(bh * d.NC * 4);
+  w.Sc = cv.take<E>(bh * d.NC * d.D * d.D * es);
+  w.ST = cv.take<float>(bh * d.D * d.D * 4);
+  return w;
+}
+
+// ---------------------------------------------------------------- checks
+prism_status check_desc(const prism_desc* desc, prism::Dims* out) {
+  if (!desc) return fail(PRISM_ERR_NULL, "desc is NULL");
+  const prism_desc& d = *desc;
+  if (d.B < 1 || d.T < 1 || d.H < 1)
+    return fail(PRISM_ERR_SHAPE, "B, T and H must be >= 1 (got B=" + std::to_string(d.B) +
+                                     " T=" + std::to_string(d.T) + " H=" + std::to_string(d.H) + ")");
+  if (d.dk < 1 || d.dv < 1 || d.L < 0 || d.chunk < 1 || d.conv_width < 1)
+    return fail(PRISM_ERR_SHAPE, "dk, dv, chunk, conv_width must be >= 1 and L >= 0");
+  if (d.dtype != PRISM_F32 && d.dtype != PRISM_BF16)
+    return fail(PRISM_ERR_UNSUPPORTED, "dtype must be PRISM_F32 or PRISM_BF16");
+  if (d.dk != d.dv) return fail(PRISM_ERR_UNSUPPORTED, "dk must equal dv");
+  const bool dok = d.dk == 16 || d.dk == 32 || d.dk == 64 || (d.dk == 128 && d.dtype == PRISM_BF16);
+  if (!dok)
+    return fail(PRISM_ERR_UNSUPPORTED, "head dimension " + std::to_string(d.dk) +
+                                           " not supported (bf16: 16/32/64/128, f32: 16/32/64)");
+  if (d.L > 8) return fail(PRISM_ERR_UNSUPPORTED, "L must be <= 8");
+  if (d.chunk != 16 && d.chunk != 32 && d.chunk != 64)
+    return fail(PRISM_ERR_UNSUPPORTED, "chunk must be 16, 32 or 64");
+  if (d.conv_width != 4) return fail(PRISM_ERR_UNSUPPORTED, "conv_width must be 4");
+  const double elems = (double)d.B * d.T * d.H * d.dk * (d.L + 1);
+  if (elems > 4.0e12) return fail(PRISM_ERR_SHAPE, "problem too large");
+  if ((long long)d.B * d.H * ((d.T + d.chunk - 1) / d.chunk) > 0x7fffffffLL)
+    return fail(PRISM_ERR_SHAPE, "too many chunks for one launch");
+  prism::Dims x;
+  x.B = d.B;
+  x.T = d.T;
+  x.H = d.H;
+  x.D = d.dk;
+  x.L = d.L;
+  x.C = d.chunk;
+  x.NC = (d.T + d.chunk - 1) / d.chunk;
+  x.Tp = x.NC * x.C;
+  *out = x;
+  return PRISM_OK;
+}
+
+prism_status check_ptr(const void* p, const char* name, bool required) {
+  if (!p) return required ? fail(PRISM_ERR_NULL, std::string(name) + " is NULL") : PRISM_OK;
+  if (reinterpret_cast<uintptr_t>(p) & 15u)
+    return fail(PRISM_ERR_ALIGN, std::string(name) + " is not 16-byte aligned");
+  return PRISM_OK;
+}
+
+#define CHECK_PTR(p, req)                              \
+  do {                                                 \
+    prism_status st_ = check_ptr((p), #p, (req));      \
+    if (st_ != PRISM_OK) return st_;                   \
+  } while (0)
+
+#define HIP_TRY(name, stream, expr)                                                   \
+  do {                                                                               \
+    hipError_t e_ = timed((name), (stream), [&]() { return (expr); });               \
+    if (e_ != hipSuccess)                                                            \
+      return fail(PRISM_ERR_HIP, std::string(name) + ": " + hipGetErrorString(e_));   \
+  } while (0)
+
+size_t fwd_ws_bytes(const prism::Dims& d, prism_dtype dt) {
+  Carve cv;
+  if (dt == PRISM_BF16)
+    carve_fwd<prism::bf16>(d, cv);
+  else
+    carve_fwd<float>(d, cv);
+  return cv.off;
+}
+
+template <typename E>
+prism_status run_forward(const prism::Dims& d, const void* q, const void* k, const void* v,
+                         const float* alpha, const float* beta, const void* Wk, const void* Wp,
+                         const void* wbeta, const void* conv, const float* S0, void* o, float* ST,
+                         void* ws, hipStream_t s) {
+  Carve cv;
+  cv.base = static_cast<char*>(ws);
+  FwdWs<E> w = carve_fwd<E>(d, cv);
+  const E* q_ = static_cast<const E*>(q);
+  const E* k_ = static_cast<const E*>(k);
+  const E* v_ = static_cast<const E*>(v);
+  if (d.L > 0)
+    HIP_TRY("refine_fwd", s,
+            prism::launch_refine_fwd<E>(d, v_, static_cast<const E*>(conv), static_cast<const E*>(Wk),
+                                        static_cast<const E*>(Wp), static_cast<const E*>(wbeta),
+                                        w.Kl, w.Wl, s));
+  HIP_TRY("chunk_fwd", s,
+          prism::launch_chunk_fwd<E>(d, q_, k_, v_, alpha, beta, w.Kl, w.Wl, nullptr, w.Mt, w.HT,
+                                     w.Qt, w.Oloc, w.gC, nullptr, nullptr, s));
+  HIP_TRY("state_fwd", s,
+          prism::launch_state_fwd<E>(d, S0, w.Mt, w.HT, w.gC, w.Sc, ST ? ST : w.ST, false, s));
+  HIP_TRY("out_fwd", s, prism::launch_out_fwd<E>(d, w.Sc, w.Qt, w.Oloc, static_cast<E*>(o), s));
+  return PRISM_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* prism_status_string(prism_status st) {
+  switch (st) {
+    case PRISM_OK: return "PRISM_OK";
+    case PRISM_ERR_NULL: return "PRISM_ERR_NULL";
+    case PRISM_ERR_SHAPE: return "PRISM_ERR_SHAPE";
+    case PRISM_ERR_UNSUPPORTED: return "PRISM_ERR_UNSUPPORTED";
+    case PRISM_ERR_ALIGN: return "PRISM_ERR_ALIGN";
+    case PRISM_ERR_WORKSPACE: return "PRISM_ERR_WORKSPACE";
+    case PRISM_ERR_HIP: return "PRISM_ERR_HIP";
+  }
+  return "PRISM_ERR_UNKNOWN";
+}
+
+const char* prism_last_error(void) { return g_err.c_str(); }
+
+prism_status prism_forward_workspace(const prism_desc* desc, size_t* bytes) {
+  if (bytes) *bytes = 0;
+  if (!bytes) return fail(PRISM_ERR_NULL, "bytes is NULL");
+  prism::Dims d;
+  prism_status st = check_desc(desc, &d);
+  if (st != PRISM_OK) return st;
+  *bytes = fwd_ws_bytes(d, desc->dtype);
+  return PRISM_OK;
+}
+
+prism_status prism_backward_workspace(const prism_desc* desc, size_t* bytes) {
+  if (bytes) *bytes = 0;
+  if (!bytes) return fail(PRISM_ERR_NULL, "bytes is NULL");
+  prism::Dims d;
+  prism_status st = check_desc(desc, &d);
+  if (st != PRISM_OK) return st;
+  return fail(PRISM_ERR_UNSUPPORTED, "backward pass not available in this build");
+}
+
+prism_status prism_forward(const prism_desc* desc, const void* q, const void* k, const void* v,
+                           const float* alpha, const float* beta, const void* Wk, const void* Wp,
+                           const void* wbeta, const void* conv, const float* S0, void* o,
+                           float* ST, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  try {
+    g_err.clear();
+    prism::Dims d;
+    prism_status st = check_desc(desc, &d);
+    if (st != PRISM_OK) return st;
+    const bool refine = d.L > 0;
+    CHECK_PTR(q, true);
+    CHECK_PTR(k, true);
+    CHECK_PTR(v, true);
+    CHECK_PTR(alpha, true);
+    CHECK_PTR(beta, true);
+    CHECK_PTR(Wk, refine);
+    CHECK_PTR(Wp, refine);
+    CHECK_PTR(wbeta, refine);
+    CHECK_PTR(conv, refine);
+    CHECK_PTR(S0, false);
+    CHECK_PTR(o, true);
+    CHECK_PTR(ST, false);
+    const size_t need = fwd_ws_bytes(d, desc->dtype);
+    if (!workspace) return fail(PRISM_ERR_WORKSPACE, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+      return fail(PRISM_ERR_ALIGN, "workspace is not 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(PRISM_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
+                                           " bytes, needs " + std::to_string(need));
+    if (desc->dtype == PRISM_BF16)
+      return run_forward<prism::bf16>(d, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, o, ST,
+                                      workspace, stream);
+    return run_forward<float>(d, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, o, ST, workspace,
+                              stream);
+  } catch (...) {
+    return fail(PRISM_ERR_HIP, "unexpected host exception");
+  }
+}
+
+prism_status prism_backward(const prism_desc* desc, const void* q, const void* k, const void* v,
+                            const float* alpha, const float* beta, const void* Wk, const void* Wp,
+                            const void* wbeta, const void* conv, const float* S0, const void* dO,
+                            const float* dST, void* dq, void* dk, void* dv, float* dalpha,
+                            float* dbeta, float* dWk, float* dWp, float* dwbeta, float* dconv,
+                            float* dS0, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  (void)q; (void)k; (void)v; (void)alpha; (void)beta; (void)Wk; (void)Wp; (void)wbeta;
+  (void)conv; (void)S0; (void)dO; (void)dST; (void)dq; (void)dk; (void)dv; (void)dalpha;
+  (void)dbeta; (void)dWk; (void)dWp; (void)dwbeta; (void)dconv; (void)dS0; (void)workspace;
+  (void)workspace_bytes; (void)stream;
+  g_err.clear();
+  prism::Dims d;
+  prism_status st = check_desc(desc, &d);
+  if (st != PRISM_OK) return st;
+  return fail(PRISM_ERR_UNSUPPORTED, "backward pass not available in this build");
+}
+
+void prism_timing_begin(void) {
+  g_timing = true;
+  g_launches.clear();
+}
+
+int prism_timing_end(const char** names, double* total_ms, int* launches, int capacity) {
+  g_timing = false;
+  std::vector<const char*> nm;
+  std::vector<double> ms;
+  std::vector<int> cnt;
+  for (auto& l : g_launches) {
+    float t = 0.f;
+    (void)hipEventSynchronize(l.b);
+    (void)hipEventElapsedTime(&t, l.a, l.b);
+    size_t i = 0;
+    for (; i < nm.size(); ++i)
+      if (std::strcmp(nm[i], l.name) == 0) break;
+    if (i == nm.size()) {
+      nm.push_back(l.name);
+      ms.push_back(0.0);
+      cnt.push_back(0);
+    }
+    ms[i] += t;
+    cnt[i] += 1;
+    g_pool.push_back(l.a);
+    g_pool.push_back(l.b);
+  }
+  g_launches.clear();
+  const int n = (int)nm.size();
+  for (int i = 0; i < n && i < capacity; ++i) {
+    if (names) names[i] = nm[i];
+    if (total_ms) total_ms[i] = ms[i];
+    if (launches) launches[i] = cnt[i];
+  }
+  return n;
+}
+
+}  // extern "C"

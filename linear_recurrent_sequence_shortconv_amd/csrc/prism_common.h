@@ -1,0 +1,289 @@
+// Device-side building blocks shared by the PRISM kernels (gfx950 / CDNA4).
+//
+// * Element type T is either __bf16 (bf16 storage, bf16 MFMA operands,
+//   fp32 accumulation) or float (fp32 storage, fp32 MFMA).
+// * All matrix products go through 16x16 output tiles of one MFMA family:
+//     bf16: v_mfma_f32_16x16x32_bf16 (k = 32 per instruction, 8 per lane)
+//     fp32: v_mfma_f32_16x16x4_f32   (k = 4 per instruction, 1 per lane)
+//   Operand fragments: lane l holds row (l & 15) of its 16-row slab and the
+//   KPL consecutive k values starting at KPL * (l >> 4).
+//   Accumulator: lane l holds column (l & 15) and rows 4 * (l >> 4) + i,
+//   i = 0..3 (four consecutive rows of one column).
+// * A workgroup of NW waves computes an M x N product by splitting the
+//   (M/16) x (N/16) tile grid into a WM x WN grid of per-wave blocks; each
+//   wave keeps its block's accumulators in registers (register blocking).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace prism {
+
+typedef __bf16 bf16;
+typedef bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int WAVE = 64;
+
+template <typename T> struct Mfma;
+
+template <> struct Mfma<bf16> {
+  static constexpr int KSTEP = 32;
+  static constexpr int KPL = 8;
+  typedef bf16x8 frag;
+  __device__ static inline f32x4 mma(const frag& a, const frag& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <> struct Mfma<float> {
+  static constexpr int KSTEP = 4;
+  static constexpr int KPL = 1;
+  typedef float frag;
+  __device__ static inline f32x4 mma(const frag& a, const frag& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+};
+
+// --------------------------------------------------------------------------
+// scalar conversions (round to nearest even for bf16)
+// --------------------------------------------------------------------------
+template <typename T> __device__ inline T to_t(float x);
+template <> __device__ inline float to_t<float>(float x) { return x; }
+template <> __device__ inline bf16 to_t<bf16>(float x) { return (bf16)x; }
+__device__ inline float to_f(float x) { return x; }
+__device__ inline float to_f(bf16 x) { return (float)x; }
+
+// 16-byte vector of T (8 bf16 or 4 float) for coalesced global <-> LDS copies
+template <typename T> struct Vec16 {
+  static constexpr int N = 16 / sizeof(T);
+  typedef uint4 raw;
+};
+
+__device__ inline uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ inline void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
+
+// --------------------------------------------------------------------------
+// MFMA fragment loads from LDS
+//   KC = true : element (row, k) at p[row * ld + k]   (k contiguous)
+//   KC = false: element (row, k) at p[k * ld + row]   (k strided)
+// --------------------------------------------------------------------------
+template <typename T, bool KC>
+__device__ inline typename Mfma<T>::frag load_frag(const T* p, int ld, int row0, int k0, int lane) {
+  constexpr int KPL = Mfma<T>::KPL;
+  const int r = row0 + (lane & 15);
+  const int k = k0 + KPL * (lane >> 4);
+  typename Mfma<T>::frag f;
+  if constexpr (KC) {
+    f = *reinterpret_cast<const typename Mfma<T>::frag*>(p + r * ld + k);
+  } else {
+    if constexpr (KPL == 1) {
+      f = p[k * ld + r];
+    } else {
+#pragma unroll
+      for (int j = 0; j < KPL; ++j) f[j] = p[(k + j) * ld + r];
+    }
+  }
+  return f;
+}
+
+// --------------------------------------------------------------------------
+// wave-grid tiling of an M x N output over NW waves
+// --------------------------------------------------------------------------
+// Choose WN (waves along N): among splits WM x WN = NW that divide the tile
+// grid evenly, the one with the fewest fragment loads per k step (RM + RN);
+// if the grid has fewer tiles than waves, some waves stay idle.
+constexpr int tiling_wn(int TM, int TN, int NW) {
+  int best = -1, cost = 1 << 30;
+  for (int wn = 1; wn <= NW; wn *= 2) {
+    const int wm = NW / wn;
+    if (wn > TN || wm > TM || TN % wn || TM % wm) continue;
+    const int c = TM / wm + TN / wn;
+    if (c < cost) { cost = c; best = wn; }
+  }
+  if (best > 0) return best;
+  return TN < NW ? TN : NW;
+}
+
+template <int M, int N, int NW> struct Tiling {
+  static constexpr int TM = M / 16;
+  static constexpr int TN = N / 16;
+  static constexpr int WN = tiling_wn(TM, TN, NW);
+  static constexpr int WM0 = NW / WN;
+  static constexpr int WM = TM < WM0 ? TM : WM0;
+  static constexpr int RM = (TM + WM - 1) / WM;   // tiles per wave along M
+  static constexpr int RN = (TN + WN - 1) / WN;   // tiles per wave along N
+  static_assert(M % 16 == 0 && N % 16 == 0, "tile multiple");
+  static_assert(TM % WM == 0 && TN % WN == 0, "even split");
+  __device__ static inline bool active(int wave) { return wave < WM * WN; }
+  // first tile row / col of this wave's block
+  __device__ static inline int m0(int wave) { return (wave / WN) * RM * 16; }
+  __device__ static inline int n0(int wave) { return (wave % WN) * RN * 16; }
+};
+
+template <int M, int N, int NW> struct Acc {
+  typedef Tiling<M, N, NW> TL;
+  f32x4 v[TL::RM][TL::RN];
+  __device__ inline void zero() {
+#pragma unroll
+    for (int i = 0; i < TL::RM; ++i)
+#pragma unroll
+      for (int j = 0; j < TL::RN; ++j) v[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+};
+
+// bf16 fragments of 4 k values for v_mfma_f32_16x16x16_bf16 (inner sizes of 16)
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+template <bool KC>
+__device__ inline s16x4 load_frag4(const bf16* p, int ld, int row0, int k0, int lane) {
+  const int r = row0 + (lane & 15);
+  const int k = k0 + 4 * (lane >> 4);
+  s16x4 f;
+  if constexpr (KC) {
+    f = *reinterpret_cast<const s16x4*>(p + r * ld + k);
+  } else {
+    const unsigned short* q = reinterpret_cast<const unsigned short*>(p);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) f[j] = (short)q[(k + j) * ld + r];
+  }
+  return f;
+}
+
+// acc += A * B^T over k in [0, K): A is M x K, B is N x K (both as LDS views)
+template <typename T, int M, int N, int K, int NW, bool AKC, bool BKC>
+__device__ inline void gemm_acc(Acc<M, N, NW>& acc, const T* A, int lda, const T* B, int ldb,
+                                int wave, int lane) {
+  typedef Tiling<M, N, NW> TL;
+  if (!TL::active(wave)) return;
+  const int m0 = TL::m0(wave), n0 = TL::n0(wave);
+  constexpr int KS = Mfma<T>::KSTEP;
+  if constexpr (sizeof(T) == 2 && K % KS != 0) {
+    static_assert(K % 16 == 0, "k multiple of 16");
+#pragma unroll
+    for (int k0 = 0; k0 < K; k0 += 16) {
+      s16x4 a[TL::RM], b[TL::RN];
+#pragma unroll
+      for (int i = 0; i < TL::RM; ++i) a[i] = load_frag4<AKC>(A, lda, m0 + 16 * i, k0, lane);
+#pragma unroll
+      for (int j = 0; j < TL::RN; ++j) b[j] = load_frag4<BKC>(B, ldb, n0 + 16 * j, k0, lane);
+#pragma unroll
+      for (int i = 0; i < TL::RM; ++i)
+#pragma unroll
+        for (int j = 0; j < TL::RN; ++j)
+          acc.v[i][j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a[i], b[j], acc.v[i][j], 0, 0, 0);
+    }
+  } else {
+    static_assert(K % KS == 0, "k multiple");
+#pragma unroll 2
+    for (int k0 = 0; k0 < K; k0 += KS) {
+      typename Mfma<T>::frag a[TL::RM], b[TL::RN];
+#pragma unroll
+      for (int i = 0; i < TL::RM; ++i) a[i] = load_frag<T, AKC>(A, lda, m0 + 16 * i, k0, lane);
+#pragma unroll
+      for (int j = 0; j < TL::RN; ++j) b[j] = load_frag<T, BKC>(B, ldb, n0 + 16 * j, k0, lane);
+#pragma unroll
+      for (int i = 0; i < TL::RM; ++i)
+#pragma unroll
+        for (int j = 0; j < TL::RN; ++j) acc.v[i][j] = Mfma<T>::mma(a[i], b[j], acc.v[i][j]);
+    }
+  }
+}
+
+// Visit this wave's accumulator tiles: f(row0, col, f32x4 vals) where
+// vals[i] belongs to (row0 + i, col).
+template <int M, int N, int NW, typename F>
+__device__ inline void for_tiles(const Acc<M, N, NW>& acc, int wave, int lane, F&& f) {
+  typedef Tiling<M, N, NW> TL;
+  if (!TL::active(wave)) return;
+  const int m0 = TL::m0(wave), n0 = TL::n0(wave);
+#pragma unroll
+  for (int i = 0; i < TL::RM; ++i)
+#pragma unroll
+    for (int j = 0; j < TL::RN; ++j)
+      f(m0 + 16 * i + 4 * (lane >> 4), n0 + 16 * j + (lane & 15), acc.v[i][j]);
+}
+
+// Same visit, with a mutable accumulator (to rescale or reset in place).
+template <int M, int N, int NW, typename F>
+__device__ inline void for_tiles_mut(Acc<M, N, NW>& acc, int wave, int lane, F&& f) {
+  typedef Tiling<M, N, NW> TL;
+  if (!TL::active(wave)) return;
+  const int m0 = TL::m0(wave), n0 = TL::n0(wave);
+#pragma unroll
+  for (int i = 0; i < TL::RM; ++i)
+#pragma unroll
+    for (int j = 0; j < TL::RN; ++j)
+      f(m0 + 16 * i + 4 * (lane >> 4), n0 + 16 * j + (lane & 15), acc.v[i][j]);
+}
+
+// --------------------------------------------------------------------------
+// cooperative global <-> LDS tile copies (16-byte vectors)
+// --------------------------------------------------------------------------
+// rows x cols tile of T; global row r at g + r * gstride; LDS row r at s + r * ld.
+// Rows >= nvalid are filled with zeros (ragged tails).
+template <typename T, int ROWS, int COLS, int NT>
+__device__ inline void g2s_rows(T* s, int ld, const T* g, long gstride, int nvalid, int tid) {
+  constexpr int VN = 16 / sizeof(T);
+  constexpr int VPR = COLS / VN;
+  for (int e = tid; e < ROWS * VPR; e += NT) {
+    const int r = e / VPR, c = (e % VPR) * VN;
+    uint4 v = {0u, 0u, 0u, 0u};
+    if (r < nvalid) v = ld16(g + r * gstride + c);
+    st16(s + r * ld + c, v);
+  }
+}
+
+// Same source, stored transposed in LDS: element (r, c) -> s[c * ld + r],
+// each value multiplied by scale[r] (nullptr = 1).
+template <typename T, int ROWS, int COLS, int NT>
+__device__ inline void g2s_rows_transposed(T* s, int ld, const T* g, long gstride, int nvalid,
+                                           const float* scale, int tid) {
+  constexpr int VN = 16 / sizeof(T);
+  constexpr int VPR = COLS / VN;
+  for (int e = tid; e < ROWS * VPR; e += NT) {
+    const int r = e / VPR, c = (e % VPR) * VN;
+    uint4 v = {0u, 0u, 0u, 0u};
+    if (r < nvalid) v = ld16(g + r * gstride + c);
+    const T* x = reinterpret_cast<const T*>(&v);
+    const float sc = scale ? scale[r] : 1.0f;
+#pragma unroll
+    for (int j = 0; j < VN; ++j) s[(c + j) * ld + r] = to_t<T>(to_f(x[j]) * sc);
+  }
+}
+
+// LDS tile -> global rows (first nvalid rows only)
+template <typename T, int ROWS, int COLS, int NT>
+__device__ inline void s2g_rows(T* g, long gstride, const T* s, int ld, int nvalid, int tid) {
+  constexpr int VN = 16 / sizeof(T);
+  constexpr int VPR = COLS / VN;
+  for (int e = tid; e < ROWS * VPR; e += NT) {
+    const int r = e / VPR, c = (e % VPR) * VN;
+    if (r < nvalid) st16(g + r * gstride + c, ld16(s + r * ld + c));
+  }
+}
+
+// Padded LDS leading dimension for a row of n elements of T (16-byte pad:
+// staggers rows across banks for 16-byte fragment reads).
+template <typename T> constexpr int ldpad(int n) { return n + 16 / (int)sizeof(T); }
+
+// --------------------------------------------------------------------------
+// math
+// --------------------------------------------------------------------------
+__device__ inline float gelu_erf(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
+__device__ inline float gelu_erf_grad(float z) {
+  return 0.5f * (1.0f + erff(z * 0.70710678118654752f)) +
+         z * 0.39894228040143268f * __expf(-0.5f * z * z);
+}
+__device__ inline float sigmoidf(float x) { return 1.0f / (1.0f + __expf(-x)); }
+
+// XCD-aware block order: consecutive hardware dispatch slots go round-robin
+// over the 8 XCDs; return a logical block id such that the blocks one XCD
+// receives are contiguous in logical order (neighbouring tiles share L2).
+__device__ inline int xcd_swizzle(int bid, int nblocks) {
+  constexpr int NXCD = 8;
+  if (nblocks % NXCD != 0) return bid;
+  const int per = nblocks / NXCD;
+  return (bid % NXCD) * per + bid / NXCD;
+}
+
+}  // namespace prism

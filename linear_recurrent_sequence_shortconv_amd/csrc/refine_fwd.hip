@@ -1,0 +1,223 @@
+// Stage 1 (ShortConv anchor) and Stage 2 (L unrolled refinement steps) of the
+// PRISM layer, one kernel.  PRISM technical summary §2.2 "Input-Anchored Loop
+// Unrolling":
+//   u_t      = sum_{j=0..3} c[:, j] * v_{t-j}      (depthwise causal conv over v)
+//   r^(1)    = v_t - u_t
+//   k^(l)    = W_k^(l) u_t,  p^(l) = W_p^(l) u_t,  beta^(l) = sigmoid(w_beta^(l) . u_t)
+//   delta^(l)= GELU(p^(l) * r^(l)),  r^(l+1) = r^(l) - delta^(l)
+//   output pairs (k^(l), w^(l) = beta^(l) delta^(l)), whose outer products form
+//   the rank-L injection B_t of §2.2.
+//
+// The step is elementwise per token apart from the two projections, so it is
+// HBM-bound: read v once, write 2 L rows per token.  One workgroup owns 64
+// tokens of one (b, h); wave w owns output features {16 n : n = w mod 4} for
+// all 64 tokens.  Its weight fragments come straight from global memory (each
+// weight row is read by exactly one wave per workgroup), the anchor u is the
+// shared MFMA A operand in LDS, and the residual chain stays in registers in
+// the accumulator layout.  Outputs are staged in LDS and stored as full
+// 16-byte rows.
+#include "prism_common.h"
+#include "prism_internal.h"
+
+namespace prism {
+
+constexpr int RF_TT = 64;    // tokens per workgroup
+constexpr int RF_NT = 256;   // threads per workgroup
+constexpr int RF_NW = 4;
+
+template <typename E, int D>
+__global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
+    const E* __restrict__ v, const E* __restrict__ conv, const E* __restrict__ Wk,
+    const E* __restrict__ Wp, const E* __restrict__ wbeta, E* __restrict__ Kl,
+    E* __restrict__ Wl, int B, int T, int H, int L, int Tp) {
+  constexpr int LD = ldpad<E>(D);
+  constexpr int NFT = D / 16;                          // feature tiles
+  constexpr int FPW = (NFT + RF_NW - 1) / RF_NW;       // feature tiles per wave
+  constexpr int KS = Mfma<E>::KSTEP;
+  constexpr int NK = D / KS;
+  constexpr int VN = 16 / sizeof(E);
+
+  __shared__ E vbuf[(RF_TT + 3) * D];
+  __shared__ __attribute__((aligned(16))) E ubuf[RF_TT * LD];
+  __shared__ __attribute__((aligned(16))) E obk[RF_TT * LD];
+  __shared__ __attribute__((aligned(16))) E obw[RF_TT * LD];
+  __shared__ float gate[8][RF_TT];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ntiles = Tp / RF_TT + ((Tp % RF_TT) ? 1 : 0);
+  const int nblk = ntiles * B * H;
+  const int bid = xcd_swizzle(blockIdx.x, nblk);
+  // head-major logical order: one XCD sees a contiguous range of heads
+  const int h = bid / (B * ntiles);
+  const int rest = bid % (B * ntiles);
+  const int b = rest / ntiles, tile = rest % ntiles;
+  const int t0 = tile * RF_TT;
+  const long tok_stride = (long)H * D;
+  const E* vseq = v + ((long)b * T * H + h) * D;       // row t at vseq + t * tok_stride
+
+  // ---- v rows t0-3 .. t0+63 (zeros outside [0, T)) ----
+  for (int e = tid; e < (RF_TT + 3) * (D / VN); e += RF_NT) {
+    const int r = e / (D / VN), c = (e % (D / VN)) * VN;
+    const int t = t0 - 3 + r;
+    uint4 x = {0u, 0u, 0u, 0u};
+    if (t >= 0 && t < T) x = ld16(vseq + t * tok_stride + c);
+    st16(vbuf + r * D + c, x);
+  }
+  __syncthreads();
+
+  // ---- anchor u (fp32 math, stored as the MFMA operand type); pad tokens u = 0 ----
+  const E* ch = conv + (long)h * D * 4;
+  for (int e = tid; e < RF_TT * D; e += RF_NT) {
+    const int t = e / D, f = e % D;
+    float u = 0.f;
+    if (t0 + t < T) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) u += to_f(ch[f * 4 + j]) * to_f(vbuf[(t + 3 - j) * D + f]);
+    }
+    ubuf[t * LD + f] = to_t<E>(u);
+  }
+  __syncthreads();
+
+  // ---- step gates beta^(l) = sigmoid(w_beta^(l) . u): 4 threads per token ----
+  {
+    const int t = tid >> 2, part = tid & 3;
+    for (int l = 0; l < L; ++l) {
+      const E* wb = wbeta + ((long)h * L + l) * D;
+      float s = 0.f;
+      for (int f = part * (D / 4); f < (part + 1) * (D / 4); ++f) s += to_f(wb[f]) * to_f(ubuf[t * LD + f]);
+      s += __shfl_xor(s, 1);
+      s += __shfl_xor(s, 2);
+      if (part == 0) gate[l][t] = sigmoidf(s);
+    }
+  }
+
+  // ---- residual r^(1) = v - u in the accumulator layout (fp32) ----
+  // element (m, n, i): token 16 m + 4 (lane >> 4) + i, feature 16 n + (lane & 15)
+  float r[4][FPW][4];
+  float taps[FPW][4];
+#pragma unroll
+  for (int nn = 0; nn < FPW; ++nn) {
+    const int n = wave + RF_NW * nn;
+    const int f = 16 * n + (lane & 15);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) taps[nn][j] = (n < NFT) ? to_f(ch[f * 4 + j]) : 0.f;
+  }
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int nn = 0; nn < FPW; ++nn) {
+      const int n = wave + RF_NW * nn;
+      const int f = 16 * n + (lane & 15);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * m + 4 * (lane >> 4) + i;
+        float val = 0.f;
+        if (n < NFT && t0 + t < T) {
+          float u = 0.f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) u += taps[nn][j] * to_f(vbuf[(t + 3 - j) * D + f]);
+          val = to_f(vbuf[(t + 3) * D + f]) - u;
+        }
+        r[m][nn][i] = val;
+      }
+    }
+  __syncthreads();   // gates visible
+
+  E* Klseq = Kl + (((long)b * H + h) * L) * Tp * D;
+  E* Wlseq = Wl + (((long)b * H + h) * L) * Tp * D;
+  const int nvalid = min(RF_TT, Tp - t0);
+
+  for (int l = 0; l < L; ++l) {
+    const E* wk = Wk + ((long)h * L + l) * D * D;
+    const E* wp = Wp + ((long)h * L + l) * D * D;
+    f32x4 ak[4][FPW], ap[4][FPW];
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int nn = 0; nn < FPW; ++nn) {
+        ak[m][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+        ap[m][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+#pragma unroll 2
+    for (int kk = 0; kk < NK; ++kk) {
+      const int k0 = kk * KS;
+      typename Mfma<E>::frag a[4], bk[FPW], bp[FPW];
+#pragma unroll
+      for (int m = 0; m < 4; ++m) a[m] = load_frag<E, true>(ubuf, LD, 16 * m, k0, lane);
+#pragma unroll
+      for (int nn = 0; nn < FPW; ++nn) {
+        const int n = wave + RF_NW * nn;
+        if (n < NFT) {
+          bk[nn] = load_frag<E, true>(wk, D, 16 * n, k0, lane);
+          bp[nn] = load_frag<E, true>(wp, D, 16 * n, k0, lane);
+        }
+      }
+#pragma unroll
+      for (int nn = 0; nn < FPW; ++nn) {
+        const int n = wave + RF_NW * nn;
+        if (n < NFT) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) {
+            ak[m][nn] = Mfma<E>::mma(a[m], bk[nn], ak[m][nn]);
+            ap[m][nn] = Mfma<E>::mma(a[m], bp[nn], ap[m][nn]);
+          }
+        }
+      }
+    }
+    // residual chain, one step
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int nn = 0; nn < FPW; ++nn) {
+        const int n = wave + RF_NW * nn;
+        if (n < NFT) {
+          const int f = 16 * n + (lane & 15);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int t = 16 * m + 4 * (lane >> 4) + i;
+            const float z = ap[m][nn][i] * r[m][nn][i];
+            const float dl = gelu_erf(z);
+            r[m][nn][i] -= dl;
+            obk[t * LD + f] = to_t<E>(ak[m][nn][i]);
+            obw[t * LD + f] = to_t<E>(gate[l][t] * dl);
+          }
+        }
+      }
+    __syncthreads();
+    s2g_rows<E, RF_TT, D, RF_NT>(Klseq + ((long)l * Tp + t0) * D, D, obk, LD, nvalid, tid);
+    s2g_rows<E, RF_TT, D, RF_NT>(Wlseq + ((long)l * Tp + t0) * D, D, obw, LD, nvalid, tid);
+    __syncthreads();
+  }
+}
+
+template <typename E, int D>
+static hipError_t refine_launch_d(const Dims& d, const E* v, const E* conv, const E* Wk,
+                                  const E* Wp, const E* wbeta, E* Kl, E* Wl, hipStream_t s) {
+  const int ntiles = (d.Tp + RF_TT - 1) / RF_TT;
+  const int nblk = ntiles * d.B * d.H;
+  hipLaunchKernelGGL((refine_fwd_kernel<E, D>), dim3(nblk), dim3(RF_NT), 0, s, v, conv, Wk, Wp,
+                     wbeta, Kl, Wl, d.B, d.T, d.H, d.L, d.Tp);
+  return hipGetLastError();
+}
+
+template <typename E>
+hipError_t launch_refine_fwd(const Dims& d, const E* v, const E* conv, const E* Wk, const E* Wp,
+                             const E* wbeta, E* Kl, E* Wl, hipStream_t s) {
+  if (d.L == 0) return hipSuccess;
+  switch (d.D) {
+    case 16: return refine_launch_d<E, 16>(d, v, conv, Wk, Wp, wbeta, Kl, Wl, s);
+    case 32: return refine_launch_d<E, 32>(d, v, conv, Wk, Wp, wbeta, Kl, Wl, s);
+    case 64: return refine_launch_d<E, 64>(d, v, conv, Wk, Wp, wbeta, Kl, Wl, s);
+    case 128:
+      if constexpr (sizeof(E) == 2) return refine_launch_d<E, 128>(d, v, conv, Wk, Wp, wbeta, Kl, Wl, s);
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+template hipError_t launch_refine_fwd<bf16>(const Dims&, const bf16*, const bf16*, const bf16*,
+                                            const bf16*, const bf16*, bf16*, bf16*, hipStream_t);
+template hipError_t launch_refine_fwd<float>(const Dims&, const float*, const float*, const float*,
+                                             const float*, const float*, float*, float*, hipStream_t);
+
+}  // namespace prism

@@ -1,0 +1,217 @@
+"""Thin ctypes binding of libprism.so (the C ABI in include/prism.h).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+behind the C ABI.  PyTorch provides device memory (outputs, workspace) and
+the current stream.  There is no fallback: if the library is missing or a
+call fails, a RuntimeError is raised.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libprism.so")
+
+PRISM_F32 = 0
+PRISM_BF16 = 1
+STATUS = {0: "PRISM_OK", 1: "PRISM_ERR_NULL", 2: "PRISM_ERR_SHAPE", 3: "PRISM_ERR_UNSUPPORTED",
+          4: "PRISM_ERR_ALIGN", 5: "PRISM_ERR_WORKSPACE", 6: "PRISM_ERR_HIP"}
+
+EXPORTS = ("prism_forward_workspace", "prism_backward_workspace", "prism_forward",
+           "prism_backward", "prism_status_string", "prism_last_error",
+           "prism_timing_begin", "prism_timing_end")
+
+
+class Desc(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int),
+                ("dk", ctypes.c_int), ("dv", ctypes.c_int), ("L", ctypes.c_int),
+                ("chunk", ctypes.c_int), ("conv_width", ctypes.c_int), ("dtype", ctypes.c_int)]
+
+
+_lib = None
+_P = ctypes.c_void_p
+
+
+def lib():
+    """Load libprism.so once.  torch is imported first so that its HIP runtime
+    (same SONAME as the system one) is the single runtime in the process."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built; run "
+                               "`python -m linear_recurrent_sequence_shortconv_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        L.prism_forward_workspace.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(ctypes.c_size_t)]
+        L.prism_backward_workspace.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(ctypes.c_size_t)]
+        L.prism_forward.argtypes = [ctypes.POINTER(Desc)] + [_P] * 12 + [_P, ctypes.c_size_t, _P]
+        L.prism_backward.argtypes = [ctypes.POINTER(Desc)] + [_P] * 22 + [_P, ctypes.c_size_t, _P]
+        for f in ("prism_forward_workspace", "prism_backward_workspace", "prism_forward",
+                  "prism_backward"):
+            getattr(L, f).restype = ctypes.c_int
+        L.prism_status_string.argtypes = [ctypes.c_int]
+        L.prism_status_string.restype = ctypes.c_char_p
+        L.prism_last_error.restype = ctypes.c_char_p
+        L.prism_timing_end.argtypes = [ctypes.POINTER(ctypes.c_char_p), ctypes.POINTER(ctypes.c_double),
+                                       ctypes.POINTER(ctypes.c_int), ctypes.c_int]
+        L.prism_timing_end.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def make_desc(B, T, H, dk, dv, L, chunk, dtype, conv_width=4):
+    return Desc(B, T, H, dk, dv, L, chunk, conv_width, dtype)
+
+
+def _check(status):
+    if status != 0:
+        msg = lib().prism_last_error().decode()
+        raise RuntimeError(f"{STATUS.get(status, status)}: {msg}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t):
+    if t.dtype == torch.bfloat16:
+        return PRISM_BF16
+    if t.dtype == torch.float32:
+        return PRISM_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _req(t, name, dtype, device):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if t.device != device:
+        raise ValueError(f"{name}: expected device {device}, got {t.device}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _desc_from(q, v, Wk, chunk):
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    L = 0 if Wk is None else Wk.shape[1]
+    return make_desc(B, T, H, dk, dv, L, chunk, _dtype_code(q))
+
+
+def _workspace(nbytes, device):
+    ws = torch.empty(max(int(nbytes), 256) + 256, dtype=torch.uint8, device=device)
+    off = (-ws.data_ptr()) % 256
+    return ws, ws[off:]
+
+
+def forward_workspace_bytes(desc):
+    n = ctypes.c_size_t(0)
+    _check(lib().prism_forward_workspace(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def backward_workspace_bytes(desc):
+    n = ctypes.c_size_t(0)
+    _check(lib().prism_backward_workspace(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def _validate_inputs(q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0):
+    dev, dt = q.device, q.dtype
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        _req(t, name, dt, dev)
+    for name, t in (("alpha", alpha), ("beta", beta)):
+        _req(t, name, torch.float32, dev)
+    if Wk is not None:
+        for name, t in (("Wk", Wk), ("Wp", Wp), ("wbeta", wbeta), ("conv", conv)):
+            if t is None:
+                raise ValueError(f"{name} is required when Wk is given")
+            _req(t, name, dt, dev)
+    if S0 is not None:
+        _req(S0, "S0", torch.float32, dev)
+
+
+def forward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None, S0=None, chunk=64,
+            workspace=None):
+    """PRISM layer forward.  Returns (o, S_T).
+
+    q, k [B,T,H,dk], v [B,T,H,dv] (bf16 or fp32); alpha, beta [B,T,H] fp32;
+    Wk [H,L,dk,dv], Wp [H,L,dv,dv], wbeta [H,L,dv], conv [H,dv,4] in q's
+    dtype (all None for L = 0); S0 [B,H,dv,dk] fp32 or None.
+    """
+    _validate_inputs(q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0)
+    desc = _desc_from(q, v, Wk, chunk)
+    B, T, H, dk = q.shape
+    dv = v.shape[-1]
+    o = torch.empty_like(v)
+    ST = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
+    need = forward_workspace_bytes(desc)
+    if workspace is None:
+        _, ws = _workspace(need, q.device)
+    else:
+        ws = workspace
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(lib().prism_forward(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                               _ptr(beta), _ptr(Wk), _ptr(Wp), _ptr(wbeta), _ptr(conv), _ptr(S0),
+                               _ptr(o), _ptr(ST), _ptr(ws), ctypes.c_size_t(ws.numel()),
+                               ctypes.c_void_p(stream)))
+    return o, ST
+
+
+def backward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None, S0=None, dO=None,
+             dST=None, chunk=64, need_dS0=False, workspace=None):
+    """Gradients of <dO, o> + <dST, S_T> with respect to every input.
+
+    Returns a dict: dq, dk, dv (input dtype), dalpha, dbeta (fp32), and for
+    L > 0 dWk, dWp, dwbeta, dconv (fp32); dS0 (fp32) when need_dS0.
+    """
+    _validate_inputs(q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0)
+    if dO is None:
+        raise ValueError("dO is required")
+    _req(dO, "dO", q.dtype, q.device)
+    if dST is not None:
+        _req(dST, "dST", torch.float32, q.device)
+    desc = _desc_from(q, v, Wk, chunk)
+    B, T, H, dk = q.shape
+    dv_ = v.shape[-1]
+    dev = q.device
+    g = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
+         "dalpha": torch.empty_like(alpha), "dbeta": torch.empty_like(beta)}
+    if Wk is not None:
+        g["dWk"] = torch.empty(Wk.shape, dtype=torch.float32, device=dev)
+        g["dWp"] = torch.empty(Wp.shape, dtype=torch.float32, device=dev)
+        g["dwbeta"] = torch.empty(wbeta.shape, dtype=torch.float32, device=dev)
+        g["dconv"] = torch.empty(conv.shape, dtype=torch.float32, device=dev)
+    if need_dS0:
+        g["dS0"] = torch.empty((B, H, dv_, dk), dtype=torch.float32, device=dev)
+    need = backward_workspace_bytes(desc)
+    if workspace is None:
+        _, ws = _workspace(need, dev)
+    else:
+        ws = workspace
+    stream = torch.cuda.current_stream(dev).cuda_stream
+    _check(lib().prism_backward(
+        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(Wk), _ptr(Wp),
+        _ptr(wbeta), _ptr(conv), _ptr(S0), _ptr(dO), _ptr(dST), _ptr(g["dq"]), _ptr(g["dk"]),
+        _ptr(g["dv"]), _ptr(g["dalpha"]), _ptr(g["dbeta"]), _ptr(g.get("dWk")), _ptr(g.get("dWp")),
+        _ptr(g.get("dwbeta")), _ptr(g.get("dconv")), _ptr(g.get("dS0")), _ptr(ws),
+        ctypes.c_size_t(ws.numel()), ctypes.c_void_p(stream)))
+    return g
+
+
+class KernelTimer:
+    """Context manager: event-measured duration of every library kernel
+    launched inside the block (prism_timing_begin / prism_timing_end)."""
+
+    def __enter__(self):
+        lib().prism_timing_begin()
+        self.result = {}
+        return self
+
+    def __exit__(self, *exc):
+        cap = 64
+        names = (ctypes.c_char_p * cap)()
+        ms = (ctypes.c_double * cap)()
+        cnt = (ctypes.c_int * cap)()
+        n = lib().prism_timing_end(names, ms, cnt, cap)
+        self.result = {names[i].decode(): (ms[i], cnt[i]) for i in range(min(n, cap))}
+        return False

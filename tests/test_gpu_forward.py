@@ -1,0 +1,148 @@
+"""GPU forward parity: the HIP library (through the C ABI) against the oracle.
+
+Inputs come from the seeded generator; the oracle sees exactly the values the
+GPU sees (bf16- or fp32-representable, upcast to float64).  Error metric per
+output tensor: max |x - y| / max |y| (over the whole tensor, or over the
+sampled sequences at full workload sizes, where the oracle runs on a few
+(b, h) sequences only -- sequences are independent).  Tolerances: 1e-4 for
+fp32 storage, 2e-2 for bf16 storage with fp32 accumulation.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import prism_oracle as O
+from linear_recurrent_sequence_shortconv_amd.workloads import make_inputs, workloads
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+TDT = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def _dev(a, dtype):
+    return None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(dtype)
+
+
+def gpu_forward(x, dtype, chunk, L):
+    from linear_recurrent_sequence_shortconv_amd import prism as P
+    t = TDT[dtype]
+    w = (lambda n: _dev(x[n], t)) if L > 0 else (lambda n: None)
+    o, ST = P.forward(_dev(x["q"], t), _dev(x["k"], t), _dev(x["v"], t),
+                      _dev(x["alpha"], torch.float32), _dev(x["beta"], torch.float32),
+                      w("Wk"), w("Wp"), w("wbeta"), w("conv"), _dev(x["S0"], torch.float32),
+                      chunk=chunk)
+    torch.cuda.synchronize()
+    return o.double().cpu().numpy(), ST.double().cpu().numpy()
+
+
+def oracle_forward(x, L, b=None, h=None):
+    """Full oracle, or the oracle on the sequences (b[i], h[i]) only
+    (sequences are independent).  Sampled results: o [n, T, dv], S [n, dv, dk]."""
+    W = lambda hs: [x[n][hs] for n in ("Wk", "Wp", "wbeta", "conv")] if L > 0 else [None] * 4
+    if b is None:
+        return O.forward(x["q"], x["k"], x["v"], x["alpha"], x["beta"], *W(slice(None)), S0=x["S0"])
+    outs, states = [], []
+    for bi, hi in zip(b, h):
+        seq = {n: x[n][bi:bi + 1, :, hi:hi + 1] for n in ("q", "k", "v", "alpha", "beta")}
+        s0 = None if x["S0"] is None else x["S0"][bi:bi + 1, hi:hi + 1]
+        o, s = O.forward(seq["q"], seq["k"], seq["v"], seq["alpha"], seq["beta"],
+                         *W(slice(hi, hi + 1)), S0=s0)
+        outs.append(o[0, :, 0])
+        states.append(s[0, 0])
+    return np.stack(outs), np.stack(states)
+
+
+def relerr(x, y):
+    return float(np.max(np.abs(x - y)) / max(np.max(np.abs(y)), 1e-30))
+
+
+def _check_full(x, dtype, chunk, L, tol=None):
+    o, s = gpu_forward(x, dtype, chunk, L)
+    oo, so = oracle_forward(x, L)
+    eo, es = relerr(o, oo), relerr(s, so)
+    tol = tol or TOL[dtype]
+    print(f"  out rel err {eo:.3e}   state rel err {es:.3e}   (tol {tol:g})", flush=True)
+    assert eo <= tol and es <= tol, (eo, es)
+
+
+# --------------------------------------------------------------------------- small, full oracle
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+@pytest.mark.parametrize("d", [16, 32, 64])
+def test_fp32_chunk_sizes_ragged(d, chunk):
+    x = make_inputs(2, 100, 3, d, 2, "f32", seed=d + chunk, random_S0=True)
+    print(f"\n[fp32 d={d} chunk={chunk} T=100 L=2]", flush=True)
+    _check_full(x, "f32", chunk, 2)
+
+
+@pytest.mark.parametrize("L", [0, 1, 3, 8])
+def test_fp32_depths(L):
+    x = make_inputs(1, 70, 2, 32, L, "f32", seed=40 + L)
+    print(f"\n[fp32 d=32 chunk=32 T=70 L={L}]", flush=True)
+    _check_full(x, "f32", 32, L)
+
+
+def test_tiny_fp32_workload():
+    w = workloads()["tiny-fp32"]
+    x = make_inputs(w.B, w.T, w.H, w.d, w.L, w.dtype, seed=0)
+    print(f"\n[{w.name}]", flush=True)
+    _check_full(x, w.dtype, w.chunk, w.L)
+
+
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_bf16_d128_chunk_sizes_ragged(chunk):
+    x = make_inputs(2, 150, 2, 128, 3, "bf16", seed=chunk)
+    print(f"\n[bf16 d=128 chunk={chunk} T=150 L=3]", flush=True)
+    _check_full(x, "bf16", chunk, 3)
+
+
+@pytest.mark.parametrize("T", [1, 5, 63, 64, 65])
+def test_bf16_short_sequences(T):
+    x = make_inputs(3, T, 2, 64, 2, "bf16", seed=T, random_S0=True)
+    print(f"\n[bf16 d=64 chunk=64 T={T} L=2 S0]", flush=True)
+    _check_full(x, "bf16", 64, 2)
+
+
+def test_bf16_long_memory():
+    """forget gate close to 1 (sigmoid(N(6, 0.5)), mean ~0.9975): memory spans
+    many chunks, so chunk-to-chunk error accumulation is exercised."""
+    x = make_inputs(2, 512, 2, 64, 2, "bf16", seed=3, alpha_logit_mean=6.0)
+    print("\n[bf16 long memory d=64 T=512 L=2]", flush=True)
+    _check_full(x, "bf16", 64, 2)
+
+
+def test_recsys_workload_full():
+    w = workloads()["recsys-T200"]
+    x = make_inputs(w.B, w.T, w.H, w.d, w.L, w.dtype, seed=0)
+    print(f"\n[{w.name}]", flush=True)
+    _check_full(x, w.dtype, w.chunk, w.L)
+
+
+# --------------------------------------------------------------------------- full sizes, sampled
+def _check_sampled(name, pairs, seed=0):
+    w = workloads()[name]
+    x = make_inputs(w.B, w.T, w.H, w.d, w.L, w.dtype, seed=seed)
+    print(f"\n[{name} sampled {pairs}]", flush=True)
+    o, s = gpu_forward(x, w.dtype, w.chunk, w.L)
+    b = [p[0] for p in pairs]
+    h = [p[1] for p in pairs]
+    oo, so = oracle_forward(x, w.L, b, h)
+    og = np.stack([o[bi, :, hi] for bi, hi in pairs])
+    sg = np.stack([s[bi, hi] for bi, hi in pairs])
+    eo, es = relerr(og, oo), relerr(sg, so)
+    print(f"  out rel err {eo:.3e}   state rel err {es:.3e}", flush=True)
+    assert eo <= TOL[w.dtype] and es <= TOL[w.dtype], (eo, es)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(s))
+
+
+def test_lm_workload_sampled():
+    _check_sampled("lm-T2048", [(0, 0), (3, 7), (7, 15)])
+
+
+def test_long_T16384_sampled():
+    _check_sampled("long-T16384", [(0, 0), (0, 11)])
+
+
+@pytest.mark.parametrize("L", [0, 8])
+def test_depth_sampled(L):
+    _check_sampled(f"depth-L{L}", [(0, 3), (3, 12)])
