@@ -1,0 +1,230 @@
+"""Benchmark of the PRISM layer hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload lm-T2048]
+
+One step = one pass of the whole hot path over one batch of synthetic input
+with the inputs already resident in HBM: the forward pass (ShortConv anchor,
+L refinement steps, chunked scan, readout, final state) followed by the
+backward pass (every input and weight gradient) when the library provides
+it.  The default workload is the language-model layer shape: B=8, H=16,
+T=2048, d_k=d_v=128, L=3, chunk 64, bf16 storage with fp32 accumulation.
+
+Prints one JSON line.  Besides the throughput it reports, for the kernel with
+the largest share of the step, its achieved rate against the MI355X peak
+(HBM 8 TB/s, dense bf16 MFMA 2.5 PFLOP/s), using algorithmic bytes / FLOPs
+per launch divided by the HIP-event-measured average launch duration; and
+the float64 oracle timed on a bounded sample on the host CPU.
+
+--calibrate-copy runs only a plain 1 GiB device copy (for scaling HBM byte
+counters of rocprofv3 runs) and exits.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
+MFMA_F32_PEAK_TFLOPS = 157.3
+
+
+def algorithmic_counts(w):
+    """Algorithmic bytes and FLOPs per launch of each kernel for workload w.
+
+    Bytes count each tensor once at its storage size (e = 2 for bf16):
+    what the kernel must read and write, not what it happens to re-read.
+    FLOPs count the dense matrix products of the algorithm (2 m n k each).
+    """
+    B, T, H, D, L, C = w.B, w.T, w.H, w.d, w.L, w.chunk
+    e = 2 if w.dtype == "bf16" else 4
+    NC = -(-T // C)
+    th = B * T * H                 # token-heads
+    nch = B * H * NC               # chunks
+    out = {}
+    out["refine_fwd"] = {
+        "bytes": th * e * (D + 2 * L * D),                        # read v, write K_l, W_l
+        "flops": th * (2 * L * 2 * D * D),                        # k^(l), p^(l) projections
+        "bound": "hbm"}
+    out["chunk_fwd"] = {
+        "bytes": nch * (C * D * e * (3 + 2 * L) + 8 * C            # q, k, v, K_l, W_l, alpha, beta
+                        + D * D * (e + 4) + C * D * (e + 4) + 4),  # M^T, H^T, Qt, O_loc, gC
+        "flops": nch * (2 * C * C * D * (4 * L + 6) + 2 * C * D * D * (L + 2)),
+        "bound": "mfma"}
+    out["state_fwd"] = {
+        "bytes": nch * D * D * (e + 4 + e) + B * H * D * D * 4,   # read M^T, H^T; write S_c; S_T
+        "flops": nch * 2 * D * D * D,
+        "bound": "hbm"}
+    out["out_fwd"] = {
+        "bytes": nch * (D * D * e + C * D * (e + 4)) + th * D * e,
+        "flops": nch * 2 * C * D * D,
+        "bound": "hbm"}
+    return out
+
+
+def roofline_for(name, counts, avg_ms, dtype):
+    c = counts.get(name)
+    if c is None or avg_ms <= 0:
+        return None
+    if c["bound"] == "mfma":
+        achieved = c["flops"] / (avg_ms * 1e-3) / 1e12
+        peak = MFMA_BF16_PEAK_TFLOPS if dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+        unit = "TFLOP/s"
+    else:
+        achieved = c["bytes"] / (avg_ms * 1e-3) / 1e9
+        peak = HBM_PEAK_GBS
+        unit = "GB/s"
+    return {"kernel": name, "bound": c["bound"], "achieved": round(achieved, 2), "peak": peak,
+            "unit": unit, "frac": round(achieved / peak, 4), "traffic": None,
+            "avg_launch_ms": round(avg_ms, 5)}
+
+
+def cpu_baseline(w, x, budget_s=15.0, backward=False):
+    """The float64 oracle, as it stands, on a bounded sample of the workload:
+    whole (b, h) sequences of the same inputs, one thread.  Returns tokens/s
+    scaled to the workload's unit (a token spans all H heads)."""
+    from threadpoolctl import threadpool_limits
+    from oracle import prism_oracle as O
+    seqs, t_used = 0, 0.0
+    with threadpool_limits(limits=1):
+        pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
+        for b, h in pairs:
+            t0 = time.perf_counter()
+            s = {n: x[n][b:b + 1, :, h:h + 1] for n in ("q", "k", "v", "alpha", "beta", "dO")}
+            W = [x[n][h:h + 1] for n in ("Wk", "Wp", "wbeta", "conv")] if w.L > 0 else [None] * 4
+            O.forward(s["q"], s["k"], s["v"], s["alpha"], s["beta"], *W)
+            if backward:
+                O.backward(s["q"], s["k"], s["v"], s["alpha"], s["beta"], *W, dO=s["dO"])
+            t_used += time.perf_counter() - t0
+            seqs += 1
+            if t_used >= budget_s:
+                break
+    tokens = seqs * w.T / w.H
+    return {"value": round(tokens / t_used, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"{seqs} of {w.B * w.H} (b,h) sequences x T={w.T}, "
+                      f"{'fwd+bwd' if backward else 'fwd'}, float64, {t_used:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="lm-T2048")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--forward-only", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+              "(sequences and heads are independent, so several GPUs would each run this same "
+              "per-GPU workload).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    if args.calibrate_copy:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibrate_copy_bytes": n, "launches": 3}))
+        return
+
+    from linear_recurrent_sequence_shortconv_amd import prism as P
+    from linear_recurrent_sequence_shortconv_amd.workloads import make_workload_inputs, workloads
+
+    w = workloads()[args.workload]
+    x = make_workload_inputs(w, seed=0)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = lambda a, t=tdt: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(t)
+    f32 = torch.float32
+    q, k, v, dO = dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["dO"])
+    alpha, beta = dev(x["alpha"], f32), dev(x["beta"], f32)
+    if w.L > 0:
+        Wk, Wp, wbeta, conv = dev(x["Wk"]), dev(x["Wp"]), dev(x["wbeta"]), dev(x["conv"])
+    else:
+        Wk = Wp = wbeta = conv = None
+
+    desc = P.make_desc(w.B, w.T, w.H, w.d, w.d, w.L, w.chunk, P.PRISM_BF16 if w.dtype == "bf16" else P.PRISM_F32)
+    backward = not args.forward_only
+    try:
+        P.backward_workspace_bytes(desc)
+    except RuntimeError:
+        backward = False
+    ws_f = P._workspace(P.forward_workspace_bytes(desc), q.device)[1]
+    ws_b = P._workspace(P.backward_workspace_bytes(desc), q.device)[1] if backward else None
+
+    def step():
+        P.forward(q, k, v, alpha, beta, Wk, Wp, wbeta, conv, chunk=w.chunk, workspace=ws_f)
+        if backward:
+            P.backward(q, k, v, alpha, beta, Wk, Wp, wbeta, conv, dO=dO, chunk=w.chunk,
+                       workspace=ws_b)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # whole-step timing (events on the current stream, which the library uses)
+    t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_start.record()
+    for _ in range(args.steps):
+        step()
+    t_end.record()
+    torch.cuda.synchronize()
+    ms = t_start.elapsed_time(t_end) / args.steps
+
+    # per-kernel timing over a second timed region (HIP events around each launch)
+    with P.KernelTimer() as kt:
+        for _ in range(args.steps):
+            step()
+        torch.cuda.synchronize()
+    kernels = {n: {"total_ms": round(tot / args.steps, 5), "launches_per_step": c // args.steps,
+                   "avg_launch_ms": round(tot / c, 5)} for n, (tot, c) in kt.result.items()}
+    counts = algorithmic_counts(w)
+    dominant = max(kernels, key=lambda n: kernels[n]["total_ms"]) if kernels else None
+    roof = roofline_for(dominant, counts, kernels[dominant]["avg_launch_ms"], w.dtype) if dominant else None
+    for n in kernels:
+        r = roofline_for(n, counts, kernels[n]["avg_launch_ms"], w.dtype)
+        if r:
+            kernels[n].update(bound=r["bound"], achieved=r["achieved"], unit=r["unit"], frac=r["frac"])
+
+    tokens = w.B * w.T
+    value = tokens / (ms * 1e-3)
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, x, backward=backward)
+
+    line = {
+        "metric": "PRISM layer tokens/s (fwd+bwd step" + ("" if backward else "; forward only") + ")",
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "d_k": w.d, "d_v": w.d,
+                   "L": w.L, "chunk": w.chunk, "global_batch": w.B, "seq_len": w.T,
+                   "passes": "fwd+bwd" if backward else "fwd", "parallelism": "single GPU"},
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -66,8 +66,9 @@ typedef enum {
  *   dk, dv     key / value head dimension; must be equal, in {16, 32, 64, 128}
  *              for PRISM_BF16 and {16, 32, 64} for PRISM_F32
  *   L          refinement steps, 0 <= L <= 8
- *   chunk      tokens per chunk of the parallel scan, in {16, 32, 64};
- *              any T >= 1 is accepted (the last chunk may be partial)
+ *   chunk      tokens per chunk of the parallel scan, in {16, 32, 64}
+ *              (PRISM_F32 also needs dk * chunk <= 2048); any T >= 1 is
+ *              accepted (the last chunk may be partial)
  *   conv_width ShortConv width; must be 4
  *   dtype      storage type of the dtype-typed tensors (see prism_dtype)   */
 typedef struct {

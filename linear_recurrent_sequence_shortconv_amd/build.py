@@ -23,6 +23,8 @@ SOURCES = [
     "refine_fwd.hip",
     "chunk_fwd.hip",
     "state.hip",
+    "chunk_bwd.hip",
+    "refine_bwd.hip",
 ]
 
 ARCH = "gfx950"

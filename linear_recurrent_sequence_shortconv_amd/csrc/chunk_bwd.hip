@@ -1,0 +1,1052 @@
+// Chunk-parallel part of the PRISM backward pass: the adjoint of the chunk
+// affine map (see chunk_fwd.hip)
+//
+//     S_next = exp(gC) S - S M + H,    O = O_loc + Qt S^T,
+//     M = Wk^T D K,  H = U^T D K + sum_l W_l^T D K_l,  Qt = e Q - R0 Wk,
+//     O_loc = R0 U + sum_l R_l W_l,  U = T diag(beta) V',  Wk = T diag(beta e) K,
+//     T = (I + A)^{-1},  A = diag(beta) (Gam * K K^T)_{i<t},
+//     V' = V - sum_l F_l W_l,  F_l = (Gam * K K_l^T)_{i<t},  R_* = (Gam * Q K_*^T)_{i<=t},
+//
+// given the state S entering each chunk (stored transposed), the adjoint dS_n
+// of the state leaving it (stored transposed) and dO.  Three kernels, all
+// parallel over B * H * NC chunks:
+//
+//   chunk_bwd_state : terms through S, dS_n and dM = -S^T dS_n
+//                     (dQt = dO S; D-weighted parts of dU, dWk, dK, dK_l, dW_l;
+//                     the D and gC parts of dg)
+//   chunk_bwd_solve : R0 terms, then the triangular solve backward
+//                     (dT, dA = -T^T dT T^T, dK from the Gram matrix), dV', dbeta
+//   chunk_bwd_pairs : the refinement-pair terms (R_l, F_l), final dq, dk, dK_l,
+//                     dW_l, dv and dalpha (reverse cumulative sum of dg).
+//
+// All products are MFMA (bf16 or fp32 operands, fp32 accumulation).  Row and
+// column sums needed for the decay gradient are reduced per wave in fixed
+// order (no atomics), so results are bitwise reproducible.
+#include "prism_common.h"
+#include "prism_internal.h"
+
+namespace prism {
+
+constexpr int CB_NW = 8;
+constexpr int CB_NT = CB_NW * WAVE;
+
+// ---------------------------------------------------------------------------
+// shared helpers
+// ---------------------------------------------------------------------------
+// Decays of one chunk: g (cumulative log alpha), e = exp(g), Dv = exp(gC - g),
+// bt = beta, be = beta e.  Padding tokens (t >= nval) have alpha = 1, beta = 0.
+template <int C>
+__device__ inline void chunk_decays(const float* alpha, const float* beta, long row0, int H,
+                                    int nval, float* g, float* ev, float* Dv, float* bt, float* be,
+                                    float* ai, int lane) {
+  float lg = 0.f, bv = 0.f, a = 1.f;
+  if (lane < nval) {
+    a = alpha[row0 + (long)lane * H];
+    lg = logf(a);
+    if (beta) bv = beta[row0 + (long)lane * H];
+  }
+  float s = lg;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const float y = __shfl_up(s, off);
+    if (lane >= off) s += y;
+  }
+  const float gC = __shfl(s, C - 1);
+  if (lane < C) {
+    const float e = expf(s);
+    g[lane] = s;
+    ev[lane] = e;
+    Dv[lane] = expf(gC - s);
+    if (bt) bt[lane] = bv;
+    if (be) be[lane] = bv * e;
+    if (ai) ai[lane] = a;
+  }
+}
+
+// Row sums (over the 16 lanes of a row group) and column sums (over the 4
+// rows of a lane and the 4 row groups) of one accumulator tile, added into
+// this wave's private slots.
+__device__ inline void add_rowsum(float* slot, int row0, const f32x4& v, int lane) {
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float s = v[i];
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 4);
+    s += __shfl_xor(s, 8);
+    if ((lane & 15) == 0) slot[row0 + i] += s;
+  }
+}
+__device__ inline void add_colsum(float* slot, int col, const f32x4& v, int lane) {
+  float s = v[0] + v[1] + v[2] + v[3];
+  s += __shfl_xor(s, 16);
+  s += __shfl_xor(s, 32);
+  if (lane < 16) slot[col] += s;
+}
+
+// fp32 global rows -> operand-type LDS rows (optionally negated)
+template <typename E, int ROWS, int COLS, int NT>
+__device__ inline void g2s_rows_f32(E* s, int ld, const float* g, long gstride, float scale, int tid) {
+  constexpr int VPR = COLS / 4;
+  for (int e = tid; e < ROWS * VPR; e += NT) {
+    const int r = e / VPR, c = (e % VPR) * 4;
+    const f32x4 x = *reinterpret_cast<const f32x4*>(g + r * gstride + c);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s[r * ld + c + j] = to_t<E>(scale * x[j]);
+  }
+}
+
+// ===========================================================================
+// chunk_bwd_state
+// ===========================================================================
+template <typename E, int D, int C>
+struct CB1Lds {
+  static constexpr int LR = ldpad<E>(D);
+  static constexpr int LD2 = ldpad<E>(D);
+  static constexpr int SZ_R = C * LR * (int)sizeof(E);
+  static constexpr int SZ_DD = D * LD2 * (int)sizeof(E);
+  static constexpr int O_VEC = 0;                                  // g, e, Dv (3C) + slots
+  static constexpr int SZ_VEC = (3 * C + CB_NW * C + CB_NW) * 4;
+  static constexpr int O_X1 = (O_VEC + SZ_VEC + 15) / 16 * 16;     // S^T, then dS_n, then dM
+  static constexpr int O_X2 = O_X1 + SZ_DD;                        // dS_n^T, then dM^T
+  static constexpr int O_R1 = O_X2 + SZ_DD;                        // dO rows, then K rows
+  static constexpr int O_R2 = O_R1 + SZ_R;                         // U rows
+  static constexpr int O_R3 = O_R2 + SZ_R;                         // K_l rows, then Wk rows
+  static constexpr int O_R4 = O_R3 + SZ_R;                         // W_l rows
+  static constexpr int TOTAL = O_R4 + SZ_R;
+};
+
+template <typename E, int D, int C>
+__global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
+    const E* __restrict__ k, const E* __restrict__ dO, const float* __restrict__ alpha,
+    const E* __restrict__ Kl, const E* __restrict__ Wl, const E* __restrict__ UT,
+    const E* __restrict__ WkT, const E* __restrict__ St, const E* __restrict__ dSnT,
+    float* __restrict__ dQt, float* __restrict__ dUs, float* __restrict__ dWks,
+    float* __restrict__ dKs, float* __restrict__ dKls, float* __restrict__ dWls,
+    float* __restrict__ dgs, int B, int T, int H, int L, int NC, int Tp) {
+  typedef CB1Lds<E, D, C> LY;
+  constexpr int NW = CB_NW, NT = CB_NT;
+  constexpr int LR = LY::LR, LD2 = LY::LD2;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[LY::TOTAL];
+  float* g = reinterpret_cast<float*>(smem + LY::O_VEC);
+  float* ev = g + C;
+  float* Dv = g + 2 * C;
+  float* ddw = g + 3 * C;            // [NW][C] per-wave row sums of dD
+  float* sdw = ddw + NW * C;         // [NW] per-wave sums of S (.) dS_n
+  E* X1 = reinterpret_cast<E*>(smem + LY::O_X1);
+  E* X2 = reinterpret_cast<E*>(smem + LY::O_X2);
+  E* R1 = reinterpret_cast<E*>(smem + LY::O_R1);
+  E* R2 = reinterpret_cast<E*>(smem + LY::O_R2);
+  E* R3 = reinterpret_cast<E*>(smem + LY::O_R3);
+  E* R4 = reinterpret_cast<E*>(smem + LY::O_R4);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nblk = B * H * NC;
+  const int bid = xcd_swizzle(blockIdx.x, nblk);
+  const int c = bid % NC, bh = bid / NC;
+  const int h = bh % H, b = bh / H;
+  const int tb = c * C;
+  const int nval = min(C, T - tb);
+  const long ts = (long)H * D;
+  const long row0 = ((long)b * T + tb) * H + h;
+  const long cidx = (long)bh * NC + c;
+
+  for (int e = tid; e < NW * C + NW; e += NT) ddw[e] = 0.f;
+  if (wave == 0) chunk_decays<C>(alpha, nullptr, row0, H, nval, g, ev, Dv, nullptr, nullptr, nullptr, lane);
+  g2s_rows<E, C, D, NT>(R1, LR, dO + row0 * D, ts, nval, tid);
+  g2s_rows<E, D, D, NT>(X1, LD2, St + cidx * D * D, D, D, tid);
+  g2s_rows<E, D, D, NT>(X2, LD2, dSnT + cidx * D * D, D, D, tid);
+  __syncthreads();
+
+  // ---- dQt = dO S  ([t][k] = sum_r dO[t][r] S^T[k][r]);  dM = -S^T dS_n ----
+  {
+    Acc<C, D, NW> a;
+    a.zero();
+    gemm_acc<E, C, D, D, NW, true, true>(a, R1, LR, X1, LD2, wave, lane);
+    float* out = dQt + cidx * C * D;
+    for_tiles(a, wave, lane, [&](int t0, int kk, const f32x4& x) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) out[(long)(t0 + r) * D + kk] = x[r];
+    });
+  }
+  Acc<D, D, NW> dm;   // [k][n] = sum_r S^T[k][r] dS_n^T[n][r]  (= -dM)
+  dm.zero();
+  gemm_acc<E, D, D, D, NW, true, true>(dm, X1, LD2, X2, LD2, wave, lane);
+  {
+    float s = 0.f;
+    for (int e = tid; e < D * D; e += NT) {
+      const int r = e / D, cc = e % D;
+      s += to_f(X1[r * LD2 + cc]) * to_f(X2[r * LD2 + cc]);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    if (lane == 0) sdw[wave] = s;
+  }
+  __syncthreads();
+
+  // ---- dS_n (row-major) into X1; K and U rows ----
+  for (int e = tid; e < D * D; e += NT) {
+    const int r = e / D, n = e % D;
+    X1[r * LD2 + n] = X2[n * LD2 + r];
+  }
+  g2s_rows<E, C, D, NT>(R1, LR, k + row0 * D, ts, nval, tid);
+  g2s_rows_transposed<E, D, C, NT>(R2, LR, UT + cidx * D * C, C, D, nullptr, tid);
+  __syncthreads();
+
+  Acc<C, D, NW> dk;   // D-weighted dK:  D (U dS_n + Wk dM)
+  dk.zero();
+  {
+    Acc<C, D, NW> a;    // U dS_n: [t][n] = sum_r U[t][r] dS_n^T[n][r]
+    a.zero();
+    gemm_acc<E, C, D, D, NW, true, true>(a, R2, LR, X2, LD2, wave, lane);
+    for_tiles_mut(dk, wave, lane, [&](int, int, f32x4&) {});
+    {
+      typedef Tiling<C, D, NW> TL;
+      if (TL::active(wave)) {
+#pragma unroll
+        for (int i = 0; i < TL::RM; ++i)
+#pragma unroll
+          for (int j = 0; j < TL::RN; ++j) {
+            const int t0 = TL::m0(wave) + 16 * i + 4 * (lane >> 4);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dk.v[i][j][r] = Dv[t0 + r] * a.v[i][j][r];
+          }
+      }
+    }
+    Acc<C, D, NW> u;    // K dS_n^T: [t][r] = sum_n K[t][n] dS_n[r][n]
+    u.zero();
+    gemm_acc<E, C, D, D, NW, true, true>(u, R1, LR, X1, LD2, wave, lane);
+    float* out = dUs + cidx * C * D;
+    for_tiles(u, wave, lane, [&](int t0, int rr, const f32x4& x) {
+      f32x4 pu;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        out[(long)(t0 + r) * D + rr] = Dv[t0 + r] * x[r];
+        pu[r] = x[r] * to_f(R2[(t0 + r) * LR + rr]);
+      }
+      add_rowsum(ddw + wave * C, t0, pu, lane);
+    });
+  }
+  // ---- refinement pairs: dW_l += D (K_l dS_n^T), dK_l += D (W_l dS_n) ----
+  for (int l = 0; l < L; ++l) {
+    const long lrow = ((long)bh * L + l) * Tp + tb;
+    g2s_rows<E, C, D, NT>(R3, LR, Kl + lrow * D, D, C, tid);
+    g2s_rows<E, C, D, NT>(R4, LR, Wl + lrow * D, D, C, tid);
+    __syncthreads();
+    Acc<C, D, NW> a;
+    a.zero();
+    gemm_acc<E, C, D, D, NW, true, true>(a, R3, LR, X1, LD2, wave, lane);
+    float* ow = dWls + lrow * D;
+    for_tiles(a, wave, lane, [&](int t0, int rr, const f32x4& x) {
+      f32x4 pw;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        ow[(long)(t0 + r) * D + rr] = Dv[t0 + r] * x[r];
+        pw[r] = x[r] * to_f(R4[(t0 + r) * LR + rr]);
+      }
+      add_rowsum(ddw + wave * C, t0, pw, lane);
+    });
+    Acc<C, D, NW> bb;
+    bb.zero();
+    gemm_acc<E, C, D, D, NW, true, true>(bb, R4, LR, X2, LD2, wave, lane);
+    float* ok = dKls + lrow * D;
+    for_tiles(bb, wave, lane, [&](int t0, int n, const f32x4& x) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ok[(long)(t0 + r) * D + n] = Dv[t0 + r] * x[r];
+    });
+    __syncthreads();
+  }
+
+  // ---- dM (row-major into X1, transposed into X2); Wk rows ----
+  for_tiles(dm, wave, lane, [&](int k0, int n, const f32x4& x) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      X1[(k0 + r) * LD2 + n] = to_t<E>(-x[r]);
+      X2[n * LD2 + k0 + r] = to_t<E>(-x[r]);
+    }
+  });
+  g2s_rows_transposed<E, D, C, NT>(R3, LR, WkT + cidx * D * C, C, D, nullptr, tid);
+  __syncthreads();
+  {
+    Acc<C, D, NW> a;    // K dM^T: [t][k] = sum_n K[t][n] dM[k][n]
+    a.zero();
+    gemm_acc<E, C, D, D, NW, true, true>(a, R1, LR, X1, LD2, wave, lane);
+    float* out = dWks + cidx * C * D;
+    for_tiles(a, wave, lane, [&](int t0, int kk, const f32x4& x) {
+      f32x4 pw;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        out[(long)(t0 + r) * D + kk] = Dv[t0 + r] * x[r];
+        pw[r] = x[r] * to_f(R3[(t0 + r) * LR + kk]);
+      }
+      add_rowsum(ddw + wave * C, t0, pw, lane);
+    });
+    Acc<C, D, NW> bb;   // Wk dM: [t][n] = sum_k Wk[t][k] dM^T[n][k]
+    bb.zero();
+    gemm_acc<E, C, D, D, NW, true, true>(bb, R3, LR, X2, LD2, wave, lane);
+    float* ok = dKs + cidx * C * D;
+    typedef Tiling<C, D, NW> TL;
+    if (TL::active(wave)) {
+#pragma unroll
+      for (int i = 0; i < TL::RM; ++i)
+#pragma unroll
+        for (int j = 0; j < TL::RN; ++j) {
+          const int t0 = TL::m0(wave) + 16 * i + 4 * (lane >> 4);
+          const int n = TL::n0(wave) + 16 * j + (lane & 15);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            ok[(long)(t0 + r) * D + n] = dk.v[i][j][r] + Dv[t0 + r] * bb.v[i][j][r];
+        }
+    }
+  }
+  __syncthreads();
+  // ---- dg from D_t = exp(gC - g_t) and exp(gC) ----
+  if (wave == 0) {
+    float dd = 0.f;
+    if (lane < C)
+      for (int w = 0; w < NW; ++w) dd += ddw[w * C + lane];
+    const float Dd = lane < C ? Dv[lane] * dd : 0.f;
+    float tot = Dd;
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) tot += __shfl_xor(tot, off);
+    float ssum = 0.f;
+    for (int w = 0; w < NW; ++w) ssum += sdw[w];
+    const float dgC = expf(g[C - 1]) * ssum + tot;
+    if (lane < C) dgs[cidx * C + lane] = -Dd + (lane == C - 1 ? dgC : 0.f);
+  }
+}
+
+// ===========================================================================
+// chunk_bwd_solve
+// ===========================================================================
+template <typename E, int D, int C>
+struct CB2Lds {
+  static constexpr int LR = ldpad<E>(D);
+  static constexpr int LT = ldpad<E>(C);
+  static constexpr int LA = C + 1;
+  static constexpr int SZ_R = C * LR * (int)sizeof(E);
+  static constexpr int SZ_CC = C * LT * (int)sizeof(E);
+  static constexpr int SZ_F = C * LA * 4;
+  // vectors: g, e, Dv, bt, be, de (6C) + slots rs, cs, bs, es [NW][C]
+  static constexpr int SZ_VEC = (6 * C + 4 * CB_NW * C) * 4;
+  static constexpr int O_K = (SZ_VEC + 15) / 16 * 16;
+  static constexpr int O_TB = O_K + SZ_R;
+  static constexpr int O_X = O_TB + SZ_CC;
+  // phase "fold": K_l, W_l, F, V rows (-> V' rows)
+  static constexpr int F_KL = O_X;
+  static constexpr int F_WL = F_KL + SZ_R;
+  static constexpr int F_F = F_WL + SZ_R;
+  static constexpr int F_V = F_F + SZ_CC;
+  static constexpr int F_END = F_V + SZ_R;
+  // phase "solve": A, T fp32, scratch; then T diag(beta), T diag(beta e)
+  static constexpr int S_AF = O_X;
+  static constexpr int S_TF = S_AF + SZ_F;
+  static constexpr int S_XS = S_TF + SZ_F;
+  static constexpr int S_TBB = cmax(S_XS + 3 * 256 * 4, F_END);
+  static constexpr int S_TBE = S_TBB + SZ_CC;
+  // phase "R0": U, Wk rows (then dU, dWk rows), Q, dO, -dQt rows, R0, X0
+  static constexpr int P_U = O_X;
+  static constexpr int P_WK = P_U + SZ_R;
+  static constexpr int P_Q = P_WK + SZ_R;
+  static constexpr int P_DO = P_Q + SZ_R;
+  static constexpr int P_NDQ = P_DO + SZ_R;
+  static constexpr int P_R0 = cmax(P_NDQ + SZ_R, S_TBE + SZ_CC);
+  static constexpr int P_XB = P_R0 + SZ_CC;
+  static constexpr int P_END = P_XB + SZ_CC;
+  // phase "tail": V' rows (Q slot), dT (R0 slot), P1 (X0 slot), Zf (dO slot), Zb
+  static constexpr int Z_F = P_DO;
+  static constexpr int Z_B = P_NDQ + (SZ_F > SZ_R ? SZ_F - SZ_R : 0);
+  static constexpr int TOTAL = cmax(P_END, cmax(Z_B + SZ_CC, S_TBE + SZ_CC));
+};
+
+template <int C, int NT>
+__device__ void invert_unit_lower_b(const float* A, float* Tm, float* Xs, int tid);
+
+template <typename E, int D, int C>
+__global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
+    const E* __restrict__ dO, const float* __restrict__ alpha, const float* __restrict__ beta,
+    const E* __restrict__ Kl, const E* __restrict__ Wl, const float* __restrict__ dQt,
+    const float* __restrict__ dUs, const float* __restrict__ dWks, const float* __restrict__ dKs,
+    const float* __restrict__ dgs, float* __restrict__ dVp, float* __restrict__ dqp,
+    float* __restrict__ dkp, float* __restrict__ dgp, float* __restrict__ dbeta, int B, int T,
+    int H, int L, int NC, int Tp) {
+  typedef CB2Lds<E, D, C> LY;
+  constexpr int NW = CB_NW, NT = CB_NT;
+  constexpr int LR = LY::LR, LT = LY::LT, LA = LY::LA;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[LY::TOTAL];
+  float* g = reinterpret_cast<float*>(smem);
+  float* ev = g + C;
+  float* Dv = g + 2 * C;
+  float* bt = g + 3 * C;
+  float* be = g + 4 * C;
+  float* de = g + 5 * C;
+  float* rs = g + 6 * C;            // [NW][C] row sums for dg
+  float* cs = rs + NW * C;          // [NW][C] column sums for dg
+  float* bs = cs + NW * C;          // [NW][C] dbeta
+  float* es = bs + NW * C;          // [NW][C] de
+  E* Kr = reinterpret_cast<E*>(smem + LY::O_K);
+  E* Tb = reinterpret_cast<E*>(smem + LY::O_TB);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nblk = B * H * NC;
+  const int bid = xcd_swizzle(blockIdx.x, nblk);
+  const int c = bid % NC, bh = bid / NC;
+  const int h = bh % H, b = bh / H;
+  const int tb = c * C;
+  const int nval = min(C, T - tb);
+  const long ts = (long)H * D;
+  const long row0 = ((long)b * T + tb) * H + h;
+  const long cidx = (long)bh * NC + c;
+  typedef Tiling<C, D, NW> TLD;
+  typedef Tiling<C, C, NW> TLC;
+  const bool actD = TLD::active(wave), actC = TLC::active(wave);
+
+  for (int e = tid; e < 4 * NW * C; e += NT) rs[e] = 0.f;
+  if (wave == 0) chunk_decays<C>(alpha, beta, row0, H, nval, g, ev, Dv, bt, be, nullptr, lane);
+  if (tid < C) de[tid] = 0.f;
+  g2s_rows<E, C, D, NT>(Kr, LR, k + row0 * D, ts, nval, tid);
+  __syncthreads();
+
+  // ---- fold: V' = V - sum_l (Gam * K K_l^T)_{i<t} W_l  (kept in registers) ----
+  Acc<C, D, NW> vp;
+  vp.zero();
+  {
+    E* Klr = reinterpret_cast<E*>(smem + LY::F_KL);
+    E* Wlr = reinterpret_cast<E*>(smem + LY::F_WL);
+    E* Fb = reinterpret_cast<E*>(smem + LY::F_F);
+    E* Vr = reinterpret_cast<E*>(smem + LY::F_V);
+    for (int l = 0; l < L; ++l) {
+      const long lrow = ((long)bh * L + l) * Tp + tb;
+      g2s_rows<E, C, D, NT>(Klr, LR, Kl + lrow * D, D, C, tid);
+      g2s_rows<E, C, D, NT>(Wlr, LR, Wl + lrow * D, D, C, tid);
+      __syncthreads();
+      Acc<C, C, NW> f;    // [t][i] = K_t . K_l,i
+      f.zero();
+      gemm_acc<E, C, C, D, NW, true, true>(f, Kr, LR, Klr, LR, wave, lane);
+      for_tiles(f, wave, lane, [&](int t0, int i, const f32x4& x) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int t = t0 + r;
+          Fb[t * LT + i] = to_t<E>(i < t ? __expf(g[t] - g[i]) * x[r] : 0.f);
+        }
+      });
+      __syncthreads();
+      gemm_acc<E, C, D, C, NW, true, false>(vp, Fb, LT, Wlr, LR, wave, lane);
+      __syncthreads();
+    }
+    g2s_rows<E, C, D, NT>(Vr, LR, v + row0 * D, ts, nval, tid);
+    __syncthreads();
+    for_tiles_mut(vp, wave, lane, [&](int t0, int f, f32x4& x) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        x[r] = to_f(Vr[(t0 + r) * LR + f]) - x[r];
+        Vr[(t0 + r) * LR + f] = to_t<E>(x[r]);      // V' rows, in place
+      }
+    });
+  }
+
+  // ---- solve: A = diag(beta)(Gam * K K^T)_{i<t}, T = (I + A)^{-1} ----
+  E* Tbb = reinterpret_cast<E*>(smem + LY::S_TBB);
+  E* Tbe = reinterpret_cast<E*>(smem + LY::S_TBE);
+  {
+    float* Af = reinterpret_cast<float*>(smem + LY::S_AF);
+    float* Tf = reinterpret_cast<float*>(smem + LY::S_TF);
+    float* Xs = reinterpret_cast<float*>(smem + LY::S_XS);
+    Acc<C, C, NW> a;
+    a.zero();
+    gemm_acc<E, C, C, D, NW, true, true>(a, Kr, LR, Kr, LR, wave, lane);
+    for_tiles(a, wave, lane, [&](int t0, int i, const f32x4& x) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = t0 + r;
+        Af[t * LA + i] = i < t ? bt[t] * __expf(g[t] - g[i]) * x[r] : 0.f;
+      }
+    });
+    __syncthreads();
+    invert_unit_lower_b<C, NT>(Af, Tf, Xs, tid);
+    for (int e = tid; e < C * C; e += NT) {
+      const int t = e / C, i = e % C;
+      const float tv = Tf[t * LA + i];
+      Tb[t * LT + i] = to_t<E>(tv);
+      Tbb[t * LT + i] = to_t<E>(tv * bt[i]);
+      Tbe[t * LT + i] = to_t<E>(tv * be[i]);
+    }
+    __syncthreads();
+  }
+  E* Vpr = reinterpret_cast<E*>(smem + LY::F_V);
+  E* Ur = reinterpret_cast<E*>(smem + LY::P_U);
+  E* Wkr = reinterpret_cast<E*>(smem + LY::P_WK);
+  {
+    Acc<C, D, NW> ua, wa;   // U = T diag(beta) V', Wk = T diag(beta e) K  ([t][f])
+    ua.zero();
+    wa.zero();
+    gemm_acc<E, C, D, C, NW, true, false>(ua, Tbb, LT, Vpr, LR, wave, lane);
+    gemm_acc<E, C, D, C, NW, true, false>(wa, Tbe, LT, Kr, LR, wave, lane);
+    __syncthreads();
+    for_tiles(ua, wave, lane, [&](int t0, int f, const f32x4& x) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Ur[(t0 + r) * LR + f] = to_t<E>(x[r]);
+    });
+    for_tiles(wa, wave, lane, [&](int t0, int f, const f32x4& x) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Wkr[(t0 + r) * LR + f] = to_t<E>(x[r]);
+    });
+  }
+  E* Qr = reinterpret_cast<E*>(smem + LY::P_Q);
+  E* dOr = reinterpret_cast<E*>(smem + LY::P_DO);
+  E* NdQ = reinterpret_cast<E*>(smem + LY::P_NDQ);
+  E* R0b = reinterpret_cast<E*>(smem + LY::P_R0);
+  E* Xb = reinterpret_cast<E*>(smem + LY::P_XB);
+  const float* dQtc = dQt + cidx * C * D;
+  g2s_rows<E, C, D, NT>(Qr, LR, q + row0 * D, ts, nval, tid);
+  g2s_rows<E, C, D, NT>(dOr, LR, dO + row0 * D, ts, nval, tid);
+  g2s_rows_f32<E, C, D, NT>(NdQ, LR, dQtc, D, -1.f, tid);
+  __syncthreads();
+  // de_t = Q_t . dQt_t (fp32 dQt)
+  for (int e = tid; e < C * 8; e += NT) {
+    const int t = e / 8, part = e % 8;
+    float s = 0.f;
+    for (int f = part * (D / 8); f < (part + 1) * (D / 8); ++f) s += to_f(Qr[t * LR + f]) * dQtc[(long)t * D + f];
+    s += __shfl_xor(s, 1);
+    s += __shfl_xor(s, 2);
+    s += __shfl_xor(s, 4);
+    if (part == 0) de[t] = s;
+  }
+
+  // ---- R0 terms ----
+  Acc<C, C, NW> r0;   // [t][i] = Gam * Q_t . K_i, i <= t
+  r0.zero();
+  gemm_acc<E, C, C, D, NW, true, true>(r0, Qr, LR, Kr, LR, wave, lane);
+  for_tiles_mut(r0, wave, lane, [&](int t0, int i, f32x4& x) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = t0 + r;
+      x[r] = i <= t ? __expf(g[t] - g[i]) * x[r] : 0.f;
+      R0b[t * LT + i] = to_t<E>(x[r]);
+    }
+  });
+  {
+    Acc<C, C, NW> dr;   // dR0 = dO U^T - dQt Wk^T
+    dr.zero();
+    gemm_acc<E, C, C, D, NW, true, true>(dr, dOr, LR, Ur, LR, wave, lane);
+    gemm_acc<E, C, C, D, NW, true, true>(dr, NdQ, LR, Wkr, LR, wave, lane);
+    if (actC) {
+#pragma unroll
+      for (int i = 0; i < TLC::RM; ++i)
+#pragma unroll
+        for (int j = 0; j < TLC::RN; ++j) {
+          const int t0 = TLC::m0(wave) + 16 * i + 4 * (lane >> 4);
+          const int ii = TLC::n0(wave) + 16 * j + (lane & 15);
+          f32x4 pr;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = t0 + r;
+            const float d_ = ii <= t ? dr.v[i][j][r] : 0.f;
+            pr[r] = d_ * r0.v[i][j][r];
+            Xb[t * LT + ii] = to_t<E>(ii <= t ? __expf(g[t] - g[ii]) * d_ : 0.f);
+          }
+          add_rowsum(rs + wave * C, t0, pr, lane);
+          add_colsum(cs + wave * C, ii, pr, lane);
+        }
+    }
+  }
+  __syncthreads();
+  Acc<C, D, NW> dq, dk;
+  dq.zero();
+  dk.zero();
+  gemm_acc<E, C, D, C, NW, true, false>(dq, Xb, LT, Kr, LR, wave, lane);    // X0 K
+  gemm_acc<E, C, D, C, NW, false, false>(dk, Xb, LT, Qr, LR, wave, lane);   // X0^T Q
+  Acc<C, D, NW> du, dw;
+  du.zero();
+  dw.zero();
+  gemm_acc<E, C, D, C, NW, false, false>(du, R0b, LT, dOr, LR, wave, lane);   // R0^T dO
+  gemm_acc<E, C, D, C, NW, false, false>(dw, R0b, LT, NdQ, LR, wave, lane);   // -R0^T dQt
+  __syncthreads();
+  // dU = dU_s + R0^T dO, dWk = dWk_s - R0^T dQt -> rows (U, Wk slots);
+  // dq += e dQt; dk += dK_s
+  {
+    const float* dUc = dUs + cidx * C * D;
+    const float* dWc = dWks + cidx * C * D;
+    const float* dKc = dKs + cidx * C * D;
+    if (actD) {
+#pragma unroll
+      for (int i = 0; i < TLD::RM; ++i)
+#pragma unroll
+        for (int j = 0; j < TLD::RN; ++j) {
+          const int t0 = TLD::m0(wave) + 16 * i + 4 * (lane >> 4);
+          const int f = TLD::n0(wave) + 16 * j + (lane & 15);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = t0 + r;
+            const long o = (long)t * D + f;
+            Ur[t * LR + f] = to_t<E>(du.v[i][j][r] + dUc[o]);
+            Wkr[t * LR + f] = to_t<E>(dw.v[i][j][r] + dWc[o]);
+            dq.v[i][j][r] += ev[t] * dQtc[o];
+            dk.v[i][j][r] += dKc[o];
+          }
+        }
+    }
+  }
+  E* dUr = Ur;
+  E* dWkr = Wkr;
+  // V' rows again (their slot was reused by Q): from the registers
+  E* Vp2 = reinterpret_cast<E*>(smem + LY::P_Q);
+  __syncthreads();
+  for_tiles(vp, wave, lane, [&](int t0, int f, const f32x4& x) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) Vp2[(t0 + r) * LR + f] = to_t<E>(x[r]);
+  });
+  __syncthreads();
+
+  // ---- solve backward ----
+  {
+    Acc<C, D, NW> x1, x2;   // T^T dU, T^T dWk  ([i][f])
+    x1.zero();
+    x2.zero();
+    gemm_acc<E, C, D, C, NW, false, false>(x1, Tb, LT, dUr, LR, wave, lane);
+    gemm_acc<E, C, D, C, NW, false, false>(x2, Tb, LT, dWkr, LR, wave, lane);
+    float* dVc = dVp + cidx * C * D;
+    if (actD) {
+#pragma unroll
+      for (int i = 0; i < TLD::RM; ++i)
+#pragma unroll
+        for (int j = 0; j < TLD::RN; ++j) {
+          const int t0 = TLD::m0(wave) + 16 * i + 4 * (lane >> 4);
+          const int f = TLD::n0(wave) + 16 * j + (lane & 15);
+          f32x4 pb, pk;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = t0 + r;
+            dVc[(long)t * D + f] = bt[t] * x1.v[i][j][r];                 // dV'
+            pb[r] = vp.v[i][j][r] * x1.v[i][j][r];
+            pk[r] = to_f(Kr[t * LR + f]) * x2.v[i][j][r];
+            dk.v[i][j][r] += be[t] * x2.v[i][j][r];
+          }
+          add_rowsum(bs + wave * C, t0, pb, lane);
+          add_rowsum(es + wave * C, t0, pk, lane);
+        }
+    }
+  }
+  E* dTb = R0b;
+  E* P1b = Xb;
+  {
+    Acc<C, C, NW> t1, t2;   // dU V'^T, dWk K^T  ([t][i])
+    t1.zero();
+    t2.zero();
+    gemm_acc<E, C, C, D, NW, true, true>(t1, dUr, LR, Vp2, LR, wave, lane);
+    gemm_acc<E, C, C, D, NW, true, true>(t2, dWkr, LR, Kr, LR, wave, lane);
+    __syncthreads();
+    if (actC) {
+#pragma unroll
+      for (int i = 0; i < TLC::RM; ++i)
+#pragma unroll
+        for (int j = 0; j < TLC::RN; ++j) {
+          const int t0 = TLC::m0(wave) + 16 * i + 4 * (lane >> 4);
+          const int ii = TLC::n0(wave) + 16 * j + (lane & 15);
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            dTb[(t0 + r) * LT + ii] = to_t<E>(bt[ii] * t1.v[i][j][r] + be[ii] * t2.v[i][j][r]);
+        }
+    }
+  }
+  __syncthreads();
+  {
+    Acc<C, C, NW> p1;   // dT T^T  ([t][i] = sum_j dT[t][j] T[i][j])
+    p1.zero();
+    gemm_acc<E, C, C, C, NW, true, true>(p1, dTb, LT, Tb, LT, wave, lane);
+    __syncthreads();
+    for_tiles(p1, wave, lane, [&](int t0, int i, const f32x4& x) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) P1b[(t0 + r) * LT + i] = to_t<E>(x[r]);
+    });
+  }
+  __syncthreads();
+  float* Zf = reinterpret_cast<float*>(smem + LY::Z_F);
+  E* Zb = reinterpret_cast<E*>(smem + LY::Z_B);
+  {
+    Acc<C, C, NW> da, y;   // dA = -T^T P1 ([i][j]); Y = Gam * K K^T (recomputed)
+    da.zero();
+    y.zero();
+    gemm_acc<E, C, C, C, NW, false, false>(da, Tb, LT, P1b, LT, wave, lane);
+    gemm_acc<E, C, C, D, NW, true, true>(y, Kr, LR, Kr, LR, wave, lane);
+    if (actC) {
+#pragma unroll
+      for (int i = 0; i < TLC::RM; ++i)
+#pragma unroll
+        for (int j = 0; j < TLC::RN; ++j) {
+          const int t0 = TLC::m0(wave) + 16 * i + 4 * (lane >> 4);
+          const int jj = TLC::n0(wave) + 16 * j + (lane & 15);
+          f32x4 pb, py;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int t = t0 + r;
+            const bool m = jj < t;
+            const float gam = m ? __expf(g[t] - g[jj]) : 0.f;
+            const float yv = gam * y.v[i][j][r];
+            const float dav = m ? -da.v[i][j][r] : 0.f;
+            pb[r] = dav * yv;                       // dbeta_t += dA . Y
+            const float dy = bt[t] * dav;
+            py[r] = dy * yv;                        // dg via Gam
+            Zf[t * LA + jj] = gam * dy;             // dG0
+          }
+          add_rowsum(bs + wave * C, t0, pb, lane);
+          add_rowsum(rs + wave * C, t0, py, lane);
+          add_colsum(cs + wave * C, jj, py, lane);
+        }
+    }
+  }
+  __syncthreads();
+  for (int e = tid; e < C * C; e += NT) {
+    const int t = e / C, i = e % C;
+    Zb[t * LT + i] = to_t<E>(Zf[t * LA + i] + Zf[i * LA + t]);
+  }
+  __syncthreads();
+  gemm_acc<E, C, D, C, NW, true, false>(dk, Zb, LT, Kr, LR, wave, lane);   // (dG0 + dG0^T) K
+
+  // ---- outputs ----
+  float* dqc = dqp + cidx * C * D;
+  float* dkc = dkp + cidx * C * D;
+  for_tiles(dq, wave, lane, [&](int t0, int f, const f32x4& x) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dqc[(long)(t0 + r) * D + f] = x[r];
+  });
+  for_tiles(dk, wave, lane, [&](int t0, int f, const f32x4& x) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) dkc[(long)(t0 + r) * D + f] = x[r];
+  });
+  __syncthreads();
+  if (tid < C) {
+    const int t = tid;
+    float sr = 0.f, sb = 0.f, se = 0.f;
+    for (int w = 0; w < NW; ++w) {
+      sr += rs[w * C + t] - cs[w * C + t];
+      sb += bs[w * C + t];
+      se += es[w * C + t];
+    }
+    // de: from Qt (Q . dQt) and from Wk (beta K . X2); e_t = exp(g_t)
+    const float det = de[t] + bt[t] * se;
+    dgp[cidx * C + t] = dgs[cidx * C + t] + sr + ev[t] * det;
+    if (t < nval) dbeta[row0 + (long)t * H] = sb + ev[t] * se;
+  }
+}
+
+// ===========================================================================
+// chunk_bwd_pairs
+// ===========================================================================
+template <typename E, int D, int C>
+struct CB3Lds {
+  static constexpr int LR = ldpad<E>(D);
+  static constexpr int LT = ldpad<E>(C);
+  static constexpr int SZ_R = C * LR * (int)sizeof(E);
+  static constexpr int SZ_CC = C * LT * (int)sizeof(E);
+  static constexpr int SZ_VEC = (2 * C + 2 * CB_NW * C) * 4;   // g, alpha, rs, cs
+  static constexpr int O_Q = (SZ_VEC + 15) / 16 * 16;
+  static constexpr int O_K = O_Q + SZ_R;
+  static constexpr int O_DO = O_K + SZ_R;
+  static constexpr int O_DV = O_DO + SZ_R;
+  static constexpr int O_KL = O_DV + SZ_R;
+  static constexpr int O_WL = O_KL + SZ_R;
+  static constexpr int O_RB = O_WL + SZ_R;
+  static constexpr int O_XB = O_RB + SZ_CC;
+  static constexpr int O_FB = O_XB + SZ_CC;
+  static constexpr int O_GB = O_FB + SZ_CC;
+  static constexpr int TOTAL = O_GB + SZ_CC;
+};
+
+template <typename E, int D, int C>
+__global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ dO,
+    const float* __restrict__ alpha, const E* __restrict__ Kl, const E* __restrict__ Wl,
+    const float* __restrict__ dVp, const float* __restrict__ dqp, const float* __restrict__ dkp,
+    const float* __restrict__ dgp, float* __restrict__ dKl, float* __restrict__ dWl,
+    E* __restrict__ dq, E* __restrict__ dk, float* __restrict__ dvdir, E* __restrict__ dv,
+    float* __restrict__ dalpha, int B, int T, int H, int L, int NC, int Tp) {
+  typedef CB3Lds<E, D, C> LY;
+  constexpr int NW = CB_NW, NT = CB_NT;
+  constexpr int LR = LY::LR, LT = LY::LT;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[LY::TOTAL];
+  float* g = reinterpret_cast<float*>(smem);
+  float* al = g + C;
+  float* rs = g + 2 * C;
+  float* cs = rs + NW * C;
+  E* Qr = reinterpret_cast<E*>(smem + LY::O_Q);
+  E* Kr = reinterpret_cast<E*>(smem + LY::O_K);
+  E* dOr = reinterpret_cast<E*>(smem + LY::O_DO);
+  E* dVr = reinterpret_cast<E*>(smem + LY::O_DV);
+  E* Klr = reinterpret_cast<E*>(smem + LY::O_KL);
+  E* Wlr = reinterpret_cast<E*>(smem + LY::O_WL);
+  E* Rb = reinterpret_cast<E*>(smem + LY::O_RB);
+  E* Xb = reinterpret_cast<E*>(smem + LY::O_XB);
+  E* NFb = reinterpret_cast<E*>(smem + LY::O_FB);
+  E* Gb = reinterpret_cast<E*>(smem + LY::O_GB);
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nblk = B * H * NC;
+  const int bid = xcd_swizzle(blockIdx.x, nblk);
+  const int c = bid % NC, bh = bid / NC;
+  const int h = bh % H, b = bh / H;
+  const int tb = c * C;
+  const int nval = min(C, T - tb);
+  const long ts = (long)H * D;
+  const long row0 = ((long)b * T + tb) * H + h;
+  const long cidx = (long)bh * NC + c;
+  typedef Tiling<C, C, NW> TLC;
+  const bool actC = TLC::active(wave);
+
+  for (int e = tid; e < 2 * NW * C; e += NT) rs[e] = 0.f;
+  if (wave == 0) {
+    __shared__ float dummy[3 * C];
+    chunk_decays<C>(alpha, nullptr, row0, H, nval, g, dummy, dummy + C, nullptr, nullptr, al, lane);
+  }
+  g2s_rows<E, C, D, NT>(Qr, LR, q + row0 * D, ts, nval, tid);
+  g2s_rows<E, C, D, NT>(Kr, LR, k + row0 * D, ts, nval, tid);
+  g2s_rows<E, C, D, NT>(dOr, LR, dO + row0 * D, ts, nval, tid);
+  g2s_rows_f32<E, C, D, NT>(dVr, LR, dVp + cidx * C * D, D, 1.f, tid);
+  __syncthreads();
+
+  Acc<C, D, NW> dqa, dka;
+  dqa.zero();
+  dka.zero();
+  for (int l = 0; l < L; ++l) {
+    const long lrow = ((long)bh * L + l) * Tp + tb;
+    g2s_rows<E, C, D, NT>(Klr, LR, Kl + lrow * D, D, C, tid);
+    g2s_rows<E, C, D, NT>(Wlr, LR, Wl + lrow * D, D, C, tid);
+    __syncthreads();
+    // R_l = (Gam * Q K_l^T)_{i<=t}, dR_l = dO W_l^T  -> Rb, Xb = Gam * dR_l
+    {
+      Acc<C, C, NW> r, dr;
+      r.zero();
+      dr.zero();
+      gemm_acc<E, C, C, D, NW, true, true>(r, Qr, LR, Klr, LR, wave, lane);
+      gemm_acc<E, C, C, D, NW, true, true>(dr, dOr, LR, Wlr, LR, wave, lane);
+      if (actC) {
+#pragma unroll
+        for (int i = 0; i < TLC::RM; ++i)
+#pragma unroll
+          for (int j = 0; j < TLC::RN; ++j) {
+            const int t0 = TLC::m0(wave) + 16 * i + 4 * (lane >> 4);
+            const int ii = TLC::n0(wave) + 16 * j + (lane & 15);
+            f32x4 p;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const int t = t0 + rr;
+              const float gam = ii <= t ? __expf(g[t] - g[ii]) : 0.f;
+              const float rv = gam * r.v[i][j][rr];
+              const float drv = ii <= t ? dr.v[i][j][rr] : 0.f;
+              p[rr] = drv * rv;
+              Rb[t * LT + ii] = to_t<E>(rv);
+              Xb[t * LT + ii] = to_t<E>(gam * drv);
+            }
+            add_rowsum(rs + wave * C, t0, p, lane);
+            add_colsum(cs + wave * C, ii, p, lane);
+          }
+      }
+    }
+    // F_l = (Gam * K K_l^T)_{i<t}, dF_l = -(dV' W_l^T)_{i<t}  -> NFb = -F_l, Gb = Gam * dF_l
+    {
+      Acc<C, C, NW> f, df;
+      f.zero();
+      df.zero();
+      gemm_acc<E, C, C, D, NW, true, true>(f, Kr, LR, Klr, LR, wave, lane);
+      gemm_acc<E, C, C, D, NW, true, true>(df, dVr, LR, Wlr, LR, wave, lane);
+      if (actC) {
+#pragma unroll
+        for (int i = 0; i < TLC::RM; ++i)
+#pragma unroll
+          for (int j = 0; j < TLC::RN; ++j) {
+            const int t0 = TLC::m0(wave) + 16 * i + 4 * (lane >> 4);
+            const int ii = TLC::n0(wave) + 16 * j + (lane & 15);
+            f32x4 p;
+#pragma unroll
+            for (int rr = 0; rr < 4; ++rr) {
+              const int t = t0 + rr;
+              const float gam = ii < t ? __expf(g[t] - g[ii]) : 0.f;
+              const float fv = gam * f.v[i][j][rr];
+              const float dfv = ii < t ? -df.v[i][j][rr] : 0.f;
+              p[rr] = dfv * fv;
+              NFb[t * LT + ii] = to_t<E>(-fv);
+              Gb[t * LT + ii] = to_t<E>(gam * dfv);
+            }
+            add_rowsum(rs + wave * C, t0, p, lane);
+            add_colsum(cs + wave * C, ii, p, lane);
+          }
+      }
+    }
+    __syncthreads();
+    Acc<C, D, NW> dkl, dwl;
+    dkl.zero();
+    dwl.zero();
+    // (scheduling barriers keep the six independent products from being
+    //  interleaved, which would multiply the live fragment registers)
+    gemm_acc<E, C, D, C, NW, false, false>(dkl, Xb, LT, Qr, LR, wave, lane);    // X_l^T Q
+    __builtin_amdgcn_sched_barrier(0);
+    gemm_acc<E, C, D, C, NW, false, false>(dkl, Gb, LT, Kr, LR, wave, lane);    // dG_l^T K
+    __builtin_amdgcn_sched_barrier(0);
+    gemm_acc<E, C, D, C, NW, false, false>(dwl, Rb, LT, dOr, LR, wave, lane);   // R_l^T dO
+    __builtin_amdgcn_sched_barrier(0);
+    gemm_acc<E, C, D, C, NW, false, false>(dwl, NFb, LT, dVr, LR, wave, lane);  // -F_l^T dV'
+    __builtin_amdgcn_sched_barrier(0);
+    gemm_acc<E, C, D, C, NW, true, false>(dqa, Xb, LT, Klr, LR, wave, lane);    // X_l K_l
+    __builtin_amdgcn_sched_barrier(0);
+    gemm_acc<E, C, D, C, NW, true, false>(dka, Gb, LT, Klr, LR, wave, lane);    // dG_l K_l
+    __builtin_amdgcn_sched_barrier(0);
+    float* okl = dKl + lrow * D;
+    float* owl = dWl + lrow * D;
+    for_tiles(dkl, wave, lane, [&](int t0, int f, const f32x4& x) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) okl[(long)(t0 + r) * D + f] += x[r];
+    });
+    for_tiles(dwl, wave, lane, [&](int t0, int f, const f32x4& x) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) owl[(long)(t0 + r) * D + f] += x[r];
+    });
+    __syncthreads();
+  }
+
+  // ---- final dq, dk, dv ----
+  const float* dqc = dqp + cidx * C * D;
+  const float* dkc = dkp + cidx * C * D;
+  const float* dvc = dVp + cidx * C * D;
+  E* dqo = dq + row0 * D;
+  E* dko = dk + row0 * D;
+  for_tiles(dqa, wave, lane, [&](int t0, int f, const f32x4& x) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = t0 + r;
+      if (t < nval) dqo[(long)t * ts + f] = to_t<E>(x[r] + dqc[(long)t * D + f]);
+    }
+  });
+  for_tiles(dka, wave, lane, [&](int t0, int f, const f32x4& x) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = t0 + r;
+      if (t < nval) dko[(long)t * ts + f] = to_t<E>(x[r] + dkc[(long)t * D + f]);
+    }
+  });
+  if (L > 0) {
+    // direct v-gradient, completed by the refinement backward
+    float* o = dvdir + ((long)bh * Tp + tb) * D;
+    for (int e = tid; e < C * D / 4; e += NT) {
+      const int t = e / (D / 4), f = (e % (D / 4)) * 4;
+      *reinterpret_cast<f32x4*>(o + (long)t * D + f) = *reinterpret_cast<const f32x4*>(dvc + (long)t * D + f);
+    }
+  } else {
+    E* dvo = dv + row0 * D;
+    for (int e = tid; e < C * D; e += NT) {
+      const int t = e / D, f = e % D;
+      if (t < nval) dvo[(long)t * ts + f] = to_t<E>(dvc[(long)t * D + f]);
+    }
+  }
+  __syncthreads();
+  // ---- dalpha: dlog(alpha)_j = sum_{t >= j} dg_t ----
+  if (wave == 0) {
+    float dg = 0.f;
+    if (lane < C) {
+      dg = dgp[cidx * C + lane];
+      for (int w = 0; w < NW; ++w) dg += rs[w * C + lane] - cs[w * C + lane];
+    }
+    // reverse inclusive scan over lanes 0..C-1
+    float s = dg;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_down(s, off);
+      if (lane + off < 64) s += y;
+    }
+    if (lane < nval) dalpha[row0 + (long)lane * H] = s / al[lane];
+  }
+}
+
+// T = (I + A)^{-1}; same algorithm as in chunk_fwd.hip (16 x 16 diagonal
+// blocks by substitution, then block rows).  Ends with a barrier.
+template <int C, int NT>
+__device__ void invert_unit_lower_b(const float* A, float* Tm, float* Xs, int tid) {
+  constexpr int NB = C / 16, LA = C + 1;
+  for (int e = tid; e < C * C; e += NT) {
+    const int r = e / C, cc = e % C;
+    if (cc > r) Tm[r * LA + cc] = 0.f;
+  }
+  if (tid < NB * 16) {
+    const int base = 16 * (tid / 16), col = tid % 16;
+    float* Tc = Tm + base * LA + base + col;
+    const float* Ab = A + base * LA + base;
+#pragma unroll 1
+    for (int r = col; r < 16; ++r) {
+      float s = (r == col) ? 1.f : 0.f;
+#pragma unroll 1
+      for (int m = col; m < r; ++m) s -= Ab[r * LA + m] * Tc[m * LA];
+      Tc[r * LA] = s;
+    }
+  }
+  __syncthreads();
+  for (int i = 1; i < NB; ++i) {
+    for (int e = tid; e < i * 256; e += NT) {
+      const int j = e / 256, r = (e / 16) % 16, cc = e % 16;
+      float s = 0.f;
+      for (int m = 16 * j; m < 16 * i; ++m) s += A[(16 * i + r) * LA + m] * Tm[m * LA + 16 * j + cc];
+      Xs[e] = s;
+    }
+    __syncthreads();
+    for (int e = tid; e < i * 256; e += NT) {
+      const int j = e / 256, r = (e / 16) % 16, cc = e % 16;
+      float s = 0.f;
+      for (int m = 0; m <= r; ++m) s += Tm[(16 * i + r) * LA + 16 * i + m] * Xs[j * 256 + m * 16 + cc];
+      Tm[(16 * i + r) * LA + 16 * j + cc] = -s;
+    }
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+template <typename E, int D, int C>
+static hipError_t cbwd_launch_dc(const Dims& d, const ChunkBwdArgs<E>& a, hipStream_t s) {
+  if constexpr (sizeof(E) == 4 && D * C > 2048) {
+    return hipErrorInvalidValue;   // outside the fp32 envelope (LDS)
+  } else {
+  const int nblk = d.B * d.H * d.NC;
+  hipLaunchKernelGGL((chunk_bwd_state_kernel<E, D, C>), dim3(nblk), dim3(CB_NT), 0, s, a.k, a.dO,
+                     a.alpha, a.Kl, a.Wl, a.UT, a.WkT, a.St, a.dSnT, a.dQt, a.dUs, a.dWks, a.dKs,
+                     a.dKl, a.dWl, a.dgs, d.B, d.T, d.H, d.L, d.NC, d.Tp);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((chunk_bwd_solve_kernel<E, D, C>), dim3(nblk), dim3(CB_NT), 0, s, a.q, a.k,
+                     a.v, a.dO, a.alpha, a.beta, a.Kl, a.Wl, a.dQt, a.dUs, a.dWks, a.dKs, a.dgs,
+                     a.dVp, a.dqp, a.dkp, a.dgp, a.dbeta, d.B, d.T, d.H, d.L, d.NC, d.Tp);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((chunk_bwd_pairs_kernel<E, D, C>), dim3(nblk), dim3(CB_NT), 0, s, a.q, a.k,
+                     a.dO, a.alpha, a.Kl, a.Wl, a.dVp, a.dqp, a.dkp, a.dgp, a.dKl, a.dWl, a.dq,
+                     a.dk, a.dvdir, a.dv, a.dalpha, d.B, d.T, d.H, d.L, d.NC, d.Tp);
+  return hipGetLastError();
+  }
+}
+
+template <typename E, int D>
+static hipError_t cbwd_launch_d(const Dims& d, const ChunkBwdArgs<E>& a, hipStream_t s) {
+  switch (d.C) {
+    case 16: return cbwd_launch_dc<E, D, 16>(d, a, s);
+    case 32: return cbwd_launch_dc<E, D, 32>(d, a, s);
+    case 64: return cbwd_launch_dc<E, D, 64>(d, a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename E>
+hipError_t launch_chunk_bwd(const Dims& d, const ChunkBwdArgs<E>& a, hipStream_t s) {
+  switch (d.D) {
+    case 16: return cbwd_launch_d<E, 16>(d, a, s);
+    case 32: return cbwd_launch_d<E, 32>(d, a, s);
+    case 64: return cbwd_launch_d<E, 64>(d, a, s);
+    case 128:
+      if constexpr (sizeof(E) == 2) return cbwd_launch_d<E, 128>(d, a, s);
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+
+template hipError_t launch_chunk_bwd<bf16>(const Dims&, const ChunkBwdArgs<bf16>&, hipStream_t);
+template hipError_t launch_chunk_bwd<float>(const Dims&, const ChunkBwdArgs<float>&, hipStream_t);
+
+}  // namespace prism

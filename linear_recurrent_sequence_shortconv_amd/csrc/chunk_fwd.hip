@@ -20,8 +20,9 @@
 // and the accumulators stay fp32.  Stored (global, per chunk):
 //   Mt [D][D] = M^T (MFMA B operand of the state pass), HT [D][D] = H^T fp32,
 //   Qt [C][D], O_loc [C][D] fp32, gC.
-// In backward mode (dO given) the kernel instead stores Mt, HT, gC, M [D][D]
-// and ET = (dO^T Qt)^T fp32, which the reverse state pass needs.
+// In backward mode (dO given) the kernel instead stores Mt, HT, gC, M [D][D],
+// ET = (dO^T Qt)^T fp32 (for the reverse state pass) and U^T, Wk^T [D][C]
+// (for the reverse chunk kernels).
 #include "prism_common.h"
 #include "prism_internal.h"
 
@@ -74,8 +75,6 @@ __device__ void invert_unit_lower(const float* A, float* Tm, float* Xs, int tid)
   }
 }
 
-constexpr int cmax(int a, int b) { return a > b ? a : b; }
-
 template <typename E, int D, int C>
 struct ChunkLds {
   static constexpr int LR = ldpad<E>(D);     // [C][LR]: C rows of D
@@ -120,7 +119,8 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
     const float* __restrict__ alpha, const float* __restrict__ beta, const E* __restrict__ Kl,
     const E* __restrict__ Wl, const E* __restrict__ dO, E* __restrict__ Mt, float* __restrict__ HT,
     E* __restrict__ Qt, float* __restrict__ Oloc, float* __restrict__ gCo, E* __restrict__ Mo,
-    float* __restrict__ ET, int B, int T, int H, int L, int NC, int Tp) {
+    float* __restrict__ ET, E* __restrict__ UTo, E* __restrict__ WkTo, int B, int T, int H, int L,
+    int NC, int Tp) {
   typedef ChunkLds<E, D, C> LY;
   constexpr int NW = CF_NW, NT = CF_NT;
   constexpr int LR = LY::LR, LT = LY::LT, LA = LY::LA;
@@ -293,6 +293,10 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
   E* Ut = Vt;
   E* Wkt = Ktbe;
   const long cidx = (long)bh * NC + c;
+  if constexpr (BWD) {   // U^T, Wk^T [D][C] for the reverse chunk kernels
+    s2g_rows<E, D, C, NT>(UTo + cidx * D * C, C, Ut, LT, D, tid);
+    s2g_rows<E, D, C, NT>(WkTo + cidx * D * C, C, Wkt, LT, D, tid);
+  }
 
   // H += U^T diag(D) K;  stored transposed (HT[n][r])
   gemm_acc<E, D, D, C, NW, true, true>(hacc, Ut, LT, KtD, LT, wave, lane);
@@ -379,16 +383,17 @@ template <typename E, int D, int C>
 static hipError_t chunk_launch_dc(const Dims& d, const E* q, const E* k, const E* v,
                                   const float* alpha, const float* beta, const E* Kl, const E* Wl,
                                   const E* dO, E* Mt, float* HT, E* Qt, float* Oloc, float* gC,
-                                  E* M, float* ET, hipStream_t s) {
+                                  E* M, float* ET, E* UT, E* WkT, hipStream_t s) {
+  if constexpr (sizeof(E) == 4 && D * C > 2048) return hipErrorInvalidValue;   // fp32 envelope
   const int nblk = d.B * d.H * d.NC;
   if (dO)
     hipLaunchKernelGGL((chunk_fwd_kernel<E, D, C, true>), dim3(nblk), dim3(CF_NT), 0, s, q, k, v,
-                       alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, M, ET, d.B, d.T, d.H, d.L,
-                       d.NC, d.Tp);
+                       alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, M, ET, UT, WkT, d.B, d.T, d.H,
+                       d.L, d.NC, d.Tp);
   else
     hipLaunchKernelGGL((chunk_fwd_kernel<E, D, C, false>), dim3(nblk), dim3(CF_NT), 0, s, q, k, v,
-                       alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, M, ET, d.B, d.T, d.H, d.L,
-                       d.NC, d.Tp);
+                       alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, M, ET, UT, WkT, d.B, d.T, d.H,
+                       d.L, d.NC, d.Tp);
   return hipGetLastError();
 }
 
@@ -396,11 +401,11 @@ template <typename E, int D>
 static hipError_t chunk_launch_d(const Dims& d, const E* q, const E* k, const E* v,
                                  const float* alpha, const float* beta, const E* Kl, const E* Wl,
                                  const E* dO, E* Mt, float* HT, E* Qt, float* Oloc, float* gC, E* M,
-                                 float* ET, hipStream_t s) {
+                                 float* ET, E* UT, E* WkT, hipStream_t s) {
   switch (d.C) {
-    case 16: return chunk_launch_dc<E, D, 16>(d, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, M, ET, s);
-    case 32: return chunk_launch_dc<E, D, 32>(d, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, M, ET, s);
-    case 64: return chunk_launch_dc<E, D, 64>(d, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, M, ET, s);
+    case 16: return chunk_launch_dc<E, D, 16>(d, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, M, ET, UT, WkT, s);
+    case 32: return chunk_launch_dc<E, D, 32>(d, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, M, ET, UT, WkT, s);
+    case 64: return chunk_launch_dc<E, D, 64>(d, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, M, ET, UT, WkT, s);
   }
   return hipErrorInvalidValue;
 }
@@ -408,15 +413,15 @@ static hipError_t chunk_launch_d(const Dims& d, const E* q, const E* k, const E*
 template <typename E>
 hipError_t launch_chunk_fwd(const Dims& d, const E* q, const E* k, const E* v, const float* alpha,
                             const float* beta, const E* Kl, const E* Wl, const E* dO, E* Mt,
-                            float* HT, E* Qt, float* Oloc, float* gC, E* M, float* ET,
-                            hipStream_t s) {
+                            float* HT, E* Qt, float* Oloc, float* gC, E* M, float* ET, E* UT,
+                            E* WkT, hipStream_t s) {
   switch (d.D) {
-    case 16: return chunk_launch_d<E, 16>(d, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, M, ET, s);
-    case 32: return chunk_launch_d<E, 32>(d, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, M, ET, s);
-    case 64: return chunk_launch_d<E, 64>(d, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, M, ET, s);
+    case 16: return chunk_launch_d<E, 16>(d, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, M, ET, UT, WkT, s);
+    case 32: return chunk_launch_d<E, 32>(d, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, M, ET, UT, WkT, s);
+    case 64: return chunk_launch_d<E, 64>(d, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, M, ET, UT, WkT, s);
     case 128:
       if constexpr (sizeof(E) == 2)
-        return chunk_launch_d<E, 128>(d, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, M, ET, s);
+        return chunk_launch_d<E, 128>(d, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, M, ET, UT, WkT, s);
       break;
   }
   return hipErrorInvalidValue;
@@ -425,10 +430,10 @@ hipError_t launch_chunk_fwd(const Dims& d, const E* q, const E* k, const E* v, c
 template hipError_t launch_chunk_fwd<bf16>(const Dims&, const bf16*, const bf16*, const bf16*,
                                            const float*, const float*, const bf16*, const bf16*,
                                            const bf16*, bf16*, float*, bf16*, float*, float*, bf16*,
-                                           float*, hipStream_t);
+                                           float*, bf16*, bf16*, hipStream_t);
 template hipError_t launch_chunk_fwd<float>(const Dims&, const float*, const float*, const float*,
                                             const float*, const float*, const float*, const float*,
                                             const float*, float*, float*, float*, float*, float*,
-                                            float*, float*, hipStream_t);
+                                            float*, float*, float*, float*, hipStream_t);
 
 }  // namespace prism

@@ -109,6 +109,8 @@ prism_status check_desc(const prism_desc* desc, prism::Dims* out) {
     return fail(PRISM_ERR_UNSUPPORTED, "head dimension " + std::to_string(d.dk) +
                                            " not supported (bf16: 16/32/64/128, f32: 16/32/64)");
   if (d.L > 8) return fail(PRISM_ERR_UNSUPPORTED, "L must be <= 8");
+  if (d.dtype == PRISM_F32 && d.dk * d.chunk > 2048)
+    return fail(PRISM_ERR_UNSUPPORTED, "PRISM_F32 needs dk * chunk <= 2048 (d=64: chunk <= 32)");
   if (d.chunk != 16 && d.chunk != 32 && d.chunk != 64)
     return fail(PRISM_ERR_UNSUPPORTED, "chunk must be 16, 32 or 64");
   if (d.conv_width != 4) return fail(PRISM_ERR_UNSUPPORTED, "conv_width must be 4");
@@ -149,6 +151,64 @@ prism_status check_ptr(const void* p, const char* name, bool required) {
       return fail(PRISM_ERR_HIP, std::string(name) + ": " + hipGetErrorString(e_));   \
   } while (0)
 
+template <typename E>
+struct BwdWs {
+  E *Kl, *Wl, *Mt, *M, *UT, *WkT, *Sct, *dSnT, *u, *dP, *WkW, *WpW;
+  float *HT, *gC, *ET, *dQt, *dUs, *dWks, *dKs, *dVp, *dqp, *dkp, *dKl, *dWl, *dgs, *dgp;
+  float *dvdir, *du, *dwbp, *dcp, *part;
+};
+
+template <typename E>
+BwdWs<E> carve_bwd(const prism::Dims& d, Carve& cv) {
+  const size_t bh = (size_t)d.B * d.H;
+  const size_t es = sizeof(E);
+  const size_t DD = (size_t)d.D * d.D, CD = (size_t)d.C * d.D;
+  const size_t ntiles = (d.Tp + 63) / 64;
+  const size_t L1 = d.L > 0 ? d.L : 1;
+  BwdWs<E> w;
+  w.Kl = cv.take<E>(bh * d.L * d.Tp * d.D * es);
+  w.Wl = cv.take<E>(bh * d.L * d.Tp * d.D * es);
+  w.Mt = cv.take<E>(bh * d.NC * DD * es);
+  w.M = cv.take<E>(bh * d.NC * DD * es);
+  w.HT = cv.take<float>(bh * d.NC * DD * 4);
+  w.ET = cv.take<float>(bh * d.NC * DD * 4);
+  w.gC = cv.take<float>(bh * d.NC * 4);
+  w.UT = cv.take<E>(bh * d.NC * CD * es);
+  w.WkT = cv.take<E>(bh * d.NC * CD * es);
+  w.Sct = cv.take<E>(bh * d.NC * DD * es);
+  w.dSnT = cv.take<E>(bh * d.NC * DD * es);
+  w.dQt = cv.take<float>(bh * d.NC * CD * 4);
+  w.dUs = cv.take<float>(bh * d.NC * CD * 4);
+  w.dWks = cv.take<float>(bh * d.NC * CD * 4);
+  w.dKs = cv.take<float>(bh * d.NC * CD * 4);
+  w.dVp = cv.take<float>(bh * d.NC * CD * 4);
+  w.dqp = cv.take<float>(bh * d.NC * CD * 4);
+  w.dkp = cv.take<float>(bh * d.NC * CD * 4);
+  w.dKl = cv.take<float>(bh * d.L * d.Tp * d.D * 4);
+  w.dWl = cv.take<float>(bh * d.L * d.Tp * d.D * 4);
+  w.dgs = cv.take<float>(bh * d.NC * d.C * 4);
+  w.dgp = cv.take<float>(bh * d.NC * d.C * 4);
+  w.dvdir = cv.take<float>(bh * d.Tp * d.D * 4);
+  w.u = cv.take<E>(bh * d.Tp * d.D * es);
+  w.du = cv.take<float>(bh * d.Tp * d.D * 4);
+  w.dP = cv.take<E>(bh * d.L * d.Tp * d.D * es);
+  w.dwbp = cv.take<float>(bh * ntiles * L1 * d.D * 4);
+  w.dcp = cv.take<float>(bh * ntiles * d.D * 4 * 4);
+  w.part = cv.take<float>((size_t)d.H * L1 * 2 * prism::refine_bwd_splits(d) * DD * 4);
+  w.WkW = cv.take<E>((size_t)d.H * d.L * DD * es);
+  w.WpW = cv.take<E>((size_t)d.H * d.L * DD * es);
+  return w;
+}
+
+size_t bwd_ws_bytes(const prism::Dims& d, prism_dtype dt) {
+  Carve cv;
+  if (dt == PRISM_BF16)
+    carve_bwd<prism::bf16>(d, cv);
+  else
+    carve_bwd<float>(d, cv);
+  return cv.off;
+}
+
 size_t fwd_ws_bytes(const prism::Dims& d, prism_dtype dt) {
   Carve cv;
   if (dt == PRISM_BF16)
@@ -176,10 +236,57 @@ prism_status run_forward(const prism::Dims& d, const void* q, const void* k, con
                                         w.Kl, w.Wl, s));
   HIP_TRY("chunk_fwd", s,
           prism::launch_chunk_fwd<E>(d, q_, k_, v_, alpha, beta, w.Kl, w.Wl, nullptr, w.Mt, w.HT,
-                                     w.Qt, w.Oloc, w.gC, nullptr, nullptr, s));
+                                     w.Qt, w.Oloc, w.gC, nullptr, nullptr, nullptr, nullptr, s));
   HIP_TRY("state_fwd", s,
-          prism::launch_state_fwd<E>(d, S0, w.Mt, w.HT, w.gC, w.Sc, ST ? ST : w.ST, false, s));
+          prism::launch_state_pass<E>(d, S0, w.Mt, w.HT, w.gC, w.Sc, ST, false, false, s));
   HIP_TRY("out_fwd", s, prism::launch_out_fwd<E>(d, w.Sc, w.Qt, w.Oloc, static_cast<E*>(o), s));
+  return PRISM_OK;
+}
+
+template <typename E>
+prism_status run_backward(const prism::Dims& d, const void* q, const void* k, const void* v,
+                          const float* alpha, const float* beta, const void* Wk, const void* Wp,
+                          const void* wbeta, const void* conv, const float* S0, const void* dO,
+                          const float* dST, void* dq, void* dk, void* dv, float* dalpha,
+                          float* dbeta, float* dWk, float* dWp, float* dwbeta, float* dconv,
+                          float* dS0, void* ws, hipStream_t s) {
+  Carve cv;
+  cv.base = static_cast<char*>(ws);
+  BwdWs<E> w = carve_bwd<E>(d, cv);
+  const E* q_ = static_cast<const E*>(q);
+  const E* k_ = static_cast<const E*>(k);
+  const E* v_ = static_cast<const E*>(v);
+  const E* dO_ = static_cast<const E*>(dO);
+  if (d.L > 0)
+    HIP_TRY("refine_fwd", s,
+            prism::launch_refine_fwd<E>(d, v_, static_cast<const E*>(conv), static_cast<const E*>(Wk),
+                                        static_cast<const E*>(Wp), static_cast<const E*>(wbeta),
+                                        w.Kl, w.Wl, s));
+  HIP_TRY("chunk_fwd_bwdmode", s,
+          prism::launch_chunk_fwd<E>(d, q_, k_, v_, alpha, beta, w.Kl, w.Wl, dO_, w.Mt, w.HT,
+                                     nullptr, nullptr, w.gC, w.M, w.ET, w.UT, w.WkT, s));
+  HIP_TRY("state_fwd", s,
+          prism::launch_state_pass<E>(d, S0, w.Mt, w.HT, w.gC, w.Sct, nullptr, true, false, s));
+  HIP_TRY("state_bwd", s,
+          prism::launch_state_pass<E>(d, dST, w.M, w.ET, w.gC, w.dSnT, dS0, true, true, s));
+  prism::ChunkBwdArgs<E> a;
+  a.q = q_; a.k = k_; a.v = v_; a.dO = dO_; a.alpha = alpha; a.beta = beta;
+  a.Kl = w.Kl; a.Wl = w.Wl; a.UT = w.UT; a.WkT = w.WkT; a.St = w.Sct; a.dSnT = w.dSnT;
+  a.dQt = w.dQt; a.dUs = w.dUs; a.dWks = w.dWks; a.dKs = w.dKs; a.dKl = w.dKl; a.dWl = w.dWl;
+  a.dgs = w.dgs; a.dVp = w.dVp; a.dqp = w.dqp; a.dkp = w.dkp; a.dgp = w.dgp; a.dbeta = dbeta;
+  a.dq = static_cast<E*>(dq); a.dk = static_cast<E*>(dk); a.dvdir = w.dvdir;
+  a.dv = static_cast<E*>(dv); a.dalpha = dalpha;
+  HIP_TRY("chunk_bwd", s, prism::launch_chunk_bwd<E>(d, a, s));
+  if (d.L > 0) {
+    prism::RefineBwdArgs<E> r;
+    r.v = v_; r.conv = static_cast<const E*>(conv); r.Wk = static_cast<const E*>(Wk);
+    r.Wp = static_cast<const E*>(Wp); r.wbeta = static_cast<const E*>(wbeta);
+    r.WkT = w.WkW; r.WpT = w.WpW; r.dKl = w.dKl; r.dWl = w.dWl; r.dvdir = w.dvdir; r.u = w.u;
+    r.du = w.du; r.dP = w.dP; r.dwbp = w.dwbp; r.dcp = w.dcp; r.part = w.part;
+    r.dv = static_cast<E*>(dv); r.dWk_o = dWk; r.dWp_o = dWp; r.dwbeta_o = dwbeta;
+    r.dconv_o = dconv;
+    HIP_TRY("refine_bwd", s, prism::launch_refine_bwd<E>(d, r, s));
+  }
   return PRISM_OK;
 }
 
@@ -218,7 +325,8 @@ prism_status prism_backward_workspace(const prism_desc* desc, size_t* bytes) {
   prism::Dims d;
   prism_status st = check_desc(desc, &d);
   if (st != PRISM_OK) return st;
-  return fail(PRISM_ERR_UNSUPPORTED, "backward pass not available in this build");
+  *bytes = bwd_ws_bytes(d, desc->dtype);
+  return PRISM_OK;
 }
 
 prism_status prism_forward(const prism_desc* desc, const void* q, const void* k, const void* v,
@@ -268,15 +376,50 @@ prism_status prism_backward(const prism_desc* desc, const void* q, const void* k
                             float* dbeta, float* dWk, float* dWp, float* dwbeta, float* dconv,
                             float* dS0, void* workspace, size_t workspace_bytes,
                             hipStream_t stream) {
-  (void)q; (void)k; (void)v; (void)alpha; (void)beta; (void)Wk; (void)Wp; (void)wbeta;
-  (void)conv; (void)S0; (void)dO; (void)dST; (void)dq; (void)dk; (void)dv; (void)dalpha;
-  (void)dbeta; (void)dWk; (void)dWp; (void)dwbeta; (void)dconv; (void)dS0; (void)workspace;
-  (void)workspace_bytes; (void)stream;
-  g_err.clear();
-  prism::Dims d;
-  prism_status st = check_desc(desc, &d);
-  if (st != PRISM_OK) return st;
-  return fail(PRISM_ERR_UNSUPPORTED, "backward pass not available in this build");
+  try {
+    g_err.clear();
+    prism::Dims d;
+    prism_status st = check_desc(desc, &d);
+    if (st != PRISM_OK) return st;
+    const bool refine = d.L > 0;
+    CHECK_PTR(q, true);
+    CHECK_PTR(k, true);
+    CHECK_PTR(v, true);
+    CHECK_PTR(alpha, true);
+    CHECK_PTR(beta, true);
+    CHECK_PTR(Wk, refine);
+    CHECK_PTR(Wp, refine);
+    CHECK_PTR(wbeta, refine);
+    CHECK_PTR(conv, refine);
+    CHECK_PTR(S0, false);
+    CHECK_PTR(dO, true);
+    CHECK_PTR(dST, false);
+    CHECK_PTR(dq, true);
+    CHECK_PTR(dk, true);
+    CHECK_PTR(dv, true);
+    CHECK_PTR(dalpha, true);
+    CHECK_PTR(dbeta, true);
+    CHECK_PTR(dWk, refine);
+    CHECK_PTR(dWp, refine);
+    CHECK_PTR(dwbeta, refine);
+    CHECK_PTR(dconv, refine);
+    CHECK_PTR(dS0, false);
+    const size_t need = bwd_ws_bytes(d, desc->dtype);
+    if (!workspace) return fail(PRISM_ERR_WORKSPACE, "workspace is NULL");
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
+      return fail(PRISM_ERR_ALIGN, "workspace is not 256-byte aligned");
+    if (workspace_bytes < need)
+      return fail(PRISM_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
+                                           " bytes, needs " + std::to_string(need));
+    if (desc->dtype == PRISM_BF16)
+      return run_backward<prism::bf16>(d, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, dO, dST,
+                                       dq, dk, dv, dalpha, dbeta, dWk, dWp, dwbeta, dconv, dS0,
+                                       workspace, stream);
+    return run_backward<float>(d, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, dO, dST, dq, dk,
+                               dv, dalpha, dbeta, dWk, dWp, dwbeta, dconv, dS0, workspace, stream);
+  } catch (...) {
+    return fail(PRISM_ERR_HIP, "unexpected host exception");
+  }
 }
 
 void prism_timing_begin(void) {

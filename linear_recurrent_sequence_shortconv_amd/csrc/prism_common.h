@@ -25,6 +25,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int WAVE = 64;
 
+constexpr int cmax(int a, int b) { return a > b ? a : b; }
+
 template <typename T> struct Mfma;
 
 template <> struct Mfma<bf16> {
@@ -171,6 +173,22 @@ __device__ inline void gemm_acc(Acc<M, N, NW>& acc, const T* A, int lda, const T
 #pragma unroll
         for (int j = 0; j < TL::RN; ++j)
           acc.v[i][j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a[i], b[j], acc.v[i][j], 0, 0, 0);
+    }
+  } else if constexpr (!AKC || !BKC) {
+    // a strided operand takes KPL scalar LDS reads per fragment: keep one
+    // k step in flight to bound the live registers
+    static_assert(K % KS == 0, "k multiple");
+#pragma unroll 1
+    for (int k0 = 0; k0 < K; k0 += KS) {
+      typename Mfma<T>::frag a[TL::RM], b[TL::RN];
+#pragma unroll
+      for (int i = 0; i < TL::RM; ++i) a[i] = load_frag<T, AKC>(A, lda, m0 + 16 * i, k0, lane);
+#pragma unroll
+      for (int j = 0; j < TL::RN; ++j) b[j] = load_frag<T, BKC>(B, ldb, n0 + 16 * j, k0, lane);
+#pragma unroll
+      for (int i = 0; i < TL::RM; ++i)
+#pragma unroll
+        for (int j = 0; j < TL::RN; ++j) acc.v[i][j] = Mfma<T>::mma(a[i], b[j], acc.v[i][j]);
     }
   } else {
     static_assert(K % KS == 0, "k multiple");

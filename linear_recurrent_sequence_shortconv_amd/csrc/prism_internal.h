@@ -25,18 +25,54 @@ hipError_t launch_refine_fwd(const Dims& d, const E* v, const E* conv, const E* 
 
 // Chunk-local affine map of every chunk (parallel over B * H * NC).
 // Forward mode writes Mt, HT, Qt, Oloc, gC.  Backward mode (dO != nullptr)
-// writes Mt, HT, gC, M, ET (E = dO^T Qt) and nothing else.
+// writes Mt, HT, gC, M, ET (E = dO^T Qt), UT, WkT and nothing else.
 template <typename E>
 hipError_t launch_chunk_fwd(const Dims& d, const E* q, const E* k, const E* v, const float* alpha,
                             const float* beta, const E* Kl, const E* Wl, const E* dO, E* Mt,
-                            float* HT, E* Qt, float* Oloc, float* gC, E* M, float* ET,
-                            hipStream_t s);
+                            float* HT, E* Qt, float* Oloc, float* gC, E* M, float* ET, E* UT,
+                            E* WkT, hipStream_t s);
 
-// Sequential pass over chunks: S_{c+1} = exp(gC) S_c - S_c M_c + H_c.
-// Stores S_c per chunk (row-major, or transposed when `transposed`).
+// Sequential pass over chunks, forward (X <- exp(gC) X - X M + H, from S0) or
+// reverse (X <- exp(gC) X - X M^T + E, from dS_T).  Bm is M^T (forward) or M
+// (reverse); AddT is H^T or E^T.  Stores X per chunk before its update
+// (row-major, or transposed), and the final X in `fin` when not null.
 template <typename E>
-hipError_t launch_state_fwd(const Dims& d, const float* S0, const E* Mt, const float* HT,
-                            const float* gC, E* Sc, float* ST, bool transposed, hipStream_t s);
+hipError_t launch_state_pass(const Dims& d, const float* init, const E* Bm, const float* AddT,
+                             const float* gC, E* Xc, float* fin, bool transposed, bool reverse,
+                             hipStream_t s);
+
+// Arguments of the three chunk-parallel backward kernels (see chunk_bwd.hip).
+template <typename E>
+struct ChunkBwdArgs {
+  const E *q, *k, *v, *dO;
+  const float *alpha, *beta;
+  const E *Kl, *Wl, *UT, *WkT, *St, *dSnT;
+  float *dQt, *dUs, *dWks, *dKs, *dKl, *dWl, *dgs, *dVp, *dqp, *dkp, *dgp, *dbeta;
+  E *dq, *dk;
+  float* dvdir;
+  E* dv;
+  float* dalpha;
+};
+template <typename E>
+hipError_t launch_chunk_bwd(const Dims& d, const ChunkBwdArgs<E>& a, hipStream_t s);
+
+// Arguments of the refinement / ShortConv backward and the weight gradients.
+template <typename E>
+struct RefineBwdArgs {
+  const E *v, *conv, *Wk, *Wp, *wbeta;
+  E *WkT, *WpT;                 // transposed weights (workspace)
+  const float *dKl, *dWl;
+  float* dvdir;                 // in: direct v-gradient; out: + refinement part
+  E* u;
+  float* du;
+  E* dP;
+  float *dwbp, *dcp, *part;     // per-tile / per-split partial sums
+  E* dv;
+  float *dWk_o, *dWp_o, *dwbeta_o, *dconv_o;
+};
+template <typename E>
+hipError_t launch_refine_bwd(const Dims& d, const RefineBwdArgs<E>& a, hipStream_t s);
+int refine_bwd_splits(const Dims& d);   // split count of the weight-gradient GEMM
 
 // O = O_loc + Qt S_c^T, written to o [B, T, H, D].
 template <typename E>

@@ -73,9 +73,10 @@ def round_to(x, dtype):
         return f.astype(np.float64)
     if dtype != "bf16":
         raise ValueError(dtype)
-    bits = f.view(np.uint32).astype(np.uint64)
-    bits = ((bits + 0x7FFF + ((bits >> 16) & 1)) >> 16) << 16
-    return bits.astype(np.uint32).view(np.float32).astype(np.float64)
+    bits = f.view(np.uint32)
+    # finite inputs only (the generator draws no inf / nan): no overflow in uint32
+    bits = (bits + np.uint32(0x7FFF) + ((bits >> np.uint32(16)) & np.uint32(1))) & np.uint32(0xFFFF0000)
+    return bits.view(np.float32).astype(np.float64)
 
 
 def _sigmoid(x):
@@ -95,8 +96,8 @@ def make_inputs(B, T, H, d, L, dtype="bf16", seed=0, alpha_logit_mean=2.0,
     q = rng.standard_normal(shape)
     k = rng.standard_normal(shape)
     v = rng.standard_normal(shape)
-    q /= np.linalg.norm(q, axis=-1, keepdims=True)
-    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    q /= np.sqrt(np.einsum("...i,...i->...", q, q))[..., None]
+    k /= np.sqrt(np.einsum("...i,...i->...", k, k))[..., None]
     a_logit = alpha_logit_mean + np.sqrt(0.5) * rng.standard_normal((B, T, H))
     b_logit = rng.standard_normal((B, T, H))
     s = 1.0 / np.sqrt(d)

@@ -1,0 +1,151 @@
+"""Host-side checks of the C ABI (no GPU needed, no kernel is launched).
+
+* libprism.so loads and exports every function include/prism.h declares.
+* Every argument check runs before any HIP call and returns its status code
+  with a message (pointers below are never dereferenced: validation fails
+  first).
+* Workspace queries are monotone in T and L.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+import torch
+
+from linear_recurrent_sequence_shortconv_amd import prism as P
+
+# The calls below pass fake device pointers that validation must reject; they
+# are never run where a GPU is visible, so a mistake in a test cannot launch a
+# kernel on real memory.
+pytestmark = pytest.mark.skipif(torch.cuda.is_available(),
+                                reason="fake-pointer ABI checks run on hosts without a GPU")
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "prism.h")
+
+OK, E_NULL, E_SHAPE, E_UNSUP, E_ALIGN, E_WS = 0, 1, 2, 3, 4, 5
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(prism_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol():
+    L = P.lib()
+    names = declared_functions()
+    assert set(names) == set(P.EXPORTS), names
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_status_strings():
+    L = P.lib()
+    for code, name in P.STATUS.items():
+        assert L.prism_status_string(code).decode() == name
+
+
+def _fwd(desc, ptrs=None, ws=None, nbytes=0):
+    """Call prism_forward with fake (never dereferenced) 16-byte aligned pointers."""
+    L = P.lib()
+    fake = ctypes.c_void_p(0x10000)
+    p = [fake] * 12 if ptrs is None else ptrs
+    return L.prism_forward(ctypes.byref(desc) if desc is not None else None, *p,
+                           ws if ws is not None else fake, ctypes.c_size_t(nbytes), None)
+
+
+def _err():
+    return P.lib().prism_last_error().decode()
+
+
+def good_desc(**kw):
+    d = dict(B=2, T=100, H=4, dk=64, dv=64, L=2, chunk=64, dtype=P.PRISM_BF16)
+    d.update(kw)
+    return P.make_desc(d["B"], d["T"], d["H"], d["dk"], d["dv"], d["L"], d["chunk"], d["dtype"])
+
+
+@pytest.mark.parametrize("field,value,code", [
+    ("B", 0, E_SHAPE), ("T", 0, E_SHAPE), ("H", -1, E_SHAPE),
+    ("dk", 48, E_UNSUP), ("dv", 32, E_UNSUP), ("L", 9, E_UNSUP), ("L", -1, E_SHAPE),
+    ("chunk", 128, E_UNSUP), ("chunk", 8, E_UNSUP), ("dtype", 7, E_UNSUP),
+])
+def test_descriptor_checks(field, value, code):
+    d = good_desc(**{field: value})
+    n = ctypes.c_size_t(123)
+    assert P.lib().prism_forward_workspace(ctypes.byref(d), ctypes.byref(n)) == code
+    assert n.value == 0
+    assert _err()
+    assert _fwd(d) == code
+
+
+def test_conv_width_and_fp32_envelope():
+    d = good_desc()
+    d.conv_width = 3
+    assert _fwd(d) == E_UNSUP
+    assert _fwd(good_desc(dtype=P.PRISM_F32, dk=128, dv=128)) == E_UNSUP
+    assert _fwd(good_desc(dtype=P.PRISM_F32, dk=64, dv=64, chunk=64)) == E_UNSUP
+    n = ctypes.c_size_t(0)
+    d = good_desc(dtype=P.PRISM_F32, dk=64, dv=64, chunk=32)
+    assert P.lib().prism_forward_workspace(ctypes.byref(d), ctypes.byref(n)) == OK and n.value > 0
+
+
+def test_null_desc_and_pointers():
+    assert _fwd(None) == E_NULL
+    fake = ctypes.c_void_p(0x10000)
+    for i, name in enumerate(["q", "k", "v", "alpha", "beta", "Wk", "Wp", "wbeta", "conv"]):
+        p = [fake] * 12
+        p[i] = None
+        assert _fwd(good_desc(), p) == E_NULL, name
+        assert name in _err()
+    # with L = 0 the weights may be NULL (then the workspace check fails next)
+    p = [fake] * 12
+    p[5] = p[6] = p[7] = p[8] = None
+    assert _fwd(good_desc(L=0), p, nbytes=0) == E_WS
+    # output o is required; S0 and ST are optional
+    p = [fake] * 12
+    p[10] = None
+    assert _fwd(good_desc(), p) == E_NULL
+    p = [fake] * 12
+    p[9] = None
+    p[11] = None
+    assert _fwd(good_desc(), p, nbytes=0) == E_WS
+
+
+def test_alignment_and_workspace():
+    fake = ctypes.c_void_p(0x10000)
+    p = [fake] * 12
+    p[2] = ctypes.c_void_p(0x10008)
+    assert _fwd(good_desc(), p) == E_ALIGN and "v" in _err()
+    assert _fwd(good_desc(), ws=ctypes.c_void_p(0x10010), nbytes=1 << 40) == E_ALIGN
+    d = good_desc()
+    need = P.forward_workspace_bytes(d)
+    assert _fwd(d, nbytes=need - 1) == E_WS and str(need) in _err()
+    L = P.lib()
+    p = [fake] * 22
+    assert L.prism_backward(ctypes.byref(d), *p, fake, ctypes.c_size_t(0), None) == E_WS
+    p[10] = None   # dO (order: q k v alpha beta Wk Wp wbeta conv S0 dO dST dq ...)
+    assert L.prism_backward(ctypes.byref(d), *p, fake, ctypes.c_size_t(1 << 40), None) == E_NULL
+    p = [fake] * 22
+    p[12] = None   # dq
+    assert L.prism_backward(ctypes.byref(d), *p, fake, ctypes.c_size_t(1 << 40), None) == E_NULL
+
+
+def test_workspace_monotone():
+    prev_f = prev_b = 0
+    for T in (1, 63, 64, 65, 1000, 4096):
+        d = good_desc(T=T)
+        f, b = P.forward_workspace_bytes(d), P.backward_workspace_bytes(d)
+        assert f >= prev_f and b >= prev_b and b > f
+        prev_f, prev_b = f, b
+    prev = 0
+    for L in range(0, 9):
+        b = P.backward_workspace_bytes(good_desc(L=L))
+        assert b >= prev
+        prev = b
+
+
+def test_workspace_query_null_output():
+    d = good_desc()
+    assert P.lib().prism_forward_workspace(ctypes.byref(d), None) == E_NULL

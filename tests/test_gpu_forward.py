@@ -67,8 +67,8 @@ def _check_full(x, dtype, chunk, L, tol=None):
 
 
 # --------------------------------------------------------------------------- small, full oracle
-@pytest.mark.parametrize("chunk", [16, 32, 64])
-@pytest.mark.parametrize("d", [16, 32, 64])
+@pytest.mark.parametrize("d,chunk", [(16, 16), (16, 32), (16, 64), (32, 16), (32, 32), (32, 64),
+                                     (64, 16), (64, 32)])
 def test_fp32_chunk_sizes_ragged(d, chunk):
     x = make_inputs(2, 100, 3, d, 2, "f32", seed=d + chunk, random_S0=True)
     print(f"\n[fp32 d={d} chunk={chunk} T=100 L=2]", flush=True)
@@ -80,6 +80,13 @@ def test_fp32_depths(L):
     x = make_inputs(1, 70, 2, 32, L, "f32", seed=40 + L)
     print(f"\n[fp32 d=32 chunk=32 T=70 L={L}]", flush=True)
     _check_full(x, "f32", 32, L)
+
+
+def test_fp32_outside_envelope_raises():
+    """fp32 storage needs d * chunk <= 2048; the library refuses before launching."""
+    x = make_inputs(1, 10, 1, 64, 1, "f32", seed=1)
+    with pytest.raises(RuntimeError, match="PRISM_ERR_UNSUPPORTED"):
+        gpu_forward(x, "f32", 64, 1)
 
 
 def test_tiny_fp32_workload():
