@@ -258,6 +258,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
   }
 
   // ---- dM (row-major into X1, transposed into X2); Wk rows ----
+  __syncthreads();   // every read of dS_n / dS_n^T (X1, X2) is done
   for_tiles(dm, wave, lane, [&](int k0, int n, const f32x4& x) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -332,31 +333,35 @@ struct CB2Lds {
   static constexpr int O_K = (SZ_VEC + 15) / 16 * 16;
   static constexpr int O_TB = O_K + SZ_R;
   static constexpr int O_X = O_TB + SZ_CC;
-  // phase "fold": K_l, W_l, F, V rows (-> V' rows)
-  static constexpr int F_KL = O_X;
+  // phase "fold": V rows (-> V' rows, live until U is formed), K_l, W_l, F
+  static constexpr int F_V = O_X;
+  static constexpr int F_KL = F_V + SZ_R;
   static constexpr int F_WL = F_KL + SZ_R;
   static constexpr int F_F = F_WL + SZ_R;
-  static constexpr int F_V = F_F + SZ_CC;
-  static constexpr int F_END = F_V + SZ_R;
-  // phase "solve": A, T fp32, scratch; then T diag(beta), T diag(beta e)
-  static constexpr int S_AF = O_X;
+  static constexpr int F_END = F_F + SZ_CC;
+  // phase "solve" (after V' rows): A, T fp32, scratch, T diag(beta), T diag(beta e)
+  static constexpr int S_AF = F_V + SZ_R;
   static constexpr int S_TF = S_AF + SZ_F;
   static constexpr int S_XS = S_TF + SZ_F;
-  static constexpr int S_TBB = cmax(S_XS + 3 * 256 * 4, F_END);
+  static constexpr int S_TBB = S_XS + 3 * 256 * 4;
   static constexpr int S_TBE = S_TBB + SZ_CC;
-  // phase "R0": U, Wk rows (then dU, dWk rows), Q, dO, -dQt rows, R0, X0
+  static constexpr int S_END = S_TBE + SZ_CC;
+  // phase "R0" (written after the U / Wk products have read everything above):
+  // U, Wk rows (then dU, dWk rows), Q, dO, -dQt rows, R0, X0
   static constexpr int P_U = O_X;
   static constexpr int P_WK = P_U + SZ_R;
   static constexpr int P_Q = P_WK + SZ_R;
   static constexpr int P_DO = P_Q + SZ_R;
   static constexpr int P_NDQ = P_DO + SZ_R;
-  static constexpr int P_R0 = cmax(P_NDQ + SZ_R, S_TBE + SZ_CC);
-  static constexpr int P_XB = P_R0 + SZ_CC;
+  static constexpr int P_R0 = P_NDQ + SZ_R;   // later dT
+  static constexpr int P_XB = P_R0 + SZ_CC;   // later P1 = dT T^T (live while dG0 is formed)
   static constexpr int P_END = P_XB + SZ_CC;
-  // phase "tail": V' rows (Q slot), dT (R0 slot), P1 (X0 slot), Zf (dO slot), Zb
-  static constexpr int Z_F = P_DO;
-  static constexpr int Z_B = P_NDQ + (SZ_F > SZ_R ? SZ_F - SZ_R : 0);
-  static constexpr int TOTAL = cmax(P_END, cmax(Z_B + SZ_CC, S_TBE + SZ_CC));
+  // phase "tail": dG0 fp32 and (dG0 + dG0^T) from the U slot on; they must
+  // stay clear of the P1 slot, which other waves read while dG0 is written
+  static constexpr int Z_F = P_U;
+  static constexpr int Z_B = Z_F + SZ_F;
+  static_assert(Z_F + SZ_F <= P_XB, "dG0 must not overlap P1");
+  static constexpr int TOTAL = cmax(P_END, cmax(Z_B + SZ_CC, cmax(S_END, F_END)));
 };
 
 template <int C, int NT>

@@ -50,6 +50,7 @@ __global__ __launch_bounds__(RB_NT) void refine_bwd_kernel(
   constexpr int VN = 16 / sizeof(E);
   __shared__ E vbuf[(RB_TT + 3) * D];
   __shared__ __attribute__((aligned(16))) E ubuf[RB_TT * LD];
+  __shared__ __attribute__((aligned(16))) E ulo[sizeof(E) == 2 ? RB_TT * LD : 16];   // u - bf16(u)
   __shared__ __attribute__((aligned(16))) E dpbuf[RB_TT * LD];
   __shared__ __attribute__((aligned(16))) E dkbuf[RB_TT * LD];
   __shared__ float gate[8][RB_TT];
@@ -86,7 +87,9 @@ __global__ __launch_bounds__(RB_NT) void refine_bwd_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) u += to_f(ch[f * 4 + j]) * to_f(vbuf[(t + 3 - j) * D + f]);
     }
-    ubuf[t * LD + f] = to_t<E>(u);
+    const E uh = to_t<E>(u);
+    ubuf[t * LD + f] = uh;
+    if constexpr (sizeof(E) == 2) ulo[t * LD + f] = to_t<E>(u - to_f(uh));
   }
   __syncthreads();
   // u rows for the weight-gradient GEMM; gates
@@ -132,23 +135,29 @@ __global__ __launch_bounds__(RB_NT) void refine_bwd_kernel(
   }
   __syncthreads();
 
-  // p^(l) = W_p^(l) u for this wave's tiles
+  // p^(l) = W_p^(l) (u_hi + u_lo) for this wave's tiles (same as the forward)
   auto project = [&](const E* W, f32x4 (&acc)[2][FPW]) {
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int nn = 0; nn < FPW; ++nn) acc[m][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
     for (int k0 = 0; k0 < D; k0 += KS) {
-      typename Mfma<E>::frag a[2];
+      typename Mfma<E>::frag a[2], al[2];
 #pragma unroll
-      for (int m = 0; m < 2; ++m) a[m] = load_frag<E, true>(ubuf, LD, 32 * th + 16 * m, k0, lane);
+      for (int m = 0; m < 2; ++m) {
+        a[m] = load_frag<E, true>(ubuf, LD, 32 * th + 16 * m, k0, lane);
+        if constexpr (sizeof(E) == 2) al[m] = load_frag<E, true>(ulo, LD, 32 * th + 16 * m, k0, lane);
+      }
 #pragma unroll
       for (int nn = 0; nn < FPW; ++nn) {
         const int n = fq + 4 * nn;
         if (n < NFT) {
           const typename Mfma<E>::frag bw = load_frag<E, true>(W, D, 16 * n, k0, lane);
 #pragma unroll
-          for (int m = 0; m < 2; ++m) acc[m][nn] = Mfma<E>::mma(a[m], bw, acc[m][nn]);
+          for (int m = 0; m < 2; ++m) {
+            acc[m][nn] = Mfma<E>::mma(a[m], bw, acc[m][nn]);
+            if constexpr (sizeof(E) == 2) acc[m][nn] = Mfma<E>::mma(al[m], bw, acc[m][nn]);
+          }
         }
       }
     }

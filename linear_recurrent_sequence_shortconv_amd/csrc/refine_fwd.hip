@@ -39,6 +39,9 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
 
   __shared__ E vbuf[(RF_TT + 3) * D];
   __shared__ __attribute__((aligned(16))) E ubuf[RF_TT * LD];
+  // bf16 only: u - bf16(u), so that p^(l) = W_p^(l) (u_hi + u_lo) is fp32-accurate
+  // (the GELU chain amplifies errors in p; k^(l) uses u_hi alone)
+  __shared__ __attribute__((aligned(16))) E ulo[sizeof(E) == 2 ? RF_TT * LD : 16];
   __shared__ __attribute__((aligned(16))) E obk[RF_TT * LD];
   __shared__ __attribute__((aligned(16))) E obw[RF_TT * LD];
   __shared__ float gate[8][RF_TT];
@@ -74,7 +77,9 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
 #pragma unroll
       for (int j = 0; j < 4; ++j) u += to_f(ch[f * 4 + j]) * to_f(vbuf[(t + 3 - j) * D + f]);
     }
-    ubuf[t * LD + f] = to_t<E>(u);
+    const E uh = to_t<E>(u);
+    ubuf[t * LD + f] = uh;
+    if constexpr (sizeof(E) == 2) ulo[t * LD + f] = to_t<E>(u - to_f(uh));
   }
   __syncthreads();
 
@@ -141,9 +146,12 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
 #pragma unroll 2
     for (int kk = 0; kk < NK; ++kk) {
       const int k0 = kk * KS;
-      typename Mfma<E>::frag a[4], bk[FPW], bp[FPW];
+      typename Mfma<E>::frag a[4], al[4], bk[FPW], bp[FPW];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) a[m] = load_frag<E, true>(ubuf, LD, 16 * m, k0, lane);
+      for (int m = 0; m < 4; ++m) {
+        a[m] = load_frag<E, true>(ubuf, LD, 16 * m, k0, lane);
+        if constexpr (sizeof(E) == 2) al[m] = load_frag<E, true>(ulo, LD, 16 * m, k0, lane);
+      }
 #pragma unroll
       for (int nn = 0; nn < FPW; ++nn) {
         const int n = wave + RF_NW * nn;
@@ -160,6 +168,7 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
           for (int m = 0; m < 4; ++m) {
             ak[m][nn] = Mfma<E>::mma(a[m], bk[nn], ak[m][nn]);
             ap[m][nn] = Mfma<E>::mma(a[m], bp[nn], ap[m][nn]);
+            if constexpr (sizeof(E) == 2) ap[m][nn] = Mfma<E>::mma(al[m], bp[nn], ap[m][nn]);
           }
         }
       }
