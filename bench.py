@@ -35,37 +35,78 @@ MFMA_F32_PEAK_TFLOPS = 157.3
 def algorithmic_counts(w):
     """Algorithmic bytes and FLOPs per launch of each kernel for workload w.
 
-    Bytes count each tensor once at its storage size (e = 2 for bf16):
-    what the kernel must read and write, not what it happens to re-read.
-    FLOPs count the dense matrix products of the algorithm (2 m n k each).
+    Bytes count each tensor once at its storage size (e = 2 for bf16; fp32
+    intermediates at 4): what the kernel must read and write, not what it
+    happens to re-read.  FLOPs count the dense matrix products of the
+    algorithm (2 m n k each); the extra product of the hi/lo split of the
+    anchor is an accuracy device and is not counted.  "bound" is the roof
+    the kernel would hit first at MI355X peak rates.
     """
     B, T, H, D, L, C = w.B, w.T, w.H, w.d, w.L, w.chunk
     e = 2 if w.dtype == "bf16" else 4
     NC = -(-T // C)
+    Tp = NC * C
     th = B * T * H                 # token-heads
+    ntp = B * Tp * H               # padded token-heads (workspace rows)
     nch = B * H * NC               # chunks
+    bh = B * H
+    c = {}
+    c["refine_fwd"] = (th * e * D + ntp * 2 * L * D * e, th * 4 * L * D * D)
+    c["chunk_fwd"] = (th * (3 * D * e + 8) + ntp * 2 * L * D * e
+                      + nch * (D * D * (e + 4) + C * D * (e + 4) + 4),
+                      nch * (2 * C * C * D * (4 * L + 6) + 2 * C * D * D * (L + 2)))
+    c["chunk_fwd_bwdmode"] = (th * (4 * D * e + 8) + ntp * 2 * L * D * e
+                              + nch * (2 * D * D * e + 2 * D * D * 4 + 2 * C * D * e + 4),
+                              nch * (2 * C * C * D * (2 * L + 5) + 2 * C * D * D * (L + 4)))
+    st = (nch * D * D * (2 * e + 4) + bh * D * D * 4, nch * 2 * D ** 3)
+    c["state_fwd"] = c["state_fwd_recompute"] = st
+    c["state_bwd"] = (st[0] + bh * D * D * 4, st[1])
+    c["out_fwd"] = (nch * (D * D * e + C * D * (e + 4)) + th * D * e, nch * 2 * C * D * D)
+    c["chunk_bwd_state"] = (th * (2 * D * e + 4) + nch * (2 * C * D * e + 2 * D * D * e + 16 * C * D + 4 * C)
+                            + ntp * L * D * (2 * e + 8),
+                            nch * (2 * C * D * D * (6 + 2 * L) + 2 * D ** 3))
+    c["chunk_bwd_solve"] = (th * (4 * D * e + 12) + ntp * 2 * L * D * e + nch * (28 * C * D + 8 * C),
+                            nch * (2 * C * C * D * (2 * L + 16) + 4 * C ** 3))
+    c["chunk_bwd_pairs"] = (th * (5 * D * e + 8) + ntp * 2 * L * D * e + nch * 12 * C * D
+                            + ntp * L * D * 16 + ntp * D * 4,
+                            nch * 2 * C * C * D * 10 * L)
+    c["refine_bwd"] = (th * D * e + ntp * (8 * L * D + 8 * D + D * e + 4 * D + L * D * e),
+                       th * 6 * L * D * D)
+    c["conv_bwd"] = (2 * th * D * e + ntp * 8 * D, 8 * th * D)
+    ns = max(1, min(1024 // (2 * H * max(L, 1)), -(-B * Tp // 64)))
+    c["wgrad_gemm"] = (ntp * L * D * (4 + e) + ntp * D * e * 2 * L + H * L * 2 * ns * D * D * 4,
+                       ntp * 4 * L * D * D)
+    c["wgrad_reduce"] = (H * L * 2 * ns * D * D * 4 + H * L * 2 * D * D * 4, H * L * 2 * ns * D * D)
+    c["transpose_weights"] = (H * L * 4 * D * D * e, 0)
+    c["refine_fwd_recompute"] = c["refine_fwd"]
+    peak_f = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
     out = {}
-    out["refine_fwd"] = {
-        "bytes": th * e * (D + 2 * L * D),                        # read v, write K_l, W_l
-        "flops": th * (2 * L * 2 * D * D),                        # k^(l), p^(l) projections
-        "bound": "hbm"}
-    out["chunk_fwd"] = {
-        "bytes": nch * (C * D * e * (3 + 2 * L) + 8 * C            # q, k, v, K_l, W_l, alpha, beta
-                        + D * D * (e + 4) + C * D * (e + 4) + 4),  # M^T, H^T, Qt, O_loc, gC
-        "flops": nch * (2 * C * C * D * (4 * L + 6) + 2 * C * D * D * (L + 2)),
-        "bound": "mfma"}
-    out["state_fwd"] = {
-        "bytes": nch * D * D * (e + 4 + e) + B * H * D * D * 4,   # read M^T, H^T; write S_c; S_T
-        "flops": nch * 2 * D * D * D,
-        "bound": "hbm"}
-    out["out_fwd"] = {
-        "bytes": nch * (D * D * e + C * D * (e + 4)) + th * D * e,
-        "flops": nch * 2 * C * D * D,
-        "bound": "hbm"}
+    for name, (byt, flo) in c.items():
+        t_hbm = byt / (HBM_PEAK_GBS * 1e9)
+        t_mfma = flo / (peak_f * 1e12)
+        out[name] = {"bytes": byt, "flops": flo, "bound": "mfma" if t_mfma > t_hbm else "hbm",
+                     "floor_ms": max(t_hbm, t_mfma) * 1e3}
     return out
 
 
-def roofline_for(name, counts, avg_ms, dtype):
+def measured_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel sources (else None for every kernel)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return {}
+    rec = json.load(open(path))
+    csrc = os.path.join(ROOT, "linear_recurrent_sequence_shortconv_amd", "csrc")
+    h = hashlib.sha256()
+    for f in sorted(os.listdir(csrc)):
+        h.update(open(os.path.join(csrc, f), "rb").read())
+    if rec.get("sources_sha256") != h.hexdigest():
+        return {}
+    return {k: v["bytes_per_launch"] for k, v in rec.get("kernels", {}).items()}
+
+
+def roofline_for(name, counts, avg_ms, dtype, traffic=None):
     c = counts.get(name)
     if c is None or avg_ms <= 0:
         return None
@@ -78,8 +119,10 @@ def roofline_for(name, counts, avg_ms, dtype):
         peak = HBM_PEAK_GBS
         unit = "GB/s"
     return {"kernel": name, "bound": c["bound"], "achieved": round(achieved, 2), "peak": peak,
-            "unit": unit, "frac": round(achieved / peak, 4), "traffic": None,
-            "avg_launch_ms": round(avg_ms, 5)}
+            "unit": unit, "frac": round(achieved / peak, 4),
+            "traffic": (traffic or {}).get(name),
+            "algorithmic_bytes": c["bytes"], "algorithmic_flops": c["flops"],
+            "avg_launch_ms": round(avg_ms, 5), "roofline_floor_ms": round(c["floor_ms"], 5)}
 
 
 def cpu_baseline(w, x, budget_s=15.0, backward=False):
@@ -190,12 +233,15 @@ def main():
     kernels = {n: {"total_ms": round(tot / args.steps, 5), "launches_per_step": c // args.steps,
                    "avg_launch_ms": round(tot / c, 5)} for n, (tot, c) in kt.result.items()}
     counts = algorithmic_counts(w)
+    traffic = measured_traffic()
     dominant = max(kernels, key=lambda n: kernels[n]["total_ms"]) if kernels else None
-    roof = roofline_for(dominant, counts, kernels[dominant]["avg_launch_ms"], w.dtype) if dominant else None
+    roof = (roofline_for(dominant, counts, kernels[dominant]["avg_launch_ms"], w.dtype, traffic)
+            if dominant else None)
     for n in kernels:
-        r = roofline_for(n, counts, kernels[n]["avg_launch_ms"], w.dtype)
+        r = roofline_for(n, counts, kernels[n]["avg_launch_ms"], w.dtype, traffic)
         if r:
-            kernels[n].update(bound=r["bound"], achieved=r["achieved"], unit=r["unit"], frac=r["frac"])
+            kernels[n].update(bound=r["bound"], achieved=r["achieved"], unit=r["unit"],
+                              frac=r["frac"], floor_ms=r["roofline_floor_ms"])
 
     tokens = w.B * w.T
     value = tokens / (ms * 1e-3)

@@ -1006,52 +1006,52 @@ __device__ void invert_unit_lower_b(const float* A, float* Tm, float* Xs, int ti
 // launchers
 // ---------------------------------------------------------------------------
 template <typename E, int D, int C>
-static hipError_t cbwd_launch_dc(const Dims& d, const ChunkBwdArgs<E>& a, hipStream_t s) {
+static hipError_t cbwd_launch_dc(const Dims& d, const ChunkBwdArgs<E>& a, int stage, hipStream_t s) {
   if constexpr (sizeof(E) == 4 && D * C > 2048) {
     return hipErrorInvalidValue;   // outside the fp32 envelope (LDS)
   } else {
-  const int nblk = d.B * d.H * d.NC;
-  hipLaunchKernelGGL((chunk_bwd_state_kernel<E, D, C>), dim3(nblk), dim3(CB_NT), 0, s, a.k, a.dO,
-                     a.alpha, a.Kl, a.Wl, a.UT, a.WkT, a.St, a.dSnT, a.dQt, a.dUs, a.dWks, a.dKs,
-                     a.dKl, a.dWl, a.dgs, d.B, d.T, d.H, d.L, d.NC, d.Tp);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((chunk_bwd_solve_kernel<E, D, C>), dim3(nblk), dim3(CB_NT), 0, s, a.q, a.k,
-                     a.v, a.dO, a.alpha, a.beta, a.Kl, a.Wl, a.dQt, a.dUs, a.dWks, a.dKs, a.dgs,
-                     a.dVp, a.dqp, a.dkp, a.dgp, a.dbeta, d.B, d.T, d.H, d.L, d.NC, d.Tp);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((chunk_bwd_pairs_kernel<E, D, C>), dim3(nblk), dim3(CB_NT), 0, s, a.q, a.k,
-                     a.dO, a.alpha, a.Kl, a.Wl, a.dVp, a.dqp, a.dkp, a.dgp, a.dKl, a.dWl, a.dq,
-                     a.dk, a.dvdir, a.dv, a.dalpha, d.B, d.T, d.H, d.L, d.NC, d.Tp);
-  return hipGetLastError();
+    const int nblk = d.B * d.H * d.NC;
+    if (stage == 0)
+      hipLaunchKernelGGL((chunk_bwd_state_kernel<E, D, C>), dim3(nblk), dim3(CB_NT), 0, s, a.k, a.dO,
+                         a.alpha, a.Kl, a.Wl, a.UT, a.WkT, a.St, a.dSnT, a.dQt, a.dUs, a.dWks,
+                         a.dKs, a.dKl, a.dWl, a.dgs, d.B, d.T, d.H, d.L, d.NC, d.Tp);
+    else if (stage == 1)
+      hipLaunchKernelGGL((chunk_bwd_solve_kernel<E, D, C>), dim3(nblk), dim3(CB_NT), 0, s, a.q,
+                         a.k, a.v, a.dO, a.alpha, a.beta, a.Kl, a.Wl, a.dQt, a.dUs, a.dWks, a.dKs,
+                         a.dgs, a.dVp, a.dqp, a.dkp, a.dgp, a.dbeta, d.B, d.T, d.H, d.L, d.NC,
+                         d.Tp);
+    else
+      hipLaunchKernelGGL((chunk_bwd_pairs_kernel<E, D, C>), dim3(nblk), dim3(CB_NT), 0, s, a.q,
+                         a.k, a.dO, a.alpha, a.Kl, a.Wl, a.dVp, a.dqp, a.dkp, a.dgp, a.dKl, a.dWl,
+                         a.dq, a.dk, a.dvdir, a.dv, a.dalpha, d.B, d.T, d.H, d.L, d.NC, d.Tp);
+    return hipGetLastError();
   }
 }
 
 template <typename E, int D>
-static hipError_t cbwd_launch_d(const Dims& d, const ChunkBwdArgs<E>& a, hipStream_t s) {
+static hipError_t cbwd_launch_d(const Dims& d, const ChunkBwdArgs<E>& a, int stage, hipStream_t s) {
   switch (d.C) {
-    case 16: return cbwd_launch_dc<E, D, 16>(d, a, s);
-    case 32: return cbwd_launch_dc<E, D, 32>(d, a, s);
-    case 64: return cbwd_launch_dc<E, D, 64>(d, a, s);
+    case 16: return cbwd_launch_dc<E, D, 16>(d, a, stage, s);
+    case 32: return cbwd_launch_dc<E, D, 32>(d, a, stage, s);
+    case 64: return cbwd_launch_dc<E, D, 64>(d, a, stage, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <typename E>
-hipError_t launch_chunk_bwd(const Dims& d, const ChunkBwdArgs<E>& a, hipStream_t s) {
+hipError_t launch_chunk_bwd(const Dims& d, const ChunkBwdArgs<E>& a, int stage, hipStream_t s) {
   switch (d.D) {
-    case 16: return cbwd_launch_d<E, 16>(d, a, s);
-    case 32: return cbwd_launch_d<E, 32>(d, a, s);
-    case 64: return cbwd_launch_d<E, 64>(d, a, s);
+    case 16: return cbwd_launch_d<E, 16>(d, a, stage, s);
+    case 32: return cbwd_launch_d<E, 32>(d, a, stage, s);
+    case 64: return cbwd_launch_d<E, 64>(d, a, stage, s);
     case 128:
-      if constexpr (sizeof(E) == 2) return cbwd_launch_d<E, 128>(d, a, s);
+      if constexpr (sizeof(E) == 2) return cbwd_launch_d<E, 128>(d, a, stage, s);
       break;
   }
   return hipErrorInvalidValue;
 }
 
-template hipError_t launch_chunk_bwd<bf16>(const Dims&, const ChunkBwdArgs<bf16>&, hipStream_t);
-template hipError_t launch_chunk_bwd<float>(const Dims&, const ChunkBwdArgs<float>&, hipStream_t);
+template hipError_t launch_chunk_bwd<bf16>(const Dims&, const ChunkBwdArgs<bf16>&, int, hipStream_t);
+template hipError_t launch_chunk_bwd<float>(const Dims&, const ChunkBwdArgs<float>&, int, hipStream_t);
 
 }  // namespace prism

@@ -258,14 +258,14 @@ prism_status run_backward(const prism::Dims& d, const void* q, const void* k, co
   const E* v_ = static_cast<const E*>(v);
   const E* dO_ = static_cast<const E*>(dO);
   if (d.L > 0)
-    HIP_TRY("refine_fwd", s,
+    HIP_TRY("refine_fwd_recompute", s,
             prism::launch_refine_fwd<E>(d, v_, static_cast<const E*>(conv), static_cast<const E*>(Wk),
                                         static_cast<const E*>(Wp), static_cast<const E*>(wbeta),
                                         w.Kl, w.Wl, s));
   HIP_TRY("chunk_fwd_bwdmode", s,
           prism::launch_chunk_fwd<E>(d, q_, k_, v_, alpha, beta, w.Kl, w.Wl, dO_, w.Mt, w.HT,
                                      nullptr, nullptr, w.gC, w.M, w.ET, w.UT, w.WkT, s));
-  HIP_TRY("state_fwd", s,
+  HIP_TRY("state_fwd_recompute", s,
           prism::launch_state_pass<E>(d, S0, w.Mt, w.HT, w.gC, w.Sct, nullptr, true, false, s));
   HIP_TRY("state_bwd", s,
           prism::launch_state_pass<E>(d, dST, w.M, w.ET, w.gC, w.dSnT, dS0, true, true, s));
@@ -276,7 +276,9 @@ prism_status run_backward(const prism::Dims& d, const void* q, const void* k, co
   a.dgs = w.dgs; a.dVp = w.dVp; a.dqp = w.dqp; a.dkp = w.dkp; a.dgp = w.dgp; a.dbeta = dbeta;
   a.dq = static_cast<E*>(dq); a.dk = static_cast<E*>(dk); a.dvdir = w.dvdir;
   a.dv = static_cast<E*>(dv); a.dalpha = dalpha;
-  HIP_TRY("chunk_bwd", s, prism::launch_chunk_bwd<E>(d, a, s));
+  HIP_TRY("chunk_bwd_state", s, prism::launch_chunk_bwd<E>(d, a, 0, s));
+  HIP_TRY("chunk_bwd_solve", s, prism::launch_chunk_bwd<E>(d, a, 1, s));
+  HIP_TRY("chunk_bwd_pairs", s, prism::launch_chunk_bwd<E>(d, a, 2, s));
   if (d.L > 0) {
     prism::RefineBwdArgs<E> r;
     r.v = v_; r.conv = static_cast<const E*>(conv); r.Wk = static_cast<const E*>(Wk);
@@ -285,7 +287,11 @@ prism_status run_backward(const prism::Dims& d, const void* q, const void* k, co
     r.du = w.du; r.dP = w.dP; r.dwbp = w.dwbp; r.dcp = w.dcp; r.part = w.part;
     r.dv = static_cast<E*>(dv); r.dWk_o = dWk; r.dWp_o = dWp; r.dwbeta_o = dwbeta;
     r.dconv_o = dconv;
-    HIP_TRY("refine_bwd", s, prism::launch_refine_bwd<E>(d, r, s));
+    HIP_TRY("transpose_weights", s, prism::launch_refine_bwd<E>(d, r, 0, s));
+    HIP_TRY("refine_bwd", s, prism::launch_refine_bwd<E>(d, r, 1, s));
+    HIP_TRY("conv_bwd", s, prism::launch_refine_bwd<E>(d, r, 2, s));
+    HIP_TRY("wgrad_gemm", s, prism::launch_refine_bwd<E>(d, r, 3, s));
+    HIP_TRY("wgrad_reduce", s, prism::launch_refine_bwd<E>(d, r, 4, s));
   }
   return PRISM_OK;
 }

@@ -54,7 +54,8 @@ struct ChunkBwdArgs {
   float* dalpha;
 };
 template <typename E>
-hipError_t launch_chunk_bwd(const Dims& d, const ChunkBwdArgs<E>& a, hipStream_t s);
+// stage 0: chunk_bwd_state, 1: chunk_bwd_solve, 2: chunk_bwd_pairs (in this order)
+hipError_t launch_chunk_bwd(const Dims& d, const ChunkBwdArgs<E>& a, int stage, hipStream_t s);
 
 // Arguments of the refinement / ShortConv backward and the weight gradients.
 template <typename E>
@@ -71,7 +72,8 @@ struct RefineBwdArgs {
   float *dWk_o, *dWp_o, *dwbeta_o, *dconv_o;
 };
 template <typename E>
-hipError_t launch_refine_bwd(const Dims& d, const RefineBwdArgs<E>& a, hipStream_t s);
+// stage 0: transpose weights, 1: refine_bwd, 2: conv_bwd, 3: wgrad_gemm, 4: wgrad_reduce
+hipError_t launch_refine_bwd(const Dims& d, const RefineBwdArgs<E>& a, int stage, hipStream_t s);
 int refine_bwd_splits(const Dims& d);   // split count of the weight-gradient GEMM
 
 // O = O_loc + Qt S_c^T, written to o [B, T, H, D].

@@ -496,31 +496,39 @@ static void refine_bwd_launch(const Dims& d, const RefineBwdArgs<E>& a, hipStrea
 }
 
 template <typename E, int D>
-static hipError_t refine_bwd_d(const Dims& d, const RefineBwdArgs<E>& a, int NS, hipStream_t s) {
+static hipError_t refine_bwd_d(const Dims& d, const RefineBwdArgs<E>& a, int NS, int stage,
+                               hipStream_t s) {
   const int ntiles = (d.Tp + RB_TT - 1) / RB_TT;
   const long nw = (long)d.H * d.L * D * D;
-  hipLaunchKernelGGL((transpose_weights_kernel<E>), dim3((unsigned)((nw + 255) / 256 < 4096 ? (nw + 255) / 256 : 4096)),
-                     dim3(256), 0, s, a.Wk, a.Wp, a.WkT, a.WpT, d.H * d.L, D);
-  if (d.L <= 2)
-    refine_bwd_launch<E, D, 2>(d, a, s);
-  else if (d.L <= 4)
-    refine_bwd_launch<E, D, 4>(d, a, s);
-  else
-    refine_bwd_launch<E, D, 8>(d, a, s);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((conv_bwd_kernel<E, D>), dim3(ntiles * d.B * d.H), dim3(256), 0, s, a.v, a.conv,
-                     a.du, a.dvdir, a.dv, a.dcp, d.B, d.T, d.H, d.Tp);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((wgrad_gemm_kernel<E, D>), dim3(d.H * d.L * 2 * NS), dim3(WG_NT), 0, s, a.dKl,
-                     a.dP, a.u, a.part, d.B, d.H, d.L, d.Tp, NS);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const long total = 2 * nw + (long)d.H * d.L * D + (long)d.H * D * 4;
-  const unsigned grid = (unsigned)((total + 255) / 256 < 8192 ? (total + 255) / 256 : 8192);
-  hipLaunchKernelGGL(wgrad_reduce_kernel, dim3(grid), dim3(256), 0, s, a.part, a.dwbp, a.dcp, a.dWk_o,
-                     a.dWp_o, a.dwbeta_o, a.dconv_o, d.B, d.H, d.L, D, NS, ntiles);
+  switch (stage) {
+    case 0:
+      hipLaunchKernelGGL((transpose_weights_kernel<E>),
+                         dim3((unsigned)((nw + 255) / 256 < 4096 ? (nw + 255) / 256 : 4096)), dim3(256),
+                         0, s, a.Wk, a.Wp, a.WkT, a.WpT, d.H * d.L, D);
+      break;
+    case 1:
+      if (d.L <= 2)
+        refine_bwd_launch<E, D, 2>(d, a, s);
+      else if (d.L <= 4)
+        refine_bwd_launch<E, D, 4>(d, a, s);
+      else
+        refine_bwd_launch<E, D, 8>(d, a, s);
+      break;
+    case 2:
+      hipLaunchKernelGGL((conv_bwd_kernel<E, D>), dim3(ntiles * d.B * d.H), dim3(256), 0, s, a.v,
+                         a.conv, a.du, a.dvdir, a.dv, a.dcp, d.B, d.T, d.H, d.Tp);
+      break;
+    case 3:
+      hipLaunchKernelGGL((wgrad_gemm_kernel<E, D>), dim3(d.H * d.L * 2 * NS), dim3(WG_NT), 0, s,
+                         a.dKl, a.dP, a.u, a.part, d.B, d.H, d.L, d.Tp, NS);
+      break;
+    default: {
+      const long total = 2 * nw + (long)d.H * d.L * D + (long)d.H * D * 4;
+      const unsigned grid = (unsigned)((total + 255) / 256 < 8192 ? (total + 255) / 256 : 8192);
+      hipLaunchKernelGGL(wgrad_reduce_kernel, dim3(grid), dim3(256), 0, s, a.part, a.dwbp, a.dcp,
+                         a.dWk_o, a.dWp_o, a.dwbeta_o, a.dconv_o, d.B, d.H, d.L, D, NS, ntiles);
+    }
+  }
   return hipGetLastError();
 }
 
@@ -534,21 +542,21 @@ int refine_bwd_splits(const Dims& d) {
 }
 
 template <typename E>
-hipError_t launch_refine_bwd(const Dims& d, const RefineBwdArgs<E>& a, hipStream_t s) {
+hipError_t launch_refine_bwd(const Dims& d, const RefineBwdArgs<E>& a, int stage, hipStream_t s) {
   if (d.L == 0) return hipSuccess;
   const int NS = refine_bwd_splits(d);
   switch (d.D) {
-    case 16: return refine_bwd_d<E, 16>(d, a, NS, s);
-    case 32: return refine_bwd_d<E, 32>(d, a, NS, s);
-    case 64: return refine_bwd_d<E, 64>(d, a, NS, s);
+    case 16: return refine_bwd_d<E, 16>(d, a, NS, stage, s);
+    case 32: return refine_bwd_d<E, 32>(d, a, NS, stage, s);
+    case 64: return refine_bwd_d<E, 64>(d, a, NS, stage, s);
     case 128:
-      if constexpr (sizeof(E) == 2) return refine_bwd_d<E, 128>(d, a, NS, s);
+      if constexpr (sizeof(E) == 2) return refine_bwd_d<E, 128>(d, a, NS, stage, s);
       break;
   }
   return hipErrorInvalidValue;
 }
 
-template hipError_t launch_refine_bwd<bf16>(const Dims&, const RefineBwdArgs<bf16>&, hipStream_t);
-template hipError_t launch_refine_bwd<float>(const Dims&, const RefineBwdArgs<float>&, hipStream_t);
+template hipError_t launch_refine_bwd<bf16>(const Dims&, const RefineBwdArgs<bf16>&, int, hipStream_t);
+template hipError_t launch_refine_bwd<float>(const Dims&, const RefineBwdArgs<float>&, int, hipStream_t);
 
 }  // namespace prism
