@@ -287,10 +287,40 @@ template <typename T> constexpr int ldpad(int n) { return n + 16 / (int)sizeof(T
 // --------------------------------------------------------------------------
 // math
 // --------------------------------------------------------------------------
-__device__ inline float gelu_erf(float z) { return 0.5f * z * (1.0f + erff(z * 0.70710678118654752f)); }
+// Standard normal CDF Phi(z) = (1 + erf(z / sqrt 2)) / 2, with erf from
+// Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26:
+//   erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
+//   t = 1 / (1 + p x), x >= 0, |error| <= 1.5e-7;  erf(-x) = -erf(x).
+// One exp and one reciprocal; e = exp(-z^2 / 2) is returned for reuse.
+__device__ inline float normal_cdf(float z, float& e) {
+  const float x = fabsf(z) * 0.70710678118654752f;
+  const float t = __frcp_rn(fmaf(0.3275911f, x, 1.0f));
+  float poly = fmaf(1.061405429f, t, -1.453152027f);
+  poly = fmaf(poly, t, 1.421413741f);
+  poly = fmaf(poly, t, -0.284496736f);
+  poly = fmaf(poly, t, 0.254829592f);
+  poly *= t;
+  e = __expf(-x * x);
+  const float erf_abs = 1.0f - poly * e;
+  return 0.5f + copysignf(0.5f * erf_abs, z);
+}
+// GELU(z) = z Phi(z) (exact-erf form, to the accuracy above)
+__device__ inline float gelu_erf(float z) {
+  float e;
+  return z * normal_cdf(z, e);
+}
+// d/dz GELU = Phi(z) + z phi(z), phi(z) = exp(-z^2/2) / sqrt(2 pi)
 __device__ inline float gelu_erf_grad(float z) {
-  return 0.5f * (1.0f + erff(z * 0.70710678118654752f)) +
-         z * 0.39894228040143268f * __expf(-0.5f * z * z);
+  float e;
+  const float c = normal_cdf(z, e);
+  return c + z * 0.39894228040143268f * e;
+}
+// both at once
+__device__ inline void gelu_and_grad(float z, float& g, float& dg) {
+  float e;
+  const float c = normal_cdf(z, e);
+  g = z * c;
+  dg = c + z * 0.39894228040143268f * e;
 }
 __device__ inline float sigmoidf(float x) { return 1.0f / (1.0f + __expf(-x)); }
 

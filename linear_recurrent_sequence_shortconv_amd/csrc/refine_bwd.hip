@@ -57,6 +57,8 @@ __global__ __launch_bounds__(RB_NT) void refine_bwd_kernel(
   __shared__ float gsum[4][RB_TT];
   __shared__ float dlog[RB_TT];
   __shared__ float wbs[2][D];
+  __shared__ __attribute__((aligned(16))) E wbl[8 * D];      // w_beta^(l) rows of this head
+  __shared__ float ctp[D * 4];                               // conv taps of this head
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int th = wave >> 2, fq = wave & 3;     // token half, feature group
@@ -72,6 +74,9 @@ __global__ __launch_bounds__(RB_NT) void refine_bwd_kernel(
   const long bh = (long)b * H + h;
   const E* ch = conv + (long)h * D * 4;
 
+  for (int e = tid; e < L * (D / VN); e += RB_NT)
+    st16(wbl + e * VN, ld16(wbeta + (long)h * L * D + e * VN));
+  for (int e = tid; e < D * 4; e += RB_NT) ctp[e] = to_f(ch[e]);
   for (int e = tid; e < (RB_TT + 3) * (D / VN); e += RB_NT) {
     const int r = e / (D / VN), c = (e % (D / VN)) * VN;
     const int t = t0 - 3 + r;
@@ -85,7 +90,7 @@ __global__ __launch_bounds__(RB_NT) void refine_bwd_kernel(
     float u = 0.f;
     if (t0 + t < T) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) u += to_f(ch[f * 4 + j]) * to_f(vbuf[(t + 3 - j) * D + f]);
+      for (int j = 0; j < 4; ++j) u += ctp[f * 4 + j] * to_f(vbuf[(t + 3 - j) * D + f]);
     }
     const E uh = to_t<E>(u);
     ubuf[t * LD + f] = uh;
@@ -100,7 +105,7 @@ __global__ __launch_bounds__(RB_NT) void refine_bwd_kernel(
   if (tid < RB_TT * 4) {
     const int t = tid >> 2, part = tid & 3;
     for (int l = 0; l < L; ++l) {
-      const E* wb = wbeta + ((long)h * L + l) * D;
+      const E* wb = wbl + l * D;
       float s = 0.f;
       for (int f = part * (D / 4); f < (part + 1) * (D / 4); ++f) s += to_f(wb[f]) * to_f(ubuf[t * LD + f]);
       s += __shfl_xor(s, 1);
@@ -117,7 +122,7 @@ __global__ __launch_bounds__(RB_NT) void refine_bwd_kernel(
     const int f = 16 * n + (lane & 15);
     float tp[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) tp[j] = (n < NFT) ? to_f(ch[f * 4 + j]) : 0.f;
+    for (int j = 0; j < 4; ++j) tp[j] = (n < NFT) ? ctp[f * 4 + j] : 0.f;
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -141,6 +146,13 @@ __global__ __launch_bounds__(RB_NT) void refine_bwd_kernel(
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int nn = 0; nn < FPW; ++nn) acc[m][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+    typename Mfma<E>::frag bws[FPW][D / KS];
+#pragma unroll
+    for (int nn = 0; nn < FPW; ++nn)
+#pragma unroll
+      for (int kk = 0; kk < D / KS; ++kk)
+        if (fq + 4 * nn < NFT) bws[nn][kk] = load_frag<E, true>(W, D, 16 * (fq + 4 * nn), kk * KS, lane);
+#pragma unroll
     for (int k0 = 0; k0 < D; k0 += KS) {
       typename Mfma<E>::frag a[2], al[2];
 #pragma unroll
@@ -152,7 +164,7 @@ __global__ __launch_bounds__(RB_NT) void refine_bwd_kernel(
       for (int nn = 0; nn < FPW; ++nn) {
         const int n = fq + 4 * nn;
         if (n < NFT) {
-          const typename Mfma<E>::frag bw = load_frag<E, true>(W, D, 16 * n, k0, lane);
+          const typename Mfma<E>::frag bw = bws[nn][k0 / KS];
 #pragma unroll
           for (int m = 0; m < 2; ++m) {
             acc[m][nn] = Mfma<E>::mma(a[m], bw, acc[m][nn]);
@@ -164,6 +176,13 @@ __global__ __launch_bounds__(RB_NT) void refine_bwd_kernel(
   };
   // acc += X W  where X is an LDS row tile [t][i] and WT[j][i] = W[i][j]
   auto project_t = [&](const E* X, const E* WT, f32x4 (&acc)[2][FPW]) {
+    typename Mfma<E>::frag bws[FPW][D / KS];
+#pragma unroll
+    for (int nn = 0; nn < FPW; ++nn)
+#pragma unroll
+      for (int kk = 0; kk < D / KS; ++kk)
+        if (fq + 4 * nn < NFT) bws[nn][kk] = load_frag<E, true>(WT, D, 16 * (fq + 4 * nn), kk * KS, lane);
+#pragma unroll
     for (int k0 = 0; k0 < D; k0 += KS) {
       typename Mfma<E>::frag a[2];
 #pragma unroll
@@ -172,7 +191,7 @@ __global__ __launch_bounds__(RB_NT) void refine_bwd_kernel(
       for (int nn = 0; nn < FPW; ++nn) {
         const int n = fq + 4 * nn;
         if (n < NFT) {
-          const typename Mfma<E>::frag bw = load_frag<E, true>(WT, D, 16 * n, k0, lane);
+          const typename Mfma<E>::frag bw = bws[nn][k0 / KS];
 #pragma unroll
           for (int m = 0; m < 2; ++m) acc[m][nn] = Mfma<E>::mma(a[m], bw, acc[m][nn]);
         }
@@ -218,8 +237,8 @@ __global__ __launch_bounds__(RB_NT) void refine_bwd_kernel(
     const float* dwl = dWl + lrow * D;
     f32x4 p[2][FPW];
     project(Wp + ((long)h * L + l) * D * D, p);
-    float dz[2][FPW][4];
-    // gate gradient: sum over features of delta . dw (this wave's part)
+    // delta = GELU(z) and GELU'(z) once per element; gate gradient sum_f delta dw
+    float dl_[2][FPW][4], dg_[2][FPW][4], dw_[2][FPW][4];
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
       f32x4 part = {0.f, 0.f, 0.f, 0.f};
@@ -230,9 +249,10 @@ __global__ __launch_bounds__(RB_NT) void refine_bwd_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int t = 32 * th + 16 * m + 4 * (lane >> 4) + i;
-          const float z = p[m][nn][i] * rs[l][m][nn][i];
+          gelu_and_grad(p[m][nn][i] * rs[l][m][nn][i], dl_[m][nn][i], dg_[m][nn][i]);
           const float dw = (n < NFT && t0 + t < Tp) ? dwl[(long)t * D + f] : 0.f;
-          part[i] += gelu_erf(z) * dw;
+          dw_[m][nn][i] = dw;
+          part[i] += dl_[m][nn][i] * dw;
         }
       }
 #pragma unroll
@@ -262,13 +282,10 @@ __global__ __launch_bounds__(RB_NT) void refine_bwd_kernel(
         for (int i = 0; i < 4; ++i) {
           const int t = 32 * th + 16 * m + 4 * (lane >> 4) + i;
           const float rr = rs[l][m][nn][i];
-          const float z = p[m][nn][i] * rr;
           const bool tin = t0 + t < Tp;    // rows past Tp do not exist
-          const float dwv = tin ? dwl[(long)t * D + f] : 0.f;
           const float dkv = tin ? dkl[(long)t * D + f] : 0.f;
-          const float ddl = gate[l][t] * dwv - a_[m][nn][i];
-          const float dzz = ddl * gelu_erf_grad(z);
-          dz[m][nn][i] = dzz;
+          const float ddl = gate[l][t] * dw_[m][nn][i] - a_[m][nn][i];
+          const float dzz = ddl * dg_[m][nn][i];
           a_[m][nn][i] += dzz * p[m][nn][i];
           const float dp = dzz * rr;
           dpbuf[t * LD + f] = to_t<E>(dp);
@@ -282,7 +299,7 @@ __global__ __launch_bounds__(RB_NT) void refine_bwd_kernel(
     }
     project_t(dpbuf, WpT + ((long)h * L + l) * D * D, du);
     project_t(dkbuf, WkT + ((long)h * L + l) * D * D, du);
-    const E* wb = wbeta + ((long)h * L + l) * D;
+    const E* wb = wbl + l * D;
     // du += dlogit w_beta; dw_beta partial = sum_t dlogit_t u_t
 #pragma unroll
     for (int nn = 0; nn < FPW; ++nn) {
@@ -391,22 +408,43 @@ constexpr int WG_NW = 8;
 constexpr int WG_NT = WG_NW * WAVE;
 constexpr int WG_ROWS = 64;
 
-template <typename E, typename X>
-__device__ inline void load_rows_transposed(E* s, int ld, const X* base, long rowstride_b,
-                                            int Tp, long n0, long N, int D, int tid) {
-  // rows n0 .. n0+63 of a [B][*][Tp][D] tensor (row n -> b = n / Tp, t = n % Tp),
-  // stored transposed: s[f * ld + r]
-  for (int e = tid; e < WG_ROWS * D; e += WG_NT) {
-    const int r = e / D, f = e % D;
-    const long n = n0 + r;
-    float x = 0.f;
-    if (n < N) {
-      const long bb = n / Tp, t = n % Tp;
-      x = to_f(base[bb * rowstride_b + t * D + f]);
+// One 64-row chunk of a [B][*][Tp][D] tensor (row n -> b = n / Tp, t = n % Tp)
+// read as 16-byte vectors into registers (coalesced), later stored
+// transposed into LDS: s[f * ld + r].
+template <typename E, typename X, int D>
+struct RowChunk {
+  static constexpr int VN = 16 / (int)sizeof(X);
+  static constexpr int NV = WG_ROWS * D / VN;               // vectors per chunk
+  static constexpr int PER = (NV + WG_NT - 1) / WG_NT;      // vectors per thread
+  uint4 v[PER];
+  __device__ inline void load(const X* base, long rowstride_b, int Tp, long n0, long nend, int tid) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int e = tid + p * WG_NT;
+      v[p] = uint4{0u, 0u, 0u, 0u};
+      if (e < NV) {
+        const int r = e / (D / VN), c = (e % (D / VN)) * VN;
+        const long n = n0 + r;
+        if (n < nend) {
+          const long bb = n / Tp, t = n % Tp;
+          v[p] = ld16(base + bb * rowstride_b + t * D + c);
+        }
+      }
     }
-    s[f * ld + r] = to_t<E>(x);
   }
-}
+  __device__ inline void store_t(E* s, int ld, int tid) const {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int e = tid + p * WG_NT;
+      if (e < NV) {
+        const int r = e / (D / VN), c = (e % (D / VN)) * VN;
+        const X* x = reinterpret_cast<const X*>(&v[p]);
+#pragma unroll
+        for (int j = 0; j < VN; ++j) s[(c + j) * ld + r] = to_t<E>(to_f(x[j]));
+      }
+    }
+  }
+};
 
 template <typename E, int D>
 __global__ __launch_bounds__(WG_NT) void wgrad_gemm_kernel(const float* __restrict__ dKl,
@@ -432,13 +470,25 @@ __global__ __launch_bounds__(WG_NT) void wgrad_gemm_kernel(const float* __restri
   const float* xk = dKl + (((long)h * L + l) * Tp) * D;
   const E* xp = dP + (((long)h * L + l) * Tp) * D;
   const E* ub = u + ((long)h * Tp) * D;
+  RowChunk<E, float, D> xf;
+  RowChunk<E, E, D> xe, uu;
+  // software pipeline: chunk n0 + 64 is fetched while chunk n0 is multiplied
+  if (n_begin < n_end) {
+    if (which == 0) xf.load(xk, xs_b, Tp, n_begin, n_end, tid);
+    else xe.load(xp, xs_b, Tp, n_begin, n_end, tid);
+    uu.load(ub, us_b, Tp, n_begin, n_end, tid);
+  }
   for (long n0 = n_begin; n0 < n_end; n0 += WG_ROWS) {
-    if (which == 0)
-      load_rows_transposed<E, float>(Xt, LTT, xk, xs_b, Tp, n0, n_end, D, tid);
-    else
-      load_rows_transposed<E, E>(Xt, LTT, xp, xs_b, Tp, n0, n_end, D, tid);
-    load_rows_transposed<E, E>(Ut, LTT, ub, us_b, Tp, n0, n_end, D, tid);
+    if (which == 0) xf.store_t(Xt, LTT, tid);
+    else xe.store_t(Xt, LTT, tid);
+    uu.store_t(Ut, LTT, tid);
     __syncthreads();
+    const long nn = n0 + WG_ROWS;
+    if (nn < n_end) {
+      if (which == 0) xf.load(xk, xs_b, Tp, nn, n_end, tid);
+      else xe.load(xp, xs_b, Tp, nn, n_end, tid);
+      uu.load(ub, us_b, Tp, nn, n_end, tid);
+    }
     gemm_acc<E, D, D, WG_ROWS, WG_NW, true, true>(acc, Xt, LTT, Ut, LTT, wave, lane);
     __syncthreads();
   }

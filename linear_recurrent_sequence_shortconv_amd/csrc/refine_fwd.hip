@@ -37,14 +37,17 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
   constexpr int NK = D / KS;
   constexpr int VN = 16 / sizeof(E);
 
-  __shared__ E vbuf[(RF_TT + 3) * D];
+  // v rows (t0-3 .. t0+63) until the residual is formed, then the k^(l) staging tile
+  constexpr int VB = cmax((RF_TT + 3) * D, RF_TT * LD);
+  __shared__ __attribute__((aligned(16))) E vbuf[VB];
+  E* obk = vbuf;
   __shared__ __attribute__((aligned(16))) E ubuf[RF_TT * LD];
   // bf16 only: u - bf16(u), so that p^(l) = W_p^(l) (u_hi + u_lo) is fp32-accurate
   // (the GELU chain amplifies errors in p; k^(l) uses u_hi alone)
   __shared__ __attribute__((aligned(16))) E ulo[sizeof(E) == 2 ? RF_TT * LD : 16];
-  __shared__ __attribute__((aligned(16))) E obk[RF_TT * LD];
   __shared__ __attribute__((aligned(16))) E obw[RF_TT * LD];
   __shared__ float gate[8][RF_TT];
+  __shared__ __attribute__((aligned(16))) E wbs[8 * D];   // w_beta^(l) rows of this head
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ntiles = Tp / RF_TT + ((Tp % RF_TT) ? 1 : 0);
@@ -58,6 +61,9 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
   const long tok_stride = (long)H * D;
   const E* vseq = v + ((long)b * T * H + h) * D;       // row t at vseq + t * tok_stride
 
+  // ---- w_beta rows of this head (L x D) ----
+  for (int e = tid; e < L * (D / VN); e += RF_NT)
+    st16(wbs + e * VN, ld16(wbeta + (long)h * L * D + e * VN));
   // ---- v rows t0-3 .. t0+63 (zeros outside [0, T)) ----
   for (int e = tid; e < (RF_TT + 3) * (D / VN); e += RF_NT) {
     const int r = e / (D / VN), c = (e % (D / VN)) * VN;
@@ -70,12 +76,17 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
 
   // ---- anchor u (fp32 math, stored as the MFMA operand type); pad tokens u = 0 ----
   const E* ch = conv + (long)h * D * 4;
+  // RF_NT is a multiple of D: this thread always handles feature f = tid % D
+  static_assert(RF_NT % D == 0, "feature per thread");
+  float ctap[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) ctap[j] = to_f(ch[(tid % D) * 4 + j]);
   for (int e = tid; e < RF_TT * D; e += RF_NT) {
     const int t = e / D, f = e % D;
     float u = 0.f;
     if (t0 + t < T) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) u += to_f(ch[f * 4 + j]) * to_f(vbuf[(t + 3 - j) * D + f]);
+      for (int j = 0; j < 4; ++j) u += ctap[j] * to_f(vbuf[(t + 3 - j) * D + f]);
     }
     const E uh = to_t<E>(u);
     ubuf[t * LD + f] = uh;
@@ -87,7 +98,7 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
   {
     const int t = tid >> 2, part = tid & 3;
     for (int l = 0; l < L; ++l) {
-      const E* wb = wbeta + ((long)h * L + l) * D;
+      const E* wb = wbs + l * D;
       float s = 0.f;
       for (int f = part * (D / 4); f < (part + 1) * (D / 4); ++f) s += to_f(wb[f]) * to_f(ubuf[t * LD + f]);
       s += __shfl_xor(s, 1);
@@ -132,47 +143,57 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
   E* Wlseq = Wl + (((long)b * H + h) * L) * Tp * D;
   const int nvalid = min(RF_TT, Tp - t0);
 
-  for (int l = 0; l < L; ++l) {
-    const E* wk = Wk + ((long)h * L + l) * D * D;
-    const E* wp = Wp + ((long)h * L + l) * D * D;
-    f32x4 ak[4][FPW], ap[4][FPW];
+  // Per step l: gain pass p = W_p (u_hi + u_lo) -> chain -> w; direction pass
+  // k = W_k u_hi.  Weight fragments of the next pass are requested before the
+  // current pass's arithmetic so their latency overlaps it.
+  typedef typename Mfma<E>::frag Frag;
+  auto load_w = [&](const E* W, Frag (&bw)[FPW][NK]) {
+#pragma unroll
+    for (int nn = 0; nn < FPW; ++nn) {
+      const int n = wave + RF_NW * nn;
+#pragma unroll
+      for (int kk = 0; kk < NK; ++kk)
+        if (n < NFT) bw[nn][kk] = load_frag<E, true>(W, D, 16 * n, kk * KS, lane);
+    }
+  };
+  auto gemm = [&](const Frag (&bw)[FPW][NK], bool with_lo, f32x4 (&acc)[4][FPW]) {
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
-      for (int nn = 0; nn < FPW; ++nn) {
-        ak[m][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
-        ap[m][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
-      }
-#pragma unroll 2
+      for (int nn = 0; nn < FPW; ++nn) acc[m][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
-      const int k0 = kk * KS;
-      typename Mfma<E>::frag a[4], al[4], bk[FPW], bp[FPW];
+      Frag a[4];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        a[m] = load_frag<E, true>(ubuf, LD, 16 * m, k0, lane);
-        if constexpr (sizeof(E) == 2) al[m] = load_frag<E, true>(ulo, LD, 16 * m, k0, lane);
-      }
+      for (int m = 0; m < 4; ++m) a[m] = load_frag<E, true>(ubuf, LD, 16 * m, kk * KS, lane);
 #pragma unroll
-      for (int nn = 0; nn < FPW; ++nn) {
-        const int n = wave + RF_NW * nn;
-        if (n < NFT) {
-          bk[nn] = load_frag<E, true>(wk, D, 16 * n, k0, lane);
-          bp[nn] = load_frag<E, true>(wp, D, 16 * n, k0, lane);
+      for (int nn = 0; nn < FPW; ++nn)
+        if (wave + RF_NW * nn < NFT) {
+#pragma unroll
+          for (int m = 0; m < 4; ++m) acc[m][nn] = Mfma<E>::mma(a[m], bw[nn][kk], acc[m][nn]);
         }
-      }
+      if constexpr (sizeof(E) == 2) {
+        if (with_lo) {
 #pragma unroll
-      for (int nn = 0; nn < FPW; ++nn) {
-        const int n = wave + RF_NW * nn;
-        if (n < NFT) {
+          for (int m = 0; m < 4; ++m) a[m] = load_frag<E, true>(ulo, LD, 16 * m, kk * KS, lane);
 #pragma unroll
-          for (int m = 0; m < 4; ++m) {
-            ak[m][nn] = Mfma<E>::mma(a[m], bk[nn], ak[m][nn]);
-            ap[m][nn] = Mfma<E>::mma(a[m], bp[nn], ap[m][nn]);
-            if constexpr (sizeof(E) == 2) ap[m][nn] = Mfma<E>::mma(al[m], bp[nn], ap[m][nn]);
-          }
+          for (int nn = 0; nn < FPW; ++nn)
+            if (wave + RF_NW * nn < NFT) {
+#pragma unroll
+              for (int m = 0; m < 4; ++m) acc[m][nn] = Mfma<E>::mma(a[m], bw[nn][kk], acc[m][nn]);
+            }
         }
       }
     }
+  };
+
+  Frag bw[FPW][NK];
+  if (L > 0) load_w(Wp + (long)h * L * D * D, bw);
+  for (int l = 0; l < L; ++l) {
+    const E* wk = Wk + ((long)h * L + l) * D * D;
+    f32x4 acc[4][FPW];
+    gemm(bw, true, acc);                       // p^(l)
+    load_w(wk, bw);                            // prefetch W_k^(l)
     // residual chain, one step
 #pragma unroll
     for (int m = 0; m < 4; ++m)
@@ -184,12 +205,23 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int t = 16 * m + 4 * (lane >> 4) + i;
-            const float z = ap[m][nn][i] * r[m][nn][i];
-            const float dl = gelu_erf(z);
+            const float dl = gelu_erf(acc[m][nn][i] * r[m][nn][i]);
             r[m][nn][i] -= dl;
-            obk[t * LD + f] = to_t<E>(ak[m][nn][i]);
             obw[t * LD + f] = to_t<E>(gate[l][t] * dl);
           }
+        }
+      }
+    gemm(bw, false, acc);                      // k^(l)
+    if (l + 1 < L) load_w(Wp + ((long)h * L + l + 1) * D * D, bw);   // prefetch W_p^(l+1)
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int nn = 0; nn < FPW; ++nn) {
+        const int n = wave + RF_NW * nn;
+        if (n < NFT) {
+          const int f = 16 * n + (lane & 15);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) obk[(16 * m + 4 * (lane >> 4) + i) * LD + f] = to_t<E>(acc[m][nn][i]);
         }
       }
     __syncthreads();
