@@ -4,12 +4,10 @@
 // o_t = S_t q_t, reading R7).  The same kernel runs the adjoint pass of the
 // backward in reverse chunk order: dS_c = exp(gC_c) dS_{c+1} - dS_{c+1} M_c^T + E_c.
 //
-// Rows of S (the value index) never mix, so the pass is split over 16-row
-// tiles: one wave per (b, h, row tile) carries its 16 x D slice of the state
-// in fp32 registers for the whole sequence; the product with M runs on MFMA
-// with the state cast to the operand type and the matrix read straight from
-// global memory (L2-resident: the D/16 row tiles of one sequence are
-// scheduled on the same XCD).
+// Rows of S (the value index) never mix, so the pass is split over row
+// blocks, each carried in fp32 registers by one workgroup for the whole
+// sequence; the product with M runs on MFMA with the state cast to the
+// operand type.
 #include "prism_common.h"
 #include "prism_internal.h"
 
@@ -21,78 +19,145 @@ namespace prism {
 // Reverse (reverse = 1): X = init (dS_T, or 0), c = NC-1..0, Bm_c = M_c
 //   (X Bm_c^T = X M_c^T), AddT_c = E_c^T; final X -> fin (dS_0).
 // The stored per-chunk matrix is row-major, or transposed when `transposed`.
-template <typename E, int D>
-__global__ __launch_bounds__(64) void state_pass_kernel(const float* __restrict__ init,
-                                                        const E* __restrict__ Bm,
-                                                        const float* __restrict__ AddT,
-                                                        const float* __restrict__ gC,
-                                                        E* __restrict__ Xc, float* __restrict__ fin,
-                                                        int B, int H, int NC, int transposed,
-                                                        int reverse) {
-  constexpr int NTL = D / 16;
+//
+// Rows of the state never mix, so the pass splits into row blocks of RB rows:
+// one workgroup of 8 waves per (b, h, row block) carries its RB x D slice of
+// the state in fp32 registers (spread over the waves).  Each step needs one
+// barrier: the chunk matrix Bm_c and the operand copy of the state live in
+// double-buffered LDS tiles, and the next step's Bm, AddT block and decay are
+// fetched from global memory (L2: the row blocks of one sequence sit on the
+// same XCD) while the current step multiplies.
+constexpr int SP_NW = 8;
+constexpr int SP_NT = SP_NW * WAVE;
+
+template <typename E, int D, int RB>
+__global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restrict__ init,
+                                                           const E* __restrict__ Bm,
+                                                           const float* __restrict__ AddT,
+                                                           const float* __restrict__ gC,
+                                                           E* __restrict__ Xc, float* __restrict__ fin,
+                                                           int B, int H, int NC, int transposed,
+                                                           int reverse) {
   constexpr int LS = ldpad<E>(D);
   constexpr int VN = 16 / sizeof(E);
-  __shared__ __attribute__((aligned(16))) E Ss[16 * LS];
-  const int lane = threadIdx.x;
-  const int nblk = B * H * NTL;
+  constexpr int NV = D * D / VN;                       // 16-byte vectors of Bm_c
+  constexpr int PER = (NV + SP_NT - 1) / SP_NT;
+  constexpr int NVR = RB * D / VN;                     // 16-byte vectors of the row block
+  constexpr int NRB = D / RB;
+  typedef Tiling<RB, D, SP_NW> TL;
+  __shared__ __attribute__((aligned(16))) E Mb[2][D * LS];
+  __shared__ __attribute__((aligned(16))) E Ss[2][RB * LS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nblk = B * H * NRB;
   const int bid = xcd_swizzle(blockIdx.x, nblk);
-  const int rt = bid % NTL, bh = bid / NTL;
-  const int r0 = 16 * rt;
-  const int rl = 4 * (lane >> 4);    // first of this lane's 4 rows within the tile
-  const int cl = lane & 15;
+  const int bh = bid / NRB, rb0 = (bid % NRB) * RB;
+  const bool act = TL::active(wave);
+  const int m0 = TL::m0(wave), n0 = TL::n0(wave);
+  const int rl = 4 * (lane >> 4), cl = lane & 15;
 
-  Acc<16, D, 1> S;
+  Acc<RB, D, SP_NW> S;   // this wave's block of the state (rows relative to rb0)
   S.zero();
-  if (init) {
+  if (init && act) {
 #pragma unroll
-    for (int j = 0; j < NTL; ++j)
+    for (int i = 0; i < TL::RM; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) S.v[0][j][i] = init[((long)bh * D + r0 + rl + i) * D + 16 * j + cl];
+      for (int j = 0; j < TL::RN; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          S.v[i][j][r] = init[((long)bh * D + rb0 + m0 + 16 * i + rl + r) * D + n0 + 16 * j + cl];
   }
+  auto chunk_of = [&](int step) { return reverse ? NC - 1 - step : step; };
+  uint4 mst[PER];                       // next Bm, staged through registers into LDS
+  f32x4 addn[TL::RM][TL::RN];           // next AddT^T block
+  float egn = 0.f;                      // next decay
+  auto fetch = [&](int step) {
+    const long cidx = (long)bh * NC + chunk_of(step);
+    const E* bm = Bm + cidx * D * D;
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int e = tid + p * SP_NT;
+      if (e < NV) mst[p] = ld16(bm + (long)e * VN);
+    }
+    if (act) {
+      const float* ac = AddT + cidx * D * D + rb0;
+#pragma unroll
+      for (int i = 0; i < TL::RM; ++i)
+#pragma unroll
+        for (int j = 0; j < TL::RN; ++j)
+          addn[i][j] = *reinterpret_cast<const f32x4*>(ac + (long)(n0 + 16 * j + cl) * D + m0 + 16 * i + rl);
+    }
+    egn = expf(gC[cidx]);
+  };
+  auto stage = [&](E* dst) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int e = tid + p * SP_NT;
+      if (e < NV) {
+        const int r = e / (D / VN), c = (e % (D / VN)) * VN;
+        st16(dst + r * LS + c, mst[p]);
+      }
+    }
+  };
+  fetch(0);
+  stage(Mb[0]);
   for (int step = 0; step < NC; ++step) {
-    const int c = reverse ? NC - 1 - step : step;
-    const long cidx = (long)bh * NC + c;
+    const int buf = step & 1;
+    const long cidx = (long)bh * NC + chunk_of(step);
+    f32x4 addc[TL::RM][TL::RN];
 #pragma unroll
-    for (int j = 0; j < NTL; ++j)
+    for (int i = 0; i < TL::RM; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Ss[(rl + i) * LS + 16 * j + cl] = to_t<E>(S.v[0][j][i]);
+      for (int j = 0; j < TL::RN; ++j) addc[i][j] = addn[i][j];
+    const float egc = egn;
+    if (act) {   // state -> operand copy
+#pragma unroll
+      for (int i = 0; i < TL::RM; ++i)
+#pragma unroll
+        for (int j = 0; j < TL::RN; ++j)
+#pragma unroll
+          for (int r = 0; r < 4; ++r)
+            Ss[buf][(m0 + 16 * i + rl + r) * LS + n0 + 16 * j + cl] = to_t<E>(S.v[i][j][r]);
+    }
+    // Ss[buf] and Mb[buf] complete; every wave is past step-1, so the other
+    // buffers are free to refill
     __syncthreads();
+    if (step + 1 < NC) fetch(step + 1);
     E* Xcc = Xc + cidx * D * D;
     if (!transposed) {
-      for (int e = lane; e < 16 * (D / VN); e += 64) {
-        const int r = e / (D / VN), cc = (e % (D / VN)) * VN;
-        st16(Xcc + (long)(r0 + r) * D + cc, ld16(Ss + r * LS + cc));
+      for (int e = tid; e < NVR; e += SP_NT) {
+        const int r = e / (D / VN), c = (e % (D / VN)) * VN;
+        st16(Xcc + (long)(rb0 + r) * D + c, ld16(Ss[buf] + r * LS + c));
       }
     } else {
-      for (int kk = lane; kk < D; kk += 64) {
+      for (int e = tid; e < NVR; e += SP_NT) {
+        const int kk = e / (RB / VN), r0 = (e % (RB / VN)) * VN;
+        E tmp[VN];
 #pragma unroll
-        for (int p = 0; p < 16 / VN; ++p) {
-          E tmp[VN];
-#pragma unroll
-          for (int r = 0; r < VN; ++r) tmp[r] = Ss[(p * VN + r) * LS + kk];
-          uint4 pk;
-          __builtin_memcpy(&pk, tmp, 16);
-          st16(Xcc + (long)kk * D + r0 + p * VN, pk);
-        }
+        for (int r = 0; r < VN; ++r) tmp[r] = Ss[buf][(r0 + r) * LS + kk];
+        uint4 pk;
+        __builtin_memcpy(&pk, tmp, 16);
+        st16(Xcc + (long)kk * D + rb0 + r0, pk);
       }
     }
-    Acc<16, D, 1> P;
+    Acc<RB, D, SP_NW> P;
     P.zero();
-    gemm_acc<E, 16, D, D, 1, true, true>(P, Ss, LS, Bm + cidx * D * D, D, 0, lane);
-    const float eg = expf(gC[cidx]);
-    const float* Ac = AddT + cidx * D * D;
+    gemm_acc<E, RB, D, D, SP_NW, true, true>(P, Ss[buf], LS, Mb[buf], LS, wave, lane);
+    if (act) {
 #pragma unroll
-    for (int j = 0; j < NTL; ++j) {
-      const f32x4 av = *reinterpret_cast<const f32x4*>(Ac + (long)(16 * j + cl) * D + r0 + rl);
-      S.v[0][j] = eg * S.v[0][j] - P.v[0][j] + av;
+      for (int i = 0; i < TL::RM; ++i)
+#pragma unroll
+        for (int j = 0; j < TL::RN; ++j) S.v[i][j] = egc * S.v[i][j] - P.v[i][j] + addc[i][j];
     }
-    __syncthreads();
+    if (step + 1 < NC) stage(Mb[buf ^ 1]);
   }
-  if (fin) {
+  if (fin && act) {
 #pragma unroll
-    for (int j = 0; j < NTL; ++j)
+    for (int i = 0; i < TL::RM; ++i)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fin[((long)bh * D + r0 + rl + i) * D + 16 * j + cl] = S.v[0][j][i];
+      for (int j = 0; j < TL::RN; ++j)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          fin[((long)bh * D + rb0 + m0 + 16 * i + rl + r) * D + n0 + 16 * j + cl] = S.v[i][j][r];
   }
 }
 
@@ -100,9 +165,11 @@ template <typename E, int D>
 static hipError_t state_launch_d(const Dims& d, const float* init, const E* Bm, const float* AddT,
                                  const float* gC, E* Xc, float* fin, bool tr, bool rev,
                                  hipStream_t s) {
-  const int nblk = d.B * d.H * (D / 16);
-  hipLaunchKernelGGL((state_pass_kernel<E, D>), dim3(nblk), dim3(64), 0, s, init, Bm, AddT, gC, Xc,
-                     fin, d.B, d.H, d.NC, tr ? 1 : 0, rev ? 1 : 0);
+  // row blocks of 64 rows at D = 128 (two workgroups per sequence), whole
+  // state below that
+  constexpr int RB = D > 64 ? 64 : D;
+  hipLaunchKernelGGL((state_pass_kernel<E, D, RB>), dim3(d.B * d.H * (D / RB)), dim3(SP_NT), 0, s,
+                     init, Bm, AddT, gC, Xc, fin, d.B, d.H, d.NC, tr ? 1 : 0, rev ? 1 : 0);
   return hipGetLastError();
 }
 
