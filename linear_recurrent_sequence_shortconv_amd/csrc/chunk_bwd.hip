@@ -343,7 +343,7 @@ struct CB2Lds {
   static constexpr int S_AF = F_V + SZ_R;
   static constexpr int S_TF = S_AF + SZ_F;
   static constexpr int S_XS = S_TF + SZ_F;
-  static constexpr int S_TBB = S_XS + 3 * 256 * 4;
+  static constexpr int S_TBB = S_XS + inv_scratch_floats(C) * 4;
   static constexpr int S_TBE = S_TBB + SZ_CC;
   static constexpr int S_END = S_TBE + SZ_CC;
   // phase "R0" (written after the U / Wk products have read everything above):
@@ -363,9 +363,6 @@ struct CB2Lds {
   static_assert(Z_F + SZ_F <= P_XB, "dG0 must not overlap P1");
   static constexpr int TOTAL = cmax(P_END, cmax(Z_B + SZ_CC, cmax(S_END, F_END)));
 };
-
-template <int C, int NT>
-__device__ void invert_unit_lower_b(const float* A, float* Tm, float* Xs, int tid);
 
 template <typename E, int D, int C>
 __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
@@ -469,7 +466,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
       }
     });
     __syncthreads();
-    invert_unit_lower_b<C, NT>(Af, Tf, Xs, tid);
+    invert_unit_lower<C, NW>(Af, Tf, Xs, tid);
     for (int e = tid; e < C * C; e += NT) {
       const int t = e / C, i = e % C;
       const float tv = Tf[t * LA + i];
@@ -959,46 +956,6 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
       if (lane + off < 64) s += y;
     }
     if (lane < nval) dalpha[row0 + (long)lane * H] = s / al[lane];
-  }
-}
-
-// T = (I + A)^{-1}; same algorithm as in chunk_fwd.hip (16 x 16 diagonal
-// blocks by substitution, then block rows).  Ends with a barrier.
-template <int C, int NT>
-__device__ void invert_unit_lower_b(const float* A, float* Tm, float* Xs, int tid) {
-  constexpr int NB = C / 16, LA = C + 1;
-  for (int e = tid; e < C * C; e += NT) {
-    const int r = e / C, cc = e % C;
-    if (cc > r) Tm[r * LA + cc] = 0.f;
-  }
-  if (tid < NB * 16) {
-    const int base = 16 * (tid / 16), col = tid % 16;
-    float* Tc = Tm + base * LA + base + col;
-    const float* Ab = A + base * LA + base;
-#pragma unroll 1
-    for (int r = col; r < 16; ++r) {
-      float s = (r == col) ? 1.f : 0.f;
-#pragma unroll 1
-      for (int m = col; m < r; ++m) s -= Ab[r * LA + m] * Tc[m * LA];
-      Tc[r * LA] = s;
-    }
-  }
-  __syncthreads();
-  for (int i = 1; i < NB; ++i) {
-    for (int e = tid; e < i * 256; e += NT) {
-      const int j = e / 256, r = (e / 16) % 16, cc = e % 16;
-      float s = 0.f;
-      for (int m = 16 * j; m < 16 * i; ++m) s += A[(16 * i + r) * LA + m] * Tm[m * LA + 16 * j + cc];
-      Xs[e] = s;
-    }
-    __syncthreads();
-    for (int e = tid; e < i * 256; e += NT) {
-      const int j = e / 256, r = (e / 16) % 16, cc = e % 16;
-      float s = 0.f;
-      for (int m = 0; m <= r; ++m) s += Tm[(16 * i + r) * LA + 16 * i + m] * Xs[j * 256 + m * 16 + cc];
-      Tm[(16 * i + r) * LA + 16 * j + cc] = -s;
-    }
-    __syncthreads();
   }
 }
 

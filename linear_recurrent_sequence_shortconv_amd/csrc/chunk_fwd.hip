@@ -31,50 +31,6 @@ namespace prism {
 constexpr int CF_NW = 8;
 constexpr int CF_NT = CF_NW * WAVE;
 
-// T = (I + A)^{-1} for strictly lower triangular A (C x C, fp32, leading
-// dimension C + 1).  16 x 16 diagonal blocks by forward substitution, then
-// block rows: T_ij = -T_ii sum_{j<=k<i} A_ik T_kj.  Ends with a barrier.
-template <int C, int NT>
-__device__ void invert_unit_lower(const float* A, float* Tm, float* Xs, int tid) {
-  constexpr int NB = C / 16, LA = C + 1;
-  for (int e = tid; e < C * C; e += NT) {
-    const int r = e / C, cc = e % C;
-    if (cc > r) Tm[r * LA + cc] = 0.f;
-  }
-  if (tid < NB * 16) {
-    // one lane per column of a 16 x 16 diagonal block; the column lives in
-    // LDS (only this lane touches it), row by row:
-    //   T[r][c] = delta_rc - sum_{c <= m < r} A[r][m] T[m][c]
-    const int base = 16 * (tid / 16), col = tid % 16;
-    float* Tc = Tm + base * LA + base + col;
-    const float* Ab = A + base * LA + base;
-#pragma unroll 1
-    for (int r = col; r < 16; ++r) {
-      float s = (r == col) ? 1.f : 0.f;
-#pragma unroll 1
-      for (int m = col; m < r; ++m) s -= Ab[r * LA + m] * Tc[m * LA];
-      Tc[r * LA] = s;
-    }
-  }
-  __syncthreads();
-  for (int i = 1; i < NB; ++i) {
-    for (int e = tid; e < i * 256; e += NT) {
-      const int j = e / 256, r = (e / 16) % 16, cc = e % 16;
-      float s = 0.f;
-      for (int m = 16 * j; m < 16 * i; ++m) s += A[(16 * i + r) * LA + m] * Tm[m * LA + 16 * j + cc];
-      Xs[e] = s;
-    }
-    __syncthreads();
-    for (int e = tid; e < i * 256; e += NT) {
-      const int j = e / 256, r = (e / 16) % 16, cc = e % 16;
-      float s = 0.f;
-      for (int m = 0; m <= r; ++m) s += Tm[(16 * i + r) * LA + 16 * i + m] * Xs[j * 256 + m * 16 + cc];
-      Tm[(16 * i + r) * LA + 16 * j + cc] = -s;
-    }
-    __syncthreads();
-  }
-}
-
 template <typename E, int D, int C>
 struct ChunkLds {
   static constexpr int LR = ldpad<E>(D);     // [C][LR]: C rows of D
@@ -102,7 +58,7 @@ struct ChunkLds {
   static constexpr int T_AF = C_TB + SZ_CC;
   static constexpr int T_TF = T_AF + SZ_F;
   static constexpr int T_XS = T_TF + SZ_F;
-  static constexpr int T_END = T_XS + 3 * 256 * 4;
+  static constexpr int T_END = T_XS + inv_scratch_floats(C) * 4;
   // phase C
   static constexpr int C_KTBE = C_TB + SZ_CC;   // later Wk^T
   static constexpr int C_KTD = C_KTBE + SZ_T;
@@ -147,6 +103,15 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
   const E* kc = k + row0 * D;
   const E* vc = v + row0 * D;
 
+  // the first refinement step's K_l, W_l tiles are fetched while phase A runs
+  const E* Klb = Kl + (long)bh * L * Tp * D + (long)tb * D;
+  const E* Wlb = Wl + (long)bh * L * Tp * D + (long)tb * D;
+  RegTile<E, C, D, NT> kn, wn;
+  if (L > 0) {
+    kn.load(Klb, D, C, tid);
+    wn.load(Wlb, D, C, tid);
+  }
+
   // ---- phase A: decays and gates; Q, K tiles ----
   if (wave == 0) {
     float lg = 0.f, bv = 0.f;
@@ -188,15 +153,15 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
     E* Wlt = reinterpret_cast<E*>(smem + LY::B_WLT);
     E* F = reinterpret_cast<E*>(smem + LY::B_F);
     E* Rl = reinterpret_cast<E*>(smem + LY::B_RL);
-    const E* Klb = Kl + (long)bh * L * Tp * D + (long)tb * D;
-    const E* Wlb = Wl + (long)bh * L * Tp * D + (long)tb * D;
     for (int l = 0; l < L; ++l) {
-      const E* klc = Klb + (long)l * Tp * D;
-      const E* wlc = Wlb + (long)l * Tp * D;
-      g2s_rows<E, C, D, NT>(Klr, LR, klc, D, C, tid);
-      g2s_rows_transposed<E, C, D, NT>(KltD, LT, klc, D, C, Dv, tid);
-      g2s_rows_transposed<E, C, D, NT>(Wlt, LT, wlc, D, C, nullptr, tid);
+      kn.store_rows(Klr, LR, tid);
+      kn.store_transposed(KltD, LT, Dv, tid);
+      wn.store_transposed(Wlt, LT, nullptr, tid);
       __syncthreads();
+      if (l + 1 < L) {   // next step's tiles are in flight during this step's products
+        kn.load(Klb + (long)(l + 1) * Tp * D, D, C, tid);
+        wn.load(Wlb + (long)(l + 1) * Tp * D, D, C, tid);
+      }
       {
         Acc<C, C, NW> a;   // [i][t] = K_l,i . K_t  ->  F[t][i], i < t
         a.zero();
@@ -230,6 +195,8 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
   }
 
   // ---- phase T: A = diag(beta) (Gam * K K^T)_{i<t};  T = (I + A)^{-1} ----
+  RegTile<E, C, D, NT> vn;   // V rows, in flight during the solve
+  vn.load(vc, ts, nval, tid);
   E* Tb = reinterpret_cast<E*>(smem + LY::C_TB);
   {
     float* Af = reinterpret_cast<float*>(smem + LY::T_AF);
@@ -246,7 +213,7 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
       }
     });
     __syncthreads();
-    invert_unit_lower<C, NT>(Af, Tf, Xs, tid);
+    invert_unit_lower<C, NW>(Af, Tf, Xs, tid);
     for (int e = tid; e < C * C; e += NT) Tb[(e / C) * LT + (e % C)] = to_t<E>(Tf[(e / C) * LA + (e % C)]);
     __syncthreads();
   }
@@ -263,8 +230,10 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
     Ktbe[f * LT + t] = to_t<E>(be[t] * kv);
     KtD[f * LT + t] = to_t<E>(Dv[t] * kv);
   }
-  g2s_rows<E, C, D, NT>(Vr, LR, vc, ts, nval, tid);
+  vn.store_rows(Vr, LR, tid);
   __syncthreads();
+  RegTile<E, C, D, NT> on;   // dO rows (backward mode), in flight during the products below
+  if constexpr (BWD) on.load(dO + row0 * D, ts, nval, tid);
   for_tiles(vacc, wave, lane, [&](int t0, int f, const f32x4& x) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -367,7 +336,7 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
       }
     });
     E* dOt = Vr;
-    g2s_rows_transposed<E, C, D, NT>(dOt, LT, dO + row0 * D, ts, nval, nullptr, tid);
+    on.store_transposed(dOt, LT, nullptr, tid);
     __syncthreads();
     Acc<D, D, NW> ea;   // E[r][n] = sum_t dO[t][r] Qt[t][n]  -> stored as ET[n][r]
     ea.zero();

@@ -163,7 +163,7 @@ BwdWs<E> carve_bwd(const prism::Dims& d, Carve& cv) {
   const size_t bh = (size_t)d.B * d.H;
   const size_t es = sizeof(E);
   const size_t DD = (size_t)d.D * d.D, CD = (size_t)d.C * d.D;
-  const size_t ntiles = (d.Tp + 63) / 64;
+  const size_t ntiles = (d.Tp + prism::kRefineTile - 1) / prism::kRefineTile;
   const size_t L1 = d.L > 0 ? d.L : 1;
   BwdWs<E> w;
   w.Kl = cv.take<E>(bh * d.L * d.Tp * d.D * es);

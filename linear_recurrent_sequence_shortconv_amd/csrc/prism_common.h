@@ -235,6 +235,90 @@ __device__ inline void for_tiles_mut(Acc<M, N, NW>& acc, int wave, int lane, F&&
 }
 
 // --------------------------------------------------------------------------
+// T = (I + A)^{-1} for a strictly lower triangular C x C matrix A (fp32 in
+// LDS, leading dimension C + 1), written to Tm (same layout, zeros above the
+// diagonal).  Xs is scratch of inv_scratch_floats(C) floats.  All NW waves of
+// the workgroup take part; ends with a barrier.
+//  * 16 x 16 diagonal blocks: forward substitution, one lane per column with
+//    the column in registers.  Row r of a column c is
+//    T[r][c] = [r == c] - sum_{m < r} A[r][m] T[m][c]; entries above the
+//    diagonal come out as zero by themselves, so every lane runs the same
+//    unrolled code.
+//  * then block doubling, S = 16, 32, ...: for each pair of S-blocks on the
+//    diagonal, T21 = -T22 (A21 T11), two fp32 MFMA products.
+// --------------------------------------------------------------------------
+constexpr int inv_scratch_floats(int C) { return C >= 32 ? (C / 2) * (C / 2 + 1) : 1; }
+
+template <int C, int S, int NW>
+__device__ inline void invert_double_level(const float* A, float* Tm, float* Xs, int wave, int lane) {
+  constexpr int LA = C + 1, P = C / (2 * S), LX = S + 1;
+  static_assert(NW % P == 0, "waves per block pair");
+  constexpr int NWP = NW / P;
+  const int pr = wave / NWP, w = wave % NWP;
+  const int o = 2 * S * pr;
+  float* X = Xs + pr * S * LX;
+  {
+    Acc<S, S, NWP> x;   // X = A21 T11
+    x.zero();
+    gemm_acc<float, S, S, S, NWP, true, false>(x, A + (o + S) * LA + o, LA, Tm + o * LA + o, LA, w, lane);
+    for_tiles(x, w, lane, [&](int r0, int cc, const f32x4& v) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) X[(r0 + r) * LX + cc] = v[r];
+    });
+  }
+  __syncthreads();
+  {
+    Acc<S, S, NWP> y;   // T21 = -T22 X
+    y.zero();
+    gemm_acc<float, S, S, S, NWP, true, false>(y, Tm + (o + S) * LA + o + S, LA, X, LX, w, lane);
+    for_tiles(y, w, lane, [&](int r0, int cc, const f32x4& v) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Tm[(o + S + r0 + r) * LA + o + cc] = -v[r];
+    });
+  }
+  __syncthreads();
+}
+
+template <int C, int NW>
+__device__ inline void invert_unit_lower(const float* A, float* Tm, float* Xs, int tid) {
+  constexpr int NB = C / 16, LA = C + 1;
+  static_assert(NB >= 1 && NB <= 4 && C % 16 == 0, "C in {16, 32, 48, 64}");
+  const int lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < C * C; e += NW * WAVE) {
+    const int r = e / C, cc = e % C;
+    if (cc > r) Tm[r * LA + cc] = 0.f;
+  }
+  if (wave == 0 && lane < NB * 16) {
+    const int base = 16 * (lane >> 4), col = lane & 15;
+    const float* Ab = A + base * LA + base;
+    // row r + 1 of A is read from LDS while row r is computed; the empty asm
+    // (which takes t[r] and clobbers memory) pins that order, so the reads
+    // are not all hoisted up front with 120 values held in registers
+    float t[16], an[16], ac[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+#pragma unroll
+      for (int m = 0; m < r; ++m) ac[m] = an[m];
+      if (r + 1 < 16) {
+#pragma unroll
+        for (int m = 0; m <= r; ++m) an[m] = Ab[(r + 1) * LA + m];
+      }
+      float s = (r == col) ? 1.f : 0.f;
+#pragma unroll
+      for (int m = 0; m < r; ++m) s = fmaf(-ac[m], t[m], s);
+      t[r] = s;
+      asm volatile("" : "+v"(t[r]) : : "memory");
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (r >= col) Tm[(base + r) * LA + base + col] = t[r];
+  }
+  __syncthreads();
+  if constexpr (C >= 32) invert_double_level<C, 16, NW>(A, Tm, Xs, wave, lane);
+  if constexpr (C >= 64) invert_double_level<C, 32, NW>(A, Tm, Xs, wave, lane);
+}
+
+// --------------------------------------------------------------------------
 // cooperative global <-> LDS tile copies (16-byte vectors)
 // --------------------------------------------------------------------------
 // rows x cols tile of T; global row r at g + r * gstride; LDS row r at s + r * ld.
@@ -268,6 +352,49 @@ __device__ inline void g2s_rows_transposed(T* s, int ld, const T* g, long gstrid
     for (int j = 0; j < VN; ++j) s[(c + j) * ld + r] = to_t<T>(to_f(x[j]) * sc);
   }
 }
+
+// A ROWS x COLS tile of T held in registers as 16-byte vectors spread over
+// NT threads: load() issues the global reads early (software prefetch);
+// store_rows / store_transposed later write it into LDS.  Rows >= nvalid are
+// zeros.
+template <typename T, int ROWS, int COLS, int NT>
+struct RegTile {
+  static constexpr int VN = 16 / (int)sizeof(T);
+  static constexpr int VPR = COLS / VN;
+  static constexpr int NV = ROWS * VPR;
+  static constexpr int PER = (NV + NT - 1) / NT;
+  uint4 v[PER];
+  __device__ inline void load(const T* g, long gstride, int nvalid, int tid) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int e = tid + p * NT;
+      const int r = e / VPR, c = (e % VPR) * VN;
+      v[p] = uint4{0u, 0u, 0u, 0u};
+      if (e < NV && r < nvalid) v[p] = ld16(g + r * gstride + c);
+    }
+  }
+  __device__ inline void store_rows(T* s, int ld, int tid) const {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int e = tid + p * NT;
+      if (e < NV) st16(s + (e / VPR) * ld + (e % VPR) * VN, v[p]);
+    }
+  }
+  // element (r, c) -> s[c * ld + r], times scale[r] (nullptr = 1)
+  __device__ inline void store_transposed(T* s, int ld, const float* scale, int tid) const {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int e = tid + p * NT;
+      if (e < NV) {
+        const int r = e / VPR, c = (e % VPR) * VN;
+        const T* x = reinterpret_cast<const T*>(&v[p]);
+        const float sc = scale ? scale[r] : 1.0f;
+#pragma unroll
+        for (int j = 0; j < VN; ++j) s[(c + j) * ld + r] = to_t<T>(to_f(x[j]) * sc);
+      }
+    }
+  }
+};
 
 // LDS tile -> global rows (first nvalid rows only)
 template <typename T, int ROWS, int COLS, int NT>

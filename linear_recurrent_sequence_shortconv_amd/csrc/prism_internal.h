@@ -75,6 +75,9 @@ template <typename E>
 // stage 0: transpose weights, 1: refine_bwd, 2: conv_bwd, 3: wgrad_gemm, 4: wgrad_reduce
 hipError_t launch_refine_bwd(const Dims& d, const RefineBwdArgs<E>& a, int stage, hipStream_t s);
 int refine_bwd_splits(const Dims& d);   // split count of the weight-gradient GEMM
+// tokens per refinement-backward tile (the per-tile partial sums of dw_beta
+// and of the ShortConv taps have one row per tile)
+constexpr int kRefineTile = 32;
 
 // O = O_loc + Qt S_c^T, written to o [B, T, H, D].
 template <typename E>

@@ -18,8 +18,9 @@
 
 namespace prism {
 
-constexpr int RB_TT = 64;
-constexpr int RB_NW = 8;
+constexpr int RB_TT = kRefineTile;      // tokens per workgroup
+constexpr int RB_TH = RB_TT / 32;       // token groups of 32 (one per 4 waves)
+constexpr int RB_NW = 4 * RB_TH;
 constexpr int RB_NT = RB_NW * WAVE;
 
 // WT[h][l][j][i] = W[h][l][i][j] for W in {Wk, Wp}
@@ -37,7 +38,7 @@ __global__ void transpose_weights_kernel(const E* __restrict__ Wk, const E* __re
 }
 
 template <typename E, int D, int LMAX>
-__global__ __launch_bounds__(RB_NT) void refine_bwd_kernel(
+__global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
     const E* __restrict__ v, const E* __restrict__ conv, const E* __restrict__ Wp,
     const E* __restrict__ WkT, const E* __restrict__ WpT, const E* __restrict__ wbeta,
     const float* __restrict__ dKl, const float* __restrict__ dWl, float* __restrict__ dvdir,
@@ -56,12 +57,12 @@ __global__ __launch_bounds__(RB_NT) void refine_bwd_kernel(
   __shared__ float gate[8][RB_TT];
   __shared__ float gsum[4][RB_TT];
   __shared__ float dlog[RB_TT];
-  __shared__ float wbs[2][D];
+  __shared__ float wbs[RB_TH][D];
   __shared__ __attribute__((aligned(16))) E wbl[8 * D];      // w_beta^(l) rows of this head
   __shared__ float ctp[D * 4];                               // conv taps of this head
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int th = wave >> 2, fq = wave & 3;     // token half, feature group
+  const int th = wave >> 2, fq = wave & 3;     // token group, feature group
   const int ntiles = (Tp + RB_TT - 1) / RB_TT;
   const int nblk = ntiles * B * H;
   const int bid = xcd_swizzle(blockIdx.x, nblk);
@@ -235,13 +236,11 @@ __global__ __launch_bounds__(RB_NT) void refine_bwd_kernel(
     const long lrow = (bh * L + l) * Tp + t0;
     const float* dkl = dKl + lrow * D;
     const float* dwl = dWl + lrow * D;
-    f32x4 p[2][FPW];
-    project(Wp + ((long)h * L + l) * D * D, p);
-    // delta = GELU(z) and GELU'(z) once per element; gate gradient sum_f delta dw
-    float dl_[2][FPW][4], dg_[2][FPW][4], dw_[2][FPW][4];
+    // this step's incoming gradients, issued before the projection so that
+    // their latency overlaps it
+    float dw_[2][FPW][4], dk_[2][FPW][4];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      f32x4 part = {0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int nn = 0; nn < FPW; ++nn) {
         const int n = fq + 4 * nn;
@@ -249,10 +248,26 @@ __global__ __launch_bounds__(RB_NT) void refine_bwd_kernel(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int t = 32 * th + 16 * m + 4 * (lane >> 4) + i;
-          gelu_and_grad(p[m][nn][i] * rs[l][m][nn][i], dl_[m][nn][i], dg_[m][nn][i]);
-          const float dw = (n < NFT && t0 + t < Tp) ? dwl[(long)t * D + f] : 0.f;
-          dw_[m][nn][i] = dw;
-          part[i] += dl_[m][nn][i] * dw;
+          const bool ok = n < NFT && t0 + t < Tp;    // rows past Tp do not exist
+          dw_[m][nn][i] = ok ? dwl[(long)t * D + f] : 0.f;
+          dk_[m][nn][i] = ok ? dkl[(long)t * D + f] : 0.f;
+        }
+      }
+    f32x4 p[2][FPW];
+    project(Wp + ((long)h * L + l) * D * D, p);
+    // GELU'(z) once per element (GELU(z) only enters the gate-gradient sum
+    // sum_f delta dw)
+    float dg_[2][FPW][4];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      f32x4 part = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int nn = 0; nn < FPW; ++nn) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float dl;
+          gelu_and_grad(p[m][nn][i] * rs[l][m][nn][i], dl, dg_[m][nn][i]);
+          part[i] += dl * dw_[m][nn][i];
         }
       }
 #pragma unroll
@@ -282,14 +297,12 @@ __global__ __launch_bounds__(RB_NT) void refine_bwd_kernel(
         for (int i = 0; i < 4; ++i) {
           const int t = 32 * th + 16 * m + 4 * (lane >> 4) + i;
           const float rr = rs[l][m][nn][i];
-          const bool tin = t0 + t < Tp;    // rows past Tp do not exist
-          const float dkv = tin ? dkl[(long)t * D + f] : 0.f;
           const float ddl = gate[l][t] * dw_[m][nn][i] - a_[m][nn][i];
           const float dzz = ddl * dg_[m][nn][i];
           a_[m][nn][i] += dzz * p[m][nn][i];
           const float dp = dzz * rr;
           dpbuf[t * LD + f] = to_t<E>(dp);
-          dkbuf[t * LD + f] = to_t<E>(dkv);
+          dkbuf[t * LD + f] = to_t<E>(dk_[m][nn][i]);
         }
       }
     __syncthreads();
@@ -321,7 +334,12 @@ __global__ __launch_bounds__(RB_NT) void refine_bwd_kernel(
       if (lane < 16) wbs[th][f] = cs;
     }
     __syncthreads();
-    for (int f = tid; f < D; f += RB_NT) dwbp[((long)tile_id * L + l) * D + f] = wbs[0][f] + wbs[1][f];
+    for (int f = tid; f < D; f += RB_NT) {
+      float x = 0.f;
+#pragma unroll
+      for (int g = 0; g < RB_TH; ++g) x += wbs[g][f];
+      dwbp[((long)tile_id * L + l) * D + f] = x;
+    }
     __syncthreads();
   }
   // ---- dv += a, du -= a ----
