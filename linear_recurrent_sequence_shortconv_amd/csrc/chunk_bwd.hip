@@ -156,6 +156,14 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
   g2s_rows<E, C, D, NT>(R1, LR, dO + row0 * D, ts, nval, tid);
   g2s_rows<E, D, D, NT>(X1, LD2, St + cidx * D * D, D, D, tid);
   g2s_rows<E, D, D, NT>(X2, LD2, dSnT + cidx * D * D, D, D, tid);
+  // tiles of the next phase, in flight during the first products: dS_n^T
+  // again (stored transposed, i.e. dS_n row-major), K rows, U^T
+  RegTile<E, D, D, NT, true> dsn;
+  RegTile<E, C, D, NT> kr;
+  RegTile<E, D, C, NT, true> ut;
+  dsn.load(dSnT + cidx * D * D, D, D, tid);
+  kr.load(k + row0 * D, ts, nval, tid);
+  ut.load(UT + cidx * D * C, C, D, tid);
   __syncthreads();
 
   // ---- dQt = dO S  ([t][k] = sum_r dO[t][r] S^T[k][r]);  dM = -S^T dS_n ----
@@ -185,12 +193,19 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
   __syncthreads();
 
   // ---- dS_n (row-major) into X1; K and U rows ----
-  for (int e = tid; e < D * D; e += NT) {
-    const int r = e / D, n = e % D;
-    X1[r * LD2 + n] = X2[n * LD2 + r];
+  dsn.store_transposed(X1, LD2, nullptr, tid);
+  kr.store_rows(R1, LR, tid);
+  ut.store_transposed(R2, LR, nullptr, tid);
+  // the first refinement step's K_l, W_l rows and the Wk^T tile of the last
+  // phase are fetched during the products below
+  RegTile<E, C, D, NT> kl, wl;
+  RegTile<E, D, C, NT, true> wkt;
+  if (L > 0) {
+    const long lrow = (long)bh * L * Tp + tb;
+    kl.load(Kl + lrow * D, D, C, tid);
+    wl.load(Wl + lrow * D, D, C, tid);
   }
-  g2s_rows<E, C, D, NT>(R1, LR, k + row0 * D, ts, nval, tid);
-  g2s_rows_transposed<E, D, C, NT>(R2, LR, UT + cidx * D * C, C, D, nullptr, tid);
+  wkt.load(WkT + cidx * D * C, C, D, tid);
   __syncthreads();
 
   Acc<C, D, NW> dk;   // D-weighted dK:  D (U dS_n + Wk dM)
@@ -230,9 +245,13 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
   // ---- refinement pairs: dW_l += D (K_l dS_n^T), dK_l += D (W_l dS_n) ----
   for (int l = 0; l < L; ++l) {
     const long lrow = ((long)bh * L + l) * Tp + tb;
-    g2s_rows<E, C, D, NT>(R3, LR, Kl + lrow * D, D, C, tid);
-    g2s_rows<E, C, D, NT>(R4, LR, Wl + lrow * D, D, C, tid);
+    kl.store_rows(R3, LR, tid);
+    wl.store_rows(R4, LR, tid);
     __syncthreads();
+    if (l + 1 < L) {
+      kl.load(Kl + (lrow + Tp) * D, D, C, tid);
+      wl.load(Wl + (lrow + Tp) * D, D, C, tid);
+    }
     Acc<C, D, NW> a;
     a.zero();
     gemm_acc<E, C, D, D, NW, true, true>(a, R3, LR, X1, LD2, wave, lane);
@@ -266,7 +285,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
       X2[n * LD2 + k0 + r] = to_t<E>(-x[r]);
     }
   });
-  g2s_rows_transposed<E, D, C, NT>(R3, LR, WkT + cidx * D * C, C, D, nullptr, tid);
+  wkt.store_transposed(R3, LR, nullptr, tid);
   __syncthreads();
   {
     Acc<C, D, NW> a;    // K dM^T: [t][k] = sum_n K[t][n] dM[k][n]

@@ -106,7 +106,7 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
   // the first refinement step's K_l, W_l tiles are fetched while phase A runs
   const E* Klb = Kl + (long)bh * L * Tp * D + (long)tb * D;
   const E* Wlb = Wl + (long)bh * L * Tp * D + (long)tb * D;
-  RegTile<E, C, D, NT> kn, wn;
+  RegTile<E, C, D, NT, true> kn, wn;
   if (L > 0) {
     kn.load(Klb, D, C, tid);
     wn.load(Wlb, D, C, tid);
@@ -232,7 +232,7 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
   }
   vn.store_rows(Vr, LR, tid);
   __syncthreads();
-  RegTile<E, C, D, NT> on;   // dO rows (backward mode), in flight during the products below
+  RegTile<E, C, D, NT, true> on;   // dO rows (backward mode), in flight during the products below
   if constexpr (BWD) on.load(dO + row0 * D, ts, nval, tid);
   for_tiles(vacc, wave, lane, [&](int t0, int f, const f32x4& x) {
 #pragma unroll

@@ -357,40 +357,84 @@ __device__ inline void g2s_rows_transposed(T* s, int ld, const T* g, long gstrid
 // NT threads: load() issues the global reads early (software prefetch);
 // store_rows / store_transposed later write it into LDS.  Rows >= nvalid are
 // zeros.
-template <typename T, int ROWS, int COLS, int NT>
+// TR = false: consecutive threads take consecutive vectors of a row (fully
+//   coalesced reads; for row stores).
+// TR = true: consecutive threads take consecutive row groups of one 16-byte
+//   column block, RG = 2 rows per thread for 2-byte T (1 for 4-byte T), so
+//   the transposed store writes one 32-bit word per column and lane, to
+//   consecutive words: free of LDS bank conflicts.
+template <typename T, int ROWS, int COLS, int NT, bool TR = false>
 struct RegTile {
   static constexpr int VN = 16 / (int)sizeof(T);
   static constexpr int VPR = COLS / VN;
-  static constexpr int NV = ROWS * VPR;
-  static constexpr int PER = (NV + NT - 1) / NT;
-  uint4 v[PER];
+  static constexpr int RG = (TR && sizeof(T) == 2) ? 2 : 1;
+  static constexpr int NG = ROWS / RG;
+  static constexpr int NU = NG * VPR;                 // units of RG vectors
+  static constexpr int PER = (NU + NT - 1) / NT;
+  static_assert(ROWS % RG == 0, "row pairs");
+  uint4 v[PER][RG];
+  __device__ static inline void unit(int u, int& r0, int& c) {
+    if constexpr (TR) {
+      r0 = (u % NG) * RG;
+      c = (u / NG) * VN;
+    } else {
+      r0 = u / VPR;
+      c = (u % VPR) * VN;
+    }
+  }
   __device__ inline void load(const T* g, long gstride, int nvalid, int tid) {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const int e = tid + p * NT;
-      const int r = e / VPR, c = (e % VPR) * VN;
-      v[p] = uint4{0u, 0u, 0u, 0u};
-      if (e < NV && r < nvalid) v[p] = ld16(g + r * gstride + c);
+      const int u = tid + p * NT;
+      int r0, c;
+      unit(u, r0, c);
+#pragma unroll
+      for (int q = 0; q < RG; ++q) {
+        v[p][q] = uint4{0u, 0u, 0u, 0u};
+        if (u < NU && r0 + q < nvalid) v[p][q] = ld16(g + (r0 + q) * gstride + c);
+      }
     }
   }
   __device__ inline void store_rows(T* s, int ld, int tid) const {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const int e = tid + p * NT;
-      if (e < NV) st16(s + (e / VPR) * ld + (e % VPR) * VN, v[p]);
+      const int u = tid + p * NT;
+      int r0, c;
+      unit(u, r0, c);
+      if (u < NU) {
+#pragma unroll
+        for (int q = 0; q < RG; ++q) st16(s + (r0 + q) * ld + c, v[p][q]);
+      }
     }
   }
   // element (r, c) -> s[c * ld + r], times scale[r] (nullptr = 1)
   __device__ inline void store_transposed(T* s, int ld, const float* scale, int tid) const {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const int e = tid + p * NT;
-      if (e < NV) {
-        const int r = e / VPR, c = (e % VPR) * VN;
-        const T* x = reinterpret_cast<const T*>(&v[p]);
-        const float sc = scale ? scale[r] : 1.0f;
+      const int u = tid + p * NT;
+      int r0, c;
+      unit(u, r0, c);
+      if (u < NU) {
+        if constexpr (RG == 2) {
+          const T* x0 = reinterpret_cast<const T*>(&v[p][0]);
+          const T* x1 = reinterpret_cast<const T*>(&v[p][1]);
+          const float s0 = scale ? scale[r0] : 1.0f, s1 = scale ? scale[r0 + 1] : 1.0f;
 #pragma unroll
-        for (int j = 0; j < VN; ++j) s[(c + j) * ld + r] = to_t<T>(to_f(x[j]) * sc);
+          for (int j = 0; j < VN; ++j) {
+            T pr[2] = {to_t<T>(to_f(x0[j]) * s0), to_t<T>(to_f(x1[j]) * s1)};
+            uint32_t w;
+            __builtin_memcpy(&w, pr, 4);
+            *reinterpret_cast<uint32_t*>(s + (c + j) * ld + r0) = w;
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < RG; ++q) {
+            const T* x = reinterpret_cast<const T*>(&v[p][q]);
+            const float sc = scale ? scale[r0 + q] : 1.0f;
+#pragma unroll
+            for (int j = 0; j < VN; ++j) s[(c + j) * ld + r0 + q] = to_t<T>(to_f(x[j]) * sc);
+          }
+        }
       }
     }
   }
