@@ -69,7 +69,25 @@ __device__ inline void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>
 // MFMA fragment loads from LDS
 //   KC = true : element (row, k) at p[row * ld + k]   (k contiguous)
 //   KC = false: element (row, k) at p[k * ld + row]   (k strided)
+// For 16-bit elements the strided case uses the gfx950 LDS transpose read
+// (ds_read_b64_tr_b16).  Its lane mapping, measured on the device: within
+// each group of 16 lanes, lane j supplies the address of 4 consecutive
+// elements M[j][0..3], and lane i receives M[4e + i/4][i % 4], e = 0..3.
+// Pointing lane j = 4e + q at p[(k + e) * ld + row + 4q] therefore hands lane
+// i the four values p[(k + e) * ld + row + i], e = 0..3, i.e. four
+// consecutive k of row (row + i): one 8-byte read replaces four 2-byte ones.
+// Needs ld and row multiples of 4 (8-byte aligned reads).
 // --------------------------------------------------------------------------
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// four consecutive k (k0 + 4 * (lane >> 4) .. + 3) of row row0 + (lane & 15)
+__device__ inline s16x4 lds_read_tr4(const bf16* p, int ld, int row0, int k0, int lane) {
+  const int j = lane & 15;
+  const bf16* a = p + (k0 + 4 * (lane >> 4) + (j >> 2)) * ld + row0 + 4 * (j & 3);
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a));
+}
+
 template <typename T, bool KC>
 __device__ inline typename Mfma<T>::frag load_frag(const T* p, int ld, int row0, int k0, int lane) {
   constexpr int KPL = Mfma<T>::KPL;
@@ -78,13 +96,17 @@ __device__ inline typename Mfma<T>::frag load_frag(const T* p, int ld, int row0,
   typename Mfma<T>::frag f;
   if constexpr (KC) {
     f = *reinterpret_cast<const typename Mfma<T>::frag*>(p + r * ld + k);
+  } else if constexpr (KPL == 1) {
+    f = p[k * ld + r];
   } else {
-    if constexpr (KPL == 1) {
-      f = p[k * ld + r];
-    } else {
-#pragma unroll
-      for (int j = 0; j < KPL; ++j) f[j] = p[(k + j) * ld + r];
-    }
+    // 8 consecutive k starting at k0 + 8 (lane >> 4): two transpose reads
+    // (k .. k+3 and k+4 .. k+7); each lane group g reads rows k0 + 8g + e
+    const int j = lane & 15;
+    const T* a = p + (k0 + 8 * (lane >> 4) + (j >> 2)) * ld + row0 + 4 * (j & 3);
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a));
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(a + 4 * ld));
+    const short __attribute__((ext_vector_type(8))) w = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    __builtin_memcpy(&f, &w, 16);
   }
   return f;
 }
@@ -135,7 +157,6 @@ template <int M, int N, int NW> struct Acc {
 };
 
 // bf16 fragments of 4 k values for v_mfma_f32_16x16x16_bf16 (inner sizes of 16)
-typedef short s16x4 __attribute__((ext_vector_type(4)));
 template <bool KC>
 __device__ inline s16x4 load_frag4(const bf16* p, int ld, int row0, int k0, int lane) {
   const int r = row0 + (lane & 15);
@@ -144,9 +165,7 @@ __device__ inline s16x4 load_frag4(const bf16* p, int ld, int row0, int k0, int 
   if constexpr (KC) {
     f = *reinterpret_cast<const s16x4*>(p + r * ld + k);
   } else {
-    const unsigned short* q = reinterpret_cast<const unsigned short*>(p);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) f[j] = (short)q[(k + j) * ld + r];
+    f = lds_read_tr4(p, ld, row0, k0, lane);
   }
   return f;
 }
@@ -173,22 +192,6 @@ __device__ inline void gemm_acc(Acc<M, N, NW>& acc, const T* A, int lda, const T
 #pragma unroll
         for (int j = 0; j < TL::RN; ++j)
           acc.v[i][j] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a[i], b[j], acc.v[i][j], 0, 0, 0);
-    }
-  } else if constexpr (!AKC || !BKC) {
-    // a strided operand takes KPL scalar LDS reads per fragment: keep one
-    // k step in flight to bound the live registers
-    static_assert(K % KS == 0, "k multiple");
-#pragma unroll 1
-    for (int k0 = 0; k0 < K; k0 += KS) {
-      typename Mfma<T>::frag a[TL::RM], b[TL::RN];
-#pragma unroll
-      for (int i = 0; i < TL::RM; ++i) a[i] = load_frag<T, AKC>(A, lda, m0 + 16 * i, k0, lane);
-#pragma unroll
-      for (int j = 0; j < TL::RN; ++j) b[j] = load_frag<T, BKC>(B, ldb, n0 + 16 * j, k0, lane);
-#pragma unroll
-      for (int i = 0; i < TL::RM; ++i)
-#pragma unroll
-        for (int j = 0; j < TL::RN; ++j) acc.v[i][j] = Mfma<T>::mma(a[i], b[j], acc.v[i][j]);
     }
   } else {
     static_assert(K % KS == 0, "k multiple");
@@ -247,7 +250,7 @@ __device__ inline void for_tiles_mut(Acc<M, N, NW>& acc, int wave, int lane, F&&
 //  * then block doubling, S = 16, 32, ...: for each pair of S-blocks on the
 //    diagonal, T21 = -T22 (A21 T11), two fp32 MFMA products.
 // --------------------------------------------------------------------------
-constexpr int inv_scratch_floats(int C) { return C >= 32 ? (C / 2) * (C / 2 + 1) : 1; }
+constexpr int inv_scratch_floats(int C) { return C >= 32 ? ((C / 2) * (C / 2 + 1) + 3) / 4 * 4 : 4; }
 
 template <int C, int S, int NW>
 __device__ inline void invert_double_level(const float* A, float* Tm, float* Xs, int wave, int lane) {
