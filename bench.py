@@ -70,13 +70,15 @@ def algorithmic_counts(w):
     c["chunk_bwd_pairs"] = (th * (5 * D * e + 8) + ntp * 2 * L * D * e + nch * 12 * C * D
                             + ntp * L * D * 16 + ntp * D * 4,
                             nch * 2 * C * C * D * 10 * L)
-    c["refine_bwd"] = (th * D * e + ntp * (8 * L * D + 8 * D + D * e + 4 * D + L * D * e),
-                       th * 6 * L * D * D)
-    c["conv_bwd"] = (2 * th * D * e + ntp * 8 * D, 8 * th * D)
+    # refinement + ShortConv backward: read v, dK_l, dW_l (fp32), the direct
+    # v-gradient (fp32); write u, dp_l (for the weight GEMM) and dv
+    c["refine_bwd"] = (th * (3 * D * e + 4 * D + L * D * (8 + e)), th * 6 * L * D * D)
     ns = max(1, min(1024 // (2 * H * max(L, 1)), -(-B * Tp // 64)))
-    c["wgrad_gemm"] = (ntp * L * D * (4 + e) + ntp * D * e * 2 * L + H * L * 2 * ns * D * D * 4,
-                       ntp * 4 * L * D * D)
+    c["wgrad_gemm"] = (th * L * D * (4 + e) + th * D * e * 2 * L + H * L * 2 * ns * D * D * 4,
+                       th * 4 * L * D * D)
     c["wgrad_reduce"] = (H * L * 2 * ns * D * D * 4 + H * L * 2 * D * D * 4, H * L * 2 * ns * D * D)
+    ntiles = -(-T // 29)
+    c["bias_reduce"] = (bh * ntiles * (L * D + 4 * D) * 4 + H * (L * D + 4 * D) * 4, 0)
     c["transpose_weights"] = (H * L * 4 * D * D * e, 0)
     c["refine_fwd_recompute"] = c["refine_fwd"]
     peak_f = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS

@@ -155,7 +155,7 @@ template <typename E>
 struct BwdWs {
   E *Kl, *Wl, *Mt, *M, *UT, *WkT, *Sct, *dSnT, *u, *dP, *WkW, *WpW;
   float *HT, *gC, *ET, *dQt, *dUs, *dWks, *dKs, *dVp, *dqp, *dkp, *dKl, *dWl, *dgs, *dgp;
-  float *dvdir, *du, *dwbp, *dcp, *part;
+  float *dvdir, *dwbp, *dcp, *part;
 };
 
 template <typename E>
@@ -163,7 +163,7 @@ BwdWs<E> carve_bwd(const prism::Dims& d, Carve& cv) {
   const size_t bh = (size_t)d.B * d.H;
   const size_t es = sizeof(E);
   const size_t DD = (size_t)d.D * d.D, CD = (size_t)d.C * d.D;
-  const size_t ntiles = (d.Tp + prism::kRefineTile - 1) / prism::kRefineTile;
+  const size_t ntiles = (size_t)prism::refine_bwd_tiles(d);
   const size_t L1 = d.L > 0 ? d.L : 1;
   BwdWs<E> w;
   w.Kl = cv.take<E>(bh * d.L * d.Tp * d.D * es);
@@ -190,7 +190,6 @@ BwdWs<E> carve_bwd(const prism::Dims& d, Carve& cv) {
   w.dgp = cv.take<float>(bh * d.NC * d.C * 4);
   w.dvdir = cv.take<float>(bh * d.Tp * d.D * 4);
   w.u = cv.take<E>(bh * d.Tp * d.D * es);
-  w.du = cv.take<float>(bh * d.Tp * d.D * 4);
   w.dP = cv.take<E>(bh * d.L * d.Tp * d.D * es);
   w.dwbp = cv.take<float>(bh * ntiles * L1 * d.D * 4);
   w.dcp = cv.take<float>(bh * ntiles * d.D * 4 * 4);
@@ -284,14 +283,14 @@ prism_status run_backward(const prism::Dims& d, const void* q, const void* k, co
     r.v = v_; r.conv = static_cast<const E*>(conv); r.Wk = static_cast<const E*>(Wk);
     r.Wp = static_cast<const E*>(Wp); r.wbeta = static_cast<const E*>(wbeta);
     r.WkT = w.WkW; r.WpT = w.WpW; r.dKl = w.dKl; r.dWl = w.dWl; r.dvdir = w.dvdir; r.u = w.u;
-    r.du = w.du; r.dP = w.dP; r.dwbp = w.dwbp; r.dcp = w.dcp; r.part = w.part;
+    r.dP = w.dP; r.dwbp = w.dwbp; r.dcp = w.dcp; r.part = w.part;
     r.dv = static_cast<E*>(dv); r.dWk_o = dWk; r.dWp_o = dWp; r.dwbeta_o = dwbeta;
     r.dconv_o = dconv;
     HIP_TRY("transpose_weights", s, prism::launch_refine_bwd<E>(d, r, 0, s));
     HIP_TRY("refine_bwd", s, prism::launch_refine_bwd<E>(d, r, 1, s));
-    HIP_TRY("conv_bwd", s, prism::launch_refine_bwd<E>(d, r, 2, s));
-    HIP_TRY("wgrad_gemm", s, prism::launch_refine_bwd<E>(d, r, 3, s));
-    HIP_TRY("wgrad_reduce", s, prism::launch_refine_bwd<E>(d, r, 4, s));
+    HIP_TRY("wgrad_gemm", s, prism::launch_refine_bwd<E>(d, r, 2, s));
+    HIP_TRY("wgrad_reduce", s, prism::launch_refine_bwd<E>(d, r, 3, s));
+    HIP_TRY("bias_reduce", s, prism::launch_refine_bwd<E>(d, r, 4, s));
   }
   return PRISM_OK;
 }

@@ -63,21 +63,20 @@ struct RefineBwdArgs {
   const E *v, *conv, *Wk, *Wp, *wbeta;
   E *WkT, *WpT;                 // transposed weights (workspace)
   const float *dKl, *dWl;
-  float* dvdir;                 // in: direct v-gradient; out: + refinement part
-  E* u;
-  float* du;
-  E* dP;
+  const float* dvdir;           // direct v-gradient of the recurrence
+  E* u;                         // ShortConv output rows (for the weight GEMM)
+  E* dP;                        // dp rows (for the weight GEMM)
   float *dwbp, *dcp, *part;     // per-tile / per-split partial sums
   E* dv;
   float *dWk_o, *dWp_o, *dwbeta_o, *dconv_o;
 };
 template <typename E>
-// stage 0: transpose weights, 1: refine_bwd, 2: conv_bwd, 3: wgrad_gemm, 4: wgrad_reduce
+// stage 0: transpose weights, 1: refinement + ShortConv backward (dv, per-tile
+// dw_beta and tap partials), 2: weight-gradient GEMM, 3: its reduction,
+// 4: reduction of the dw_beta and tap partials
 hipError_t launch_refine_bwd(const Dims& d, const RefineBwdArgs<E>& a, int stage, hipStream_t s);
 int refine_bwd_splits(const Dims& d);   // split count of the weight-gradient GEMM
-// tokens per refinement-backward tile (the per-tile partial sums of dw_beta
-// and of the ShortConv taps have one row per tile)
-constexpr int kRefineTile = 32;
+int refine_bwd_tiles(const Dims& d);    // token tiles per sequence (rows of the per-tile partials)
 
 // O = O_loc + Qt S_c^T, written to o [B, T, H, D].
 template <typename E>
