@@ -68,7 +68,7 @@ def algorithmic_counts(w):
     c["chunk_bwd_solve"] = (th * (4 * D * e + 12) + ntp * 2 * L * D * e + nch * (28 * C * D + 8 * C),
                             nch * (2 * C * C * D * (2 * L + 16) + 4 * C ** 3))
     c["chunk_bwd_pairs"] = (th * (5 * D * e + 8) + ntp * 2 * L * D * e + nch * 12 * C * D
-                            + ntp * L * D * 16 + ntp * D * 4,
+                            + ntp * L * D * 16,
                             nch * 2 * C * C * D * 10 * L)
     # refinement + ShortConv backward: read v, dK_l, dW_l (fp32), the direct
     # v-gradient (fp32); write u, dp_l (for the weight GEMM) and dv

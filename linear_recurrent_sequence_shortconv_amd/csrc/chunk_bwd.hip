@@ -423,9 +423,16 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
   typedef Tiling<C, C, NW> TLC;
   const bool actD = TLD::active(wave), actC = TLC::active(wave);
 
+  // K_l, W_l rows of the first fold step and the V rows are fetched early
+  RegTile<E, C, D, NT> kl, wl, vn;
+  if (L > 0) {
+    const long lrow = (long)bh * L * Tp + tb;
+    kl.load(Kl + lrow * D, D, C, tid);
+    wl.load(Wl + lrow * D, D, C, tid);
+  }
+  vn.load(v + row0 * D, ts, nval, tid);
   for (int e = tid; e < 4 * NW * C; e += NT) rs[e] = 0.f;
   if (wave == 0) chunk_decays<C>(alpha, beta, row0, H, nval, g, ev, Dv, bt, be, nullptr, lane);
-  if (tid < C) de[tid] = 0.f;
   g2s_rows<E, C, D, NT>(Kr, LR, k + row0 * D, ts, nval, tid);
   __syncthreads();
 
@@ -439,9 +446,13 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
     E* Vr = reinterpret_cast<E*>(smem + LY::F_V);
     for (int l = 0; l < L; ++l) {
       const long lrow = ((long)bh * L + l) * Tp + tb;
-      g2s_rows<E, C, D, NT>(Klr, LR, Kl + lrow * D, D, C, tid);
-      g2s_rows<E, C, D, NT>(Wlr, LR, Wl + lrow * D, D, C, tid);
+      kl.store_rows(Klr, LR, tid);
+      wl.store_rows(Wlr, LR, tid);
       __syncthreads();
+      if (l + 1 < L) {
+        kl.load(Kl + (lrow + Tp) * D, D, C, tid);
+        wl.load(Wl + (lrow + Tp) * D, D, C, tid);
+      }
       Acc<C, C, NW> f;    // [t][i] = K_t . K_l,i
       f.zero();
       gemm_acc<E, C, C, D, NW, true, true>(f, Kr, LR, Klr, LR, wave, lane);
@@ -456,7 +467,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
       gemm_acc<E, C, D, C, NW, true, false>(vp, Fb, LT, Wlr, LR, wave, lane);
       __syncthreads();
     }
-    g2s_rows<E, C, D, NT>(Vr, LR, v + row0 * D, ts, nval, tid);
+    vn.store_rows(Vr, LR, tid);
     __syncthreads();
     for_tiles_mut(vp, wave, lane, [&](int t0, int f, f32x4& x) {
 #pragma unroll
@@ -468,6 +479,13 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
   }
 
   // ---- solve: A = diag(beta)(Gam * K K^T)_{i<t}, T = (I + A)^{-1} ----
+  // Q, dO rows and dQt (fp32) of the next phase are fetched during the solve
+  const float* dQtc = dQt + cidx * C * D;
+  RegTile<E, C, D, NT> qn, on;
+  RegTile<float, C, D, NT> dqn;
+  qn.load(q + row0 * D, ts, nval, tid);
+  on.load(dO + row0 * D, ts, nval, tid);
+  dqn.load(dQtc, D, C, tid);
   E* Tbb = reinterpret_cast<E*>(smem + LY::S_TBB);
   E* Tbe = reinterpret_cast<E*>(smem + LY::S_TBE);
   {
@@ -519,20 +537,59 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
   E* NdQ = reinterpret_cast<E*>(smem + LY::P_NDQ);
   E* R0b = reinterpret_cast<E*>(smem + LY::P_R0);
   E* Xb = reinterpret_cast<E*>(smem + LY::P_XB);
-  const float* dQtc = dQt + cidx * C * D;
-  g2s_rows<E, C, D, NT>(Qr, LR, q + row0 * D, ts, nval, tid);
-  g2s_rows<E, C, D, NT>(dOr, LR, dO + row0 * D, ts, nval, tid);
-  g2s_rows_f32<E, C, D, NT>(NdQ, LR, dQtc, D, -1.f, tid);
+  qn.store_rows(Qr, LR, tid);
+  on.store_rows(dOr, LR, tid);
+  // -dQt rows (operand type)
+  typedef RegTile<float, C, D, NT> DQT;
+#pragma unroll
+  for (int p = 0; p < DQT::PER; ++p) {
+    const int u = tid + p * NT;
+    const int r = u / DQT::VPR, c0 = (u % DQT::VPR) * 4;
+    const f32x4 x = *reinterpret_cast<const f32x4*>(&dqn.v[p][0]);
+    if (u < DQT::NU) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) NdQ[r * LR + c0 + j] = to_t<E>(-x[j]);
+    }
+  }
   __syncthreads();
-  // de_t = Q_t . dQt_t (fp32 dQt)
-  for (int e = tid; e < C * 8; e += NT) {
-    const int t = e / 8, part = e % 8;
-    float s = 0.f;
-    for (int f = part * (D / 8); f < (part + 1) * (D / 8); ++f) s += to_f(Qr[t * LR + f]) * dQtc[(long)t * D + f];
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
-    s += __shfl_xor(s, 4);
-    if (part == 0) de[t] = s;
+  // de_t = Q_t . dQt_t (fp32 dQt): each row is held by VPR consecutive lanes
+  static_assert(DQT::VPR <= 64 && (64 % DQT::VPR) == 0, "a row within one wave");
+#pragma unroll
+  for (int p = 0; p < DQT::PER; ++p) {
+    const int u = tid + p * NT;
+    const int r = u / DQT::VPR, c0 = (u % DQT::VPR) * 4;
+    const f32x4 x = *reinterpret_cast<const f32x4*>(&dqn.v[p][0]);
+    float sdq = 0.f;
+    if (u < DQT::NU) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sdq += to_f(Qr[r * LR + c0 + j]) * x[j];
+    }
+#pragma unroll
+    for (int off = 1; off < DQT::VPR; off <<= 1) sdq += __shfl_xor(sdq, off);
+    if (u < DQT::NU && (u % DQT::VPR) == 0) de[r] = sdq;
+  }
+  // dU_s, dWk_s, dK_s and dQt in the accumulator layout, for the epilogue
+  // of the R0 products (fetched while they run)
+  const float* dUc = dUs + cidx * C * D;
+  const float* dWc = dWks + cidx * C * D;
+  const float* dKc = dKs + cidx * C * D;
+  f32x4 pU[TLD::RM][TLD::RN], pW[TLD::RM][TLD::RN], pK[TLD::RM][TLD::RN], pQ[TLD::RM][TLD::RN];
+  if (actD) {
+#pragma unroll
+    for (int i = 0; i < TLD::RM; ++i)
+#pragma unroll
+      for (int j = 0; j < TLD::RN; ++j) {
+        const int t0 = TLD::m0(wave) + 16 * i + 4 * (lane >> 4);
+        const int f = TLD::n0(wave) + 16 * j + (lane & 15);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const long o = (long)(t0 + r) * D + f;
+          pU[i][j][r] = dUc[o];
+          pW[i][j][r] = dWc[o];
+          pK[i][j][r] = dKc[o];
+          pQ[i][j][r] = dQtc[o];
+        }
+      }
   }
 
   // ---- R0 terms ----
@@ -586,28 +643,22 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
   __syncthreads();
   // dU = dU_s + R0^T dO, dWk = dWk_s - R0^T dQt -> rows (U, Wk slots);
   // dq += e dQt; dk += dK_s
-  {
-    const float* dUc = dUs + cidx * C * D;
-    const float* dWc = dWks + cidx * C * D;
-    const float* dKc = dKs + cidx * C * D;
-    if (actD) {
+  if (actD) {
 #pragma unroll
-      for (int i = 0; i < TLD::RM; ++i)
+    for (int i = 0; i < TLD::RM; ++i)
 #pragma unroll
-        for (int j = 0; j < TLD::RN; ++j) {
-          const int t0 = TLD::m0(wave) + 16 * i + 4 * (lane >> 4);
-          const int f = TLD::n0(wave) + 16 * j + (lane & 15);
+      for (int j = 0; j < TLD::RN; ++j) {
+        const int t0 = TLD::m0(wave) + 16 * i + 4 * (lane >> 4);
+        const int f = TLD::n0(wave) + 16 * j + (lane & 15);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int t = t0 + r;
-            const long o = (long)t * D + f;
-            Ur[t * LR + f] = to_t<E>(du.v[i][j][r] + dUc[o]);
-            Wkr[t * LR + f] = to_t<E>(dw.v[i][j][r] + dWc[o]);
-            dq.v[i][j][r] += ev[t] * dQtc[o];
-            dk.v[i][j][r] += dKc[o];
-          }
+        for (int r = 0; r < 4; ++r) {
+          const int t = t0 + r;
+          Ur[t * LR + f] = to_t<E>(du.v[i][j][r] + pU[i][j][r]);
+          Wkr[t * LR + f] = to_t<E>(dw.v[i][j][r] + pW[i][j][r]);
+          dq.v[i][j][r] += ev[t] * pQ[i][j][r];
+          dk.v[i][j][r] += pK[i][j][r];
         }
-    }
+      }
   }
   E* dUr = Ur;
   E* dWkr = Wkr;
@@ -781,7 +832,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
     const float* __restrict__ alpha, const E* __restrict__ Kl, const E* __restrict__ Wl,
     const float* __restrict__ dVp, const float* __restrict__ dqp, const float* __restrict__ dkp,
     const float* __restrict__ dgp, float* __restrict__ dKl, float* __restrict__ dWl,
-    E* __restrict__ dq, E* __restrict__ dk, float* __restrict__ dvdir, E* __restrict__ dv,
+    E* __restrict__ dq, E* __restrict__ dk, E* __restrict__ dv,
     float* __restrict__ dalpha, int B, int T, int H, int L, int NC, int Tp) {
   typedef CB3Lds<E, D, C> LY;
   constexpr int NW = CB_NW, NT = CB_NT;
@@ -829,11 +880,39 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
   Acc<C, D, NW> dqa, dka;
   dqa.zero();
   dka.zero();
+  typedef Tiling<C, D, NW> TLD;
+  RegTile<E, C, D, NT> kl, wl;   // next step's K_l, W_l rows (software prefetch)
+  if (L > 0) {
+    const long lrow = (long)bh * L * Tp + tb;
+    kl.load(Kl + lrow * D, D, C, tid);
+    wl.load(Wl + lrow * D, D, C, tid);
+  }
   for (int l = 0; l < L; ++l) {
     const long lrow = ((long)bh * L + l) * Tp + tb;
-    g2s_rows<E, C, D, NT>(Klr, LR, Kl + lrow * D, D, C, tid);
-    g2s_rows<E, C, D, NT>(Wlr, LR, Wl + lrow * D, D, C, tid);
+    kl.store_rows(Klr, LR, tid);
+    wl.store_rows(Wlr, LR, tid);
     __syncthreads();
+    if (l + 1 < L) {
+      kl.load(Kl + (lrow + Tp) * D, D, C, tid);
+      wl.load(Wl + (lrow + Tp) * D, D, C, tid);
+    }
+    // the partial dK_l, dW_l of the state-gradient kernel (accumulator
+    // layout), in flight during the products of this step
+    f32x4 pkl[TLD::RM][TLD::RN], pwl[TLD::RM][TLD::RN];
+    if (TLD::active(wave)) {
+#pragma unroll
+      for (int i = 0; i < TLD::RM; ++i)
+#pragma unroll
+        for (int j = 0; j < TLD::RN; ++j) {
+          const int t0 = TLD::m0(wave) + 16 * i + 4 * (lane >> 4);
+          const int f = TLD::n0(wave) + 16 * j + (lane & 15);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            pkl[i][j][r] = dKl[(lrow + t0 + r) * D + f];
+            pwl[i][j][r] = dWl[(lrow + t0 + r) * D + f];
+          }
+        }
+    }
     // R_l = (Gam * Q K_l^T)_{i<=t}, dR_l = dO W_l^T  -> Rb, Xb = Gam * dR_l
     {
       Acc<C, C, NW> r, dr;
@@ -912,16 +991,20 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
     __builtin_amdgcn_sched_barrier(0);
     gemm_acc<E, C, D, C, NW, true, false>(dka, Gb, LT, Klr, LR, wave, lane);    // dG_l K_l
     __builtin_amdgcn_sched_barrier(0);
-    float* okl = dKl + lrow * D;
-    float* owl = dWl + lrow * D;
-    for_tiles(dkl, wave, lane, [&](int t0, int f, const f32x4& x) {
+    if (TLD::active(wave)) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) okl[(long)(t0 + r) * D + f] += x[r];
-    });
-    for_tiles(dwl, wave, lane, [&](int t0, int f, const f32x4& x) {
+      for (int i = 0; i < TLD::RM; ++i)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) owl[(long)(t0 + r) * D + f] += x[r];
-    });
+        for (int j = 0; j < TLD::RN; ++j) {
+          const int t0 = TLD::m0(wave) + 16 * i + 4 * (lane >> 4);
+          const int f = TLD::n0(wave) + 16 * j + (lane & 15);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            dKl[(lrow + t0 + r) * D + f] = pkl[i][j][r] + dkl.v[i][j][r];
+            dWl[(lrow + t0 + r) * D + f] = pwl[i][j][r] + dwl.v[i][j][r];
+          }
+        }
+    }
     __syncthreads();
   }
 
@@ -945,14 +1028,9 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
       if (t < nval) dko[(long)t * ts + f] = to_t<E>(x[r] + dkc[(long)t * D + f]);
     }
   });
-  if (L > 0) {
-    // direct v-gradient, completed by the refinement backward
-    float* o = dvdir + ((long)bh * Tp + tb) * D;
-    for (int e = tid; e < C * D / 4; e += NT) {
-      const int t = e / (D / 4), f = (e % (D / 4)) * 4;
-      *reinterpret_cast<f32x4*>(o + (long)t * D + f) = *reinterpret_cast<const f32x4*>(dvc + (long)t * D + f);
-    }
-  } else {
+  // with L > 0 the direct v-gradient dV' (chunk rows [bh][c][t] = token rows
+  // [bh][c C + t]) is completed by the refinement backward
+  if (L == 0) {
     E* dvo = dv + row0 * D;
     for (int e = tid; e < C * D; e += NT) {
       const int t = e / D, f = e % D;
@@ -999,7 +1077,7 @@ static hipError_t cbwd_launch_dc(const Dims& d, const ChunkBwdArgs<E>& a, int st
     else
       hipLaunchKernelGGL((chunk_bwd_pairs_kernel<E, D, C>), dim3(nblk), dim3(CB_NT), 0, s, a.q,
                          a.k, a.dO, a.alpha, a.Kl, a.Wl, a.dVp, a.dqp, a.dkp, a.dgp, a.dKl, a.dWl,
-                         a.dq, a.dk, a.dvdir, a.dv, a.dalpha, d.B, d.T, d.H, d.L, d.NC, d.Tp);
+                         a.dq, a.dk, a.dv, a.dalpha, d.B, d.T, d.H, d.L, d.NC, d.Tp);
     return hipGetLastError();
   }
 }

@@ -155,7 +155,7 @@ template <typename E>
 struct BwdWs {
   E *Kl, *Wl, *Mt, *M, *UT, *WkT, *Sct, *dSnT, *u, *dP, *WkW, *WpW;
   float *HT, *gC, *ET, *dQt, *dUs, *dWks, *dKs, *dVp, *dqp, *dkp, *dKl, *dWl, *dgs, *dgp;
-  float *dvdir, *dwbp, *dcp, *part;
+  float *dwbp, *dcp, *part;
 };
 
 template <typename E>
@@ -188,7 +188,6 @@ BwdWs<E> carve_bwd(const prism::Dims& d, Carve& cv) {
   w.dWl = cv.take<float>(bh * d.L * d.Tp * d.D * 4);
   w.dgs = cv.take<float>(bh * d.NC * d.C * 4);
   w.dgp = cv.take<float>(bh * d.NC * d.C * 4);
-  w.dvdir = cv.take<float>(bh * d.Tp * d.D * 4);
   w.u = cv.take<E>(bh * d.Tp * d.D * es);
   w.dP = cv.take<E>(bh * d.L * d.Tp * d.D * es);
   w.dwbp = cv.take<float>(bh * ntiles * L1 * d.D * 4);
@@ -273,7 +272,7 @@ prism_status run_backward(const prism::Dims& d, const void* q, const void* k, co
   a.Kl = w.Kl; a.Wl = w.Wl; a.UT = w.UT; a.WkT = w.WkT; a.St = w.Sct; a.dSnT = w.dSnT;
   a.dQt = w.dQt; a.dUs = w.dUs; a.dWks = w.dWks; a.dKs = w.dKs; a.dKl = w.dKl; a.dWl = w.dWl;
   a.dgs = w.dgs; a.dVp = w.dVp; a.dqp = w.dqp; a.dkp = w.dkp; a.dgp = w.dgp; a.dbeta = dbeta;
-  a.dq = static_cast<E*>(dq); a.dk = static_cast<E*>(dk); a.dvdir = w.dvdir;
+  a.dq = static_cast<E*>(dq); a.dk = static_cast<E*>(dk);
   a.dv = static_cast<E*>(dv); a.dalpha = dalpha;
   HIP_TRY("chunk_bwd_state", s, prism::launch_chunk_bwd<E>(d, a, 0, s));
   HIP_TRY("chunk_bwd_solve", s, prism::launch_chunk_bwd<E>(d, a, 1, s));
@@ -282,7 +281,7 @@ prism_status run_backward(const prism::Dims& d, const void* q, const void* k, co
     prism::RefineBwdArgs<E> r;
     r.v = v_; r.conv = static_cast<const E*>(conv); r.Wk = static_cast<const E*>(Wk);
     r.Wp = static_cast<const E*>(Wp); r.wbeta = static_cast<const E*>(wbeta);
-    r.WkT = w.WkW; r.WpT = w.WpW; r.dKl = w.dKl; r.dWl = w.dWl; r.dvdir = w.dvdir; r.u = w.u;
+    r.WkT = w.WkW; r.WpT = w.WpW; r.dKl = w.dKl; r.dWl = w.dWl; r.dvdir = w.dVp; r.u = w.u;
     r.dP = w.dP; r.dwbp = w.dwbp; r.dcp = w.dcp; r.part = w.part;
     r.dv = static_cast<E*>(dv); r.dWk_o = dWk; r.dWp_o = dWp; r.dwbeta_o = dwbeta;
     r.dconv_o = dconv;

@@ -49,8 +49,7 @@ struct ChunkBwdArgs {
   const E *Kl, *Wl, *UT, *WkT, *St, *dSnT;
   float *dQt, *dUs, *dWks, *dKs, *dKl, *dWl, *dgs, *dVp, *dqp, *dkp, *dgp, *dbeta;
   E *dq, *dk;
-  float* dvdir;
-  E* dv;
+  E* dv;                        // written here only when L = 0
   float* dalpha;
 };
 template <typename E>
@@ -63,7 +62,7 @@ struct RefineBwdArgs {
   const E *v, *conv, *Wk, *Wp, *wbeta;
   E *WkT, *WpT;                 // transposed weights (workspace)
   const float *dKl, *dWl;
-  const float* dvdir;           // direct v-gradient of the recurrence
+  const float* dvdir;           // direct v-gradient of the recurrence ([bh][Tp][D])
   E* u;                         // ShortConv output rows (for the weight GEMM)
   E* dP;                        // dp rows (for the weight GEMM)
   float *dwbp, *dcp, *part;     // per-tile / per-split partial sums
