@@ -465,10 +465,11 @@ template <typename T> constexpr int ldpad(int n) { return n + 16 / (int)sizeof(T
 // Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26:
 //   erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
 //   t = 1 / (1 + p x), x >= 0, |error| <= 1.5e-7;  erf(-x) = -erf(x).
-// One exp and one reciprocal; e = exp(-z^2 / 2) is returned for reuse.
+// One exp and one hardware reciprocal (v_rcp_f32, 1 ulp: far below the
+// formula's own error); e = exp(-z^2 / 2) is returned for reuse.
 __device__ inline float normal_cdf(float z, float& e) {
   const float x = fabsf(z) * 0.70710678118654752f;
-  const float t = __frcp_rn(fmaf(0.3275911f, x, 1.0f));
+  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));   // v_rcp_f32 (1 ulp)
   float poly = fmaf(1.061405429f, t, -1.453152027f);
   poly = fmaf(poly, t, 1.421413741f);
   poly = fmaf(poly, t, -0.284496736f);
@@ -496,7 +497,7 @@ __device__ inline void gelu_and_grad(float z, float& g, float& dg) {
   g = z * c;
   dg = c + z * 0.39894228040143268f * e;
 }
-__device__ inline float sigmoidf(float x) { return 1.0f / (1.0f + __expf(-x)); }
+__device__ inline float sigmoidf(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // XCD-aware block order: consecutive hardware dispatch slots go round-robin
 // over the 8 XCDs; return a logical block id such that the blocks one XCD

@@ -126,32 +126,8 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
     pk.load(dKl + lrow * D, D, nrow, tid);
   }
   __syncthreads();
-  for (int e = tid; e < RB_TT * D; e += RB_NT) {
-    const int t = e / D, f = e % D;
-    float u = 0.f;
-    if (t < nrow) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) u += ctp[f * 4 + j] * to_f(vbuf[(t + 3 - j) * D + f]);
-    }
-    const E uh = to_t<E>(u);
-    ubuf[t * LD + f] = uh;
-    if constexpr (sizeof(E) == 2) ulo[t * LD + f] = to_t<E>(u - to_f(uh));
-  }
-  __syncthreads();
-  // owned u rows for the weight-gradient GEMM; gates
-  s2g_rows<E, RB_TT, D, RB_NT>(uo + (bh * Tp + t0) * D, D, ubuf, LD, own, tid);
-  if (tid < RB_TT * 4) {
-    const int t = tid >> 2, part = tid & 3;
-    for (int l = 0; l < L; ++l) {
-      const E* wb = wbl + l * D;
-      float s = 0.f;
-      for (int f = part * (D / 4); f < (part + 1) * (D / 4); ++f) s += to_f(wb[f]) * to_f(ubuf[t * LD + f]);
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      if (part == 0) gate[l][t] = sigmoidf(s);
-    }
-  }
-  // residual r^(1) = v - u in the accumulator layout:
+  // anchor u (fp32; to LDS as the MFMA operand, hi and lo parts) and residual
+  // r^(1) = v - u in the accumulator layout:
   // element (m, nn, i): token 16 m + 4 (lane >> 4) + i, feature 16 n + (lane & 15), n = fq + 4 nn
   float r[2][FPW][4];
 #pragma unroll
@@ -166,15 +142,39 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 16 * m + 4 * (lane >> 4) + i;
-        float val = 0.f;
+        float u = 0.f, val = 0.f;
         if (n < NFT && t < nrow) {
-          float u = 0.f;
 #pragma unroll
           for (int j = 0; j < 4; ++j) u += tp[j] * to_f(vbuf[(t + 3 - j) * D + f]);
           val = to_f(vbuf[(t + 3) * D + f]) - u;
         }
         r[m][nn][i] = val;
+        if (n < NFT) {
+          const E uh = to_t<E>(u);
+          ubuf[t * LD + f] = uh;
+          if constexpr (sizeof(E) == 2) ulo[t * LD + f] = to_t<E>(u - to_f(uh));
+        }
       }
+  }
+  __syncthreads();
+  // owned u rows for the weight-gradient GEMM; gates (4 threads per token,
+  // 16-byte reads of u and w_beta)
+  s2g_rows<E, RB_TT, D, RB_NT>(uo + (bh * Tp + t0) * D, D, ubuf, LD, own, tid);
+  if (tid < RB_TT * 4) {
+    const int t = tid >> 2, part = tid & 3;
+    for (int l = 0; l < L; ++l) {
+      float s = 0.f;
+      for (int c = part * VN; c < D; c += 4 * VN) {
+        const uint4 ua = ld16(ubuf + t * LD + c), wa = ld16(wbl + l * D + c);
+        const E* ue = reinterpret_cast<const E*>(&ua);
+        const E* we = reinterpret_cast<const E*>(&wa);
+#pragma unroll
+        for (int j = 0; j < VN; ++j) s += to_f(we[j]) * to_f(ue[j]);
+      }
+      s += __shfl_xor(s, 1);
+      s += __shfl_xor(s, 2);
+      if (part == 0) gate[l][t] = sigmoidf(s);
+    }
   }
   pw.store_rows(gw, LW, tid);
   pk.store_rows(gkk, LW, tid);
@@ -424,10 +424,14 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
   {
     const int f = tid % D, grp = tid / D;
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    for (int t = grp; t < own; t += NG) {
-      const float d_ = dub[t * LW + f];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j] += d_ * to_f(vbuf[(t + 3 - j) * D + f]);
+    for (int k = 0; k < (RB_OWN + NG - 1) / NG; ++k) {
+      const int t = grp + k * NG;
+      if (t < own) {
+        const float d_ = dub[t * LW + f];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] += d_ * to_f(vbuf[(t + 3 - j) * D + f]);
+      }
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) red[(grp * D + f) * 4 + j] = acc[j];

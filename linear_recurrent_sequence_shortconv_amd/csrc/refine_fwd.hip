@@ -72,80 +72,6 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
     if (t >= 0 && t < T) x = ld16(vseq + t * tok_stride + c);
     st16(vbuf + r * D + c, x);
   }
-  __syncthreads();
-
-  // ---- anchor u (fp32 math, stored as the MFMA operand type); pad tokens u = 0 ----
-  const E* ch = conv + (long)h * D * 4;
-  // RF_NT is a multiple of D: this thread always handles feature f = tid % D
-  static_assert(RF_NT % D == 0, "feature per thread");
-  float ctap[4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) ctap[j] = to_f(ch[(tid % D) * 4 + j]);
-  for (int e = tid; e < RF_TT * D; e += RF_NT) {
-    const int t = e / D, f = e % D;
-    float u = 0.f;
-    if (t0 + t < T) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) u += ctap[j] * to_f(vbuf[(t + 3 - j) * D + f]);
-    }
-    const E uh = to_t<E>(u);
-    ubuf[t * LD + f] = uh;
-    if constexpr (sizeof(E) == 2) ulo[t * LD + f] = to_t<E>(u - to_f(uh));
-  }
-  __syncthreads();
-
-  // ---- step gates beta^(l) = sigmoid(w_beta^(l) . u): 4 threads per token ----
-  {
-    const int t = tid >> 2, part = tid & 3;
-    for (int l = 0; l < L; ++l) {
-      const E* wb = wbs + l * D;
-      float s = 0.f;
-      for (int f = part * (D / 4); f < (part + 1) * (D / 4); ++f) s += to_f(wb[f]) * to_f(ubuf[t * LD + f]);
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
-      if (part == 0) gate[l][t] = sigmoidf(s);
-    }
-  }
-
-  // ---- residual r^(1) = v - u in the accumulator layout (fp32) ----
-  // element (m, n, i): token 16 m + 4 (lane >> 4) + i, feature 16 n + (lane & 15)
-  float r[4][FPW][4];
-  float taps[FPW][4];
-#pragma unroll
-  for (int nn = 0; nn < FPW; ++nn) {
-    const int n = wave + RF_NW * nn;
-    const int f = 16 * n + (lane & 15);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) taps[nn][j] = (n < NFT) ? to_f(ch[f * 4 + j]) : 0.f;
-  }
-#pragma unroll
-  for (int m = 0; m < 4; ++m)
-#pragma unroll
-    for (int nn = 0; nn < FPW; ++nn) {
-      const int n = wave + RF_NW * nn;
-      const int f = 16 * n + (lane & 15);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int t = 16 * m + 4 * (lane >> 4) + i;
-        float val = 0.f;
-        if (n < NFT && t0 + t < T) {
-          float u = 0.f;
-#pragma unroll
-          for (int j = 0; j < 4; ++j) u += taps[nn][j] * to_f(vbuf[(t + 3 - j) * D + f]);
-          val = to_f(vbuf[(t + 3) * D + f]) - u;
-        }
-        r[m][nn][i] = val;
-      }
-    }
-  __syncthreads();   // gates visible
-
-  E* Klseq = Kl + (((long)b * H + h) * L) * Tp * D;
-  E* Wlseq = Wl + (((long)b * H + h) * L) * Tp * D;
-  const int nvalid = min(RF_TT, Tp - t0);
-
-  // Per step l: gain pass p = W_p (u_hi + u_lo) -> chain -> w; direction pass
-  // k = W_k u_hi.  Weight fragments of the next pass are requested before the
-  // current pass's arithmetic so their latency overlaps it.
   typedef typename Mfma<E>::frag Frag;
   auto load_w = [&](const E* W, Frag (&bw)[FPW][NK]) {
 #pragma unroll
@@ -156,6 +82,70 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
         if (n < NFT) bw[nn][kk] = load_frag<E, true>(W, D, 16 * n, kk * KS, lane);
     }
   };
+  Frag bw[FPW][NK];   // weight fragments of the next projection (W_p^(1) now)
+  if (L > 0) load_w(Wp + (long)h * L * D * D, bw);
+  __syncthreads();
+
+  // ---- anchor u (fp32; to LDS as the MFMA operand, hi and lo parts) and
+  //      residual r^(1) = v - u, both in the accumulator layout:
+  //      element (m, n, i): token 16 m + 4 (lane >> 4) + i, feature 16 n + (lane & 15)
+  const E* ch = conv + (long)h * D * 4;
+  float r[4][FPW][4];
+#pragma unroll
+  for (int nn = 0; nn < FPW; ++nn) {
+    const int n = wave + RF_NW * nn;
+    const int f = 16 * n + (lane & 15);
+    float taps[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) taps[j] = (n < NFT) ? to_f(ch[f * 4 + j]) : 0.f;
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = 16 * m + 4 * (lane >> 4) + i;
+        float u = 0.f, val = 0.f;
+        if (n < NFT && t0 + t < T) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) u += taps[j] * to_f(vbuf[(t + 3 - j) * D + f]);
+          val = to_f(vbuf[(t + 3) * D + f]) - u;
+        }
+        r[m][nn][i] = val;
+        if (n < NFT) {
+          const E uh = to_t<E>(u);
+          ubuf[t * LD + f] = uh;
+          if constexpr (sizeof(E) == 2) ulo[t * LD + f] = to_t<E>(u - to_f(uh));
+        }
+      }
+  }
+  __syncthreads();
+
+  // ---- step gates beta^(l) = sigmoid(w_beta^(l) . u): 4 threads per token,
+  //      16-byte reads of u and w_beta ----
+  {
+    const int t = tid >> 2, part = tid & 3;
+    for (int l = 0; l < L; ++l) {
+      float s = 0.f;
+      for (int c = part * VN; c < D; c += 4 * VN) {
+        const uint4 ua = ld16(ubuf + t * LD + c), wa = ld16(wbs + l * D + c);
+        const E* ue = reinterpret_cast<const E*>(&ua);
+        const E* we = reinterpret_cast<const E*>(&wa);
+#pragma unroll
+        for (int j = 0; j < VN; ++j) s += to_f(we[j]) * to_f(ue[j]);
+      }
+      s += __shfl_xor(s, 1);
+      s += __shfl_xor(s, 2);
+      if (part == 0) gate[l][t] = sigmoidf(s);
+    }
+  }
+  __syncthreads();   // gates visible
+
+  E* Klseq = Kl + (((long)b * H + h) * L) * Tp * D;
+  E* Wlseq = Wl + (((long)b * H + h) * L) * Tp * D;
+  const int nvalid = min(RF_TT, Tp - t0);
+
+  // Per step l: gain pass p = W_p (u_hi + u_lo) -> chain -> w; direction pass
+  // k = W_k u_hi.  Weight fragments of the next pass are requested before the
+  // current pass's arithmetic so their latency overlaps it.
   auto gemm = [&](const Frag (&bw)[FPW][NK], bool with_lo, f32x4 (&acc)[4][FPW]) {
 #pragma unroll
     for (int m = 0; m < 4; ++m)
@@ -187,8 +177,6 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
     }
   };
 
-  Frag bw[FPW][NK];
-  if (L > 0) load_w(Wp + (long)h * L * D * D, bw);
   for (int l = 0; l < L; ++l) {
     const E* wk = Wk + ((long)h * L + l) * D * D;
     f32x4 acc[4][FPW];
