@@ -94,18 +94,133 @@ def algorithmic_counts(w):
 def measured_traffic():
     """HBM bytes per launch from the committed rocprofv3 counter summary, if it
     was taken on the current kernel sources (else None for every kernel)."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
     if not os.path.exists(path):
         return {}
     rec = json.load(open(path))
+    if rec.get("sources_sha256") != _sources_sha256():
+        return {}
+    return {k: v["bytes_per_launch"] for k, v in rec.get("kernels", {}).items()}
+
+
+# rocprofv3 kernel names -> the timer names used by the library and above
+_FAMILIES = [("refine_fwd_kernel", ["refine_fwd", "refine_fwd_recompute"]),
+             ("state_pass_kernel", ["state_fwd", "state_fwd_recompute", "state_bwd"]),
+             ("out_fwd_kernel", ["out_fwd"]),
+             ("chunk_bwd_state_kernel", ["chunk_bwd_state"]),
+             ("chunk_bwd_solve_kernel", ["chunk_bwd_solve"]),
+             ("chunk_bwd_pairs_kernel", ["chunk_bwd_pairs"]),
+             ("refine_bwd_kernel", ["refine_bwd"]),
+             ("wgrad_gemm_kernel", ["wgrad_gemm"]),
+             ("wgrad_reduce_kernel", ["wgrad_reduce"]),
+             ("bias_reduce_kernel", ["bias_reduce"]),
+             ("transpose_weights_kernel", ["transpose_weights"])]
+
+
+def _family(kernel_name):
+    if "chunk_fwd_kernel" in kernel_name:
+        bwd = "Lb1E" in kernel_name or "true>" in kernel_name
+        return ["chunk_fwd_bwdmode"] if bwd else ["chunk_fwd"]
+    for key, names in _FAMILIES:
+        if key in kernel_name:
+            return names
+    return None
+
+
+def _sources_sha256():
+    import hashlib
     csrc = os.path.join(ROOT, "linear_recurrent_sequence_shortconv_amd", "csrc")
     h = hashlib.sha256()
     for f in sorted(os.listdir(csrc)):
         h.update(open(os.path.join(csrc, f), "rb").read())
-    if rec.get("sources_sha256") != h.hexdigest():
-        return {}
-    return {k: v["bytes_per_launch"] for k, v in rec.get("kernels", {}).items()}
+    return h.hexdigest()
+
+
+def summarize_profiles(d, workload):
+    """Turn the rocprofv3 runs under directory d (trace/, fetch/, write/,
+    cfetch/, cwrite/: the commands are listed in the written summary) into
+    profiles/hbm_traffic.json and profiles/<workload>_kernels.md."""
+    import csv
+    import collections
+    from linear_recurrent_sequence_shortconv_amd.workloads import workloads
+    w = workloads()[workload]
+
+    def counters(sub):
+        agg = collections.defaultdict(list)
+        for r in csv.DictReader(open(os.path.join(d, sub, "run_counter_collection.csv"))):
+            agg[r["Kernel_Name"]].append(float(r["Counter_Value"]))
+        return agg
+
+    def copy_kib(sub):   # the 1 GiB calibration copy: the largest dispatch
+        return max(max(v) for v in counters(sub).values())
+
+    f_factor = (1 << 30) / 1024 / copy_kib("cfetch")
+    w_factor = (1 << 30) / 1024 / copy_kib("cwrite")
+    names_of = {}          # first timer name of a kernel -> all its timer names
+    per = collections.defaultdict(lambda: {"fetch": [], "write": []})
+    for sub in ("fetch", "write"):
+        for name, vals in counters(sub).items():
+            fam = _family(name)
+            if fam:
+                names_of[fam[0]] = fam
+                per[fam[0]][sub] += vals
+    traffic = {}
+    for first, v in per.items():
+        if not v["fetch"] or not v["write"]:
+            continue
+        fb = sum(v["fetch"]) / len(v["fetch"]) * 1024 * f_factor
+        wb = sum(v["write"]) / len(v["write"]) * 1024 * w_factor
+        for n in names_of[first]:
+            traffic[n] = {"bytes_per_launch": round(fb + wb), "fetch_bytes": round(fb), "write_bytes": round(wb)}
+    times = {}
+    for r in csv.DictReader(open(os.path.join(d, "trace", "run_kernel_stats.csv"))):
+        fam = _family(r["Name"])
+        if fam:
+            names_of[fam[0]] = fam
+            t = times.setdefault(fam[0], [0, 0.0])
+            t[0] += int(r["Calls"])
+            t[1] += float(r["TotalDurationNs"])
+    counts = algorithmic_counts(w)
+    cmds = [
+        "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof/trace -o run -- python -u $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline",
+        "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof/fetch -o run -- python -u $R/bench.py --steps 1 --warmup 1 --no-cpu-baseline",
+        "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof/write -o run -- python -u $R/bench.py --steps 1 --warmup 1 --no-cpu-baseline",
+        "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof/cfetch -o run -- python -u $R/bench.py --calibrate-copy",
+        "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof/cwrite -o run -- python -u $R/bench.py --calibrate-copy",
+        f"python bench.py --summarize-profiles gpurun_out/prof --workload {workload}",
+    ]
+    rec = {"workload": workload, "sources_sha256": _sources_sha256(),
+           "calibration": {"fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4),
+                           "copy_bytes": 1 << 30},
+           "commands": cmds, "kernels": traffic}
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", "hbm_traffic.json"), "w") as f:
+        json.dump(rec, f, indent=1)
+    lines = [f"# Kernel time and HBM traffic, workload {workload}",
+             "",
+             f"B={w.B} T={w.T} H={w.H} d_k=d_v={w.d} L={w.L} chunk={w.chunk} {w.dtype}; one forward + backward step.",
+             "Made with (R = repository root on the GPU host; each rocprofv3 run on its own):",
+             "", "```"] + cmds + ["```", "",
+             f"HBM byte counters are scaled by the readings of a plain 1 GiB device copy: FETCH_SIZE x {f_factor:.3f}, "
+             f"WRITE_SIZE x {w_factor:.3f}.  `algorithmic` is the byte count each kernel must move "
+             "(bench.py, algorithmic_counts); `ratio` = measured / algorithmic.", "",
+             "| kernel | launches | avg us (rocprofv3) | algorithmic MB | measured MB | ratio | GB/s (algorithmic) | frac of 8 TB/s |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|"]
+    rows = []
+    for first, (calls, tot) in times.items():
+        avg_us = tot / calls / 1e3
+        c = counts.get(first)
+        if not c:
+            continue
+        meas = traffic.get(first, {}).get("bytes_per_launch")
+        gbs = c["bytes"] / (avg_us * 1e-6) / 1e9
+        rows.append((tot, f"| {' / '.join(names_of[first])} | {calls} | {avg_us:.1f} | {c['bytes'] / 1e6:.1f} | "
+                          f"{(meas / 1e6) if meas else float('nan'):.1f} | "
+                          f"{(meas / c['bytes']) if meas else float('nan'):.2f} | {gbs:.0f} | {gbs / HBM_PEAK_GBS:.3f} |"))
+    lines += [r for _, r in sorted(rows, reverse=True)]
+    with open(os.path.join(ROOT, "profiles", f"{workload}_kernels.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
 
 
 def roofline_for(name, counts, avg_ms, dtype, traffic=None):
@@ -162,7 +277,13 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--forward-only", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--summarize-profiles", metavar="DIR",
+                    help="write profiles/ summaries from the rocprofv3 runs under DIR and exit")
     args = ap.parse_args()
+
+    if args.summarize_profiles:
+        summarize_profiles(args.summarize_profiles, args.workload)
+        return
 
     if args.gpus != 1:
         print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -227,6 +348,21 @@ def main():
     torch.cuda.synchronize()
     ms = t_start.elapsed_time(t_end) / args.steps
 
+    # forward pass alone (same inputs, same workspace)
+    def fwd_step():
+        P.forward(q, k, v, alpha, beta, Wk, Wp, wbeta, conv, chunk=w.chunk, workspace=ws_f)
+
+    for _ in range(2):
+        fwd_step()
+    torch.cuda.synchronize()
+    f_start, f_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    f_start.record()
+    for _ in range(args.steps):
+        fwd_step()
+    f_end.record()
+    torch.cuda.synchronize()
+    ms_fwd = f_start.elapsed_time(f_end) / args.steps
+
     # per-kernel timing over a second timed region (HIP events around each launch)
     with P.KernelTimer() as kt:
         for _ in range(args.steps):
@@ -252,7 +388,7 @@ def main():
         cpu = cpu_baseline(w, x, backward=backward)
 
     line = {
-        "metric": "PRISM layer tokens/s (fwd+bwd step" + ("" if backward else "; forward only") + ")",
+        "metric": "PRISM layer tokens/s fwd and fwd+bwd at T=2K\u201316K; % of MFMA/HBM peak",
         "value": round(value, 1),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -267,6 +403,7 @@ def main():
         "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "d_k": w.d, "d_v": w.d,
                    "L": w.L, "chunk": w.chunk, "global_batch": w.B, "seq_len": w.T,
                    "passes": "fwd+bwd" if backward else "fwd", "parallelism": "single GPU"},
+        "forward": {"ms_per_step": round(ms_fwd, 4), "tokens_per_s": round(tokens / (ms_fwd * 1e-3), 1)},
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,
