@@ -84,6 +84,54 @@ __device__ inline void add_colsum(float* slot, int col, const f32x4& v, int lane
   if (lane < 16) slot[col] += s;
 }
 
+// Row and column sums of products over all of a wave's accumulator tiles,
+// kept in registers and reduced across lanes once (flush_*), instead of per
+// tile: r[i][q] is row m0 + 16 i + 4 (lane >> 4) + q summed over this lane's
+// columns, c[j] is column n0 + 16 j + (lane & 15) summed over this lane's rows.
+template <int RM, int RN>
+struct TileSums {
+  float r[RM][4];
+  float c[RN];
+  __device__ inline void zero() {
+#pragma unroll
+    for (int i = 0; i < RM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) r[i][q] = 0.f;
+#pragma unroll
+    for (int j = 0; j < RN; ++j) c[j] = 0.f;
+  }
+  __device__ inline void add(int i, int j, const f32x4& v, bool rows = true, bool cols = true) {
+    if (rows) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q) r[i][q] += v[q];
+    }
+    if (cols) c[j] += v[0] + v[1] + v[2] + v[3];
+  }
+  // slot[row] += row sums (one wave's private slots)
+  __device__ inline void flush_rows(float* slot, int m0, int lane) const {
+#pragma unroll
+    for (int i = 0; i < RM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float s = r[i][q];
+        s += __shfl_xor(s, 1);
+        s += __shfl_xor(s, 2);
+        s += __shfl_xor(s, 4);
+        s += __shfl_xor(s, 8);
+        if ((lane & 15) == 0) slot[m0 + 16 * i + 4 * (lane >> 4) + q] += s;
+      }
+  }
+  __device__ inline void flush_cols(float* slot, int n0, int lane) const {
+#pragma unroll
+    for (int j = 0; j < RN; ++j) {
+      float s = c[j];
+      s += __shfl_xor(s, 16);
+      s += __shfl_xor(s, 32);
+      if (lane < 16) slot[n0 + 16 * j + lane] += s;
+    }
+  }
+};
+
 // fp32 global rows -> operand-type LDS rows (optionally negated)
 template <typename E, int ROWS, int COLS, int NT>
 __device__ inline void g2s_rows_f32(E* s, int ld, const float* g, long gstride, float scale, int tid) {
@@ -881,6 +929,8 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
   dqa.zero();
   dka.zero();
   typedef Tiling<C, D, NW> TLD;
+  TileSums<TLC::RM, TLC::RN> dgs_;   // decay-gradient row / column sums over all steps
+  dgs_.zero();
   RegTile<E, C, D, NT> kl, wl;   // next step's K_l, W_l rows (software prefetch)
   if (L > 0) {
     const long lrow = (long)bh * L * Tp + tb;
@@ -938,8 +988,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
               Rb[t * LT + ii] = to_t<E>(rv);
               Xb[t * LT + ii] = to_t<E>(gam * drv);
             }
-            add_rowsum(rs + wave * C, t0, p, lane);
-            add_colsum(cs + wave * C, ii, p, lane);
+            dgs_.add(i, j, p);
           }
       }
     }
@@ -968,8 +1017,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
               NFb[t * LT + ii] = to_t<E>(-fv);
               Gb[t * LT + ii] = to_t<E>(gam * dfv);
             }
-            add_rowsum(rs + wave * C, t0, p, lane);
-            add_colsum(cs + wave * C, ii, p, lane);
+            dgs_.add(i, j, p);
           }
       }
     }
@@ -1008,33 +1056,86 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
     __syncthreads();
   }
 
-  // ---- final dq, dk, dv ----
+  // ---- final dq, dk (and dv when L = 0) ----
+  if (actC) {
+    dgs_.flush_rows(rs + wave * C, TLC::m0(wave), lane);
+    dgs_.flush_cols(cs + wave * C, TLC::n0(wave), lane);
+  }
+  // fp32 products staged in LDS (every tile buffer is free now), then added
+  // to the solve kernel's parts and stored as full rows
   const float* dqc = dqp + cidx * C * D;
   const float* dkc = dkp + cidx * C * D;
   const float* dvc = dVp + cidx * C * D;
-  E* dqo = dq + row0 * D;
-  E* dko = dk + row0 * D;
+  RegTile<float, C, D, NT> rq, rk;
+  rq.load(dqc, D, C, tid);
+  rk.load(dkc, D, C, tid);
+  constexpr int LF = D + 4;
+  float* Sq = reinterpret_cast<float*>(smem + LY::O_Q);
+  float* Sk = Sq + C * LF;
+  static_assert(LY::O_Q + 2 * C * LF * 4 <= LY::TOTAL, "staging fits");
   for_tiles(dqa, wave, lane, [&](int t0, int f, const f32x4& x) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = t0 + r;
-      if (t < nval) dqo[(long)t * ts + f] = to_t<E>(x[r] + dqc[(long)t * D + f]);
-    }
+    for (int r = 0; r < 4; ++r) Sq[(t0 + r) * LF + f] = x[r];
   });
   for_tiles(dka, wave, lane, [&](int t0, int f, const f32x4& x) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = t0 + r;
-      if (t < nval) dko[(long)t * ts + f] = to_t<E>(x[r] + dkc[(long)t * D + f]);
-    }
+    for (int r = 0; r < 4; ++r) Sk[(t0 + r) * LF + f] = x[r];
   });
+  __syncthreads();
+  {
+    typedef RegTile<float, C, D, NT> RT;
+    E* dqo = dq + row0 * D;
+    E* dko = dk + row0 * D;
+#pragma unroll
+    for (int p = 0; p < RT::PER; ++p) {
+      const int u = tid + p * NT;
+      const int r = u / RT::VPR, c0 = (u % RT::VPR) * 4;
+      if (u < RT::NU && r < nval) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(&rq.v[p][0]);
+        const f32x4 b = *reinterpret_cast<const f32x4*>(&rk.v[p][0]);
+        E oq[4], ok[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          oq[j] = to_t<E>(a[j] + Sq[r * LF + c0 + j]);
+          ok[j] = to_t<E>(b[j] + Sk[r * LF + c0 + j]);
+        }
+        if constexpr (sizeof(E) == 2) {
+          uint2 wq, wk;
+          __builtin_memcpy(&wq, oq, 8);
+          __builtin_memcpy(&wk, ok, 8);
+          *reinterpret_cast<uint2*>(dqo + (long)r * ts + c0) = wq;
+          *reinterpret_cast<uint2*>(dko + (long)r * ts + c0) = wk;
+        } else {
+          uint4 wq, wk;
+          __builtin_memcpy(&wq, oq, 16);
+          __builtin_memcpy(&wk, ok, 16);
+          *reinterpret_cast<uint4*>(dqo + (long)r * ts + c0) = wq;
+          *reinterpret_cast<uint4*>(dko + (long)r * ts + c0) = wk;
+        }
+      }
+    }
+  }
   // with L > 0 the direct v-gradient dV' (chunk rows [bh][c][t] = token rows
   // [bh][c C + t]) is completed by the refinement backward
   if (L == 0) {
     E* dvo = dv + row0 * D;
-    for (int e = tid; e < C * D; e += NT) {
-      const int t = e / D, f = e % D;
-      if (t < nval) dvo[(long)t * ts + f] = to_t<E>(dvc[(long)t * D + f]);
+    for (int e = tid; e < C * D / 4; e += NT) {
+      const int t = e / (D / 4), f = (e % (D / 4)) * 4;
+      if (t < nval) {
+        const f32x4 a = *reinterpret_cast<const f32x4*>(dvc + (long)t * D + f);
+        E o4[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) o4[j] = to_t<E>(a[j]);
+        if constexpr (sizeof(E) == 2) {
+          uint2 w2;
+          __builtin_memcpy(&w2, o4, 8);
+          *reinterpret_cast<uint2*>(dvo + (long)t * ts + f) = w2;
+        } else {
+          uint4 w4;
+          __builtin_memcpy(&w4, o4, 16);
+          *reinterpret_cast<uint4*>(dvo + (long)t * ts + f) = w4;
+        }
+      }
     }
   }
   __syncthreads();
