@@ -63,27 +63,6 @@ __device__ inline void chunk_decays(const float* alpha, const float* beta, long 
   }
 }
 
-// Row sums (over the 16 lanes of a row group) and column sums (over the 4
-// rows of a lane and the 4 row groups) of one accumulator tile, added into
-// this wave's private slots.
-__device__ inline void add_rowsum(float* slot, int row0, const f32x4& v, int lane) {
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    float s = v[i];
-    s += __shfl_xor(s, 1);
-    s += __shfl_xor(s, 2);
-    s += __shfl_xor(s, 4);
-    s += __shfl_xor(s, 8);
-    if ((lane & 15) == 0) slot[row0 + i] += s;
-  }
-}
-__device__ inline void add_colsum(float* slot, int col, const f32x4& v, int lane) {
-  float s = v[0] + v[1] + v[2] + v[3];
-  s += __shfl_xor(s, 16);
-  s += __shfl_xor(s, 32);
-  if (lane < 16) slot[col] += s;
-}
-
 // Row and column sums of products over all of a wave's accumulator tiles,
 // kept in registers and reduced across lanes once (flush_*), instead of per
 // tile: r[i][q] is row m0 + 16 i + 4 (lane >> 4) + q summed over this lane's
@@ -200,6 +179,9 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
   const long cidx = (long)bh * NC + c;
 
   for (int e = tid; e < NW * C + NW; e += NT) ddw[e] = 0.f;
+  typedef Tiling<C, D, NW> TLS;
+  TileSums<TLS::RM, TLS::RN> dds;   // row sums of the dD terms, over all products
+  dds.zero();
   if (wave == 0) chunk_decays<C>(alpha, nullptr, row0, H, nval, g, ev, Dv, nullptr, nullptr, nullptr, lane);
   g2s_rows<E, C, D, NT>(R1, LR, dO + row0 * D, ts, nval, tid);
   g2s_rows<E, D, D, NT>(X1, LD2, St + cidx * D * D, D, D, tid);
@@ -280,14 +262,14 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
     u.zero();
     gemm_acc<E, C, D, D, NW, true, true>(u, R1, LR, X1, LD2, wave, lane);
     float* out = dUs + cidx * C * D;
-    for_tiles(u, wave, lane, [&](int t0, int rr, const f32x4& x) {
+    for_tiles_ij(u, wave, lane, [&](int i, int j, int t0, int rr, const f32x4& x) {
       f32x4 pu;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         out[(long)(t0 + r) * D + rr] = Dv[t0 + r] * x[r];
         pu[r] = x[r] * to_f(R2[(t0 + r) * LR + rr]);
       }
-      add_rowsum(ddw + wave * C, t0, pu, lane);
+      dds.add(i, j, pu, true, false);
     });
   }
   // ---- refinement pairs: dW_l += D (K_l dS_n^T), dK_l += D (W_l dS_n) ----
@@ -304,14 +286,14 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
     a.zero();
     gemm_acc<E, C, D, D, NW, true, true>(a, R3, LR, X1, LD2, wave, lane);
     float* ow = dWls + lrow * D;
-    for_tiles(a, wave, lane, [&](int t0, int rr, const f32x4& x) {
+    for_tiles_ij(a, wave, lane, [&](int i, int j, int t0, int rr, const f32x4& x) {
       f32x4 pw;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         ow[(long)(t0 + r) * D + rr] = Dv[t0 + r] * x[r];
         pw[r] = x[r] * to_f(R4[(t0 + r) * LR + rr]);
       }
-      add_rowsum(ddw + wave * C, t0, pw, lane);
+      dds.add(i, j, pw, true, false);
     });
     Acc<C, D, NW> bb;
     bb.zero();
@@ -340,14 +322,14 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
     a.zero();
     gemm_acc<E, C, D, D, NW, true, true>(a, R1, LR, X1, LD2, wave, lane);
     float* out = dWks + cidx * C * D;
-    for_tiles(a, wave, lane, [&](int t0, int kk, const f32x4& x) {
+    for_tiles_ij(a, wave, lane, [&](int i, int j, int t0, int kk, const f32x4& x) {
       f32x4 pw;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         out[(long)(t0 + r) * D + kk] = Dv[t0 + r] * x[r];
         pw[r] = x[r] * to_f(R3[(t0 + r) * LR + kk]);
       }
-      add_rowsum(ddw + wave * C, t0, pw, lane);
+      dds.add(i, j, pw, true, false);
     });
     Acc<C, D, NW> bb;   // Wk dM: [t][n] = sum_k Wk[t][k] dM^T[n][k]
     bb.zero();
@@ -367,6 +349,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
         }
     }
   }
+  if (TLS::active(wave)) dds.flush_rows(ddw + wave * C, TLS::m0(wave), lane);
   __syncthreads();
   // ---- dg from D_t = exp(gC - g_t) and exp(gC) ----
   if (wave == 0) {
@@ -470,6 +453,15 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
   typedef Tiling<C, D, NW> TLD;
   typedef Tiling<C, C, NW> TLC;
   const bool actD = TLD::active(wave), actC = TLC::active(wave);
+  // row / column sums over all products, reduced across lanes once at the end
+  TileSums<TLC::RM, TLC::RN> sgc;   // rs (rows), cs (columns): decay gradient
+  TileSums<TLC::RM, TLC::RN> sbc;   // bs (rows): beta gradient, C x C products
+  TileSums<TLD::RM, TLD::RN> sbd;   // bs (rows): beta gradient, C x D products
+  TileSums<TLD::RM, TLD::RN> sed;   // es (rows)
+  sgc.zero();
+  sbc.zero();
+  sbd.zero();
+  sed.zero();
 
   // K_l, W_l rows of the first fold step and the V rows are fetched early
   RegTile<E, C, D, NT> kl, wl, vn;
@@ -672,8 +664,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
             pr[r] = d_ * r0.v[i][j][r];
             Xb[t * LT + ii] = to_t<E>(ii <= t ? __expf(g[t] - g[ii]) * d_ : 0.f);
           }
-          add_rowsum(rs + wave * C, t0, pr, lane);
-          add_colsum(cs + wave * C, ii, pr, lane);
+          sgc.add(i, j, pr);
         }
     }
   }
@@ -743,8 +734,8 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
             pk[r] = to_f(Kr[t * LR + f]) * x2.v[i][j][r];
             dk.v[i][j][r] += be[t] * x2.v[i][j][r];
           }
-          add_rowsum(bs + wave * C, t0, pb, lane);
-          add_rowsum(es + wave * C, t0, pk, lane);
+          sbd.add(i, j, pb, true, false);
+          sed.add(i, j, pk, true, false);
         }
     }
   }
@@ -810,9 +801,8 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
             py[r] = dy * yv;                        // dg via Gam
             Zf[t * LA + jj] = gam * dy;             // dG0
           }
-          add_rowsum(bs + wave * C, t0, pb, lane);
-          add_rowsum(rs + wave * C, t0, py, lane);
-          add_colsum(cs + wave * C, jj, py, lane);
+          sbc.add(i, j, pb, true, false);
+          sgc.add(i, j, py);
         }
     }
   }
@@ -835,6 +825,15 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
 #pragma unroll
     for (int r = 0; r < 4; ++r) dkc[(long)(t0 + r) * D + f] = x[r];
   });
+  if (actC) {
+    sgc.flush_rows(rs + wave * C, TLC::m0(wave), lane);
+    sgc.flush_cols(cs + wave * C, TLC::n0(wave), lane);
+    sbc.flush_rows(bs + wave * C, TLC::m0(wave), lane);
+  }
+  if (actD) {
+    sbd.flush_rows(bs + wave * C, TLD::m0(wave), lane);
+    sed.flush_rows(es + wave * C, TLD::m0(wave), lane);
+  }
   __syncthreads();
   if (tid < C) {
     const int t = tid;

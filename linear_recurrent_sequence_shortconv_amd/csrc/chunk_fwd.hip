@@ -90,35 +90,60 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
   E* Qr = reinterpret_cast<E*>(smem + LY::O_Q);
   E* Kr = reinterpret_cast<E*>(smem + LY::O_K);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nblk = B * H * NC;
-  const int bid = xcd_swizzle(blockIdx.x, nblk);
+  const long ts = (long)H * D;
+  // At d = 128 (one workgroup per CU) workgroups are persistent: they take
+  // the virtual block ids blockIdx.x, + gridDim.x, ..., and a chunk's first
+  // operands (Q and K rows, alpha, beta, the first K_l and W_l tiles) are
+  // fetched while the previous chunk is being finished.  Smaller d launch one
+  // workgroup per chunk (the loop runs once).
+  constexpr bool PERSIST = D >= 128;
+  const int vstride = PERSIST ? (int)gridDim.x : nblk;
+  RegTile<E, C, D, NT, true> kn, wn;   // K_l, W_l tiles of the next product step
+  RegTile<E, C, D, NT> qn, kr;         // Q, K rows of the next chunk
+  float pa = 1.f, pb = 0.f;            // alpha, beta of the next chunk (wave 0, lane < C)
+  auto prefetch = [&](int vid) {
+    const int bid = xcd_swizzle(vid, nblk);
+    const int c = bid % NC, bh = bid / NC;
+    const int h = bh % H, b = bh / H;
+    const int tb = c * C;
+    const int nval = min(C, T - tb);
+    const long row0 = ((long)b * T + tb) * H + h;
+    if (L > 0) {
+      kn.load(Kl + (long)bh * L * Tp * D + (long)tb * D, D, C, tid);
+      wn.load(Wl + (long)bh * L * Tp * D + (long)tb * D, D, C, tid);
+    }
+    qn.load(q + row0 * D, ts, nval, tid);
+    kr.load(k + row0 * D, ts, nval, tid);
+    if (wave == 0) {
+      pa = lane < nval ? alpha[row0 + (long)lane * H] : 1.f;
+      pb = lane < nval ? beta[row0 + (long)lane * H] : 0.f;
+    }
+  };
+  if ((int)blockIdx.x < nblk) prefetch(blockIdx.x);
+  for (int vid = blockIdx.x; vid < nblk; vid += vstride) {
+  // per-lane values are redefined each iteration, so that the lane-dependent
+  // address arithmetic of the body is not hoisted out of the loop and kept
+  // live across it
+  if constexpr (PERSIST) {
+    asm volatile("" : "+v"(tid));
+    lane = tid & 63;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  }
+  const int bid = xcd_swizzle(vid, nblk);
   const int c = bid % NC, bh = bid / NC;
   const int h = bh % H, b = bh / H;
   const int tb = c * C;
   const int nval = min(C, T - tb);
-  const long ts = (long)H * D;
   const long row0 = ((long)b * T + tb) * H + h;
-  const E* qc = q + row0 * D;
-  const E* kc = k + row0 * D;
   const E* vc = v + row0 * D;
-
-  // the first refinement step's K_l, W_l tiles are fetched while phase A runs
   const E* Klb = Kl + (long)bh * L * Tp * D + (long)tb * D;
   const E* Wlb = Wl + (long)bh * L * Tp * D + (long)tb * D;
-  RegTile<E, C, D, NT, true> kn, wn;
-  if (L > 0) {
-    kn.load(Klb, D, C, tid);
-    wn.load(Wlb, D, C, tid);
-  }
 
   // ---- phase A: decays and gates; Q, K tiles ----
   if (wave == 0) {
-    float lg = 0.f, bv = 0.f;
-    if (lane < nval) {
-      lg = logf(alpha[row0 + (long)lane * H]);
-      bv = beta[row0 + (long)lane * H];
-    }
+    const float lg = logf(pa), bv = pb;   // alpha = 1, beta = 0 past the end
     float s = lg;
 #pragma unroll
     for (int off = 1; off < 64; off <<= 1) {
@@ -136,8 +161,8 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
     }
     if (lane == 0) gCo[(long)bh * NC + c] = gC;
   }
-  g2s_rows<E, C, D, NT>(Qr, LR, qc, ts, nval, tid);
-  g2s_rows<E, C, D, NT>(Kr, LR, kc, ts, nval, tid);
+  qn.store_rows(Qr, LR, tid);
+  kr.store_rows(Kr, LR, tid);
   __syncthreads();
 
   // ---- phase B: refinement pairs, one step l at a time ----
@@ -231,9 +256,15 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
     KtD[f * LT + t] = to_t<E>(Dv[t] * kv);
   }
   vn.store_rows(Vr, LR, tid);
-  __syncthreads();
   RegTile<E, C, D, NT, true> on;   // dO rows (backward mode), in flight during the products below
   if constexpr (BWD) on.load(dO + row0 * D, ts, nval, tid);
+  // the next chunk's first operands are fetched during the rest of this one
+  // (issued after every load this chunk still waits for: loads complete in
+  // order)
+  if constexpr (PERSIST) {
+    if (vid + vstride < nblk) prefetch(vid + vstride);
+  }
+  __syncthreads();
   for_tiles(vacc, wave, lane, [&](int t0, int f, const f32x4& x) {
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -346,6 +377,9 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
       *reinterpret_cast<f32x4*>(ETc + (long)n * D + r0) = x;
     });
   }
+  if constexpr (!PERSIST) break;
+  __syncthreads();   // LDS is reused by the next chunk
+  }
 }
 
 template <typename E, int D, int C>
@@ -356,13 +390,15 @@ static hipError_t chunk_launch_dc(const Dims& d, const E* q, const E* k, const E
   if constexpr (sizeof(E) == 4 && D * C > 2048) return hipErrorInvalidValue;   // fp32 envelope
   const int nblk = d.B * d.H * d.NC;
   if (dO)
-    hipLaunchKernelGGL((chunk_fwd_kernel<E, D, C, true>), dim3(nblk), dim3(CF_NT), 0, s, q, k, v,
-                       alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, M, ET, UT, WkT, d.B, d.T, d.H,
-                       d.L, d.NC, d.Tp);
+    hipLaunchKernelGGL((chunk_fwd_kernel<E, D, C, true>),
+                       dim3(D >= 128 ? persistent_grid(chunk_fwd_kernel<E, D, C, true>, CF_NT, nblk) : nblk),
+                       dim3(CF_NT), 0, s, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC,
+                       M, ET, UT, WkT, d.B, d.T, d.H, d.L, d.NC, d.Tp);
   else
-    hipLaunchKernelGGL((chunk_fwd_kernel<E, D, C, false>), dim3(nblk), dim3(CF_NT), 0, s, q, k, v,
-                       alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, M, ET, UT, WkT, d.B, d.T, d.H,
-                       d.L, d.NC, d.Tp);
+    hipLaunchKernelGGL((chunk_fwd_kernel<E, D, C, false>),
+                       dim3(D >= 128 ? persistent_grid(chunk_fwd_kernel<E, D, C, false>, CF_NT, nblk) : nblk),
+                       dim3(CF_NT), 0, s, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC,
+                       M, ET, UT, WkT, d.B, d.T, d.H, d.L, d.NC, d.Tp);
   return hipGetLastError();
 }
 

@@ -17,6 +17,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <map>
+#include <mutex>
+#include <utility>
+
 namespace prism {
 
 typedef __bf16 bf16;
@@ -222,6 +226,19 @@ __device__ inline void for_tiles(const Acc<M, N, NW>& acc, int wave, int lane, F
 #pragma unroll
     for (int j = 0; j < TL::RN; ++j)
       f(m0 + 16 * i + 4 * (lane >> 4), n0 + 16 * j + (lane & 15), acc.v[i][j]);
+}
+
+// Same visit, also passing the tile indices: f(i, j, row0, col, vals).
+template <int M, int N, int NW, typename F>
+__device__ inline void for_tiles_ij(const Acc<M, N, NW>& acc, int wave, int lane, F&& f) {
+  typedef Tiling<M, N, NW> TL;
+  if (!TL::active(wave)) return;
+  const int m0 = TL::m0(wave), n0 = TL::n0(wave);
+#pragma unroll
+  for (int i = 0; i < TL::RM; ++i)
+#pragma unroll
+    for (int j = 0; j < TL::RN; ++j)
+      f(i, j, m0 + 16 * i + 4 * (lane >> 4), n0 + 16 * j + (lane & 15), acc.v[i][j]);
 }
 
 // Same visit, with a mutable accumulator (to rescale or reset in place).
@@ -507,6 +524,36 @@ __device__ inline int xcd_swizzle(int bid, int nblocks) {
   if (nblocks % NXCD != 0) return bid;
   const int per = nblocks / NXCD;
   return (bid % NXCD) * per + bid / NXCD;
+}
+
+// --------------------------------------------------------------------------
+// host: grid of a persistent kernel = resident workgroups per CU x CUs on the
+// current device (at most nblk), cached per kernel and device
+// --------------------------------------------------------------------------
+template <typename K>
+inline int persistent_grid(K kernel, int threads, int nblk) {
+  static std::mutex mu;
+  static std::map<std::pair<const void*, int>, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nblk;
+  const std::pair<const void*, int> key(reinterpret_cast<const void*>(kernel), dev);
+  int g = 0;
+  {
+    std::lock_guard<std::mutex> lk(mu);
+    auto it = cache.find(key);
+    if (it != cache.end()) g = it->second;
+  }
+  if (g == 0) {
+    int ncu = 0, per = 0;
+    if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per, kernel, threads, 0) != hipSuccess ||
+        ncu <= 0 || per <= 0)
+      return nblk;
+    g = ncu * per;
+    std::lock_guard<std::mutex> lk(mu);
+    cache[key] = g;
+  }
+  return g < nblk ? g : nblk;
 }
 
 }  // namespace prism
