@@ -1024,20 +1024,12 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
     Acc<C, D, NW> dkl, dwl;
     dkl.zero();
     dwl.zero();
-    // (scheduling barriers keep the six independent products from being
-    //  interleaved, which would multiply the live fragment registers)
     gemm_acc<E, C, D, C, NW, false, false>(dkl, Xb, LT, Qr, LR, wave, lane);    // X_l^T Q
-    __builtin_amdgcn_sched_barrier(0);
     gemm_acc<E, C, D, C, NW, false, false>(dkl, Gb, LT, Kr, LR, wave, lane);    // dG_l^T K
-    __builtin_amdgcn_sched_barrier(0);
     gemm_acc<E, C, D, C, NW, false, false>(dwl, Rb, LT, dOr, LR, wave, lane);   // R_l^T dO
-    __builtin_amdgcn_sched_barrier(0);
     gemm_acc<E, C, D, C, NW, false, false>(dwl, NFb, LT, dVr, LR, wave, lane);  // -F_l^T dV'
-    __builtin_amdgcn_sched_barrier(0);
     gemm_acc<E, C, D, C, NW, true, false>(dqa, Xb, LT, Klr, LR, wave, lane);    // X_l K_l
-    __builtin_amdgcn_sched_barrier(0);
     gemm_acc<E, C, D, C, NW, true, false>(dka, Gb, LT, Klr, LR, wave, lane);    // dG_l K_l
-    __builtin_amdgcn_sched_barrier(0);
     if (TLD::active(wave)) {
 #pragma unroll
       for (int i = 0; i < TLD::RM; ++i)

@@ -143,7 +143,9 @@ template <int M, int N, int NW> struct Tiling {
   static constexpr int RN = (TN + WN - 1) / WN;   // tiles per wave along N
   static_assert(M % 16 == 0 && N % 16 == 0, "tile multiple");
   static_assert(TM % WM == 0 && TN % WN == 0, "even split");
-  __device__ static inline bool active(int wave) { return wave < WM * WN; }
+  // every wave of the workgroup is active when the grid uses all NW (folds at
+  // compile time)
+  __device__ static inline bool active(int wave) { return WM * WN >= NW || wave < WM * WN; }
   // first tile row / col of this wave's block
   __device__ static inline int m0(int wave) { return (wave / WN) * RM * 16; }
   __device__ static inline int n0(int wave) { return (wave % WN) * RN * 16; }

@@ -77,6 +77,9 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
   constexpr int LW = D + 4;               // fp32 rows: staggers rows 4 apart across banks
   constexpr int NFT = D / 16;
   constexpr int FPW = (NFT + 3) / 4;      // feature tiles per wave
+  // feature tile n exists; always true when the tiles divide evenly over the
+  // feature groups (then the test folds away at compile time)
+#define FT_OK(n) (NFT % 4 == 0 || (n) < NFT)
   constexpr int KS = Mfma<E>::KSTEP;
   constexpr int VN = 16 / sizeof(E);
   __shared__ __attribute__((aligned(16))) E vbuf[(RB_TT + 3) * D];   // v rows t0-3 .. t0+RB_TT-1
@@ -136,20 +139,20 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
     const int f = 16 * n + (lane & 15);
     float tp[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) tp[j] = (n < NFT) ? ctp[f * 4 + j] : 0.f;
+    for (int j = 0; j < 4; ++j) tp[j] = (FT_OK(n)) ? ctp[f * 4 + j] : 0.f;
 #pragma unroll
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 16 * m + 4 * (lane >> 4) + i;
         float u = 0.f, val = 0.f;
-        if (n < NFT && t < nrow) {
+        if (FT_OK(n) && t < nrow) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) u += tp[j] * to_f(vbuf[(t + 3 - j) * D + f]);
           val = to_f(vbuf[(t + 3) * D + f]) - u;
         }
         r[m][nn][i] = val;
-        if (n < NFT) {
+        if (FT_OK(n)) {
           const E uh = to_t<E>(u);
           ubuf[t * LD + f] = uh;
           if constexpr (sizeof(E) == 2) ulo[t * LD + f] = to_t<E>(u - to_f(uh));
@@ -191,7 +194,7 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
     for (int nn = 0; nn < FPW; ++nn)
 #pragma unroll
       for (int kk = 0; kk < D / KS; ++kk)
-        if (fq + 4 * nn < NFT) bws[nn][kk] = load_frag<E, true>(W, D, 16 * (fq + 4 * nn), kk * KS, lane);
+        if (FT_OK(fq + 4 * nn)) bws[nn][kk] = load_frag<E, true>(W, D, 16 * (fq + 4 * nn), kk * KS, lane);
 #pragma unroll
     for (int k0 = 0; k0 < D; k0 += KS) {
       typename Mfma<E>::frag a[2], al[2];
@@ -203,7 +206,7 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
 #pragma unroll
       for (int nn = 0; nn < FPW; ++nn) {
         const int n = fq + 4 * nn;
-        if (n < NFT) {
+        if (FT_OK(n)) {
           const typename Mfma<E>::frag bw = bws[nn][k0 / KS];
 #pragma unroll
           for (int m = 0; m < 2; ++m) {
@@ -223,7 +226,7 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
     for (int nn = 0; nn < FPW; ++nn)
 #pragma unroll
       for (int kk = 0; kk < D / KS; ++kk)
-        if (fq + 4 * nn < NFT) bws[nn][kk] = load_frag<E, true>(WT, D, 16 * (fq + 4 * nn), kk * KS, lane);
+        if (FT_OK(fq + 4 * nn)) bws[nn][kk] = load_frag<E, true>(WT, D, 16 * (fq + 4 * nn), kk * KS, lane);
 #pragma unroll
     for (int k0 = 0; k0 < D; k0 += KS) {
       typename Mfma<E>::frag a[2];
@@ -235,7 +238,7 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
 #pragma unroll
       for (int nn = 0; nn < FPW; ++nn) {
         const int n = fq + 4 * nn;
-        if (n < NFT) {
+        if (FT_OK(n)) {
           const typename Mfma<E>::frag bw = bws[nn][k0 / KS];
 #pragma unroll
           for (int m = 0; m < 2; ++m) acc[m][nn] = Mfma<E>::mma(a[m], bw, acc[m][nn]);
@@ -293,7 +296,7 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
           const int t = 16 * m + 4 * (lane >> 4) + i;
           float dl;
           gelu_and_grad(p[m][nn][i] * rs[l][m][nn][i], dl, dg_[m][nn][i]);
-          if (n < NFT) part[i] += dl * gw[t * LW + f];
+          if (FT_OK(n)) part[i] += dl * gw[t * LW + f];
         }
       }
 #pragma unroll
@@ -317,7 +320,7 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
 #pragma unroll
       for (int nn = 0; nn < FPW; ++nn) {
         const int n = fq + 4 * nn;
-        if (n >= NFT) continue;
+        if (!FT_OK(n)) continue;
         const int f = 16 * n + (lane & 15);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -346,7 +349,7 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int t = 16 * m + 4 * (lane >> 4) + i;
-            dvd[m][nn][i] = (n < NFT && t < own) ? dvs[(long)t * D + f] : 0.f;
+            dvd[m][nn][i] = (FT_OK(n) && t < own) ? dvs[(long)t * D + f] : 0.f;
           }
         }
     }
@@ -359,7 +362,7 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
 #pragma unroll
     for (int nn = 0; nn < FPW; ++nn) {
       const int n = fq + 4 * nn;
-      if (n >= NFT) continue;
+      if (!FT_OK(n)) continue;
       const int f = 16 * n + (lane & 15);
       const float wbf = to_f(wb[f]);
       float cs = 0.f;
@@ -390,7 +393,7 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
 #pragma unroll
     for (int nn = 0; nn < FPW; ++nn) {
       const int n = fq + 4 * nn;
-      if (n >= NFT) continue;
+      if (!FT_OK(n)) continue;
       const int f = 16 * n + (lane & 15);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -405,7 +408,7 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
 #pragma unroll
     for (int nn = 0; nn < FPW; ++nn) {
       const int n = fq + 4 * nn;
-      if (n >= NFT) continue;
+      if (!FT_OK(n)) continue;
       const int f = 16 * n + (lane & 15);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -694,4 +697,5 @@ hipError_t launch_refine_bwd(const Dims& d, const RefineBwdArgs<E>& a, int stage
 template hipError_t launch_refine_bwd<bf16>(const Dims&, const RefineBwdArgs<bf16>&, int, hipStream_t);
 template hipError_t launch_refine_bwd<float>(const Dims&, const RefineBwdArgs<float>&, int, hipStream_t);
 
+#undef FT_OK
 }  // namespace prism

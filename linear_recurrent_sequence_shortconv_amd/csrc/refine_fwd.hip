@@ -33,6 +33,9 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
   constexpr int LD = ldpad<E>(D);
   constexpr int NFT = D / 16;                          // feature tiles
   constexpr int FPW = (NFT + RF_NW - 1) / RF_NW;       // feature tiles per wave
+  // feature tile n exists; always true when the tiles divide evenly over the
+  // feature groups (then the test folds away at compile time)
+#define FT_OK(n) (NFT % RF_NW == 0 || (n) < NFT)
   constexpr int KS = Mfma<E>::KSTEP;
   constexpr int NK = D / KS;
   constexpr int VN = 16 / sizeof(E);
@@ -79,7 +82,7 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
       const int n = wave + RF_NW * nn;
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk)
-        if (n < NFT) bw[nn][kk] = load_frag<E, true>(W, D, 16 * n, kk * KS, lane);
+        if (FT_OK(n)) bw[nn][kk] = load_frag<E, true>(W, D, 16 * n, kk * KS, lane);
     }
   };
   Frag bw[FPW][NK];   // weight fragments of the next projection (W_p^(1) now)
@@ -97,20 +100,20 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
     const int f = 16 * n + (lane & 15);
     float taps[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) taps[j] = (n < NFT) ? to_f(ch[f * 4 + j]) : 0.f;
+    for (int j = 0; j < 4; ++j) taps[j] = (FT_OK(n)) ? to_f(ch[f * 4 + j]) : 0.f;
 #pragma unroll
     for (int m = 0; m < 4; ++m)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int t = 16 * m + 4 * (lane >> 4) + i;
         float u = 0.f, val = 0.f;
-        if (n < NFT && t0 + t < T) {
+        if (FT_OK(n) && t0 + t < T) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) u += taps[j] * to_f(vbuf[(t + 3 - j) * D + f]);
           val = to_f(vbuf[(t + 3) * D + f]) - u;
         }
         r[m][nn][i] = val;
-        if (n < NFT) {
+        if (FT_OK(n)) {
           const E uh = to_t<E>(u);
           ubuf[t * LD + f] = uh;
           if constexpr (sizeof(E) == 2) ulo[t * LD + f] = to_t<E>(u - to_f(uh));
@@ -158,7 +161,7 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
       for (int m = 0; m < 4; ++m) a[m] = load_frag<E, true>(ubuf, LD, 16 * m, kk * KS, lane);
 #pragma unroll
       for (int nn = 0; nn < FPW; ++nn)
-        if (wave + RF_NW * nn < NFT) {
+        if (FT_OK(wave + RF_NW * nn)) {
 #pragma unroll
           for (int m = 0; m < 4; ++m) acc[m][nn] = Mfma<E>::mma(a[m], bw[nn][kk], acc[m][nn]);
         }
@@ -168,7 +171,7 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
           for (int m = 0; m < 4; ++m) a[m] = load_frag<E, true>(ulo, LD, 16 * m, kk * KS, lane);
 #pragma unroll
           for (int nn = 0; nn < FPW; ++nn)
-            if (wave + RF_NW * nn < NFT) {
+            if (FT_OK(wave + RF_NW * nn)) {
 #pragma unroll
               for (int m = 0; m < 4; ++m) acc[m][nn] = Mfma<E>::mma(a[m], bw[nn][kk], acc[m][nn]);
             }
@@ -188,7 +191,7 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
 #pragma unroll
       for (int nn = 0; nn < FPW; ++nn) {
         const int n = wave + RF_NW * nn;
-        if (n < NFT) {
+        if (FT_OK(n)) {
           const int f = 16 * n + (lane & 15);
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
@@ -206,7 +209,7 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
 #pragma unroll
       for (int nn = 0; nn < FPW; ++nn) {
         const int n = wave + RF_NW * nn;
-        if (n < NFT) {
+        if (FT_OK(n)) {
           const int f = 16 * n + (lane & 15);
 #pragma unroll
           for (int i = 0; i < 4; ++i) obk[(16 * m + 4 * (lane >> 4) + i) * LD + f] = to_t<E>(acc[m][nn][i]);
@@ -249,4 +252,5 @@ template hipError_t launch_refine_fwd<bf16>(const Dims&, const bf16*, const bf16
 template hipError_t launch_refine_fwd<float>(const Dims&, const float*, const float*, const float*,
                                              const float*, const float*, float*, float*, hipStream_t);
 
+#undef FT_OK
 }  // namespace prism
