@@ -3,10 +3,12 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload lm-T2048]
 
 One step = one pass of the whole hot path over one batch of synthetic input
-with the inputs already resident in HBM: the forward pass (ShortConv anchor,
-L refinement steps, chunked scan, readout, final state) followed by the
-backward pass (every input and weight gradient) when the library provides
-it.  The default workload is the language-model layer shape: B=8, H=16,
+with the inputs already resident in HBM: the training forward (ShortConv
+anchor, L refinement steps, chunked scan, readout, final state; it keeps the
+intermediates the backward needs) followed by the training backward (every
+input and weight gradient).  The stateless pair (prism_forward +
+prism_backward, which recomputes the forward) is timed as well and reported
+beside it.  The default workload is the language-model layer shape: B=8, H=16,
 T=2048, d_k=d_v=128, L=3, chunk 64, bf16 storage with fp32 accumulation.
 
 Prints one JSON line.  Besides the throughput it reports, for the kernel with
@@ -52,12 +54,14 @@ def algorithmic_counts(w):
     bh = B * H
     c = {}
     c["refine_fwd"] = (th * e * D + ntp * 2 * L * D * e, th * 4 * L * D * D)
+    # (the training forward also keeps U^T, W_k^T: + 2 C D e per chunk)
     c["chunk_fwd"] = (th * (3 * D * e + 8) + ntp * 2 * L * D * e
-                      + nch * (D * D * (e + 4) + C * D * (e + 4) + 4),
+                      + nch * (D * D * (e + 4) + C * D * (e + 4) + 4 + 2 * C * D * e),
                       nch * (2 * C * C * D * (4 * L + 6) + 2 * C * D * D * (L + 2)))
     c["chunk_fwd_bwdmode"] = (th * (4 * D * e + 8) + ntp * 2 * L * D * e
                               + nch * (2 * D * D * e + 2 * D * D * 4 + 2 * C * D * e + 4),
                               nch * (2 * C * C * D * (2 * L + 5) + 2 * C * D * D * (L + 4)))
+    c["et_chunks"] = (nch * (2 * C * D * e + D * D * 4), nch * 2 * C * D * D)
     st = (nch * D * D * (2 * e + 4) + bh * D * D * 4, nch * 2 * D ** 3)
     c["state_fwd"] = c["state_fwd_recompute"] = st
     c["state_bwd"] = (st[0] + bh * D * D * 4, st[1])
@@ -105,6 +109,7 @@ def measured_traffic():
 
 # rocprofv3 kernel names -> the timer names used by the library and above
 _FAMILIES = [("refine_fwd_kernel", ["refine_fwd", "refine_fwd_recompute"]),
+             ("et_kernel", ["et_chunks"]),
              ("state_pass_kernel", ["state_fwd", "state_fwd_recompute", "state_bwd"]),
              ("out_fwd_kernel", ["out_fwd"]),
              ("chunk_bwd_state_kernel", ["chunk_bwd_state"]),
@@ -327,12 +332,20 @@ def main():
         backward = False
     ws_f = P._workspace(P.forward_workspace_bytes(desc), q.device)[1]
     ws_b = P._workspace(P.backward_workspace_bytes(desc), q.device)[1] if backward else None
+    saved = P._workspace(P.saved_bytes(desc), q.device)[1] if backward else None
 
     def step():
-        P.forward(q, k, v, alpha, beta, Wk, Wp, wbeta, conv, chunk=w.chunk, workspace=ws_f)
+        # a training step: the forward keeps what the backward needs
+        P.forward(q, k, v, alpha, beta, Wk, Wp, wbeta, conv, chunk=w.chunk, workspace=ws_f,
+                  saved=saved)
         if backward:
             P.backward(q, k, v, alpha, beta, Wk, Wp, wbeta, conv, dO=dO, chunk=w.chunk,
-                       workspace=ws_b)
+                       workspace=ws_b, saved=saved)
+
+    def stateless_step():
+        P.forward(q, k, v, alpha, beta, Wk, Wp, wbeta, conv, chunk=w.chunk, workspace=ws_f)
+        P.backward(q, k, v, alpha, beta, Wk, Wp, wbeta, conv, dO=dO, chunk=w.chunk,
+                   workspace=ws_b)
 
     for _ in range(args.warmup):
         step()
@@ -347,6 +360,20 @@ def main():
     t_end.record()
     torch.cuda.synchronize()
     ms = t_start.elapsed_time(t_end) / args.steps
+
+    # the stateless pair (prism_forward + prism_backward, which recomputes)
+    ms_stateless = None
+    if backward:
+        for _ in range(2):
+            stateless_step()
+        torch.cuda.synchronize()
+        s_start, s_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_start.record()
+        for _ in range(args.steps):
+            stateless_step()
+        s_end.record()
+        torch.cuda.synchronize()
+        ms_stateless = s_start.elapsed_time(s_end) / args.steps
 
     # forward pass alone (same inputs, same workspace)
     def fwd_step():
@@ -404,6 +431,9 @@ def main():
                    "L": w.L, "chunk": w.chunk, "global_batch": w.B, "seq_len": w.T,
                    "passes": "fwd+bwd" if backward else "fwd", "parallelism": "single GPU"},
         "forward": {"ms_per_step": round(ms_fwd, 4), "tokens_per_s": round(tokens / (ms_fwd * 1e-3), 1)},
+        "stateless_pair": (None if ms_stateless is None else
+                           {"ms_per_step": round(ms_stateless, 4),
+                            "tokens_per_s": round(tokens / (ms_stateless * 1e-3), 1)}),
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,

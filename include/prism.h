@@ -116,6 +116,38 @@ prism_status prism_backward(const prism_desc* desc, const void* q, const void* k
                             float* dS0, void* workspace, size_t workspace_bytes,
                             hipStream_t stream);
 
+/* Training pair (saved intermediates).  prism_forward_train computes what
+ * prism_forward computes and also keeps, in the caller-owned `saved` buffer,
+ * the intermediates the backward needs: the refinement pairs (k^(l), w^(l))
+ * of every token, and per chunk the affine map M^T, the decay sum g_C, the
+ * chunk-entry state S_c, the readout operand Qt and the solve results U^T,
+ * W_k^T (summary §2.1-2.2 as rewritten per chunk).  prism_backward_train then
+ * returns the same gradients as prism_backward with the same inputs, starting
+ * from those intermediates instead of recomputing the forward.
+ *   saved:     device buffer of prism_saved_bytes() bytes, 256-byte aligned,
+ *              written by prism_forward_train, read by prism_backward_train;
+ *              the caller keeps it unchanged in between (same desc, same
+ *              inputs; the backward does not check this).
+ *   workspace: as for prism_forward / prism_backward (same sizes).
+ * Errors: as for the plain entry points; a NULL, misaligned or too small
+ * `saved` buffer gives PRISM_ERR_WORKSPACE / PRISM_ERR_ALIGN before any HIP
+ * call. */
+prism_status prism_saved_bytes(const prism_desc* desc, size_t* bytes);
+prism_status prism_forward_train(const prism_desc* desc, const void* q, const void* k,
+                                 const void* v, const float* alpha, const float* beta,
+                                 const void* Wk, const void* Wp, const void* wbeta,
+                                 const void* conv, const float* S0, void* o, float* ST,
+                                 void* saved, size_t saved_bytes, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
+prism_status prism_backward_train(const prism_desc* desc, const void* q, const void* k,
+                                  const void* v, const float* alpha, const float* beta,
+                                  const void* Wk, const void* Wp, const void* wbeta,
+                                  const void* conv, const float* S0, const void* saved,
+                                  size_t saved_bytes, const void* dO, const float* dST, void* dq,
+                                  void* dk, void* dv, float* dalpha, float* dbeta, float* dWk,
+                                  float* dWp, float* dwbeta, float* dconv, float* dS0,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 /* Human-readable name of a status code (static string). */
 const char* prism_status_string(prism_status status);
 

@@ -134,7 +134,7 @@ struct CB1Lds {
   static constexpr int SZ_DD = D * LD2 * (int)sizeof(E);
   static constexpr int O_VEC = 0;                                  // g, e, Dv (3C) + slots
   static constexpr int SZ_VEC = (3 * C + CB_NW * C + CB_NW) * 4;
-  static constexpr int O_X1 = (O_VEC + SZ_VEC + 15) / 16 * 16;     // S^T, then dS_n, then dM
+  static constexpr int O_X1 = (O_VEC + SZ_VEC + 15) / 16 * 16;     // S, then dS_n, then dM
   static constexpr int O_X2 = O_X1 + SZ_DD;                        // dS_n^T, then dM^T
   static constexpr int O_R1 = O_X2 + SZ_DD;                        // dO rows, then K rows
   static constexpr int O_R2 = O_R1 + SZ_R;                         // U rows
@@ -147,7 +147,7 @@ template <typename E, int D, int C>
 __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
     const E* __restrict__ k, const E* __restrict__ dO, const float* __restrict__ alpha,
     const E* __restrict__ Kl, const E* __restrict__ Wl, const E* __restrict__ UT,
-    const E* __restrict__ WkT, const E* __restrict__ St, const E* __restrict__ dSnT,
+    const E* __restrict__ WkT, const E* __restrict__ Sc, const E* __restrict__ dSnT,
     float* __restrict__ dQt, float* __restrict__ dUs, float* __restrict__ dWks,
     float* __restrict__ dKs, float* __restrict__ dKls, float* __restrict__ dWls,
     float* __restrict__ dgs, int B, int T, int H, int L, int NC, int Tp) {
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
   dds.zero();
   if (wave == 0) chunk_decays<C>(alpha, nullptr, row0, H, nval, g, ev, Dv, nullptr, nullptr, nullptr, lane);
   g2s_rows<E, C, D, NT>(R1, LR, dO + row0 * D, ts, nval, tid);
-  g2s_rows<E, D, D, NT>(X1, LD2, St + cidx * D * D, D, D, tid);
+  g2s_rows<E, D, D, NT>(X1, LD2, Sc + cidx * D * D, D, D, tid);   // S_c row-major
   g2s_rows<E, D, D, NT>(X2, LD2, dSnT + cidx * D * D, D, D, tid);
   // tiles of the next phase, in flight during the first products: dS_n^T
   // again (stored transposed, i.e. dS_n row-major), K rows, U^T
@@ -196,25 +196,27 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
   ut.load(UT + cidx * D * C, C, D, tid);
   __syncthreads();
 
-  // ---- dQt = dO S  ([t][k] = sum_r dO[t][r] S^T[k][r]);  dM = -S^T dS_n ----
+  // ---- dQt = dO S  ([t][k] = sum_r dO[t][r] S[r][k]);  dM = -S^T dS_n ----
+  // (X1 holds S row-major: both products read it k-strided)
   {
     Acc<C, D, NW> a;
     a.zero();
-    gemm_acc<E, C, D, D, NW, true, true>(a, R1, LR, X1, LD2, wave, lane);
+    gemm_acc<E, C, D, D, NW, true, false>(a, R1, LR, X1, LD2, wave, lane);
     float* out = dQt + cidx * C * D;
     for_tiles(a, wave, lane, [&](int t0, int kk, const f32x4& x) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) out[(long)(t0 + r) * D + kk] = x[r];
     });
   }
-  Acc<D, D, NW> dm;   // [k][n] = sum_r S^T[k][r] dS_n^T[n][r]  (= -dM)
+  Acc<D, D, NW> dm;   // [k][n] = sum_r S[r][k] dS_n^T[n][r]  (= -dM)
   dm.zero();
-  gemm_acc<E, D, D, D, NW, true, true>(dm, X1, LD2, X2, LD2, wave, lane);
+  gemm_acc<E, D, D, D, NW, false, true>(dm, X1, LD2, X2, LD2, wave, lane);
   {
+    // sum over all entries of S (.) dS_n = sum_{r,c} S[r][c] dS_n^T[c][r]
     float s = 0.f;
     for (int e = tid; e < D * D; e += NT) {
       const int r = e / D, cc = e % D;
-      s += to_f(X1[r * LD2 + cc]) * to_f(X2[r * LD2 + cc]);
+      s += to_f(X1[r * LD2 + cc]) * to_f(X2[cc * LD2 + r]);
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
@@ -1159,7 +1161,7 @@ static hipError_t cbwd_launch_dc(const Dims& d, const ChunkBwdArgs<E>& a, int st
     const int nblk = d.B * d.H * d.NC;
     if (stage == 0)
       hipLaunchKernelGGL((chunk_bwd_state_kernel<E, D, C>), dim3(nblk), dim3(CB_NT), 0, s, a.k, a.dO,
-                         a.alpha, a.Kl, a.Wl, a.UT, a.WkT, a.St, a.dSnT, a.dQt, a.dUs, a.dWks,
+                         a.alpha, a.Kl, a.Wl, a.UT, a.WkT, a.Sc, a.dSnT, a.dQt, a.dUs, a.dWks,
                          a.dKs, a.dKl, a.dWl, a.dgs, d.B, d.T, d.H, d.L, d.NC, d.Tp);
     else if (stage == 1)
       hipLaunchKernelGGL((chunk_bwd_solve_kernel<E, D, C>), dim3(nblk), dim3(CB_NT), 0, s, a.q,

@@ -18,11 +18,12 @@
 //
 // All products are bf16 (or fp32) MFMA with fp32 accumulation; T, the decays
 // and the accumulators stay fp32.  Stored (global, per chunk):
-//   Mt [D][D] = M^T (MFMA B operand of the state pass), HT [D][D] = H^T fp32,
-//   Qt [C][D], O_loc [C][D] fp32, gC.
-// In backward mode (dO given) the kernel instead stores Mt, HT, gC, M [D][D],
-// ET = (dO^T Qt)^T fp32 (for the reverse state pass) and U^T, Wk^T [D][C]
-// (for the reverse chunk kernels).
+//   Mt [D][D] = M^T (MFMA B operand of the state pass, both directions),
+//   HT [D][D] = H^T fp32, Qt [C][D], O_loc [C][D] fp32, gC, and when asked
+//   (training forward) U^T, Wk^T [D][C] for the reverse chunk kernels.
+// In backward mode (dO given) the kernel instead stores Mt, HT, gC,
+// ET = (dO^T Qt)^T fp32 (for the reverse state pass) and U^T, Wk^T.
+// et_kernel forms ET from a saved Qt when the forward was kept.
 #include "prism_common.h"
 #include "prism_internal.h"
 
@@ -74,7 +75,7 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, const E* __restrict__ Kl,
     const E* __restrict__ Wl, const E* __restrict__ dO, E* __restrict__ Mt, float* __restrict__ HT,
-    E* __restrict__ Qt, float* __restrict__ Oloc, float* __restrict__ gCo, E* __restrict__ Mo,
+    E* __restrict__ Qt, float* __restrict__ Oloc, float* __restrict__ gCo,
     float* __restrict__ ET, E* __restrict__ UTo, E* __restrict__ WkTo, int B, int T, int H, int L,
     int NC, int Tp) {
   typedef ChunkLds<E, D, C> LY;
@@ -293,7 +294,7 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
   E* Ut = Vt;
   E* Wkt = Ktbe;
   const long cidx = (long)bh * NC + c;
-  if constexpr (BWD) {   // U^T, Wk^T [D][C] for the reverse chunk kernels
+  if (UTo) {   // U^T, Wk^T [D][C] for the reverse chunk kernels (backward mode, training forward)
     s2g_rows<E, D, C, NT>(UTo + cidx * D * C, C, Ut, LT, D, tid);
     s2g_rows<E, D, C, NT>(WkTo + cidx * D * C, C, Wkt, LT, D, tid);
   }
@@ -314,16 +315,6 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
     for_tiles(ma, wave, lane, [&](int k0, int n, const f32x4& x) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) Mtc[(long)n * D + k0 + r] = to_t<E>(x[r]);
-    });
-  }
-  if constexpr (BWD) {
-    Acc<D, D, NW> mb;   // [n][k] = M^T  -> stored as M[k][n]
-    mb.zero();
-    gemm_acc<E, D, D, C, NW, true, true>(mb, KtD, LT, Wkt, LT, wave, lane);
-    E* Mc = Mo + cidx * D * D;
-    for_tiles(mb, wave, lane, [&](int n0, int kk, const f32x4& x) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Mc[(long)kk * D + n0 + r] = to_t<E>(x[r]);
     });
   }
   {
@@ -382,35 +373,100 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
   }
 }
 
+// ET[n][r] = sum_t Qt[t][n] dO[t][r] per chunk (fp32 [D][D]), from the Qt a
+// training forward kept: the reverse state pass's additive term.
+template <typename E, int D, int C>
+__global__ __launch_bounds__(CF_NT) void et_kernel(const E* __restrict__ Qt, const E* __restrict__ dO,
+                                                   float* __restrict__ ET, int B, int T, int H, int NC) {
+  constexpr int NW = CF_NW, NT = CF_NT;
+  constexpr int LR = ldpad<E>(D);
+  __shared__ __attribute__((aligned(16))) E Qs[C * LR];
+  __shared__ __attribute__((aligned(16))) E Os[C * LR];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nblk = B * H * NC;
+  const int bid = xcd_swizzle(blockIdx.x, nblk);
+  const int c = bid % NC, bh = bid / NC;
+  const int h = bh % H, b = bh / H;
+  const int tb = c * C;
+  const int nval = min(C, T - tb);
+  const long ts = (long)H * D;
+  const long row0 = ((long)b * T + tb) * H + h;
+  const long cidx = (long)bh * NC + c;
+  g2s_rows<E, C, D, NT>(Qs, LR, Qt + cidx * C * D, D, C, tid);
+  g2s_rows<E, C, D, NT>(Os, LR, dO + row0 * D, ts, nval, tid);
+  __syncthreads();
+  Acc<D, D, NW> ea;   // [n][r] = sum_t Qt[t][n] dO[t][r]: both operands k-strided in LDS
+  ea.zero();
+  gemm_acc<E, D, D, C, NW, false, false>(ea, Qs, LR, Os, LR, wave, lane);
+  float* ETc = ET + cidx * D * D;
+  for_tiles(ea, wave, lane, [&](int n0, int r, const f32x4& x) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ETc[(long)(n0 + i) * D + r] = x[i];
+  });
+}
+
+template <typename E, int D, int C>
+static hipError_t et_launch_dc(const Dims& d, const E* Qt, const E* dO, float* ET, hipStream_t s) {
+  if constexpr (sizeof(E) == 4 && D * C > 2048) return hipErrorInvalidValue;   // fp32 envelope
+  hipLaunchKernelGGL((et_kernel<E, D, C>), dim3(d.B * d.H * d.NC), dim3(CF_NT), 0, s, Qt, dO, ET,
+                     d.B, d.T, d.H, d.NC);
+  return hipGetLastError();
+}
+
+template <typename E, int D>
+static hipError_t et_launch_d(const Dims& d, const E* Qt, const E* dO, float* ET, hipStream_t s) {
+  switch (d.C) {
+    case 16: return et_launch_dc<E, D, 16>(d, Qt, dO, ET, s);
+    case 32: return et_launch_dc<E, D, 32>(d, Qt, dO, ET, s);
+    case 64: return et_launch_dc<E, D, 64>(d, Qt, dO, ET, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+template <typename E>
+hipError_t launch_et(const Dims& d, const E* Qt, const E* dO, float* ET, hipStream_t s) {
+  switch (d.D) {
+    case 16: return et_launch_d<E, 16>(d, Qt, dO, ET, s);
+    case 32: return et_launch_d<E, 32>(d, Qt, dO, ET, s);
+    case 64: return et_launch_d<E, 64>(d, Qt, dO, ET, s);
+    case 128:
+      if constexpr (sizeof(E) == 2) return et_launch_d<E, 128>(d, Qt, dO, ET, s);
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+template hipError_t launch_et<bf16>(const Dims&, const bf16*, const bf16*, float*, hipStream_t);
+template hipError_t launch_et<float>(const Dims&, const float*, const float*, float*, hipStream_t);
+
 template <typename E, int D, int C>
 static hipError_t chunk_launch_dc(const Dims& d, const E* q, const E* k, const E* v,
                                   const float* alpha, const float* beta, const E* Kl, const E* Wl,
                                   const E* dO, E* Mt, float* HT, E* Qt, float* Oloc, float* gC,
-                                  E* M, float* ET, E* UT, E* WkT, hipStream_t s) {
+                                  float* ET, E* UT, E* WkT, hipStream_t s) {
   if constexpr (sizeof(E) == 4 && D * C > 2048) return hipErrorInvalidValue;   // fp32 envelope
   const int nblk = d.B * d.H * d.NC;
   if (dO)
     hipLaunchKernelGGL((chunk_fwd_kernel<E, D, C, true>),
                        dim3(D >= 128 ? persistent_grid(chunk_fwd_kernel<E, D, C, true>, CF_NT, nblk) : nblk),
                        dim3(CF_NT), 0, s, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC,
-                       M, ET, UT, WkT, d.B, d.T, d.H, d.L, d.NC, d.Tp);
+                       ET, UT, WkT, d.B, d.T, d.H, d.L, d.NC, d.Tp);
   else
     hipLaunchKernelGGL((chunk_fwd_kernel<E, D, C, false>),
                        dim3(D >= 128 ? persistent_grid(chunk_fwd_kernel<E, D, C, false>, CF_NT, nblk) : nblk),
                        dim3(CF_NT), 0, s, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC,
-                       M, ET, UT, WkT, d.B, d.T, d.H, d.L, d.NC, d.Tp);
+                       ET, UT, WkT, d.B, d.T, d.H, d.L, d.NC, d.Tp);
   return hipGetLastError();
 }
 
 template <typename E, int D>
 static hipError_t chunk_launch_d(const Dims& d, const E* q, const E* k, const E* v,
                                  const float* alpha, const float* beta, const E* Kl, const E* Wl,
-                                 const E* dO, E* Mt, float* HT, E* Qt, float* Oloc, float* gC, E* M,
+                                 const E* dO, E* Mt, float* HT, E* Qt, float* Oloc, float* gC,
                                  float* ET, E* UT, E* WkT, hipStream_t s) {
   switch (d.C) {
-    case 16: return chunk_launch_dc<E, D, 16>(d, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, M, ET, UT, WkT, s);
-    case 32: return chunk_launch_dc<E, D, 32>(d, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, M, ET, UT, WkT, s);
-    case 64: return chunk_launch_dc<E, D, 64>(d, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, M, ET, UT, WkT, s);
+    case 16: return chunk_launch_dc<E, D, 16>(d, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, ET, UT, WkT, s);
+    case 32: return chunk_launch_dc<E, D, 32>(d, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, ET, UT, WkT, s);
+    case 64: return chunk_launch_dc<E, D, 64>(d, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, ET, UT, WkT, s);
   }
   return hipErrorInvalidValue;
 }
@@ -418,15 +474,15 @@ static hipError_t chunk_launch_d(const Dims& d, const E* q, const E* k, const E*
 template <typename E>
 hipError_t launch_chunk_fwd(const Dims& d, const E* q, const E* k, const E* v, const float* alpha,
                             const float* beta, const E* Kl, const E* Wl, const E* dO, E* Mt,
-                            float* HT, E* Qt, float* Oloc, float* gC, E* M, float* ET, E* UT,
+                            float* HT, E* Qt, float* Oloc, float* gC, float* ET, E* UT,
                             E* WkT, hipStream_t s) {
   switch (d.D) {
-    case 16: return chunk_launch_d<E, 16>(d, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, M, ET, UT, WkT, s);
-    case 32: return chunk_launch_d<E, 32>(d, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, M, ET, UT, WkT, s);
-    case 64: return chunk_launch_d<E, 64>(d, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, M, ET, UT, WkT, s);
+    case 16: return chunk_launch_d<E, 16>(d, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, ET, UT, WkT, s);
+    case 32: return chunk_launch_d<E, 32>(d, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, ET, UT, WkT, s);
+    case 64: return chunk_launch_d<E, 64>(d, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, ET, UT, WkT, s);
     case 128:
       if constexpr (sizeof(E) == 2)
-        return chunk_launch_d<E, 128>(d, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, M, ET, UT, WkT, s);
+        return chunk_launch_d<E, 128>(d, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, ET, UT, WkT, s);
       break;
   }
   return hipErrorInvalidValue;
@@ -434,11 +490,11 @@ hipError_t launch_chunk_fwd(const Dims& d, const E* q, const E* k, const E* v, c
 
 template hipError_t launch_chunk_fwd<bf16>(const Dims&, const bf16*, const bf16*, const bf16*,
                                            const float*, const float*, const bf16*, const bf16*,
-                                           const bf16*, bf16*, float*, bf16*, float*, float*, bf16*,
+                                           const bf16*, bf16*, float*, bf16*, float*, float*,
                                            float*, bf16*, bf16*, hipStream_t);
 template hipError_t launch_chunk_fwd<float>(const Dims&, const float*, const float*, const float*,
                                             const float*, const float*, const float*, const float*,
                                             const float*, float*, float*, float*, float*, float*,
-                                            float*, float*, float*, float*, hipStream_t);
+                                            float*, float*, float*, hipStream_t);
 
 }  // namespace prism

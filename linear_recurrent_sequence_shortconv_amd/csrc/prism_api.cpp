@@ -4,6 +4,9 @@
 //   chunk_fwd   (chunk-local affine maps of S_t = S_{t-1} A_t + B_t, §2.1)
 //   state_fwd   (sequential pass over chunks, fp32 state)
 //   out_fwd     (readout o_t = S_t q_t)
+// The training pair keeps the forward's refinement pairs, chunk maps, chunk
+// states and solve results in a caller buffer, so that its backward starts at
+// the reverse state pass instead of recomputing them.
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
@@ -71,9 +74,33 @@ struct Carve {
 
 template <typename E>
 struct FwdWs {
-  E *Kl, *Wl, *Mt, *Qt, *Sc;
-  float *HT, *Oloc, *gC, *ST;
+  E *Kl, *Wl, *Mt, *Qt, *Sc, *UT, *WkT;
+  float *HT, *Oloc, *gC;
 };
+
+// What a training forward keeps for its backward (caller-owned buffer).
+template <typename E>
+struct Kept {
+  E *Kl, *Wl, *Mt, *Qt, *Sc, *UT, *WkT;
+  float* gC;
+};
+
+template <typename E>
+Kept<E> carve_kept(const prism::Dims& d, Carve& cv) {
+  const size_t bh = (size_t)d.B * d.H;
+  const size_t es = sizeof(E);
+  const size_t DD = (size_t)d.D * d.D, CD = (size_t)d.C * d.D;
+  Kept<E> k;
+  k.Kl = cv.take<E>(bh * d.L * d.Tp * d.D * es);
+  k.Wl = cv.take<E>(bh * d.L * d.Tp * d.D * es);
+  k.Mt = cv.take<E>(bh * d.NC * DD * es);
+  k.Qt = cv.take<E>(bh * d.NC * CD * es);
+  k.Sc = cv.take<E>(bh * d.NC * DD * es);
+  k.UT = cv.take<E>(bh * d.NC * CD * es);
+  k.WkT = cv.take<E>(bh * d.NC * CD * es);
+  k.gC = cv.take<float>(bh * d.NC * 4);
+  return k;
+}
 
 template <typename E>
 FwdWs<E> carve_fwd(const prism::Dims& d, Carve& cv) {
@@ -88,7 +115,7 @@ FwdWs<E> carve_fwd(const prism::Dims& d, Carve& cv) {
   w.Oloc = cv.take<float>(bh * d.NC * d.C * d.D * 4);
   w.gC = cv.take<float>(bh * d.NC * 4);
   w.Sc = cv.take<E>(bh * d.NC * d.D * d.D * es);
-  w.ST = cv.take<float>(bh * d.D * d.D * 4);
+  w.UT = w.WkT = nullptr;
   return w;
 }
 
@@ -153,7 +180,7 @@ prism_status check_ptr(const void* p, const char* name, bool required) {
 
 template <typename E>
 struct BwdWs {
-  E *Kl, *Wl, *Mt, *M, *UT, *WkT, *Sct, *dSnT, *u, *dP, *WkW, *WpW;
+  E *Kl, *Wl, *Mt, *UT, *WkT, *Sc, *dSnT, *u, *dP, *WkW, *WpW;
   float *HT, *gC, *ET, *dQt, *dUs, *dWks, *dKs, *dVp, *dqp, *dkp, *dKl, *dWl, *dgs, *dgp;
   float *dwbp, *dcp, *part;
 };
@@ -169,13 +196,12 @@ BwdWs<E> carve_bwd(const prism::Dims& d, Carve& cv) {
   w.Kl = cv.take<E>(bh * d.L * d.Tp * d.D * es);
   w.Wl = cv.take<E>(bh * d.L * d.Tp * d.D * es);
   w.Mt = cv.take<E>(bh * d.NC * DD * es);
-  w.M = cv.take<E>(bh * d.NC * DD * es);
   w.HT = cv.take<float>(bh * d.NC * DD * 4);
   w.ET = cv.take<float>(bh * d.NC * DD * 4);
   w.gC = cv.take<float>(bh * d.NC * 4);
   w.UT = cv.take<E>(bh * d.NC * CD * es);
   w.WkT = cv.take<E>(bh * d.NC * CD * es);
-  w.Sct = cv.take<E>(bh * d.NC * DD * es);
+  w.Sc = cv.take<E>(bh * d.NC * DD * es);
   w.dSnT = cv.take<E>(bh * d.NC * DD * es);
   w.dQt = cv.take<float>(bh * d.NC * CD * 4);
   w.dUs = cv.take<float>(bh * d.NC * CD * 4);
@@ -207,6 +233,15 @@ size_t bwd_ws_bytes(const prism::Dims& d, prism_dtype dt) {
   return cv.off;
 }
 
+size_t kept_bytes(const prism::Dims& d, prism_dtype dt) {
+  Carve cv;
+  if (dt == PRISM_BF16)
+    carve_kept<prism::bf16>(d, cv);
+  else
+    carve_kept<float>(d, cv);
+  return cv.off;
+}
+
 size_t fwd_ws_bytes(const prism::Dims& d, prism_dtype dt) {
   Carve cv;
   if (dt == PRISM_BF16)
@@ -220,10 +255,23 @@ template <typename E>
 prism_status run_forward(const prism::Dims& d, const void* q, const void* k, const void* v,
                          const float* alpha, const float* beta, const void* Wk, const void* Wp,
                          const void* wbeta, const void* conv, const float* S0, void* o, float* ST,
-                         void* ws, hipStream_t s) {
+                         void* ws, void* keep, hipStream_t s) {
   Carve cv;
   cv.base = static_cast<char*>(ws);
   FwdWs<E> w = carve_fwd<E>(d, cv);
+  if (keep) {   // training forward: what the backward reads lives in the kept buffer
+    Carve ck;
+    ck.base = static_cast<char*>(keep);
+    const Kept<E> kp = carve_kept<E>(d, ck);
+    w.Kl = kp.Kl;
+    w.Wl = kp.Wl;
+    w.Mt = kp.Mt;
+    w.Qt = kp.Qt;
+    w.Sc = kp.Sc;
+    w.UT = kp.UT;
+    w.WkT = kp.WkT;
+    w.gC = kp.gC;
+  }
   const E* q_ = static_cast<const E*>(q);
   const E* k_ = static_cast<const E*>(k);
   const E* v_ = static_cast<const E*>(v);
@@ -234,7 +282,7 @@ prism_status run_forward(const prism::Dims& d, const void* q, const void* k, con
                                         w.Kl, w.Wl, s));
   HIP_TRY("chunk_fwd", s,
           prism::launch_chunk_fwd<E>(d, q_, k_, v_, alpha, beta, w.Kl, w.Wl, nullptr, w.Mt, w.HT,
-                                     w.Qt, w.Oloc, w.gC, nullptr, nullptr, nullptr, nullptr, s));
+                                     w.Qt, w.Oloc, w.gC, nullptr, w.UT, w.WkT, s));
   HIP_TRY("state_fwd", s,
           prism::launch_state_pass<E>(d, S0, w.Mt, w.HT, w.gC, w.Sc, ST, false, false, s));
   HIP_TRY("out_fwd", s, prism::launch_out_fwd<E>(d, w.Sc, w.Qt, w.Oloc, static_cast<E*>(o), s));
@@ -247,7 +295,7 @@ prism_status run_backward(const prism::Dims& d, const void* q, const void* k, co
                           const void* wbeta, const void* conv, const float* S0, const void* dO,
                           const float* dST, void* dq, void* dk, void* dv, float* dalpha,
                           float* dbeta, float* dWk, float* dWp, float* dwbeta, float* dconv,
-                          float* dS0, void* ws, hipStream_t s) {
+                          float* dS0, void* ws, const void* kept, hipStream_t s) {
   Carve cv;
   cv.base = static_cast<char*>(ws);
   BwdWs<E> w = carve_bwd<E>(d, cv);
@@ -255,21 +303,36 @@ prism_status run_backward(const prism::Dims& d, const void* q, const void* k, co
   const E* k_ = static_cast<const E*>(k);
   const E* v_ = static_cast<const E*>(v);
   const E* dO_ = static_cast<const E*>(dO);
-  if (d.L > 0)
-    HIP_TRY("refine_fwd_recompute", s,
-            prism::launch_refine_fwd<E>(d, v_, static_cast<const E*>(conv), static_cast<const E*>(Wk),
-                                        static_cast<const E*>(Wp), static_cast<const E*>(wbeta),
-                                        w.Kl, w.Wl, s));
-  HIP_TRY("chunk_fwd_bwdmode", s,
-          prism::launch_chunk_fwd<E>(d, q_, k_, v_, alpha, beta, w.Kl, w.Wl, dO_, w.Mt, w.HT,
-                                     nullptr, nullptr, w.gC, w.M, w.ET, w.UT, w.WkT, s));
-  HIP_TRY("state_fwd_recompute", s,
-          prism::launch_state_pass<E>(d, S0, w.Mt, w.HT, w.gC, w.Sct, nullptr, true, false, s));
+  if (kept) {
+    // the forward's intermediates: only E = dO^T Qt per chunk is new
+    Carve ck;
+    ck.base = static_cast<char*>(const_cast<void*>(kept));
+    const Kept<E> kp = carve_kept<E>(d, ck);
+    w.Kl = kp.Kl;
+    w.Wl = kp.Wl;
+    w.Mt = kp.Mt;
+    w.Sc = kp.Sc;
+    w.UT = kp.UT;
+    w.WkT = kp.WkT;
+    w.gC = kp.gC;
+    HIP_TRY("et_chunks", s, prism::launch_et<E>(d, kp.Qt, dO_, w.ET, s));
+  } else {
+    if (d.L > 0)
+      HIP_TRY("refine_fwd_recompute", s,
+              prism::launch_refine_fwd<E>(d, v_, static_cast<const E*>(conv),
+                                          static_cast<const E*>(Wk), static_cast<const E*>(Wp),
+                                          static_cast<const E*>(wbeta), w.Kl, w.Wl, s));
+    HIP_TRY("chunk_fwd_bwdmode", s,
+            prism::launch_chunk_fwd<E>(d, q_, k_, v_, alpha, beta, w.Kl, w.Wl, dO_, w.Mt, w.HT,
+                                       nullptr, nullptr, w.gC, w.ET, w.UT, w.WkT, s));
+    HIP_TRY("state_fwd_recompute", s,
+            prism::launch_state_pass<E>(d, S0, w.Mt, w.HT, w.gC, w.Sc, nullptr, false, false, s));
+  }
   HIP_TRY("state_bwd", s,
-          prism::launch_state_pass<E>(d, dST, w.M, w.ET, w.gC, w.dSnT, dS0, true, true, s));
+          prism::launch_state_pass<E>(d, dST, w.Mt, w.ET, w.gC, w.dSnT, dS0, true, true, s));
   prism::ChunkBwdArgs<E> a;
   a.q = q_; a.k = k_; a.v = v_; a.dO = dO_; a.alpha = alpha; a.beta = beta;
-  a.Kl = w.Kl; a.Wl = w.Wl; a.UT = w.UT; a.WkT = w.WkT; a.St = w.Sct; a.dSnT = w.dSnT;
+  a.Kl = w.Kl; a.Wl = w.Wl; a.UT = w.UT; a.WkT = w.WkT; a.Sc = w.Sc; a.dSnT = w.dSnT;
   a.dQt = w.dQt; a.dUs = w.dUs; a.dWks = w.dWks; a.dKs = w.dKs; a.dKl = w.dKl; a.dWl = w.dWl;
   a.dgs = w.dgs; a.dVp = w.dVp; a.dqp = w.dqp; a.dkp = w.dkp; a.dgp = w.dgp; a.dbeta = dbeta;
   a.dq = static_cast<E*>(dq); a.dk = static_cast<E*>(dk);
@@ -333,11 +396,35 @@ prism_status prism_backward_workspace(const prism_desc* desc, size_t* bytes) {
   return PRISM_OK;
 }
 
-prism_status prism_forward(const prism_desc* desc, const void* q, const void* k, const void* v,
+prism_status prism_saved_bytes(const prism_desc* desc, size_t* bytes) {
+  if (bytes) *bytes = 0;
+  if (!bytes) return fail(PRISM_ERR_NULL, "bytes is NULL");
+  prism::Dims d;
+  prism_status st = check_desc(desc, &d);
+  if (st != PRISM_OK) return st;
+  *bytes = kept_bytes(d, desc->dtype);
+  return PRISM_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+prism_status check_buffer(const void* p, size_t have, size_t need, const char* what) {
+  if (!p) return fail(PRISM_ERR_WORKSPACE, std::string(what) + " is NULL");
+  if (reinterpret_cast<uintptr_t>(p) & 255u)
+    return fail(PRISM_ERR_ALIGN, std::string(what) + " is not 256-byte aligned");
+  if (have < need)
+    return fail(PRISM_ERR_WORKSPACE, std::string(what) + " has " + std::to_string(have) +
+                                         " bytes, needs " + std::to_string(need));
+  return PRISM_OK;
+}
+
+prism_status forward_entry(const prism_desc* desc, const void* q, const void* k, const void* v,
                            const float* alpha, const float* beta, const void* Wk, const void* Wp,
-                           const void* wbeta, const void* conv, const float* S0, void* o,
-                           float* ST, void* workspace, size_t workspace_bytes,
-                           hipStream_t stream) {
+                           const void* wbeta, const void* conv, const float* S0, void* o, float* ST,
+                           void* saved, size_t saved_bytes, bool train, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
   try {
     g_err.clear();
     prism::Dims d;
@@ -356,26 +443,27 @@ prism_status prism_forward(const prism_desc* desc, const void* q, const void* k,
     CHECK_PTR(S0, false);
     CHECK_PTR(o, true);
     CHECK_PTR(ST, false);
-    const size_t need = fwd_ws_bytes(d, desc->dtype);
-    if (!workspace) return fail(PRISM_ERR_WORKSPACE, "workspace is NULL");
-    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
-      return fail(PRISM_ERR_ALIGN, "workspace is not 256-byte aligned");
-    if (workspace_bytes < need)
-      return fail(PRISM_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
-                                           " bytes, needs " + std::to_string(need));
+    if (train) {
+      st = check_buffer(saved, saved_bytes, kept_bytes(d, desc->dtype), "saved");
+      if (st != PRISM_OK) return st;
+    }
+    st = check_buffer(workspace, workspace_bytes, fwd_ws_bytes(d, desc->dtype), "workspace");
+    if (st != PRISM_OK) return st;
+    void* keep = train ? saved : nullptr;
     if (desc->dtype == PRISM_BF16)
       return run_forward<prism::bf16>(d, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, o, ST,
-                                      workspace, stream);
+                                      workspace, keep, stream);
     return run_forward<float>(d, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, o, ST, workspace,
-                              stream);
+                              keep, stream);
   } catch (...) {
     return fail(PRISM_ERR_HIP, "unexpected host exception");
   }
 }
 
-prism_status prism_backward(const prism_desc* desc, const void* q, const void* k, const void* v,
+prism_status backward_entry(const prism_desc* desc, const void* q, const void* k, const void* v,
                             const float* alpha, const float* beta, const void* Wk, const void* Wp,
-                            const void* wbeta, const void* conv, const float* S0, const void* dO,
+                            const void* wbeta, const void* conv, const float* S0,
+                            const void* saved, size_t saved_bytes, bool train, const void* dO,
                             const float* dST, void* dq, void* dk, void* dv, float* dalpha,
                             float* dbeta, float* dWk, float* dWp, float* dwbeta, float* dconv,
                             float* dS0, void* workspace, size_t workspace_bytes,
@@ -408,22 +496,71 @@ prism_status prism_backward(const prism_desc* desc, const void* q, const void* k
     CHECK_PTR(dwbeta, refine);
     CHECK_PTR(dconv, refine);
     CHECK_PTR(dS0, false);
-    const size_t need = bwd_ws_bytes(d, desc->dtype);
-    if (!workspace) return fail(PRISM_ERR_WORKSPACE, "workspace is NULL");
-    if (reinterpret_cast<uintptr_t>(workspace) & 255u)
-      return fail(PRISM_ERR_ALIGN, "workspace is not 256-byte aligned");
-    if (workspace_bytes < need)
-      return fail(PRISM_ERR_WORKSPACE, "workspace has " + std::to_string(workspace_bytes) +
-                                           " bytes, needs " + std::to_string(need));
+    if (train) {
+      st = check_buffer(saved, saved_bytes, kept_bytes(d, desc->dtype), "saved");
+      if (st != PRISM_OK) return st;
+    }
+    st = check_buffer(workspace, workspace_bytes, bwd_ws_bytes(d, desc->dtype), "workspace");
+    if (st != PRISM_OK) return st;
+    const void* kept = train ? saved : nullptr;
     if (desc->dtype == PRISM_BF16)
       return run_backward<prism::bf16>(d, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, dO, dST,
                                        dq, dk, dv, dalpha, dbeta, dWk, dWp, dwbeta, dconv, dS0,
-                                       workspace, stream);
+                                       workspace, kept, stream);
     return run_backward<float>(d, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, dO, dST, dq, dk,
-                               dv, dalpha, dbeta, dWk, dWp, dwbeta, dconv, dS0, workspace, stream);
+                               dv, dalpha, dbeta, dWk, dWp, dwbeta, dconv, dS0, workspace, kept,
+                               stream);
   } catch (...) {
     return fail(PRISM_ERR_HIP, "unexpected host exception");
   }
+}
+
+}  // namespace
+
+extern "C" {
+
+prism_status prism_forward(const prism_desc* desc, const void* q, const void* k, const void* v,
+                           const float* alpha, const float* beta, const void* Wk, const void* Wp,
+                           const void* wbeta, const void* conv, const float* S0, void* o,
+                           float* ST, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  return forward_entry(desc, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, o, ST, nullptr, 0,
+                       false, workspace, workspace_bytes, stream);
+}
+
+prism_status prism_forward_train(const prism_desc* desc, const void* q, const void* k,
+                                 const void* v, const float* alpha, const float* beta,
+                                 const void* Wk, const void* Wp, const void* wbeta,
+                                 const void* conv, const float* S0, void* o, float* ST,
+                                 void* saved, size_t saved_bytes, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  return forward_entry(desc, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, o, ST, saved,
+                       saved_bytes, true, workspace, workspace_bytes, stream);
+}
+
+prism_status prism_backward(const prism_desc* desc, const void* q, const void* k, const void* v,
+                            const float* alpha, const float* beta, const void* Wk, const void* Wp,
+                            const void* wbeta, const void* conv, const float* S0, const void* dO,
+                            const float* dST, void* dq, void* dk, void* dv, float* dalpha,
+                            float* dbeta, float* dWk, float* dWp, float* dwbeta, float* dconv,
+                            float* dS0, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  return backward_entry(desc, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, nullptr, 0, false,
+                        dO, dST, dq, dk, dv, dalpha, dbeta, dWk, dWp, dwbeta, dconv, dS0,
+                        workspace, workspace_bytes, stream);
+}
+
+prism_status prism_backward_train(const prism_desc* desc, const void* q, const void* k,
+                                  const void* v, const float* alpha, const float* beta,
+                                  const void* Wk, const void* Wp, const void* wbeta,
+                                  const void* conv, const float* S0, const void* saved,
+                                  size_t saved_bytes, const void* dO, const float* dST, void* dq,
+                                  void* dk, void* dv, float* dalpha, float* dbeta, float* dWk,
+                                  float* dWp, float* dwbeta, float* dconv, float* dS0,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return backward_entry(desc, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, saved, saved_bytes,
+                        true, dO, dST, dq, dk, dv, dalpha, dbeta, dWk, dWp, dwbeta, dconv, dS0,
+                        workspace, workspace_bytes, stream);
 }
 
 void prism_timing_begin(void) {

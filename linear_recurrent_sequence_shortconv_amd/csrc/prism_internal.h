@@ -24,20 +24,25 @@ hipError_t launch_refine_fwd(const Dims& d, const E* v, const E* conv, const E* 
                              const E* wbeta, E* Kl, E* Wl, hipStream_t s);
 
 // Chunk-local affine map of every chunk (parallel over B * H * NC).
-// Forward mode writes Mt, HT, Qt, Oloc, gC.  Backward mode (dO != nullptr)
-// writes Mt, HT, gC, M, ET (E = dO^T Qt), UT, WkT and nothing else.
+// Forward mode writes Mt, HT, Qt, Oloc, gC, and UT, WkT when they are not
+// null (training forward).  Backward mode (dO != nullptr) writes Mt, HT, gC,
+// ET (E = dO^T Qt), UT, WkT and nothing else.
 template <typename E>
 hipError_t launch_chunk_fwd(const Dims& d, const E* q, const E* k, const E* v, const float* alpha,
                             const float* beta, const E* Kl, const E* Wl, const E* dO, E* Mt,
-                            float* HT, E* Qt, float* Oloc, float* gC, E* M, float* ET, E* UT,
-                            E* WkT, hipStream_t s);
+                            float* HT, E* Qt, float* Oloc, float* gC, float* ET, E* UT, E* WkT,
+                            hipStream_t s);
+
+// ET per chunk from a kept Qt and dO (the backward of a training forward).
+template <typename E>
+hipError_t launch_et(const Dims& d, const E* Qt, const E* dO, float* ET, hipStream_t s);
 
 // Sequential pass over chunks, forward (X <- exp(gC) X - X M + H, from S0) or
-// reverse (X <- exp(gC) X - X M^T + E, from dS_T).  Bm is M^T (forward) or M
-// (reverse); AddT is H^T or E^T.  Stores X per chunk before its update
-// (row-major, or transposed), and the final X in `fin` when not null.
+// reverse (X <- exp(gC) X - X M^T + E, from dS_T).  Both read Mt = M^T; AddT
+// is H^T or E^T.  Stores X per chunk before its update (row-major, or
+// transposed), and the final X in `fin` when not null.
 template <typename E>
-hipError_t launch_state_pass(const Dims& d, const float* init, const E* Bm, const float* AddT,
+hipError_t launch_state_pass(const Dims& d, const float* init, const E* Mt, const float* AddT,
                              const float* gC, E* Xc, float* fin, bool transposed, bool reverse,
                              hipStream_t s);
 
@@ -46,7 +51,9 @@ template <typename E>
 struct ChunkBwdArgs {
   const E *q, *k, *v, *dO;
   const float *alpha, *beta;
-  const E *Kl, *Wl, *UT, *WkT, *St, *dSnT;
+  const E *Kl, *Wl, *UT, *WkT;
+  const E* Sc;                  // chunk-entry states S_c, row-major [D][D]
+  const E* dSnT;
   float *dQt, *dUs, *dWks, *dKs, *dKl, *dWl, *dgs, *dVp, *dqp, *dkp, *dgp, *dbeta;
   E *dq, *dk;
   E* dv;                        // written here only when L = 0

@@ -13,11 +13,13 @@
 
 namespace prism {
 
+// Both directions take Mt_c = M_c^T (row-major in HBM and LDS):
 // Forward (reverse = 0): X_0 = init (S0, or 0), per chunk c = 0..NC-1 store
-//   X_c, then X <- exp(gC_c) X - X Bm_c^T + AddT_c^T, where Bm_c = M_c^T
-//   (so X Bm_c^T = X M_c) and AddT_c = H_c^T.  Final X -> fin (S_T).
-// Reverse (reverse = 1): X = init (dS_T, or 0), c = NC-1..0, Bm_c = M_c
-//   (X Bm_c^T = X M_c^T), AddT_c = E_c^T; final X -> fin (dS_0).
+//   X_c, then X <- exp(gC_c) X - X Mt_c^T + AddT_c^T (X Mt_c^T = X M_c), with
+//   AddT_c = H_c^T.  Final X -> fin (S_T).
+// Reverse (reverse = 1): X = init (dS_T, or 0), c = NC-1..0,
+//   X <- exp(gC_c) X - X Mt_c + AddT_c^T (X Mt_c = X M_c^T; the MFMA B operand
+//   is then read k-strided from LDS), with AddT_c = E_c^T; final X -> fin (dS_0).
 // The stored per-chunk matrix is row-major, or transposed when `transposed`.
 //
 // Rows of the state never mix, so the pass splits into row blocks of RB rows:
@@ -30,7 +32,7 @@ namespace prism {
 constexpr int SP_NW = 8;
 constexpr int SP_NT = SP_NW * WAVE;
 
-template <typename E, int D, int RB>
+template <typename E, int D, int RB, bool REV>
 __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restrict__ init,
                                                            const E* __restrict__ Bm,
                                                            const float* __restrict__ AddT,
@@ -66,7 +68,8 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
         for (int r = 0; r < 4; ++r)
           S.v[i][j][r] = init[((long)bh * D + rb0 + m0 + 16 * i + rl + r) * D + n0 + 16 * j + cl];
   }
-  auto chunk_of = [&](int step) { return reverse ? NC - 1 - step : step; };
+  (void)reverse;   // the direction is the template parameter REV
+  auto chunk_of = [&](int step) { return REV ? NC - 1 - step : step; };
   uint4 mst[PER];                       // next Bm, staged through registers into LDS
   f32x4 addn[TL::RM][TL::RN];           // next AddT^T block
   float egn = 0.f;                      // next decay
@@ -141,7 +144,7 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
     }
     Acc<RB, D, SP_NW> P;
     P.zero();
-    gemm_acc<E, RB, D, D, SP_NW, true, true>(P, Ss[buf], LS, Mb[buf], LS, wave, lane);
+    gemm_acc<E, RB, D, D, SP_NW, true, !REV>(P, Ss[buf], LS, Mb[buf], LS, wave, lane);
     if (act) {
 #pragma unroll
       for (int i = 0; i < TL::RM; ++i)
@@ -168,8 +171,12 @@ static hipError_t state_launch_d(const Dims& d, const float* init, const E* Bm, 
   // row blocks of 64 rows at D = 128 (two workgroups per sequence), whole
   // state below that
   constexpr int RB = D > 64 ? 64 : D;
-  hipLaunchKernelGGL((state_pass_kernel<E, D, RB>), dim3(d.B * d.H * (D / RB)), dim3(SP_NT), 0, s,
-                     init, Bm, AddT, gC, Xc, fin, d.B, d.H, d.NC, tr ? 1 : 0, rev ? 1 : 0);
+  if (rev)
+    hipLaunchKernelGGL((state_pass_kernel<E, D, RB, true>), dim3(d.B * d.H * (D / RB)), dim3(SP_NT),
+                       0, s, init, Bm, AddT, gC, Xc, fin, d.B, d.H, d.NC, tr ? 1 : 0, 1);
+  else
+    hipLaunchKernelGGL((state_pass_kernel<E, D, RB, false>), dim3(d.B * d.H * (D / RB)), dim3(SP_NT),
+                       0, s, init, Bm, AddT, gC, Xc, fin, d.B, d.H, d.NC, tr ? 1 : 0, 0);
   return hipGetLastError();
 }
 

@@ -19,8 +19,8 @@ STATUS = {0: "PRISM_OK", 1: "PRISM_ERR_NULL", 2: "PRISM_ERR_SHAPE", 3: "PRISM_ER
           4: "PRISM_ERR_ALIGN", 5: "PRISM_ERR_WORKSPACE", 6: "PRISM_ERR_HIP"}
 
 EXPORTS = ("prism_forward_workspace", "prism_backward_workspace", "prism_forward",
-           "prism_backward", "prism_status_string", "prism_last_error",
-           "prism_timing_begin", "prism_timing_end")
+           "prism_backward", "prism_saved_bytes", "prism_forward_train", "prism_backward_train",
+           "prism_status_string", "prism_last_error", "prism_timing_begin", "prism_timing_end")
 
 
 class Desc(ctypes.Structure):
@@ -46,8 +46,14 @@ def lib():
         L.prism_backward_workspace.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(ctypes.c_size_t)]
         L.prism_forward.argtypes = [ctypes.POINTER(Desc)] + [_P] * 12 + [_P, ctypes.c_size_t, _P]
         L.prism_backward.argtypes = [ctypes.POINTER(Desc)] + [_P] * 22 + [_P, ctypes.c_size_t, _P]
+        L.prism_saved_bytes.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(ctypes.c_size_t)]
+        L.prism_forward_train.argtypes = ([ctypes.POINTER(Desc)] + [_P] * 12
+                                          + [_P, ctypes.c_size_t, _P, ctypes.c_size_t, _P])
+        L.prism_backward_train.argtypes = ([ctypes.POINTER(Desc)] + [_P] * 10 + [_P, ctypes.c_size_t]
+                                           + [_P] * 12 + [_P, ctypes.c_size_t, _P])
         for f in ("prism_forward_workspace", "prism_backward_workspace", "prism_forward",
-                  "prism_backward"):
+                  "prism_backward", "prism_saved_bytes", "prism_forward_train",
+                  "prism_backward_train"):
             getattr(L, f).restype = ctypes.c_int
         L.prism_status_string.argtypes = [ctypes.c_int]
         L.prism_status_string.restype = ctypes.c_char_p
@@ -115,6 +121,12 @@ def backward_workspace_bytes(desc):
     return n.value
 
 
+def saved_bytes(desc):
+    n = ctypes.c_size_t(0)
+    _check(lib().prism_saved_bytes(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
 def _validate_inputs(q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0):
     dev, dt = q.device, q.dtype
     for name, t in (("q", q), ("k", k), ("v", v)):
@@ -131,12 +143,15 @@ def _validate_inputs(q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0):
 
 
 def forward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None, S0=None, chunk=64,
-            workspace=None):
+            workspace=None, saved=None):
     """PRISM layer forward.  Returns (o, S_T).
 
     q, k [B,T,H,dk], v [B,T,H,dv] (bf16 or fp32); alpha, beta [B,T,H] fp32;
     Wk [H,L,dk,dv], Wp [H,L,dv,dv], wbeta [H,L,dv], conv [H,dv,4] in q's
     dtype (all None for L = 0); S0 [B,H,dv,dk] fp32 or None.
+    With `saved` (a buffer from saved_buffer()) this is the training forward
+    (prism_forward_train): the buffer then holds what backward(saved=...)
+    needs.
     """
     _validate_inputs(q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0)
     desc = _desc_from(q, v, Wk, chunk)
@@ -150,19 +165,34 @@ def forward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None, S0=No
     else:
         ws = workspace
     stream = torch.cuda.current_stream(q.device).cuda_stream
-    _check(lib().prism_forward(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
-                               _ptr(beta), _ptr(Wk), _ptr(Wp), _ptr(wbeta), _ptr(conv), _ptr(S0),
-                               _ptr(o), _ptr(ST), _ptr(ws), ctypes.c_size_t(ws.numel()),
-                               ctypes.c_void_p(stream)))
+    if saved is None:
+        _check(lib().prism_forward(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                   _ptr(beta), _ptr(Wk), _ptr(Wp), _ptr(wbeta), _ptr(conv),
+                                   _ptr(S0), _ptr(o), _ptr(ST), _ptr(ws),
+                                   ctypes.c_size_t(ws.numel()), ctypes.c_void_p(stream)))
+    else:
+        _check(lib().prism_forward_train(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                         _ptr(beta), _ptr(Wk), _ptr(Wp), _ptr(wbeta), _ptr(conv),
+                                         _ptr(S0), _ptr(o), _ptr(ST), _ptr(saved),
+                                         ctypes.c_size_t(saved.numel()), _ptr(ws),
+                                         ctypes.c_size_t(ws.numel()), ctypes.c_void_p(stream)))
     return o, ST
 
 
+def saved_buffer(q, v, Wk=None, chunk=64):
+    """A 256-byte aligned device buffer for the training pair (uint8 view)."""
+    desc = _desc_from(q, v, Wk, chunk)
+    return _workspace(saved_bytes(desc), q.device)[1]
+
+
 def backward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None, S0=None, dO=None,
-             dST=None, chunk=64, need_dS0=False, workspace=None):
+             dST=None, chunk=64, need_dS0=False, workspace=None, saved=None):
     """Gradients of <dO, o> + <dST, S_T> with respect to every input.
 
     Returns a dict: dq, dk, dv (input dtype), dalpha, dbeta (fp32), and for
     L > 0 dWk, dWp, dwbeta, dconv (fp32); dS0 (fp32) when need_dS0.
+    With `saved` (filled by forward(..., saved=...) on the same inputs) this is
+    prism_backward_train, which skips the forward recompute.
     """
     _validate_inputs(q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0)
     if dO is None:
@@ -189,12 +219,19 @@ def backward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None, S0=N
     else:
         ws = workspace
     stream = torch.cuda.current_stream(dev).cuda_stream
-    _check(lib().prism_backward(
-        ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(Wk), _ptr(Wp),
-        _ptr(wbeta), _ptr(conv), _ptr(S0), _ptr(dO), _ptr(dST), _ptr(g["dq"]), _ptr(g["dk"]),
-        _ptr(g["dv"]), _ptr(g["dalpha"]), _ptr(g["dbeta"]), _ptr(g.get("dWk")), _ptr(g.get("dWp")),
-        _ptr(g.get("dwbeta")), _ptr(g.get("dconv")), _ptr(g.get("dS0")), _ptr(ws),
-        ctypes.c_size_t(ws.numel()), ctypes.c_void_p(stream)))
+    grads = (_ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dalpha"]), _ptr(g["dbeta"]),
+             _ptr(g.get("dWk")), _ptr(g.get("dWp")), _ptr(g.get("dwbeta")), _ptr(g.get("dconv")),
+             _ptr(g.get("dS0")))
+    inputs = (_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(Wk), _ptr(Wp),
+              _ptr(wbeta), _ptr(conv), _ptr(S0))
+    if saved is None:
+        _check(lib().prism_backward(ctypes.byref(desc), *inputs, _ptr(dO), _ptr(dST), *grads,
+                                    _ptr(ws), ctypes.c_size_t(ws.numel()), ctypes.c_void_p(stream)))
+    else:
+        _check(lib().prism_backward_train(ctypes.byref(desc), *inputs, _ptr(saved),
+                                          ctypes.c_size_t(saved.numel()), _ptr(dO), _ptr(dST),
+                                          *grads, _ptr(ws), ctypes.c_size_t(ws.numel()),
+                                          ctypes.c_void_p(stream)))
     return g
 
 

@@ -149,3 +149,35 @@ def test_workspace_monotone():
 def test_workspace_query_null_output():
     d = good_desc()
     assert P.lib().prism_forward_workspace(ctypes.byref(d), None) == E_NULL
+
+
+def test_training_pair_checks():
+    """prism_forward_train / prism_backward_train validate the kept buffer
+    before any HIP call."""
+    L = P.lib()
+    d = good_desc()
+    need = P.saved_bytes(d)
+    assert need > 0
+    fake = ctypes.c_void_p(0x10000)
+    ws_ok = ctypes.c_size_t(1 << 40)
+    p12 = [fake] * 12
+    # saved NULL, misaligned, too small
+    assert L.prism_forward_train(ctypes.byref(d), *p12, None, ctypes.c_size_t(need), fake, ws_ok,
+                                 None) == E_WS
+    assert "saved" in _err()
+    assert L.prism_forward_train(ctypes.byref(d), *p12, ctypes.c_void_p(0x10010),
+                                 ctypes.c_size_t(need), fake, ws_ok, None) == E_ALIGN
+    assert L.prism_forward_train(ctypes.byref(d), *p12, fake, ctypes.c_size_t(need - 1), fake, ws_ok,
+                                 None) == E_WS
+    assert str(need) in _err()
+    p10 = [fake] * 10
+    p12 = [fake] * 12   # dO dST dq dk dv dalpha dbeta dWk dWp dwbeta dconv dS0
+    assert L.prism_backward_train(ctypes.byref(d), *p10, None, ctypes.c_size_t(need), *p12, fake,
+                                  ws_ok, None) == E_WS
+    assert "saved" in _err()
+    # the workspace check still applies
+    assert L.prism_backward_train(ctypes.byref(d), *p10, fake, ctypes.c_size_t(need), *p12, fake,
+                                  ctypes.c_size_t(0), None) == E_WS
+    assert "workspace" in _err()
+    # saved size grows with T and L
+    assert P.saved_bytes(good_desc(T=4096)) > need and P.saved_bytes(good_desc(L=4)) > need
