@@ -305,7 +305,8 @@ template <int C, int NW>
 __device__ inline void invert_unit_lower(const float* A, float* Tm, float* Xs, int tid) {
   constexpr int NB = C / 16, LA = C + 1;
   static_assert(NB >= 1 && NB <= 4 && C % 16 == 0, "C in {16, 32, 48, 64}");
-  const int lane = tid & 63, wave = tid >> 6;
+  // (tid >> 6 is the same in every lane of a wave: keep the wave index scalar)
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   for (int e = tid; e < C * C; e += NW * WAVE) {
     const int r = e / C, cc = e % C;
     if (cc > r) Tm[r * LA + cc] = 0.f;
