@@ -27,7 +27,9 @@ in the kernels; each is listed with its reason in the design notes):
       Without it L = 0 would not be Gated DeltaNet (§3 item 3).
 * R2  ShortConv: depthwise, causal, width 4, over v, tap j multiplies
       v_{t-j} (j = 0 is the current token), zero history before t = 1,
-      no bias, no activation.
+      no bias, no activation.  conv_offset = 1 selects the strictly-past
+      variant, tap j multiplying v_{t-1-j} (the anchor then only sees tokens
+      the state S_{t-1} has seen).
 * R3  r^(1) = v_t - u_t.
 * R4  beta_t^(l) = sigmoid(w_beta^(l) . u_t), one scalar per token, head, step.
 * R5  GELU is the exact erf form z * Phi(z).
@@ -79,13 +81,16 @@ def _activation(name):
 # ---------------------------------------------------------------------------
 # Stage 1: ShortConv anchor (§2.2 Stage 1; reading R2)
 # ---------------------------------------------------------------------------
-def shortconv(v, conv):
-    """u_t = sum_j conv[:, :, j] * v_{t-j}, with v_s = 0 before the sequence."""
+def shortconv(v, conv, conv_offset=0):
+    """u_t = sum_j conv[:, :, j] * v_{t-o-j} (o = conv_offset), with v_s = 0
+    before the sequence."""
     B, T, H, dv = v.shape
     W = conv.shape[-1]
     u = np.zeros_like(v)
-    for j in range(min(W, T)):
-        u[:, j:] += conv[None, None, :, :, j] * v[:, : T - j]
+    for j in range(W):
+        s = j + conv_offset
+        if s < T:
+            u[:, s:] += conv[None, None, :, :, j] * v[:, : T - s]
     return u
 
 
@@ -155,7 +160,7 @@ def _unflat(x, B, H):
 
 
 def forward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None,
-            S0=None, activation="gelu", return_states=False):
+            S0=None, activation="gelu", return_states=False, conv_offset=0):
     """The PRISM layer, token by token.  Returns (o [B,T,H,dv], S_T [B,H,dv,dk]).
 
     With ``return_states`` also returns S_1..S_T as [B, T, H, dv, dk].
@@ -165,7 +170,7 @@ def forward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None,
     dv = v.shape[-1]
     L = 0 if Wk is None else Wk.shape[1]
     if L > 0:
-        u = shortconv(v, conv)
+        u = shortconv(v, conv, conv_offset)
         ref = refine(u, v, Wk, Wp, wbeta, activation)
         kap = [_flat(x) for x in ref["kappa"]]
         w = [_flat(x) for x in ref["w"]]
@@ -187,10 +192,10 @@ def forward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None,
     return out
 
 
-def injection(v, Wk, Wp, wbeta, conv, activation="gelu"):
+def injection(v, Wk, Wp, wbeta, conv, activation="gelu", conv_offset=0):
     """The refinement part of the write, sum_l beta^(l) delta^(l) k^(l)^T,
     materialised per token: [B, T, H, dv, dk] (§2.2, final injection matrix)."""
-    u = shortconv(v, conv)
+    u = shortconv(v, conv, conv_offset)
     ref = refine(u, v, Wk, Wp, wbeta, activation)
     dv, dk = v.shape[-1], Wk.shape[2]
     out = np.zeros(v.shape[:3] + (dv, dk))
@@ -203,7 +208,7 @@ def injection(v, Wk, Wp, wbeta, conv, activation="gelu"):
 # backward: the adjoint of forward(), token by token in reverse
 # ---------------------------------------------------------------------------
 def backward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None,
-             S0=None, dO=None, dST=None, activation="gelu", segment=64):
+             S0=None, dO=None, dST=None, activation="gelu", segment=64, conv_offset=0):
     """Gradients of  <dO, o> + <dST, S_T>  with respect to every input.
 
     The reverse pass needs S_{t-1} and S_t at each t.  States are recomputed
@@ -220,7 +225,7 @@ def backward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None,
     act, act_grad = _activation(activation)
 
     if L > 0:
-        u = shortconv(v, conv)
+        u = shortconv(v, conv, conv_offset)
         ref = refine(u, v, Wk, Wp, wbeta, activation)
         kap = [_flat(x) for x in ref["kappa"]]
         w = [_flat(x) for x in ref["w"]]
@@ -307,11 +312,13 @@ def backward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None,
             du += np.einsum("hij,bthi->bthj", Wk[:, l], dkap_b[l])
         dv_full = dv_full + a
         du = du - a
-        # ShortConv: u_t = sum_j c_j * v_{t-j}
+        # ShortConv: u_t = sum_j c_j * v_{t-o-j}
         dconv = np.zeros_like(conv)
-        for j in range(min(conv.shape[-1], T)):
-            dconv[:, :, j] += np.einsum("bthi,bthi->hi", du[:, j:], v[:, : T - j])
-            dv_full[:, : T - j] += conv[None, None, :, :, j] * du[:, j:]
+        for j in range(conv.shape[-1]):
+            s = j + conv_offset
+            if s < T:
+                dconv[:, :, j] += np.einsum("bthi,bthi->hi", du[:, s:], v[:, : T - s])
+                dv_full[:, : T - s] += conv[None, None, :, :, j] * du[:, s:]
         grads.update(dWk=dWk, dWp=dWp, dwbeta=dwbeta, dconv=dconv)
     grads["dv"] = dv_full
     return grads

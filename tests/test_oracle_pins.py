@@ -76,6 +76,25 @@ def test_shortconv_impulse_response_and_no_leak_across_batch():
     assert np.all(u[1, :2] == 0) and np.all(u[1, 6:] == 0)
 
 
+def test_shortconv_strictly_past_is_current_taps_on_delayed_input():
+    """conv_offset = 1 equals the current-token convolution of v delayed by one
+    token (zero first row); an impulse at t reaches u_{t+1+j} through tap j."""
+    x = _inputs(B=2, T=11, H=3, d=5)
+    vd = np.zeros_like(x["v"])
+    vd[:, 1:] = x["v"][:, :-1]
+    assert np.array_equal(O.shortconv(x["v"], x["conv"], conv_offset=1),
+                          O.shortconv(vd, x["conv"]))
+    conv = np.arange(1, 1 + 3 * 4, dtype=np.float64).reshape(1, 3, 4)
+    v = np.zeros((1, 9, 1, 3))
+    v[0, 2, 0, :] = 1.0
+    u = O.shortconv(v, conv, conv_offset=1)
+    for j in range(4):
+        assert np.array_equal(u[0, 3 + j, 0], conv[0, :, j])
+    assert np.all(u[0, :3] == 0) and np.all(u[0, 7:] == 0)
+    # first token sees no history at all
+    assert np.all(O.shortconv(x["v"], x["conv"], conv_offset=1)[:, 0] == 0)
+
+
 # ---------------------------------------------------------------------------
 # Stage 2: refinement chain (§2.2 Stage 2)
 # ---------------------------------------------------------------------------
@@ -259,13 +278,16 @@ def test_injection_rank():
 # ---------------------------------------------------------------------------
 # backward: central finite differences in float64
 # ---------------------------------------------------------------------------
-def _loss(x, dO, dST, L):
-    o, s = _fwd(x, L=L)
+def _loss(x, dO, dST, L, **kw):
+    o, s = _fwd(x, L=L, **kw)
     return float(np.sum(dO * o) + np.sum(dST * s))
 
 
-@pytest.mark.parametrize("L", [0, 1, 2])
-def test_backward_matches_finite_differences(L):
+@pytest.mark.parametrize("L,kw", [(0, {}), (1, {}), (2, {}),
+                                  (2, {"activation": "identity"}),
+                                  (2, {"conv_offset": 1})],
+                         ids=["L0", "L1", "L2", "L2-identity", "L2-past-conv"])
+def test_backward_matches_finite_differences(L, kw):
     x = make_inputs(1, 7, 2, 3, L, "f32", seed=11 + L, random_S0=True, with_dST=True)
     x = {k_: (None if v_ is None else v_.copy()) for k_, v_ in x.items()}
     dO, dST = x["dO"], x["dST"]
@@ -274,7 +296,7 @@ def test_backward_matches_finite_differences(L):
         args.update(Wk=None, Wp=None, wbeta=None, conv=None)
     g = O.backward(args["q"], args["k"], args["v"], args["alpha"], args["beta"],
                    args["Wk"], args["Wp"], args["wbeta"], args["conv"], S0=args["S0"],
-                   dO=dO, dST=dST, segment=3)
+                   dO=dO, dST=dST, segment=3, **kw)
     names = {"q": "dq", "k": "dk", "v": "dv", "alpha": "dalpha", "beta": "dbeta", "S0": "dS0"}
     if L > 0:
         names.update(Wk="dWk", Wp="dWp", wbeta="dwbeta", conv="dconv")
@@ -285,9 +307,9 @@ def test_backward_matches_finite_differences(L):
         for idx in np.ndindex(X.shape):
             old = X[idx]
             X[idx] = old + h
-            fp = _loss(x, dO, dST, L)
+            fp = _loss(x, dO, dST, L, **kw)
             X[idx] = old - h
-            fm = _loss(x, dO, dST, L)
+            fm = _loss(x, dO, dST, L, **kw)
             X[idx] = old
             fd[idx] = (fp - fm) / (2 * h)
         err = np.max(np.abs(fd - g[gname])) / max(1e-3, np.max(np.abs(fd)))
