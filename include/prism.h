@@ -61,6 +61,14 @@ typedef enum {
   PRISM_BF16 = 1  /* the same tensors in bfloat16 (round-to-nearest-even)  */
 } prism_dtype;
 
+/* Refinement step activation (summary §2.2 "Residual Update"): the step
+ * correction is delta = GELU(p * r) (the method) or delta = p * r (the
+ * ablation without the nonlinearity). */
+typedef enum {
+  PRISM_ACT_GELU = 0,
+  PRISM_ACT_IDENTITY = 1
+} prism_activation;
+
 /* Problem descriptor.
  *   B, T, H    batch, sequence length, heads            (each >= 1)
  *   dk, dv     key / value head dimension; must be equal, in {16, 32, 64, 128}
@@ -70,10 +78,19 @@ typedef enum {
  *              (PRISM_F32 also needs dk * chunk <= 2048); any T >= 1 is
  *              accepted (the last chunk may be partial)
  *   conv_width ShortConv width; must be 4
- *   dtype      storage type of the dtype-typed tensors (see prism_dtype)   */
+ *   dtype      storage type of the dtype-typed tensors (see prism_dtype)
+ *   activation refinement step activation, a prism_activation value
+ *              (0 = GELU, the method's step)
+ *   conv_offset ShortConv tap offset: 0 = tap j multiplies v_{t-j} (the
+ *              current token and the three before it), 1 = tap j multiplies
+ *              v_{t-1-j} (strictly past tokens, the ones the state S_{t-1}
+ *              has seen; summary §2.2 Stage 1)
+ * A zero-initialised tail (activation = conv_offset = 0) is the method as
+ * described.  Both fields are ignored when L = 0.                          */
 typedef struct {
   int B, T, H, dk, dv, L, chunk, conv_width;
   prism_dtype dtype;
+  int activation, conv_offset;
 } prism_desc;
 
 /* Tensor layouts (element type "dt" = desc->dtype; f32 = float32):

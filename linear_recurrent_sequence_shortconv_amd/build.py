@@ -18,13 +18,18 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libprism.so")
 
+# slowest first, so the parallel compile finishes early
 SOURCES = [
-    "prism_api.cpp",
-    "refine_fwd.hip",
-    "chunk_fwd.hip",
-    "state.hip",
     "chunk_bwd.hip",
+    "chunk_fwd.hip",
+    "refine_bwd_gelu.hip",
+    "refine_bwd_gelu_past.hip",
+    "refine_bwd_identity.hip",
+    "refine_bwd_identity_past.hip",
+    "refine_fwd.hip",
+    "state.hip",
     "refine_bwd.hip",
+    "prism_api.cpp",
 ]
 
 ARCH = "gfx950"

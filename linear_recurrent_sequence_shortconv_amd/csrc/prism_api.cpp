@@ -141,6 +141,10 @@ prism_status check_desc(const prism_desc* desc, prism::Dims* out) {
   if (d.chunk != 16 && d.chunk != 32 && d.chunk != 64)
     return fail(PRISM_ERR_UNSUPPORTED, "chunk must be 16, 32 or 64");
   if (d.conv_width != 4) return fail(PRISM_ERR_UNSUPPORTED, "conv_width must be 4");
+  if (d.activation != PRISM_ACT_GELU && d.activation != PRISM_ACT_IDENTITY)
+    return fail(PRISM_ERR_UNSUPPORTED, "activation must be PRISM_ACT_GELU or PRISM_ACT_IDENTITY");
+  if (d.conv_offset != 0 && d.conv_offset != 1)
+    return fail(PRISM_ERR_UNSUPPORTED, "conv_offset must be 0 or 1");
   const double elems = (double)d.B * d.T * d.H * d.dk * (d.L + 1);
   if (elems > 4.0e12) return fail(PRISM_ERR_SHAPE, "problem too large");
   if ((long long)d.B * d.H * ((d.T + d.chunk - 1) / d.chunk) > 0x7fffffffLL)
@@ -154,6 +158,8 @@ prism_status check_desc(const prism_desc* desc, prism::Dims* out) {
   x.C = d.chunk;
   x.NC = (d.T + d.chunk - 1) / d.chunk;
   x.Tp = x.NC * x.C;
+  x.act = d.activation == PRISM_ACT_IDENTITY ? prism::ACT_IDENTITY : prism::ACT_GELU;
+  x.off = d.conv_offset;
   *out = x;
   return PRISM_OK;
 }

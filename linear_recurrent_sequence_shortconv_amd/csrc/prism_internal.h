@@ -8,10 +8,16 @@ namespace prism {
 
 typedef __bf16 bf16;
 
+// Refinement step activation: delta = GELU(p * r) or delta = p * r.
+constexpr int ACT_GELU = 0, ACT_IDENTITY = 1;
+
 // Problem dimensions after validation.  D = d_k = d_v; C = chunk length;
-// NC = ceil(T / C) chunks per sequence; Tp = NC * C padded length.
+// NC = ceil(T / C) chunks per sequence; Tp = NC * C padded length;
+// act = step activation; off = ShortConv tap offset (0: tap j reads v_{t-j},
+// 1: tap j reads v_{t-1-j}).
 struct Dims {
   int B, T, H, D, L, C, NC, Tp;
+  int act, off;
 };
 
 // Every launcher enqueues on `stream` and returns hipGetLastError().

@@ -1,0 +1,9 @@
+// Refinement / ShortConv backward instantiated for GELU steps, strictly past ShortConv taps.
+#include "refine_bwd_kernel.h"
+
+namespace prism {
+template hipError_t launch_refine_bwd_main<bf16, ACT_GELU, 1>(const Dims&, const RefineBwdArgs<bf16>&,
+                                                         hipStream_t);
+template hipError_t launch_refine_bwd_main<float, ACT_GELU, 1>(const Dims&, const RefineBwdArgs<float>&,
+                                                          hipStream_t);
+}  // namespace prism

@@ -1,10 +1,11 @@
 // Stage 1 (ShortConv anchor) and Stage 2 (L unrolled refinement steps) of the
 // PRISM layer, one kernel.  PRISM technical summary §2.2 "Input-Anchored Loop
 // Unrolling":
-//   u_t      = sum_{j=0..3} c[:, j] * v_{t-j}      (depthwise causal conv over v)
+//   u_t      = sum_{j=0..3} c[:, j] * v_{t-o-j}    (depthwise causal conv over v;
+//              o = 0 taps the current token, o = 1 strictly past tokens)
 //   r^(1)    = v_t - u_t
 //   k^(l)    = W_k^(l) u_t,  p^(l) = W_p^(l) u_t,  beta^(l) = sigmoid(w_beta^(l) . u_t)
-//   delta^(l)= GELU(p^(l) * r^(l)),  r^(l+1) = r^(l) - delta^(l)
+//   delta^(l)= GELU(p^(l) * r^(l)) (or p^(l) * r^(l)),  r^(l+1) = r^(l) - delta^(l)
 //   output pairs (k^(l), w^(l) = beta^(l) delta^(l)), whose outer products form
 //   the rank-L injection B_t of §2.2.
 //
@@ -25,7 +26,7 @@ constexpr int RF_TT = 64;    // tokens per workgroup
 constexpr int RF_NT = 256;   // threads per workgroup
 constexpr int RF_NW = 4;
 
-template <typename E, int D>
+template <typename E, int D, int ACT, int OFF>
 __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
     const E* __restrict__ v, const E* __restrict__ conv, const E* __restrict__ Wk,
     const E* __restrict__ Wp, const E* __restrict__ wbeta, E* __restrict__ Kl,
@@ -39,9 +40,10 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
   constexpr int KS = Mfma<E>::KSTEP;
   constexpr int NK = D / KS;
   constexpr int VN = 16 / sizeof(E);
+  constexpr int HL = 3 + OFF;   // v rows before the tile that the taps reach
 
-  // v rows (t0-3 .. t0+63) until the residual is formed, then the k^(l) staging tile
-  constexpr int VB = cmax((RF_TT + 3) * D, RF_TT * LD);
+  // v rows (t0-HL .. t0+63) until the residual is formed, then the k^(l) staging tile
+  constexpr int VB = cmax((RF_TT + HL) * D, RF_TT * LD);
   __shared__ __attribute__((aligned(16))) E vbuf[VB];
   E* obk = vbuf;
   __shared__ __attribute__((aligned(16))) E ubuf[RF_TT * LD];
@@ -67,10 +69,10 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
   // ---- w_beta rows of this head (L x D) ----
   for (int e = tid; e < L * (D / VN); e += RF_NT)
     st16(wbs + e * VN, ld16(wbeta + (long)h * L * D + e * VN));
-  // ---- v rows t0-3 .. t0+63 (zeros outside [0, T)) ----
-  for (int e = tid; e < (RF_TT + 3) * (D / VN); e += RF_NT) {
+  // ---- v rows t0-HL .. t0+63 (zeros outside [0, T)) ----
+  for (int e = tid; e < (RF_TT + HL) * (D / VN); e += RF_NT) {
     const int r = e / (D / VN), c = (e % (D / VN)) * VN;
-    const int t = t0 - 3 + r;
+    const int t = t0 - HL + r;
     uint4 x = {0u, 0u, 0u, 0u};
     if (t >= 0 && t < T) x = ld16(vseq + t * tok_stride + c);
     st16(vbuf + r * D + c, x);
@@ -109,8 +111,8 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
         float u = 0.f, val = 0.f;
         if (FT_OK(n) && t0 + t < T) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) u += taps[j] * to_f(vbuf[(t + 3 - j) * D + f]);
-          val = to_f(vbuf[(t + 3) * D + f]) - u;
+          for (int j = 0; j < 4; ++j) u += taps[j] * to_f(vbuf[(t + HL - OFF - j) * D + f]);
+          val = to_f(vbuf[(t + HL) * D + f]) - u;
         }
         r[m][nn][i] = val;
         if (FT_OK(n)) {
@@ -196,7 +198,10 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int t = 16 * m + 4 * (lane >> 4) + i;
-            const float dl = gelu_erf(acc[m][nn][i] * r[m][nn][i]);
+            const float z = acc[m][nn][i] * r[m][nn][i];
+            float dl;
+            if constexpr (ACT == ACT_IDENTITY) dl = z;
+            else dl = gelu_erf(z);
             r[m][nn][i] -= dl;
             obw[t * LD + f] = to_t<E>(gate[l][t] * dl);
           }
@@ -227,8 +232,14 @@ static hipError_t refine_launch_d(const Dims& d, const E* v, const E* conv, cons
                                   const E* Wp, const E* wbeta, E* Kl, E* Wl, hipStream_t s) {
   const int ntiles = (d.Tp + RF_TT - 1) / RF_TT;
   const int nblk = ntiles * d.B * d.H;
-  hipLaunchKernelGGL((refine_fwd_kernel<E, D>), dim3(nblk), dim3(RF_NT), 0, s, v, conv, Wk, Wp,
-                     wbeta, Kl, Wl, d.B, d.T, d.H, d.L, d.Tp);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(nblk), dim3(RF_NT), 0, s, v, conv, Wk, Wp, wbeta, Kl, Wl, d.B, d.T,
+                       d.H, d.L, d.Tp);
+  };
+  if (d.act == ACT_IDENTITY)
+    d.off ? go(refine_fwd_kernel<E, D, ACT_IDENTITY, 1>) : go(refine_fwd_kernel<E, D, ACT_IDENTITY, 0>);
+  else
+    d.off ? go(refine_fwd_kernel<E, D, ACT_GELU, 1>) : go(refine_fwd_kernel<E, D, ACT_GELU, 0>);
   return hipGetLastError();
 }
 

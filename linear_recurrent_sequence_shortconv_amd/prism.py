@@ -26,7 +26,8 @@ EXPORTS = ("prism_forward_workspace", "prism_backward_workspace", "prism_forward
 class Desc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int),
                 ("dk", ctypes.c_int), ("dv", ctypes.c_int), ("L", ctypes.c_int),
-                ("chunk", ctypes.c_int), ("conv_width", ctypes.c_int), ("dtype", ctypes.c_int)]
+                ("chunk", ctypes.c_int), ("conv_width", ctypes.c_int), ("dtype", ctypes.c_int),
+                ("activation", ctypes.c_int), ("conv_offset", ctypes.c_int)]
 
 
 _lib = None
@@ -65,8 +66,14 @@ def lib():
     return _lib
 
 
-def make_desc(B, T, H, dk, dv, L, chunk, dtype, conv_width=4):
-    return Desc(B, T, H, dk, dv, L, chunk, conv_width, dtype)
+ACTIVATIONS = {"gelu": 0, "identity": 1}
+
+
+def make_desc(B, T, H, dk, dv, L, chunk, dtype, conv_width=4, activation="gelu", conv_offset=0):
+    if activation not in ACTIVATIONS:
+        raise ValueError(f"activation must be one of {sorted(ACTIVATIONS)}, got {activation!r}")
+    return Desc(B, T, H, dk, dv, L, chunk, conv_width, dtype, ACTIVATIONS[activation],
+                int(conv_offset))
 
 
 def _check(status):
@@ -96,11 +103,12 @@ def _req(t, name, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _desc_from(q, v, Wk, chunk):
+def _desc_from(q, v, Wk, chunk, activation="gelu", conv_offset=0):
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     L = 0 if Wk is None else Wk.shape[1]
-    return make_desc(B, T, H, dk, dv, L, chunk, _dtype_code(q))
+    return make_desc(B, T, H, dk, dv, L, chunk, _dtype_code(q), activation=activation,
+                     conv_offset=conv_offset)
 
 
 def _workspace(nbytes, device):
@@ -143,18 +151,20 @@ def _validate_inputs(q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0):
 
 
 def forward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None, S0=None, chunk=64,
-            workspace=None, saved=None):
+            workspace=None, saved=None, activation="gelu", conv_offset=0):
     """PRISM layer forward.  Returns (o, S_T).
 
     q, k [B,T,H,dk], v [B,T,H,dv] (bf16 or fp32); alpha, beta [B,T,H] fp32;
     Wk [H,L,dk,dv], Wp [H,L,dv,dv], wbeta [H,L,dv], conv [H,dv,4] in q's
     dtype (all None for L = 0); S0 [B,H,dv,dk] fp32 or None.
+    activation: "gelu" (delta = GELU(p r)) or "identity" (delta = p r);
+    conv_offset: 0 (tap j on v_{t-j}) or 1 (tap j on v_{t-1-j}).
     With `saved` (a buffer from saved_buffer()) this is the training forward
     (prism_forward_train): the buffer then holds what backward(saved=...)
     needs.
     """
     _validate_inputs(q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0)
-    desc = _desc_from(q, v, Wk, chunk)
+    desc = _desc_from(q, v, Wk, chunk, activation, conv_offset)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     o = torch.empty_like(v)
@@ -180,19 +190,22 @@ def forward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None, S0=No
 
 
 def saved_buffer(q, v, Wk=None, chunk=64):
-    """A 256-byte aligned device buffer for the training pair (uint8 view)."""
+    """A 256-byte aligned device buffer for the training pair (uint8 view);
+    its size does not depend on the activation or the tap offset."""
     desc = _desc_from(q, v, Wk, chunk)
     return _workspace(saved_bytes(desc), q.device)[1]
 
 
 def backward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None, S0=None, dO=None,
-             dST=None, chunk=64, need_dS0=False, workspace=None, saved=None):
+             dST=None, chunk=64, need_dS0=False, workspace=None, saved=None, activation="gelu",
+             conv_offset=0):
     """Gradients of <dO, o> + <dST, S_T> with respect to every input.
 
     Returns a dict: dq, dk, dv (input dtype), dalpha, dbeta (fp32), and for
     L > 0 dWk, dWp, dwbeta, dconv (fp32); dS0 (fp32) when need_dS0.
     With `saved` (filled by forward(..., saved=...) on the same inputs) this is
-    prism_backward_train, which skips the forward recompute.
+    prism_backward_train, which skips the forward recompute.  activation and
+    conv_offset as in forward() (and equal to the forward's with `saved`).
     """
     _validate_inputs(q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0)
     if dO is None:
@@ -200,7 +213,7 @@ def backward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None, S0=N
     _req(dO, "dO", q.dtype, q.device)
     if dST is not None:
         _req(dST, "dST", torch.float32, q.device)
-    desc = _desc_from(q, v, Wk, chunk)
+    desc = _desc_from(q, v, Wk, chunk, activation, conv_offset)
     B, T, H, dk = q.shape
     dv_ = v.shape[-1]
     dev = q.device

@@ -91,6 +91,28 @@ def test_conv_width_and_fp32_envelope():
     assert P.lib().prism_forward_workspace(ctypes.byref(d), ctypes.byref(n)) == OK and n.value > 0
 
 
+def test_variant_fields():
+    """activation in {GELU, identity} and conv_offset in {0, 1}; anything else
+    is rejected; the strictly-past taps own one token less per backward tile,
+    so the backward workspace grows, while the training buffer does not change."""
+    for act, off in ((0, 0), (1, 0), (0, 1), (1, 1)):
+        d = good_desc()
+        d.activation, d.conv_offset = act, off
+        n = ctypes.c_size_t(0)
+        assert P.lib().prism_forward_workspace(ctypes.byref(d), ctypes.byref(n)) == OK
+    for field, value in (("activation", 2), ("activation", -1), ("conv_offset", 2),
+                         ("conv_offset", -1)):
+        d = good_desc()
+        setattr(d, field, value)
+        assert _fwd(d) == E_UNSUP and field in _err()
+    with pytest.raises(ValueError):
+        P.make_desc(1, 8, 1, 16, 16, 1, 16, P.PRISM_BF16, activation="relu")
+    d0, d1 = good_desc(T=4096), good_desc(T=4096)
+    d1.conv_offset = 1
+    assert P.backward_workspace_bytes(d1) > P.backward_workspace_bytes(d0)
+    assert P.saved_bytes(d1) == P.saved_bytes(d0)
+
+
 def test_null_desc_and_pointers():
     assert _fwd(None) == E_NULL
     fake = ctypes.c_void_p(0x10000)
