@@ -29,7 +29,9 @@ in the kernels; each is listed with its reason in the design notes):
       v_{t-j} (j = 0 is the current token), zero history before t = 1,
       no bias, no activation.  conv_offset = 1 selects the strictly-past
       variant, tap j multiplying v_{t-1-j} (the anchor then only sees tokens
-      the state S_{t-1} has seen).
+      the state S_{t-1} has seen).  A call may continue an earlier one: then
+      the four values before the sequence come in as ``conv_hist`` instead of
+      zeros, as S0 carries the state.
 * R3  r^(1) = v_t - u_t.
 * R4  beta_t^(l) = sigmoid(w_beta^(l) . u_t), one scalar per token, head, step.
 * R5  GELU is the exact erf form z * Phi(z).
@@ -42,6 +44,7 @@ Array layouts (all float64 numpy arrays):
   alpha, beta [B, T, H]            S0, S_T  [B, H, dv, dk]
   Wk          [H, L, dk, dv]       Wp       [H, L, dv, dv]
   wbeta       [H, L, dv]           conv     [H, dv, W]   (W = 4)
+  conv_hist   [B, 4, H, dv]        (v_{-4} .. v_{-1}, v's own layout)
 """
 
 import math
@@ -81,9 +84,13 @@ def _activation(name):
 # ---------------------------------------------------------------------------
 # Stage 1: ShortConv anchor (§2.2 Stage 1; reading R2)
 # ---------------------------------------------------------------------------
-def shortconv(v, conv, conv_offset=0):
-    """u_t = sum_j conv[:, :, j] * v_{t-o-j} (o = conv_offset), with v_s = 0
-    before the sequence."""
+def shortconv(v, conv, conv_offset=0, hist=None):
+    """u_t = sum_j conv[:, :, j] * v_{t-o-j} (o = conv_offset).  Before the
+    sequence v_s is zero, or, with ``hist`` [B, 4, H, dv], the four values
+    v_{-4} .. v_{-1} that preceded it (oldest first)."""
+    if hist is not None:
+        ext = np.concatenate([hist, v], axis=1)
+        return shortconv(ext, conv, conv_offset)[:, hist.shape[1]:]
     B, T, H, dv = v.shape
     W = conv.shape[-1]
     u = np.zeros_like(v)
@@ -159,8 +166,16 @@ def _unflat(x, B, H):
     return np.moveaxis(x.reshape((T, B, H) + x.shape[2:]), 0, 1)
 
 
+def conv_state(v, hist=None):
+    """The ShortConv history after the sequence: the last four values of
+    (hist or zeros) followed by v, [B, 4, H, dv], oldest first."""
+    B, T, H, dv = v.shape
+    h = np.zeros((B, 4, H, dv)) if hist is None else hist
+    return np.concatenate([h, v], axis=1)[:, -4:]
+
+
 def forward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None,
-            S0=None, activation="gelu", return_states=False, conv_offset=0):
+            S0=None, activation="gelu", return_states=False, conv_offset=0, conv_hist=None):
     """The PRISM layer, token by token.  Returns (o [B,T,H,dv], S_T [B,H,dv,dk]).
 
     With ``return_states`` also returns S_1..S_T as [B, T, H, dv, dk].
@@ -170,7 +185,7 @@ def forward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None,
     dv = v.shape[-1]
     L = 0 if Wk is None else Wk.shape[1]
     if L > 0:
-        u = shortconv(v, conv, conv_offset)
+        u = shortconv(v, conv, conv_offset, conv_hist)
         ref = refine(u, v, Wk, Wp, wbeta, activation)
         kap = [_flat(x) for x in ref["kappa"]]
         w = [_flat(x) for x in ref["w"]]
@@ -208,7 +223,8 @@ def injection(v, Wk, Wp, wbeta, conv, activation="gelu", conv_offset=0):
 # backward: the adjoint of forward(), token by token in reverse
 # ---------------------------------------------------------------------------
 def backward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None,
-             S0=None, dO=None, dST=None, activation="gelu", segment=64, conv_offset=0):
+             S0=None, dO=None, dST=None, activation="gelu", segment=64, conv_offset=0,
+             conv_hist=None):
     """Gradients of  <dO, o> + <dST, S_T>  with respect to every input.
 
     The reverse pass needs S_{t-1} and S_t at each t.  States are recomputed
@@ -216,7 +232,8 @@ def backward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None,
     memory stays at (T/segment + segment) states per sequence.
 
     Returns a dict with dq, dk, dv, dalpha, dbeta, dS0 and, when L > 0,
-    dWk, dWp, dwbeta, dconv (same shapes as the inputs).
+    dWk, dWp, dwbeta, dconv (same shapes as the inputs), and dconv_hist when
+    ``conv_hist`` is given.
     """
     B, T, H, dk = k.shape
     dv_ = v.shape[-1]
@@ -225,7 +242,7 @@ def backward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None,
     act, act_grad = _activation(activation)
 
     if L > 0:
-        u = shortconv(v, conv, conv_offset)
+        u = shortconv(v, conv, conv_offset, conv_hist)
         ref = refine(u, v, Wk, Wp, wbeta, activation)
         kap = [_flat(x) for x in ref["kappa"]]
         w = [_flat(x) for x in ref["w"]]
@@ -312,13 +329,22 @@ def backward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None,
             du += np.einsum("hij,bthi->bthj", Wk[:, l], dkap_b[l])
         dv_full = dv_full + a
         du = du - a
-        # ShortConv: u_t = sum_j c_j * v_{t-o-j}
+        # ShortConv: u_t = sum_j c_j * v_{t-o-j}, over the history (zeros
+        # without one) followed by the sequence
+        hist = np.zeros((B, 4, H, dv_)) if conv_hist is None else conv_hist
+        ve = np.concatenate([hist, v], axis=1)
+        due = np.concatenate([np.zeros_like(hist), du], axis=1)
+        dve = np.zeros_like(ve)
+        Te = T + 4
         dconv = np.zeros_like(conv)
         for j in range(conv.shape[-1]):
             s = j + conv_offset
-            if s < T:
-                dconv[:, :, j] += np.einsum("bthi,bthi->hi", du[:, s:], v[:, : T - s])
-                dv_full[:, : T - s] += conv[None, None, :, :, j] * du[:, s:]
+            if s < Te:
+                dconv[:, :, j] += np.einsum("bthi,bthi->hi", due[:, s:], ve[:, : Te - s])
+                dve[:, : Te - s] += conv[None, None, :, :, j] * due[:, s:]
+        dv_full = dv_full + dve[:, 4:]
+        if conv_hist is not None:
+            grads["dconv_hist"] = dve[:, :4]
         grads.update(dWk=dWk, dWp=dWp, dwbeta=dwbeta, dconv=dconv)
     grads["dv"] = dv_full
     return grads

@@ -285,11 +285,18 @@ def _loss(x, dO, dST, L, **kw):
 
 @pytest.mark.parametrize("L,kw", [(0, {}), (1, {}), (2, {}),
                                   (2, {"activation": "identity"}),
-                                  (2, {"conv_offset": 1})],
-                         ids=["L0", "L1", "L2", "L2-identity", "L2-past-conv"])
+                                  (2, {"conv_offset": 1}),
+                                  (2, {"conv_offset": 1, "conv_hist": True}),
+                                  (1, {"conv_hist": True})],
+                         ids=["L0", "L1", "L2", "L2-identity", "L2-past-conv",
+                              "L2-past-conv-history", "L1-history"])
 def test_backward_matches_finite_differences(L, kw):
     x = make_inputs(1, 7, 2, 3, L, "f32", seed=11 + L, random_S0=True, with_dST=True)
     x = {k_: (None if v_ is None else v_.copy()) for k_, v_ in x.items()}
+    kw = dict(kw)
+    if kw.get("conv_hist"):
+        x["conv_hist"] = np.random.default_rng(5).standard_normal((1, 4, 2, 3))
+        kw["conv_hist"] = x["conv_hist"]          # the array FD perturbs in place
     dO, dST = x["dO"], x["dST"]
     args = dict(x)
     if L == 0:
@@ -300,6 +307,8 @@ def test_backward_matches_finite_differences(L, kw):
     names = {"q": "dq", "k": "dk", "v": "dv", "alpha": "dalpha", "beta": "dbeta", "S0": "dS0"}
     if L > 0:
         names.update(Wk="dWk", Wp="dWp", wbeta="dwbeta", conv="dconv")
+    if "conv_hist" in kw:
+        names.update(conv_hist="dconv_hist")
     h = 1e-6
     for name, gname in names.items():
         X = x[name]
@@ -324,3 +333,72 @@ def test_backward_segmenting_does_not_change_result():
     for key in gs[0]:
         for other in gs[1:]:
             assert np.max(np.abs(gs[0][key] - other[key])) < 1e-12, key
+
+
+# ---------------------------------------------------------------------------
+# continuation: S0 and the ShortConv history carry one call into the next
+# ---------------------------------------------------------------------------
+def _split_forward(x, cuts, **kw):
+    """Run the oracle piece by piece, handing S_T and the conv history on."""
+    W = [x[n] for n in ("Wk", "Wp", "wbeta", "conv")]
+    S, hist, outs = x["S0"], None, []
+    edges = [0] + list(cuts) + [x["q"].shape[1]]
+    for a, b in zip(edges[:-1], edges[1:]):
+        sl = lambda n: x[n][:, a:b]
+        o, S = O.forward(sl("q"), sl("k"), sl("v"), sl("alpha"), sl("beta"), *W, S0=S,
+                         conv_hist=hist, **kw)
+        hist = O.conv_state(sl("v"), hist)
+        outs.append(o)
+    return np.concatenate(outs, axis=1), S, hist
+
+
+@pytest.mark.parametrize("off", [0, 1])
+@pytest.mark.parametrize("cuts", [(5,), (1, 2, 3), (2, 4, 6, 8, 10), (11,)])
+def test_forward_continuation_is_exact(off, cuts):
+    """Splitting a sequence anywhere (pieces shorter than the taps included)
+    and carrying S and the last four values of v reproduces the whole run."""
+    x = _inputs(B=2, T=12, H=2, d=4, L=2, seed=21, random_S0=True)
+    W = [x[n] for n in ("Wk", "Wp", "wbeta", "conv")]
+    o, S = O.forward(x["q"], x["k"], x["v"], x["alpha"], x["beta"], *W, S0=x["S0"],
+                     conv_offset=off)
+    o2, S2, hist = _split_forward(x, cuts, conv_offset=off)
+    assert np.max(np.abs(o2 - o)) < 1e-13 and np.max(np.abs(S2 - S)) < 1e-13
+    assert np.array_equal(hist, x["v"][:, -4:])
+
+
+def test_conv_state_of_short_pieces():
+    v = np.arange(2 * 3 * 1 * 2, dtype=np.float64).reshape(2, 3, 1, 2) + 1
+    h = O.conv_state(v)                      # zero history, 3 tokens: one zero row first
+    assert np.all(h[:, 0] == 0) and np.array_equal(h[:, 1:], v)
+    h2 = O.conv_state(v[:, :1], h)           # one more token shifts by one
+    assert np.array_equal(h2[:, :3], h[:, 1:]) and np.array_equal(h2[:, 3], v[:, 0])
+
+
+@pytest.mark.parametrize("off", [0, 1])
+def test_backward_continuation_is_exact(off):
+    """Gradients of a run split in two: the second piece's dS0 is the first
+    piece's dST, its dconv_hist adds to dv of the first piece's last four
+    tokens, and weight gradients add up; together they equal the whole run's."""
+    T, T1 = 11, 6
+    x = make_inputs(1, T, 2, 3, 2, "f32", seed=77, random_S0=True, with_dST=True)
+    W = [x[n] for n in ("Wk", "Wp", "wbeta", "conv")]
+    g = O.backward(x["q"], x["k"], x["v"], x["alpha"], x["beta"], *W, S0=x["S0"], dO=x["dO"],
+                   dST=x["dST"], conv_offset=off)
+    p1 = {n: x[n][:, :T1] for n in ("q", "k", "v", "alpha", "beta", "dO")}
+    p2 = {n: x[n][:, T1:] for n in ("q", "k", "v", "alpha", "beta", "dO")}
+    _, S1 = O.forward(p1["q"], p1["k"], p1["v"], p1["alpha"], p1["beta"], *W, S0=x["S0"],
+                      conv_offset=off)
+    hist = O.conv_state(p1["v"])
+    g2 = O.backward(p2["q"], p2["k"], p2["v"], p2["alpha"], p2["beta"], *W, S0=S1, dO=p2["dO"],
+                    dST=x["dST"], conv_offset=off, conv_hist=hist)
+    g1 = O.backward(p1["q"], p1["k"], p1["v"], p1["alpha"], p1["beta"], *W, S0=x["S0"],
+                    dO=p1["dO"], dST=g2["dS0"], conv_offset=off)
+    dv1 = g1["dv"].copy()
+    dv1[:, T1 - 4:] += g2["dconv_hist"]
+    cat = lambda n: np.concatenate([g1[n], g2[n]], axis=1)
+    assert np.max(np.abs(np.concatenate([dv1, g2["dv"]], axis=1) - g["dv"])) < 1e-12
+    for n in ("dq", "dk", "dalpha", "dbeta"):
+        assert np.max(np.abs(cat(n) - g[n])) < 1e-12, n
+    for n in ("dWk", "dWp", "dwbeta", "dconv"):
+        assert np.max(np.abs(g1[n] + g2[n] - g[n])) < 1e-12, n
+    assert np.max(np.abs(g1["dS0"] - g["dS0"])) < 1e-12
