@@ -99,38 +99,53 @@ typedef struct {
  *   Wk          [H, L, dk, dv] dt      k^(l) = Wk[h, l] u   (row i . u)
  *   Wp          [H, L, dv, dv] dt      p^(l) = Wp[h, l] u
  *   wbeta       [H, L, dv]     dt      beta^(l) = sigmoid(wbeta[h, l] . u)
- *   conv        [H, dv, 4]     dt      tap j multiplies v_{t-j} (j = 0: current token)
+ *   conv        [H, dv, 4]     dt      tap j multiplies v_{t-j} (j = 0: current token),
+ *                                      or v_{t-1-j} with conv_offset = 1
+ *   conv_hist   [B, 4, H, dv]  dt      v_{-4} .. v_{-1}: the four values before the
+ *                                      sequence, oldest first (v's own layout)
  *   S0, ST      [B, H, dv, dk] f32     state entering / leaving the sequence
  *   dST, dS0    [B, H, dv, dk] f32
  *   dq, dk, dv  as q, k, v     dt
  *   dalpha, dbeta [B, T, H]    f32
  *   dWk, dWp, dwbeta, dconv    f32, layouts of Wk, Wp, wbeta, conv
+ *   dconv_hist  [B, 4, H, dv]  f32
  * q and k are used as given (callers normalise them if they wish).  With
- * L = 0, Wk, Wp, wbeta, conv (and their gradients) may be NULL. */
+ * L = 0, Wk, Wp, wbeta, conv (and their gradients) may be NULL.
+ *
+ * Continuation.  A sequence split over several calls gives the same result
+ * as one call when each call after the first receives S0 = the previous ST
+ * and conv_hist = the previous call's conv_hist_out (summary §2.1: the state
+ * carries the past; §2.2 Stage 1: the ShortConv reads the last few values).
+ * NULL conv_hist means zeros before the sequence. */
 
 /* Workspace sizes in bytes for a descriptor; *bytes = 0 on error. */
 prism_status prism_forward_workspace(const prism_desc* desc, size_t* bytes);
 prism_status prism_backward_workspace(const prism_desc* desc, size_t* bytes);
 
 /* Forward pass: o = readout of S_1..S_T, ST = S_T (ST may be NULL).
- * S0 may be NULL (zero initial state). */
+ * S0 may be NULL (zero initial state); conv_hist may be NULL (zeros).
+ * conv_hist_out (may be NULL) receives the four values of v before the end
+ * of the sequence (from conv_hist, or zeros, where T < 4); it may be the same
+ * buffer as conv_hist, which is then updated in place after every read. */
 prism_status prism_forward(const prism_desc* desc, const void* q, const void* k, const void* v,
                            const float* alpha, const float* beta, const void* Wk, const void* Wp,
-                           const void* wbeta, const void* conv, const float* S0, void* o,
-                           float* ST, void* workspace, size_t workspace_bytes,
-                           hipStream_t stream);
+                           const void* wbeta, const void* conv, const float* S0,
+                           const void* conv_hist, void* o, float* ST, void* conv_hist_out,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Backward pass: gradients of <dO, o> + <dST, S_T> with respect to every
  * input.  Stateless: recomputes what it needs from the forward inputs.
- * dST may be NULL (zero).  dS0 may be NULL; it is written when given.
- * Every other gradient pointer is required (weight / tap gradients only
- * when L > 0).  Gradients are written, not accumulated. */
+ * dST may be NULL (zero).  dS0 and dconv_hist may be NULL; each is written
+ * when given (dconv_hist is the gradient with respect to conv_hist, zero
+ * when L = 0).  Every other gradient pointer is required (weight / tap
+ * gradients only when L > 0).  Gradients are written, not accumulated. */
 prism_status prism_backward(const prism_desc* desc, const void* q, const void* k, const void* v,
                             const float* alpha, const float* beta, const void* Wk, const void* Wp,
-                            const void* wbeta, const void* conv, const float* S0, const void* dO,
-                            const float* dST, void* dq, void* dk, void* dv, float* dalpha,
-                            float* dbeta, float* dWk, float* dWp, float* dwbeta, float* dconv,
-                            float* dS0, void* workspace, size_t workspace_bytes,
+                            const void* wbeta, const void* conv, const float* S0,
+                            const void* conv_hist, const void* dO, const float* dST, void* dq,
+                            void* dk, void* dv, float* dalpha, float* dbeta, float* dWk,
+                            float* dWp, float* dwbeta, float* dconv, float* dS0,
+                            float* dconv_hist, void* workspace, size_t workspace_bytes,
                             hipStream_t stream);
 
 /* Training pair (saved intermediates).  prism_forward_train computes what
@@ -144,7 +159,8 @@ prism_status prism_backward(const prism_desc* desc, const void* q, const void* k
  *   saved:     device buffer of prism_saved_bytes() bytes, 256-byte aligned,
  *              written by prism_forward_train, read by prism_backward_train;
  *              the caller keeps it unchanged in between (same desc, same
- *              inputs; the backward does not check this).
+ *              inputs, the same conv_hist contents, so not one that
+ *              conv_hist_out overwrote; the backward does not check this).
  *   workspace: as for prism_forward / prism_backward (same sizes).
  * Errors: as for the plain entry points; a NULL, misaligned or too small
  * `saved` buffer gives PRISM_ERR_WORKSPACE / PRISM_ERR_ALIGN before any HIP
@@ -153,17 +169,38 @@ prism_status prism_saved_bytes(const prism_desc* desc, size_t* bytes);
 prism_status prism_forward_train(const prism_desc* desc, const void* q, const void* k,
                                  const void* v, const float* alpha, const float* beta,
                                  const void* Wk, const void* Wp, const void* wbeta,
-                                 const void* conv, const float* S0, void* o, float* ST,
-                                 void* saved, size_t saved_bytes, void* workspace,
-                                 size_t workspace_bytes, hipStream_t stream);
+                                 const void* conv, const float* S0, const void* conv_hist, void* o,
+                                 float* ST, void* conv_hist_out, void* saved, size_t saved_bytes,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
 prism_status prism_backward_train(const prism_desc* desc, const void* q, const void* k,
                                   const void* v, const float* alpha, const float* beta,
                                   const void* Wk, const void* Wp, const void* wbeta,
-                                  const void* conv, const float* S0, const void* saved,
-                                  size_t saved_bytes, const void* dO, const float* dST, void* dq,
-                                  void* dk, void* dv, float* dalpha, float* dbeta, float* dWk,
-                                  float* dWp, float* dwbeta, float* dconv, float* dS0,
-                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
+                                  const void* conv, const float* S0, const void* conv_hist,
+                                  const void* saved, size_t saved_bytes, const void* dO,
+                                  const float* dST, void* dq, void* dk, void* dv, float* dalpha,
+                                  float* dbeta, float* dWk, float* dWp, float* dwbeta,
+                                  float* dconv, float* dS0, float* dconv_hist, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
+/* Recurrent form: the layer token by token (summary §2.1 S_t = S_{t-1} A_t
+ * + B_t with §2.2's B_t, then o_t = S_t q_t), for the desc->T tokens of each
+ * sequence in order.  With T = 1 this is the decode step of serving.
+ *   S:          [B, H, dv, dk] f32, required, read as S_0 and overwritten
+ *               with S_T (in place).
+ *   conv_state: [B, 4, H, dv] dt, read as the ShortConv history before the
+ *               tokens and overwritten with the history after them (in
+ *               place); NULL means zeros, and nothing is written.
+ *   o:          [B, T, H, dv] dt.
+ * The other inputs and desc fields are those of prism_forward; desc->chunk
+ * must be valid but is not used.  A prism_forward over the first tokens
+ * with ST and conv_hist_out, then prism_step over the rest, equals one
+ * prism_forward over all of them up to rounding.  No workspace: the state
+ * stays in registers between tokens (one workgroup per sequence and head),
+ * so S crosses HBM once per call.  Errors: as prism_forward. */
+prism_status prism_step(const prism_desc* desc, const void* q, const void* k, const void* v,
+                        const float* alpha, const float* beta, const void* Wk, const void* Wp,
+                        const void* wbeta, const void* conv, float* S, void* conv_state, void* o,
+                        hipStream_t stream);
 
 /* Human-readable name of a status code (static string). */
 const char* prism_status_string(prism_status status);

@@ -28,6 +28,7 @@ SOURCES = [
     "refine_bwd_identity_past.hip",
     "refine_fwd.hip",
     "state.hip",
+    "step.hip",
     "refine_bwd.hip",
     "prism_api.cpp",
 ]

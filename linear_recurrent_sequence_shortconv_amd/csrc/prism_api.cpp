@@ -260,8 +260,8 @@ size_t fwd_ws_bytes(const prism::Dims& d, prism_dtype dt) {
 template <typename E>
 prism_status run_forward(const prism::Dims& d, const void* q, const void* k, const void* v,
                          const float* alpha, const float* beta, const void* Wk, const void* Wp,
-                         const void* wbeta, const void* conv, const float* S0, void* o, float* ST,
-                         void* ws, void* keep, hipStream_t s) {
+                         const void* wbeta, const void* conv, const float* S0, const void* hist,
+                         void* o, float* ST, void* hist_out, void* ws, void* keep, hipStream_t s) {
   Carve cv;
   cv.base = static_cast<char*>(ws);
   FwdWs<E> w = carve_fwd<E>(d, cv);
@@ -281,27 +281,32 @@ prism_status run_forward(const prism::Dims& d, const void* q, const void* k, con
   const E* q_ = static_cast<const E*>(q);
   const E* k_ = static_cast<const E*>(k);
   const E* v_ = static_cast<const E*>(v);
+  const E* hist_ = static_cast<const E*>(hist);
   if (d.L > 0)
     HIP_TRY("refine_fwd", s,
-            prism::launch_refine_fwd<E>(d, v_, static_cast<const E*>(conv), static_cast<const E*>(Wk),
-                                        static_cast<const E*>(Wp), static_cast<const E*>(wbeta),
-                                        w.Kl, w.Wl, s));
+            prism::launch_refine_fwd<E>(d, v_, hist_, static_cast<const E*>(conv),
+                                        static_cast<const E*>(Wk), static_cast<const E*>(Wp),
+                                        static_cast<const E*>(wbeta), w.Kl, w.Wl, s));
   HIP_TRY("chunk_fwd", s,
           prism::launch_chunk_fwd<E>(d, q_, k_, v_, alpha, beta, w.Kl, w.Wl, nullptr, w.Mt, w.HT,
                                      w.Qt, w.Oloc, w.gC, nullptr, w.UT, w.WkT, s));
   HIP_TRY("state_fwd", s,
           prism::launch_state_pass<E>(d, S0, w.Mt, w.HT, w.gC, w.Sc, ST, false, false, s));
   HIP_TRY("out_fwd", s, prism::launch_out_fwd<E>(d, w.Sc, w.Qt, w.Oloc, static_cast<E*>(o), s));
+  // after every read of hist, which hist_out may overwrite
+  if (hist_out)
+    HIP_TRY("conv_state", s, prism::launch_conv_state<E>(d, v_, hist_, static_cast<E*>(hist_out), s));
   return PRISM_OK;
 }
 
 template <typename E>
 prism_status run_backward(const prism::Dims& d, const void* q, const void* k, const void* v,
                           const float* alpha, const float* beta, const void* Wk, const void* Wp,
-                          const void* wbeta, const void* conv, const float* S0, const void* dO,
-                          const float* dST, void* dq, void* dk, void* dv, float* dalpha,
-                          float* dbeta, float* dWk, float* dWp, float* dwbeta, float* dconv,
-                          float* dS0, void* ws, const void* kept, hipStream_t s) {
+                          const void* wbeta, const void* conv, const float* S0, const void* hist,
+                          const void* dO, const float* dST, void* dq, void* dk, void* dv,
+                          float* dalpha, float* dbeta, float* dWk, float* dWp, float* dwbeta,
+                          float* dconv, float* dS0, float* dhist, void* ws, const void* kept,
+                          hipStream_t s) {
   Carve cv;
   cv.base = static_cast<char*>(ws);
   BwdWs<E> w = carve_bwd<E>(d, cv);
@@ -309,6 +314,7 @@ prism_status run_backward(const prism::Dims& d, const void* q, const void* k, co
   const E* k_ = static_cast<const E*>(k);
   const E* v_ = static_cast<const E*>(v);
   const E* dO_ = static_cast<const E*>(dO);
+  const E* hist_ = static_cast<const E*>(hist);
   if (kept) {
     // the forward's intermediates: only E = dO^T Qt per chunk is new
     Carve ck;
@@ -325,7 +331,7 @@ prism_status run_backward(const prism::Dims& d, const void* q, const void* k, co
   } else {
     if (d.L > 0)
       HIP_TRY("refine_fwd_recompute", s,
-              prism::launch_refine_fwd<E>(d, v_, static_cast<const E*>(conv),
+              prism::launch_refine_fwd<E>(d, v_, hist_, static_cast<const E*>(conv),
                                           static_cast<const E*>(Wk), static_cast<const E*>(Wp),
                                           static_cast<const E*>(wbeta), w.Kl, w.Wl, s));
     HIP_TRY("chunk_fwd_bwdmode", s,
@@ -354,11 +360,15 @@ prism_status run_backward(const prism::Dims& d, const void* q, const void* k, co
     r.dP = w.dP; r.dwbp = w.dwbp; r.dcp = w.dcp; r.part = w.part;
     r.dv = static_cast<E*>(dv); r.dWk_o = dWk; r.dWp_o = dWp; r.dwbeta_o = dwbeta;
     r.dconv_o = dconv;
+    r.hist = hist_;
+    r.dhist = dhist;
     HIP_TRY("transpose_weights", s, prism::launch_refine_bwd<E>(d, r, 0, s));
     HIP_TRY("refine_bwd", s, prism::launch_refine_bwd<E>(d, r, 1, s));
     HIP_TRY("wgrad_gemm", s, prism::launch_refine_bwd<E>(d, r, 2, s));
     HIP_TRY("wgrad_reduce", s, prism::launch_refine_bwd<E>(d, r, 3, s));
     HIP_TRY("bias_reduce", s, prism::launch_refine_bwd<E>(d, r, 4, s));
+  } else if (dhist) {   // without refinement the history does not reach the outputs
+    HIP_TRY("zero_hist_grad", s, prism::launch_zero(dhist, (long)d.B * 4 * d.H * d.D, s));
   }
   return PRISM_OK;
 }
@@ -428,7 +438,8 @@ prism_status check_buffer(const void* p, size_t have, size_t need, const char* w
 
 prism_status forward_entry(const prism_desc* desc, const void* q, const void* k, const void* v,
                            const float* alpha, const float* beta, const void* Wk, const void* Wp,
-                           const void* wbeta, const void* conv, const float* S0, void* o, float* ST,
+                           const void* wbeta, const void* conv, const float* S0,
+                           const void* conv_hist, void* o, float* ST, void* conv_hist_out,
                            void* saved, size_t saved_bytes, bool train, void* workspace,
                            size_t workspace_bytes, hipStream_t stream) {
   try {
@@ -447,8 +458,10 @@ prism_status forward_entry(const prism_desc* desc, const void* q, const void* k,
     CHECK_PTR(wbeta, refine);
     CHECK_PTR(conv, refine);
     CHECK_PTR(S0, false);
+    CHECK_PTR(conv_hist, false);
     CHECK_PTR(o, true);
     CHECK_PTR(ST, false);
+    CHECK_PTR(conv_hist_out, false);
     if (train) {
       st = check_buffer(saved, saved_bytes, kept_bytes(d, desc->dtype), "saved");
       if (st != PRISM_OK) return st;
@@ -457,10 +470,10 @@ prism_status forward_entry(const prism_desc* desc, const void* q, const void* k,
     if (st != PRISM_OK) return st;
     void* keep = train ? saved : nullptr;
     if (desc->dtype == PRISM_BF16)
-      return run_forward<prism::bf16>(d, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, o, ST,
-                                      workspace, keep, stream);
-    return run_forward<float>(d, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, o, ST, workspace,
-                              keep, stream);
+      return run_forward<prism::bf16>(d, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, conv_hist,
+                                      o, ST, conv_hist_out, workspace, keep, stream);
+    return run_forward<float>(d, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, conv_hist, o, ST,
+                              conv_hist_out, workspace, keep, stream);
   } catch (...) {
     return fail(PRISM_ERR_HIP, "unexpected host exception");
   }
@@ -469,11 +482,11 @@ prism_status forward_entry(const prism_desc* desc, const void* q, const void* k,
 prism_status backward_entry(const prism_desc* desc, const void* q, const void* k, const void* v,
                             const float* alpha, const float* beta, const void* Wk, const void* Wp,
                             const void* wbeta, const void* conv, const float* S0,
-                            const void* saved, size_t saved_bytes, bool train, const void* dO,
-                            const float* dST, void* dq, void* dk, void* dv, float* dalpha,
-                            float* dbeta, float* dWk, float* dWp, float* dwbeta, float* dconv,
-                            float* dS0, void* workspace, size_t workspace_bytes,
-                            hipStream_t stream) {
+                            const void* conv_hist, const void* saved, size_t saved_bytes,
+                            bool train, const void* dO, const float* dST, void* dq, void* dk,
+                            void* dv, float* dalpha, float* dbeta, float* dWk, float* dWp,
+                            float* dwbeta, float* dconv, float* dS0, float* dconv_hist,
+                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
   try {
     g_err.clear();
     prism::Dims d;
@@ -490,6 +503,7 @@ prism_status backward_entry(const prism_desc* desc, const void* q, const void* k
     CHECK_PTR(wbeta, refine);
     CHECK_PTR(conv, refine);
     CHECK_PTR(S0, false);
+    CHECK_PTR(conv_hist, false);
     CHECK_PTR(dO, true);
     CHECK_PTR(dST, false);
     CHECK_PTR(dq, true);
@@ -502,6 +516,7 @@ prism_status backward_entry(const prism_desc* desc, const void* q, const void* k
     CHECK_PTR(dwbeta, refine);
     CHECK_PTR(dconv, refine);
     CHECK_PTR(dS0, false);
+    CHECK_PTR(dconv_hist, false);
     if (train) {
       st = check_buffer(saved, saved_bytes, kept_bytes(d, desc->dtype), "saved");
       if (st != PRISM_OK) return st;
@@ -510,12 +525,12 @@ prism_status backward_entry(const prism_desc* desc, const void* q, const void* k
     if (st != PRISM_OK) return st;
     const void* kept = train ? saved : nullptr;
     if (desc->dtype == PRISM_BF16)
-      return run_backward<prism::bf16>(d, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, dO, dST,
-                                       dq, dk, dv, dalpha, dbeta, dWk, dWp, dwbeta, dconv, dS0,
-                                       workspace, kept, stream);
-    return run_backward<float>(d, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, dO, dST, dq, dk,
-                               dv, dalpha, dbeta, dWk, dWp, dwbeta, dconv, dS0, workspace, kept,
-                               stream);
+      return run_backward<prism::bf16>(d, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, conv_hist,
+                                       dO, dST, dq, dk, dv, dalpha, dbeta, dWk, dWp, dwbeta,
+                                       dconv, dS0, dconv_hist, workspace, kept, stream);
+    return run_backward<float>(d, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, conv_hist, dO,
+                               dST, dq, dk, dv, dalpha, dbeta, dWk, dWp, dwbeta, dconv, dS0,
+                               dconv_hist, workspace, kept, stream);
   } catch (...) {
     return fail(PRISM_ERR_HIP, "unexpected host exception");
   }
@@ -527,46 +542,93 @@ extern "C" {
 
 prism_status prism_forward(const prism_desc* desc, const void* q, const void* k, const void* v,
                            const float* alpha, const float* beta, const void* Wk, const void* Wp,
-                           const void* wbeta, const void* conv, const float* S0, void* o,
-                           float* ST, void* workspace, size_t workspace_bytes,
-                           hipStream_t stream) {
-  return forward_entry(desc, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, o, ST, nullptr, 0,
-                       false, workspace, workspace_bytes, stream);
+                           const void* wbeta, const void* conv, const float* S0,
+                           const void* conv_hist, void* o, float* ST, void* conv_hist_out,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return forward_entry(desc, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, conv_hist, o, ST,
+                       conv_hist_out, nullptr, 0, false, workspace, workspace_bytes, stream);
 }
 
 prism_status prism_forward_train(const prism_desc* desc, const void* q, const void* k,
                                  const void* v, const float* alpha, const float* beta,
                                  const void* Wk, const void* Wp, const void* wbeta,
-                                 const void* conv, const float* S0, void* o, float* ST,
-                                 void* saved, size_t saved_bytes, void* workspace,
-                                 size_t workspace_bytes, hipStream_t stream) {
-  return forward_entry(desc, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, o, ST, saved,
-                       saved_bytes, true, workspace, workspace_bytes, stream);
+                                 const void* conv, const float* S0, const void* conv_hist, void* o,
+                                 float* ST, void* conv_hist_out, void* saved, size_t saved_bytes,
+                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return forward_entry(desc, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, conv_hist, o, ST,
+                       conv_hist_out, saved, saved_bytes, true, workspace, workspace_bytes, stream);
 }
 
 prism_status prism_backward(const prism_desc* desc, const void* q, const void* k, const void* v,
                             const float* alpha, const float* beta, const void* Wk, const void* Wp,
-                            const void* wbeta, const void* conv, const float* S0, const void* dO,
-                            const float* dST, void* dq, void* dk, void* dv, float* dalpha,
-                            float* dbeta, float* dWk, float* dWp, float* dwbeta, float* dconv,
-                            float* dS0, void* workspace, size_t workspace_bytes,
+                            const void* wbeta, const void* conv, const float* S0,
+                            const void* conv_hist, const void* dO, const float* dST, void* dq,
+                            void* dk, void* dv, float* dalpha, float* dbeta, float* dWk,
+                            float* dWp, float* dwbeta, float* dconv, float* dS0,
+                            float* dconv_hist, void* workspace, size_t workspace_bytes,
                             hipStream_t stream) {
-  return backward_entry(desc, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, nullptr, 0, false,
-                        dO, dST, dq, dk, dv, dalpha, dbeta, dWk, dWp, dwbeta, dconv, dS0,
-                        workspace, workspace_bytes, stream);
+  return backward_entry(desc, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, conv_hist, nullptr,
+                        0, false, dO, dST, dq, dk, dv, dalpha, dbeta, dWk, dWp, dwbeta, dconv,
+                        dS0, dconv_hist, workspace, workspace_bytes, stream);
 }
 
 prism_status prism_backward_train(const prism_desc* desc, const void* q, const void* k,
                                   const void* v, const float* alpha, const float* beta,
                                   const void* Wk, const void* Wp, const void* wbeta,
-                                  const void* conv, const float* S0, const void* saved,
-                                  size_t saved_bytes, const void* dO, const float* dST, void* dq,
-                                  void* dk, void* dv, float* dalpha, float* dbeta, float* dWk,
-                                  float* dWp, float* dwbeta, float* dconv, float* dS0,
-                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return backward_entry(desc, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, saved, saved_bytes,
-                        true, dO, dST, dq, dk, dv, dalpha, dbeta, dWk, dWp, dwbeta, dconv, dS0,
-                        workspace, workspace_bytes, stream);
+                                  const void* conv, const float* S0, const void* conv_hist,
+                                  const void* saved, size_t saved_bytes, const void* dO,
+                                  const float* dST, void* dq, void* dk, void* dv, float* dalpha,
+                                  float* dbeta, float* dWk, float* dWp, float* dwbeta,
+                                  float* dconv, float* dS0, float* dconv_hist, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  return backward_entry(desc, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, conv_hist, saved,
+                        saved_bytes, true, dO, dST, dq, dk, dv, dalpha, dbeta, dWk, dWp, dwbeta,
+                        dconv, dS0, dconv_hist, workspace, workspace_bytes, stream);
+}
+
+prism_status prism_step(const prism_desc* desc, const void* q, const void* k, const void* v,
+                        const float* alpha, const float* beta, const void* Wk, const void* Wp,
+                        const void* wbeta, const void* conv, float* S, void* conv_state, void* o,
+                        hipStream_t stream) {
+  try {
+    g_err.clear();
+    prism::Dims d;
+    prism_status st = check_desc(desc, &d);
+    if (st != PRISM_OK) return st;
+    const bool refine = d.L > 0;
+    CHECK_PTR(q, true);
+    CHECK_PTR(k, true);
+    CHECK_PTR(v, true);
+    CHECK_PTR(alpha, true);
+    CHECK_PTR(beta, true);
+    CHECK_PTR(Wk, refine);
+    CHECK_PTR(Wp, refine);
+    CHECK_PTR(wbeta, refine);
+    CHECK_PTR(conv, refine);
+    CHECK_PTR(S, true);
+    CHECK_PTR(conv_state, false);
+    CHECK_PTR(o, true);
+    if (desc->dtype == PRISM_BF16) {
+      typedef prism::bf16 E;
+      HIP_TRY("step", stream,
+              prism::launch_step<E>(d, static_cast<const E*>(q), static_cast<const E*>(k),
+                                    static_cast<const E*>(v), alpha, beta,
+                                    static_cast<const E*>(Wk), static_cast<const E*>(Wp),
+                                    static_cast<const E*>(wbeta), static_cast<const E*>(conv), S,
+                                    static_cast<E*>(conv_state), static_cast<E*>(o), stream));
+    } else {
+      typedef float E;
+      HIP_TRY("step", stream,
+              prism::launch_step<E>(d, static_cast<const E*>(q), static_cast<const E*>(k),
+                                    static_cast<const E*>(v), alpha, beta,
+                                    static_cast<const E*>(Wk), static_cast<const E*>(Wp),
+                                    static_cast<const E*>(wbeta), static_cast<const E*>(conv), S,
+                                    static_cast<E*>(conv_state), static_cast<E*>(o), stream));
+    }
+    return PRISM_OK;
+  } catch (...) {
+    return fail(PRISM_ERR_HIP, "unexpected host exception");
+  }
 }
 
 void prism_timing_begin(void) {

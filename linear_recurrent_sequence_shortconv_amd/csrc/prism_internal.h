@@ -24,10 +24,11 @@ struct Dims {
 // Element type E is __bf16 or float.
 
 // Stage 1 + Stage 2: ShortConv anchor and the L refinement steps.
-// Writes Kl, Wl [B, H, L, Tp, D] (rows t >= T are zero).
+// Writes Kl, Wl [B, H, L, Tp, D] (rows t >= T are zero).  hist [B, 4, H, D]
+// holds the four v values before the sequence (nullptr: zeros).
 template <typename E>
-hipError_t launch_refine_fwd(const Dims& d, const E* v, const E* conv, const E* Wk, const E* Wp,
-                             const E* wbeta, E* Kl, E* Wl, hipStream_t s);
+hipError_t launch_refine_fwd(const Dims& d, const E* v, const E* hist, const E* conv, const E* Wk,
+                             const E* Wp, const E* wbeta, E* Kl, E* Wl, hipStream_t s);
 
 // Chunk-local affine map of every chunk (parallel over B * H * NC).
 // Forward mode writes Mt, HT, Qt, Oloc, gC, and UT, WkT when they are not
@@ -73,6 +74,8 @@ hipError_t launch_chunk_bwd(const Dims& d, const ChunkBwdArgs<E>& a, int stage, 
 template <typename E>
 struct RefineBwdArgs {
   const E *v, *conv, *Wk, *Wp, *wbeta;
+  const E* hist;                // v before the sequence [B, 4, H, D] (nullptr: zeros)
+  float* dhist;                 // its gradient (nullptr: not wanted)
   E *WkT, *WpT;                 // transposed weights (workspace)
   const float *dKl, *dWl;
   const float* dvdir;           // direct v-gradient of the recurrence ([bh][Tp][D])
@@ -89,6 +92,22 @@ template <typename E>
 hipError_t launch_refine_bwd(const Dims& d, const RefineBwdArgs<E>& a, int stage, hipStream_t s);
 int refine_bwd_splits(const Dims& d);   // split count of the weight-gradient GEMM
 int refine_bwd_tiles(const Dims& d);    // token tiles per sequence (rows of the per-tile partials)
+
+// The ShortConv history after the sequence, out[b][r] = v_{T-4+r} (from
+// hist, or zero, where T-4+r < 0).  out may be hist itself.
+template <typename E>
+hipError_t launch_conv_state(const Dims& d, const E* v, const E* hist, E* out, hipStream_t s);
+
+// Zero n floats (a kernel, so that the call may be captured in a graph).
+hipError_t launch_zero(float* p, long n, hipStream_t s);
+
+// Token-by-token recurrence for T tokens per sequence: S [B, H, D, D] fp32
+// and the ShortConv history cstate [B, 4, H, D] (nullptr: zeros, not kept)
+// are read, carried and written back in place; o [B, T, H, D].
+template <typename E>
+hipError_t launch_step(const Dims& d, const E* q, const E* k, const E* v, const float* alpha,
+                       const float* beta, const E* Wk, const E* Wp, const E* wbeta, const E* conv,
+                       float* S, E* cstate, E* o, hipStream_t s);
 
 // O = O_loc + Qt S_c^T, written to o [B, T, H, D].
 template <typename E>

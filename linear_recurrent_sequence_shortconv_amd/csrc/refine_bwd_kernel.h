@@ -59,11 +59,13 @@ __device__ inline typename Mfma<E>::frag frag_from_f32(const float* X, int ld, i
 
 template <typename E, int D, int LMAX, int ACT, int OFF>
 __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
-    const E* __restrict__ v, const E* __restrict__ conv, const E* __restrict__ Wp,
+    const E* __restrict__ v, const E* __restrict__ hist, const E* __restrict__ conv,
+    const E* __restrict__ Wp,
     const E* __restrict__ WkT, const E* __restrict__ WpT, const E* __restrict__ wbeta,
     const float* __restrict__ dKl, const float* __restrict__ dWl, const float* __restrict__ dvdir,
     E* __restrict__ uo, E* __restrict__ dPo, E* __restrict__ dv, float* __restrict__ dwbp,
-    float* __restrict__ dcp, int B, int T, int H, int L, int Tp, int ntiles) {
+    float* __restrict__ dcp, float* __restrict__ dhist, int B, int T, int H, int L, int Tp,
+    int ntiles) {
   constexpr int LD = ldpad<E>(D);
   constexpr int LW = D + 4;               // fp32 rows: staggers rows 4 apart across banks
   constexpr int NFT = D / 16;
@@ -112,6 +114,7 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
     const int t = t0 - HL + r;
     uint4 x = {0u, 0u, 0u, 0u};
     if (t >= 0 && t < T) x = ld16(vseq + t * tok_stride + c);
+    else if (t < 0 && hist) x = ld16(hist + (((long)b * 4 + 4 + t) * H + h) * D + c);
     st16(vbuf + r * D + c, x);
   }
   // dW, dK rows of the first reverse step, in flight during the set-up
@@ -451,6 +454,20 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
       dcp[((long)tile_id * D + tid) * 4 + j] = x;
     }
   }
+  // gradient of the history rows v_{-4} .. v_{-1}: the adjoint at s < 0,
+  // dh_s = sum_j conv[:, j] du_{s+o+j} over 0 <= s+o+j (first tile only)
+  if (tile == 0 && dhist) {
+    for (int e = tid; e < 4 * D; e += RB_NT) {
+      const int r = e / D, f = e % D;
+      float x = 0.f;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = r - 4 + OFF + j;
+        if (t >= 0 && t < nrow) x += ctp[f * 4 + j] * dub[t * LW + f];
+      }
+      dhist[(((long)b * 4 + r) * H + h) * D + f] = x;
+    }
+  }
 }
 
 // Stage 1 of the refinement backward for one (activation, tap offset)
@@ -459,9 +476,9 @@ template <typename E, int ACT, int OFF>
 hipError_t launch_refine_bwd_main(const Dims& d, const RefineBwdArgs<E>& a, hipStream_t s) {
   const int ntiles = refine_bwd_tiles(d);
   auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3(ntiles * d.B * d.H), dim3(RB_NT), 0, s, a.v, a.conv, a.Wp, a.WkT,
-                       a.WpT, a.wbeta, a.dKl, a.dWl, a.dvdir, a.u, a.dP, a.dv, a.dwbp, a.dcp, d.B,
-                       d.T, d.H, d.L, d.Tp, ntiles);
+    hipLaunchKernelGGL(kern, dim3(ntiles * d.B * d.H), dim3(RB_NT), 0, s, a.v, a.hist, a.conv, a.Wp,
+                       a.WkT, a.WpT, a.wbeta, a.dKl, a.dWl, a.dvdir, a.u, a.dP, a.dv, a.dwbp, a.dcp,
+                       a.dhist, d.B, d.T, d.H, d.L, d.Tp, ntiles);
     return hipGetLastError();
   };
   auto by_l = [&](auto dd) {

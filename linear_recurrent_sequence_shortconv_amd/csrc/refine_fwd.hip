@@ -28,9 +28,9 @@ constexpr int RF_NW = 4;
 
 template <typename E, int D, int ACT, int OFF>
 __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
-    const E* __restrict__ v, const E* __restrict__ conv, const E* __restrict__ Wk,
-    const E* __restrict__ Wp, const E* __restrict__ wbeta, E* __restrict__ Kl,
-    E* __restrict__ Wl, int B, int T, int H, int L, int Tp) {
+    const E* __restrict__ v, const E* __restrict__ hist, const E* __restrict__ conv,
+    const E* __restrict__ Wk, const E* __restrict__ Wp, const E* __restrict__ wbeta,
+    E* __restrict__ Kl, E* __restrict__ Wl, int B, int T, int H, int L, int Tp) {
   constexpr int LD = ldpad<E>(D);
   constexpr int NFT = D / 16;                          // feature tiles
   constexpr int FPW = (NFT + RF_NW - 1) / RF_NW;       // feature tiles per wave
@@ -69,12 +69,14 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
   // ---- w_beta rows of this head (L x D) ----
   for (int e = tid; e < L * (D / VN); e += RF_NT)
     st16(wbs + e * VN, ld16(wbeta + (long)h * L * D + e * VN));
-  // ---- v rows t0-HL .. t0+63 (zeros outside [0, T)) ----
+  // ---- v rows t0-HL .. t0+63 (zeros past T; before 0 the history rows
+  //      [B, 4, H, D], or zeros without a history) ----
   for (int e = tid; e < (RF_TT + HL) * (D / VN); e += RF_NT) {
     const int r = e / (D / VN), c = (e % (D / VN)) * VN;
     const int t = t0 - HL + r;
     uint4 x = {0u, 0u, 0u, 0u};
     if (t >= 0 && t < T) x = ld16(vseq + t * tok_stride + c);
+    else if (t < 0 && hist) x = ld16(hist + (((long)b * 4 + 4 + t) * H + h) * D + c);
     st16(vbuf + r * D + c, x);
   }
   typedef typename Mfma<E>::frag Frag;
@@ -228,13 +230,14 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
 }
 
 template <typename E, int D>
-static hipError_t refine_launch_d(const Dims& d, const E* v, const E* conv, const E* Wk,
-                                  const E* Wp, const E* wbeta, E* Kl, E* Wl, hipStream_t s) {
+static hipError_t refine_launch_d(const Dims& d, const E* v, const E* hist, const E* conv,
+                                  const E* Wk, const E* Wp, const E* wbeta, E* Kl, E* Wl,
+                                  hipStream_t s) {
   const int ntiles = (d.Tp + RF_TT - 1) / RF_TT;
   const int nblk = ntiles * d.B * d.H;
   auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3(nblk), dim3(RF_NT), 0, s, v, conv, Wk, Wp, wbeta, Kl, Wl, d.B, d.T,
-                       d.H, d.L, d.Tp);
+    hipLaunchKernelGGL(kern, dim3(nblk), dim3(RF_NT), 0, s, v, hist, conv, Wk, Wp, wbeta, Kl, Wl,
+                       d.B, d.T, d.H, d.L, d.Tp);
   };
   if (d.act == ACT_IDENTITY)
     d.off ? go(refine_fwd_kernel<E, D, ACT_IDENTITY, 1>) : go(refine_fwd_kernel<E, D, ACT_IDENTITY, 0>);
@@ -244,24 +247,27 @@ static hipError_t refine_launch_d(const Dims& d, const E* v, const E* conv, cons
 }
 
 template <typename E>
-hipError_t launch_refine_fwd(const Dims& d, const E* v, const E* conv, const E* Wk, const E* Wp,
-                             const E* wbeta, E* Kl, E* Wl, hipStream_t s) {
+hipError_t launch_refine_fwd(const Dims& d, const E* v, const E* hist, const E* conv, const E* Wk,
+                             const E* Wp, const E* wbeta, E* Kl, E* Wl, hipStream_t s) {
   if (d.L == 0) return hipSuccess;
   switch (d.D) {
-    case 16: return refine_launch_d<E, 16>(d, v, conv, Wk, Wp, wbeta, Kl, Wl, s);
-    case 32: return refine_launch_d<E, 32>(d, v, conv, Wk, Wp, wbeta, Kl, Wl, s);
-    case 64: return refine_launch_d<E, 64>(d, v, conv, Wk, Wp, wbeta, Kl, Wl, s);
+    case 16: return refine_launch_d<E, 16>(d, v, hist, conv, Wk, Wp, wbeta, Kl, Wl, s);
+    case 32: return refine_launch_d<E, 32>(d, v, hist, conv, Wk, Wp, wbeta, Kl, Wl, s);
+    case 64: return refine_launch_d<E, 64>(d, v, hist, conv, Wk, Wp, wbeta, Kl, Wl, s);
     case 128:
-      if constexpr (sizeof(E) == 2) return refine_launch_d<E, 128>(d, v, conv, Wk, Wp, wbeta, Kl, Wl, s);
+      if constexpr (sizeof(E) == 2)
+        return refine_launch_d<E, 128>(d, v, hist, conv, Wk, Wp, wbeta, Kl, Wl, s);
       break;
   }
   return hipErrorInvalidValue;
 }
 
 template hipError_t launch_refine_fwd<bf16>(const Dims&, const bf16*, const bf16*, const bf16*,
-                                            const bf16*, const bf16*, bf16*, bf16*, hipStream_t);
+                                            const bf16*, const bf16*, const bf16*, bf16*, bf16*,
+                                            hipStream_t);
 template hipError_t launch_refine_fwd<float>(const Dims&, const float*, const float*, const float*,
-                                             const float*, const float*, float*, float*, hipStream_t);
+                                             const float*, const float*, const float*, float*,
+                                             float*, hipStream_t);
 
 #undef FT_OK
 }  // namespace prism

@@ -20,7 +20,8 @@ STATUS = {0: "PRISM_OK", 1: "PRISM_ERR_NULL", 2: "PRISM_ERR_SHAPE", 3: "PRISM_ER
 
 EXPORTS = ("prism_forward_workspace", "prism_backward_workspace", "prism_forward",
            "prism_backward", "prism_saved_bytes", "prism_forward_train", "prism_backward_train",
-           "prism_status_string", "prism_last_error", "prism_timing_begin", "prism_timing_end")
+           "prism_step", "prism_status_string", "prism_last_error", "prism_timing_begin",
+           "prism_timing_end")
 
 
 class Desc(ctypes.Structure):
@@ -45,16 +46,19 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         L.prism_forward_workspace.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(ctypes.c_size_t)]
         L.prism_backward_workspace.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(ctypes.c_size_t)]
-        L.prism_forward.argtypes = [ctypes.POINTER(Desc)] + [_P] * 12 + [_P, ctypes.c_size_t, _P]
-        L.prism_backward.argtypes = [ctypes.POINTER(Desc)] + [_P] * 22 + [_P, ctypes.c_size_t, _P]
+        # inputs q..conv, S0, conv_hist (11); forward outputs o, ST, conv_hist_out (3);
+        # backward: dO, dST, then 11 gradients (dq..dconv, dS0, dconv_hist)
+        L.prism_forward.argtypes = [ctypes.POINTER(Desc)] + [_P] * 14 + [_P, ctypes.c_size_t, _P]
+        L.prism_backward.argtypes = [ctypes.POINTER(Desc)] + [_P] * 24 + [_P, ctypes.c_size_t, _P]
         L.prism_saved_bytes.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(ctypes.c_size_t)]
-        L.prism_forward_train.argtypes = ([ctypes.POINTER(Desc)] + [_P] * 12
+        L.prism_forward_train.argtypes = ([ctypes.POINTER(Desc)] + [_P] * 14
                                           + [_P, ctypes.c_size_t, _P, ctypes.c_size_t, _P])
-        L.prism_backward_train.argtypes = ([ctypes.POINTER(Desc)] + [_P] * 10 + [_P, ctypes.c_size_t]
-                                           + [_P] * 12 + [_P, ctypes.c_size_t, _P])
+        L.prism_backward_train.argtypes = ([ctypes.POINTER(Desc)] + [_P] * 11 + [_P, ctypes.c_size_t]
+                                           + [_P] * 13 + [_P, ctypes.c_size_t, _P])
+        L.prism_step.argtypes = [ctypes.POINTER(Desc)] + [_P] * 12 + [_P]
         for f in ("prism_forward_workspace", "prism_backward_workspace", "prism_forward",
                   "prism_backward", "prism_saved_bytes", "prism_forward_train",
-                  "prism_backward_train"):
+                  "prism_backward_train", "prism_step"):
             getattr(L, f).restype = ctypes.c_int
         L.prism_status_string.argtypes = [ctypes.c_int]
         L.prism_status_string.restype = ctypes.c_char_p
@@ -150,8 +154,16 @@ def _validate_inputs(q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0):
         _req(S0, "S0", torch.float32, dev)
 
 
+def _req_hist(h, name, q, v):
+    B, _, H, _ = v.shape
+    _req(h, name, q.dtype, q.device)
+    if tuple(h.shape) != (B, 4, H, v.shape[-1]):
+        raise ValueError(f"{name}: expected shape {(B, 4, H, v.shape[-1])}, got {tuple(h.shape)}")
+
+
 def forward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None, S0=None, chunk=64,
-            workspace=None, saved=None, activation="gelu", conv_offset=0):
+            workspace=None, saved=None, activation="gelu", conv_offset=0, conv_hist=None,
+            conv_hist_out=None):
     """PRISM layer forward.  Returns (o, S_T).
 
     q, k [B,T,H,dk], v [B,T,H,dv] (bf16 or fp32); alpha, beta [B,T,H] fp32;
@@ -159,12 +171,18 @@ def forward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None, S0=No
     dtype (all None for L = 0); S0 [B,H,dv,dk] fp32 or None.
     activation: "gelu" (delta = GELU(p r)) or "identity" (delta = p r);
     conv_offset: 0 (tap j on v_{t-j}) or 1 (tap j on v_{t-1-j}).
+    conv_hist [B,4,H,dv] (v's dtype): the four values of v before the
+    sequence (None: zeros); conv_hist_out (same shape, may be conv_hist)
+    receives them for the next call.
     With `saved` (a buffer from saved_buffer()) this is the training forward
     (prism_forward_train): the buffer then holds what backward(saved=...)
     needs.
     """
     _validate_inputs(q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0)
     desc = _desc_from(q, v, Wk, chunk, activation, conv_offset)
+    for name, h in (("conv_hist", conv_hist), ("conv_hist_out", conv_hist_out)):
+        if h is not None:
+            _req_hist(h, name, q, v)
     B, T, H, dk = q.shape
     dv = v.shape[-1]
     o = torch.empty_like(v)
@@ -178,12 +196,14 @@ def forward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None, S0=No
     if saved is None:
         _check(lib().prism_forward(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
                                    _ptr(beta), _ptr(Wk), _ptr(Wp), _ptr(wbeta), _ptr(conv),
-                                   _ptr(S0), _ptr(o), _ptr(ST), _ptr(ws),
-                                   ctypes.c_size_t(ws.numel()), ctypes.c_void_p(stream)))
+                                   _ptr(S0), _ptr(conv_hist), _ptr(o), _ptr(ST),
+                                   _ptr(conv_hist_out), _ptr(ws), ctypes.c_size_t(ws.numel()),
+                                   ctypes.c_void_p(stream)))
     else:
         _check(lib().prism_forward_train(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
                                          _ptr(beta), _ptr(Wk), _ptr(Wp), _ptr(wbeta), _ptr(conv),
-                                         _ptr(S0), _ptr(o), _ptr(ST), _ptr(saved),
+                                         _ptr(S0), _ptr(conv_hist), _ptr(o), _ptr(ST),
+                                         _ptr(conv_hist_out), _ptr(saved),
                                          ctypes.c_size_t(saved.numel()), _ptr(ws),
                                          ctypes.c_size_t(ws.numel()), ctypes.c_void_p(stream)))
     return o, ST
@@ -198,19 +218,22 @@ def saved_buffer(q, v, Wk=None, chunk=64):
 
 def backward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None, S0=None, dO=None,
              dST=None, chunk=64, need_dS0=False, workspace=None, saved=None, activation="gelu",
-             conv_offset=0):
+             conv_offset=0, conv_hist=None, need_dconv_hist=False):
     """Gradients of <dO, o> + <dST, S_T> with respect to every input.
 
     Returns a dict: dq, dk, dv (input dtype), dalpha, dbeta (fp32), and for
     L > 0 dWk, dWp, dwbeta, dconv (fp32); dS0 (fp32) when need_dS0.
     With `saved` (filled by forward(..., saved=...) on the same inputs) this is
-    prism_backward_train, which skips the forward recompute.  activation and
-    conv_offset as in forward() (and equal to the forward's with `saved`).
+    prism_backward_train, which skips the forward recompute.  activation,
+    conv_offset and conv_hist as in forward() (and equal to the forward's
+    with `saved`); need_dconv_hist adds dconv_hist [B,4,H,dv] fp32.
     """
     _validate_inputs(q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0)
     if dO is None:
         raise ValueError("dO is required")
     _req(dO, "dO", q.dtype, q.device)
+    if conv_hist is not None:
+        _req_hist(conv_hist, "conv_hist", q, v)
     if dST is not None:
         _req(dST, "dST", torch.float32, q.device)
     desc = _desc_from(q, v, Wk, chunk, activation, conv_offset)
@@ -226,6 +249,8 @@ def backward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None, S0=N
         g["dconv"] = torch.empty(conv.shape, dtype=torch.float32, device=dev)
     if need_dS0:
         g["dS0"] = torch.empty((B, H, dv_, dk), dtype=torch.float32, device=dev)
+    if need_dconv_hist:
+        g["dconv_hist"] = torch.empty((B, 4, H, dv_), dtype=torch.float32, device=dev)
     need = backward_workspace_bytes(desc)
     if workspace is None:
         _, ws = _workspace(need, dev)
@@ -234,9 +259,9 @@ def backward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None, S0=N
     stream = torch.cuda.current_stream(dev).cuda_stream
     grads = (_ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]), _ptr(g["dalpha"]), _ptr(g["dbeta"]),
              _ptr(g.get("dWk")), _ptr(g.get("dWp")), _ptr(g.get("dwbeta")), _ptr(g.get("dconv")),
-             _ptr(g.get("dS0")))
+             _ptr(g.get("dS0")), _ptr(g.get("dconv_hist")))
     inputs = (_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(Wk), _ptr(Wp),
-              _ptr(wbeta), _ptr(conv), _ptr(S0))
+              _ptr(wbeta), _ptr(conv), _ptr(S0), _ptr(conv_hist))
     if saved is None:
         _check(lib().prism_backward(ctypes.byref(desc), *inputs, _ptr(dO), _ptr(dST), *grads,
                                     _ptr(ws), ctypes.c_size_t(ws.numel()), ctypes.c_void_p(stream)))
@@ -246,6 +271,30 @@ def backward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None, S0=N
                                           *grads, _ptr(ws), ctypes.c_size_t(ws.numel()),
                                           ctypes.c_void_p(stream)))
     return g
+
+
+def step(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None, S=None, conv_state=None,
+         activation="gelu", conv_offset=0):
+    """Recurrent form (prism_step): the T tokens of each sequence in order,
+    token by token.  S [B,H,dv,dk] fp32 is required and updated in place
+    (S_0 in, S_T out); conv_state [B,4,H,dv] (v's dtype) likewise, or None
+    for a zero history that is not kept.  Returns o [B,T,H,dv].  With T = 1
+    this is one decode step."""
+    _validate_inputs(q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S)
+    if S is None:
+        raise ValueError("S is required")
+    B, T, H, dk = q.shape
+    if tuple(S.shape) != (B, H, v.shape[-1], dk):
+        raise ValueError(f"S: expected shape {(B, H, v.shape[-1], dk)}, got {tuple(S.shape)}")
+    if conv_state is not None:
+        _req_hist(conv_state, "conv_state", q, v)
+    desc = _desc_from(q, v, Wk, 16, activation, conv_offset)
+    o = torch.empty_like(v)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    _check(lib().prism_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                            _ptr(beta), _ptr(Wk), _ptr(Wp), _ptr(wbeta), _ptr(conv), _ptr(S),
+                            _ptr(conv_state), _ptr(o), ctypes.c_void_p(stream)))
+    return o
 
 
 class KernelTimer:

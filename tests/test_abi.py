@@ -51,7 +51,7 @@ def _fwd(desc, ptrs=None, ws=None, nbytes=0):
     """Call prism_forward with fake (never dereferenced) 16-byte aligned pointers."""
     L = P.lib()
     fake = ctypes.c_void_p(0x10000)
-    p = [fake] * 12 if ptrs is None else ptrs
+    p = [fake] * 14 if ptrs is None else ptrs
     return L.prism_forward(ctypes.byref(desc) if desc is not None else None, *p,
                            ws if ws is not None else fake, ctypes.c_size_t(nbytes), None)
 
@@ -114,30 +114,35 @@ def test_variant_fields():
 
 
 def test_null_desc_and_pointers():
+    # forward pointers: q k v alpha beta Wk Wp wbeta conv S0 conv_hist o ST conv_hist_out
     assert _fwd(None) == E_NULL
     fake = ctypes.c_void_p(0x10000)
     for i, name in enumerate(["q", "k", "v", "alpha", "beta", "Wk", "Wp", "wbeta", "conv"]):
-        p = [fake] * 12
+        p = [fake] * 14
         p[i] = None
         assert _fwd(good_desc(), p) == E_NULL, name
         assert name in _err()
     # with L = 0 the weights may be NULL (then the workspace check fails next)
-    p = [fake] * 12
+    p = [fake] * 14
     p[5] = p[6] = p[7] = p[8] = None
     assert _fwd(good_desc(L=0), p, nbytes=0) == E_WS
-    # output o is required; S0 and ST are optional
-    p = [fake] * 12
-    p[10] = None
-    assert _fwd(good_desc(), p) == E_NULL
-    p = [fake] * 12
-    p[9] = None
+    # output o is required; S0, conv_hist, ST and conv_hist_out are optional
+    p = [fake] * 14
     p[11] = None
+    assert _fwd(good_desc(), p) == E_NULL
+    p = [fake] * 14
+    p[9] = p[10] = p[12] = p[13] = None
     assert _fwd(good_desc(), p, nbytes=0) == E_WS
+    # the history buffers are checked for alignment like every tensor
+    for i, name in ((10, "conv_hist"), (13, "conv_hist_out")):
+        p = [fake] * 14
+        p[i] = ctypes.c_void_p(0x10004)
+        assert _fwd(good_desc(), p) == E_ALIGN and name in _err()
 
 
 def test_alignment_and_workspace():
     fake = ctypes.c_void_p(0x10000)
-    p = [fake] * 12
+    p = [fake] * 14
     p[2] = ctypes.c_void_p(0x10008)
     assert _fwd(good_desc(), p) == E_ALIGN and "v" in _err()
     assert _fwd(good_desc(), ws=ctypes.c_void_p(0x10010), nbytes=1 << 40) == E_ALIGN
@@ -145,13 +150,16 @@ def test_alignment_and_workspace():
     need = P.forward_workspace_bytes(d)
     assert _fwd(d, nbytes=need - 1) == E_WS and str(need) in _err()
     L = P.lib()
-    p = [fake] * 22
+    p = [fake] * 24
     assert L.prism_backward(ctypes.byref(d), *p, fake, ctypes.c_size_t(0), None) == E_WS
-    p[10] = None   # dO (order: q k v alpha beta Wk Wp wbeta conv S0 dO dST dq ...)
+    p[11] = None   # dO (order: q k v alpha beta Wk Wp wbeta conv S0 conv_hist dO dST dq ...)
     assert L.prism_backward(ctypes.byref(d), *p, fake, ctypes.c_size_t(1 << 40), None) == E_NULL
-    p = [fake] * 22
-    p[12] = None   # dq
+    p = [fake] * 24
+    p[13] = None   # dq
     assert L.prism_backward(ctypes.byref(d), *p, fake, ctypes.c_size_t(1 << 40), None) == E_NULL
+    p = [fake] * 24
+    p[10] = p[22] = p[23] = None   # conv_hist, dS0, dconv_hist are optional
+    assert L.prism_backward(ctypes.byref(d), *p, fake, ctypes.c_size_t(0), None) == E_WS
 
 
 def test_workspace_monotone():
@@ -182,24 +190,41 @@ def test_training_pair_checks():
     assert need > 0
     fake = ctypes.c_void_p(0x10000)
     ws_ok = ctypes.c_size_t(1 << 40)
-    p12 = [fake] * 12
+    p14 = [fake] * 14
     # saved NULL, misaligned, too small
-    assert L.prism_forward_train(ctypes.byref(d), *p12, None, ctypes.c_size_t(need), fake, ws_ok,
+    assert L.prism_forward_train(ctypes.byref(d), *p14, None, ctypes.c_size_t(need), fake, ws_ok,
                                  None) == E_WS
     assert "saved" in _err()
-    assert L.prism_forward_train(ctypes.byref(d), *p12, ctypes.c_void_p(0x10010),
+    assert L.prism_forward_train(ctypes.byref(d), *p14, ctypes.c_void_p(0x10010),
                                  ctypes.c_size_t(need), fake, ws_ok, None) == E_ALIGN
-    assert L.prism_forward_train(ctypes.byref(d), *p12, fake, ctypes.c_size_t(need - 1), fake, ws_ok,
+    assert L.prism_forward_train(ctypes.byref(d), *p14, fake, ctypes.c_size_t(need - 1), fake, ws_ok,
                                  None) == E_WS
     assert str(need) in _err()
-    p10 = [fake] * 10
-    p12 = [fake] * 12   # dO dST dq dk dv dalpha dbeta dWk dWp dwbeta dconv dS0
-    assert L.prism_backward_train(ctypes.byref(d), *p10, None, ctypes.c_size_t(need), *p12, fake,
+    p11 = [fake] * 11   # q k v alpha beta Wk Wp wbeta conv S0 conv_hist
+    p13 = [fake] * 13   # dO dST dq dk dv dalpha dbeta dWk dWp dwbeta dconv dS0 dconv_hist
+    assert L.prism_backward_train(ctypes.byref(d), *p11, None, ctypes.c_size_t(need), *p13, fake,
                                   ws_ok, None) == E_WS
     assert "saved" in _err()
     # the workspace check still applies
-    assert L.prism_backward_train(ctypes.byref(d), *p10, fake, ctypes.c_size_t(need), *p12, fake,
+    assert L.prism_backward_train(ctypes.byref(d), *p11, fake, ctypes.c_size_t(need), *p13, fake,
                                   ctypes.c_size_t(0), None) == E_WS
     assert "workspace" in _err()
     # saved size grows with T and L
     assert P.saved_bytes(good_desc(T=4096)) > need and P.saved_bytes(good_desc(L=4)) > need
+
+
+def test_step_checks():
+    """prism_step: q k v alpha beta Wk Wp wbeta conv S conv_state o; S and o
+    are required, conv_state is optional; checks come before any HIP call."""
+    L = P.lib()
+    fake = ctypes.c_void_p(0x10000)
+    d = good_desc(T=1)
+    for i, name in ((0, "q"), (5, "Wk"), (9, "S"), (11, "o")):
+        p = [fake] * 12
+        p[i] = None
+        assert L.prism_step(ctypes.byref(d), *p, None) == E_NULL and name in _err()
+    p = [fake] * 12
+    p[10] = ctypes.c_void_p(0x10002)
+    assert L.prism_step(ctypes.byref(d), *p, None) == E_ALIGN and "conv_state" in _err()
+    bad = good_desc(T=1, L=9)
+    assert L.prism_step(ctypes.byref(bad), *([fake] * 12), None) == E_UNSUP
