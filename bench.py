@@ -273,6 +273,55 @@ def cpu_baseline(w, x, budget_s=15.0, backward=False):
                       f"{'fwd+bwd' if backward else 'fwd'}, float64, {t_used:.1f} s"}
 
 
+def decode_bench(w, steps, batch=64):
+    """The decode step (prism_step, one token per sequence) at the workload's
+    head shape with `batch` sequences: event-timed calls, each kernel's own
+    average from the library's event timer, and the HBM roofline of the
+    state kernel, which dominates.  Its bytes per call: the fp32 state read
+    and written (8 d^2 per sequence and head), q, k, v, o, alpha, beta, the
+    L refinement pairs and the ShortConv history read and written."""
+    import numpy as np
+    import torch
+    from linear_recurrent_sequence_shortconv_amd import prism as P
+    from linear_recurrent_sequence_shortconv_amd.workloads import make_inputs
+
+    B, H, d, L = batch, w.H, w.d, w.L
+    x = make_inputs(B, 1, H, d, L, w.dtype, seed=1, random_S0=True)
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = lambda a, t=tdt: None if a is None else torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(t)
+    args = tuple(dev(x[n]) for n in ("q", "k", "v")) + tuple(
+        dev(x[n], torch.float32) for n in ("alpha", "beta")) + tuple(
+        dev(x.get(n)) for n in ("Wk", "Wp", "wbeta", "conv"))
+    S = dev(x["S0"], torch.float32)
+    cs = torch.zeros((B, 4, H, d), dtype=tdt, device="cuda")
+    for _ in range(3):
+        P.step(*args, S=S, conv_state=cs)
+    torch.cuda.synchronize()
+    n = max(steps, 50)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(n):
+        P.step(*args, S=S, conv_state=cs)
+    e1.record()
+    torch.cuda.synchronize()
+    us_call = e0.elapsed_time(e1) * 1e3 / n
+    with P.KernelTimer() as kt:
+        for _ in range(n):
+            P.step(*args, S=S, conv_state=cs)
+        torch.cuda.synchronize()
+    us = {n: tot * 1e3 / cnt for n, (tot, cnt) in kt.result.items()}
+    e = 2 if w.dtype == "bf16" else 4
+    nbytes = B * H * (8 * d * d + 4 * d * e + 2 * L * d * e + 2 * 4 * d * e + 8)
+    gbps = nbytes / (us["step_state"] * 1e-6) / 1e9
+    return {"workload": f"decode step B={B} H={H} d={d} L={L} {w.dtype}",
+            "us_per_call": round(us_call, 2),
+            "kernels_us": {n: round(x, 2) for n, x in us.items()},
+            "tokens_per_s": round(B / (us_call * 1e-6), 1),
+            "roofline": {"kernel": "step_state", "bound": "hbm", "achieved": round(gbps, 1),
+                         "peak": 8000.0, "unit": "GB/s", "frac": round(gbps / 8000.0, 4),
+                         "bytes_per_call": nbytes}}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -282,6 +331,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--forward-only", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write profiles/ summaries from the rocprofv3 runs under DIR and exit")
     args = ap.parse_args()
@@ -408,6 +458,8 @@ def main():
             kernels[n].update(bound=r["bound"], achieved=r["achieved"], unit=r["unit"],
                               frac=r["frac"], floor_ms=r["roofline_floor_ms"])
 
+    decode = None if args.no_decode else decode_bench(w, args.steps)
+
     tokens = w.B * w.T
     value = tokens / (ms * 1e-3)
     cpu = None
@@ -437,6 +489,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kernels,
+        "decode": decode,
     }
     print(json.dumps(line))
 

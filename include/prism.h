@@ -191,16 +191,20 @@ prism_status prism_backward_train(const prism_desc* desc, const void* q, const v
  *               tokens and overwritten with the history after them (in
  *               place); NULL means zeros, and nothing is written.
  *   o:          [B, T, H, dv] dt.
+ *   workspace:  prism_step_workspace() bytes, 256-byte aligned (the
+ *               refinement pairs of the tokens; 0 bytes and NULL allowed
+ *               when L = 0).
  * The other inputs and desc fields are those of prism_forward; desc->chunk
  * must be valid but is not used.  A prism_forward over the first tokens
  * with ST and conv_hist_out, then prism_step over the rest, equals one
- * prism_forward over all of them up to rounding.  No workspace: the state
- * stays in registers between tokens (one workgroup per sequence and head),
- * so S crosses HBM once per call.  Errors: as prism_forward. */
+ * prism_forward over all of them up to rounding.  The state stays in
+ * registers between tokens (one workgroup per sequence and head), so S
+ * crosses HBM once per call.  Errors: as prism_forward. */
+prism_status prism_step_workspace(const prism_desc* desc, size_t* bytes);
 prism_status prism_step(const prism_desc* desc, const void* q, const void* k, const void* v,
                         const float* alpha, const float* beta, const void* Wk, const void* Wp,
                         const void* wbeta, const void* conv, float* S, void* conv_state, void* o,
-                        hipStream_t stream);
+                        void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Human-readable name of a status code (static string). */
 const char* prism_status_string(prism_status status);

@@ -248,6 +248,14 @@ size_t kept_bytes(const prism::Dims& d, prism_dtype dt) {
   return cv.off;
 }
 
+// prism_step: the refinement pairs of every token, two arrays of
+// B * H * L * T * D elements, each rounded up to 256 bytes
+size_t step_ws_bytes(const prism::Dims& d, prism_dtype dt) {
+  const size_t es = dt == PRISM_BF16 ? 2 : 4;
+  const size_t one = ((size_t)d.B * d.H * d.L * d.T * d.D * es + 255) / 256 * 256;
+  return 2 * one;
+}
+
 size_t fwd_ws_bytes(const prism::Dims& d, prism_dtype dt) {
   Carve cv;
   if (dt == PRISM_BF16)
@@ -370,6 +378,24 @@ prism_status run_backward(const prism::Dims& d, const void* q, const void* k, co
   } else if (dhist) {   // without refinement the history does not reach the outputs
     HIP_TRY("zero_hist_grad", s, prism::launch_zero(dhist, (long)d.B * 4 * d.H * d.D, s));
   }
+  return PRISM_OK;
+}
+
+template <typename E>
+prism_status run_step(const prism::Dims& d, const void* q, const void* k, const void* v,
+                      const float* alpha, const float* beta, const void* Wk, const void* Wp,
+                      const void* wbeta, const void* conv, float* S, void* cs, void* o, char* Kl,
+                      char* Wl, hipStream_t s) {
+  auto go = [&](int stage) {
+    return prism::launch_step<E>(d, static_cast<const E*>(q), static_cast<const E*>(k),
+                                 static_cast<const E*>(v), alpha, beta, static_cast<const E*>(Wk),
+                                 static_cast<const E*>(Wp), static_cast<const E*>(wbeta),
+                                 static_cast<const E*>(conv), S, static_cast<E*>(cs),
+                                 static_cast<E*>(o), reinterpret_cast<E*>(Kl),
+                                 reinterpret_cast<E*>(Wl), stage, s);
+  };
+  if (d.L > 0) HIP_TRY("step_refine", s, go(0));
+  HIP_TRY("step_state", s, go(1));
   return PRISM_OK;
 }
 
@@ -586,10 +612,20 @@ prism_status prism_backward_train(const prism_desc* desc, const void* q, const v
                         dconv, dS0, dconv_hist, workspace, workspace_bytes, stream);
 }
 
+prism_status prism_step_workspace(const prism_desc* desc, size_t* bytes) {
+  if (bytes) *bytes = 0;
+  if (!bytes) return fail(PRISM_ERR_NULL, "bytes is NULL");
+  prism::Dims d;
+  prism_status st = check_desc(desc, &d);
+  if (st != PRISM_OK) return st;
+  *bytes = step_ws_bytes(d, desc->dtype);
+  return PRISM_OK;
+}
+
 prism_status prism_step(const prism_desc* desc, const void* q, const void* k, const void* v,
                         const float* alpha, const float* beta, const void* Wk, const void* Wp,
                         const void* wbeta, const void* conv, float* S, void* conv_state, void* o,
-                        hipStream_t stream) {
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
   try {
     g_err.clear();
     prism::Dims d;
@@ -608,24 +644,19 @@ prism_status prism_step(const prism_desc* desc, const void* q, const void* k, co
     CHECK_PTR(S, true);
     CHECK_PTR(conv_state, false);
     CHECK_PTR(o, true);
-    if (desc->dtype == PRISM_BF16) {
-      typedef prism::bf16 E;
-      HIP_TRY("step", stream,
-              prism::launch_step<E>(d, static_cast<const E*>(q), static_cast<const E*>(k),
-                                    static_cast<const E*>(v), alpha, beta,
-                                    static_cast<const E*>(Wk), static_cast<const E*>(Wp),
-                                    static_cast<const E*>(wbeta), static_cast<const E*>(conv), S,
-                                    static_cast<E*>(conv_state), static_cast<E*>(o), stream));
-    } else {
-      typedef float E;
-      HIP_TRY("step", stream,
-              prism::launch_step<E>(d, static_cast<const E*>(q), static_cast<const E*>(k),
-                                    static_cast<const E*>(v), alpha, beta,
-                                    static_cast<const E*>(Wk), static_cast<const E*>(Wp),
-                                    static_cast<const E*>(wbeta), static_cast<const E*>(conv), S,
-                                    static_cast<E*>(conv_state), static_cast<E*>(o), stream));
+    const size_t need = step_ws_bytes(d, desc->dtype);
+    if (need > 0) {
+      st = check_buffer(workspace, workspace_bytes, need, "workspace");
+      if (st != PRISM_OK) return st;
     }
-    return PRISM_OK;
+    // the refinement pairs, [B, H, L, T, D] each
+    const size_t half = need / 2;
+    char* ws = static_cast<char*>(workspace);
+    if (desc->dtype == PRISM_BF16)
+      return run_step<prism::bf16>(d, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S, conv_state, o,
+                                   need ? ws : nullptr, need ? ws + half : nullptr, stream);
+    return run_step<float>(d, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S, conv_state, o,
+                           need ? ws : nullptr, need ? ws + half : nullptr, stream);
   } catch (...) {
     return fail(PRISM_ERR_HIP, "unexpected host exception");
   }

@@ -103,11 +103,13 @@ hipError_t launch_zero(float* p, long n, hipStream_t s);
 
 // Token-by-token recurrence for T tokens per sequence: S [B, H, D, D] fp32
 // and the ShortConv history cstate [B, 4, H, D] (nullptr: zeros, not kept)
-// are read, carried and written back in place; o [B, T, H, D].
+// are read, carried and written back in place; o [B, T, H, D].  Kl, Wl:
+// room for the refinement pairs, [B, H, L, T, D] each.  stage 0 writes the
+// pairs (refinement kernel, nothing when L = 0), stage 1 runs the state.
 template <typename E>
 hipError_t launch_step(const Dims& d, const E* q, const E* k, const E* v, const float* alpha,
                        const float* beta, const E* Wk, const E* Wp, const E* wbeta, const E* conv,
-                       float* S, E* cstate, E* o, hipStream_t s);
+                       float* S, E* cstate, E* o, E* Kl, E* Wl, int stage, hipStream_t s);
 
 // O = O_loc + Qt S_c^T, written to o [B, T, H, D].
 template <typename E>

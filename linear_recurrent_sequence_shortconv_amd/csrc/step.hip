@@ -2,44 +2,46 @@
 // Decoupling" and §2.2 "Input-Anchored Loop Unrolling"): the decode step of
 // serving, and the exact hand-over of a sequence from one call to the next.
 //
-// For each token of one (b, h):
-//   u   = sum_j c[:, j] v_{t-o-j}        (ShortConv over the carried history)
-//   r   = v - u;  for l: p = W_p^(l) u, k^(l) = W_k^(l) u,
-//         g = sigmoid(w_beta^(l) . u), delta = act(p * r), r -= delta,
-//         w^(l) = g delta
-//   S  <- alpha (S - beta (S k) k^T) + beta v k^T + sum_l w^(l) k^(l)^T
-//   o   = S q
+// The refinement pairs (k^(l), w^(l)) depend on v and the ShortConv history
+// only, never on S, so a step is two kernels: the refinement kernel (with
+// one token per sequence it tiles 64 sequences of a head on MFMA, reading
+// the head's weights once per tile) writes the pairs, then the state kernel
+// here applies, per token of one (b, h),
+//   S <- alpha (S - beta (S k) k^T) + beta v k^T + sum_l w^(l) k^(l)^T,
+//   o  = S q.
 // One workgroup owns one (b, h) for all T tokens: the fp32 state stays in
-// registers between tokens, so it crosses HBM once per call (read and
-// write, 8 D^2 bytes), which is what bounds a decode step.  Workgroups are
-// ordered head-major so that the sequences of one head share an XCD and its
-// L2 holds that head's weights.
+// registers between tokens, so it crosses HBM once per call (8 D^2 bytes
+// read and written), which is what bounds a decode step.  The workgroup
+// also rolls the ShortConv history forward.
+#include <type_traits>
+
 #include "prism_common.h"
 #include "prism_internal.h"
 
 namespace prism {
 
-constexpr int ST_NT = 256;
-constexpr int ST_NW = ST_NT / WAVE;
 constexpr int ST_LMAX = 8;
 
-template <typename E, int D, int ACT, int OFF>
-__global__ __launch_bounds__(ST_NT) void step_kernel(
+// Threads of the state kernel: four waves, or one for d = 16 (each lane
+// holds four consecutive columns of one or more rows).
+constexpr int st_waves(int D) { return D * D / 256 < 4 ? D * D / 256 : 4; }
+
+template <typename E, int D>
+__global__ __launch_bounds__(64 * st_waves(D)) void step_state_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
-    const float* __restrict__ alpha, const float* __restrict__ beta, const E* __restrict__ Wk,
-    const E* __restrict__ Wp, const E* __restrict__ wbeta, const E* __restrict__ conv,
-    float* __restrict__ S, E* __restrict__ cstate, E* __restrict__ o, int B, int T, int H, int L) {
-  constexpr int TPR = ST_NT / D;            // threads per state row
-  constexpr int NCOL = D / TPR;             // state columns per thread
-  constexpr int VN = 16 / (int)sizeof(E);   // weight elements per 16-byte load
-  constexpr int LPR = D / VN;               // lanes per weight row
-  constexpr int RPW = WAVE / LPR;           // weight rows per wave and pass
-  constexpr int PS = 2 * D + 4;             // projections of one step: p, k^(l), gate logit
+    const float* __restrict__ alpha, const float* __restrict__ beta, const E* __restrict__ Kl,
+    const E* __restrict__ Wl, float* __restrict__ S, E* __restrict__ cstate, E* __restrict__ o,
+    int B, int T, int H, int L) {
+  constexpr int NW = st_waves(D);
+  constexpr int NT = 64 * NW;
+  constexpr int CPR = D / 4;                // lanes per state row (four columns each)
+  constexpr int RPI = WAVE / CPR;           // rows per wave per load: one contiguous block
+  constexpr int RPW = D / NW;               // rows per wave
+  constexpr int NR = RPW / RPI;             // rows per lane
   __shared__ __attribute__((aligned(16))) float kv[D];
   __shared__ __attribute__((aligned(16))) float qv[D];
   __shared__ __attribute__((aligned(16))) float vv[D];
-  __shared__ __attribute__((aligned(16))) float uv[D];
-  __shared__ __attribute__((aligned(16))) float proj[ST_LMAX * PS];
+  __shared__ __attribute__((aligned(16))) float kl[ST_LMAX * D];
   __shared__ __attribute__((aligned(16))) float wl[ST_LMAX * D];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -50,130 +52,247 @@ __global__ __launch_bounds__(ST_NT) void step_kernel(
   const long tok = (long)H * D;
   const long base = ((long)b * T * H + h) * D;   // token t of this (b, h) at base + t * tok
 
-  // state row `row`, columns c0 .. c0 + NCOL - 1
-  const int row = tid / TPR, c0 = (tid % TPR) * NCOL;
-  float* Sp = S + (bh * D + row) * D + c0;
-  float s[NCOL];
-  if constexpr (NCOL % 4 == 0) {
+  // lane (wave w, lane l): columns 4 cc .. 4 cc + 3 of rows w RPW + j RPI + l / CPR,
+  // so each load instruction of a wave reads RPI whole consecutive rows
+  const int cc = lane % CPR;
+  const int row0 = wave * RPW + lane / CPR;
+  float* Sp = S + (bh * D + row0) * D + 4 * cc;
+  f32x4 s[NR];
 #pragma unroll
-    for (int c = 0; c < NCOL; c += 4) *reinterpret_cast<f32x4*>(s + c) = *reinterpret_cast<const f32x4*>(Sp + c);
-  } else {
+  for (int j = 0; j < NR; ++j) s[j] = *reinterpret_cast<const f32x4*>(Sp + (long)j * RPI * D);
+
+  // sum over the CPR lanes of a row, left in every one of them
+  auto row_sum = [](float x) {
 #pragma unroll
-    for (int c = 0; c < NCOL; ++c) s[c] = Sp[c];
-  }
-  // feature f = tid (< D): its taps and the four values before the sequence
-  float tp[4] = {0.f, 0.f, 0.f, 0.f}, hv[4] = {0.f, 0.f, 0.f, 0.f};
-  if (tid < D) {
-    if (L > 0) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) tp[j] = to_f(conv[((long)h * D + tid) * 4 + j]);
-    }
-    if (cstate) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) hv[r] = to_f(cstate[(((long)b * 4 + r) * H + h) * D + tid]);
-    }
-  }
-  const int nproj = L * PS;
+    for (int off = CPR / 2; off > 0; off >>= 1) x += __shfl_xor(x, off);
+    return x;
+  };
 
   for (int t = 0; t < T; ++t) {
     const long at = base + t * tok;
-    float vt = 0.f;
-    if (tid < D) {
-      vt = to_f(v[at + tid]);
-      kv[tid] = to_f(k[at + tid]);
-      qv[tid] = to_f(q[at + tid]);
-      vv[tid] = vt;
+    for (int e = tid; e < D; e += NT) {
+      kv[e] = to_f(k[at + e]);
+      qv[e] = to_f(q[at + e]);
+      vv[e] = to_f(v[at + e]);
+    }
+    for (int e = tid; e < L * D; e += NT) {
+      const int l = e / D, f = e % D;
+      const long src = ((bh * L + l) * T + t) * D + f;
+      kl[e] = to_f(Kl[src]);
+      wl[e] = to_f(Wl[src]);
     }
     const long ab = ((long)b * T + t) * H + h;
     const float a = alpha[ab], bt = beta[ab];
-    float r = 0.f;
-    if (L > 0 && tid < D) {
-      float u;
-      if constexpr (OFF == 0) u = tp[0] * vt + tp[1] * hv[3] + tp[2] * hv[2] + tp[3] * hv[1];
-      else u = tp[0] * hv[3] + tp[1] * hv[2] + tp[2] * hv[1] + tp[3] * hv[0];
-      uv[tid] = u;
-      r = vt - u;
-    }
-    hv[0] = hv[1];
-    hv[1] = hv[2];
-    hv[2] = hv[3];
-    hv[3] = vt;
     __syncthreads();
 
-    if (L > 0) {
-      // every projection of every step at once (none depends on the chain):
-      // row n of step l = n / PS is W_p^(l) row m (m < D), W_k^(l) row m - D
-      // (m < 2D) or w_beta^(l) (m = 2D); LPR lanes share one row
-      const int sub = lane / LPR, part = lane % LPR;
-      float ue[VN];
+    const f32x4 k4 = *reinterpret_cast<const f32x4*>(kv + 4 * cc);
+    // S <- a (S - bt (S k) k^T) + bt v k^T + sum_l w^(l) k^(l)^T, row by row
 #pragma unroll
-      for (int j = 0; j < VN; ++j) ue[j] = uv[part * VN + j];
-      for (int n0 = wave * RPW; n0 < nproj; n0 += ST_NW * RPW) {
-        const int n = n0 + sub;
-        const int l = n / PS, m = n % PS;
-        float acc = 0.f;
-        if (n < nproj && m <= 2 * D) {
-          const E* wr = m < D ? Wp + (((long)h * L + l) * D + m) * D
-                       : m < 2 * D ? Wk + (((long)h * L + l) * D + (m - D)) * D
-                                   : wbeta + ((long)h * L + l) * D;
-          const uint4 x = ld16(wr + part * VN);
-          const E* xe = reinterpret_cast<const E*>(&x);
+    for (int j = 0; j < NR; ++j) {
+      const int row = row0 + j * RPI;
+      const float y = row_sum(s[j][0] * k4[0] + s[j][1] * k4[1] + s[j][2] * k4[2] + s[j][3] * k4[3]);
+      const float coef = bt * (vv[row] - a * y);
 #pragma unroll
-          for (int j = 0; j < VN; ++j) acc += to_f(xe[j]) * ue[j];
-        }
-#pragma unroll
-        for (int off = LPR / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
-        if (part == 0 && n < nproj) proj[n] = acc;
-      }
-      __syncthreads();
-      // the residual chain of feature tid
-      if (tid < D) {
-        for (int l = 0; l < L; ++l) {
-          const float z = proj[l * PS + tid] * r;
-          float dl;
-          if constexpr (ACT == ACT_IDENTITY) dl = z;
-          else dl = gelu_erf(z);
-          r -= dl;
-          wl[l * D + tid] = sigmoidf(proj[l * PS + 2 * D]) * dl;
-        }
-      }
-      __syncthreads();
+      for (int c = 0; c < 4; ++c) s[j][c] = a * s[j][c] + coef * k4[c];
     }
-
-    // S k for this row (TPR consecutive lanes share the row)
-    float y = 0.f;
-#pragma unroll
-    for (int c = 0; c < NCOL; ++c) y += s[c] * kv[c0 + c];
-#pragma unroll
-    for (int off = TPR / 2; off > 0; off >>= 1) y += __shfl_xor(y, off);
-    const float coef = bt * (vv[row] - a * y);
-#pragma unroll
-    for (int c = 0; c < NCOL; ++c) s[c] = a * s[c] + coef * kv[c0 + c];
     for (int l = 0; l < L; ++l) {
-      const float wi = wl[l * D + row];
-      const float* kl = proj + l * PS + D + c0;
+      const f32x4 kr = *reinterpret_cast<const f32x4*>(kl + l * D + 4 * cc);
 #pragma unroll
-      for (int c = 0; c < NCOL; ++c) s[c] += wi * kl[c];
+      for (int j = 0; j < NR; ++j) {
+        const float wi = wl[l * D + row0 + j * RPI];
+#pragma unroll
+        for (int c = 0; c < 4; ++c) s[j][c] += wi * kr[c];
+      }
     }
-    float ot = 0.f;
+    // o = S q
+    const f32x4 q4 = *reinterpret_cast<const f32x4*>(qv + 4 * cc);
 #pragma unroll
-    for (int c = 0; c < NCOL; ++c) ot += s[c] * qv[c0 + c];
-#pragma unroll
-    for (int off = TPR / 2; off > 0; off >>= 1) ot += __shfl_xor(ot, off);
-    if (tid % TPR == 0) o[at + row] = to_t<E>(ot);
-    __syncthreads();   // the next token rewrites kv, qv, vv, uv, proj, wl
+    for (int j = 0; j < NR; ++j) {
+      const float ot = row_sum(s[j][0] * q4[0] + s[j][1] * q4[1] + s[j][2] * q4[2] + s[j][3] * q4[3]);
+      if (cc == 0) o[at + row0 + j * RPI] = to_t<E>(ot);
+    }
+    __syncthreads();   // the next token rewrites kv, qv, vv, kl, wl
   }
 
-  if constexpr (NCOL % 4 == 0) {
 #pragma unroll
-    for (int c = 0; c < NCOL; c += 4) *reinterpret_cast<f32x4*>(Sp + c) = *reinterpret_cast<const f32x4*>(s + c);
-  } else {
+  for (int j = 0; j < NR; ++j) *reinterpret_cast<f32x4*>(Sp + (long)j * RPI * D) = s[j];
+  // ShortConv history after the tokens: row r holds v_{T-4+r}; each thread
+  // reads its feature's four values before writing any
+  for (int f = tid; cstate && f < D; f += NT) {
+    E x[4];
 #pragma unroll
-    for (int c = 0; c < NCOL; ++c) Sp[c] = s[c];
+    for (int r = 0; r < 4; ++r) {
+      const int t = T - 4 + r;
+      x[r] = t >= 0 ? v[base + t * tok + f] : cstate[(((long)b * 4 + T + r) * H + h) * D + f];
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) cstate[(((long)b * 4 + r) * H + h) * D + f] = x[r];
   }
-  if (cstate && tid < D) {
+}
+
+// Refinement pairs of a decode step (one token per sequence), summary §2.2
+// Stages 1-2: a workgroup owns 64 sequences of one head and 64 of its output
+// features (one 16-feature MFMA tile per wave), so the pairs of all
+// sequences of a head come from MFMA products with the head's weights, read
+// once per 64 sequences.  The weights of two steps are in flight at a time;
+// the anchor of every feature (the MFMA operand) is formed from each
+// sequence's token and carried history; the chain runs in registers and the
+// pairs are stored from the accumulators, so the L steps need no barrier.
+constexpr int DR_NT = 256;
+constexpr int DR_ROWS = 64;   // sequences per workgroup
+constexpr int DR_FG = 64;     // output features per workgroup (4 waves x 16)
+
+template <typename E, int D, int ACT, int OFF>
+__global__ __launch_bounds__(DR_NT) void decode_refine_kernel(
+    const E* __restrict__ v, const E* __restrict__ hist, const E* __restrict__ conv,
+    const E* __restrict__ Wk, const E* __restrict__ Wp, const E* __restrict__ wbeta,
+    E* __restrict__ Kl, E* __restrict__ Wl, int B, int H, int L) {
+  constexpr int LD = ldpad<E>(D);
+  constexpr int KS = Mfma<E>::KSTEP;
+  constexpr int NK = D / KS;
+  constexpr int VN = 16 / (int)sizeof(E);
+  constexpr int FG = D < DR_FG ? D : DR_FG;   // features of this workgroup
+  constexpr int NFG = D / FG;
+  constexpr int RW = FG + 4;                  // fp32 residual rows
+  typedef typename Mfma<E>::frag Frag;
+  __shared__ __attribute__((aligned(16))) E ubuf[DR_ROWS * LD];
+  __shared__ __attribute__((aligned(16))) E ulo[sizeof(E) == 2 ? DR_ROWS * LD : 16];
+  __shared__ __attribute__((aligned(16))) float rbuf[DR_ROWS * RW];
+  __shared__ float gate[ST_LMAX][DR_ROWS];
+  __shared__ __attribute__((aligned(16))) E wbs[ST_LMAX * D];
+  __shared__ float ctp[D * 4];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nbt = (B + DR_ROWS - 1) / DR_ROWS;
+  const int bid = blockIdx.x;
+  const int h = bid / (nbt * NFG);
+  const int rest = bid % (nbt * NFG);
+  const int b0 = (rest / NFG) * DR_ROWS, f0 = (rest % NFG) * FG;
+  const bool has = wave < FG / 16;            // this wave owns a feature tile
+  const int n = f0 / 16 + wave;               // its tile
+
+  Frag wp[2][NK], wk[2][NK];
+  auto load_w = [&](int l, Frag (&p)[NK], Frag (&k)[NK]) {
+    const E* P = Wp + ((long)h * L + l) * D * D;
+    const E* K = Wk + ((long)h * L + l) * D * D;
 #pragma unroll
-    for (int r = 0; r < 4; ++r) cstate[(((long)b * 4 + r) * H + h) * D + tid] = to_t<E>(hv[r]);
+    for (int kk = 0; kk < NK; ++kk) {
+      p[kk] = load_frag<E, true>(P, D, 16 * n, kk * KS, lane);
+      k[kk] = load_frag<E, true>(K, D, 16 * n, kk * KS, lane);
+    }
+  };
+  if (has) {
+    load_w(0, wp[0], wk[0]);
+    if (L > 1) load_w(1, wp[1], wk[1]);
+  }
+  for (int e = tid; e < L * (D / VN); e += DR_NT)
+    st16(wbs + e * VN, ld16(wbeta + (long)h * L * D + e * VN));
+  for (int e = tid; e < D * 4; e += DR_NT) ctp[e] = to_f(conv[(long)h * D * 4 + e]);
+  __syncthreads();
+
+  // anchor u of every feature (hi and lo parts, the MFMA operand) and the
+  // residual r = v - u of this workgroup's features; x_s = v_{-s}, where
+  // x_0 is the token and x_s (s >= 1) history row 4 - s
+  for (int e = tid; e < DR_ROWS * (D / VN); e += DR_NT) {
+    const int r = e / (D / VN), c = (e % (D / VN)) * VN;
+    const int bs = b0 + r;
+    float x[4 + OFF][VN];
+#pragma unroll
+    for (int s = 0; s < 4 + OFF; ++s)
+#pragma unroll
+      for (int j = 0; j < VN; ++j) x[s][j] = 0.f;
+    if (bs < B) {
+      uint4 w = ld16(v + ((long)bs * H + h) * D + c);
+      const E* we = reinterpret_cast<const E*>(&w);
+#pragma unroll
+      for (int j = 0; j < VN; ++j) x[0][j] = to_f(we[j]);
+      if (hist) {
+#pragma unroll
+        for (int s = 1; s < 4 + OFF; ++s) {
+          w = ld16(hist + (((long)bs * 4 + 4 - s) * H + h) * D + c);
+#pragma unroll
+          for (int j = 0; j < VN; ++j) x[s][j] = to_f(we[j]);
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < VN; ++j) {
+      const float* tp = ctp + (c + j) * 4;
+      const float u = tp[0] * x[OFF][j] + tp[1] * x[OFF + 1][j] + tp[2] * x[OFF + 2][j] +
+                      tp[3] * x[OFF + 3][j];
+      const E uh = to_t<E>(u);
+      ubuf[r * LD + c + j] = uh;
+      if constexpr (sizeof(E) == 2) ulo[r * LD + c + j] = to_t<E>(u - to_f(uh));
+      if (c + j >= f0 && c + j < f0 + FG) rbuf[r * RW + c + j - f0] = x[0][j] - u;
+    }
+  }
+  __syncthreads();
+  // step gates sigmoid(w_beta^(l) . u): four threads per sequence
+  {
+    const int t = tid >> 2, part = tid & 3;
+    for (int l = 0; l < L; ++l) {
+      float s = 0.f;
+      for (int c = part * VN; c < D; c += 4 * VN) {
+        const uint4 ua = ld16(ubuf + t * LD + c), wa = ld16(wbs + l * D + c);
+        const E* ue = reinterpret_cast<const E*>(&ua);
+        const E* we = reinterpret_cast<const E*>(&wa);
+#pragma unroll
+        for (int j = 0; j < VN; ++j) s += to_f(we[j]) * to_f(ue[j]);
+      }
+      s += __shfl_xor(s, 1);
+      s += __shfl_xor(s, 2);
+      if (part == 0) gate[l][t] = sigmoidf(s);
+    }
+  }
+  __syncthreads();
+  if (!has) return;   // no barrier follows
+
+  // residual in the accumulator layout: (m, i) is sequence 16 m + 4 (lane >> 4) + i
+  const int fl = 16 * wave + (lane & 15);
+  float r[4][4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) r[m][i] = rbuf[(16 * m + 4 * (lane >> 4) + i) * RW + fl];
+
+#pragma unroll
+  for (int l = 0; l < ST_LMAX; ++l) {
+    if (l >= L) break;
+    const int sl = l & 1;
+    f32x4 ap[4], ak[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) ap[m] = ak[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const Frag a = load_frag<E, true>(ubuf, LD, 16 * m, kk * KS, lane);
+        ap[m] = Mfma<E>::mma(a, wp[sl][kk], ap[m]);
+        ak[m] = Mfma<E>::mma(a, wk[sl][kk], ak[m]);
+        if constexpr (sizeof(E) == 2) {
+          const Frag al = load_frag<E, true>(ulo, LD, 16 * m, kk * KS, lane);
+          ap[m] = Mfma<E>::mma(al, wp[sl][kk], ap[m]);
+        }
+      }
+    }
+    if (l + 2 < L) load_w(l + 2, wp[sl], wk[sl]);
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = 16 * m + 4 * (lane >> 4) + i;
+        const float z = ap[m][i] * r[m][i];
+        float dl;
+        if constexpr (ACT == ACT_IDENTITY) dl = z;
+        else dl = gelu_erf(z);
+        r[m][i] -= dl;
+        const int bs = b0 + row;
+        if (bs < B) {
+          const long o = (((long)bs * H + h) * L + l) * D + f0 + fl;
+          Kl[o] = to_t<E>(ak[m][i]);
+          Wl[o] = to_t<E>(gate[l][row] * dl);
+        }
+      }
   }
 }
 
@@ -220,31 +339,51 @@ hipError_t launch_zero(float* p, long n, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <typename E, int D>
-static hipError_t step_d(const Dims& d, const E* q, const E* k, const E* v, const float* alpha,
-                         const float* beta, const E* Wk, const E* Wp, const E* wbeta,
-                         const E* conv, float* S, E* cs, E* o, hipStream_t s) {
-  auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3(d.B * d.H), dim3(ST_NT), 0, s, q, k, v, alpha, beta, Wk, Wp,
-                       wbeta, conv, S, cs, o, d.B, d.T, d.H, d.L);
-  };
-  if (d.act == ACT_IDENTITY)
-    d.off ? go(step_kernel<E, D, ACT_IDENTITY, 1>) : go(step_kernel<E, D, ACT_IDENTITY, 0>);
-  else
-    d.off ? go(step_kernel<E, D, ACT_GELU, 1>) : go(step_kernel<E, D, ACT_GELU, 0>);
-  return hipGetLastError();
-}
-
 template <typename E>
 hipError_t launch_step(const Dims& d, const E* q, const E* k, const E* v, const float* alpha,
                        const float* beta, const E* Wk, const E* Wp, const E* wbeta, const E* conv,
-                       float* S, E* cs, E* o, hipStream_t s) {
+                       float* S, E* cs, E* o, E* Kl, E* Wl, int stage, hipStream_t s) {
   if (d.L > ST_LMAX) return hipErrorInvalidValue;
+  if (stage == 0) {
+    if (d.L == 0) return hipSuccess;
+    if (d.T > 1) {
+      Dims r = d;
+      r.Tp = d.T;   // pairs stored unpadded: [B, H, L, T, D]
+      return launch_refine_fwd<E>(r, v, cs, conv, Wk, Wp, wbeta, Kl, Wl, s);
+    }
+    auto go = [&](auto kern, int nfg) {
+      const int nblk = d.H * ((d.B + DR_ROWS - 1) / DR_ROWS) * nfg;
+      hipLaunchKernelGGL(kern, dim3(nblk), dim3(DR_NT), 0, s, v, cs, conv, Wk, Wp, wbeta, Kl, Wl,
+                         d.B, d.H, d.L);
+      return hipGetLastError();
+    };
+    auto by_d = [&](auto dd) {
+      constexpr int D = decltype(dd)::value;
+      constexpr int nfg = D < DR_FG ? 1 : D / DR_FG;
+      if (d.act == ACT_IDENTITY)
+        return d.off ? go(decode_refine_kernel<E, D, ACT_IDENTITY, 1>, nfg)
+                     : go(decode_refine_kernel<E, D, ACT_IDENTITY, 0>, nfg);
+      return d.off ? go(decode_refine_kernel<E, D, ACT_GELU, 1>, nfg)
+                   : go(decode_refine_kernel<E, D, ACT_GELU, 0>, nfg);
+    };
+    switch (d.D) {
+      case 16: return by_d(std::integral_constant<int, 16>{});
+      case 32: return by_d(std::integral_constant<int, 32>{});
+      case 64: return by_d(std::integral_constant<int, 64>{});
+      case 128: return by_d(std::integral_constant<int, 128>{});
+    }
+    return hipErrorInvalidValue;
+  }
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, dim3(d.B * d.H), dim3(64 * st_waves(d.D)), 0, s, q, k, v, alpha, beta,
+                       Kl, Wl, S, cs, o, d.B, d.T, d.H, d.L);
+    return hipGetLastError();
+  };
   switch (d.D) {
-    case 16: return step_d<E, 16>(d, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S, cs, o, s);
-    case 32: return step_d<E, 32>(d, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S, cs, o, s);
-    case 64: return step_d<E, 64>(d, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S, cs, o, s);
-    case 128: return step_d<E, 128>(d, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S, cs, o, s);
+    case 16: return go(step_state_kernel<E, 16>);
+    case 32: return go(step_state_kernel<E, 32>);
+    case 64: return go(step_state_kernel<E, 64>);
+    case 128: return go(step_state_kernel<E, 128>);
   }
   return hipErrorInvalidValue;
 }
@@ -254,10 +393,11 @@ template hipError_t launch_conv_state<float>(const Dims&, const float*, const fl
                                              hipStream_t);
 template hipError_t launch_step<bf16>(const Dims&, const bf16*, const bf16*, const bf16*,
                                       const float*, const float*, const bf16*, const bf16*,
-                                      const bf16*, const bf16*, float*, bf16*, bf16*, hipStream_t);
+                                      const bf16*, const bf16*, float*, bf16*, bf16*, bf16*, bf16*,
+                                      int, hipStream_t);
 template hipError_t launch_step<float>(const Dims&, const float*, const float*, const float*,
                                        const float*, const float*, const float*, const float*,
-                                       const float*, const float*, float*, float*, float*,
-                                       hipStream_t);
+                                       const float*, const float*, float*, float*, float*, float*,
+                                       float*, int, hipStream_t);
 
 }  // namespace prism

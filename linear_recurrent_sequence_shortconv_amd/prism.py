@@ -20,7 +20,7 @@ STATUS = {0: "PRISM_OK", 1: "PRISM_ERR_NULL", 2: "PRISM_ERR_SHAPE", 3: "PRISM_ER
 
 EXPORTS = ("prism_forward_workspace", "prism_backward_workspace", "prism_forward",
            "prism_backward", "prism_saved_bytes", "prism_forward_train", "prism_backward_train",
-           "prism_step", "prism_status_string", "prism_last_error", "prism_timing_begin",
+           "prism_step_workspace", "prism_step", "prism_status_string", "prism_last_error", "prism_timing_begin",
            "prism_timing_end")
 
 
@@ -55,10 +55,11 @@ def lib():
                                           + [_P, ctypes.c_size_t, _P, ctypes.c_size_t, _P])
         L.prism_backward_train.argtypes = ([ctypes.POINTER(Desc)] + [_P] * 11 + [_P, ctypes.c_size_t]
                                            + [_P] * 13 + [_P, ctypes.c_size_t, _P])
-        L.prism_step.argtypes = [ctypes.POINTER(Desc)] + [_P] * 12 + [_P]
+        L.prism_step_workspace.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(ctypes.c_size_t)]
+        L.prism_step.argtypes = [ctypes.POINTER(Desc)] + [_P] * 12 + [_P, ctypes.c_size_t, _P]
         for f in ("prism_forward_workspace", "prism_backward_workspace", "prism_forward",
                   "prism_backward", "prism_saved_bytes", "prism_forward_train",
-                  "prism_backward_train", "prism_step"):
+                  "prism_backward_train", "prism_step_workspace", "prism_step"):
             getattr(L, f).restype = ctypes.c_int
         L.prism_status_string.argtypes = [ctypes.c_int]
         L.prism_status_string.restype = ctypes.c_char_p
@@ -273,8 +274,14 @@ def backward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None, S0=N
     return g
 
 
+def step_workspace_bytes(desc):
+    n = ctypes.c_size_t(0)
+    _check(lib().prism_step_workspace(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
 def step(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None, S=None, conv_state=None,
-         activation="gelu", conv_offset=0):
+         activation="gelu", conv_offset=0, workspace=None):
     """Recurrent form (prism_step): the T tokens of each sequence in order,
     token by token.  S [B,H,dv,dk] fp32 is required and updated in place
     (S_0 in, S_T out); conv_state [B,4,H,dv] (v's dtype) likewise, or None
@@ -290,10 +297,13 @@ def step(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None, S=None, 
         _req_hist(conv_state, "conv_state", q, v)
     desc = _desc_from(q, v, Wk, 16, activation, conv_offset)
     o = torch.empty_like(v)
+    if workspace is None:
+        _, workspace = _workspace(step_workspace_bytes(desc), q.device)
     stream = torch.cuda.current_stream(q.device).cuda_stream
     _check(lib().prism_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
                             _ptr(beta), _ptr(Wk), _ptr(Wp), _ptr(wbeta), _ptr(conv), _ptr(S),
-                            _ptr(conv_state), _ptr(o), ctypes.c_void_p(stream)))
+                            _ptr(conv_state), _ptr(o), _ptr(workspace),
+                            ctypes.c_size_t(workspace.numel()), ctypes.c_void_p(stream)))
     return o
 
 

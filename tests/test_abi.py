@@ -219,12 +219,18 @@ def test_step_checks():
     L = P.lib()
     fake = ctypes.c_void_p(0x10000)
     d = good_desc(T=1)
+    need = P.step_workspace_bytes(d)
+    assert need == 2 * ((2 * 4 * 2 * 64 * 2 + 255) // 256 * 256)   # pairs [B,H,L,T,D] bf16
+    ws = (fake, ctypes.c_size_t(need), None)
     for i, name in ((0, "q"), (5, "Wk"), (9, "S"), (11, "o")):
         p = [fake] * 12
         p[i] = None
-        assert L.prism_step(ctypes.byref(d), *p, None) == E_NULL and name in _err()
+        assert L.prism_step(ctypes.byref(d), *p, *ws) == E_NULL and name in _err()
     p = [fake] * 12
     p[10] = ctypes.c_void_p(0x10002)
-    assert L.prism_step(ctypes.byref(d), *p, None) == E_ALIGN and "conv_state" in _err()
+    assert L.prism_step(ctypes.byref(d), *p, *ws) == E_ALIGN and "conv_state" in _err()
     bad = good_desc(T=1, L=9)
-    assert L.prism_step(ctypes.byref(bad), *([fake] * 12), None) == E_UNSUP
+    assert L.prism_step(ctypes.byref(bad), *([fake] * 12), *ws) == E_UNSUP
+    assert L.prism_step(ctypes.byref(d), *([fake] * 12), fake, ctypes.c_size_t(need - 1),
+                        None) == E_WS
+    assert P.step_workspace_bytes(good_desc(T=1, L=0)) == 0
