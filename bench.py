@@ -85,6 +85,7 @@ def algorithmic_counts(w):
     c["bias_reduce"] = (bh * ntiles * (L * D + 4 * D) * 4 + H * (L * D + 4 * D) * 4, 0)
     c["transpose_weights"] = (H * L * 4 * D * D * e, 0)
     c["refine_fwd_recompute"] = c["refine_fwd"]
+    c.update(decode_counts(w))
     peak_f = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
     out = {}
     for name, (byt, flo) in c.items():
@@ -93,6 +94,25 @@ def algorithmic_counts(w):
         out[name] = {"bytes": byt, "flops": flo, "bound": "mfma" if t_mfma > t_hbm else "hbm",
                      "floor_ms": max(t_hbm, t_mfma) * 1e3}
     return out
+
+
+DECODE_BATCH = 64   # sequences in flight in the decode-step measurement
+
+
+def decode_counts(w, batch=DECODE_BATCH):
+    """Algorithmic (bytes, FLOPs) per launch of the two decode-step kernels:
+    one token for each of `batch` sequences at the workload's head shape.
+    step_refine reads v, the ShortConv history, each head's weights and taps
+    once, and writes the L pairs; step_state reads and writes the fp32 state
+    (8 d^2 bytes per sequence and head), the history, and reads q, k, v,
+    alpha, beta and the pairs, and writes o."""
+    B, H, D, L = batch, w.H, w.d, w.L
+    e = 2 if w.dtype == "bf16" else 4
+    bh = B * H
+    refine = (bh * (D * e + 4 * D * e + 2 * L * D * e) + H * (L * (2 * D * D + D) + 4 * D) * e,
+              bh * L * 4 * D * D)
+    state = (bh * (8 * D * D + 4 * D * e + 2 * L * D * e + 2 * 4 * D * e + 8), bh * (4 + 2 * L) * D * D)
+    return {"step_refine": refine, "step_state": state}
 
 
 def measured_traffic():
@@ -119,7 +139,9 @@ _FAMILIES = [("refine_fwd_kernel", ["refine_fwd", "refine_fwd_recompute"]),
              ("wgrad_gemm_kernel", ["wgrad_gemm"]),
              ("wgrad_reduce_kernel", ["wgrad_reduce"]),
              ("bias_reduce_kernel", ["bias_reduce"]),
-             ("transpose_weights_kernel", ["transpose_weights"])]
+             ("transpose_weights_kernel", ["transpose_weights"]),
+             ("decode_refine_kernel", ["step_refine"]),
+             ("step_state_kernel", ["step_state"])]
 
 
 def _family(kernel_name):
@@ -204,6 +226,8 @@ def summarize_profiles(d, workload):
     lines = [f"# Kernel time and HBM traffic, workload {workload}",
              "",
              f"B={w.B} T={w.T} H={w.H} d_k=d_v={w.d} L={w.L} chunk={w.chunk} {w.dtype}; one forward + backward step.",
+             f"step_refine / step_state: the decode step (prism_step, one token) for B={DECODE_BATCH} sequences "
+             "at the same head shape, which bench.py also times.",
              "Made with (R = repository root on the GPU host; each rocprofv3 run on its own):",
              "", "```"] + cmds + ["```", "",
              f"HBM byte counters are scaled by the readings of a plain 1 GiB device copy: FETCH_SIZE x {f_factor:.3f}, "
@@ -273,7 +297,7 @@ def cpu_baseline(w, x, budget_s=15.0, backward=False):
                       f"{'fwd+bwd' if backward else 'fwd'}, float64, {t_used:.1f} s"}
 
 
-def decode_bench(w, steps, batch=64):
+def decode_bench(w, steps, batch=DECODE_BATCH):
     """The decode step (prism_step, one token per sequence) at the workload's
     head shape with `batch` sequences: event-timed calls, each kernel's own
     average from the library's event timer, and the HBM roofline of the
@@ -310,16 +334,16 @@ def decode_bench(w, steps, batch=64):
             P.step(*args, S=S, conv_state=cs)
         torch.cuda.synchronize()
     us = {n: tot * 1e3 / cnt for n, (tot, cnt) in kt.result.items()}
-    e = 2 if w.dtype == "bf16" else 4
-    nbytes = B * H * (8 * d * d + 4 * d * e + 2 * L * d * e + 2 * 4 * d * e + 8)
+    nbytes = decode_counts(w, B)["step_state"][0]
     gbps = nbytes / (us["step_state"] * 1e-6) / 1e9
     return {"workload": f"decode step B={B} H={H} d={d} L={L} {w.dtype}",
             "us_per_call": round(us_call, 2),
             "kernels_us": {n: round(x, 2) for n, x in us.items()},
             "tokens_per_s": round(B / (us_call * 1e-6), 1),
             "roofline": {"kernel": "step_state", "bound": "hbm", "achieved": round(gbps, 1),
-                         "peak": 8000.0, "unit": "GB/s", "frac": round(gbps / 8000.0, 4),
-                         "bytes_per_call": nbytes}}
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBS, 4),
+                         "algorithmic_bytes": nbytes,
+                         "traffic": measured_traffic().get("step_state")}}
 
 
 def main():

@@ -132,15 +132,17 @@ __global__ __launch_bounds__(64 * st_waves(D)) void step_state_kernel(
 
 // Refinement pairs of a decode step (one token per sequence), summary §2.2
 // Stages 1-2: a workgroup owns 64 sequences of one head and 64 of its output
-// features (one 16-feature MFMA tile per wave), so the pairs of all
-// sequences of a head come from MFMA products with the head's weights, read
-// once per 64 sequences.  The weights of two steps are in flight at a time;
-// the anchor of every feature (the MFMA operand) is formed from each
-// sequence's token and carried history; the chain runs in registers and the
-// pairs are stored from the accumulators, so the L steps need no barrier.
-constexpr int DR_NT = 256;
+// features; wave w takes the 16-feature MFMA tile w mod 4 for 32 of the
+// sequences (two waves per SIMD hide each other's latency).  The pairs of
+// all sequences of a head thus come from MFMA products with the head's
+// weights, read once per 64 sequences.  All loads of the set-up (weights of
+// two steps, taps, w_beta, tokens and histories) are issued before the first
+// barrier; the chain runs in registers and the pairs are stored from the
+// accumulators, so the L steps need no barrier.
+constexpr int DR_NW = 8;
+constexpr int DR_NT = DR_NW * WAVE;
 constexpr int DR_ROWS = 64;   // sequences per workgroup
-constexpr int DR_FG = 64;     // output features per workgroup (4 waves x 16)
+constexpr int DR_FG = 64;     // output features per workgroup (4 tiles of 16)
 
 template <typename E, int D, int ACT, int OFF>
 __global__ __launch_bounds__(DR_NT) void decode_refine_kernel(
@@ -154,6 +156,7 @@ __global__ __launch_bounds__(DR_NT) void decode_refine_kernel(
   constexpr int FG = D < DR_FG ? D : DR_FG;   // features of this workgroup
   constexpr int NFG = D / FG;
   constexpr int RW = FG + 4;                  // fp32 residual rows
+  constexpr int GT = 8;                       // threads per gate dot product
   typedef typename Mfma<E>::frag Frag;
   __shared__ __attribute__((aligned(16))) E ubuf[DR_ROWS * LD];
   __shared__ __attribute__((aligned(16))) E ulo[sizeof(E) == 2 ? DR_ROWS * LD : 16];
@@ -168,8 +171,9 @@ __global__ __launch_bounds__(DR_NT) void decode_refine_kernel(
   const int h = bid / (nbt * NFG);
   const int rest = bid % (nbt * NFG);
   const int b0 = (rest / NFG) * DR_ROWS, f0 = (rest % NFG) * FG;
-  const bool has = wave < FG / 16;            // this wave owns a feature tile
-  const int n = f0 / 16 + wave;               // its tile
+  const int ft = wave & 3, half = wave >> 2;  // feature tile, half of the sequences
+  const bool has = ft < FG / 16;              // this wave owns a feature tile
+  const int n = f0 / 16 + ft;
 
   Frag wp[2][NK], wk[2][NK];
   auto load_w = [&](int l, Frag (&p)[NK], Frag (&k)[NK]) {
@@ -188,99 +192,105 @@ __global__ __launch_bounds__(DR_NT) void decode_refine_kernel(
   for (int e = tid; e < L * (D / VN); e += DR_NT)
     st16(wbs + e * VN, ld16(wbeta + (long)h * L * D + e * VN));
   for (int e = tid; e < D * 4; e += DR_NT) ctp[e] = to_f(conv[(long)h * D * 4 + e]);
-  __syncthreads();
-
-  // anchor u of every feature (hi and lo parts, the MFMA operand) and the
-  // residual r = v - u of this workgroup's features; x_s = v_{-s}, where
-  // x_0 is the token and x_s (s >= 1) history row 4 - s
-  for (int e = tid; e < DR_ROWS * (D / VN); e += DR_NT) {
+  // tokens and histories of the thread's 16-byte chunks, x_s = v_{-s}:
+  // x_0 is the token, x_s (s >= 1) history row 4 - s
+  constexpr int NCHUNK = DR_ROWS * (D / VN);
+  constexpr int NCH = (NCHUNK + DR_NT - 1) / DR_NT;
+  uint4 xv[NCH][4 + OFF];
+#pragma unroll
+  for (int ci = 0; ci < NCH; ++ci) {
+    const int e = tid + ci * DR_NT;
     const int r = e / (D / VN), c = (e % (D / VN)) * VN;
     const int bs = b0 + r;
-    float x[4 + OFF][VN];
 #pragma unroll
-    for (int s = 0; s < 4 + OFF; ++s)
-#pragma unroll
-      for (int j = 0; j < VN; ++j) x[s][j] = 0.f;
-    if (bs < B) {
-      uint4 w = ld16(v + ((long)bs * H + h) * D + c);
-      const E* we = reinterpret_cast<const E*>(&w);
-#pragma unroll
-      for (int j = 0; j < VN; ++j) x[0][j] = to_f(we[j]);
+    for (int s = 0; s < 4 + OFF; ++s) xv[ci][s] = uint4{0u, 0u, 0u, 0u};
+    if (e < NCHUNK && bs < B) {
+      xv[ci][0] = ld16(v + ((long)bs * H + h) * D + c);
       if (hist) {
 #pragma unroll
-        for (int s = 1; s < 4 + OFF; ++s) {
-          w = ld16(hist + (((long)bs * 4 + 4 - s) * H + h) * D + c);
-#pragma unroll
-          for (int j = 0; j < VN; ++j) x[s][j] = to_f(we[j]);
-        }
+        for (int s = 1; s < 4 + OFF; ++s) xv[ci][s] = ld16(hist + (((long)bs * 4 + 4 - s) * H + h) * D + c);
       }
     }
+  }
+  __syncthreads();   // taps and w_beta in LDS
+
+  // anchor u of every feature (hi and lo parts, the MFMA operand) and the
+  // residual r = v - u of this workgroup's features
+#pragma unroll
+  for (int ci = 0; ci < NCH; ++ci) {
+    const int e = tid + ci * DR_NT;
+    if (e >= NCHUNK) break;
+    const int r = e / (D / VN), c = (e % (D / VN)) * VN;
 #pragma unroll
     for (int j = 0; j < VN; ++j) {
+      float x[4 + OFF];
+#pragma unroll
+      for (int s = 0; s < 4 + OFF; ++s) x[s] = to_f(reinterpret_cast<const E*>(&xv[ci][s])[j]);
       const float* tp = ctp + (c + j) * 4;
-      const float u = tp[0] * x[OFF][j] + tp[1] * x[OFF + 1][j] + tp[2] * x[OFF + 2][j] +
-                      tp[3] * x[OFF + 3][j];
+      const float u = tp[0] * x[OFF] + tp[1] * x[OFF + 1] + tp[2] * x[OFF + 2] + tp[3] * x[OFF + 3];
       const E uh = to_t<E>(u);
       ubuf[r * LD + c + j] = uh;
       if constexpr (sizeof(E) == 2) ulo[r * LD + c + j] = to_t<E>(u - to_f(uh));
-      if (c + j >= f0 && c + j < f0 + FG) rbuf[r * RW + c + j - f0] = x[0][j] - u;
+      if (c + j >= f0 && c + j < f0 + FG) rbuf[r * RW + c + j - f0] = x[0] - u;
     }
   }
   __syncthreads();
-  // step gates sigmoid(w_beta^(l) . u): four threads per sequence
+  // step gates sigmoid(w_beta^(l) . u): GT threads per sequence
   {
-    const int t = tid >> 2, part = tid & 3;
+    const int t = tid / GT, part = tid % GT;
     for (int l = 0; l < L; ++l) {
       float s = 0.f;
-      for (int c = part * VN; c < D; c += 4 * VN) {
+      for (int c = part * VN; c < D; c += GT * VN) {
         const uint4 ua = ld16(ubuf + t * LD + c), wa = ld16(wbs + l * D + c);
         const E* ue = reinterpret_cast<const E*>(&ua);
         const E* we = reinterpret_cast<const E*>(&wa);
 #pragma unroll
         for (int j = 0; j < VN; ++j) s += to_f(we[j]) * to_f(ue[j]);
       }
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
+#pragma unroll
+      for (int off = GT / 2; off > 0; off >>= 1) s += __shfl_xor(s, off);
       if (part == 0) gate[l][t] = sigmoidf(s);
     }
   }
   __syncthreads();
   if (!has) return;   // no barrier follows
 
-  // residual in the accumulator layout: (m, i) is sequence 16 m + 4 (lane >> 4) + i
-  const int fl = 16 * wave + (lane & 15);
-  float r[4][4];
+  // residual in the accumulator layout: (m, i) is sequence
+  // 32 half + 16 m + 4 (lane >> 4) + i
+  const int fl = 16 * ft + (lane & 15);
+  const int rb = 32 * half;
+  float r[2][4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m)
+  for (int m = 0; m < 2; ++m)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) r[m][i] = rbuf[(16 * m + 4 * (lane >> 4) + i) * RW + fl];
+    for (int i = 0; i < 4; ++i) r[m][i] = rbuf[(rb + 16 * m + 4 * (lane >> 4) + i) * RW + fl];
 
 #pragma unroll
   for (int l = 0; l < ST_LMAX; ++l) {
     if (l >= L) break;
     const int sl = l & 1;
-    f32x4 ap[4], ak[4];
+    f32x4 ap[2], ak[2];
 #pragma unroll
-    for (int m = 0; m < 4; ++m) ap[m] = ak[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < 2; ++m) ap[m] = ak[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
 #pragma unroll
-      for (int m = 0; m < 4; ++m) {
-        const Frag a = load_frag<E, true>(ubuf, LD, 16 * m, kk * KS, lane);
+      for (int m = 0; m < 2; ++m) {
+        const Frag a = load_frag<E, true>(ubuf, LD, rb + 16 * m, kk * KS, lane);
         ap[m] = Mfma<E>::mma(a, wp[sl][kk], ap[m]);
         ak[m] = Mfma<E>::mma(a, wk[sl][kk], ak[m]);
         if constexpr (sizeof(E) == 2) {
-          const Frag al = load_frag<E, true>(ulo, LD, 16 * m, kk * KS, lane);
+          const Frag al = load_frag<E, true>(ulo, LD, rb + 16 * m, kk * KS, lane);
           ap[m] = Mfma<E>::mma(al, wp[sl][kk], ap[m]);
         }
       }
     }
     if (l + 2 < L) load_w(l + 2, wp[sl], wk[sl]);
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int row = 16 * m + 4 * (lane >> 4) + i;
+        const int row = rb + 16 * m + 4 * (lane >> 4) + i;
         const float z = ap[m][i] * r[m][i];
         float dl;
         if constexpr (ACT == ACT_IDENTITY) dl = z;
