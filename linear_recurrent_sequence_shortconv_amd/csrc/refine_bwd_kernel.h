@@ -243,24 +243,34 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
     }
   };
 
-  // ---- forward chain: keep r^(l) for every step ----
-  float rs[LMAX][2][FPW][4];
+  // ---- forward quantities of every step.  Up to four steps: the gains
+  // p^(l) (they depend on u only; r stays r^(1) and the reverse replays the
+  // chain, VALU work instead of a second projection).  More steps: the
+  // residuals r^(l) (registers for L gains would spill), p^(l) projected again
+  // in the reverse. ----
+  constexpr bool REPLAY = LMAX <= 4;
+  f32x4 ps[REPLAY ? LMAX : 1][2][FPW];
+  float rs[REPLAY ? 1 : LMAX][2][FPW][4];
 #pragma unroll
   for (int l = 0; l < LMAX; ++l) {
     if (l >= L) break;
-    f32x4 p[2][FPW];
-    project(Wp + ((long)h * L + l) * D * D, p);
+    if constexpr (REPLAY) {
+      project(Wp + ((long)h * L + l) * D * D, ps[l]);
+    } else {
+      f32x4 p[2][FPW];
+      project(Wp + ((long)h * L + l) * D * D, p);
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+      for (int m = 0; m < 2; ++m)
 #pragma unroll
-      for (int nn = 0; nn < FPW; ++nn)
+        for (int nn = 0; nn < FPW; ++nn)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          rs[l][m][nn][i] = r[m][nn][i];
-          const float z = p[m][nn][i] * r[m][nn][i];
-          if constexpr (ACT == ACT_IDENTITY) r[m][nn][i] -= z;
-          else r[m][nn][i] -= gelu_erf(z);
-        }
+          for (int i = 0; i < 4; ++i) {
+            rs[l][m][nn][i] = r[m][nn][i];
+            const float z = p[m][nn][i] * r[m][nn][i];
+            if constexpr (ACT == ACT_IDENTITY) r[m][nn][i] -= z;
+            else r[m][nn][i] -= gelu_erf(z);
+          }
+    }
   }
 
   // ---- reverse: gw / gkk hold dW_l, dK_l of the current step ----
@@ -278,8 +288,40 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
 #pragma unroll
   for (int l = LMAX - 1; l >= 0; --l) {
     if (l >= L) continue;
+    // p^(l) and r^(l) of this step
     f32x4 p[2][FPW];
-    project(Wp + ((long)h * L + l) * D * D, p);
+    float rl[2][FPW][4];
+    if constexpr (REPLAY) {
+      // r^(l) by replaying the chain from r^(1): l steps of VALU work
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int nn = 0; nn < FPW; ++nn) {
+          p[m][nn] = ps[l][m][nn];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) rl[m][nn][i] = r[m][nn][i];
+        }
+#pragma unroll
+      for (int j = 0; j < l; ++j)
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int nn = 0; nn < FPW; ++nn)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float z = ps[j][m][nn][i] * rl[m][nn][i];
+              if constexpr (ACT == ACT_IDENTITY) rl[m][nn][i] -= z;
+              else rl[m][nn][i] -= gelu_erf(z);
+            }
+    } else {
+      project(Wp + ((long)h * L + l) * D * D, p);
+#pragma unroll
+      for (int m = 0; m < 2; ++m)
+#pragma unroll
+        for (int nn = 0; nn < FPW; ++nn)
+#pragma unroll
+          for (int i = 0; i < 4; ++i) rl[m][nn][i] = rs[l][m][nn][i];
+    }
     // GELU'(z) once per element; gate-gradient sum_f delta dw
     float dg_[2][FPW][4];
 #pragma unroll
@@ -293,7 +335,7 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
         for (int i = 0; i < 4; ++i) {
           const int t = 16 * m + 4 * (lane >> 4) + i;
           float dl;
-          const float z = p[m][nn][i] * rs[l][m][nn][i];
+          const float z = p[m][nn][i] * rl[m][nn][i];
           if constexpr (ACT == ACT_IDENTITY) {
             dl = z;
             dg_[m][nn][i] = 1.f;
@@ -332,7 +374,7 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
           const float ddl = gate[l][t] * gw[t * LW + f] - a_[m][nn][i];
           const float dzz = ddl * dg_[m][nn][i];
           a_[m][nn][i] += dzz * p[m][nn][i];
-          dpbuf[t * LD + f] = to_t<E>(dzz * rs[l][m][nn][i]);
+          dpbuf[t * LD + f] = to_t<E>(dzz * rl[m][nn][i]);
         }
       }
     __syncthreads();
@@ -406,39 +448,61 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
       }
     }
   __syncthreads();
-  // dv_s = dv_direct_s + a_s + sum_j conv[:, j] du_{s+o+j}   (owned s; s + o + j < T)
+  // dv_s = dv_direct_s + a_s + sum_j conv[:, j] du_{s+o+j}   (owned s; s + o + j < T):
+  // the lane's four tokens need seven consecutive du rows (rows >= nrow are zero)
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
+  for (int nn = 0; nn < FPW; ++nn) {
+    const int n = fq + 4 * nn;
+    if (!FT_OK(n)) continue;
+    const int f = 16 * n + (lane & 15);
+    float tp[4];
 #pragma unroll
-    for (int nn = 0; nn < FPW; ++nn) {
-      const int n = fq + 4 * nn;
-      if (!FT_OK(n)) continue;
-      const int f = 16 * n + (lane & 15);
+    for (int j = 0; j < 4; ++j) tp[j] = ctp[f * 4 + j];
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int t0m = 16 * m + 4 * (lane >> 4);
+      float w[7];
+#pragma unroll
+      for (int q = 0; q < 7; ++q) {
+        const int row = t0m + OFF + q;
+        w[q] = row < RB_TT ? dub[row * LW + f] : 0.f;
+      }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int t = 16 * m + 4 * (lane >> 4) + i;
+        const int t = t0m + i;
         if (t < own) {
           float val = dvd[m][nn][i] + a_[m][nn][i];
 #pragma unroll
-          for (int j = 0; j < 4; ++j)
-            if (t + OFF + j < nrow) val += ctp[f * 4 + j] * dub[(t + OFF + j) * LW + f];
+          for (int j = 0; j < 4; ++j) val += tp[j] * w[i + j];
           dpbuf[t * LD + f] = to_t<E>(val);
         }
       }
     }
-  // dconv partial: sum over owned t of du_t v_{t-o-j}  (vbuf row t + HL - o - j)
+  }
+  // dconv partial: sum over owned t of du_t v_{t-o-j} (vbuf row t + 3 - j);
+  // each token group takes a contiguous range, so the four v rows slide
   constexpr int NG = RB_NT / D;   // token groups; red is [NG][D][4]
+  constexpr int TPG = (OWN + NG - 1) / NG;
   {
     const int f = tid % D, grp = tid / D;
+    const int tb = grp * TPG;
+    auto vrow = [&](int row) { return row < RB_TT + HL ? to_f(vbuf[row * D + f]) : 0.f; };
     float acc[4] = {0.f, 0.f, 0.f, 0.f};
+    float x0 = vrow(tb), x1 = vrow(tb + 1), x2 = vrow(tb + 2);
 #pragma unroll
-    for (int k = 0; k < (OWN + NG - 1) / NG; ++k) {
-      const int t = grp + k * NG;
+    for (int k = 0; k < TPG; ++k) {
+      const int t = tb + k;
+      const float x3 = vrow(t + 3);
       if (t < own) {
         const float d_ = dub[t * LW + f];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[j] += d_ * to_f(vbuf[(t + HL - OFF - j) * D + f]);
+        acc[0] += d_ * x3;
+        acc[1] += d_ * x2;
+        acc[2] += d_ * x1;
+        acc[3] += d_ * x0;
       }
+      x0 = x1;
+      x1 = x2;
+      x2 = x3;
     }
 #pragma unroll
     for (int j = 0; j < 4; ++j) red[(grp * D + f) * 4 + j] = acc[j];
