@@ -112,6 +112,18 @@ typedef struct {
  * q and k are used as given (callers normalise them if they wish).  With
  * L = 0, Wk, Wp, wbeta, conv (and their gradients) may be NULL.
  *
+ * Packed batches (variable lengths).  With cu_seqlens (a device array of
+ * B + 1 int32 offsets, 4-byte aligned; NULL = dense) the token tensors q, k,
+ * v, o, dO, dq, dk, dv are [N, H, d] and alpha, beta, dalpha, dbeta [N, H],
+ * N = cu_seqlens[B], sequence b being tokens cu_seqlens[b] ..
+ * cu_seqlens[b+1] - 1; desc->T is then the longest length (it sizes the
+ * workspaces).  Required: cu_seqlens[0] = 0, non-decreasing, every length
+ * <= desc->T (lengths of 0 are allowed: S_T = S0).  The offsets are read on
+ * the device only, so these conditions are the caller's to meet; longer
+ * sequences are cut at T.  conv_hist, S0, ST and their gradients stay per
+ * sequence.  A packed batch computes exactly what each sequence would
+ * compute alone.
+ *
  * Continuation.  A sequence split over several calls gives the same result
  * as one call when each call after the first receives S0 = the previous ST
  * and conv_hist = the previous call's conv_hist_out (summary §2.1: the state
@@ -130,8 +142,9 @@ prism_status prism_backward_workspace(const prism_desc* desc, size_t* bytes);
 prism_status prism_forward(const prism_desc* desc, const void* q, const void* k, const void* v,
                            const float* alpha, const float* beta, const void* Wk, const void* Wp,
                            const void* wbeta, const void* conv, const float* S0,
-                           const void* conv_hist, void* o, float* ST, void* conv_hist_out,
-                           void* workspace, size_t workspace_bytes, hipStream_t stream);
+                           const void* conv_hist, const int* cu_seqlens, void* o, float* ST,
+                           void* conv_hist_out, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream);
 
 /* Backward pass: gradients of <dO, o> + <dST, S_T> with respect to every
  * input.  Stateless: recomputes what it needs from the forward inputs.
@@ -142,11 +155,11 @@ prism_status prism_forward(const prism_desc* desc, const void* q, const void* k,
 prism_status prism_backward(const prism_desc* desc, const void* q, const void* k, const void* v,
                             const float* alpha, const float* beta, const void* Wk, const void* Wp,
                             const void* wbeta, const void* conv, const float* S0,
-                            const void* conv_hist, const void* dO, const float* dST, void* dq,
-                            void* dk, void* dv, float* dalpha, float* dbeta, float* dWk,
-                            float* dWp, float* dwbeta, float* dconv, float* dS0,
-                            float* dconv_hist, void* workspace, size_t workspace_bytes,
-                            hipStream_t stream);
+                            const void* conv_hist, const int* cu_seqlens, const void* dO,
+                            const float* dST, void* dq, void* dk, void* dv, float* dalpha,
+                            float* dbeta, float* dWk, float* dWp, float* dwbeta, float* dconv,
+                            float* dS0, float* dconv_hist, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream);
 
 /* Training pair (saved intermediates).  prism_forward_train computes what
  * prism_forward computes and also keeps, in the caller-owned `saved` buffer,
@@ -169,18 +182,19 @@ prism_status prism_saved_bytes(const prism_desc* desc, size_t* bytes);
 prism_status prism_forward_train(const prism_desc* desc, const void* q, const void* k,
                                  const void* v, const float* alpha, const float* beta,
                                  const void* Wk, const void* Wp, const void* wbeta,
-                                 const void* conv, const float* S0, const void* conv_hist, void* o,
-                                 float* ST, void* conv_hist_out, void* saved, size_t saved_bytes,
-                                 void* workspace, size_t workspace_bytes, hipStream_t stream);
+                                 const void* conv, const float* S0, const void* conv_hist,
+                                 const int* cu_seqlens, void* o, float* ST, void* conv_hist_out,
+                                 void* saved, size_t saved_bytes, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
 prism_status prism_backward_train(const prism_desc* desc, const void* q, const void* k,
                                   const void* v, const float* alpha, const float* beta,
                                   const void* Wk, const void* Wp, const void* wbeta,
                                   const void* conv, const float* S0, const void* conv_hist,
-                                  const void* saved, size_t saved_bytes, const void* dO,
-                                  const float* dST, void* dq, void* dk, void* dv, float* dalpha,
-                                  float* dbeta, float* dWk, float* dWp, float* dwbeta,
-                                  float* dconv, float* dS0, float* dconv_hist, void* workspace,
-                                  size_t workspace_bytes, hipStream_t stream);
+                                  const int* cu_seqlens, const void* saved, size_t saved_bytes,
+                                  const void* dO, const float* dST, void* dq, void* dk, void* dv,
+                                  float* dalpha, float* dbeta, float* dWk, float* dWp,
+                                  float* dwbeta, float* dconv, float* dS0, float* dconv_hist,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* Recurrent form: the layer token by token (summary §2.1 S_t = S_{t-1} A_t
  * + B_t with §2.2's B_t, then o_t = S_t q_t), for the desc->T tokens of each

@@ -150,7 +150,8 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
     const E* __restrict__ WkT, const E* __restrict__ Sc, const E* __restrict__ dSnT,
     float* __restrict__ dQt, float* __restrict__ dUs, float* __restrict__ dWks,
     float* __restrict__ dKs, float* __restrict__ dKls, float* __restrict__ dWls,
-    float* __restrict__ dgs, int B, int T, int H, int L, int NC, int Tp) {
+    float* __restrict__ dgs, int B, int T, int H, int L, int NC, int Tp,
+    const int* __restrict__ cu) {
   typedef CB1Lds<E, D, C> LY;
   constexpr int NW = CB_NW, NT = CB_NT;
   constexpr int LR = LY::LR, LD2 = LY::LD2;
@@ -173,9 +174,9 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
   const int c = bid % NC, bh = bid / NC;
   const int h = bh % H, b = bh / H;
   const int tb = c * C;
-  const int nval = min(C, T - tb);
+  const int nval = min(C, seq_len(cu, b, T) - tb);
   const long ts = (long)H * D;
-  const long row0 = ((long)b * T + tb) * H + h;
+  const long row0 = (seq_start(cu, b, T) + tb) * H + h;
   const long cidx = (long)bh * NC + c;
 
   for (int e = tid; e < NW * C + NW; e += NT) ddw[e] = 0.f;
@@ -424,7 +425,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
     const float* __restrict__ dUs, const float* __restrict__ dWks, const float* __restrict__ dKs,
     const float* __restrict__ dgs, float* __restrict__ dVp, float* __restrict__ dqp,
     float* __restrict__ dkp, float* __restrict__ dgp, float* __restrict__ dbeta, int B, int T,
-    int H, int L, int NC, int Tp) {
+    int H, int L, int NC, int Tp, const int* __restrict__ cu) {
   typedef CB2Lds<E, D, C> LY;
   constexpr int NW = CB_NW, NT = CB_NT;
   constexpr int LR = LY::LR, LT = LY::LT, LA = LY::LA;
@@ -448,9 +449,9 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
   const int c = bid % NC, bh = bid / NC;
   const int h = bh % H, b = bh / H;
   const int tb = c * C;
-  const int nval = min(C, T - tb);
+  const int nval = min(C, seq_len(cu, b, T) - tb);
   const long ts = (long)H * D;
-  const long row0 = ((long)b * T + tb) * H + h;
+  const long row0 = (seq_start(cu, b, T) + tb) * H + h;
   const long cidx = (long)bh * NC + c;
   typedef Tiling<C, D, NW> TLD;
   typedef Tiling<C, C, NW> TLC;
@@ -882,7 +883,8 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
     const float* __restrict__ dVp, const float* __restrict__ dqp, const float* __restrict__ dkp,
     const float* __restrict__ dgp, float* __restrict__ dKl, float* __restrict__ dWl,
     E* __restrict__ dq, E* __restrict__ dk, E* __restrict__ dv,
-    float* __restrict__ dalpha, int B, int T, int H, int L, int NC, int Tp) {
+    float* __restrict__ dalpha, int B, int T, int H, int L, int NC, int Tp,
+    const int* __restrict__ cu) {
   typedef CB3Lds<E, D, C> LY;
   constexpr int NW = CB_NW, NT = CB_NT;
   constexpr int LR = LY::LR, LT = LY::LT;
@@ -908,9 +910,9 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
   const int c = bid % NC, bh = bid / NC;
   const int h = bh % H, b = bh / H;
   const int tb = c * C;
-  const int nval = min(C, T - tb);
+  const int nval = min(C, seq_len(cu, b, T) - tb);
   const long ts = (long)H * D;
-  const long row0 = ((long)b * T + tb) * H + h;
+  const long row0 = (seq_start(cu, b, T) + tb) * H + h;
   const long cidx = (long)bh * NC + c;
   typedef Tiling<C, C, NW> TLC;
   const bool actC = TLC::active(wave);
@@ -1162,16 +1164,16 @@ static hipError_t cbwd_launch_dc(const Dims& d, const ChunkBwdArgs<E>& a, int st
     if (stage == 0)
       hipLaunchKernelGGL((chunk_bwd_state_kernel<E, D, C>), dim3(nblk), dim3(CB_NT), 0, s, a.k, a.dO,
                          a.alpha, a.Kl, a.Wl, a.UT, a.WkT, a.Sc, a.dSnT, a.dQt, a.dUs, a.dWks,
-                         a.dKs, a.dKl, a.dWl, a.dgs, d.B, d.T, d.H, d.L, d.NC, d.Tp);
+                         a.dKs, a.dKl, a.dWl, a.dgs, d.B, d.T, d.H, d.L, d.NC, d.Tp, d.cu);
     else if (stage == 1)
       hipLaunchKernelGGL((chunk_bwd_solve_kernel<E, D, C>), dim3(nblk), dim3(CB_NT), 0, s, a.q,
                          a.k, a.v, a.dO, a.alpha, a.beta, a.Kl, a.Wl, a.dQt, a.dUs, a.dWks, a.dKs,
                          a.dgs, a.dVp, a.dqp, a.dkp, a.dgp, a.dbeta, d.B, d.T, d.H, d.L, d.NC,
-                         d.Tp);
+                         d.Tp, d.cu);
     else
       hipLaunchKernelGGL((chunk_bwd_pairs_kernel<E, D, C>), dim3(nblk), dim3(CB_NT), 0, s, a.q,
                          a.k, a.dO, a.alpha, a.Kl, a.Wl, a.dVp, a.dqp, a.dkp, a.dgp, a.dKl, a.dWl,
-                         a.dq, a.dk, a.dv, a.dalpha, d.B, d.T, d.H, d.L, d.NC, d.Tp);
+                         a.dq, a.dk, a.dv, a.dalpha, d.B, d.T, d.H, d.L, d.NC, d.Tp, d.cu);
     return hipGetLastError();
   }
 }

@@ -77,7 +77,7 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
     const E* __restrict__ Wl, const E* __restrict__ dO, E* __restrict__ Mt, float* __restrict__ HT,
     E* __restrict__ Qt, float* __restrict__ Oloc, float* __restrict__ gCo,
     float* __restrict__ ET, E* __restrict__ UTo, E* __restrict__ WkTo, int B, int T, int H, int L,
-    int NC, int Tp) {
+    int NC, int Tp, const int* __restrict__ cu) {
   typedef ChunkLds<E, D, C> LY;
   constexpr int NW = CF_NW, NT = CF_NT;
   constexpr int LR = LY::LR, LT = LY::LT, LA = LY::LA;
@@ -109,8 +109,8 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
     const int c = bid % NC, bh = bid / NC;
     const int h = bh % H, b = bh / H;
     const int tb = c * C;
-    const int nval = min(C, T - tb);
-    const long row0 = ((long)b * T + tb) * H + h;
+    const int nval = min(C, seq_len(cu, b, T) - tb);
+    const long row0 = (seq_start(cu, b, T) + tb) * H + h;
     if (L > 0) {
       kn.load(Kl + (long)bh * L * Tp * D + (long)tb * D, D, C, tid);
       wn.load(Wl + (long)bh * L * Tp * D + (long)tb * D, D, C, tid);
@@ -136,8 +136,8 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
   const int c = bid % NC, bh = bid / NC;
   const int h = bh % H, b = bh / H;
   const int tb = c * C;
-  const int nval = min(C, T - tb);
-  const long row0 = ((long)b * T + tb) * H + h;
+  const int nval = min(C, seq_len(cu, b, T) - tb);
+  const long row0 = (seq_start(cu, b, T) + tb) * H + h;
   const E* vc = v + row0 * D;
   const E* Klb = Kl + (long)bh * L * Tp * D + (long)tb * D;
   const E* Wlb = Wl + (long)bh * L * Tp * D + (long)tb * D;
@@ -377,7 +377,8 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
 // training forward kept: the reverse state pass's additive term.
 template <typename E, int D, int C>
 __global__ __launch_bounds__(CF_NT) void et_kernel(const E* __restrict__ Qt, const E* __restrict__ dO,
-                                                   float* __restrict__ ET, int B, int T, int H, int NC) {
+                                                   float* __restrict__ ET, int B, int T, int H, int NC,
+                                                   const int* __restrict__ cu) {
   constexpr int NW = CF_NW, NT = CF_NT;
   constexpr int LR = ldpad<E>(D);
   __shared__ __attribute__((aligned(16))) E Qs[C * LR];
@@ -388,9 +389,9 @@ __global__ __launch_bounds__(CF_NT) void et_kernel(const E* __restrict__ Qt, con
   const int c = bid % NC, bh = bid / NC;
   const int h = bh % H, b = bh / H;
   const int tb = c * C;
-  const int nval = min(C, T - tb);
+  const int nval = min(C, seq_len(cu, b, T) - tb);
   const long ts = (long)H * D;
-  const long row0 = ((long)b * T + tb) * H + h;
+  const long row0 = (seq_start(cu, b, T) + tb) * H + h;
   const long cidx = (long)bh * NC + c;
   g2s_rows<E, C, D, NT>(Qs, LR, Qt + cidx * C * D, D, C, tid);
   g2s_rows<E, C, D, NT>(Os, LR, dO + row0 * D, ts, nval, tid);
@@ -409,7 +410,7 @@ template <typename E, int D, int C>
 static hipError_t et_launch_dc(const Dims& d, const E* Qt, const E* dO, float* ET, hipStream_t s) {
   if constexpr (sizeof(E) == 4 && D * C > 2048) return hipErrorInvalidValue;   // fp32 envelope
   hipLaunchKernelGGL((et_kernel<E, D, C>), dim3(d.B * d.H * d.NC), dim3(CF_NT), 0, s, Qt, dO, ET,
-                     d.B, d.T, d.H, d.NC);
+                     d.B, d.T, d.H, d.NC, d.cu);
   return hipGetLastError();
 }
 
@@ -449,12 +450,12 @@ static hipError_t chunk_launch_dc(const Dims& d, const E* q, const E* k, const E
     hipLaunchKernelGGL((chunk_fwd_kernel<E, D, C, true>),
                        dim3(D >= 128 ? persistent_grid(chunk_fwd_kernel<E, D, C, true>, CF_NT, nblk) : nblk),
                        dim3(CF_NT), 0, s, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC,
-                       ET, UT, WkT, d.B, d.T, d.H, d.L, d.NC, d.Tp);
+                       ET, UT, WkT, d.B, d.T, d.H, d.L, d.NC, d.Tp, d.cu);
   else
     hipLaunchKernelGGL((chunk_fwd_kernel<E, D, C, false>),
                        dim3(D >= 128 ? persistent_grid(chunk_fwd_kernel<E, D, C, false>, CF_NT, nblk) : nblk),
                        dim3(CF_NT), 0, s, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC,
-                       ET, UT, WkT, d.B, d.T, d.H, d.L, d.NC, d.Tp);
+                       ET, UT, WkT, d.B, d.T, d.H, d.L, d.NC, d.Tp, d.cu);
   return hipGetLastError();
 }
 

@@ -171,6 +171,15 @@ prism_status check_ptr(const void* p, const char* name, bool required) {
   return PRISM_OK;
 }
 
+// Packed batches: the offsets must be a 4-byte aligned device array; their
+// values are the caller's contract (read on the device only).
+prism_status check_cu(const int* cu, prism::Dims* d) {
+  if (cu && (reinterpret_cast<uintptr_t>(cu) & 3u))
+    return fail(PRISM_ERR_ALIGN, "cu_seqlens is not 4-byte aligned");
+  d->cu = cu;
+  return PRISM_OK;
+}
+
 #define CHECK_PTR(p, req)                              \
   do {                                                 \
     prism_status st_ = check_ptr((p), #p, (req));      \
@@ -465,13 +474,15 @@ prism_status check_buffer(const void* p, size_t have, size_t need, const char* w
 prism_status forward_entry(const prism_desc* desc, const void* q, const void* k, const void* v,
                            const float* alpha, const float* beta, const void* Wk, const void* Wp,
                            const void* wbeta, const void* conv, const float* S0,
-                           const void* conv_hist, void* o, float* ST, void* conv_hist_out,
-                           void* saved, size_t saved_bytes, bool train, void* workspace,
-                           size_t workspace_bytes, hipStream_t stream) {
+                           const void* conv_hist, const int* cu_seqlens, void* o, float* ST,
+                           void* conv_hist_out, void* saved, size_t saved_bytes, bool train,
+                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
   try {
     g_err.clear();
     prism::Dims d;
     prism_status st = check_desc(desc, &d);
+    if (st != PRISM_OK) return st;
+    st = check_cu(cu_seqlens, &d);
     if (st != PRISM_OK) return st;
     const bool refine = d.L > 0;
     CHECK_PTR(q, true);
@@ -508,15 +519,18 @@ prism_status forward_entry(const prism_desc* desc, const void* q, const void* k,
 prism_status backward_entry(const prism_desc* desc, const void* q, const void* k, const void* v,
                             const float* alpha, const float* beta, const void* Wk, const void* Wp,
                             const void* wbeta, const void* conv, const float* S0,
-                            const void* conv_hist, const void* saved, size_t saved_bytes,
-                            bool train, const void* dO, const float* dST, void* dq, void* dk,
-                            void* dv, float* dalpha, float* dbeta, float* dWk, float* dWp,
-                            float* dwbeta, float* dconv, float* dS0, float* dconv_hist,
-                            void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                            const void* conv_hist, const int* cu_seqlens, const void* saved,
+                            size_t saved_bytes, bool train, const void* dO, const float* dST,
+                            void* dq, void* dk, void* dv, float* dalpha, float* dbeta, float* dWk,
+                            float* dWp, float* dwbeta, float* dconv, float* dS0,
+                            float* dconv_hist, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
   try {
     g_err.clear();
     prism::Dims d;
     prism_status st = check_desc(desc, &d);
+    if (st != PRISM_OK) return st;
+    st = check_cu(cu_seqlens, &d);
     if (st != PRISM_OK) return st;
     const bool refine = d.L > 0;
     CHECK_PTR(q, true);
@@ -569,47 +583,51 @@ extern "C" {
 prism_status prism_forward(const prism_desc* desc, const void* q, const void* k, const void* v,
                            const float* alpha, const float* beta, const void* Wk, const void* Wp,
                            const void* wbeta, const void* conv, const float* S0,
-                           const void* conv_hist, void* o, float* ST, void* conv_hist_out,
-                           void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return forward_entry(desc, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, conv_hist, o, ST,
-                       conv_hist_out, nullptr, 0, false, workspace, workspace_bytes, stream);
+                           const void* conv_hist, const int* cu_seqlens, void* o, float* ST,
+                           void* conv_hist_out, void* workspace, size_t workspace_bytes,
+                           hipStream_t stream) {
+  return forward_entry(desc, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, conv_hist, cu_seqlens,
+                       o, ST, conv_hist_out, nullptr, 0, false, workspace, workspace_bytes, stream);
 }
 
 prism_status prism_forward_train(const prism_desc* desc, const void* q, const void* k,
                                  const void* v, const float* alpha, const float* beta,
                                  const void* Wk, const void* Wp, const void* wbeta,
-                                 const void* conv, const float* S0, const void* conv_hist, void* o,
-                                 float* ST, void* conv_hist_out, void* saved, size_t saved_bytes,
-                                 void* workspace, size_t workspace_bytes, hipStream_t stream) {
-  return forward_entry(desc, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, conv_hist, o, ST,
-                       conv_hist_out, saved, saved_bytes, true, workspace, workspace_bytes, stream);
+                                 const void* conv, const float* S0, const void* conv_hist,
+                                 const int* cu_seqlens, void* o, float* ST, void* conv_hist_out,
+                                 void* saved, size_t saved_bytes, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  return forward_entry(desc, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, conv_hist, cu_seqlens,
+                       o, ST, conv_hist_out, saved, saved_bytes, true, workspace, workspace_bytes,
+                       stream);
 }
 
 prism_status prism_backward(const prism_desc* desc, const void* q, const void* k, const void* v,
                             const float* alpha, const float* beta, const void* Wk, const void* Wp,
                             const void* wbeta, const void* conv, const float* S0,
-                            const void* conv_hist, const void* dO, const float* dST, void* dq,
-                            void* dk, void* dv, float* dalpha, float* dbeta, float* dWk,
-                            float* dWp, float* dwbeta, float* dconv, float* dS0,
-                            float* dconv_hist, void* workspace, size_t workspace_bytes,
-                            hipStream_t stream) {
-  return backward_entry(desc, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, conv_hist, nullptr,
-                        0, false, dO, dST, dq, dk, dv, dalpha, dbeta, dWk, dWp, dwbeta, dconv,
-                        dS0, dconv_hist, workspace, workspace_bytes, stream);
+                            const void* conv_hist, const int* cu_seqlens, const void* dO,
+                            const float* dST, void* dq, void* dk, void* dv, float* dalpha,
+                            float* dbeta, float* dWk, float* dWp, float* dwbeta, float* dconv,
+                            float* dS0, float* dconv_hist, void* workspace,
+                            size_t workspace_bytes, hipStream_t stream) {
+  return backward_entry(desc, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, conv_hist,
+                        cu_seqlens, nullptr, 0, false, dO, dST, dq, dk, dv, dalpha, dbeta, dWk,
+                        dWp, dwbeta, dconv, dS0, dconv_hist, workspace, workspace_bytes, stream);
 }
 
 prism_status prism_backward_train(const prism_desc* desc, const void* q, const void* k,
                                   const void* v, const float* alpha, const float* beta,
                                   const void* Wk, const void* Wp, const void* wbeta,
                                   const void* conv, const float* S0, const void* conv_hist,
-                                  const void* saved, size_t saved_bytes, const void* dO,
-                                  const float* dST, void* dq, void* dk, void* dv, float* dalpha,
-                                  float* dbeta, float* dWk, float* dWp, float* dwbeta,
-                                  float* dconv, float* dS0, float* dconv_hist, void* workspace,
-                                  size_t workspace_bytes, hipStream_t stream) {
-  return backward_entry(desc, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, conv_hist, saved,
-                        saved_bytes, true, dO, dST, dq, dk, dv, dalpha, dbeta, dWk, dWp, dwbeta,
-                        dconv, dS0, dconv_hist, workspace, workspace_bytes, stream);
+                                  const int* cu_seqlens, const void* saved, size_t saved_bytes,
+                                  const void* dO, const float* dST, void* dq, void* dk, void* dv,
+                                  float* dalpha, float* dbeta, float* dWk, float* dWp,
+                                  float* dwbeta, float* dconv, float* dS0, float* dconv_hist,
+                                  void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return backward_entry(desc, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, conv_hist,
+                        cu_seqlens, saved, saved_bytes, true, dO, dST, dq, dk, dv, dalpha, dbeta,
+                        dWk, dWp, dwbeta, dconv, dS0, dconv_hist, workspace, workspace_bytes,
+                        stream);
 }
 
 prism_status prism_step_workspace(const prism_desc* desc, size_t* bytes) {

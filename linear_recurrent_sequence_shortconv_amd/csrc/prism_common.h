@@ -519,6 +519,14 @@ __device__ inline void gelu_and_grad(float z, float& g, float& dg) {
 }
 __device__ inline float sigmoidf(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
+// Sequence b of a batch: its first token and its length.  A dense batch
+// (cu == nullptr) has B sequences of T tokens; a packed one lists offsets
+// cu[0..B], sequence b being tokens cu[b] .. cu[b+1] - 1 (at most T of them).
+__device__ inline long seq_start(const int* cu, int b, int T) { return cu ? (long)cu[b] : (long)b * T; }
+__device__ inline int seq_len(const int* cu, int b, int T) {
+  return cu ? max(0, min(cu[b + 1] - cu[b], T)) : T;
+}
+
 // XCD-aware block order: consecutive hardware dispatch slots go round-robin
 // over the 8 XCDs; return a logical block id such that the blocks one XCD
 // receives are contiguous in logical order (neighbouring tiles share L2).

@@ -18,6 +18,10 @@ constexpr int ACT_GELU = 0, ACT_IDENTITY = 1;
 struct Dims {
   int B, T, H, D, L, C, NC, Tp;
   int act, off;
+  // packed batch: sequence b is tokens cu[b] .. cu[b+1]-1 of the [*, H, D]
+  // token tensors (device array of B + 1 offsets, at most T tokens each);
+  // nullptr: dense [B, T, H, D]
+  const int* cu = nullptr;
 };
 
 // Every launcher enqueues on `stream` and returns hipGetLastError().

@@ -45,7 +45,8 @@ struct RowChunk {
   static constexpr int NU = NG * VPR;
   static constexpr int PER = (NU + WG_NT - 1) / WG_NT;
   uint4 v[PER][RG];
-  __device__ inline void load(const X* base, long rowstride_b, int Tp, int T, long n0, long nend, int tid) {
+  __device__ inline void load(const X* base, long rowstride_b, int Tp, int T, const int* cu, long n0,
+                              long nend, int tid) {
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const int u = tid + p * WG_NT;
@@ -56,7 +57,7 @@ struct RowChunk {
         const long n = n0 + r0 + q;
         if (u < NU && n < nend) {
           const long bb = n / Tp, t = n % Tp;
-          if (t < T) v[p][q] = ld16(base + bb * rowstride_b + t * D + c);
+          if (t < seq_len(cu, (int)bb, T)) v[p][q] = ld16(base + bb * rowstride_b + t * D + c);
         }
       }
     }
@@ -91,7 +92,8 @@ __global__ __launch_bounds__(WG_NT) void wgrad_gemm_kernel(const float* __restri
                                                            const E* __restrict__ dP,
                                                            const E* __restrict__ u,
                                                            float* __restrict__ part, int B, int H,
-                                                           int L, int T, int Tp, int NS) {
+                                                           int L, int T, int Tp, int NS,
+                                                           const int* __restrict__ cu) {
   constexpr int LTT = ldpad<E>(WG_ROWS);
   __shared__ __attribute__((aligned(16))) E Xt[D * LTT];
   __shared__ __attribute__((aligned(16))) E Ut[D * LTT];
@@ -114,9 +116,9 @@ __global__ __launch_bounds__(WG_NT) void wgrad_gemm_kernel(const float* __restri
   RowChunk<E, E, D> xe, uu;
   // software pipeline: chunk n0 + 64 is fetched while chunk n0 is multiplied
   if (n_begin < n_end) {
-    if (which == 0) xf.load(xk, xs_b, Tp, T, n_begin, n_end, tid);
-    else xe.load(xp, xs_b, Tp, T, n_begin, n_end, tid);
-    uu.load(ub, us_b, Tp, T, n_begin, n_end, tid);
+    if (which == 0) xf.load(xk, xs_b, Tp, T, cu, n_begin, n_end, tid);
+    else xe.load(xp, xs_b, Tp, T, cu, n_begin, n_end, tid);
+    uu.load(ub, us_b, Tp, T, cu, n_begin, n_end, tid);
   }
   for (long n0 = n_begin; n0 < n_end; n0 += WG_ROWS) {
     if (which == 0) xf.store_t(Xt, LTT, tid);
@@ -125,9 +127,9 @@ __global__ __launch_bounds__(WG_NT) void wgrad_gemm_kernel(const float* __restri
     __syncthreads();
     const long nn = n0 + WG_ROWS;
     if (nn < n_end) {
-      if (which == 0) xf.load(xk, xs_b, Tp, T, nn, n_end, tid);
-      else xe.load(xp, xs_b, Tp, T, nn, n_end, tid);
-      uu.load(ub, us_b, Tp, T, nn, n_end, tid);
+      if (which == 0) xf.load(xk, xs_b, Tp, T, cu, nn, n_end, tid);
+      else xe.load(xp, xs_b, Tp, T, cu, nn, n_end, tid);
+      uu.load(ub, us_b, Tp, T, cu, nn, n_end, tid);
     }
     gemm_acc<E, D, D, WG_ROWS, WG_NW, true, true>(acc, Xt, LTT, Ut, LTT, wave, lane);
     __syncthreads();
@@ -214,7 +216,7 @@ static hipError_t refine_bwd_d(const Dims& d, const RefineBwdArgs<E>& a, int NS,
                    : launch_refine_bwd_main<E, ACT_GELU, 0>(d, a, s);
     case 2:
       hipLaunchKernelGGL((wgrad_gemm_kernel<E, D>), dim3(d.H * d.L * 2 * NS), dim3(WG_NT), 0, s,
-                         a.dKl, a.dP, a.u, a.part, d.B, d.H, d.L, d.T, d.Tp, NS);
+                         a.dKl, a.dP, a.u, a.part, d.B, d.H, d.L, d.T, d.Tp, NS, d.cu);
       break;
     case 3: {
       const unsigned grid = (unsigned)((2 * nw + 255) / 256 < 8192 ? (2 * nw + 255) / 256 : 8192);

@@ -65,7 +65,7 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
     const float* __restrict__ dKl, const float* __restrict__ dWl, const float* __restrict__ dvdir,
     E* __restrict__ uo, E* __restrict__ dPo, E* __restrict__ dv, float* __restrict__ dwbp,
     float* __restrict__ dcp, float* __restrict__ dhist, int B, int T, int H, int L, int Tp,
-    int ntiles) {
+    int ntiles, const int* __restrict__ cu) {
   constexpr int LD = ldpad<E>(D);
   constexpr int LW = D + 4;               // fp32 rows: staggers rows 4 apart across banks
   constexpr int NFT = D / 16;
@@ -98,10 +98,11 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
   const int rest = bid % (B * ntiles);
   const int b = rest / ntiles, tile = rest % ntiles;
   const int t0 = tile * OWN;
-  const int own = min(OWN, T - t0);         // owned tokens (>= 1)
-  const int nrow = min(RB_TT, T - t0);      // computed tokens that exist
+  const int Tb = seq_len(cu, b, T);        // this sequence's length
+  const int own = min(OWN, Tb - t0);        // owned tokens (<= 0 past the end)
+  const int nrow = min(RB_TT, Tb - t0);     // computed tokens that exist
   const long tok_stride = (long)H * D;
-  const E* vseq = v + ((long)b * T * H + h) * D;
+  const E* vseq = v + (seq_start(cu, b, T) * H + h) * D;
   const long bh = (long)b * H + h;
   const E* ch = conv + (long)h * D * 4;
   const int tile_id = (int)(bh * ntiles + tile);
@@ -113,7 +114,7 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
     const int r = e / (D / VN), c = (e % (D / VN)) * VN;
     const int t = t0 - HL + r;
     uint4 x = {0u, 0u, 0u, 0u};
-    if (t >= 0 && t < T) x = ld16(vseq + t * tok_stride + c);
+    if (t >= 0 && t < Tb) x = ld16(vseq + t * tok_stride + c);
     else if (t < 0 && hist) x = ld16(hist + (((long)b * 4 + 4 + t) * H + h) * D + c);
     st16(vbuf + r * D + c, x);
   }
@@ -508,7 +509,7 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
     for (int j = 0; j < 4; ++j) red[(grp * D + f) * 4 + j] = acc[j];
   }
   __syncthreads();
-  s2g_rows<E, RB_TT, D, RB_NT>(dv + ((long)b * T + t0) * tok_stride + (long)h * D, tok_stride,
+  s2g_rows<E, RB_TT, D, RB_NT>(dv + (seq_start(cu, b, T) + t0) * tok_stride + (long)h * D, tok_stride,
                                dpbuf, LD, own, tid);
   if (tid < D) {
 #pragma unroll
@@ -542,7 +543,7 @@ hipError_t launch_refine_bwd_main(const Dims& d, const RefineBwdArgs<E>& a, hipS
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3(ntiles * d.B * d.H), dim3(RB_NT), 0, s, a.v, a.hist, a.conv, a.Wp,
                        a.WkT, a.WpT, a.wbeta, a.dKl, a.dWl, a.dvdir, a.u, a.dP, a.dv, a.dwbp, a.dcp,
-                       a.dhist, d.B, d.T, d.H, d.L, d.Tp, ntiles);
+                       a.dhist, d.B, d.T, d.H, d.L, d.Tp, ntiles, d.cu);
     return hipGetLastError();
   };
   auto by_l = [&](auto dd) {

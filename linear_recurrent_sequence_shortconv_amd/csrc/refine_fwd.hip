@@ -30,7 +30,8 @@ template <typename E, int D, int ACT, int OFF>
 __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
     const E* __restrict__ v, const E* __restrict__ hist, const E* __restrict__ conv,
     const E* __restrict__ Wk, const E* __restrict__ Wp, const E* __restrict__ wbeta,
-    E* __restrict__ Kl, E* __restrict__ Wl, int B, int T, int H, int L, int Tp) {
+    E* __restrict__ Kl, E* __restrict__ Wl, int B, int T, int H, int L, int Tp,
+    const int* __restrict__ cu) {
   constexpr int LD = ldpad<E>(D);
   constexpr int NFT = D / 16;                          // feature tiles
   constexpr int FPW = (NFT + RF_NW - 1) / RF_NW;       // feature tiles per wave
@@ -64,7 +65,8 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
   const int b = rest / ntiles, tile = rest % ntiles;
   const int t0 = tile * RF_TT;
   const long tok_stride = (long)H * D;
-  const E* vseq = v + ((long)b * T * H + h) * D;       // row t at vseq + t * tok_stride
+  const E* vseq = v + (seq_start(cu, b, T) * H + h) * D;   // row t at vseq + t * tok_stride
+  const int Tb = seq_len(cu, b, T);
 
   // ---- w_beta rows of this head (L x D) ----
   for (int e = tid; e < L * (D / VN); e += RF_NT)
@@ -75,7 +77,7 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
     const int r = e / (D / VN), c = (e % (D / VN)) * VN;
     const int t = t0 - HL + r;
     uint4 x = {0u, 0u, 0u, 0u};
-    if (t >= 0 && t < T) x = ld16(vseq + t * tok_stride + c);
+    if (t >= 0 && t < Tb) x = ld16(vseq + t * tok_stride + c);
     else if (t < 0 && hist) x = ld16(hist + (((long)b * 4 + 4 + t) * H + h) * D + c);
     st16(vbuf + r * D + c, x);
   }
@@ -111,7 +113,7 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
       for (int i = 0; i < 4; ++i) {
         const int t = 16 * m + 4 * (lane >> 4) + i;
         float u = 0.f, val = 0.f;
-        if (FT_OK(n) && t0 + t < T) {
+        if (FT_OK(n) && t0 + t < Tb) {
 #pragma unroll
           for (int j = 0; j < 4; ++j) u += taps[j] * to_f(vbuf[(t + HL - OFF - j) * D + f]);
           val = to_f(vbuf[(t + HL) * D + f]) - u;
@@ -237,7 +239,7 @@ static hipError_t refine_launch_d(const Dims& d, const E* v, const E* hist, cons
   const int nblk = ntiles * d.B * d.H;
   auto go = [&](auto kern) {
     hipLaunchKernelGGL(kern, dim3(nblk), dim3(RF_NT), 0, s, v, hist, conv, Wk, Wp, wbeta, Kl, Wl,
-                       d.B, d.T, d.H, d.L, d.Tp);
+                       d.B, d.T, d.H, d.L, d.Tp, d.cu);
   };
   if (d.act == ACT_IDENTITY)
     d.off ? go(refine_fwd_kernel<E, D, ACT_IDENTITY, 1>) : go(refine_fwd_kernel<E, D, ACT_IDENTITY, 0>);

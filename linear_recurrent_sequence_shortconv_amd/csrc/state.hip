@@ -207,7 +207,7 @@ __global__ __launch_bounds__(OF_NT) void out_fwd_kernel(const E* __restrict__ Sc
                                                         const E* __restrict__ Qt,
                                                         const float* __restrict__ Oloc,
                                                         E* __restrict__ o, int B, int T, int H,
-                                                        int NC) {
+                                                        int NC, const int* __restrict__ cu) {
   constexpr int LR = ldpad<E>(D);
   __shared__ __attribute__((aligned(16))) E Ss[D * LR];
   __shared__ __attribute__((aligned(16))) E Qs[C * LR];
@@ -224,8 +224,8 @@ __global__ __launch_bounds__(OF_NT) void out_fwd_kernel(const E* __restrict__ Sc
   a.zero();
   gemm_acc<E, D, C, D, OF_NW, true, true>(a, Ss, LR, Qs, LR, wave, lane);
   const float* Oc = Oloc + cidx * C * D;
-  const int nval = min(C, T - c * C);
-  E* oc = o + (((long)b * T + c * C) * H + h) * D;
+  const int nval = min(C, seq_len(cu, b, T) - c * C);
+  E* oc = o + ((seq_start(cu, b, T) + c * C) * H + h) * D;
   for_tiles(a, wave, lane, [&](int f0, int t, const f32x4& x) {
     if (t < nval) {
       const f32x4 ol = *reinterpret_cast<const f32x4*>(Oc + (long)t * D + f0);
@@ -240,7 +240,7 @@ static hipError_t out_launch_dc(const Dims& d, const E* Sc, const E* Qt, const f
                                 hipStream_t s) {
   if constexpr (sizeof(E) == 4 && D * C > 2048) return hipErrorInvalidValue;   // fp32 envelope
   hipLaunchKernelGGL((out_fwd_kernel<E, D, C>), dim3(d.B * d.H * d.NC), dim3(OF_NT), 0, s, Sc, Qt,
-                     Oloc, o, d.B, d.T, d.H, d.NC);
+                     Oloc, o, d.B, d.T, d.H, d.NC, d.cu);
   return hipGetLastError();
 }
 

@@ -311,15 +311,17 @@ __global__ __launch_bounds__(DR_NT) void decode_refine_kernel(
 // be hist itself.
 template <typename E>
 __global__ void conv_state_kernel(const E* __restrict__ v, const E* hist, E* out, int B, int T,
-                                  int HD) {
+                                  int HD, const int* __restrict__ cu) {
   const long n = (long)B * HD;
   for (long e = blockIdx.x * (long)blockDim.x + threadIdx.x; e < n; e += (long)gridDim.x * blockDim.x) {
     const long b = e / HD, hf = e % HD;
+    const long s0 = seq_start(cu, (int)b, T);
+    const int Tb = seq_len(cu, (int)b, T);
     E x[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int t = T - 4 + r;
-      x[r] = t >= 0 ? v[(b * T + t) * HD + hf] : hist ? hist[(b * 4 + 4 + t) * HD + hf] : to_t<E>(0.f);
+      const int t = Tb - 4 + r;
+      x[r] = t >= 0 ? v[(s0 + t) * HD + hf] : hist ? hist[(b * 4 + 4 + t) * HD + hf] : to_t<E>(0.f);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) out[(b * 4 + r) * HD + hf] = x[r];
@@ -340,7 +342,7 @@ template <typename E>
 hipError_t launch_conv_state(const Dims& d, const E* v, const E* hist, E* out, hipStream_t s) {
   const long n = (long)d.B * d.H * d.D;
   hipLaunchKernelGGL((conv_state_kernel<E>), dim3(grid_for(n)), dim3(256), 0, s, v, hist, out, d.B,
-                     d.T, d.H * d.D);
+                     d.T, d.H * d.D, d.cu);
   return hipGetLastError();
 }
 

@@ -46,14 +46,14 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         L.prism_forward_workspace.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(ctypes.c_size_t)]
         L.prism_backward_workspace.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(ctypes.c_size_t)]
-        # inputs q..conv, S0, conv_hist (11); forward outputs o, ST, conv_hist_out (3);
-        # backward: dO, dST, then 11 gradients (dq..dconv, dS0, dconv_hist)
-        L.prism_forward.argtypes = [ctypes.POINTER(Desc)] + [_P] * 14 + [_P, ctypes.c_size_t, _P]
-        L.prism_backward.argtypes = [ctypes.POINTER(Desc)] + [_P] * 24 + [_P, ctypes.c_size_t, _P]
+        # inputs q..conv, S0, conv_hist, cu_seqlens (12); forward outputs o, ST,
+        # conv_hist_out (3); backward: dO, dST, then 11 gradients (dq..dconv, dS0, dconv_hist)
+        L.prism_forward.argtypes = [ctypes.POINTER(Desc)] + [_P] * 15 + [_P, ctypes.c_size_t, _P]
+        L.prism_backward.argtypes = [ctypes.POINTER(Desc)] + [_P] * 25 + [_P, ctypes.c_size_t, _P]
         L.prism_saved_bytes.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(ctypes.c_size_t)]
-        L.prism_forward_train.argtypes = ([ctypes.POINTER(Desc)] + [_P] * 14
+        L.prism_forward_train.argtypes = ([ctypes.POINTER(Desc)] + [_P] * 15
                                           + [_P, ctypes.c_size_t, _P, ctypes.c_size_t, _P])
-        L.prism_backward_train.argtypes = ([ctypes.POINTER(Desc)] + [_P] * 11 + [_P, ctypes.c_size_t]
+        L.prism_backward_train.argtypes = ([ctypes.POINTER(Desc)] + [_P] * 12 + [_P, ctypes.c_size_t]
                                            + [_P] * 13 + [_P, ctypes.c_size_t, _P])
         L.prism_step_workspace.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(ctypes.c_size_t)]
         L.prism_step.argtypes = [ctypes.POINTER(Desc)] + [_P] * 12 + [_P, ctypes.c_size_t, _P]
@@ -108,12 +108,30 @@ def _req(t, name, dtype, device):
         raise ValueError(f"{name} must be contiguous")
 
 
-def _desc_from(q, v, Wk, chunk, activation="gelu", conv_offset=0):
-    B, T, H, dk = q.shape
+def _desc_from(q, v, Wk, chunk, activation="gelu", conv_offset=0, cu_seqlens=None,
+               max_seqlen=None):
+    """Descriptor of a dense batch (q [B,T,H,dk]) or, with cu_seqlens, of a
+    packed one (q [N,H,dk], B = len(cu_seqlens) - 1, T = max_seqlen)."""
+    if cu_seqlens is None:
+        B, T, H, dk = q.shape
+    else:
+        if max_seqlen is None:
+            raise ValueError("max_seqlen is required with cu_seqlens")
+        _, H, dk = q.shape
+        B, T = cu_seqlens.numel() - 1, int(max_seqlen)
     dv = v.shape[-1]
     L = 0 if Wk is None else Wk.shape[1]
     return make_desc(B, T, H, dk, dv, L, chunk, _dtype_code(q), activation=activation,
                      conv_offset=conv_offset)
+
+
+def _req_cu(cu, q):
+    if cu is None:
+        return
+    if cu.dtype != torch.int32 or cu.device != q.device or not cu.is_contiguous() or cu.dim() != 1:
+        raise ValueError("cu_seqlens must be a contiguous 1-D int32 tensor on q's device")
+    if q.dim() != 3:
+        raise ValueError("with cu_seqlens, q, k, v are packed [N, H, d]")
 
 
 def _workspace(nbytes, device):
@@ -155,8 +173,9 @@ def _validate_inputs(q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0):
         _req(S0, "S0", torch.float32, dev)
 
 
-def _req_hist(h, name, q, v):
-    B, _, H, _ = v.shape
+def _req_hist(h, name, q, v, B=None):
+    B = v.shape[0] if B is None else B
+    H = v.shape[-2]
     _req(h, name, q.dtype, q.device)
     if tuple(h.shape) != (B, 4, H, v.shape[-1]):
         raise ValueError(f"{name}: expected shape {(B, 4, H, v.shape[-1])}, got {tuple(h.shape)}")
@@ -164,7 +183,7 @@ def _req_hist(h, name, q, v):
 
 def forward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None, S0=None, chunk=64,
             workspace=None, saved=None, activation="gelu", conv_offset=0, conv_hist=None,
-            conv_hist_out=None):
+            conv_hist_out=None, cu_seqlens=None, max_seqlen=None):
     """PRISM layer forward.  Returns (o, S_T).
 
     q, k [B,T,H,dk], v [B,T,H,dv] (bf16 or fp32); alpha, beta [B,T,H] fp32;
@@ -174,18 +193,20 @@ def forward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None, S0=No
     conv_offset: 0 (tap j on v_{t-j}) or 1 (tap j on v_{t-1-j}).
     conv_hist [B,4,H,dv] (v's dtype): the four values of v before the
     sequence (None: zeros); conv_hist_out (same shape, may be conv_hist)
-    receives them for the next call.
+    receives them for the next call.  cu_seqlens (int32 [B+1] on the device)
+    with max_seqlen packs B sequences of different lengths: q, k, v are then
+    [N, H, d], alpha, beta [N, H].
     With `saved` (a buffer from saved_buffer()) this is the training forward
     (prism_forward_train): the buffer then holds what backward(saved=...)
     needs.
     """
     _validate_inputs(q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0)
-    desc = _desc_from(q, v, Wk, chunk, activation, conv_offset)
+    _req_cu(cu_seqlens, q)
+    desc = _desc_from(q, v, Wk, chunk, activation, conv_offset, cu_seqlens, max_seqlen)
+    B, H, dk, dv = desc.B, desc.H, desc.dk, desc.dv
     for name, h in (("conv_hist", conv_hist), ("conv_hist_out", conv_hist_out)):
         if h is not None:
-            _req_hist(h, name, q, v)
-    B, T, H, dk = q.shape
-    dv = v.shape[-1]
+            _req_hist(h, name, q, v, B)
     o = torch.empty_like(v)
     ST = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
     need = forward_workspace_bytes(desc)
@@ -197,29 +218,30 @@ def forward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None, S0=No
     if saved is None:
         _check(lib().prism_forward(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
                                    _ptr(beta), _ptr(Wk), _ptr(Wp), _ptr(wbeta), _ptr(conv),
-                                   _ptr(S0), _ptr(conv_hist), _ptr(o), _ptr(ST),
+                                   _ptr(S0), _ptr(conv_hist), _ptr(cu_seqlens), _ptr(o), _ptr(ST),
                                    _ptr(conv_hist_out), _ptr(ws), ctypes.c_size_t(ws.numel()),
                                    ctypes.c_void_p(stream)))
     else:
         _check(lib().prism_forward_train(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
                                          _ptr(beta), _ptr(Wk), _ptr(Wp), _ptr(wbeta), _ptr(conv),
-                                         _ptr(S0), _ptr(conv_hist), _ptr(o), _ptr(ST),
-                                         _ptr(conv_hist_out), _ptr(saved),
+                                         _ptr(S0), _ptr(conv_hist), _ptr(cu_seqlens), _ptr(o),
+                                         _ptr(ST), _ptr(conv_hist_out), _ptr(saved),
                                          ctypes.c_size_t(saved.numel()), _ptr(ws),
                                          ctypes.c_size_t(ws.numel()), ctypes.c_void_p(stream)))
     return o, ST
 
 
-def saved_buffer(q, v, Wk=None, chunk=64):
+def saved_buffer(q, v, Wk=None, chunk=64, cu_seqlens=None, max_seqlen=None):
     """A 256-byte aligned device buffer for the training pair (uint8 view);
     its size does not depend on the activation or the tap offset."""
-    desc = _desc_from(q, v, Wk, chunk)
+    desc = _desc_from(q, v, Wk, chunk, cu_seqlens=cu_seqlens, max_seqlen=max_seqlen)
     return _workspace(saved_bytes(desc), q.device)[1]
 
 
 def backward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None, S0=None, dO=None,
              dST=None, chunk=64, need_dS0=False, workspace=None, saved=None, activation="gelu",
-             conv_offset=0, conv_hist=None, need_dconv_hist=False):
+             conv_offset=0, conv_hist=None, need_dconv_hist=False, cu_seqlens=None,
+             max_seqlen=None):
     """Gradients of <dO, o> + <dST, S_T> with respect to every input.
 
     Returns a dict: dq, dk, dv (input dtype), dalpha, dbeta (fp32), and for
@@ -228,18 +250,19 @@ def backward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None, S0=N
     prism_backward_train, which skips the forward recompute.  activation,
     conv_offset and conv_hist as in forward() (and equal to the forward's
     with `saved`); need_dconv_hist adds dconv_hist [B,4,H,dv] fp32.
+    cu_seqlens and max_seqlen as in forward().
     """
     _validate_inputs(q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0)
     if dO is None:
         raise ValueError("dO is required")
     _req(dO, "dO", q.dtype, q.device)
+    _req_cu(cu_seqlens, q)
+    desc = _desc_from(q, v, Wk, chunk, activation, conv_offset, cu_seqlens, max_seqlen)
+    B, H, dk, dv_ = desc.B, desc.H, desc.dk, desc.dv
     if conv_hist is not None:
-        _req_hist(conv_hist, "conv_hist", q, v)
+        _req_hist(conv_hist, "conv_hist", q, v, B)
     if dST is not None:
         _req(dST, "dST", torch.float32, q.device)
-    desc = _desc_from(q, v, Wk, chunk, activation, conv_offset)
-    B, T, H, dk = q.shape
-    dv_ = v.shape[-1]
     dev = q.device
     g = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
          "dalpha": torch.empty_like(alpha), "dbeta": torch.empty_like(beta)}
@@ -262,7 +285,7 @@ def backward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None, S0=N
              _ptr(g.get("dWk")), _ptr(g.get("dWp")), _ptr(g.get("dwbeta")), _ptr(g.get("dconv")),
              _ptr(g.get("dS0")), _ptr(g.get("dconv_hist")))
     inputs = (_ptr(q), _ptr(k), _ptr(v), _ptr(alpha), _ptr(beta), _ptr(Wk), _ptr(Wp),
-              _ptr(wbeta), _ptr(conv), _ptr(S0), _ptr(conv_hist))
+              _ptr(wbeta), _ptr(conv), _ptr(S0), _ptr(conv_hist), _ptr(cu_seqlens))
     if saved is None:
         _check(lib().prism_backward(ctypes.byref(desc), *inputs, _ptr(dO), _ptr(dST), *grads,
                                     _ptr(ws), ctypes.c_size_t(ws.numel()), ctypes.c_void_p(stream)))

@@ -51,7 +51,7 @@ def _fwd(desc, ptrs=None, ws=None, nbytes=0):
     """Call prism_forward with fake (never dereferenced) 16-byte aligned pointers."""
     L = P.lib()
     fake = ctypes.c_void_p(0x10000)
-    p = [fake] * 14 if ptrs is None else ptrs
+    p = [fake] * 15 if ptrs is None else ptrs
     return L.prism_forward(ctypes.byref(desc) if desc is not None else None, *p,
                            ws if ws is not None else fake, ctypes.c_size_t(nbytes), None)
 
@@ -114,35 +114,40 @@ def test_variant_fields():
 
 
 def test_null_desc_and_pointers():
-    # forward pointers: q k v alpha beta Wk Wp wbeta conv S0 conv_hist o ST conv_hist_out
+    # forward pointers: q k v alpha beta Wk Wp wbeta conv S0 conv_hist cu_seqlens o ST
+    # conv_hist_out
     assert _fwd(None) == E_NULL
     fake = ctypes.c_void_p(0x10000)
     for i, name in enumerate(["q", "k", "v", "alpha", "beta", "Wk", "Wp", "wbeta", "conv"]):
-        p = [fake] * 14
+        p = [fake] * 15
         p[i] = None
         assert _fwd(good_desc(), p) == E_NULL, name
         assert name in _err()
     # with L = 0 the weights may be NULL (then the workspace check fails next)
-    p = [fake] * 14
+    p = [fake] * 15
     p[5] = p[6] = p[7] = p[8] = None
     assert _fwd(good_desc(L=0), p, nbytes=0) == E_WS
-    # output o is required; S0, conv_hist, ST and conv_hist_out are optional
-    p = [fake] * 14
-    p[11] = None
+    # output o is required; S0, conv_hist, cu_seqlens, ST and conv_hist_out are optional
+    p = [fake] * 15
+    p[12] = None
     assert _fwd(good_desc(), p) == E_NULL
-    p = [fake] * 14
-    p[9] = p[10] = p[12] = p[13] = None
+    p = [fake] * 15
+    p[9] = p[10] = p[11] = p[13] = p[14] = None
     assert _fwd(good_desc(), p, nbytes=0) == E_WS
-    # the history buffers are checked for alignment like every tensor
-    for i, name in ((10, "conv_hist"), (13, "conv_hist_out")):
-        p = [fake] * 14
-        p[i] = ctypes.c_void_p(0x10004)
+    # the history buffers are checked for alignment like every tensor; the
+    # packed-batch offsets need 4 bytes
+    for i, name in ((10, "conv_hist"), (14, "conv_hist_out"), (11, "cu_seqlens")):
+        p = [fake] * 15
+        p[i] = ctypes.c_void_p(0x10002)
         assert _fwd(good_desc(), p) == E_ALIGN and name in _err()
+    p = [fake] * 15
+    p[11] = ctypes.c_void_p(0x10004)   # 4-byte aligned offsets pass
+    assert _fwd(good_desc(), p, nbytes=0) == E_WS
 
 
 def test_alignment_and_workspace():
     fake = ctypes.c_void_p(0x10000)
-    p = [fake] * 14
+    p = [fake] * 15
     p[2] = ctypes.c_void_p(0x10008)
     assert _fwd(good_desc(), p) == E_ALIGN and "v" in _err()
     assert _fwd(good_desc(), ws=ctypes.c_void_p(0x10010), nbytes=1 << 40) == E_ALIGN
@@ -150,15 +155,16 @@ def test_alignment_and_workspace():
     need = P.forward_workspace_bytes(d)
     assert _fwd(d, nbytes=need - 1) == E_WS and str(need) in _err()
     L = P.lib()
-    p = [fake] * 24
+    p = [fake] * 25
     assert L.prism_backward(ctypes.byref(d), *p, fake, ctypes.c_size_t(0), None) == E_WS
-    p[11] = None   # dO (order: q k v alpha beta Wk Wp wbeta conv S0 conv_hist dO dST dq ...)
+    # order: q k v alpha beta Wk Wp wbeta conv S0 conv_hist cu_seqlens dO dST dq ...
+    p[12] = None   # dO
     assert L.prism_backward(ctypes.byref(d), *p, fake, ctypes.c_size_t(1 << 40), None) == E_NULL
-    p = [fake] * 24
-    p[13] = None   # dq
+    p = [fake] * 25
+    p[14] = None   # dq
     assert L.prism_backward(ctypes.byref(d), *p, fake, ctypes.c_size_t(1 << 40), None) == E_NULL
-    p = [fake] * 24
-    p[10] = p[22] = p[23] = None   # conv_hist, dS0, dconv_hist are optional
+    p = [fake] * 25
+    p[10] = p[11] = p[23] = p[24] = None   # conv_hist, cu_seqlens, dS0, dconv_hist are optional
     assert L.prism_backward(ctypes.byref(d), *p, fake, ctypes.c_size_t(0), None) == E_WS
 
 
@@ -190,7 +196,7 @@ def test_training_pair_checks():
     assert need > 0
     fake = ctypes.c_void_p(0x10000)
     ws_ok = ctypes.c_size_t(1 << 40)
-    p14 = [fake] * 14
+    p14 = [fake] * 15
     # saved NULL, misaligned, too small
     assert L.prism_forward_train(ctypes.byref(d), *p14, None, ctypes.c_size_t(need), fake, ws_ok,
                                  None) == E_WS
@@ -200,7 +206,7 @@ def test_training_pair_checks():
     assert L.prism_forward_train(ctypes.byref(d), *p14, fake, ctypes.c_size_t(need - 1), fake, ws_ok,
                                  None) == E_WS
     assert str(need) in _err()
-    p11 = [fake] * 11   # q k v alpha beta Wk Wp wbeta conv S0 conv_hist
+    p11 = [fake] * 12   # q k v alpha beta Wk Wp wbeta conv S0 conv_hist cu_seqlens
     p13 = [fake] * 13   # dO dST dq dk dv dalpha dbeta dWk dWp dwbeta dconv dS0 dconv_hist
     assert L.prism_backward_train(ctypes.byref(d), *p11, None, ctypes.c_size_t(need), *p13, fake,
                                   ws_ok, None) == E_WS
