@@ -346,6 +346,56 @@ def decode_bench(w, steps, batch=DECODE_BATCH):
                          "traffic": measured_traffic().get("step_state")}}
 
 
+def varlen_bench(steps, B=64, H=4, d=64, L=2, chunk=64, tmax=200, seed=3):
+    """Packed batch of ragged histories at the sequential-recommendation head
+    shape (forward, as that configuration is quoted): lengths uniform in
+    [tmax / 10, tmax], seeded.  Real tokens per second of the packed call and
+    of the same sequences padded to tmax in a dense call."""
+    import numpy as np
+    import torch
+    from linear_recurrent_sequence_shortconv_amd import prism as P
+    from linear_recurrent_sequence_shortconv_amd.workloads import make_inputs
+
+    rng = np.random.default_rng(seed)
+    lengths = rng.integers(tmax // 10, tmax + 1, size=B)
+    N = int(lengths.sum())
+    x = make_inputs(1, N, H, d, L, "bf16", seed=seed)
+    bf, f32 = torch.bfloat16, torch.float32
+    dev = lambda a, t=bf: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(t)
+    packed = (dev(x["q"][0]), dev(x["k"][0]), dev(x["v"][0]), dev(x["alpha"][0], f32),
+              dev(x["beta"][0], f32)) + tuple(dev(x[n]) for n in ("Wk", "Wp", "wbeta", "conv"))
+    cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lengths)]).astype(np.int32)).to("cuda")
+    # the same sequences, right-padded to tmax (alpha = 1, beta = 0 past the end)
+    cpu = np.concatenate([[0], np.cumsum(lengths)])
+    def pad(a, fill):
+        out = np.full((B, tmax) + a.shape[2:], fill, dtype=np.float64)
+        for b in range(B):
+            out[b, :lengths[b]] = a[0, cpu[b]:cpu[b + 1]]
+        return out
+    dense = (dev(pad(x["q"], 0.0)), dev(pad(x["k"], 0.0)), dev(pad(x["v"], 0.0)),
+             dev(pad(x["alpha"], 1.0), f32), dev(pad(x["beta"], 0.0), f32)) + packed[5:]
+
+    def timed(fn):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(steps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / steps
+
+    ms_p = timed(lambda: P.forward(*packed, chunk=chunk, cu_seqlens=cu, max_seqlen=tmax))
+    ms_d = timed(lambda: P.forward(*dense, chunk=chunk))
+    return {"workload": f"packed histories B={B} H={H} d={d} L={L} bf16, lengths U[{tmax // 10},{tmax}] "
+                        f"(mean {lengths.mean():.0f}), forward",
+            "tokens": N, "ms_packed": round(ms_p, 4), "ms_padded_dense": round(ms_d, 4),
+            "tokens_per_s_packed": round(N / (ms_p * 1e-3), 1),
+            "tokens_per_s_padded": round(N / (ms_d * 1e-3), 1)}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -356,6 +406,7 @@ def main():
     ap.add_argument("--forward-only", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
+    ap.add_argument("--no-varlen", action="store_true", help="skip the packed-batch measurement")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write profiles/ summaries from the rocprofv3 runs under DIR and exit")
     args = ap.parse_args()
@@ -483,6 +534,7 @@ def main():
                               frac=r["frac"], floor_ms=r["roofline_floor_ms"])
 
     decode = None if args.no_decode else decode_bench(w, args.steps)
+    varlen = None if args.no_varlen else varlen_bench(args.steps)
 
     tokens = w.B * w.T
     value = tokens / (ms * 1e-3)
@@ -514,6 +566,7 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kernels,
         "decode": decode,
+        "varlen": varlen,
     }
     print(json.dumps(line))
 

@@ -177,6 +177,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
   const int nval = min(C, seq_len(cu, b, T) - tb);
   const long ts = (long)H * D;
   const long row0 = (seq_start(cu, b, T) + tb) * H + h;
+  if (nval <= 0) return;   // past the end of a packed sequence: nothing to do
   const long cidx = (long)bh * NC + c;
 
   for (int e = tid; e < NW * C + NW; e += NT) ddw[e] = 0.f;
@@ -452,6 +453,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
   const int nval = min(C, seq_len(cu, b, T) - tb);
   const long ts = (long)H * D;
   const long row0 = (seq_start(cu, b, T) + tb) * H + h;
+  if (nval <= 0) return;   // past the end of a packed sequence: nothing to do
   const long cidx = (long)bh * NC + c;
   typedef Tiling<C, D, NW> TLD;
   typedef Tiling<C, C, NW> TLC;
@@ -913,6 +915,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
   const int nval = min(C, seq_len(cu, b, T) - tb);
   const long ts = (long)H * D;
   const long row0 = (seq_start(cu, b, T) + tb) * H + h;
+  if (nval <= 0) return;   // past the end of a packed sequence: nothing to do
   const long cidx = (long)bh * NC + c;
   typedef Tiling<C, C, NW> TLC;
   const bool actC = TLC::active(wave);

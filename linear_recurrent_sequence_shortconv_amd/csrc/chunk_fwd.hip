@@ -138,6 +138,12 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
   const int tb = c * C;
   const int nval = min(C, seq_len(cu, b, T) - tb);
   const long row0 = (seq_start(cu, b, T) + tb) * H + h;
+  // past the end of a packed sequence no pass reads the chunk: a one-chunk
+  // workgroup leaves; a persistent one computes its identity map (all tokens
+  // padding), since a skip path here costs registers on every chunk
+  if constexpr (!PERSIST) {
+    if (nval <= 0) return;
+  }
   const E* vc = v + row0 * D;
   const E* Klb = Kl + (long)bh * L * Tp * D + (long)tb * D;
   const E* Wlb = Wl + (long)bh * L * Tp * D + (long)tb * D;
@@ -392,6 +398,7 @@ __global__ __launch_bounds__(CF_NT) void et_kernel(const E* __restrict__ Qt, con
   const int nval = min(C, seq_len(cu, b, T) - tb);
   const long ts = (long)H * D;
   const long row0 = (seq_start(cu, b, T) + tb) * H + h;
+  if (nval <= 0) return;   // past the end of a packed sequence
   const long cidx = (long)bh * NC + c;
   g2s_rows<E, C, D, NT>(Qs, LR, Qt + cidx * C * D, D, C, tid);
   g2s_rows<E, C, D, NT>(Os, LR, dO + row0 * D, ts, nval, tid);

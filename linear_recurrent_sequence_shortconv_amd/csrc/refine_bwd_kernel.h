@@ -101,6 +101,17 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
   const int Tb = seq_len(cu, b, T);        // this sequence's length
   const int own = min(OWN, Tb - t0);        // owned tokens (<= 0 past the end)
   const int nrow = min(RB_TT, Tb - t0);     // computed tokens that exist
+  if (own <= 0) {
+    // past the end of a packed sequence: zero partial sums (and a zero
+    // history gradient for an empty sequence), nothing else
+    const int tile_id_ = (int)(((long)b * H + h) * ntiles + tile);
+    for (int e = tid; e < L * D; e += RB_NT) dwbp[(long)tile_id_ * L * D + e] = 0.f;
+    for (int e = tid; e < 4 * D; e += RB_NT) dcp[(long)tile_id_ * D * 4 + e] = 0.f;
+    if (tile == 0 && dhist)
+      for (int e = tid; e < 4 * D; e += RB_NT)
+        dhist[(((long)b * 4 + e / D) * H + h) * D + e % D] = 0.f;
+    return;
+  }
   const long tok_stride = (long)H * D;
   const E* vseq = v + (seq_start(cu, b, T) * H + h) * D;
   const long bh = (long)b * H + h;

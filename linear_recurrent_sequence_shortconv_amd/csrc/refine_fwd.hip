@@ -67,6 +67,10 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
   const long tok_stride = (long)H * D;
   const E* vseq = v + (seq_start(cu, b, T) * H + h) * D;   // row t at vseq + t * tok_stride
   const int Tb = seq_len(cu, b, T);
+  // a tile past the end of a packed sequence lies past its last chunk (tiles
+  // are multiples of the chunk length): nothing reads it.  Never in a dense
+  // batch, whose tiles all start before T.
+  if (t0 >= Tb) return;
 
   // ---- w_beta rows of this head (L x D) ----
   for (int e = tid; e < L * (D / VN); e += RF_NT)

@@ -39,7 +39,8 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
                                                            const float* __restrict__ gC,
                                                            E* __restrict__ Xc, float* __restrict__ fin,
                                                            int B, int H, int NC, int transposed,
-                                                           int reverse) {
+                                                           int reverse, int T, int C,
+                                                           const int* __restrict__ cu) {
   constexpr int LS = ldpad<E>(D);
   constexpr int VN = 16 / sizeof(E);
   constexpr int NV = D * D / VN;                       // 16-byte vectors of Bm_c
@@ -69,7 +70,10 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
           S.v[i][j][r] = init[((long)bh * D + rb0 + m0 + 16 * i + rl + r) * D + n0 + 16 * j + cl];
   }
   (void)reverse;   // the direction is the template parameter REV
-  auto chunk_of = [&](int step) { return REV ? NC - 1 - step : step; };
+  // chunks of this sequence (all NC in a dense batch; a packed sequence stops
+  // at its own end, and the chunks after it are never read)
+  const int ncb = (seq_len(cu, bh / H, T) + C - 1) / C;
+  auto chunk_of = [&](int step) { return REV ? ncb - 1 - step : step; };
   uint4 mst[PER];                       // next Bm, staged through registers into LDS
   f32x4 addn[TL::RM][TL::RN];           // next AddT^T block
   float egn = 0.f;                      // next decay
@@ -101,9 +105,11 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
       }
     }
   };
-  fetch(0);
-  stage(Mb[0]);
-  for (int step = 0; step < NC; ++step) {
+  if (ncb > 0) {
+    fetch(0);
+    stage(Mb[0]);
+  }
+  for (int step = 0; step < ncb; ++step) {
     const int buf = step & 1;
     const long cidx = (long)bh * NC + chunk_of(step);
     f32x4 addc[TL::RM][TL::RN];
@@ -124,7 +130,7 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
     // Ss[buf] and Mb[buf] complete; every wave is past step-1, so the other
     // buffers are free to refill
     __syncthreads();
-    if (step + 1 < NC) fetch(step + 1);
+    if (step + 1 < ncb) fetch(step + 1);
     E* Xcc = Xc + cidx * D * D;
     if (!transposed) {
       for (int e = tid; e < NVR; e += SP_NT) {
@@ -151,7 +157,7 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
 #pragma unroll
         for (int j = 0; j < TL::RN; ++j) S.v[i][j] = egc * S.v[i][j] - P.v[i][j] + addc[i][j];
     }
-    if (step + 1 < NC) stage(Mb[buf ^ 1]);
+    if (step + 1 < ncb) stage(Mb[buf ^ 1]);
   }
   if (fin && act) {
 #pragma unroll
@@ -173,10 +179,12 @@ static hipError_t state_launch_d(const Dims& d, const float* init, const E* Bm, 
   constexpr int RB = D > 64 ? 64 : D;
   if (rev)
     hipLaunchKernelGGL((state_pass_kernel<E, D, RB, true>), dim3(d.B * d.H * (D / RB)), dim3(SP_NT),
-                       0, s, init, Bm, AddT, gC, Xc, fin, d.B, d.H, d.NC, tr ? 1 : 0, 1);
+                       0, s, init, Bm, AddT, gC, Xc, fin, d.B, d.H, d.NC, tr ? 1 : 0, 1, d.T, d.C,
+                       d.cu);
   else
     hipLaunchKernelGGL((state_pass_kernel<E, D, RB, false>), dim3(d.B * d.H * (D / RB)), dim3(SP_NT),
-                       0, s, init, Bm, AddT, gC, Xc, fin, d.B, d.H, d.NC, tr ? 1 : 0, 0);
+                       0, s, init, Bm, AddT, gC, Xc, fin, d.B, d.H, d.NC, tr ? 1 : 0, 0, d.T, d.C,
+                       d.cu);
   return hipGetLastError();
 }
 
@@ -216,6 +224,8 @@ __global__ __launch_bounds__(OF_NT) void out_fwd_kernel(const E* __restrict__ Sc
   const int bid = xcd_swizzle(blockIdx.x, nblk);
   const int c = bid % NC, bh = bid / NC;
   const int h = bh % H, b = bh / H;
+  const int nval = min(C, seq_len(cu, b, T) - c * C);
+  if (nval <= 0) return;   // past the end of a packed sequence: S_c was never written
   const long cidx = (long)bh * NC + c;
   g2s_rows<E, D, D, OF_NT>(Ss, LR, Sc + cidx * D * D, D, D, tid);
   g2s_rows<E, C, D, OF_NT>(Qs, LR, Qt + cidx * C * D, D, C, tid);
@@ -224,7 +234,6 @@ __global__ __launch_bounds__(OF_NT) void out_fwd_kernel(const E* __restrict__ Sc
   a.zero();
   gemm_acc<E, D, C, D, OF_NW, true, true>(a, Ss, LR, Qs, LR, wave, lane);
   const float* Oc = Oloc + cidx * C * D;
-  const int nval = min(C, seq_len(cu, b, T) - c * C);
   E* oc = o + ((seq_start(cu, b, T) + c * C) * H + h) * D;
   for_tiles(a, wave, lane, [&](int f0, int t, const f32x4& x) {
     if (t < nval) {
