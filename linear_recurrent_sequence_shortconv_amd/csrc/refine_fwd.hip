@@ -97,30 +97,43 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
   };
   Frag bw[FPW][NK];   // weight fragments of the next projection (W_p^(1) now)
   if (L > 0) load_w(Wp + (long)h * L * D * D, bw);
+  // taps of the lane's features, requested with the v rows (one round trip)
+  const E* ch = conv + (long)h * D * 4;
+  float taps[FPW][4];
+#pragma unroll
+  for (int nn = 0; nn < FPW; ++nn) {
+    const int n = wave + RF_NW * nn;
+    const int f = 16 * n + (lane & 15);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) taps[nn][j] = (FT_OK(n)) ? to_f(ch[f * 4 + j]) : 0.f;
+  }
   __syncthreads();
 
   // ---- anchor u (fp32; to LDS as the MFMA operand, hi and lo parts) and
   //      residual r^(1) = v - u, both in the accumulator layout:
   //      element (m, n, i): token 16 m + 4 (lane >> 4) + i, feature 16 n + (lane & 15)
-  const E* ch = conv + (long)h * D * 4;
   float r[4][FPW][4];
 #pragma unroll
   for (int nn = 0; nn < FPW; ++nn) {
     const int n = wave + RF_NW * nn;
     const int f = 16 * n + (lane & 15);
-    float taps[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) taps[j] = (FT_OK(n)) ? to_f(ch[f * 4 + j]) : 0.f;
+    for (int m = 0; m < 4; ++m) {
+      // the lane's four tokens t0m .. t0m + 3 read v rows t0m .. t0m + 6 + o
+      // of the tile (tap j of token t is row t + 3 - j, the token itself row
+      // t + 3 + o): each row once
+      const int t0m = 16 * m + 4 * (lane >> 4);
+      float w[7 + OFF];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+      for (int q = 0; q < 7 + OFF; ++q) w[q] = FT_OK(n) ? to_f(vbuf[(t0m + q) * D + f]) : 0.f;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int t = 16 * m + 4 * (lane >> 4) + i;
+        const int t = t0m + i;
         float u = 0.f, val = 0.f;
         if (FT_OK(n) && t0 + t < Tb) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) u += taps[j] * to_f(vbuf[(t + HL - OFF - j) * D + f]);
-          val = to_f(vbuf[(t + HL) * D + f]) - u;
+          for (int j = 0; j < 4; ++j) u += taps[nn][j] * w[i + 3 - j];
+          val = w[i + 3 + OFF] - u;
         }
         r[m][nn][i] = val;
         if (FT_OK(n)) {
@@ -129,6 +142,7 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
           if constexpr (sizeof(E) == 2) ulo[t * LD + f] = to_t<E>(u - to_f(uh));
         }
       }
+    }
   }
   __syncthreads();
 
