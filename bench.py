@@ -209,9 +209,9 @@ def summarize_profiles(d, workload):
             t[1] += float(r["TotalDurationNs"])
     counts = algorithmic_counts(w)
     cmds = [
-        "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof/trace -o run -- python -u $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline",
-        "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof/fetch -o run -- python -u $R/bench.py --steps 1 --warmup 1 --no-cpu-baseline",
-        "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof/write -o run -- python -u $R/bench.py --steps 1 --warmup 1 --no-cpu-baseline",
+        "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof/trace -o run -- python -u $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-varlen",
+        "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof/fetch -o run -- python -u $R/bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-varlen",
+        "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof/write -o run -- python -u $R/bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-varlen",
         "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof/cfetch -o run -- python -u $R/bench.py --calibrate-copy",
         "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof/cwrite -o run -- python -u $R/bench.py --calibrate-copy",
         f"python bench.py --summarize-profiles gpurun_out/prof --workload {workload}",
