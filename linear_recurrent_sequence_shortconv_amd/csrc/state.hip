@@ -8,6 +8,8 @@
 // blocks, each carried in fp32 registers by one workgroup for the whole
 // sequence; the product with M runs on MFMA with the state cast to the
 // operand type.
+#include <type_traits>
+
 #include "prism_common.h"
 #include "prism_internal.h"
 
@@ -74,16 +76,20 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
   // at its own end, and the chunks after it are never read)
   const int ncb = (seq_len(cu, bh / H, T) + C - 1) / C;
   auto chunk_of = [&](int step) { return REV ? ncb - 1 - step : step; };
-  uint4 mst[PER];                       // next Bm, staged through registers into LDS
-  f32x4 addn[TL::RM][TL::RN];           // next AddT^T block
-  float egn = 0.f;                      // next decay
-  auto fetch = [&](int step) {
+  // The operands of step s + 2 are requested at the start of step s (two
+  // register sets, indexed by the step's parity at compile time): a step
+  // then stages into LDS only data that has had a whole step to arrive.
+  uint4 mst[2][PER];                    // Bm of a coming step, staged through registers
+  f32x4 addn[2][TL::RM][TL::RN];        // AddT^T block of a coming step
+  float egn[2] = {0.f, 0.f};            // decay of a coming step
+  auto fetch = [&](int step, auto setc) {
+    constexpr int Z = decltype(setc)::value;
     const long cidx = (long)bh * NC + chunk_of(step);
     const E* bm = Bm + cidx * D * D;
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const int e = tid + p * SP_NT;
-      if (e < NV) mst[p] = ld16(bm + (long)e * VN);
+      if (e < NV) mst[Z][p] = ld16(bm + (long)e * VN);
     }
     if (act) {
       const float* ac = AddT + cidx * D * D + rb0;
@@ -91,33 +97,33 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
       for (int i = 0; i < TL::RM; ++i)
 #pragma unroll
         for (int j = 0; j < TL::RN; ++j)
-          addn[i][j] = *reinterpret_cast<const f32x4*>(ac + (long)(n0 + 16 * j + cl) * D + m0 + 16 * i + rl);
+          addn[Z][i][j] = *reinterpret_cast<const f32x4*>(ac + (long)(n0 + 16 * j + cl) * D + m0 + 16 * i + rl);
     }
-    egn = expf(gC[cidx]);
+    egn[Z] = expf(gC[cidx]);
   };
-  auto stage = [&](E* dst) {
+  auto stage = [&](E* dst, auto setc) {
+    constexpr int Z = decltype(setc)::value;
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
       const int e = tid + p * SP_NT;
       if (e < NV) {
         const int r = e / (D / VN), c = (e % (D / VN)) * VN;
-        st16(dst + r * LS + c, mst[p]);
+        st16(dst + r * LS + c, mst[Z][p]);
       }
     }
   };
-  if (ncb > 0) {
-    fetch(0);
-    stage(Mb[0]);
-  }
-  for (int step = 0; step < ncb; ++step) {
-    const int buf = step & 1;
+  using Z0 = std::integral_constant<int, 0>;
+  using Z1 = std::integral_constant<int, 1>;
+  // one step; its operands are in set Z (Bm already staged in Mb[Z])
+  auto body = [&](int step, auto setc) {
+    constexpr int Z = decltype(setc)::value;
     const long cidx = (long)bh * NC + chunk_of(step);
     f32x4 addc[TL::RM][TL::RN];
 #pragma unroll
     for (int i = 0; i < TL::RM; ++i)
 #pragma unroll
-      for (int j = 0; j < TL::RN; ++j) addc[i][j] = addn[i][j];
-    const float egc = egn;
+      for (int j = 0; j < TL::RN; ++j) addc[i][j] = addn[Z][i][j];
+    const float egc = egn[Z];
     if (act) {   // state -> operand copy
 #pragma unroll
       for (int i = 0; i < TL::RM; ++i)
@@ -125,24 +131,24 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
         for (int j = 0; j < TL::RN; ++j)
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            Ss[buf][(m0 + 16 * i + rl + r) * LS + n0 + 16 * j + cl] = to_t<E>(S.v[i][j][r]);
+            Ss[Z][(m0 + 16 * i + rl + r) * LS + n0 + 16 * j + cl] = to_t<E>(S.v[i][j][r]);
     }
-    // Ss[buf] and Mb[buf] complete; every wave is past step-1, so the other
-    // buffers are free to refill
+    // Ss[Z] and Mb[Z] complete; every wave is past the previous step, so the
+    // other buffers are free to refill
     __syncthreads();
-    if (step + 1 < ncb) fetch(step + 1);
+    if (step + 2 < ncb) fetch(step + 2, setc);
     E* Xcc = Xc + cidx * D * D;
     if (!transposed) {
       for (int e = tid; e < NVR; e += SP_NT) {
         const int r = e / (D / VN), c = (e % (D / VN)) * VN;
-        st16(Xcc + (long)(rb0 + r) * D + c, ld16(Ss[buf] + r * LS + c));
+        st16(Xcc + (long)(rb0 + r) * D + c, ld16(Ss[Z] + r * LS + c));
       }
     } else {
       for (int e = tid; e < NVR; e += SP_NT) {
         const int kk = e / (RB / VN), r0 = (e % (RB / VN)) * VN;
         E tmp[VN];
 #pragma unroll
-        for (int r = 0; r < VN; ++r) tmp[r] = Ss[buf][(r0 + r) * LS + kk];
+        for (int r = 0; r < VN; ++r) tmp[r] = Ss[Z][(r0 + r) * LS + kk];
         uint4 pk;
         __builtin_memcpy(&pk, tmp, 16);
         st16(Xcc + (long)kk * D + rb0 + r0, pk);
@@ -150,14 +156,23 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
     }
     Acc<RB, D, SP_NW> P;
     P.zero();
-    gemm_acc<E, RB, D, D, SP_NW, true, !REV>(P, Ss[buf], LS, Mb[buf], LS, wave, lane);
+    gemm_acc<E, RB, D, D, SP_NW, true, !REV>(P, Ss[Z], LS, Mb[Z], LS, wave, lane);
     if (act) {
 #pragma unroll
       for (int i = 0; i < TL::RM; ++i)
 #pragma unroll
         for (int j = 0; j < TL::RN; ++j) S.v[i][j] = egc * S.v[i][j] - P.v[i][j] + addc[i][j];
     }
-    if (step + 1 < ncb) stage(Mb[buf ^ 1]);
+    if (step + 1 < ncb) stage(Mb[Z ^ 1], std::integral_constant<int, Z ^ 1>{});
+  };
+  if (ncb > 0) {
+    fetch(0, Z0{});
+    stage(Mb[0], Z0{});
+    if (ncb > 1) fetch(1, Z1{});
+  }
+  for (int step = 0; step < ncb; step += 2) {
+    body(step, Z0{});
+    if (step + 1 < ncb) body(step + 1, Z1{});
   }
   if (fin && act) {
 #pragma unroll
