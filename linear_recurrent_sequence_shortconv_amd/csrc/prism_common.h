@@ -272,7 +272,7 @@ __device__ inline void for_tiles_mut(Acc<M, N, NW>& acc, int wave, int lane, F&&
 constexpr int inv_scratch_floats(int C) { return C >= 32 ? ((C / 2) * (C / 2 + 1) + 3) / 4 * 4 : 4; }
 
 template <int C, int S, int NW>
-__device__ inline void invert_double_level(const float* A, float* Tm, float* Xs, int wave, int lane) {
+__device__ __attribute__((always_inline)) inline void invert_double_level(const float* A, float* Tm, float* Xs, int wave, int lane) {
   constexpr int LA = C + 1, P = C / (2 * S), LX = S + 1;
   static_assert(NW % P == 0, "waves per block pair");
   constexpr int NWP = NW / P;
@@ -301,8 +301,11 @@ __device__ inline void invert_double_level(const float* A, float* Tm, float* Xs,
   __syncthreads();
 }
 
+// Always inlined: as a call it would make the caller wait for every load in
+// flight (its prefetches of the next phase) and spill around the call.
 template <int C, int NW>
-__device__ inline void invert_unit_lower(const float* A, float* Tm, float* Xs, int tid) {
+__device__ __attribute__((always_inline)) inline void invert_unit_lower(const float* A, float* Tm,
+                                                                       float* Xs, int tid) {
   constexpr int NB = C / 16, LA = C + 1;
   static_assert(NB >= 1 && NB <= 4 && C % 16 == 0, "C in {16, 32, 48, 64}");
   // (tid >> 6 is the same in every lane of a wave: keep the wave index scalar)
