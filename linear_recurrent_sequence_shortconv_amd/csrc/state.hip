@@ -244,17 +244,29 @@ __global__ __launch_bounds__(OF_NT) void out_fwd_kernel(const E* __restrict__ Sc
   const long cidx = (long)bh * NC + c;
   g2s_rows<E, D, D, OF_NT>(Ss, LR, Sc + cidx * D * D, D, D, tid);
   g2s_rows<E, C, D, OF_NT>(Qs, LR, Qt + cidx * C * D, D, C, tid);
+  // O_loc in the accumulator layout, requested before the product so that
+  // its latency overlaps it: tile (i, j) holds features f0 .. f0 + 3 of token t
+  typedef Tiling<D, C, OF_NW> TL;
+  const float* Oc = Oloc + cidx * C * D;
+  f32x4 ol[TL::RM][TL::RN];
+  if (TL::active(wave)) {
+#pragma unroll
+    for (int i = 0; i < TL::RM; ++i)
+#pragma unroll
+      for (int j = 0; j < TL::RN; ++j) {
+        const int f0 = TL::m0(wave) + 16 * i + 4 * (lane >> 4), t = TL::n0(wave) + 16 * j + (lane & 15);
+        ol[i][j] = t < nval ? *reinterpret_cast<const f32x4*>(Oc + (long)t * D + f0) : f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+  }
   __syncthreads();
   Acc<D, C, OF_NW> a;   // [f][t] = S[f] . Qt[t]
   a.zero();
   gemm_acc<E, D, C, D, OF_NW, true, true>(a, Ss, LR, Qs, LR, wave, lane);
-  const float* Oc = Oloc + cidx * C * D;
   E* oc = o + ((seq_start(cu, b, T) + c * C) * H + h) * D;
-  for_tiles(a, wave, lane, [&](int f0, int t, const f32x4& x) {
+  for_tiles_ij(a, wave, lane, [&](int i, int j, int f0, int t, const f32x4& x) {
     if (t < nval) {
-      const f32x4 ol = *reinterpret_cast<const f32x4*>(Oc + (long)t * D + f0);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) oc[(long)t * H * D + f0 + r] = to_t<E>(ol[r] + x[r]);
+      for (int r = 0; r < 4; ++r) oc[(long)t * H * D + f0 + r] = to_t<E>(ol[i][j][r] + x[r]);
     }
   });
 }
