@@ -396,6 +396,64 @@ def varlen_bench(steps, B=64, H=4, d=64, L=2, chunk=64, tmax=200, seed=3):
             "tokens_per_s_padded": round(N / (ms_d * 1e-3), 1)}
 
 
+SWEEP = ("long-T2048", "long-T4096", "long-T8192", "long-T16384",
+         "depth-L0", "depth-L1", "depth-L2", "depth-L4", "depth-L8")
+
+
+def sweep(steps, names=SWEEP):
+    """Training-pair step (forward keeping the intermediates + backward) and
+    forward alone for the long-context sweep (T = 2K..16K at 16384 tokens per
+    batch) and the refinement-depth sweep (L = 0..8, B=4, T=4096); inputs are
+    resident in HBM before timing.  One JSON line."""
+    import numpy as np
+    import torch
+    from linear_recurrent_sequence_shortconv_amd import prism as P
+    from linear_recurrent_sequence_shortconv_amd.workloads import make_workload_inputs, workloads
+
+    rows = []
+    for name in names:
+        w = workloads()[name]
+        x = make_workload_inputs(w, seed=0)
+        tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+        dev = lambda a, t=tdt: torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(t)
+        f32 = torch.float32
+        a = (dev(x["q"]), dev(x["k"]), dev(x["v"]), dev(x["alpha"], f32), dev(x["beta"], f32)) + (
+            tuple(dev(x[n]) for n in ("Wk", "Wp", "wbeta", "conv")) if w.L > 0 else (None,) * 4)
+        dO = dev(x["dO"])
+        del x
+        desc = P.make_desc(w.B, w.T, w.H, w.d, w.d, w.L, w.chunk, P.PRISM_BF16)
+        ws_f = P._workspace(P.forward_workspace_bytes(desc), a[0].device)[1]
+        ws_b = P._workspace(P.backward_workspace_bytes(desc), a[0].device)[1]
+        saved = P._workspace(P.saved_bytes(desc), a[0].device)[1]
+
+        def train():
+            P.forward(*a, chunk=w.chunk, workspace=ws_f, saved=saved)
+            P.backward(*a, dO=dO, chunk=w.chunk, workspace=ws_b, saved=saved)
+
+        def fwd():
+            P.forward(*a, chunk=w.chunk, workspace=ws_f)
+
+        res = {"workload": name, "B": w.B, "T": w.T, "L": w.L}
+        for key, fn in (("fwd_bwd", train), ("fwd", fwd)):
+            for _ in range(2):
+                fn()
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(steps):
+                fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            res[f"ms_{key}"] = round(ms, 4)
+            res[f"tokens_per_s_{key}"] = round(w.B * w.T / (ms * 1e-3), 1)
+        rows.append(res)
+        print(json.dumps(res), file=sys.stderr, flush=True)
+        del a, dO, ws_f, ws_b, saved
+        torch.cuda.empty_cache()
+    print(json.dumps({"sweep": rows, "dtype": "bf16", "data": "synthetic", "steps": steps}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -407,6 +465,8 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode-step measurement")
     ap.add_argument("--no-varlen", action="store_true", help="skip the packed-batch measurement")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the long-context and refinement-depth sweeps instead (one JSON line)")
     ap.add_argument("--summarize-profiles", metavar="DIR",
                     help="write profiles/ summaries from the rocprofv3 runs under DIR and exit")
     args = ap.parse_args()
@@ -423,6 +483,10 @@ def main():
 
     import numpy as np
     import torch
+
+    if args.sweep:
+        sweep(args.steps)
+        return
 
     if args.calibrate_copy:
         n = 1 << 30

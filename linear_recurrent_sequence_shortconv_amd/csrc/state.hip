@@ -33,6 +33,7 @@ namespace prism {
 // same XCD) while the current step multiplies.
 constexpr int SP_NW = 8;
 constexpr int SP_NT = SP_NW * WAVE;
+constexpr long SP_WIDE = 256;   // workgroups that fill the chip (one per CU)
 
 template <typename E, int D, int RB, bool REV>
 __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restrict__ init,
@@ -189,18 +190,31 @@ template <typename E, int D>
 static hipError_t state_launch_d(const Dims& d, const float* init, const E* Bm, const float* AddT,
                                  const float* gC, E* Xc, float* fin, bool tr, bool rev,
                                  hipStream_t s) {
-  // row blocks of 64 rows at D = 128 (two workgroups per sequence), whole
-  // state below that
-  constexpr int RB = D > 64 ? 64 : D;
-  if (rev)
-    hipLaunchKernelGGL((state_pass_kernel<E, D, RB, true>), dim3(d.B * d.H * (D / RB)), dim3(SP_NT),
-                       0, s, init, Bm, AddT, gC, Xc, fin, d.B, d.H, d.NC, tr ? 1 : 0, 1, d.T, d.C,
-                       d.cu);
-  else
-    hipLaunchKernelGGL((state_pass_kernel<E, D, RB, false>), dim3(d.B * d.H * (D / RB)), dim3(SP_NT),
-                       0, s, init, Bm, AddT, gC, Xc, fin, d.B, d.H, d.NC, tr ? 1 : 0, 0, d.T, d.C,
-                       d.cu);
-  return hipGetLastError();
+  // Row blocks: the whole state below D = 128; at D = 128 blocks of 64 rows
+  // (two workgroups per sequence), or of 32 or 16 rows when there are too few
+  // sequence-heads to give every CU a workgroup (long sequences, small
+  // batches: the pass is sequential over chunks, so its width is all the
+  // parallelism it has).
+  auto go = [&](auto rbc) {
+    constexpr int RB = decltype(rbc)::value;
+    if (rev)
+      hipLaunchKernelGGL((state_pass_kernel<E, D, RB, true>), dim3(d.B * d.H * (D / RB)), dim3(SP_NT),
+                         0, s, init, Bm, AddT, gC, Xc, fin, d.B, d.H, d.NC, tr ? 1 : 0, 1, d.T, d.C,
+                         d.cu);
+    else
+      hipLaunchKernelGGL((state_pass_kernel<E, D, RB, false>), dim3(d.B * d.H * (D / RB)), dim3(SP_NT),
+                         0, s, init, Bm, AddT, gC, Xc, fin, d.B, d.H, d.NC, tr ? 1 : 0, 0, d.T, d.C,
+                         d.cu);
+    return hipGetLastError();
+  };
+  if constexpr (D > 64) {
+    const long nbh = (long)d.B * d.H;
+    if (nbh * 2 >= SP_WIDE) return go(std::integral_constant<int, 64>{});
+    if (nbh * 4 >= SP_WIDE) return go(std::integral_constant<int, 32>{});
+    return go(std::integral_constant<int, 16>{});
+  } else {
+    return go(std::integral_constant<int, D>{});
+  }
 }
 
 template <typename E>

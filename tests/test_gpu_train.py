@@ -93,3 +93,22 @@ def test_train_pair_lm_workload_sampled():
         errs = {n: relerr(g[n][b:b + 1, :, h:h + 1].double().cpu().numpy(), go[n]) for n in SEQ_GRADS}
         print(f"  (b={b},h={h}) " + "  ".join(f"{n} {e:.2e}" for n, e in errs.items()), flush=True)
         assert all(e <= TOL[w.dtype] for e in errs.values()), errs
+
+
+@pytest.mark.parametrize("B,H", [(1, 4), (4, 16), (8, 16)], ids=["rows16", "rows32", "rows64"])
+def test_state_row_block_widths(B, H):
+    """At d = 128 the state passes split the state into row blocks of 16, 32
+    or 64 rows depending on how many sequence-heads fill the chip (B H = 4,
+    64, 128 here): each width against the oracle, forward and training pair."""
+    x = make_inputs(B, 50, H, 128, 1, "bf16", seed=90 + B * H, random_S0=True, with_dST=True)
+    print(f"\n[state row blocks B={B} H={H} d=128 T=50]", flush=True)
+    o, ST, g = train_pair(x, "bf16", 32, 1)
+    Wn = [x[n] for n in ("Wk", "Wp", "wbeta", "conv")]
+    oo, so = O.forward(x["q"], x["k"], x["v"], x["alpha"], x["beta"], *Wn, S0=x["S0"])
+    go = O.backward(x["q"], x["k"], x["v"], x["alpha"], x["beta"], *Wn, S0=x["S0"], dO=x["dO"],
+                    dST=x["dST"])
+    errs = {"o": relerr(o.double().cpu().numpy(), oo), "ST": relerr(ST.double().cpu().numpy(), so)}
+    for n in SEQ_GRADS + ("dS0",):
+        errs[n] = relerr(g[n].double().cpu().numpy(), go[n])
+    print("  " + "  ".join(f"{n} {e:.2e}" for n, e in errs.items()), flush=True)
+    assert all(e <= TOL["bf16"] for e in errs.values()), errs
