@@ -209,12 +209,12 @@ def summarize_profiles(d, workload):
             t[1] += float(r["TotalDurationNs"])
     counts = algorithmic_counts(w)
     cmds = [
-        "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d $R/gpurun_out/prof/trace -o run -- python -u $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-varlen",
-        "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof/fetch -o run -- python -u $R/bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-varlen",
-        "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof/write -o run -- python -u $R/bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-varlen",
-        "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $R/gpurun_out/prof/cfetch -o run -- python -u $R/bench.py --calibrate-copy",
-        "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $R/gpurun_out/prof/cwrite -o run -- python -u $R/bench.py --calibrate-copy",
-        f"python bench.py --summarize-profiles gpurun_out/prof --workload {workload}",
+        "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/trace -o run -- python -u $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-varlen",
+        "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/fetch -o run -- python -u $R/bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-varlen",
+        "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/write -o run -- python -u $R/bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-varlen",
+        "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/cfetch -o run -- python -u $R/bench.py --calibrate-copy",
+        "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/cwrite -o run -- python -u $R/bench.py --calibrate-copy",
+        f"python bench.py --summarize-profiles $OUT --workload {workload}",
     ]
     rec = {"workload": workload, "sources_sha256": _sources_sha256(),
            "calibration": {"fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4),
@@ -228,7 +228,7 @@ def summarize_profiles(d, workload):
              f"B={w.B} T={w.T} H={w.H} d_k=d_v={w.d} L={w.L} chunk={w.chunk} {w.dtype}; one forward + backward step.",
              f"step_refine / step_state: the decode step (prism_step, one token) for B={DECODE_BATCH} sequences "
              "at the same head shape, which bench.py also times.",
-             "Made with (R = repository root on the GPU host; each rocprofv3 run on its own):",
+             "Made with (R = repository root, OUT = an output directory; each rocprofv3 run on its own):",
              "", "```"] + cmds + ["```", "",
              f"HBM byte counters are scaled by the readings of a plain 1 GiB device copy: FETCH_SIZE x {f_factor:.3f}, "
              f"WRITE_SIZE x {w_factor:.3f}.  `algorithmic` is the byte count each kernel must move "
@@ -476,7 +476,7 @@ def main():
         return
 
     if args.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {args.gpus} is not supported "
+        print(f"bench.py: measures one GPU only; --gpus {args.gpus} is not supported "
               "(sequences and heads are independent, so several GPUs would each run this same "
               "per-GPU workload).", file=sys.stderr)
         sys.exit(2)
