@@ -1,0 +1,82 @@
+"""Host-side logic of bench.py (no GPU): the one-GPU contract, the
+algorithmic byte / FLOP counts behind the roofline figures, and the profile
+summarizer on synthetic rocprofv3 CSV files."""
+import csv
+import json
+import os
+import subprocess
+import sys
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+sys.path.insert(0, ROOT)
+import bench  # noqa: E402
+from linear_recurrent_sequence_shortconv_amd.workloads import workloads  # noqa: E402
+
+
+def test_more_than_one_gpu_is_refused():
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and "one GPU" in r.stderr and r.stdout == ""
+
+
+def test_algorithmic_counts_cover_every_timed_kernel():
+    w = workloads()["lm-T2048"]
+    c = bench.algorithmic_counts(w)
+    timer_names = {n for _, names in bench._FAMILIES for n in names} | {"chunk_fwd",
+                                                                          "chunk_fwd_bwdmode"}
+    assert timer_names <= set(c), timer_names - set(c)
+    for name, v in c.items():
+        assert v["bytes"] > 0 and v["flops"] >= 0 and v["floor_ms"] > 0, name
+        assert v["bound"] in ("hbm", "mfma")
+    # per token-head, the refinement forward moves e (d + 2 L d) bytes
+    th = w.B * w.T * w.H
+    assert c["refine_fwd"]["bytes"] == th * 2 * w.d + w.B * w.T * w.H * 2 * w.L * w.d * 2
+    # the decode state kernel reads and writes the fp32 state: 8 d^2 bytes per sequence-head
+    dec = bench.decode_counts(w)
+    assert dec["step_state"][0] > bench.DECODE_BATCH * w.H * 8 * w.d * w.d
+
+
+def test_kernel_names_map_to_timer_names():
+    assert bench._family("_ZN5prism17refine_bwd_kernelIDF16bLi128ELi4ELi0ELi0EEEv") == ["refine_bwd"]
+    assert bench._family("_ZN5prism16chunk_fwd_kernelIDF16bLi128ELi64ELb1EEEv") == ["chunk_fwd_bwdmode"]
+    assert bench._family("_ZN5prism16chunk_fwd_kernelIDF16bLi128ELi64ELb0EEEv") == ["chunk_fwd"]
+    assert bench._family("_ZN5prism17step_state_kernelIDF16bLi128EEEv") == ["step_state"]
+    assert bench._family("some_other_kernel") is None
+
+
+def _write_csv(path, header, rows):
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w", newline="") as f:
+        wr = csv.writer(f)
+        wr.writerow(header)
+        wr.writerows(rows)
+
+
+def test_summarize_profiles_scales_counters_by_the_copy(tmp_path, monkeypatch):
+    d = str(tmp_path)
+    k = "_ZN5prism14out_fwd_kernelIDF16bLi128ELi64EEEv"
+    # copy: FETCH reads half of 1 GiB (KiB), WRITE all of it
+    _write_csv(os.path.join(d, "cfetch", "run_counter_collection.csv"),
+               ["Kernel_Name", "Counter_Value"], [["copy", (1 << 30) / 1024 / 2]])
+    _write_csv(os.path.join(d, "cwrite", "run_counter_collection.csv"),
+               ["Kernel_Name", "Counter_Value"], [["copy", (1 << 30) / 1024]])
+    _write_csv(os.path.join(d, "fetch", "run_counter_collection.csv"),
+               ["Kernel_Name", "Counter_Value"], [[k, 1000.0], [k, 1000.0]])
+    _write_csv(os.path.join(d, "write", "run_counter_collection.csv"),
+               ["Kernel_Name", "Counter_Value"], [[k, 500.0]])
+    _write_csv(os.path.join(d, "trace", "run_kernel_stats.csv"),
+               ["Name", "Calls", "TotalDurationNs"], [[k, 4, 400000]])
+    out = tmp_path / "repo"
+    (out / "profiles").mkdir(parents=True)
+    monkeypatch.setattr(bench, "ROOT", str(out))
+    monkeypatch.setattr(bench, "_sources_sha256", lambda: "sha")
+    bench.summarize_profiles(d, "lm-T2048")
+    rec = json.load(open(out / "profiles" / "hbm_traffic.json"))
+    assert abs(rec["calibration"]["fetch_factor"] - 2.0) < 1e-9
+    assert abs(rec["calibration"]["write_factor"] - 1.0) < 1e-9
+    t = rec["kernels"]["out_fwd"]
+    assert t["fetch_bytes"] == 2 * 1000 * 1024 and t["write_bytes"] == 500 * 1024
+    md = open(out / "profiles" / "lm-T2048_kernels.md").read()
+    assert "| out_fwd | 4 | 100.0 |" in md
