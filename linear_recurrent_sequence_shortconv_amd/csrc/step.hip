@@ -131,17 +131,18 @@ __global__ __launch_bounds__(64 * st_waves(D)) void step_state_kernel(
 }
 
 // Refinement pairs of a decode step (one token per sequence), summary §2.2
-// Stages 1-2: a workgroup owns 64 sequences of one head and 64 of its output
-// features; wave w takes the 16-feature MFMA tile w mod 4 for 32 of the
+// Stages 1-2: a workgroup owns 32 sequences of one head and 64 of its output
+// features; wave w takes the 16-feature MFMA tile w mod 4 for 16 of the
 // sequences (two waves per SIMD hide each other's latency).  The pairs of
 // all sequences of a head thus come from MFMA products with the head's
-// weights, read once per 64 sequences.  All loads of the set-up (weights of
+// weights, read once per 32 sequences.  All loads of the set-up (weights of
 // two steps, taps, w_beta, tokens and histories) are issued before the first
 // barrier; the chain runs in registers and the pairs are stored from the
 // accumulators, so the L steps need no barrier.
 constexpr int DR_NW = 8;
 constexpr int DR_NT = DR_NW * WAVE;
-constexpr int DR_ROWS = 64;   // sequences per workgroup
+constexpr int DR_ROWS = 32;   // sequences per workgroup
+constexpr int DR_MPW = DR_ROWS / 32;   // 16-sequence MFMA tiles per wave
 constexpr int DR_FG = 64;     // output features per workgroup (4 tiles of 16)
 
 template <typename E, int D, int ACT, int OFF>
@@ -156,7 +157,7 @@ __global__ __launch_bounds__(DR_NT) void decode_refine_kernel(
   constexpr int FG = D < DR_FG ? D : DR_FG;   // features of this workgroup
   constexpr int NFG = D / FG;
   constexpr int RW = FG + 4;                  // fp32 residual rows
-  constexpr int GT = 8;                       // threads per gate dot product
+  constexpr int GT = DR_NT / DR_ROWS;         // threads per gate dot product
   typedef typename Mfma<E>::frag Frag;
   __shared__ __attribute__((aligned(16))) E ubuf[DR_ROWS * LD];
   __shared__ __attribute__((aligned(16))) E ulo[sizeof(E) == 2 ? DR_ROWS * LD : 16];
@@ -256,12 +257,12 @@ __global__ __launch_bounds__(DR_NT) void decode_refine_kernel(
   if (!has) return;   // no barrier follows
 
   // residual in the accumulator layout: (m, i) is sequence
-  // 32 half + 16 m + 4 (lane >> 4) + i
+  // rb + 16 m + 4 (lane >> 4) + i of the tile
   const int fl = 16 * ft + (lane & 15);
-  const int rb = 32 * half;
-  float r[2][4];
+  const int rb = 16 * DR_MPW * half;
+  float r[DR_MPW][4];
 #pragma unroll
-  for (int m = 0; m < 2; ++m)
+  for (int m = 0; m < DR_MPW; ++m)
 #pragma unroll
     for (int i = 0; i < 4; ++i) r[m][i] = rbuf[(rb + 16 * m + 4 * (lane >> 4) + i) * RW + fl];
 
@@ -269,13 +270,13 @@ __global__ __launch_bounds__(DR_NT) void decode_refine_kernel(
   for (int l = 0; l < ST_LMAX; ++l) {
     if (l >= L) break;
     const int sl = l & 1;
-    f32x4 ap[2], ak[2];
+    f32x4 ap[DR_MPW], ak[DR_MPW];
 #pragma unroll
-    for (int m = 0; m < 2; ++m) ap[m] = ak[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int m = 0; m < DR_MPW; ++m) ap[m] = ak[m] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
+      for (int m = 0; m < DR_MPW; ++m) {
         const Frag a = load_frag<E, true>(ubuf, LD, rb + 16 * m, kk * KS, lane);
         ap[m] = Mfma<E>::mma(a, wp[sl][kk], ap[m]);
         ak[m] = Mfma<E>::mma(a, wk[sl][kk], ak[m]);
@@ -287,7 +288,7 @@ __global__ __launch_bounds__(DR_NT) void decode_refine_kernel(
     }
     if (l + 2 < L) load_w(l + 2, wp[sl], wk[sl]);
 #pragma unroll
-    for (int m = 0; m < 2; ++m)
+    for (int m = 0; m < DR_MPW; ++m)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int row = rb + 16 * m + 4 * (lane >> 4) + i;
