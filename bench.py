@@ -23,6 +23,7 @@ counters of rocprofv3 runs) and exits.
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -58,6 +59,12 @@ def algorithmic_counts(w):
     c["chunk_fwd"] = (th * (3 * D * e + 8) + ntp * 2 * L * D * e
                       + nch * (D * D * (e + 4) + C * D * (e + 4) + 4 + 2 * C * D * e),
                       nch * (2 * C * C * D * (4 * L + 6) + 2 * C * D * D * (L + 2)))
+    # refinement formed inside the chunk kernel (inference forward): no pairs
+    # in HBM; weights and taps once per head
+    c["chunk_fwd_fused"] = (th * (3 * D * e + 8) + H * (L * (2 * D * D + D) + 4 * D) * e
+                            + nch * (D * D * (e + 4) + C * D * (e + 4) + 4),
+                            nch * (2 * C * C * D * (4 * L + 6) + 2 * C * D * D * (L + 2))
+                            + th * 4 * L * D * D)
     c["chunk_fwd_bwdmode"] = (th * (4 * D * e + 8) + ntp * 2 * L * D * e
                               + nch * (2 * D * D * e + 2 * D * D * 4 + 2 * C * D * e + 4),
                               nch * (2 * C * C * D * (2 * L + 5) + 2 * C * D * D * (L + 4)))
@@ -146,8 +153,13 @@ _FAMILIES = [("refine_fwd_kernel", ["refine_fwd", "refine_fwd_recompute"]),
 
 def _family(kernel_name):
     if "chunk_fwd_kernel" in kernel_name:
-        bwd = "Lb1E" in kernel_name or "true>" in kernel_name
-        return ["chunk_fwd_bwdmode"] if bwd else ["chunk_fwd"]
+        # template flags <E, D, C, BWD, FUSE, ...>: mangled Lb0/Lb1, or demangled false/true
+        flags = re.findall(r"Lb([01])E", kernel_name) or [
+            "1" if x == "true" else "0" for x in re.findall(r"\b(true|false)\b", kernel_name)]
+        flags += ["0", "0"]
+        if flags[1] == "1":
+            return ["chunk_fwd_fused"]
+        return ["chunk_fwd_bwdmode"] if flags[0] == "1" else ["chunk_fwd"]
     for key, names in _FAMILIES:
         if key in kernel_name:
             return names
@@ -579,7 +591,13 @@ def main():
     torch.cuda.synchronize()
     ms_fwd = f_start.elapsed_time(f_end) / args.steps
 
-    # per-kernel timing over a second timed region (HIP events around each launch)
+    # per-kernel timing of the forward alone, then of the training step, each
+    # over its own timed region (HIP events around each launch)
+    with P.KernelTimer() as kf:
+        for _ in range(args.steps):
+            fwd_step()
+        torch.cuda.synchronize()
+    fwd_kernels = {n: round(tot / c, 5) for n, (tot, c) in kf.result.items()}
     with P.KernelTimer() as kt:
         for _ in range(args.steps):
             step()
@@ -622,7 +640,8 @@ def main():
         "config": {"workload": w.name, "B": w.B, "T": w.T, "H": w.H, "d_k": w.d, "d_v": w.d,
                    "L": w.L, "chunk": w.chunk, "global_batch": w.B, "seq_len": w.T,
                    "passes": "fwd+bwd" if backward else "fwd", "parallelism": "single GPU"},
-        "forward": {"ms_per_step": round(ms_fwd, 4), "tokens_per_s": round(tokens / (ms_fwd * 1e-3), 1)},
+        "forward": {"ms_per_step": round(ms_fwd, 4), "tokens_per_s": round(tokens / (ms_fwd * 1e-3), 1),
+                    "kernels_avg_ms": fwd_kernels},
         "stateless_pair": (None if ms_stateless is None else
                            {"ms_per_step": round(ms_stateless, 4),
                             "tokens_per_s": round(tokens / (ms_stateless * 1e-3), 1)}),

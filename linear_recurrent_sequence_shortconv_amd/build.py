@@ -22,6 +22,8 @@ LIB = os.path.join(HERE, "libprism.so")
 SOURCES = [
     "chunk_bwd.hip",
     "chunk_fwd.hip",
+    "chunk_fused_gelu.hip",
+    "chunk_fused_identity.hip",
     "refine_bwd_gelu.hip",
     "refine_bwd_gelu_past.hip",
     "refine_bwd_identity.hip",

@@ -1,0 +1,671 @@
+// Chunk-local part of the PRISM recurrence S_t = S_{t-1} A_t + B_t
+// (PRISM technical summary §2.1, with A_t = alpha_t (I - beta_t k_t k_t^T) and
+// B_t = beta_t v_t k_t^T + sum_l w_t^(l) k_t^(l)^T).  §2.2 (last paragraph)
+// notes that every part of the update depends on the input only; hence a
+// chunk of C tokens acts on the entering state S as one affine map
+//
+//     S_next = exp(gC) S - S M + H,        O = O_loc + Qt S^T,
+//
+// whose coefficients this kernel computes, one workgroup per (b, h, chunk):
+//
+//     g_t = sum_{j<=t} log alpha_j,  Gam_ti = exp(g_t - g_i),  D_t = exp(gC - g_t)
+//     A   = diag(beta) (Gam * K K^T)_{i<t},   T = (I + A)^{-1}   (fp32, LDS)
+//     V'  = V - sum_l (Gam * K K_l^T)_{i<t} W_l
+//     U   = T diag(beta) V',   Wk = T diag(beta e^g) K
+//     M   = Wk^T diag(D) K,    H  = U^T diag(D) K + sum_l W_l^T diag(D) K_l
+//     R0  = (Gam * Q K^T)_{i<=t},  R_l = (Gam * Q K_l^T)_{i<=t}
+//     Qt  = diag(e^g) Q - R0 Wk,   O_loc = R0 U + sum_l R_l W_l
+//
+// All products are bf16 (or fp32) MFMA with fp32 accumulation; T, the decays
+// and the accumulators stay fp32.  Stored (global, per chunk):
+//   Mt [D][D] = M^T (MFMA B operand of the state pass, both directions),
+//   HT [D][D] = H^T fp32, Qt [C][D], O_loc [C][D] fp32, gC, and when asked
+//   (training forward) U^T, Wk^T [D][C] for the reverse chunk kernels.
+// In backward mode (dO given) the kernel instead stores Mt, HT, gC,
+// ET = (dO^T Qt)^T fp32 (for the reverse state pass) and U^T, Wk^T.
+// et_kernel forms ET from a saved Qt when the forward was kept.
+//
+// Fused form (FUSE): the refinement pairs K_l, W_l are formed inside the
+// kernel from the chunk's v rows (and the 3 or 4 rows before it that the
+// ShortConv taps reach) instead of being read back from HBM: the anchor,
+// the two projections per step on MFMA, the activation chain and the step
+// gates, in the same arithmetic and rounding as the separate refinement
+// kernel, so both forms give the same bits.
+#pragma once
+#include <type_traits>
+#include <utility>
+
+#include "prism_common.h"
+#include "prism_internal.h"
+
+namespace prism {
+
+// four consecutive elements (8 or 16 bytes, aligned) to LDS
+template <typename E>
+__device__ inline void st4(E* p, const E (&x)[4]) {
+  if constexpr (sizeof(E) == 2) {
+    uint2 w;
+    __builtin_memcpy(&w, x, 8);
+    *reinterpret_cast<uint2*>(p) = w;
+  } else {
+    uint4 w;
+    __builtin_memcpy(&w, x, 16);
+    *reinterpret_cast<uint4*>(p) = w;
+  }
+}
+
+constexpr int CF_NW = 8;
+constexpr int CF_NT = CF_NW * WAVE;
+constexpr int FUSE_LMAX = 8;   // refinement steps the fused kernel's LDS is sized for
+
+template <typename E, int D, int C, bool FUSE = false, int HL = 3>
+struct ChunkLds {
+  static constexpr int LR = ldpad<E>(D);     // [C][LR]: C rows of D
+  static constexpr int LT = ldpad<E>(C);     // [D][LT] transposed, and [C][LT] C x C
+  static constexpr int LA = C + 1;           // fp32 C x C
+  static constexpr int SZ_R = C * LR * (int)sizeof(E);
+  static constexpr int SZ_T = D * LT * (int)sizeof(E);
+  static constexpr int SZ_CC = C * LT * (int)sizeof(E);
+  static constexpr int SZ_F = C * LA * 4;
+  static constexpr int SZ_VEC = 5 * C * 4;
+  // persistent
+  static constexpr int O_VEC = 0;
+  static constexpr int O_Q = O_VEC + SZ_VEC;
+  static constexpr int O_K = O_Q + SZ_R;
+  static constexpr int O_X = O_K + SZ_R;
+  // phase B (per refinement step)
+  static constexpr int B_KLR = O_X;
+  static constexpr int B_KLTD = B_KLR + SZ_R;
+  static constexpr int B_WLT = B_KLTD + SZ_T;
+  static constexpr int B_F = B_WLT + SZ_T;
+  static constexpr int B_RL = B_F + SZ_CC;
+  static constexpr int B_END = B_RL + SZ_CC;
+  // phase T (solve)
+  static constexpr int C_TB = O_X;
+  static constexpr int T_AF = C_TB + SZ_CC;
+  static constexpr int T_TF = T_AF + SZ_F;
+  static constexpr int T_XS = T_TF + SZ_F;
+  static constexpr int T_END = T_XS + inv_scratch_floats(C) * 4;
+  // phase C
+  static constexpr int C_KTBE = C_TB + SZ_CC;   // later Wk^T
+  static constexpr int C_KTD = C_KTBE + SZ_T;
+  static constexpr int C_VT = C_KTD + SZ_T;     // (beta V')^T, later U^T, later Qt^T
+  static constexpr int C_R0 = C_VT + SZ_T;
+  static constexpr int C_V = cmax(C_R0 + SZ_CC, T_END);   // V rows, later dO^T
+  static constexpr int C_END = C_V + cmax(SZ_R, SZ_T);
+  // refinement formed in the kernel (phase B): anchor u (bf16: hi and lo
+  // parts), step gates, w_beta rows; the v rows of the chunk and its halo
+  // share the K_l^T D region, which is free until the first K_l is written
+  static constexpr int SZ_U = FUSE ? SZ_R : 0;
+  static constexpr int F_U = B_END;
+  static constexpr int F_UL = F_U + SZ_U;
+  static constexpr int F_G = F_UL + (sizeof(E) == 2 ? SZ_U : 0);
+  static constexpr int F_WB = F_G + (FUSE ? FUSE_LMAX * C * 4 : 0);
+  static constexpr int F_END = F_WB + (FUSE ? FUSE_LMAX * D * (int)sizeof(E) : 0);
+  static constexpr int F_V = B_KLTD;
+  static_assert(!FUSE || (C + HL) * D <= D * LT, "v rows and halo fit the K_l^T region");
+  static constexpr int TOTAL = cmax(cmax(B_END, F_END), C_END);
+};
+
+template <typename E, int D, int C, bool BWD, bool FUSE, int ACT, int OFF>
+__global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
+    const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
+    const float* __restrict__ alpha, const float* __restrict__ beta, const E* __restrict__ Kl,
+    const E* __restrict__ Wl, const E* __restrict__ dO, E* __restrict__ Mt, float* __restrict__ HT,
+    E* __restrict__ Qt, float* __restrict__ Oloc, float* __restrict__ gCo,
+    float* __restrict__ ET, E* __restrict__ UTo, E* __restrict__ WkTo, int B, int T, int H, int L,
+    int NC, int Tp, const int* __restrict__ cu, FuseIn<E> fz) {
+  constexpr int HL = 3 + OFF;   // v rows before the chunk that the taps reach
+  typedef ChunkLds<E, D, C, FUSE, HL> LY;
+  constexpr int NW = CF_NW, NT = CF_NT;
+  constexpr int LR = LY::LR, LT = LY::LT, LA = LY::LA;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[LY::TOTAL];
+
+  float* g = reinterpret_cast<float*>(smem + LY::O_VEC);
+  float* ev = g + C;
+  float* Dv = g + 2 * C;
+  float* bt = g + 3 * C;
+  float* be = g + 4 * C;
+  E* Qr = reinterpret_cast<E*>(smem + LY::O_Q);
+  E* Kr = reinterpret_cast<E*>(smem + LY::O_K);
+
+  int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nblk = B * H * NC;
+  const long ts = (long)H * D;
+  // At d = 128 (one workgroup per CU) workgroups are persistent: they take
+  // the virtual block ids blockIdx.x, + gridDim.x, ..., and a chunk's first
+  // operands (Q and K rows, alpha, beta, the first K_l and W_l tiles) are
+  // fetched while the previous chunk is being finished.  Smaller d launch one
+  // workgroup per chunk (the loop runs once).
+  constexpr bool PERSIST = D >= 128;
+  const int vstride = PERSIST ? (int)gridDim.x : nblk;
+  RegTile<E, C, D, NT, true> kn, wn;   // K_l, W_l tiles of the next product step
+  RegTile<E, C, D, NT> qn, kr;         // Q, K rows of the next chunk
+  float pa = 1.f, pb = 0.f;            // alpha, beta of the next chunk (wave 0, lane < C)
+  // fused: v rows tb - HL .. tb + C - 1 of the next chunk (zeros past the
+  // end; before 0 the history rows, or zeros without a history)
+  constexpr int VN = 16 / (int)sizeof(E);
+  constexpr int VPRW = D / VN;
+  constexpr int VUN = FUSE ? (C + HL) * VPRW : 0;
+  constexpr int VPER = FUSE ? (VUN + NT - 1) / NT : 1;
+  uint4 vh[VPER];
+  auto prefetch = [&](int vid) {
+    const int bid = xcd_swizzle(vid, nblk);
+    const int c = bid % NC, bh = bid / NC;
+    const int h = bh % H, b = bh / H;
+    const int tb = c * C;
+    const int nval = min(C, seq_len(cu, b, T) - tb);
+    const long row0 = (seq_start(cu, b, T) + tb) * H + h;
+    if constexpr (FUSE) {
+      const int Tb = seq_len(cu, b, T);
+      const E* vs = v + (seq_start(cu, b, T) * H + h) * D;
+#pragma unroll
+      for (int p = 0; p < VPER; ++p) {
+        const int u = tid + p * NT;
+        const int r = u / VPRW, cc = (u % VPRW) * VN;
+        const int t = tb - HL + r;
+        uint4 x = {0u, 0u, 0u, 0u};
+        if (u < VUN) {
+          if (t >= 0 && t < Tb) x = ld16(vs + t * ts + cc);
+          else if (t < 0 && fz.hist) x = ld16(fz.hist + (((long)b * 4 + 4 + t) * H + h) * D + cc);
+        }
+        vh[p] = x;
+      }
+    } else if (L > 0) {
+      kn.load(Kl + (long)bh * L * Tp * D + (long)tb * D, D, C, tid);
+      wn.load(Wl + (long)bh * L * Tp * D + (long)tb * D, D, C, tid);
+    }
+    qn.load(q + row0 * D, ts, nval, tid);
+    kr.load(k + row0 * D, ts, nval, tid);
+    if (wave == 0) {
+      pa = lane < nval ? alpha[row0 + (long)lane * H] : 1.f;
+      pb = lane < nval ? beta[row0 + (long)lane * H] : 0.f;
+    }
+  };
+  if ((int)blockIdx.x < nblk) prefetch(blockIdx.x);
+  for (int vid = blockIdx.x; vid < nblk; vid += vstride) {
+  // per-lane values are redefined each iteration, so that the lane-dependent
+  // address arithmetic of the body is not hoisted out of the loop and kept
+  // live across it
+  if constexpr (PERSIST) {
+    asm volatile("" : "+v"(tid));
+    lane = tid & 63;
+    wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  }
+  const int bid = xcd_swizzle(vid, nblk);
+  const int c = bid % NC, bh = bid / NC;
+  const int h = bh % H, b = bh / H;
+  const int tb = c * C;
+  const int nval = min(C, seq_len(cu, b, T) - tb);
+  const long row0 = (seq_start(cu, b, T) + tb) * H + h;
+  // past the end of a packed sequence no pass reads the chunk: a one-chunk
+  // workgroup leaves; a persistent one computes its identity map (all tokens
+  // padding), since a skip path here costs registers on every chunk
+  if constexpr (!PERSIST) {
+    if (nval <= 0) return;
+  }
+  const E* vc = v + row0 * D;
+  const E* Klb = Kl + (long)bh * L * Tp * D + (long)tb * D;
+  const E* Wlb = Wl + (long)bh * L * Tp * D + (long)tb * D;
+
+  // fused refinement: wave w owns feature tile fn = w mod NFT for the token
+  // tiles mb, mb + WPF, ...; its weight fragments come straight from global
+  // memory (L2), the anchor u is the shared MFMA A operand in LDS, and the
+  // residual chain stays in registers in the accumulator layout:
+  // element (j, i) is token 16 (mb + WPF j) + 4 (lane >> 4) + i, feature f
+  typedef MfmaK<E, D> MK;
+  typedef typename MK::frag Frag;
+  constexpr int KS = MK::KSTEP;
+  constexpr int NK = D / KS;
+  constexpr int NFT = D / 16;
+  static_assert(NW % NFT == 0, "feature tiles divide the waves");
+  constexpr int WPF = NW / NFT;
+  constexpr int MT = C / 16;
+  constexpr int MPW = (MT + WPF - 1) / WPF;
+  const int fn = wave % NFT, mb = wave / NFT;
+  const int f = 16 * fn + (lane & 15);
+  auto tile_ok = [&](int j) { return MT % WPF == 0 || mb + WPF * j < MT; };
+  Frag bw[FUSE ? NK : 1];   // weight fragments of the next projection
+  float tp[4];              // ShortConv taps of feature f
+  auto load_w = [&](const E* W) {
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) bw[kk] = load_fragK<E, D>(W, D, 16 * fn, kk * KS, lane);
+  };
+  if constexpr (FUSE) {
+    load_w(fz.Wp + (long)h * L * D * D);   // W_p^(1)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) tp[j] = to_f(fz.conv[((long)h * D + f) * 4 + j]);
+    E* wbs = reinterpret_cast<E*>(smem + LY::F_WB);
+    for (int e = tid; e < L * VPRW; e += NT) st16(wbs + e * VN, ld16(fz.wbeta + (long)h * L * D + e * VN));
+    E* vb = reinterpret_cast<E*>(smem + LY::F_V);
+#pragma unroll
+    for (int p = 0; p < VPER; ++p) {
+      const int u = tid + p * NT;
+      if (u < VUN) st16(vb + (u / VPRW) * D + (u % VPRW) * VN, vh[p]);
+    }
+  }
+
+  // ---- phase A: decays and gates; Q, K tiles ----
+  if (wave == 0) {
+    const float lg = logf(pa), bv = pb;   // alpha = 1, beta = 0 past the end
+    float s = lg;
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const float y = __shfl_up(s, off);
+      if (lane >= off) s += y;
+    }
+    const float gC = __shfl(s, C - 1);
+    if (lane < C) {
+      const float e = expf(s);
+      g[lane] = s;
+      ev[lane] = e;
+      Dv[lane] = expf(gC - s);
+      bt[lane] = bv;
+      be[lane] = bv * e;
+    }
+    if (lane == 0) gCo[(long)bh * NC + c] = gC;
+  }
+  qn.store_rows(Qr, LR, tid);
+  kr.store_rows(Kr, LR, tid);
+  __syncthreads();
+
+  // ---- fused: anchor u_t = sum_j c_j v_{t-o-j} (to LDS, bf16 as hi + lo so
+  //      that p^(l) = W_p^(l) u is fp32-accurate), residual r^(1) = v - u in
+  //      registers, then the step gates sigmoid(w_beta^(l) . u_hi) ----
+  float r[FUSE ? MPW : 1][4];
+  if constexpr (FUSE) {
+    const E* vb = reinterpret_cast<const E*>(smem + LY::F_V);   // row q: token tb - HL + q
+    E* Ub = reinterpret_cast<E*>(smem + LY::F_U);
+    E* Ul = reinterpret_cast<E*>(smem + LY::F_UL);
+#pragma unroll
+    for (int j = 0; j < MPW; ++j) {
+      const int t0m = 16 * (mb + WPF * j) + 4 * (lane >> 4);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) r[j][i] = 0.f;
+      if (tile_ok(j)) {
+        // tap j of token t is buffer row t + 3 - j; the token itself row t + 3 + o
+        float w[7 + OFF];
+#pragma unroll
+        for (int q = 0; q < 7 + OFF; ++q) w[q] = to_f(vb[(t0m + q) * D + f]);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int t = t0m + i;
+          float u = 0.f;
+          if (t < nval) {
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) u += tp[jj] * w[i + 3 - jj];
+            r[j][i] = w[i + 3 + OFF] - u;
+          }
+          const E uh = to_t<E>(u);
+          Ub[t * LR + f] = uh;
+          if constexpr (sizeof(E) == 2) Ul[t * LR + f] = to_t<E>(u - to_f(uh));
+        }
+      }
+    }
+    __syncthreads();
+    // four threads per token, 16-byte reads of u and w_beta
+    const E* wbs = reinterpret_cast<const E*>(smem + LY::F_WB);
+    float* Gt = reinterpret_cast<float*>(smem + LY::F_G);
+    if (tid < 4 * C) {
+      const int t = tid >> 2, part = tid & 3;
+      for (int l = 0; l < L; ++l) {
+        float s = 0.f;
+        for (int cc = part * VN; cc < D; cc += 4 * VN) {
+          const uint4 ua = ld16(Ub + t * LR + cc), wa = ld16(wbs + l * D + cc);
+          const E* ue = reinterpret_cast<const E*>(&ua);
+          const E* we = reinterpret_cast<const E*>(&wa);
+#pragma unroll
+          for (int jj = 0; jj < VN; ++jj) s += to_f(we[jj]) * to_f(ue[jj]);
+        }
+        s += __shfl_xor(s, 1);
+        s += __shfl_xor(s, 2);
+        if (part == 0) Gt[l * C + t] = sigmoidf(s);
+      }
+    }
+  }
+  // p^(l) = W_p (u_hi + u_lo) or k^(l) = W_k u_hi for the wave's tiles
+  auto fgemm = [&](bool with_lo, f32x4 (&acc)[FUSE ? MPW : 1]) {
+    const E* Ub = reinterpret_cast<const E*>(smem + LY::F_U);
+    const E* Ul = reinterpret_cast<const E*>(smem + LY::F_UL);
+#pragma unroll
+    for (int j = 0; j < MPW; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < NK; ++kk) {
+      Frag a[MPW];
+#pragma unroll
+      for (int j = 0; j < MPW; ++j)
+        if (tile_ok(j)) a[j] = load_fragK<E, D>(Ub, LR, 16 * (mb + WPF * j), kk * KS, lane);
+#pragma unroll
+      for (int j = 0; j < MPW; ++j)
+        if (tile_ok(j)) acc[j] = MK::mma(a[j], bw[kk], acc[j]);
+      if constexpr (sizeof(E) == 2) {
+        if (with_lo) {
+#pragma unroll
+          for (int j = 0; j < MPW; ++j)
+            if (tile_ok(j)) a[j] = load_fragK<E, D>(Ul, LR, 16 * (mb + WPF * j), kk * KS, lane);
+#pragma unroll
+          for (int j = 0; j < MPW; ++j)
+            if (tile_ok(j)) acc[j] = MK::mma(a[j], bw[kk], acc[j]);
+        }
+      }
+    }
+  };
+
+  // ---- phase B: refinement pairs, one step l at a time ----
+  Acc<C, D, NW> vacc;    // sum_l (Gam * K K_l^T)_{i<t} W_l       [t][f]
+  Acc<D, C, NW> oacc;    // O_loc^T                              [f][t]
+  Acc<D, D, NW> hacc;    // H                                    [r][n]
+  vacc.zero();
+  oacc.zero();
+  hacc.zero();
+  {
+    E* Klr = reinterpret_cast<E*>(smem + LY::B_KLR);
+    E* KltD = reinterpret_cast<E*>(smem + LY::B_KLTD);
+    E* Wlt = reinterpret_cast<E*>(smem + LY::B_WLT);
+    E* F = reinterpret_cast<E*>(smem + LY::B_F);
+    E* Rl = reinterpret_cast<E*>(smem + LY::B_RL);
+    for (int l = 0; l < L; ++l) {
+      if constexpr (FUSE) {
+        // delta = act(p * r), r -= delta, w = beta^(l) delta  -> W_l^T;
+        // k^(l) -> K_l rows and (D K_l)^T.  The next projection's weight
+        // fragments are requested before each pass's arithmetic.
+        const float* Gt = reinterpret_cast<const float*>(smem + LY::F_G);
+        f32x4 acc[MPW];
+        fgemm(true, acc);                                 // p^(l)
+        load_w(fz.Wk + ((long)h * L + l) * D * D);        // W_k^(l)
+        if (l == 0) __syncthreads();                      // step gates visible
+#pragma unroll
+        for (int j = 0; j < MPW; ++j) {
+          if (!tile_ok(j)) continue;
+          const int t0m = 16 * (mb + WPF * j) + 4 * (lane >> 4);
+          E wv[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const float z = acc[j][i] * r[j][i];
+            float dl;
+            if constexpr (ACT == ACT_IDENTITY) dl = z;
+            else dl = gelu_erf(z);
+            r[j][i] -= dl;
+            wv[i] = to_t<E>(Gt[l * C + t0m + i] * dl);
+          }
+          st4(Wlt + f * LT + t0m, wv);
+        }
+        fgemm(false, acc);                                // k^(l)
+        if (l + 1 < L) load_w(fz.Wp + ((long)h * L + l + 1) * D * D);   // W_p^(l+1)
+#pragma unroll
+        for (int j = 0; j < MPW; ++j) {
+          if (!tile_ok(j)) continue;
+          const int t0m = 16 * (mb + WPF * j) + 4 * (lane >> 4);
+          E kd[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const E kb = to_t<E>(acc[j][i]);
+            Klr[(t0m + i) * LR + f] = kb;
+            kd[i] = to_t<E>(to_f(kb) * Dv[t0m + i]);
+          }
+          st4(KltD + f * LT + t0m, kd);
+        }
+      } else {
+        kn.store_rows(Klr, LR, tid);
+        kn.store_transposed(KltD, LT, Dv, tid);
+        wn.store_transposed(Wlt, LT, nullptr, tid);
+      }
+      __syncthreads();
+      if constexpr (!FUSE) {
+        if (l + 1 < L) {   // next step's tiles are in flight during this step's products
+          kn.load(Klb + (long)(l + 1) * Tp * D, D, C, tid);
+          wn.load(Wlb + (long)(l + 1) * Tp * D, D, C, tid);
+        }
+      }
+      {
+        Acc<C, C, NW> a;   // [i][t] = K_l,i . K_t  ->  F[t][i], i < t
+        a.zero();
+        gemm_acc<E, C, C, D, NW, true, true>(a, Klr, LR, Kr, LR, wave, lane);
+        for_tiles(a, wave, lane, [&](int i0, int t, const f32x4& x) {
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int i = i0 + r;
+            F[t * LT + i] = to_t<E>(i < t ? __expf(g[t] - g[i]) * x[r] : 0.f);
+          }
+        });
+        if constexpr (!BWD) {
+          Acc<C, C, NW> p;   // [i][t] = K_l,i . Q_t  ->  R_l[t][i], i <= t
+          p.zero();
+          gemm_acc<E, C, C, D, NW, true, true>(p, Klr, LR, Qr, LR, wave, lane);
+          for_tiles(p, wave, lane, [&](int i0, int t, const f32x4& x) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+              const int i = i0 + r;
+              Rl[t * LT + i] = to_t<E>(i <= t ? __expf(g[t] - g[i]) * x[r] : 0.f);
+            }
+          });
+        }
+      }
+      __syncthreads();
+      gemm_acc<E, C, D, C, NW, true, true>(vacc, F, LT, Wlt, LT, wave, lane);
+      if constexpr (!BWD) gemm_acc<E, D, C, C, NW, true, true>(oacc, Wlt, LT, Rl, LT, wave, lane);
+      gemm_acc<E, D, D, C, NW, true, true>(hacc, Wlt, LT, KltD, LT, wave, lane);
+      __syncthreads();
+    }
+  }
+
+  // ---- phase T: A = diag(beta) (Gam * K K^T)_{i<t};  T = (I + A)^{-1} ----
+  RegTile<E, C, D, NT> vn;   // V rows, in flight during the solve
+  vn.load(vc, ts, nval, tid);
+  E* Tb = reinterpret_cast<E*>(smem + LY::C_TB);
+  {
+    float* Af = reinterpret_cast<float*>(smem + LY::T_AF);
+    float* Tf = reinterpret_cast<float*>(smem + LY::T_TF);
+    float* Xs = reinterpret_cast<float*>(smem + LY::T_XS);
+    Acc<C, C, NW> a;   // [t][i] = K_t . K_i
+    a.zero();
+    gemm_acc<E, C, C, D, NW, true, true>(a, Kr, LR, Kr, LR, wave, lane);
+    for_tiles(a, wave, lane, [&](int t0, int i, const f32x4& x) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = t0 + r;
+        Af[t * LA + i] = i < t ? bt[t] * __expf(g[t] - g[i]) * x[r] : 0.f;
+      }
+    });
+    __syncthreads();
+    invert_unit_lower<C, NW>(Af, Tf, Xs, tid);
+    for (int e = tid; e < C * C; e += NT) Tb[(e / C) * LT + (e % C)] = to_t<E>(Tf[(e / C) * LA + (e % C)]);
+    __syncthreads();
+  }
+
+  // ---- phase C ----
+  E* Ktbe = reinterpret_cast<E*>(smem + LY::C_KTBE);   // (beta e K)^T, later Wk^T
+  E* KtD = reinterpret_cast<E*>(smem + LY::C_KTD);     // (D K)^T
+  E* Vt = reinterpret_cast<E*>(smem + LY::C_VT);       // (beta V')^T, later U^T / Qt^T
+  E* R0 = reinterpret_cast<E*>(smem + LY::C_R0);
+  E* Vr = reinterpret_cast<E*>(smem + LY::C_V);        // V rows, later dO^T
+  for (int e = tid; e < C * D; e += NT) {
+    const int t = e / D, f = e % D;
+    const float kv = to_f(Kr[t * LR + f]);
+    Ktbe[f * LT + t] = to_t<E>(be[t] * kv);
+    KtD[f * LT + t] = to_t<E>(Dv[t] * kv);
+  }
+  vn.store_rows(Vr, LR, tid);
+  RegTile<E, C, D, NT, true> on;   // dO rows (backward mode), in flight during the products below
+  if constexpr (BWD) on.load(dO + row0 * D, ts, nval, tid);
+  // the next chunk's first operands are fetched during the rest of this one
+  // (issued after every load this chunk still waits for: loads complete in
+  // order)
+  if constexpr (PERSIST) {
+    if (vid + vstride < nblk) prefetch(vid + vstride);
+  }
+  __syncthreads();
+  for_tiles(vacc, wave, lane, [&](int t0, int f, const f32x4& x) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = t0 + r;
+      Vt[f * LT + t] = to_t<E>(bt[t] * (to_f(Vr[t * LR + f]) - x[r]));
+    }
+  });
+  __syncthreads();
+  {
+    Acc<C, D, NW> ua, wa;   // U[t][f], Wk[t][f]
+    ua.zero();
+    wa.zero();
+    gemm_acc<E, C, D, C, NW, true, true>(ua, Tb, LT, Vt, LT, wave, lane);
+    gemm_acc<E, C, D, C, NW, true, true>(wa, Tb, LT, Ktbe, LT, wave, lane);
+    __syncthreads();
+    for_tiles(ua, wave, lane, [&](int t0, int f, const f32x4& x) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Vt[f * LT + t0 + r] = to_t<E>(x[r]);
+    });
+    for_tiles(wa, wave, lane, [&](int t0, int f, const f32x4& x) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Ktbe[f * LT + t0 + r] = to_t<E>(x[r]);
+    });
+  }
+  __syncthreads();
+  E* Ut = Vt;
+  E* Wkt = Ktbe;
+  const long cidx = (long)bh * NC + c;
+  if (UTo) {   // U^T, Wk^T [D][C] for the reverse chunk kernels (backward mode, training forward)
+    s2g_rows<E, D, C, NT>(UTo + cidx * D * C, C, Ut, LT, D, tid);
+    s2g_rows<E, D, C, NT>(WkTo + cidx * D * C, C, Wkt, LT, D, tid);
+  }
+
+  // H += U^T diag(D) K;  stored transposed (HT[n][r])
+  gemm_acc<E, D, D, C, NW, true, true>(hacc, Ut, LT, KtD, LT, wave, lane);
+  {
+    float* HTc = HT + cidx * D * D;
+    for_tiles(hacc, wave, lane, [&](int r0, int n, const f32x4& x) {
+      *reinterpret_cast<f32x4*>(HTc + (long)n * D + r0) = x;
+    });
+  }
+  {
+    Acc<D, D, NW> ma;   // [k][n] = sum_t Wk[t][k] D_t K[t][n] = M[k][n]  -> stored as Mt[n][k]
+    ma.zero();
+    gemm_acc<E, D, D, C, NW, true, true>(ma, Wkt, LT, KtD, LT, wave, lane);
+    E* Mtc = Mt + cidx * D * D;
+    for_tiles(ma, wave, lane, [&](int k0, int n, const f32x4& x) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) Mtc[(long)n * D + k0 + r] = to_t<E>(x[r]);
+    });
+  }
+  {
+    Acc<C, C, NW> a;   // [i][t] = K_i . Q_t  ->  R0[t][i], i <= t
+    a.zero();
+    gemm_acc<E, C, C, D, NW, true, true>(a, Kr, LR, Qr, LR, wave, lane);
+    for_tiles(a, wave, lane, [&](int i0, int t, const f32x4& x) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int i = i0 + r;
+        R0[t * LT + i] = to_t<E>(i <= t ? __expf(g[t] - g[i]) * x[r] : 0.f);
+      }
+    });
+  }
+  __syncthreads();
+  if constexpr (!BWD) {
+    Acc<D, C, NW> qa;   // [f][t] = sum_i Wk[i][f] R0[t][i]
+    qa.zero();
+    gemm_acc<E, D, C, C, NW, true, true>(qa, Wkt, LT, R0, LT, wave, lane);
+    E* Qtc = Qt + cidx * C * D;
+    for_tiles(qa, wave, lane, [&](int f0, int t, const f32x4& x) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        Qtc[(long)t * D + f0 + r] = to_t<E>(ev[t] * to_f(Qr[t * LR + f0 + r]) - x[r]);
+    });
+    gemm_acc<E, D, C, C, NW, true, true>(oacc, Ut, LT, R0, LT, wave, lane);
+    float* Oc = Oloc + cidx * C * D;
+    for_tiles(oacc, wave, lane, [&](int f0, int t, const f32x4& x) {
+      *reinterpret_cast<f32x4*>(Oc + (long)t * D + f0) = x;
+    });
+  } else {
+    Acc<C, D, NW> qa;   // [t][f] = sum_i R0[t][i] Wk[i][f]  ->  Qt^T[f][t]
+    qa.zero();
+    gemm_acc<E, C, D, C, NW, true, true>(qa, R0, LT, Wkt, LT, wave, lane);
+    E* Qtt = Vt;        // U^T is dead in backward mode once H is done
+    for_tiles(qa, wave, lane, [&](int t0, int f, const f32x4& x) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = t0 + r;
+        Qtt[f * LT + t] = to_t<E>(ev[t] * to_f(Qr[t * LR + f]) - x[r]);
+      }
+    });
+    E* dOt = Vr;
+    on.store_transposed(dOt, LT, nullptr, tid);
+    __syncthreads();
+    Acc<D, D, NW> ea;   // E[r][n] = sum_t dO[t][r] Qt[t][n]  -> stored as ET[n][r]
+    ea.zero();
+    gemm_acc<E, D, D, C, NW, true, true>(ea, dOt, LT, Qtt, LT, wave, lane);
+    float* ETc = ET + cidx * D * D;
+    for_tiles(ea, wave, lane, [&](int r0, int n, const f32x4& x) {
+      *reinterpret_cast<f32x4*>(ETc + (long)n * D + r0) = x;
+    });
+  }
+  if constexpr (!PERSIST) break;
+  __syncthreads();   // LDS is reused by the next chunk
+  }
+}
+
+template <typename E, int D, int C, bool BWD, bool FUSE, int ACT, int OFF>
+hipError_t chunk_launch_k(const Dims& d, const E* q, const E* k, const E* v, const float* alpha,
+                          const float* beta, const E* Kl, const E* Wl, const E* dO, E* Mt,
+                          float* HT, E* Qt, float* Oloc, float* gC, float* ET, E* UT, E* WkT,
+                          const FuseIn<E>& fz, hipStream_t s) {
+  if constexpr (sizeof(E) == 4 && D * C > 2048) {   // fp32 envelope
+    return hipErrorInvalidValue;
+  } else {
+    auto kern = chunk_fwd_kernel<E, D, C, BWD, FUSE, ACT, OFF>;
+    const int nblk = d.B * d.H * d.NC;
+    hipLaunchKernelGGL(kern, dim3(D >= 128 ? persistent_grid(kern, CF_NT, nblk) : nblk),
+                       dim3(CF_NT), 0, s, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC,
+                       ET, UT, WkT, d.B, d.T, d.H, d.L, d.NC, d.Tp, d.cu, fz);
+    return hipGetLastError();
+  }
+}
+
+// The fused forward for one (activation, tap offset) variant; instantiated
+// in chunk_fused_<activation>.hip.
+template <typename E, int ACT, int OFF>
+hipError_t launch_chunk_fused_var(const Dims& d, const E* q, const E* k, const E* v,
+                                  const float* alpha, const float* beta, const FuseIn<E>& fz,
+                                  E* Mt, float* HT, E* Qt, float* Oloc, float* gC,
+                                  hipStream_t s) {
+  auto go = [&](auto dc) -> hipError_t {
+    constexpr int D = decltype(dc)::first_type::value, C = decltype(dc)::second_type::value;
+    if constexpr (sizeof(E) == 4 && D > 64) {
+      return hipErrorInvalidValue;
+    } else {
+      return chunk_launch_k<E, D, C, false, true, ACT, OFF>(
+          d, q, k, v, alpha, beta, nullptr, nullptr, nullptr, Mt, HT, Qt, Oloc, gC, nullptr,
+          nullptr, nullptr, fz, s);
+    }
+  };
+  auto byc = [&](auto dd) -> hipError_t {
+    typedef decltype(dd) DI;
+    switch (d.C) {
+      case 16: return go(std::pair<DI, std::integral_constant<int, 16>>());
+      case 32: return go(std::pair<DI, std::integral_constant<int, 32>>());
+      case 64: return go(std::pair<DI, std::integral_constant<int, 64>>());
+    }
+    return hipErrorInvalidValue;
+  };
+  switch (d.D) {
+    case 16: return byc(std::integral_constant<int, 16>());
+    case 32: return byc(std::integral_constant<int, 32>());
+    case 64: return byc(std::integral_constant<int, 64>());
+    case 128: return byc(std::integral_constant<int, 128>());
+  }
+  return hipErrorInvalidValue;
+}
+
+#define PRISM_CHUNK_FUSED_VARIANT(E, ACT, OFF)                                                    \
+  extern template hipError_t launch_chunk_fused_var<E, ACT, OFF>(                                \
+      const Dims&, const E*, const E*, const E*, const float*, const float*, const FuseIn<E>&,  \
+      E*, float*, E*, float*, float*, hipStream_t);
+PRISM_CHUNK_FUSED_VARIANT(bf16, ACT_GELU, 0)
+PRISM_CHUNK_FUSED_VARIANT(bf16, ACT_GELU, 1)
+PRISM_CHUNK_FUSED_VARIANT(bf16, ACT_IDENTITY, 0)
+PRISM_CHUNK_FUSED_VARIANT(bf16, ACT_IDENTITY, 1)
+PRISM_CHUNK_FUSED_VARIANT(float, ACT_GELU, 0)
+PRISM_CHUNK_FUSED_VARIANT(float, ACT_GELU, 1)
+PRISM_CHUNK_FUSED_VARIANT(float, ACT_IDENTITY, 0)
+PRISM_CHUNK_FUSED_VARIANT(float, ACT_IDENTITY, 1)
+#undef PRISM_CHUNK_FUSED_VARIANT
+
+}  // namespace prism

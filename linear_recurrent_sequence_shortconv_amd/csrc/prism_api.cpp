@@ -299,14 +299,29 @@ prism_status run_forward(const prism::Dims& d, const void* q, const void* k, con
   const E* k_ = static_cast<const E*>(k);
   const E* v_ = static_cast<const E*>(v);
   const E* hist_ = static_cast<const E*>(hist);
-  if (d.L > 0)
-    HIP_TRY("refine_fwd", s,
-            prism::launch_refine_fwd<E>(d, v_, hist_, static_cast<const E*>(conv),
-                                        static_cast<const E*>(Wk), static_cast<const E*>(Wp),
-                                        static_cast<const E*>(wbeta), w.Kl, w.Wl, s));
-  HIP_TRY("chunk_fwd", s,
-          prism::launch_chunk_fwd<E>(d, q_, k_, v_, alpha, beta, w.Kl, w.Wl, nullptr, w.Mt, w.HT,
-                                     w.Qt, w.Oloc, w.gC, nullptr, w.UT, w.WkT, s));
+  if (d.L > 0 && !keep) {
+    // inference: the chunk kernel forms the refinement pairs itself, so they
+    // never go to HBM
+    prism::FuseIn<E> fz;
+    fz.hist = hist_;
+    fz.conv = static_cast<const E*>(conv);
+    fz.Wk = static_cast<const E*>(Wk);
+    fz.Wp = static_cast<const E*>(Wp);
+    fz.wbeta = static_cast<const E*>(wbeta);
+    HIP_TRY("chunk_fwd_fused", s,
+            prism::launch_chunk_fwd_fused<E>(d, q_, k_, v_, alpha, beta, fz, w.Mt, w.HT, w.Qt,
+                                             w.Oloc, w.gC, s));
+  } else {
+    // training forward (the backward reads the pairs), or no refinement
+    if (d.L > 0)
+      HIP_TRY("refine_fwd", s,
+              prism::launch_refine_fwd<E>(d, v_, hist_, static_cast<const E*>(conv),
+                                          static_cast<const E*>(Wk), static_cast<const E*>(Wp),
+                                          static_cast<const E*>(wbeta), w.Kl, w.Wl, s));
+    HIP_TRY("chunk_fwd", s,
+            prism::launch_chunk_fwd<E>(d, q_, k_, v_, alpha, beta, w.Kl, w.Wl, nullptr, w.Mt,
+                                       w.HT, w.Qt, w.Oloc, w.gC, nullptr, w.UT, w.WkT, s));
+  }
   HIP_TRY("state_fwd", s,
           prism::launch_state_pass<E>(d, S0, w.Mt, w.HT, w.gC, w.Sc, ST, false, false, s));
   HIP_TRY("out_fwd", s, prism::launch_out_fwd<E>(d, w.Sc, w.Qt, w.Oloc, static_cast<E*>(o), s));

@@ -115,6 +115,29 @@ __device__ inline typename Mfma<T>::frag load_frag(const T* p, int ld, int row0,
   return f;
 }
 
+// MFMA of the projection kernels for an inner size K: bf16 takes
+// v_mfma_f32_16x16x32_bf16 (8 k per lane) unless K = 16, where it takes
+// v_mfma_f32_16x16x16_bf16 (4 k per lane); fp32 takes 16x16x4 in both cases.
+template <typename T, int K> struct MfmaK : Mfma<T> {};
+template <> struct MfmaK<bf16, 16> {
+  static constexpr int KSTEP = 16;
+  static constexpr int KPL = 4;
+  typedef s16x4 frag;
+  __device__ static inline f32x4 mma(const frag& a, const frag& b, const f32x4& c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+  }
+};
+
+// k-contiguous MfmaK fragment: KPL consecutive k (from k0 + KPL (lane >> 4))
+// of row row0 + (lane & 15), from LDS or global memory
+template <typename T, int K>
+__device__ inline typename MfmaK<T, K>::frag load_fragK(const T* p, int ld, int row0, int k0, int lane) {
+  typedef MfmaK<T, K> MK;
+  const int r = row0 + (lane & 15);
+  const int k = k0 + MK::KPL * (lane >> 4);
+  return *reinterpret_cast<const typename MK::frag*>(p + r * ld + k);
+}
+
 // --------------------------------------------------------------------------
 // wave-grid tiling of an M x N output over NW waves
 // --------------------------------------------------------------------------

@@ -44,6 +44,25 @@ hipError_t launch_chunk_fwd(const Dims& d, const E* q, const E* k, const E* v, c
                             float* HT, E* Qt, float* Oloc, float* gC, float* ET, E* UT, E* WkT,
                             hipStream_t s);
 
+// Inputs of the refinement when the chunk kernel forms the pairs itself.
+template <typename E>
+struct FuseIn {
+  const E* hist = nullptr;    // [B, 4, H, D] v rows before each sequence (nullptr: zeros)
+  const E* conv = nullptr;    // [H, D, 4]
+  const E* Wk = nullptr;      // [H, L, D, D]
+  const E* Wp = nullptr;      // [H, L, D, D]
+  const E* wbeta = nullptr;   // [H, L, D]
+};
+
+// Forward mode of launch_chunk_fwd with the refinement pairs formed inside
+// the kernel from v (1 <= L <= 8): writes Mt, HT, Qt, Oloc, gC.  Same results
+// as launch_refine_fwd followed by launch_chunk_fwd.
+template <typename E>
+hipError_t launch_chunk_fwd_fused(const Dims& d, const E* q, const E* k, const E* v,
+                                  const float* alpha, const float* beta, const FuseIn<E>& fz,
+                                  E* Mt, float* HT, E* Qt, float* Oloc, float* gC,
+                                  hipStream_t s);
+
 // ET per chunk from a kept Qt and dO (the backward of a training forward).
 template <typename E>
 hipError_t launch_et(const Dims& d, const E* Qt, const E* dO, float* ET, hipStream_t s);

@@ -39,19 +39,23 @@ constexpr int rb_own(int off) { return RB_TT - 3 - off; }
 
 // MFMA A-operand fragment of bf16 (or fp32) values read from an fp32 LDS
 // row tile X[row][k] (k contiguous), rounded to the operand type.
-template <typename E>
-__device__ inline typename Mfma<E>::frag frag_from_f32(const float* X, int ld, int row0, int k0, int lane) {
+template <typename E, int K>
+__device__ inline typename MfmaK<E, K>::frag frag_from_f32(const float* X, int ld, int row0, int k0, int lane) {
   if constexpr (sizeof(E) == 4) {
     return load_frag<float, true>(X, ld, row0, k0, lane);
   } else {
-    const float* p = X + (row0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4);
-    const f32x4 x0 = *reinterpret_cast<const f32x4*>(p);
-    const f32x4 x1 = *reinterpret_cast<const f32x4*>(p + 4);
-    bf16x8 f;
+    constexpr int KPL = MfmaK<E, K>::KPL;
+    const float* p = X + (row0 + (lane & 15)) * ld + k0 + KPL * (lane >> 4);
+    typename MfmaK<E, K>::frag f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      f[j] = (bf16)x0[j];
-      f[4 + j] = (bf16)x1[j];
+    for (int h = 0; h < KPL / 4; ++h) {
+      const f32x4 x = *reinterpret_cast<const f32x4*>(p + 4 * h);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const bf16 y = (bf16)x[j];
+        if constexpr (KPL == 4) f[4 * h + j] = __builtin_bit_cast(short, y);
+        else f[4 * h + j] = y;
+      }
     }
     return f;
   }
@@ -73,7 +77,8 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
   // feature tile n exists; always true when the tiles divide evenly over the
   // feature groups (then the test folds away at compile time)
 #define FT_OK(n) (NFT % 4 == 0 || (n) < NFT)
-  constexpr int KS = Mfma<E>::KSTEP;
+  typedef MfmaK<E, D> MK;
+  constexpr int KS = MK::KSTEP;
   constexpr int VN = 16 / sizeof(E);
   constexpr int HL = 3 + OFF;             // v rows before the tile that the taps reach
   constexpr int OWN = rb_own(OFF);
@@ -197,29 +202,29 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
     for (int m = 0; m < 2; ++m)
 #pragma unroll
       for (int nn = 0; nn < FPW; ++nn) acc[m][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
-    typename Mfma<E>::frag bws[FPW][D / KS];
+    typename MK::frag bws[FPW][D / KS];
 #pragma unroll
     for (int nn = 0; nn < FPW; ++nn)
 #pragma unroll
       for (int kk = 0; kk < D / KS; ++kk)
-        if (FT_OK(fq + 4 * nn)) bws[nn][kk] = load_frag<E, true>(W, D, 16 * (fq + 4 * nn), kk * KS, lane);
+        if (FT_OK(fq + 4 * nn)) bws[nn][kk] = load_fragK<E, D>(W, D, 16 * (fq + 4 * nn), kk * KS, lane);
 #pragma unroll
     for (int k0 = 0; k0 < D; k0 += KS) {
-      typename Mfma<E>::frag a[2], al[2];
+      typename MK::frag a[2], al[2];
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        a[m] = load_frag<E, true>(ubuf, LD, 16 * m, k0, lane);
-        if constexpr (sizeof(E) == 2) al[m] = load_frag<E, true>(ulo, LD, 16 * m, k0, lane);
+        a[m] = load_fragK<E, D>(ubuf, LD, 16 * m, k0, lane);
+        if constexpr (sizeof(E) == 2) al[m] = load_fragK<E, D>(ulo, LD, 16 * m, k0, lane);
       }
 #pragma unroll
       for (int nn = 0; nn < FPW; ++nn) {
         const int n = fq + 4 * nn;
         if (FT_OK(n)) {
-          const typename Mfma<E>::frag bw = bws[nn][k0 / KS];
+          const typename MK::frag bw = bws[nn][k0 / KS];
 #pragma unroll
           for (int m = 0; m < 2; ++m) {
-            acc[m][nn] = Mfma<E>::mma(a[m], bw, acc[m][nn]);
-            if constexpr (sizeof(E) == 2) acc[m][nn] = Mfma<E>::mma(al[m], bw, acc[m][nn]);
+            acc[m][nn] = MK::mma(a[m], bw, acc[m][nn]);
+            if constexpr (sizeof(E) == 2) acc[m][nn] = MK::mma(al[m], bw, acc[m][nn]);
           }
         }
       }
@@ -229,27 +234,27 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
   // LDS when XF) and WT[j][i] = W[i][j]
   auto project_t = [&](auto xf, const void* X, int ldx, const E* WT, f32x4 (&acc)[2][FPW]) {
     constexpr bool XF = decltype(xf)::value;
-    typename Mfma<E>::frag bws[FPW][D / KS];
+    typename MK::frag bws[FPW][D / KS];
 #pragma unroll
     for (int nn = 0; nn < FPW; ++nn)
 #pragma unroll
       for (int kk = 0; kk < D / KS; ++kk)
-        if (FT_OK(fq + 4 * nn)) bws[nn][kk] = load_frag<E, true>(WT, D, 16 * (fq + 4 * nn), kk * KS, lane);
+        if (FT_OK(fq + 4 * nn)) bws[nn][kk] = load_fragK<E, D>(WT, D, 16 * (fq + 4 * nn), kk * KS, lane);
 #pragma unroll
     for (int k0 = 0; k0 < D; k0 += KS) {
-      typename Mfma<E>::frag a[2];
+      typename MK::frag a[2];
 #pragma unroll
       for (int m = 0; m < 2; ++m) {
-        if constexpr (XF) a[m] = frag_from_f32<E>(static_cast<const float*>(X), ldx, 16 * m, k0, lane);
-        else a[m] = load_frag<E, true>(static_cast<const E*>(X), ldx, 16 * m, k0, lane);
+        if constexpr (XF) a[m] = frag_from_f32<E, D>(static_cast<const float*>(X), ldx, 16 * m, k0, lane);
+        else a[m] = load_fragK<E, D>(static_cast<const E*>(X), ldx, 16 * m, k0, lane);
       }
 #pragma unroll
       for (int nn = 0; nn < FPW; ++nn) {
         const int n = fq + 4 * nn;
         if (FT_OK(n)) {
-          const typename Mfma<E>::frag bw = bws[nn][k0 / KS];
+          const typename MK::frag bw = bws[nn][k0 / KS];
 #pragma unroll
-          for (int m = 0; m < 2; ++m) acc[m][nn] = Mfma<E>::mma(a[m], bw, acc[m][nn]);
+          for (int m = 0; m < 2; ++m) acc[m][nn] = MK::mma(a[m], bw, acc[m][nn]);
         }
       }
     }

@@ -17,6 +17,10 @@
 // shared MFMA A operand in LDS, and the residual chain stays in registers in
 // the accumulator layout.  Outputs are staged in LDS and stored as full
 // 16-byte rows.
+// Multiply-adds fuse only within one expression (the C rule), never across
+// statements: the refinement kernel and the chunk kernel that repeats its
+// arithmetic then round identically, whatever code surrounds each.
+#pragma clang fp contract(on)
 #include "prism_common.h"
 #include "prism_internal.h"
 
@@ -38,7 +42,8 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
   // feature tile n exists; always true when the tiles divide evenly over the
   // feature groups (then the test folds away at compile time)
 #define FT_OK(n) (NFT % RF_NW == 0 || (n) < NFT)
-  constexpr int KS = Mfma<E>::KSTEP;
+  typedef MfmaK<E, D> MK;
+  constexpr int KS = MK::KSTEP;
   constexpr int NK = D / KS;
   constexpr int VN = 16 / sizeof(E);
   constexpr int HL = 3 + OFF;   // v rows before the tile that the taps reach
@@ -85,14 +90,14 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
     else if (t < 0 && hist) x = ld16(hist + (((long)b * 4 + 4 + t) * H + h) * D + c);
     st16(vbuf + r * D + c, x);
   }
-  typedef typename Mfma<E>::frag Frag;
+  typedef typename MK::frag Frag;
   auto load_w = [&](const E* W, Frag (&bw)[FPW][NK]) {
 #pragma unroll
     for (int nn = 0; nn < FPW; ++nn) {
       const int n = wave + RF_NW * nn;
 #pragma unroll
       for (int kk = 0; kk < NK; ++kk)
-        if (FT_OK(n)) bw[nn][kk] = load_frag<E, true>(W, D, 16 * n, kk * KS, lane);
+        if (FT_OK(n)) bw[nn][kk] = load_fragK<E, D>(W, D, 16 * n, kk * KS, lane);
     }
   };
   Frag bw[FPW][NK];   // weight fragments of the next projection (W_p^(1) now)
@@ -182,22 +187,22 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
     for (int kk = 0; kk < NK; ++kk) {
       Frag a[4];
 #pragma unroll
-      for (int m = 0; m < 4; ++m) a[m] = load_frag<E, true>(ubuf, LD, 16 * m, kk * KS, lane);
+      for (int m = 0; m < 4; ++m) a[m] = load_fragK<E, D>(ubuf, LD, 16 * m, kk * KS, lane);
 #pragma unroll
       for (int nn = 0; nn < FPW; ++nn)
         if (FT_OK(wave + RF_NW * nn)) {
 #pragma unroll
-          for (int m = 0; m < 4; ++m) acc[m][nn] = Mfma<E>::mma(a[m], bw[nn][kk], acc[m][nn]);
+          for (int m = 0; m < 4; ++m) acc[m][nn] = MK::mma(a[m], bw[nn][kk], acc[m][nn]);
         }
       if constexpr (sizeof(E) == 2) {
         if (with_lo) {
 #pragma unroll
-          for (int m = 0; m < 4; ++m) a[m] = load_frag<E, true>(ulo, LD, 16 * m, kk * KS, lane);
+          for (int m = 0; m < 4; ++m) a[m] = load_fragK<E, D>(ulo, LD, 16 * m, kk * KS, lane);
 #pragma unroll
           for (int nn = 0; nn < FPW; ++nn)
             if (FT_OK(wave + RF_NW * nn)) {
 #pragma unroll
-              for (int m = 0; m < 4; ++m) acc[m][nn] = Mfma<E>::mma(a[m], bw[nn][kk], acc[m][nn]);
+              for (int m = 0; m < 4; ++m) acc[m][nn] = MK::mma(a[m], bw[nn][kk], acc[m][nn]);
             }
         }
       }

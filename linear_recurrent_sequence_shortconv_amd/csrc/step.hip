@@ -151,14 +151,15 @@ __global__ __launch_bounds__(DR_NT) void decode_refine_kernel(
     const E* __restrict__ Wk, const E* __restrict__ Wp, const E* __restrict__ wbeta,
     E* __restrict__ Kl, E* __restrict__ Wl, int B, int H, int L) {
   constexpr int LD = ldpad<E>(D);
-  constexpr int KS = Mfma<E>::KSTEP;
+  typedef MfmaK<E, D> MK;
+  constexpr int KS = MK::KSTEP;
   constexpr int NK = D / KS;
   constexpr int VN = 16 / (int)sizeof(E);
   constexpr int FG = D < DR_FG ? D : DR_FG;   // features of this workgroup
   constexpr int NFG = D / FG;
   constexpr int RW = FG + 4;                  // fp32 residual rows
   constexpr int GT = DR_NT / DR_ROWS;         // threads per gate dot product
-  typedef typename Mfma<E>::frag Frag;
+  typedef typename MK::frag Frag;
   __shared__ __attribute__((aligned(16))) E ubuf[DR_ROWS * LD];
   __shared__ __attribute__((aligned(16))) E ulo[sizeof(E) == 2 ? DR_ROWS * LD : 16];
   __shared__ __attribute__((aligned(16))) float rbuf[DR_ROWS * RW];
@@ -182,8 +183,8 @@ __global__ __launch_bounds__(DR_NT) void decode_refine_kernel(
     const E* K = Wk + ((long)h * L + l) * D * D;
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) {
-      p[kk] = load_frag<E, true>(P, D, 16 * n, kk * KS, lane);
-      k[kk] = load_frag<E, true>(K, D, 16 * n, kk * KS, lane);
+      p[kk] = load_fragK<E, D>(P, D, 16 * n, kk * KS, lane);
+      k[kk] = load_fragK<E, D>(K, D, 16 * n, kk * KS, lane);
     }
   };
   if (has) {
@@ -277,12 +278,12 @@ __global__ __launch_bounds__(DR_NT) void decode_refine_kernel(
     for (int kk = 0; kk < NK; ++kk) {
 #pragma unroll
       for (int m = 0; m < DR_MPW; ++m) {
-        const Frag a = load_frag<E, true>(ubuf, LD, rb + 16 * m, kk * KS, lane);
-        ap[m] = Mfma<E>::mma(a, wp[sl][kk], ap[m]);
-        ak[m] = Mfma<E>::mma(a, wk[sl][kk], ak[m]);
+        const Frag a = load_fragK<E, D>(ubuf, LD, rb + 16 * m, kk * KS, lane);
+        ap[m] = MK::mma(a, wp[sl][kk], ap[m]);
+        ak[m] = MK::mma(a, wk[sl][kk], ak[m]);
         if constexpr (sizeof(E) == 2) {
-          const Frag al = load_frag<E, true>(ulo, LD, rb + 16 * m, kk * KS, lane);
-          ap[m] = Mfma<E>::mma(al, wp[sl][kk], ap[m]);
+          const Frag al = load_fragK<E, D>(ulo, LD, rb + 16 * m, kk * KS, lane);
+          ap[m] = MK::mma(al, wp[sl][kk], ap[m]);
         }
       }
     }

@@ -24,8 +24,8 @@ def test_more_than_one_gpu_is_refused():
 def test_algorithmic_counts_cover_every_timed_kernel():
     w = workloads()["lm-T2048"]
     c = bench.algorithmic_counts(w)
-    timer_names = {n for _, names in bench._FAMILIES for n in names} | {"chunk_fwd",
-                                                                          "chunk_fwd_bwdmode"}
+    timer_names = {n for _, names in bench._FAMILIES for n in names} | {
+        "chunk_fwd", "chunk_fwd_bwdmode", "chunk_fwd_fused"}
     assert timer_names <= set(c), timer_names - set(c)
     for name, v in c.items():
         assert v["bytes"] > 0 and v["flops"] >= 0 and v["floor_ms"] > 0, name
@@ -40,8 +40,14 @@ def test_algorithmic_counts_cover_every_timed_kernel():
 
 def test_kernel_names_map_to_timer_names():
     assert bench._family("_ZN5prism17refine_bwd_kernelIDF16bLi128ELi4ELi0ELi0EEEv") == ["refine_bwd"]
-    assert bench._family("_ZN5prism16chunk_fwd_kernelIDF16bLi128ELi64ELb1EEEv") == ["chunk_fwd_bwdmode"]
-    assert bench._family("_ZN5prism16chunk_fwd_kernelIDF16bLi128ELi64ELb0EEEv") == ["chunk_fwd"]
+    cf = "_ZN5prism16chunk_fwd_kernelIDF16bLi128ELi64ELb{}ELb{}ELi0ELi1EEEvPKT_S3_"
+    assert bench._family(cf.format(1, 0)) == ["chunk_fwd_bwdmode"]
+    assert bench._family(cf.format(0, 0)) == ["chunk_fwd"]
+    assert bench._family(cf.format(0, 1)) == ["chunk_fwd_fused"]
+    assert bench._family("void prism::chunk_fwd_kernel<__bf16, 128, 64, false, true, 0, 0>(...)") == [
+        "chunk_fwd_fused"]
+    assert bench._family("void prism::chunk_fwd_kernel<__bf16, 128, 64, true, false, 0, 0>(...)") == [
+        "chunk_fwd_bwdmode"]
     assert bench._family("_ZN5prism17step_state_kernelIDF16bLi128EEEv") == ["step_state"]
     assert bench._family("some_other_kernel") is None
 
