@@ -73,9 +73,10 @@ struct ChunkLds {
   static constexpr int O_Q = O_VEC + SZ_VEC;
   static constexpr int O_K = O_Q + SZ_R;
   static constexpr int O_X = O_K + SZ_R;
-  // phase B (per refinement step)
+  // phase B (per refinement step); the fused form keeps K_l transposed
+  static constexpr int SZ_KL = FUSE ? cmax(SZ_R, SZ_T) : SZ_R;
   static constexpr int B_KLR = O_X;
-  static constexpr int B_KLTD = B_KLR + SZ_R;
+  static constexpr int B_KLTD = B_KLR + SZ_KL;
   static constexpr int B_WLT = B_KLTD + SZ_T;
   static constexpr int B_F = B_WLT + SZ_T;
   static constexpr int B_RL = B_F + SZ_CC;
@@ -303,24 +304,30 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
       }
     }
     __syncthreads();
-    // four threads per token, 16-byte reads of u and w_beta
+    // four threads per token (16-byte reads of u and w_beta, each thread a
+    // fixed set of feature blocks in order); NT / 4C groups take the steps
+    // round robin
     const E* wbs = reinterpret_cast<const E*>(smem + LY::F_WB);
     float* Gt = reinterpret_cast<float*>(smem + LY::F_G);
-    if (tid < 4 * C) {
-      const int t = tid >> 2, part = tid & 3;
-      for (int l = 0; l < L; ++l) {
-        float s = 0.f;
-        for (int cc = part * VN; cc < D; cc += 4 * VN) {
+    constexpr int GG = NT / (4 * C);
+    constexpr int KQ = (VPRW + 3) / 4;
+    const int grp = tid / (4 * C), t = (tid % (4 * C)) >> 2, part = tid & 3;
+    for (int l = grp; l < L; l += GG) {
+      float s = 0.f;
+#pragma unroll
+      for (int kq = 0; kq < KQ; ++kq) {
+        const int cc = (part + 4 * kq) * VN;
+        if (VPRW % 4 == 0 || cc < D) {
           const uint4 ua = ld16(Ub + t * LR + cc), wa = ld16(wbs + l * D + cc);
           const E* ue = reinterpret_cast<const E*>(&ua);
           const E* we = reinterpret_cast<const E*>(&wa);
 #pragma unroll
           for (int jj = 0; jj < VN; ++jj) s += to_f(we[jj]) * to_f(ue[jj]);
         }
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        if (part == 0) Gt[l * C + t] = sigmoidf(s);
       }
+      s += __shfl_xor(s, 1);
+      s += __shfl_xor(s, 2);
+      if (part == 0) Gt[l * C + t] = sigmoidf(s);
     }
   }
   // p^(l) = W_p (u_hi + u_lo) or k^(l) = W_k u_hi for the wave's tiles
@@ -396,13 +403,13 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
         for (int j = 0; j < MPW; ++j) {
           if (!tile_ok(j)) continue;
           const int t0m = 16 * (mb + WPF * j) + 4 * (lane >> 4);
-          E kd[4];
+          E kb[4], kd[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            const E kb = to_t<E>(acc[j][i]);
-            Klr[(t0m + i) * LR + f] = kb;
-            kd[i] = to_t<E>(to_f(kb) * Dv[t0m + i]);
+            kb[i] = to_t<E>(acc[j][i]);
+            kd[i] = to_t<E>(to_f(kb[i]) * Dv[t0m + i]);
           }
+          st4(Klr + f * LT + t0m, kb);   // K_l^T
           st4(KltD + f * LT + t0m, kd);
         }
       } else {
@@ -420,7 +427,8 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
       {
         Acc<C, C, NW> a;   // [i][t] = K_l,i . K_t  ->  F[t][i], i < t
         a.zero();
-        gemm_acc<E, C, C, D, NW, true, true>(a, Klr, LR, Kr, LR, wave, lane);
+        if constexpr (FUSE) gemm_acc<E, C, C, D, NW, false, true>(a, Klr, LT, Kr, LR, wave, lane);
+        else gemm_acc<E, C, C, D, NW, true, true>(a, Klr, LR, Kr, LR, wave, lane);
         for_tiles(a, wave, lane, [&](int i0, int t, const f32x4& x) {
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
@@ -431,7 +439,8 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
         if constexpr (!BWD) {
           Acc<C, C, NW> p;   // [i][t] = K_l,i . Q_t  ->  R_l[t][i], i <= t
           p.zero();
-          gemm_acc<E, C, C, D, NW, true, true>(p, Klr, LR, Qr, LR, wave, lane);
+          if constexpr (FUSE) gemm_acc<E, C, C, D, NW, false, true>(p, Klr, LT, Qr, LR, wave, lane);
+          else gemm_acc<E, C, C, D, NW, true, true>(p, Klr, LR, Qr, LR, wave, lane);
           for_tiles(p, wave, lane, [&](int i0, int t, const f32x4& x) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
