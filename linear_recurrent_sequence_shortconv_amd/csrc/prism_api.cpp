@@ -107,8 +107,9 @@ FwdWs<E> carve_fwd(const prism::Dims& d, Carve& cv) {
   const size_t bh = (size_t)d.B * d.H;
   const size_t es = sizeof(E);
   FwdWs<E> w;
-  w.Kl = cv.take<E>(bh * d.L * d.Tp * d.D * es);
-  w.Wl = cv.take<E>(bh * d.L * d.Tp * d.D * es);
+  // no room for the refinement pairs: the inference forward forms them
+  // inside the chunk kernel, the training forward keeps them in its buffer
+  w.Kl = w.Wl = nullptr;
   w.Mt = cv.take<E>(bh * d.NC * d.D * d.D * es);
   w.HT = cv.take<float>(bh * d.NC * d.D * d.D * 4);
   w.Qt = cv.take<E>(bh * d.NC * d.C * d.D * es);
