@@ -196,18 +196,25 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
   pk.store_rows(gkk, LW, tid);
   __syncthreads();
 
-  // p^(l) = W_p^(l) (u_hi + u_lo) for this wave's tiles (same as the forward)
-  auto project = [&](const E* W, f32x4 (&acc)[2][FPW]) {
-#pragma unroll
-    for (int m = 0; m < 2; ++m)
-#pragma unroll
-      for (int nn = 0; nn < FPW; ++nn) acc[m][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
-    typename MK::frag bws[FPW][D / KS];
+  // Weight fragments (B operands) of this wave's feature tiles.  Every
+  // product takes them preloaded: a fragment load issued ahead of the work
+  // that precedes its product keeps its L2 latency off the critical path, and
+  // issuing it before the row prefetches and stores of a step keeps the
+  // product's wait (vmcnt counts in issue order) from covering those.
+  typedef typename MK::frag Frag;
+  auto load_w = [&](const E* W, Frag (&bw)[FPW][D / KS]) {
 #pragma unroll
     for (int nn = 0; nn < FPW; ++nn)
 #pragma unroll
       for (int kk = 0; kk < D / KS; ++kk)
-        if (FT_OK(fq + 4 * nn)) bws[nn][kk] = load_fragK<E, D>(W, D, 16 * (fq + 4 * nn), kk * KS, lane);
+        if (FT_OK(fq + 4 * nn)) bw[nn][kk] = load_fragK<E, D>(W, D, 16 * (fq + 4 * nn), kk * KS, lane);
+  };
+  // p^(l) = W_p^(l) (u_hi + u_lo) for this wave's tiles (same as the forward)
+  auto project = [&](const Frag (&bws)[FPW][D / KS], f32x4 (&acc)[2][FPW]) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m)
+#pragma unroll
+      for (int nn = 0; nn < FPW; ++nn) acc[m][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k0 = 0; k0 < D; k0 += KS) {
       typename MK::frag a[2], al[2];
@@ -231,15 +238,10 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
     }
   };
   // acc += X W  where X holds rows [t][i] (operand type in LDS, or fp32 in
-  // LDS when XF) and WT[j][i] = W[i][j]
-  auto project_t = [&](auto xf, const void* X, int ldx, const E* WT, f32x4 (&acc)[2][FPW]) {
+  // LDS when XF) and bws holds the fragments of WT[j][i] = W[i][j]
+  auto project_t = [&](auto xf, const void* X, int ldx, const Frag (&bws)[FPW][D / KS],
+                       f32x4 (&acc)[2][FPW]) {
     constexpr bool XF = decltype(xf)::value;
-    typename MK::frag bws[FPW][D / KS];
-#pragma unroll
-    for (int nn = 0; nn < FPW; ++nn)
-#pragma unroll
-      for (int kk = 0; kk < D / KS; ++kk)
-        if (FT_OK(fq + 4 * nn)) bws[nn][kk] = load_fragK<E, D>(WT, D, 16 * (fq + 4 * nn), kk * KS, lane);
 #pragma unroll
     for (int k0 = 0; k0 < D; k0 += KS) {
       typename MK::frag a[2];
@@ -268,14 +270,24 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
   constexpr bool REPLAY = LMAX <= 4;
   f32x4 ps[REPLAY ? LMAX : 1][2][FPW];
   float rs[REPLAY ? 1 : LMAX][2][FPW][4];
+  // Up to three steps the registers hold a second fragment set: the next
+  // step's fragments are requested before this step's product, and each
+  // reverse step requests its first product's fragments before the chain
+  // replay.  More steps keep one set, requested just before its product.
+  constexpr bool EARLY_W = LMAX <= 3;
+  Frag bwp[FPW][D / KS];   // W_p^(l) fragments
+  if (EARLY_W && L > 0) load_w(Wp + (long)h * L * D * D, bwp);
 #pragma unroll
   for (int l = 0; l < LMAX; ++l) {
     if (l >= L) break;
+    Frag bwn[FPW][D / KS];
+    if (!EARLY_W) load_w(Wp + ((long)h * L + l) * D * D, bwp);
+    else if (l + 1 < L) load_w(Wp + ((long)h * L + l + 1) * D * D, bwn);
     if constexpr (REPLAY) {
-      project(Wp + ((long)h * L + l) * D * D, ps[l]);
+      project(bwp, ps[l]);
     } else {
       f32x4 p[2][FPW];
-      project(Wp + ((long)h * L + l) * D * D, p);
+      project(bwp, p);
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -287,6 +299,12 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
             if constexpr (ACT == ACT_IDENTITY) r[m][nn][i] -= z;
             else r[m][nn][i] -= gelu_erf(z);
           }
+    }
+    if constexpr (EARLY_W) {
+#pragma unroll
+      for (int nn = 0; nn < FPW; ++nn)
+#pragma unroll
+        for (int kk = 0; kk < D / KS; ++kk) bwp[nn][kk] = bwn[nn][kk];
     }
   }
 
@@ -305,6 +323,10 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
 #pragma unroll
   for (int l = LMAX - 1; l >= 0; --l) {
     if (l >= L) continue;
+    // W_p^(l)^T fragments of this step's first transposed product (in flight
+    // during the chain replay and the gate gradient when EARLY_W)
+    Frag bpt[FPW][D / KS], bkt[FPW][D / KS];
+    if constexpr (EARLY_W) load_w(WpT + ((long)h * L + l) * D * D, bpt);
     // p^(l) and r^(l) of this step
     f32x4 p[2][FPW];
     float rl[2][FPW][4];
@@ -331,7 +353,9 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
               else rl[m][nn][i] -= gelu_erf(z);
             }
     } else {
-      project(Wp + ((long)h * L + l) * D * D, p);
+      Frag bw[FPW][D / KS];
+      load_w(Wp + ((long)h * L + l) * D * D, bw);
+      project(bw, p);
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -395,8 +419,11 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
         }
       }
     __syncthreads();
-    // the next step's dW, dK rows (or, in the last step, the direct
-    // v-gradient) are fetched during the products below
+    // weight fragments of both products first, then the next step's dW, dK
+    // rows (or, in the last step, the direct v-gradient), fetched during the
+    // products below
+    if constexpr (!EARLY_W) load_w(WpT + ((long)h * L + l) * D * D, bpt);
+    else load_w(WkT + ((long)h * L + l) * D * D, bkt);
     if (l > 0) {
       const long lrow = (bh * L + (l - 1)) * Tp + t0;
       pw.load(dWl + lrow * D, D, nrow, tid);
@@ -418,8 +445,9 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
     }
     const long lrow = (bh * L + l) * Tp + t0;
     s2g_rows<E, RB_TT, D, RB_NT>(dPo + lrow * D, D, dpbuf, LD, own, tid);
-    project_t(std::false_type{}, dpbuf, LD, WpT + ((long)h * L + l) * D * D, du);
-    project_t(std::true_type{}, gkk, LW, WkT + ((long)h * L + l) * D * D, du);
+    project_t(std::false_type{}, dpbuf, LD, bpt, du);
+    if constexpr (!EARLY_W) load_w(WkT + ((long)h * L + l) * D * D, bkt);
+    project_t(std::true_type{}, gkk, LW, bkt, du);
     // du += dlogit w_beta; dw_beta partial = sum over owned t of dlogit_t u_t
     const E* wb = wbl + l * D;
 #pragma unroll
@@ -565,6 +593,7 @@ hipError_t launch_refine_bwd_main(const Dims& d, const RefineBwdArgs<E>& a, hipS
   auto by_l = [&](auto dd) {
     constexpr int D = decltype(dd)::value;
     if (d.L <= 2) return go(refine_bwd_kernel<E, D, 2, ACT, OFF>);
+    if (d.L == 3) return go(refine_bwd_kernel<E, D, 3, ACT, OFF>);
     if (d.L <= 4) return go(refine_bwd_kernel<E, D, 4, ACT, OFF>);
     return go(refine_bwd_kernel<E, D, 8, ACT, OFF>);
   };
