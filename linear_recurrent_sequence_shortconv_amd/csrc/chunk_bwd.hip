@@ -149,7 +149,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
     const E* __restrict__ Kl, const E* __restrict__ Wl, const E* __restrict__ UT,
     const E* __restrict__ WkT, const E* __restrict__ Sc, const E* __restrict__ dSnT,
     float* __restrict__ dQt, float* __restrict__ dUs, float* __restrict__ dWks,
-    float* __restrict__ dKs, float* __restrict__ dKls, float* __restrict__ dWls,
+    float* __restrict__ dKs, E* __restrict__ dKls, E* __restrict__ dWls,
     float* __restrict__ dgs, int B, int T, int H, int L, int NC, int Tp,
     const int* __restrict__ cu) {
   typedef CB1Lds<E, D, C> LY;
@@ -289,12 +289,12 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
     Acc<C, D, NW> a;
     a.zero();
     gemm_acc<E, C, D, D, NW, true, true>(a, R3, LR, X1, LD2, wave, lane);
-    float* ow = dWls + lrow * D;
+    E* ow = dWls + lrow * D;
     for_tiles_ij(a, wave, lane, [&](int i, int j, int t0, int rr, const f32x4& x) {
       f32x4 pw;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        ow[(long)(t0 + r) * D + rr] = Dv[t0 + r] * x[r];
+        ow[(long)(t0 + r) * D + rr] = to_t<E>(Dv[t0 + r] * x[r]);
         pw[r] = x[r] * to_f(R4[(t0 + r) * LR + rr]);
       }
       dds.add(i, j, pw, true, false);
@@ -302,10 +302,10 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
     Acc<C, D, NW> bb;
     bb.zero();
     gemm_acc<E, C, D, D, NW, true, true>(bb, R4, LR, X2, LD2, wave, lane);
-    float* ok = dKls + lrow * D;
+    E* ok = dKls + lrow * D;
     for_tiles(bb, wave, lane, [&](int t0, int n, const f32x4& x) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ok[(long)(t0 + r) * D + n] = Dv[t0 + r] * x[r];
+      for (int r = 0; r < 4; ++r) ok[(long)(t0 + r) * D + n] = to_t<E>(Dv[t0 + r] * x[r]);
     });
     __syncthreads();
   }
@@ -883,7 +883,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ dO,
     const float* __restrict__ alpha, const E* __restrict__ Kl, const E* __restrict__ Wl,
     const float* __restrict__ dVp, const float* __restrict__ dqp, const float* __restrict__ dkp,
-    const float* __restrict__ dgp, float* __restrict__ dKl, float* __restrict__ dWl,
+    const float* __restrict__ dgp, E* __restrict__ dKl, E* __restrict__ dWl,
     E* __restrict__ dq, E* __restrict__ dk, E* __restrict__ dv,
     float* __restrict__ dalpha, int B, int T, int H, int L, int NC, int Tp,
     const int* __restrict__ cu) {
@@ -964,8 +964,8 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
           const int f = TLD::n0(wave) + 16 * j + (lane & 15);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            pkl[i][j][r] = dKl[(lrow + t0 + r) * D + f];
-            pwl[i][j][r] = dWl[(lrow + t0 + r) * D + f];
+            pkl[i][j][r] = to_f(dKl[(lrow + t0 + r) * D + f]);
+            pwl[i][j][r] = to_f(dWl[(lrow + t0 + r) * D + f]);
           }
         }
     }
@@ -1046,8 +1046,8 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
           const int f = TLD::n0(wave) + 16 * j + (lane & 15);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            dKl[(lrow + t0 + r) * D + f] = pkl[i][j][r] + dkl.v[i][j][r];
-            dWl[(lrow + t0 + r) * D + f] = pwl[i][j][r] + dwl.v[i][j][r];
+            dKl[(lrow + t0 + r) * D + f] = to_t<E>(pkl[i][j][r] + dkl.v[i][j][r]);
+            dWl[(lrow + t0 + r) * D + f] = to_t<E>(pwl[i][j][r] + dwl.v[i][j][r]);
           }
         }
     }

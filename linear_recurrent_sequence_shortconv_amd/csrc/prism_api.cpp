@@ -196,8 +196,8 @@ prism_status check_cu(const int* cu, prism::Dims* d) {
 
 template <typename E>
 struct BwdWs {
-  E *Kl, *Wl, *Mt, *UT, *WkT, *Sc, *dSnT, *u, *dP, *WkW, *WpW;
-  float *HT, *gC, *ET, *dQt, *dUs, *dWks, *dKs, *dVp, *dqp, *dkp, *dKl, *dWl, *dgs, *dgp;
+  E *Kl, *Wl, *Mt, *UT, *WkT, *Sc, *dSnT, *u, *dP, *WkW, *WpW, *dKl, *dWl;
+  float *HT, *gC, *ET, *dQt, *dUs, *dWks, *dKs, *dVp, *dqp, *dkp, *dgs, *dgp;
   float *dwbp, *dcp, *part;
 };
 
@@ -226,8 +226,8 @@ BwdWs<E> carve_bwd(const prism::Dims& d, Carve& cv) {
   w.dVp = cv.take<float>(bh * d.NC * CD * 4);
   w.dqp = cv.take<float>(bh * d.NC * CD * 4);
   w.dkp = cv.take<float>(bh * d.NC * CD * 4);
-  w.dKl = cv.take<float>(bh * d.L * d.Tp * d.D * 4);
-  w.dWl = cv.take<float>(bh * d.L * d.Tp * d.D * 4);
+  w.dKl = cv.take<E>(bh * d.L * d.Tp * d.D * es);
+  w.dWl = cv.take<E>(bh * d.L * d.Tp * d.D * es);
   w.dgs = cv.take<float>(bh * d.NC * d.C * 4);
   w.dgp = cv.take<float>(bh * d.NC * d.C * 4);
   w.u = cv.take<E>(bh * d.Tp * d.D * es);

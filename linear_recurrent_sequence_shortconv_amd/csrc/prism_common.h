@@ -456,6 +456,29 @@ struct RegTile {
       }
     }
   }
+  // rows into an fp32 LDS tile (values converted from T).  The empty asm
+  // keeps the conversion here: hoisted into load(), it would make the
+  // prefetch wait for its own data right after issuing it.
+  __device__ inline void store_rows_f32(float* s, int ld, int tid) const {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int u = tid + p * NT;
+      int r0, c;
+      unit(u, r0, c);
+      if (u < NU) {
+#pragma unroll
+        for (int q = 0; q < RG; ++q) {
+          uint4 w = v[p][q];
+          asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
+          const T* x = reinterpret_cast<const T*>(&w);
+#pragma unroll
+          for (int j = 0; j < VN; j += 4)
+            *reinterpret_cast<f32x4*>(s + (r0 + q) * ld + c + j) =
+                f32x4{to_f(x[j]), to_f(x[j + 1]), to_f(x[j + 2]), to_f(x[j + 3])};
+        }
+      }
+    }
+  }
   // element (r, c) -> s[c * ld + r], times scale[r] (nullptr = 1)
   __device__ inline void store_transposed(T* s, int ld, const float* scale, int tid) const {
 #pragma unroll

@@ -84,7 +84,8 @@ struct ChunkBwdArgs {
   const E *Kl, *Wl, *UT, *WkT;
   const E* Sc;                  // chunk-entry states S_c, row-major [D][D]
   const E* dSnT;
-  float *dQt, *dUs, *dWks, *dKs, *dKl, *dWl, *dgs, *dVp, *dqp, *dkp, *dgp, *dbeta;
+  float *dQt, *dUs, *dWks, *dKs, *dgs, *dVp, *dqp, *dkp, *dgp, *dbeta;
+  E *dKl, *dWl;                 // gradients of the refinement pairs (storage type)
   E *dq, *dk;
   E* dv;                        // written here only when L = 0
   float* dalpha;
@@ -100,7 +101,7 @@ struct RefineBwdArgs {
   const E* hist;                // v before the sequence [B, 4, H, D] (nullptr: zeros)
   float* dhist;                 // its gradient (nullptr: not wanted)
   E *WkT, *WpT;                 // transposed weights (workspace)
-  const float *dKl, *dWl;
+  const E *dKl, *dWl;          // gradients of the refinement pairs (storage type)
   const float* dvdir;           // direct v-gradient of the recurrence ([bh][Tp][D])
   E* u;                         // ShortConv output rows (for the weight GEMM)
   E* dP;                        // dp rows (for the weight GEMM)

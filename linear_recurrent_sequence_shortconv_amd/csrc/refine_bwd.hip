@@ -88,7 +88,7 @@ struct RowChunk {
 };
 
 template <typename E, int D>
-__global__ __launch_bounds__(WG_NT) void wgrad_gemm_kernel(const float* __restrict__ dKl,
+__global__ __launch_bounds__(WG_NT) void wgrad_gemm_kernel(const E* __restrict__ dKl,
                                                            const E* __restrict__ dP,
                                                            const E* __restrict__ u,
                                                            float* __restrict__ part, int B, int H,
@@ -109,26 +109,22 @@ __global__ __launch_bounds__(WG_NT) void wgrad_gemm_kernel(const float* __restri
   acc.zero();
   const long xs_b = (long)H * L * Tp * D;      // X row stride between batches
   const long us_b = (long)H * Tp * D;
-  const float* xk = dKl + (((long)h * L + l) * Tp) * D;
-  const E* xp = dP + (((long)h * L + l) * Tp) * D;
+  // rows of dK_l (which = 0) or dp_l (which = 1), and of u
+  const E* xs = (which == 0 ? dKl : dP) + (((long)h * L + l) * Tp) * D;
   const E* ub = u + ((long)h * Tp) * D;
-  RowChunk<E, float, D> xf;
   RowChunk<E, E, D> xe, uu;
   // software pipeline: chunk n0 + 64 is fetched while chunk n0 is multiplied
   if (n_begin < n_end) {
-    if (which == 0) xf.load(xk, xs_b, Tp, T, cu, n_begin, n_end, tid);
-    else xe.load(xp, xs_b, Tp, T, cu, n_begin, n_end, tid);
+    xe.load(xs, xs_b, Tp, T, cu, n_begin, n_end, tid);
     uu.load(ub, us_b, Tp, T, cu, n_begin, n_end, tid);
   }
   for (long n0 = n_begin; n0 < n_end; n0 += WG_ROWS) {
-    if (which == 0) xf.store_t(Xt, LTT, tid);
-    else xe.store_t(Xt, LTT, tid);
+    xe.store_t(Xt, LTT, tid);
     uu.store_t(Ut, LTT, tid);
     __syncthreads();
     const long nn = n0 + WG_ROWS;
     if (nn < n_end) {
-      if (which == 0) xf.load(xk, xs_b, Tp, T, cu, nn, n_end, tid);
-      else xe.load(xp, xs_b, Tp, T, cu, nn, n_end, tid);
+      xe.load(xs, xs_b, Tp, T, cu, nn, n_end, tid);
       uu.load(ub, us_b, Tp, T, cu, nn, n_end, tid);
     }
     gemm_acc<E, D, D, WG_ROWS, WG_NW, true, true>(acc, Xt, LTT, Ut, LTT, wave, lane);
