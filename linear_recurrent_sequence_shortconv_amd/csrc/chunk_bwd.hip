@@ -111,18 +111,6 @@ struct TileSums {
   }
 };
 
-// fp32 global rows -> operand-type LDS rows (optionally negated)
-template <typename E, int ROWS, int COLS, int NT>
-__device__ inline void g2s_rows_f32(E* s, int ld, const float* g, long gstride, float scale, int tid) {
-  constexpr int VPR = COLS / 4;
-  for (int e = tid; e < ROWS * VPR; e += NT) {
-    const int r = e / VPR, c = (e % VPR) * 4;
-    const f32x4 x = *reinterpret_cast<const f32x4*>(g + r * gstride + c);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) s[r * ld + c + j] = to_t<E>(scale * x[j]);
-  }
-}
-
 // ===========================================================================
 // chunk_bwd_state
 // ===========================================================================
@@ -148,8 +136,8 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
     const E* __restrict__ k, const E* __restrict__ dO, const float* __restrict__ alpha,
     const E* __restrict__ Kl, const E* __restrict__ Wl, const E* __restrict__ UT,
     const E* __restrict__ WkT, const E* __restrict__ Sc, const E* __restrict__ dSnT,
-    float* __restrict__ dQt, float* __restrict__ dUs, float* __restrict__ dWks,
-    float* __restrict__ dKs, E* __restrict__ dKls, E* __restrict__ dWls,
+    E* __restrict__ dQt, E* __restrict__ dUs, E* __restrict__ dWks,
+    E* __restrict__ dKs, E* __restrict__ dKls, E* __restrict__ dWls,
     float* __restrict__ dgs, int B, int T, int H, int L, int NC, int Tp,
     const int* __restrict__ cu) {
   typedef CB1Lds<E, D, C> LY;
@@ -204,10 +192,10 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
     Acc<C, D, NW> a;
     a.zero();
     gemm_acc<E, C, D, D, NW, true, false>(a, R1, LR, X1, LD2, wave, lane);
-    float* out = dQt + cidx * C * D;
+    E* out = dQt + cidx * C * D;
     for_tiles(a, wave, lane, [&](int t0, int kk, const f32x4& x) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) out[(long)(t0 + r) * D + kk] = x[r];
+      for (int r = 0; r < 4; ++r) out[(long)(t0 + r) * D + kk] = to_t<E>(x[r]);
     });
   }
   Acc<D, D, NW> dm;   // [k][n] = sum_r S[r][k] dS_n^T[n][r]  (= -dM)
@@ -265,12 +253,12 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
     Acc<C, D, NW> u;    // K dS_n^T: [t][r] = sum_n K[t][n] dS_n[r][n]
     u.zero();
     gemm_acc<E, C, D, D, NW, true, true>(u, R1, LR, X1, LD2, wave, lane);
-    float* out = dUs + cidx * C * D;
+    E* out = dUs + cidx * C * D;
     for_tiles_ij(u, wave, lane, [&](int i, int j, int t0, int rr, const f32x4& x) {
       f32x4 pu;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        out[(long)(t0 + r) * D + rr] = Dv[t0 + r] * x[r];
+        out[(long)(t0 + r) * D + rr] = to_t<E>(Dv[t0 + r] * x[r]);
         pu[r] = x[r] * to_f(R2[(t0 + r) * LR + rr]);
       }
       dds.add(i, j, pu, true, false);
@@ -325,12 +313,12 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
     Acc<C, D, NW> a;    // K dM^T: [t][k] = sum_n K[t][n] dM[k][n]
     a.zero();
     gemm_acc<E, C, D, D, NW, true, true>(a, R1, LR, X1, LD2, wave, lane);
-    float* out = dWks + cidx * C * D;
+    E* out = dWks + cidx * C * D;
     for_tiles_ij(a, wave, lane, [&](int i, int j, int t0, int kk, const f32x4& x) {
       f32x4 pw;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        out[(long)(t0 + r) * D + kk] = Dv[t0 + r] * x[r];
+        out[(long)(t0 + r) * D + kk] = to_t<E>(Dv[t0 + r] * x[r]);
         pw[r] = x[r] * to_f(R3[(t0 + r) * LR + kk]);
       }
       dds.add(i, j, pw, true, false);
@@ -338,7 +326,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
     Acc<C, D, NW> bb;   // Wk dM: [t][n] = sum_k Wk[t][k] dM^T[n][k]
     bb.zero();
     gemm_acc<E, C, D, D, NW, true, true>(bb, R3, LR, X2, LD2, wave, lane);
-    float* ok = dKs + cidx * C * D;
+    E* ok = dKs + cidx * C * D;
     typedef Tiling<C, D, NW> TL;
     if (TL::active(wave)) {
 #pragma unroll
@@ -349,7 +337,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
           const int n = TL::n0(wave) + 16 * j + (lane & 15);
 #pragma unroll
           for (int r = 0; r < 4; ++r)
-            ok[(long)(t0 + r) * D + n] = dk.v[i][j][r] + Dv[t0 + r] * bb.v[i][j][r];
+            ok[(long)(t0 + r) * D + n] = to_t<E>(dk.v[i][j][r] + Dv[t0 + r] * bb.v[i][j][r]);
         }
     }
   }
@@ -422,10 +410,10 @@ template <typename E, int D, int C>
 __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const E* __restrict__ dO, const float* __restrict__ alpha, const float* __restrict__ beta,
-    const E* __restrict__ Kl, const E* __restrict__ Wl, const float* __restrict__ dQt,
-    const float* __restrict__ dUs, const float* __restrict__ dWks, const float* __restrict__ dKs,
-    const float* __restrict__ dgs, float* __restrict__ dVp, float* __restrict__ dqp,
-    float* __restrict__ dkp, float* __restrict__ dgp, float* __restrict__ dbeta, int B, int T,
+    const E* __restrict__ Kl, const E* __restrict__ Wl, const E* __restrict__ dQt,
+    const E* __restrict__ dUs, const E* __restrict__ dWks, const E* __restrict__ dKs,
+    const float* __restrict__ dgs, E* __restrict__ dVp, E* __restrict__ dqp,
+    E* __restrict__ dkp, float* __restrict__ dgp, float* __restrict__ dbeta, int B, int T,
     int H, int L, int NC, int Tp, const int* __restrict__ cu) {
   typedef CB2Lds<E, D, C> LY;
   constexpr int NW = CB_NW, NT = CB_NT;
@@ -524,10 +512,10 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
   }
 
   // ---- solve: A = diag(beta)(Gam * K K^T)_{i<t}, T = (I + A)^{-1} ----
-  // Q, dO rows and dQt (fp32) of the next phase are fetched during the solve
-  const float* dQtc = dQt + cidx * C * D;
+  // Q, dO rows and dQt of the next phase are fetched during the solve
+  const E* dQtc = dQt + cidx * C * D;
   RegTile<E, C, D, NT> qn, on;
-  RegTile<float, C, D, NT> dqn;
+  RegTile<E, C, D, NT> dqn;
   qn.load(q + row0 * D, ts, nval, tid);
   on.load(dO + row0 * D, ts, nval, tid);
   dqn.load(dQtc, D, C, tid);
@@ -585,29 +573,29 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
   qn.store_rows(Qr, LR, tid);
   on.store_rows(dOr, LR, tid);
   // -dQt rows (operand type)
-  typedef RegTile<float, C, D, NT> DQT;
+  typedef RegTile<E, C, D, NT> DQT;
 #pragma unroll
   for (int p = 0; p < DQT::PER; ++p) {
     const int u = tid + p * NT;
-    const int r = u / DQT::VPR, c0 = (u % DQT::VPR) * 4;
-    const f32x4 x = *reinterpret_cast<const f32x4*>(&dqn.v[p][0]);
+    const int r = u / DQT::VPR, c0 = (u % DQT::VPR) * DQT::VN;
+    const E* x = reinterpret_cast<const E*>(&dqn.v[p][0]);
     if (u < DQT::NU) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) NdQ[r * LR + c0 + j] = to_t<E>(-x[j]);
+      for (int j = 0; j < DQT::VN; ++j) NdQ[r * LR + c0 + j] = to_t<E>(-to_f(x[j]));
     }
   }
   __syncthreads();
-  // de_t = Q_t . dQt_t (fp32 dQt): each row is held by VPR consecutive lanes
+  // de_t = Q_t . dQt_t: each row is held by VPR consecutive lanes
   static_assert(DQT::VPR <= 64 && (64 % DQT::VPR) == 0, "a row within one wave");
 #pragma unroll
   for (int p = 0; p < DQT::PER; ++p) {
     const int u = tid + p * NT;
-    const int r = u / DQT::VPR, c0 = (u % DQT::VPR) * 4;
-    const f32x4 x = *reinterpret_cast<const f32x4*>(&dqn.v[p][0]);
+    const int r = u / DQT::VPR, c0 = (u % DQT::VPR) * DQT::VN;
+    const E* x = reinterpret_cast<const E*>(&dqn.v[p][0]);
     float sdq = 0.f;
     if (u < DQT::NU) {
 #pragma unroll
-      for (int j = 0; j < 4; ++j) sdq += to_f(Qr[r * LR + c0 + j]) * x[j];
+      for (int j = 0; j < DQT::VN; ++j) sdq += to_f(Qr[r * LR + c0 + j]) * to_f(x[j]);
     }
 #pragma unroll
     for (int off = 1; off < DQT::VPR; off <<= 1) sdq += __shfl_xor(sdq, off);
@@ -615,9 +603,9 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
   }
   // dU_s, dWk_s, dK_s and dQt in the accumulator layout, for the epilogue
   // of the R0 products (fetched while they run)
-  const float* dUc = dUs + cidx * C * D;
-  const float* dWc = dWks + cidx * C * D;
-  const float* dKc = dKs + cidx * C * D;
+  const E* dUc = dUs + cidx * C * D;
+  const E* dWc = dWks + cidx * C * D;
+  const E* dKc = dKs + cidx * C * D;
   f32x4 pU[TLD::RM][TLD::RN], pW[TLD::RM][TLD::RN], pK[TLD::RM][TLD::RN], pQ[TLD::RM][TLD::RN];
   if (actD) {
 #pragma unroll
@@ -629,10 +617,10 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const long o = (long)(t0 + r) * D + f;
-          pU[i][j][r] = dUc[o];
-          pW[i][j][r] = dWc[o];
-          pK[i][j][r] = dKc[o];
-          pQ[i][j][r] = dQtc[o];
+          pU[i][j][r] = to_f(dUc[o]);
+          pW[i][j][r] = to_f(dWc[o]);
+          pK[i][j][r] = to_f(dKc[o]);
+          pQ[i][j][r] = to_f(dQtc[o]);
         }
       }
   }
@@ -722,7 +710,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
     x2.zero();
     gemm_acc<E, C, D, C, NW, false, false>(x1, Tb, LT, dUr, LR, wave, lane);
     gemm_acc<E, C, D, C, NW, false, false>(x2, Tb, LT, dWkr, LR, wave, lane);
-    float* dVc = dVp + cidx * C * D;
+    E* dVc = dVp + cidx * C * D;
     if (actD) {
 #pragma unroll
       for (int i = 0; i < TLD::RM; ++i)
@@ -734,7 +722,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             const int t = t0 + r;
-            dVc[(long)t * D + f] = bt[t] * x1.v[i][j][r];                 // dV'
+            dVc[(long)t * D + f] = to_t<E>(bt[t] * x1.v[i][j][r]);        // dV'
             pb[r] = vp.v[i][j][r] * x1.v[i][j][r];
             pk[r] = to_f(Kr[t * LR + f]) * x2.v[i][j][r];
             dk.v[i][j][r] += be[t] * x2.v[i][j][r];
@@ -820,15 +808,15 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
   gemm_acc<E, C, D, C, NW, true, false>(dk, Zb, LT, Kr, LR, wave, lane);   // (dG0 + dG0^T) K
 
   // ---- outputs ----
-  float* dqc = dqp + cidx * C * D;
-  float* dkc = dkp + cidx * C * D;
+  E* dqc = dqp + cidx * C * D;
+  E* dkc = dkp + cidx * C * D;
   for_tiles(dq, wave, lane, [&](int t0, int f, const f32x4& x) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dqc[(long)(t0 + r) * D + f] = x[r];
+    for (int r = 0; r < 4; ++r) dqc[(long)(t0 + r) * D + f] = to_t<E>(x[r]);
   });
   for_tiles(dk, wave, lane, [&](int t0, int f, const f32x4& x) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) dkc[(long)(t0 + r) * D + f] = x[r];
+    for (int r = 0; r < 4; ++r) dkc[(long)(t0 + r) * D + f] = to_t<E>(x[r]);
   });
   if (actC) {
     sgc.flush_rows(rs + wave * C, TLC::m0(wave), lane);
@@ -882,7 +870,7 @@ template <typename E, int D, int C>
 __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ dO,
     const float* __restrict__ alpha, const E* __restrict__ Kl, const E* __restrict__ Wl,
-    const float* __restrict__ dVp, const float* __restrict__ dqp, const float* __restrict__ dkp,
+    const E* __restrict__ dVp, const E* __restrict__ dqp, const E* __restrict__ dkp,
     const float* __restrict__ dgp, E* __restrict__ dKl, E* __restrict__ dWl,
     E* __restrict__ dq, E* __restrict__ dk, E* __restrict__ dv,
     float* __restrict__ dalpha, int B, int T, int H, int L, int NC, int Tp,
@@ -928,7 +916,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
   g2s_rows<E, C, D, NT>(Qr, LR, q + row0 * D, ts, nval, tid);
   g2s_rows<E, C, D, NT>(Kr, LR, k + row0 * D, ts, nval, tid);
   g2s_rows<E, C, D, NT>(dOr, LR, dO + row0 * D, ts, nval, tid);
-  g2s_rows_f32<E, C, D, NT>(dVr, LR, dVp + cidx * C * D, D, 1.f, tid);
+  g2s_rows<E, C, D, NT>(dVr, LR, dVp + cidx * C * D, D, C, tid);
   __syncthreads();
 
   Acc<C, D, NW> dqa, dka;
@@ -1061,10 +1049,10 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
   }
   // fp32 products staged in LDS (every tile buffer is free now), then added
   // to the solve kernel's parts and stored as full rows
-  const float* dqc = dqp + cidx * C * D;
-  const float* dkc = dkp + cidx * C * D;
-  const float* dvc = dVp + cidx * C * D;
-  RegTile<float, C, D, NT> rq, rk;
+  const E* dqc = dqp + cidx * C * D;
+  const E* dkc = dkp + cidx * C * D;
+  const E* dvc = dVp + cidx * C * D;
+  RegTile<E, C, D, NT> rq, rk;
   rq.load(dqc, D, C, tid);
   rk.load(dkc, D, C, tid);
   constexpr int LF = D + 4;
@@ -1081,59 +1069,38 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
   });
   __syncthreads();
   {
-    typedef RegTile<float, C, D, NT> RT;
+    typedef RegTile<E, C, D, NT> RT;
     E* dqo = dq + row0 * D;
     E* dko = dk + row0 * D;
 #pragma unroll
     for (int p = 0; p < RT::PER; ++p) {
       const int u = tid + p * NT;
-      const int r = u / RT::VPR, c0 = (u % RT::VPR) * 4;
+      const int r = u / RT::VPR, c0 = (u % RT::VPR) * RT::VN;
       if (u < RT::NU && r < nval) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(&rq.v[p][0]);
-        const f32x4 b = *reinterpret_cast<const f32x4*>(&rk.v[p][0]);
-        E oq[4], ok[4];
+        const E* a = reinterpret_cast<const E*>(&rq.v[p][0]);
+        const E* b = reinterpret_cast<const E*>(&rk.v[p][0]);
+        E oq[RT::VN], ok[RT::VN];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          oq[j] = to_t<E>(a[j] + Sq[r * LF + c0 + j]);
-          ok[j] = to_t<E>(b[j] + Sk[r * LF + c0 + j]);
+        for (int j = 0; j < RT::VN; ++j) {
+          oq[j] = to_t<E>(to_f(a[j]) + Sq[r * LF + c0 + j]);
+          ok[j] = to_t<E>(to_f(b[j]) + Sk[r * LF + c0 + j]);
         }
-        if constexpr (sizeof(E) == 2) {
-          uint2 wq, wk;
-          __builtin_memcpy(&wq, oq, 8);
-          __builtin_memcpy(&wk, ok, 8);
-          *reinterpret_cast<uint2*>(dqo + (long)r * ts + c0) = wq;
-          *reinterpret_cast<uint2*>(dko + (long)r * ts + c0) = wk;
-        } else {
-          uint4 wq, wk;
-          __builtin_memcpy(&wq, oq, 16);
-          __builtin_memcpy(&wk, ok, 16);
-          *reinterpret_cast<uint4*>(dqo + (long)r * ts + c0) = wq;
-          *reinterpret_cast<uint4*>(dko + (long)r * ts + c0) = wk;
-        }
+        uint4 wq, wk;
+        __builtin_memcpy(&wq, oq, 16);
+        __builtin_memcpy(&wk, ok, 16);
+        st16(dqo + (long)r * ts + c0, wq);
+        st16(dko + (long)r * ts + c0, wk);
       }
     }
   }
   // with L > 0 the direct v-gradient dV' (chunk rows [bh][c][t] = token rows
-  // [bh][c C + t]) is completed by the refinement backward
+  // [bh][c C + t]) is completed by the refinement backward; at L = 0 it is dv
   if (L == 0) {
+    constexpr int VN = 16 / (int)sizeof(E);
     E* dvo = dv + row0 * D;
-    for (int e = tid; e < C * D / 4; e += NT) {
-      const int t = e / (D / 4), f = (e % (D / 4)) * 4;
-      if (t < nval) {
-        const f32x4 a = *reinterpret_cast<const f32x4*>(dvc + (long)t * D + f);
-        E o4[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) o4[j] = to_t<E>(a[j]);
-        if constexpr (sizeof(E) == 2) {
-          uint2 w2;
-          __builtin_memcpy(&w2, o4, 8);
-          *reinterpret_cast<uint2*>(dvo + (long)t * ts + f) = w2;
-        } else {
-          uint4 w4;
-          __builtin_memcpy(&w4, o4, 16);
-          *reinterpret_cast<uint4*>(dvo + (long)t * ts + f) = w4;
-        }
-      }
+    for (int e = tid; e < C * D / VN; e += NT) {
+      const int t = e / (D / VN), f = (e % (D / VN)) * VN;
+      if (t < nval) st16(dvo + (long)t * ts + f, ld16(dvc + (long)t * D + f));
     }
   }
   __syncthreads();

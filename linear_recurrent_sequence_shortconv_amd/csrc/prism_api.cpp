@@ -197,7 +197,8 @@ prism_status check_cu(const int* cu, prism::Dims* d) {
 template <typename E>
 struct BwdWs {
   E *Kl, *Wl, *Mt, *UT, *WkT, *Sc, *dSnT, *u, *dP, *WkW, *WpW, *dKl, *dWl;
-  float *HT, *gC, *ET, *dQt, *dUs, *dWks, *dKs, *dVp, *dqp, *dkp, *dgs, *dgp;
+  E *dQt, *dUs, *dWks, *dKs, *dVp, *dqp, *dkp;
+  float *HT, *gC, *ET, *dgs, *dgp;
   float *dwbp, *dcp, *part;
 };
 
@@ -219,13 +220,13 @@ BwdWs<E> carve_bwd(const prism::Dims& d, Carve& cv) {
   w.WkT = cv.take<E>(bh * d.NC * CD * es);
   w.Sc = cv.take<E>(bh * d.NC * DD * es);
   w.dSnT = cv.take<E>(bh * d.NC * DD * es);
-  w.dQt = cv.take<float>(bh * d.NC * CD * 4);
-  w.dUs = cv.take<float>(bh * d.NC * CD * 4);
-  w.dWks = cv.take<float>(bh * d.NC * CD * 4);
-  w.dKs = cv.take<float>(bh * d.NC * CD * 4);
-  w.dVp = cv.take<float>(bh * d.NC * CD * 4);
-  w.dqp = cv.take<float>(bh * d.NC * CD * 4);
-  w.dkp = cv.take<float>(bh * d.NC * CD * 4);
+  w.dQt = cv.take<E>(bh * d.NC * CD * es);
+  w.dUs = cv.take<E>(bh * d.NC * CD * es);
+  w.dWks = cv.take<E>(bh * d.NC * CD * es);
+  w.dKs = cv.take<E>(bh * d.NC * CD * es);
+  w.dVp = cv.take<E>(bh * d.NC * CD * es);
+  w.dqp = cv.take<E>(bh * d.NC * CD * es);
+  w.dkp = cv.take<E>(bh * d.NC * CD * es);
   w.dKl = cv.take<E>(bh * d.L * d.Tp * d.D * es);
   w.dWl = cv.take<E>(bh * d.L * d.Tp * d.D * es);
   w.dgs = cv.take<float>(bh * d.NC * d.C * 4);

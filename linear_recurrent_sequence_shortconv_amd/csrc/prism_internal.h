@@ -84,7 +84,9 @@ struct ChunkBwdArgs {
   const E *Kl, *Wl, *UT, *WkT;
   const E* Sc;                  // chunk-entry states S_c, row-major [D][D]
   const E* dSnT;
-  float *dQt, *dUs, *dWks, *dKs, *dgs, *dVp, *dqp, *dkp, *dgp, *dbeta;
+  float *dgs, *dgp, *dbeta;
+  E *dQt, *dUs, *dWks, *dKs;    // state-gradient partials (storage type)
+  E *dVp, *dqp, *dkp;           // solve partials (storage type)
   E *dKl, *dWl;                 // gradients of the refinement pairs (storage type)
   E *dq, *dk;
   E* dv;                        // written here only when L = 0
@@ -102,7 +104,7 @@ struct RefineBwdArgs {
   float* dhist;                 // its gradient (nullptr: not wanted)
   E *WkT, *WpT;                 // transposed weights (workspace)
   const E *dKl, *dWl;          // gradients of the refinement pairs (storage type)
-  const float* dvdir;           // direct v-gradient of the recurrence ([bh][Tp][D])
+  const E* dvdir;               // direct v-gradient of the recurrence ([bh][Tp][D])
   E* u;                         // ShortConv output rows (for the weight GEMM)
   E* dP;                        // dp rows (for the weight GEMM)
   float *dwbp, *dcp, *part;     // per-tile / per-split partial sums

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
     const E* __restrict__ v, const E* __restrict__ hist, const E* __restrict__ conv,
     const E* __restrict__ Wp,
     const E* __restrict__ WkT, const E* __restrict__ WpT, const E* __restrict__ wbeta,
-    const E* __restrict__ dKl, const E* __restrict__ dWl, const float* __restrict__ dvdir,
+    const E* __restrict__ dKl, const E* __restrict__ dWl, const E* __restrict__ dvdir,
     E* __restrict__ uo, E* __restrict__ dPo, E* __restrict__ dv, float* __restrict__ dwbp,
     float* __restrict__ dcp, float* __restrict__ dhist, int B, int T, int H, int L, int Tp,
     int ntiles, const int* __restrict__ cu) {
@@ -310,7 +310,7 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
 
   // ---- reverse: gw / gkk hold dW_l, dK_l of the current step ----
   float a_[2][FPW][4];
-  float dvd[2][FPW][4];     // direct v-gradient (fetched during the last step)
+  E dvd[2][FPW][4];         // direct v-gradient (fetched during the last step; converted at use)
   f32x4 du[2][FPW];
 #pragma unroll
   for (int m = 0; m < 2; ++m)
@@ -318,7 +318,10 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
     for (int nn = 0; nn < FPW; ++nn) {
       du[m][nn] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a_[m][nn][i] = dvd[m][nn][i] = 0.f;
+      for (int i = 0; i < 4; ++i) {
+        a_[m][nn][i] = 0.f;
+        dvd[m][nn][i] = to_t<E>(0.f);
+      }
     }
 #pragma unroll
   for (int l = LMAX - 1; l >= 0; --l) {
@@ -429,7 +432,7 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
       pw.load(dWl + lrow * D, D, nrow, tid);
       pk.load(dKl + lrow * D, D, nrow, tid);
     } else {
-      const float* dvs = dvdir + (bh * Tp + t0) * D;
+      const E* dvs = dvdir + (bh * Tp + t0) * D;
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -439,7 +442,7 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
             const int t = 16 * m + 4 * (lane >> 4) + i;
-            dvd[m][nn][i] = (FT_OK(n) && t < own) ? dvs[(long)t * D + f] : 0.f;
+            dvd[m][nn][i] = (FT_OK(n) && t < own) ? dvs[(long)t * D + f] : to_t<E>(0.f);
           }
         }
     }
@@ -516,7 +519,11 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
       for (int i = 0; i < 4; ++i) {
         const int t = t0m + i;
         if (t < own) {
-          float val = dvd[m][nn][i] + a_[m][nn][i];
+          // the conversion stays here (empty asm): next to the load it
+          // would make the prefetch wait for its data at issue
+          E dr = dvd[m][nn][i];
+          asm volatile("" : "+v"(dr));
+          float val = to_f(dr) + a_[m][nn][i];
 #pragma unroll
           for (int j = 0; j < 4; ++j) val += tp[j] * w[i + j];
           dpbuf[t * LD + f] = to_t<E>(val);
