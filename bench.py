@@ -74,16 +74,16 @@ def algorithmic_counts(w):
     c["state_bwd"] = (st[0] + bh * D * D * 4, st[1])
     c["out_fwd"] = (nch * (D * D * e + C * D * (e + 4)) + th * D * e, nch * 2 * C * D * D)
     c["chunk_bwd_state"] = (th * (2 * D * e + 4) + nch * (2 * C * D * e + 2 * D * D * e + 4 * e * C * D + 4 * C)
-                            + ntp * L * D * 4 * e,       # read K_l, W_l; write dK_l, dW_l partials
+                            + ntp * L * D * (3 * e + 4),  # read K_l, W_l; write dK_l, dW_l (fp32) partials
                             nch * (2 * C * D * D * (6 + 2 * L) + 2 * D ** 3))
     c["chunk_bwd_solve"] = (th * (4 * D * e + 12) + ntp * 2 * L * D * e + nch * (7 * e * C * D + 8 * C),
                             nch * (2 * C * C * D * (2 * L + 16) + 4 * C ** 3))
     c["chunk_bwd_pairs"] = (th * (5 * D * e + 8) + ntp * 2 * L * D * e + nch * 3 * e * C * D
-                            + ntp * L * D * 4 * e,       # dK_l, dW_l read and rewritten
+                            + ntp * L * D * (2 * e + 8),  # dK_l, dW_l (fp32) read and rewritten
                             nch * 2 * C * C * D * 10 * L)
-    # refinement + ShortConv backward: read v, dK_l, dW_l, the direct
-    # v-gradient (all storage type); write u, dp_l (for the weight GEMM) and dv
-    c["refine_bwd"] = (th * (4 * D * e + L * D * 3 * e), th * 6 * L * D * D)
+    # refinement + ShortConv backward: read v, dK_l, dW_l (fp32), the direct
+    # v-gradient; write u, dp_l (for the weight GEMM) and dv
+    c["refine_bwd"] = (th * (4 * D * e + L * D * (2 * e + 4)), th * 6 * L * D * D)
     ns = max(1, min(1024 // (2 * H * max(L, 1)), -(-B * Tp // 64)))
     c["wgrad_gemm"] = (th * L * D * 2 * e + th * D * e * 2 * L + H * L * 2 * ns * D * D * 4,
                        th * 4 * L * D * D)

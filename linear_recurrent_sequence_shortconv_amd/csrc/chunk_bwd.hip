@@ -137,7 +137,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
     const E* __restrict__ Kl, const E* __restrict__ Wl, const E* __restrict__ UT,
     const E* __restrict__ WkT, const E* __restrict__ Sc, const E* __restrict__ dSnT,
     E* __restrict__ dQt, E* __restrict__ dUs, E* __restrict__ dWks,
-    E* __restrict__ dKs, E* __restrict__ dKls, E* __restrict__ dWls,
+    E* __restrict__ dKs, E* __restrict__ dKls, float* __restrict__ dWls,
     float* __restrict__ dgs, int B, int T, int H, int L, int NC, int Tp,
     const int* __restrict__ cu) {
   typedef CB1Lds<E, D, C> LY;
@@ -277,12 +277,12 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
     Acc<C, D, NW> a;
     a.zero();
     gemm_acc<E, C, D, D, NW, true, true>(a, R3, LR, X1, LD2, wave, lane);
-    E* ow = dWls + lrow * D;
+    float* ow = dWls + lrow * D;
     for_tiles_ij(a, wave, lane, [&](int i, int j, int t0, int rr, const f32x4& x) {
       f32x4 pw;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        ow[(long)(t0 + r) * D + rr] = to_t<E>(Dv[t0 + r] * x[r]);
+        ow[(long)(t0 + r) * D + rr] = Dv[t0 + r] * x[r];
         pw[r] = x[r] * to_f(R4[(t0 + r) * LR + rr]);
       }
       dds.add(i, j, pw, true, false);
@@ -871,7 +871,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ dO,
     const float* __restrict__ alpha, const E* __restrict__ Kl, const E* __restrict__ Wl,
     const E* __restrict__ dVp, const E* __restrict__ dqp, const E* __restrict__ dkp,
-    const float* __restrict__ dgp, E* __restrict__ dKl, E* __restrict__ dWl,
+    const float* __restrict__ dgp, E* __restrict__ dKl, float* __restrict__ dWl,
     E* __restrict__ dq, E* __restrict__ dk, E* __restrict__ dv,
     float* __restrict__ dalpha, int B, int T, int H, int L, int NC, int Tp,
     const int* __restrict__ cu) {
@@ -953,7 +953,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             pkl[i][j][r] = to_f(dKl[(lrow + t0 + r) * D + f]);
-            pwl[i][j][r] = to_f(dWl[(lrow + t0 + r) * D + f]);
+            pwl[i][j][r] = dWl[(lrow + t0 + r) * D + f];
           }
         }
     }
@@ -1035,7 +1035,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
             dKl[(lrow + t0 + r) * D + f] = to_t<E>(pkl[i][j][r] + dkl.v[i][j][r]);
-            dWl[(lrow + t0 + r) * D + f] = to_t<E>(pwl[i][j][r] + dwl.v[i][j][r]);
+            dWl[(lrow + t0 + r) * D + f] = pwl[i][j][r] + dwl.v[i][j][r];
           }
         }
     }

@@ -196,7 +196,8 @@ prism_status check_cu(const int* cu, prism::Dims* d) {
 
 template <typename E>
 struct BwdWs {
-  E *Kl, *Wl, *Mt, *UT, *WkT, *Sc, *dSnT, *u, *dP, *WkW, *WpW, *dKl, *dWl;
+  E *Kl, *Wl, *Mt, *UT, *WkT, *Sc, *dSnT, *u, *dP, *WkW, *WpW, *dKl;
+  float* dWl;
   E *dQt, *dUs, *dWks, *dKs, *dVp, *dqp, *dkp;
   float *HT, *gC, *ET, *dgs, *dgp;
   float *dwbp, *dcp, *part;
@@ -228,7 +229,7 @@ BwdWs<E> carve_bwd(const prism::Dims& d, Carve& cv) {
   w.dqp = cv.take<E>(bh * d.NC * CD * es);
   w.dkp = cv.take<E>(bh * d.NC * CD * es);
   w.dKl = cv.take<E>(bh * d.L * d.Tp * d.D * es);
-  w.dWl = cv.take<E>(bh * d.L * d.Tp * d.D * es);
+  w.dWl = cv.take<float>(bh * d.L * d.Tp * d.D * 4);
   w.dgs = cv.take<float>(bh * d.NC * d.C * 4);
   w.dgp = cv.take<float>(bh * d.NC * d.C * 4);
   w.u = cv.take<E>(bh * d.Tp * d.D * es);

@@ -87,7 +87,11 @@ struct ChunkBwdArgs {
   float *dgs, *dgp, *dbeta;
   E *dQt, *dUs, *dWks, *dKs;    // state-gradient partials (storage type)
   E *dVp, *dqp, *dkp;           // solve partials (storage type)
-  E *dKl, *dWl;                 // gradients of the refinement pairs (storage type)
+  // gradients of the refinement pairs: dK_l in the storage type (its users
+  // round it to the MFMA operand type anyway); dW_l in fp32, since it enters
+  // the difference beta^(l) dW_l - dL/dr^(l+1), which can cancel
+  E* dKl;
+  float* dWl;
   E *dq, *dk;
   E* dv;                        // written here only when L = 0
   float* dalpha;
@@ -103,7 +107,8 @@ struct RefineBwdArgs {
   const E* hist;                // v before the sequence [B, 4, H, D] (nullptr: zeros)
   float* dhist;                 // its gradient (nullptr: not wanted)
   E *WkT, *WpT;                 // transposed weights (workspace)
-  const E *dKl, *dWl;          // gradients of the refinement pairs (storage type)
+  const E* dKl;                 // gradient of the directions k^(l) (storage type)
+  const float* dWl;             // gradient of the values w^(l) (fp32)
   const E* dvdir;               // direct v-gradient of the recurrence ([bh][Tp][D])
   E* u;                         // ShortConv output rows (for the weight GEMM)
   E* dP;                        // dp rows (for the weight GEMM)

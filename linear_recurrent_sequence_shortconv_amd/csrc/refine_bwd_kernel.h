@@ -66,7 +66,7 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
     const E* __restrict__ v, const E* __restrict__ hist, const E* __restrict__ conv,
     const E* __restrict__ Wp,
     const E* __restrict__ WkT, const E* __restrict__ WpT, const E* __restrict__ wbeta,
-    const E* __restrict__ dKl, const E* __restrict__ dWl, const E* __restrict__ dvdir,
+    const E* __restrict__ dKl, const float* __restrict__ dWl, const E* __restrict__ dvdir,
     E* __restrict__ uo, E* __restrict__ dPo, E* __restrict__ dv, float* __restrict__ dwbp,
     float* __restrict__ dcp, float* __restrict__ dhist, int B, int T, int H, int L, int Tp,
     int ntiles, const int* __restrict__ cu) {
@@ -135,7 +135,8 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
     st16(vbuf + r * D + c, x);
   }
   // dW, dK rows of the first reverse step, in flight during the set-up
-  RegTile<E, RB_TT, D, RB_NT> pw, pk;
+  RegTile<float, RB_TT, D, RB_NT> pw;   // dW_l rows (fp32)
+  RegTile<E, RB_TT, D, RB_NT> pk;       // dK_l rows
   {
     const long lrow = (bh * L + (L - 1)) * Tp + t0;
     pw.load(dWl + lrow * D, D, nrow, tid);
