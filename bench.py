@@ -57,22 +57,22 @@ def algorithmic_counts(w):
     c["refine_fwd"] = (th * e * D + ntp * 2 * L * D * e, th * 4 * L * D * D)
     # (the training forward also keeps U^T, W_k^T: + 2 C D e per chunk)
     c["chunk_fwd"] = (th * (3 * D * e + 8) + ntp * 2 * L * D * e
-                      + nch * (D * D * (e + 4) + C * D * (e + 4) + 4 + 2 * C * D * e),
+                      + nch * (2 * D * D * e + 2 * C * D * e + 4 + 2 * C * D * e),
                       nch * (2 * C * C * D * (4 * L + 6) + 2 * C * D * D * (L + 2)))
     # refinement formed inside the chunk kernel (inference forward): no pairs
     # in HBM; weights and taps once per head
     c["chunk_fwd_fused"] = (th * (3 * D * e + 8) + H * (L * (2 * D * D + D) + 4 * D) * e
-                            + nch * (D * D * (e + 4) + C * D * (e + 4) + 4),
+                            + nch * (2 * D * D * e + 2 * C * D * e + 4),
                             nch * (2 * C * C * D * (4 * L + 6) + 2 * C * D * D * (L + 2))
                             + th * 4 * L * D * D)
     c["chunk_fwd_bwdmode"] = (th * (4 * D * e + 8) + ntp * 2 * L * D * e
-                              + nch * (2 * D * D * e + 2 * D * D * 4 + 2 * C * D * e + 4),
+                              + nch * (4 * D * D * e + 2 * C * D * e + 4),
                               nch * (2 * C * C * D * (2 * L + 5) + 2 * C * D * D * (L + 4)))
-    c["et_chunks"] = (nch * (2 * C * D * e + D * D * 4), nch * 2 * C * D * D)
-    st = (nch * D * D * (2 * e + 4) + bh * D * D * 4, nch * 2 * D ** 3)
+    c["et_chunks"] = (nch * (2 * C * D * e + D * D * e), nch * 2 * C * D * D)
+    st = (nch * D * D * 3 * e + bh * D * D * 4, nch * 2 * D ** 3)
     c["state_fwd"] = c["state_fwd_recompute"] = st
     c["state_bwd"] = (st[0] + bh * D * D * 4, st[1])
-    c["out_fwd"] = (nch * (D * D * e + C * D * (e + 4)) + th * D * e, nch * 2 * C * D * D)
+    c["out_fwd"] = (nch * (D * D * e + C * D * 2 * e) + th * D * e, nch * 2 * C * D * D)
     c["chunk_bwd_state"] = (th * (2 * D * e + 4) + nch * (2 * C * D * e + 2 * D * D * e + 4 * e * C * D + 4 * C)
                             + ntp * L * D * (3 * e + 4),  # read K_l, W_l; write dK_l, dW_l (fp32) partials
                             nch * (2 * C * D * D * (6 + 2 * L) + 2 * D ** 3))

@@ -10,7 +10,7 @@ namespace prism {
 #define INST(E, OFF)                                                                          \
   template hipError_t launch_chunk_fused_var<E, ACT_GELU, OFF>(                                 \
       const Dims&, const E*, const E*, const E*, const float*, const float*, const FuseIn<E>&, \
-      E*, float*, E*, float*, float*, hipStream_t);
+      E*, E*, E*, E*, float*, hipStream_t);
 INST(bf16, 0)
 INST(bf16, 1)
 INST(float, 0)

@@ -13,7 +13,7 @@ namespace prism {
 // training forward kept: the reverse state pass's additive term.
 template <typename E, int D, int C>
 __global__ __launch_bounds__(CF_NT) void et_kernel(const E* __restrict__ Qt, const E* __restrict__ dO,
-                                                   float* __restrict__ ET, int B, int T, int H, int NC,
+                                                   E* __restrict__ ET, int B, int T, int H, int NC,
                                                    const int* __restrict__ cu) {
   constexpr int NW = CF_NW, NT = CF_NT;
   constexpr int LR = ldpad<E>(D);
@@ -36,15 +36,15 @@ __global__ __launch_bounds__(CF_NT) void et_kernel(const E* __restrict__ Qt, con
   Acc<D, D, NW> ea;   // [n][r] = sum_t Qt[t][n] dO[t][r]: both operands k-strided in LDS
   ea.zero();
   gemm_acc<E, D, D, C, NW, false, false>(ea, Qs, LR, Os, LR, wave, lane);
-  float* ETc = ET + cidx * D * D;
+  E* ETc = ET + cidx * D * D;
   for_tiles(ea, wave, lane, [&](int n0, int r, const f32x4& x) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) ETc[(long)(n0 + i) * D + r] = x[i];
+    for (int i = 0; i < 4; ++i) ETc[(long)(n0 + i) * D + r] = to_t<E>(x[i]);
   });
 }
 
 template <typename E, int D, int C>
-static hipError_t et_launch_dc(const Dims& d, const E* Qt, const E* dO, float* ET, hipStream_t s) {
+static hipError_t et_launch_dc(const Dims& d, const E* Qt, const E* dO, E* ET, hipStream_t s) {
   if constexpr (sizeof(E) == 4 && D * C > 2048) return hipErrorInvalidValue;   // fp32 envelope
   hipLaunchKernelGGL((et_kernel<E, D, C>), dim3(d.B * d.H * d.NC), dim3(CF_NT), 0, s, Qt, dO, ET,
                      d.B, d.T, d.H, d.NC, d.cu);
@@ -52,7 +52,7 @@ static hipError_t et_launch_dc(const Dims& d, const E* Qt, const E* dO, float* E
 }
 
 template <typename E, int D>
-static hipError_t et_launch_d(const Dims& d, const E* Qt, const E* dO, float* ET, hipStream_t s) {
+static hipError_t et_launch_d(const Dims& d, const E* Qt, const E* dO, E* ET, hipStream_t s) {
   switch (d.C) {
     case 16: return et_launch_dc<E, D, 16>(d, Qt, dO, ET, s);
     case 32: return et_launch_dc<E, D, 32>(d, Qt, dO, ET, s);
@@ -62,7 +62,7 @@ static hipError_t et_launch_d(const Dims& d, const E* Qt, const E* dO, float* ET
 }
 
 template <typename E>
-hipError_t launch_et(const Dims& d, const E* Qt, const E* dO, float* ET, hipStream_t s) {
+hipError_t launch_et(const Dims& d, const E* Qt, const E* dO, E* ET, hipStream_t s) {
   switch (d.D) {
     case 16: return et_launch_d<E, 16>(d, Qt, dO, ET, s);
     case 32: return et_launch_d<E, 32>(d, Qt, dO, ET, s);
@@ -73,14 +73,14 @@ hipError_t launch_et(const Dims& d, const E* Qt, const E* dO, float* ET, hipStre
   }
   return hipErrorInvalidValue;
 }
-template hipError_t launch_et<bf16>(const Dims&, const bf16*, const bf16*, float*, hipStream_t);
+template hipError_t launch_et<bf16>(const Dims&, const bf16*, const bf16*, bf16*, hipStream_t);
 template hipError_t launch_et<float>(const Dims&, const float*, const float*, float*, hipStream_t);
 
 template <typename E, int D, int C>
 static hipError_t chunk_launch_dc(const Dims& d, const E* q, const E* k, const E* v,
                                   const float* alpha, const float* beta, const E* Kl, const E* Wl,
-                                  const E* dO, E* Mt, float* HT, E* Qt, float* Oloc, float* gC,
-                                  float* ET, E* UT, E* WkT, hipStream_t s) {
+                                  const E* dO, E* Mt, E* HT, E* Qt, E* Oloc, float* gC,
+                                  E* ET, E* UT, E* WkT, hipStream_t s) {
   const FuseIn<E> none{};
   if (dO)
     return chunk_launch_k<E, D, C, true, false, 0, 0>(d, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT,
@@ -92,8 +92,8 @@ static hipError_t chunk_launch_dc(const Dims& d, const E* q, const E* k, const E
 template <typename E, int D>
 static hipError_t chunk_launch_d(const Dims& d, const E* q, const E* k, const E* v,
                                  const float* alpha, const float* beta, const E* Kl, const E* Wl,
-                                 const E* dO, E* Mt, float* HT, E* Qt, float* Oloc, float* gC,
-                                 float* ET, E* UT, E* WkT, hipStream_t s) {
+                                 const E* dO, E* Mt, E* HT, E* Qt, E* Oloc, float* gC,
+                                 E* ET, E* UT, E* WkT, hipStream_t s) {
   switch (d.C) {
     case 16: return chunk_launch_dc<E, D, 16>(d, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, ET, UT, WkT, s);
     case 32: return chunk_launch_dc<E, D, 32>(d, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, ET, UT, WkT, s);
@@ -105,7 +105,7 @@ static hipError_t chunk_launch_d(const Dims& d, const E* q, const E* k, const E*
 template <typename E>
 hipError_t launch_chunk_fwd(const Dims& d, const E* q, const E* k, const E* v, const float* alpha,
                             const float* beta, const E* Kl, const E* Wl, const E* dO, E* Mt,
-                            float* HT, E* Qt, float* Oloc, float* gC, float* ET, E* UT,
+                            E* HT, E* Qt, E* Oloc, float* gC, E* ET, E* UT,
                             E* WkT, hipStream_t s) {
   switch (d.D) {
     case 16: return chunk_launch_d<E, 16>(d, q, k, v, alpha, beta, Kl, Wl, dO, Mt, HT, Qt, Oloc, gC, ET, UT, WkT, s);
@@ -121,8 +121,8 @@ hipError_t launch_chunk_fwd(const Dims& d, const E* q, const E* k, const E* v, c
 
 template hipError_t launch_chunk_fwd<bf16>(const Dims&, const bf16*, const bf16*, const bf16*,
                                            const float*, const float*, const bf16*, const bf16*,
-                                           const bf16*, bf16*, float*, bf16*, float*, float*,
-                                           float*, bf16*, bf16*, hipStream_t);
+                                           const bf16*, bf16*, bf16*, bf16*, bf16*, float*,
+                                           bf16*, bf16*, bf16*, hipStream_t);
 template hipError_t launch_chunk_fwd<float>(const Dims&, const float*, const float*, const float*,
                                             const float*, const float*, const float*, const float*,
                                             const float*, float*, float*, float*, float*, float*,
@@ -131,7 +131,7 @@ template hipError_t launch_chunk_fwd<float>(const Dims&, const float*, const flo
 template <typename E>
 hipError_t launch_chunk_fwd_fused(const Dims& d, const E* q, const E* k, const E* v,
                                   const float* alpha, const float* beta, const FuseIn<E>& fz,
-                                  E* Mt, float* HT, E* Qt, float* Oloc, float* gC,
+                                  E* Mt, E* HT, E* Qt, E* Oloc, float* gC,
                                   hipStream_t s) {
   if (d.L <= 0 || d.L > FUSE_LMAX) return hipErrorInvalidValue;
   if (d.act == ACT_IDENTITY)
@@ -142,7 +142,7 @@ hipError_t launch_chunk_fwd_fused(const Dims& d, const E* q, const E* k, const E
 }
 template hipError_t launch_chunk_fwd_fused<bf16>(const Dims&, const bf16*, const bf16*, const bf16*,
                                                  const float*, const float*, const FuseIn<bf16>&,
-                                                 bf16*, float*, bf16*, float*, float*, hipStream_t);
+                                                 bf16*, bf16*, bf16*, bf16*, float*, hipStream_t);
 template hipError_t launch_chunk_fwd_fused<float>(const Dims&, const float*, const float*,
                                                   const float*, const float*, const float*,
                                                   const FuseIn<float>&, float*, float*, float*,

@@ -112,9 +112,9 @@ template <typename E, int D, int C, bool BWD, bool FUSE, int ACT, int OFF>
 __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
     const E* __restrict__ q, const E* __restrict__ k, const E* __restrict__ v,
     const float* __restrict__ alpha, const float* __restrict__ beta, const E* __restrict__ Kl,
-    const E* __restrict__ Wl, const E* __restrict__ dO, E* __restrict__ Mt, float* __restrict__ HT,
-    E* __restrict__ Qt, float* __restrict__ Oloc, float* __restrict__ gCo,
-    float* __restrict__ ET, E* __restrict__ UTo, E* __restrict__ WkTo, int B, int T, int H, int L,
+    const E* __restrict__ Wl, const E* __restrict__ dO, E* __restrict__ Mt, E* __restrict__ HT,
+    E* __restrict__ Qt, E* __restrict__ Oloc, float* __restrict__ gCo,
+    E* __restrict__ ET, E* __restrict__ UTo, E* __restrict__ WkTo, int B, int T, int H, int L,
     int NC, int Tp, const int* __restrict__ cu, FuseIn<E> fz) {
   constexpr int HL = 3 + OFF;   // v rows before the chunk that the taps reach
   typedef ChunkLds<E, D, C, FUSE, HL> LY;
@@ -540,9 +540,9 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
   // H += U^T diag(D) K;  stored transposed (HT[n][r])
   gemm_acc<E, D, D, C, NW, true, true>(hacc, Ut, LT, KtD, LT, wave, lane);
   {
-    float* HTc = HT + cidx * D * D;
+    E* HTc = HT + cidx * D * D;
     for_tiles(hacc, wave, lane, [&](int r0, int n, const f32x4& x) {
-      *reinterpret_cast<f32x4*>(HTc + (long)n * D + r0) = x;
+      st_f4(HTc + (long)n * D + r0, x);
     });
   }
   {
@@ -579,9 +579,9 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
         Qtc[(long)t * D + f0 + r] = to_t<E>(ev[t] * to_f(Qr[t * LR + f0 + r]) - x[r]);
     });
     gemm_acc<E, D, C, C, NW, true, true>(oacc, Ut, LT, R0, LT, wave, lane);
-    float* Oc = Oloc + cidx * C * D;
+    E* Oc = Oloc + cidx * C * D;
     for_tiles(oacc, wave, lane, [&](int f0, int t, const f32x4& x) {
-      *reinterpret_cast<f32x4*>(Oc + (long)t * D + f0) = x;
+      st_f4(Oc + (long)t * D + f0, x);
     });
   } else {
     Acc<C, D, NW> qa;   // [t][f] = sum_i R0[t][i] Wk[i][f]  ->  Qt^T[f][t]
@@ -601,9 +601,9 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
     Acc<D, D, NW> ea;   // E[r][n] = sum_t dO[t][r] Qt[t][n]  -> stored as ET[n][r]
     ea.zero();
     gemm_acc<E, D, D, C, NW, true, true>(ea, dOt, LT, Qtt, LT, wave, lane);
-    float* ETc = ET + cidx * D * D;
+    E* ETc = ET + cidx * D * D;
     for_tiles(ea, wave, lane, [&](int r0, int n, const f32x4& x) {
-      *reinterpret_cast<f32x4*>(ETc + (long)n * D + r0) = x;
+      st_f4(ETc + (long)n * D + r0, x);
     });
   }
   if constexpr (!PERSIST) break;
@@ -614,7 +614,7 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
 template <typename E, int D, int C, bool BWD, bool FUSE, int ACT, int OFF>
 hipError_t chunk_launch_k(const Dims& d, const E* q, const E* k, const E* v, const float* alpha,
                           const float* beta, const E* Kl, const E* Wl, const E* dO, E* Mt,
-                          float* HT, E* Qt, float* Oloc, float* gC, float* ET, E* UT, E* WkT,
+                          E* HT, E* Qt, E* Oloc, float* gC, E* ET, E* UT, E* WkT,
                           const FuseIn<E>& fz, hipStream_t s) {
   if constexpr (sizeof(E) == 4 && D * C > 2048) {   // fp32 envelope
     return hipErrorInvalidValue;
@@ -633,7 +633,7 @@ hipError_t chunk_launch_k(const Dims& d, const E* q, const E* k, const E* v, con
 template <typename E, int ACT, int OFF>
 hipError_t launch_chunk_fused_var(const Dims& d, const E* q, const E* k, const E* v,
                                   const float* alpha, const float* beta, const FuseIn<E>& fz,
-                                  E* Mt, float* HT, E* Qt, float* Oloc, float* gC,
+                                  E* Mt, E* HT, E* Qt, E* Oloc, float* gC,
                                   hipStream_t s) {
   auto go = [&](auto dc) -> hipError_t {
     constexpr int D = decltype(dc)::first_type::value, C = decltype(dc)::second_type::value;
@@ -666,7 +666,7 @@ hipError_t launch_chunk_fused_var(const Dims& d, const E* q, const E* k, const E
 #define PRISM_CHUNK_FUSED_VARIANT(E, ACT, OFF)                                                    \
   extern template hipError_t launch_chunk_fused_var<E, ACT, OFF>(                                \
       const Dims&, const E*, const E*, const E*, const float*, const float*, const FuseIn<E>&,  \
-      E*, float*, E*, float*, float*, hipStream_t);
+      E*, E*, E*, E*, float*, hipStream_t);
 PRISM_CHUNK_FUSED_VARIANT(bf16, ACT_GELU, 0)
 PRISM_CHUNK_FUSED_VARIANT(bf16, ACT_GELU, 1)
 PRISM_CHUNK_FUSED_VARIANT(bf16, ACT_IDENTITY, 0)

@@ -75,7 +75,8 @@ struct Carve {
 template <typename E>
 struct FwdWs {
   E *Kl, *Wl, *Mt, *Qt, *Sc, *UT, *WkT;
-  float *HT, *Oloc, *gC;
+  E *HT, *Oloc;   // H^T and O_loc per chunk (storage type)
+  float* gC;
 };
 
 // What a training forward keeps for its backward (caller-owned buffer).
@@ -111,9 +112,9 @@ FwdWs<E> carve_fwd(const prism::Dims& d, Carve& cv) {
   // inside the chunk kernel, the training forward keeps them in its buffer
   w.Kl = w.Wl = nullptr;
   w.Mt = cv.take<E>(bh * d.NC * d.D * d.D * es);
-  w.HT = cv.take<float>(bh * d.NC * d.D * d.D * 4);
+  w.HT = cv.take<E>(bh * d.NC * d.D * d.D * sizeof(E));
   w.Qt = cv.take<E>(bh * d.NC * d.C * d.D * es);
-  w.Oloc = cv.take<float>(bh * d.NC * d.C * d.D * 4);
+  w.Oloc = cv.take<E>(bh * d.NC * d.C * d.D * sizeof(E));
   w.gC = cv.take<float>(bh * d.NC * 4);
   w.Sc = cv.take<E>(bh * d.NC * d.D * d.D * es);
   w.UT = w.WkT = nullptr;
@@ -199,7 +200,8 @@ struct BwdWs {
   E *Kl, *Wl, *Mt, *UT, *WkT, *Sc, *dSnT, *u, *dP, *WkW, *WpW, *dKl;
   float* dWl;
   E *dQt, *dUs, *dWks, *dKs, *dVp, *dqp, *dkp;
-  float *HT, *gC, *ET, *dgs, *dgp;
+  E *HT, *ET;     // H^T, E^T per chunk (storage type)
+  float *gC, *dgs, *dgp;
   float *dwbp, *dcp, *part;
 };
 
@@ -214,8 +216,8 @@ BwdWs<E> carve_bwd(const prism::Dims& d, Carve& cv) {
   w.Kl = cv.take<E>(bh * d.L * d.Tp * d.D * es);
   w.Wl = cv.take<E>(bh * d.L * d.Tp * d.D * es);
   w.Mt = cv.take<E>(bh * d.NC * DD * es);
-  w.HT = cv.take<float>(bh * d.NC * DD * 4);
-  w.ET = cv.take<float>(bh * d.NC * DD * 4);
+  w.HT = cv.take<E>(bh * d.NC * DD * es);
+  w.ET = cv.take<E>(bh * d.NC * DD * es);
   w.gC = cv.take<float>(bh * d.NC * 4);
   w.UT = cv.take<E>(bh * d.NC * CD * es);
   w.WkT = cv.take<E>(bh * d.NC * CD * es);

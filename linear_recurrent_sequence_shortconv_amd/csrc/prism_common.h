@@ -512,6 +512,30 @@ struct RegTile {
   }
 };
 
+// Four consecutive values of T to global memory, converted from fp32.
+__device__ inline void st_f4(float* p, const f32x4& x) { *reinterpret_cast<f32x4*>(p) = x; }
+__device__ inline void st_f4(bf16* p, const f32x4& x) {
+  const bf16 b[4] = {(bf16)x[0], (bf16)x[1], (bf16)x[2], (bf16)x[3]};
+  uint2 w;
+  __builtin_memcpy(&w, b, 8);
+  *reinterpret_cast<uint2*>(p) = w;
+}
+// Four consecutive values of T from global memory, held as raw bits until
+// raw4_to_f converts them where they are used: a conversion next to the load
+// would make a prefetch wait for its data at issue (the empty asm keeps the
+// conversion at the use).
+template <typename T> struct Raw4Of { typedef f32x4 type; };
+template <> struct Raw4Of<bf16> { typedef uint2 type; };
+template <typename T> __device__ inline typename Raw4Of<T>::type ld_raw4(const T* p) {
+  return *reinterpret_cast<const typename Raw4Of<T>::type*>(p);
+}
+__device__ inline f32x4 raw4_to_f(const f32x4& x) { return x; }
+__device__ inline f32x4 raw4_to_f(uint2 w) {
+  asm volatile("" : "+v"(w.x), "+v"(w.y));
+  return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
+               __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+}
+
 // LDS tile -> global rows (first nvalid rows only)
 template <typename T, int ROWS, int COLS, int NT>
 __device__ inline void s2g_rows(T* g, long gstride, const T* s, int ld, int nvalid, int tid) {

@@ -41,7 +41,7 @@ hipError_t launch_refine_fwd(const Dims& d, const E* v, const E* hist, const E* 
 template <typename E>
 hipError_t launch_chunk_fwd(const Dims& d, const E* q, const E* k, const E* v, const float* alpha,
                             const float* beta, const E* Kl, const E* Wl, const E* dO, E* Mt,
-                            float* HT, E* Qt, float* Oloc, float* gC, float* ET, E* UT, E* WkT,
+                            E* HT, E* Qt, E* Oloc, float* gC, E* ET, E* UT, E* WkT,
                             hipStream_t s);
 
 // Inputs of the refinement when the chunk kernel forms the pairs itself.
@@ -60,19 +60,19 @@ struct FuseIn {
 template <typename E>
 hipError_t launch_chunk_fwd_fused(const Dims& d, const E* q, const E* k, const E* v,
                                   const float* alpha, const float* beta, const FuseIn<E>& fz,
-                                  E* Mt, float* HT, E* Qt, float* Oloc, float* gC,
+                                  E* Mt, E* HT, E* Qt, E* Oloc, float* gC,
                                   hipStream_t s);
 
 // ET per chunk from a kept Qt and dO (the backward of a training forward).
 template <typename E>
-hipError_t launch_et(const Dims& d, const E* Qt, const E* dO, float* ET, hipStream_t s);
+hipError_t launch_et(const Dims& d, const E* Qt, const E* dO, E* ET, hipStream_t s);
 
 // Sequential pass over chunks, forward (X <- exp(gC) X - X M + H, from S0) or
 // reverse (X <- exp(gC) X - X M^T + E, from dS_T).  Both read Mt = M^T; AddT
 // is H^T or E^T.  Stores X per chunk before its update (row-major, or
 // transposed), and the final X in `fin` when not null.
 template <typename E>
-hipError_t launch_state_pass(const Dims& d, const float* init, const E* Mt, const float* AddT,
+hipError_t launch_state_pass(const Dims& d, const float* init, const E* Mt, const E* AddT,
                              const float* gC, E* Xc, float* fin, bool transposed, bool reverse,
                              hipStream_t s);
 
@@ -144,7 +144,7 @@ hipError_t launch_step(const Dims& d, const E* q, const E* k, const E* v, const 
 
 // O = O_loc + Qt S_c^T, written to o [B, T, H, D].
 template <typename E>
-hipError_t launch_out_fwd(const Dims& d, const E* Sc, const E* Qt, const float* Oloc, E* o,
+hipError_t launch_out_fwd(const Dims& d, const E* Sc, const E* Qt, const E* Oloc, E* o,
                           hipStream_t s);
 
 }  // namespace prism

@@ -38,7 +38,7 @@ constexpr long SP_WIDE = 256;   // workgroups that fill the chip (one per CU)
 template <typename E, int D, int RB, bool REV>
 __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restrict__ init,
                                                            const E* __restrict__ Bm,
-                                                           const float* __restrict__ AddT,
+                                                           const E* __restrict__ AddT,
                                                            const float* __restrict__ gC,
                                                            E* __restrict__ Xc, float* __restrict__ fin,
                                                            int B, int H, int NC, int transposed,
@@ -81,7 +81,7 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
   // register sets, indexed by the step's parity at compile time): a step
   // then stages into LDS only data that has had a whole step to arrive.
   uint4 mst[2][PER];                    // Bm of a coming step, staged through registers
-  f32x4 addn[2][TL::RM][TL::RN];        // AddT^T block of a coming step
+  typename Raw4Of<E>::type addn[2][TL::RM][TL::RN];   // AddT^T block of a coming step (raw)
   float egn[2] = {0.f, 0.f};            // decay of a coming step
   auto fetch = [&](int step, auto setc) {
     constexpr int Z = decltype(setc)::value;
@@ -93,12 +93,12 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
       if (e < NV) mst[Z][p] = ld16(bm + (long)e * VN);
     }
     if (act) {
-      const float* ac = AddT + cidx * D * D + rb0;
+      const E* ac = AddT + cidx * D * D + rb0;
 #pragma unroll
       for (int i = 0; i < TL::RM; ++i)
 #pragma unroll
         for (int j = 0; j < TL::RN; ++j)
-          addn[Z][i][j] = *reinterpret_cast<const f32x4*>(ac + (long)(n0 + 16 * j + cl) * D + m0 + 16 * i + rl);
+          addn[Z][i][j] = ld_raw4(ac + (long)(n0 + 16 * j + cl) * D + m0 + 16 * i + rl);
     }
     egn[Z] = expf(gC[cidx]);
   };
@@ -123,7 +123,7 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
 #pragma unroll
     for (int i = 0; i < TL::RM; ++i)
 #pragma unroll
-      for (int j = 0; j < TL::RN; ++j) addc[i][j] = addn[Z][i][j];
+      for (int j = 0; j < TL::RN; ++j) addc[i][j] = raw4_to_f(addn[Z][i][j]);
     const float egc = egn[Z];
     if (act) {   // state -> operand copy
 #pragma unroll
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
 }
 
 template <typename E, int D>
-static hipError_t state_launch_d(const Dims& d, const float* init, const E* Bm, const float* AddT,
+static hipError_t state_launch_d(const Dims& d, const float* init, const E* Bm, const E* AddT,
                                  const float* gC, E* Xc, float* fin, bool tr, bool rev,
                                  hipStream_t s) {
   // Row blocks: the whole state below D = 128; at D = 128 blocks of 64 rows
@@ -218,7 +218,7 @@ static hipError_t state_launch_d(const Dims& d, const float* init, const E* Bm, 
 }
 
 template <typename E>
-hipError_t launch_state_pass(const Dims& d, const float* init, const E* Bm, const float* AddT,
+hipError_t launch_state_pass(const Dims& d, const float* init, const E* Bm, const E* AddT,
                              const float* gC, E* Xc, float* fin, bool transposed, bool reverse,
                              hipStream_t s) {
   switch (d.D) {
@@ -242,7 +242,7 @@ constexpr int OF_NT = OF_NW * WAVE;
 template <typename E, int D, int C>
 __global__ __launch_bounds__(OF_NT) void out_fwd_kernel(const E* __restrict__ Sc,
                                                         const E* __restrict__ Qt,
-                                                        const float* __restrict__ Oloc,
+                                                        const E* __restrict__ Oloc,
                                                         E* __restrict__ o, int B, int T, int H,
                                                         int NC, const int* __restrict__ cu) {
   constexpr int LR = ldpad<E>(D);
@@ -261,15 +261,15 @@ __global__ __launch_bounds__(OF_NT) void out_fwd_kernel(const E* __restrict__ Sc
   // O_loc in the accumulator layout, requested before the product so that
   // its latency overlaps it: tile (i, j) holds features f0 .. f0 + 3 of token t
   typedef Tiling<D, C, OF_NW> TL;
-  const float* Oc = Oloc + cidx * C * D;
-  f32x4 ol[TL::RM][TL::RN];
+  const E* Oc = Oloc + cidx * C * D;
+  typename Raw4Of<E>::type ol[TL::RM][TL::RN];
   if (TL::active(wave)) {
 #pragma unroll
     for (int i = 0; i < TL::RM; ++i)
 #pragma unroll
       for (int j = 0; j < TL::RN; ++j) {
         const int f0 = TL::m0(wave) + 16 * i + 4 * (lane >> 4), t = TL::n0(wave) + 16 * j + (lane & 15);
-        ol[i][j] = t < nval ? *reinterpret_cast<const f32x4*>(Oc + (long)t * D + f0) : f32x4{0.f, 0.f, 0.f, 0.f};
+        ol[i][j] = t < nval ? ld_raw4(Oc + (long)t * D + f0) : typename Raw4Of<E>::type{};
       }
   }
   __syncthreads();
@@ -279,14 +279,15 @@ __global__ __launch_bounds__(OF_NT) void out_fwd_kernel(const E* __restrict__ Sc
   E* oc = o + ((seq_start(cu, b, T) + c * C) * H + h) * D;
   for_tiles_ij(a, wave, lane, [&](int i, int j, int f0, int t, const f32x4& x) {
     if (t < nval) {
+      const f32x4 lo = raw4_to_f(ol[i][j]);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) oc[(long)t * H * D + f0 + r] = to_t<E>(ol[i][j][r] + x[r]);
+      for (int r = 0; r < 4; ++r) oc[(long)t * H * D + f0 + r] = to_t<E>(lo[r] + x[r]);
     }
   });
 }
 
 template <typename E, int D, int C>
-static hipError_t out_launch_dc(const Dims& d, const E* Sc, const E* Qt, const float* Oloc, E* o,
+static hipError_t out_launch_dc(const Dims& d, const E* Sc, const E* Qt, const E* Oloc, E* o,
                                 hipStream_t s) {
   if constexpr (sizeof(E) == 4 && D * C > 2048) return hipErrorInvalidValue;   // fp32 envelope
   hipLaunchKernelGGL((out_fwd_kernel<E, D, C>), dim3(d.B * d.H * d.NC), dim3(OF_NT), 0, s, Sc, Qt,
@@ -295,7 +296,7 @@ static hipError_t out_launch_dc(const Dims& d, const E* Sc, const E* Qt, const f
 }
 
 template <typename E, int D>
-static hipError_t out_launch_d(const Dims& d, const E* Sc, const E* Qt, const float* Oloc, E* o,
+static hipError_t out_launch_d(const Dims& d, const E* Sc, const E* Qt, const E* Oloc, E* o,
                                hipStream_t s) {
   switch (d.C) {
     case 16: return out_launch_dc<E, D, 16>(d, Sc, Qt, Oloc, o, s);
@@ -306,7 +307,7 @@ static hipError_t out_launch_d(const Dims& d, const E* Sc, const E* Qt, const fl
 }
 
 template <typename E>
-hipError_t launch_out_fwd(const Dims& d, const E* Sc, const E* Qt, const float* Oloc, E* o,
+hipError_t launch_out_fwd(const Dims& d, const E* Sc, const E* Qt, const E* Oloc, E* o,
                           hipStream_t s) {
   switch (d.D) {
     case 16: return out_launch_d<E, 16>(d, Sc, Qt, Oloc, o, s);
@@ -319,11 +320,11 @@ hipError_t launch_out_fwd(const Dims& d, const E* Sc, const E* Qt, const float* 
   return hipErrorInvalidValue;
 }
 
-template hipError_t launch_state_pass<bf16>(const Dims&, const float*, const bf16*, const float*,
+template hipError_t launch_state_pass<bf16>(const Dims&, const float*, const bf16*, const bf16*,
                                             const float*, bf16*, float*, bool, bool, hipStream_t);
 template hipError_t launch_state_pass<float>(const Dims&, const float*, const float*, const float*,
                                              const float*, float*, float*, bool, bool, hipStream_t);
-template hipError_t launch_out_fwd<bf16>(const Dims&, const bf16*, const bf16*, const float*,
+template hipError_t launch_out_fwd<bf16>(const Dims&, const bf16*, const bf16*, const bf16*,
                                          bf16*, hipStream_t);
 template hipError_t launch_out_fwd<float>(const Dims&, const float*, const float*, const float*,
                                           float*, hipStream_t);
