@@ -62,6 +62,7 @@ def _check_full(x, dtype, chunk, L):
     go = oracle_backward(x, L)
     names = SEQ_GRADS + (W_GRADS if L > 0 else ()) + ("dS0",)
     _compare(gg, go, names, TOL[dtype])
+    return gg, go
 
 
 @pytest.mark.parametrize("d,chunk", [(16, 16), (16, 64), (32, 32), (64, 16), (64, 32)])
@@ -96,7 +97,12 @@ def test_bf16_d128_backward(chunk):
 def test_bf16_backward_long_memory():
     x = make_inputs(2, 300, 2, 64, 2, "bf16", seed=8, alpha_logit_mean=6.0, with_dST=True)
     print("\n[bf16 bwd long memory d=64 T=300 L=2]", flush=True)
-    _check_full(x, "bf16", 64, 2)
+    gg, go = _check_full(x, "bf16", 64, 2)
+    # The gradient of the refinement values dW_l is kept in fp32 between the
+    # chunk and refinement backward kernels: it enters beta^(l) dW_l - dL/dr,
+    # which can nearly cancel.  Held in bf16 it gave 1.5e-2 here (5.5e-3 in
+    # fp32); this bound keeps that margin.
+    assert relerr(gg["dWp"], go["dWp"]) <= 1e-2
 
 
 def _check_workload(name, pairs, weight_head):
