@@ -69,10 +69,12 @@ def algorithmic_counts(w):
                               + nch * (4 * D * D * e + 2 * C * D * e + 4),
                               nch * (2 * C * C * D * (2 * L + 5) + 2 * C * D * D * (L + 4)))
     c["et_chunks"] = (nch * (2 * C * D * e + D * D * e), nch * 2 * C * D * D)
+    # state pass: read M^T, H^T, write S_c (kept by the training forward), S0 /
+    # S_T; the forward pass also forms the readout: read Qt, O_loc, write o
     st = (nch * D * D * 3 * e + bh * D * D * 4, nch * 2 * D ** 3)
-    c["state_fwd"] = c["state_fwd_recompute"] = st
+    c["state_fwd"] = (st[0] + nch * C * D * 2 * e + th * D * e, st[1] + nch * 2 * C * D * D)
+    c["state_fwd_recompute"] = st
     c["state_bwd"] = (st[0] + bh * D * D * 4, st[1])
-    c["out_fwd"] = (nch * (D * D * e + C * D * 2 * e) + th * D * e, nch * 2 * C * D * D)
     c["chunk_bwd_state"] = (th * (2 * D * e + 4) + nch * (2 * C * D * e + 2 * D * D * e + 4 * e * C * D + 4 * C)
                             + ntp * L * D * (3 * e + 4),  # read K_l, W_l; write dK_l, dW_l (fp32) partials
                             nch * (2 * C * D * D * (6 + 2 * L) + 2 * D ** 3))
@@ -138,7 +140,6 @@ def measured_traffic():
 _FAMILIES = [("refine_fwd_kernel", ["refine_fwd", "refine_fwd_recompute"]),
              ("et_kernel", ["et_chunks"]),
              ("state_pass_kernel", ["state_fwd", "state_fwd_recompute", "state_bwd"]),
-             ("out_fwd_kernel", ["out_fwd"]),
              ("chunk_bwd_state_kernel", ["chunk_bwd_state"]),
              ("chunk_bwd_solve_kernel", ["chunk_bwd_solve"]),
              ("chunk_bwd_pairs_kernel", ["chunk_bwd_pairs"]),

@@ -2,8 +2,8 @@
 // launch sequence.  The launch sequence of the forward pass is
 //   refine_fwd  (ShortConv anchor + L refinement steps, summary §2.2)
 //   chunk_fwd   (chunk-local affine maps of S_t = S_{t-1} A_t + B_t, §2.1)
-//   state_fwd   (sequential pass over chunks, fp32 state)
-//   out_fwd     (readout o_t = S_t q_t)
+//   state_fwd   (sequential pass over chunks, fp32 state, with the readout
+//                o_t = S_t q_t of each chunk formed in the same step)
 // The training pair keeps the forward's refinement pairs, chunk maps, chunk
 // states and solve results in a caller buffer, so that its backward starts at
 // the reverse state pass instead of recomputing them.
@@ -327,9 +327,11 @@ prism_status run_forward(const prism::Dims& d, const void* q, const void* k, con
             prism::launch_chunk_fwd<E>(d, q_, k_, v_, alpha, beta, w.Kl, w.Wl, nullptr, w.Mt,
                                        w.HT, w.Qt, w.Oloc, w.gC, nullptr, w.UT, w.WkT, s));
   }
+  // state pass with the readout fused; the chunk-entry states go to HBM only
+  // when the training forward keeps them
   HIP_TRY("state_fwd", s,
-          prism::launch_state_pass<E>(d, S0, w.Mt, w.HT, w.gC, w.Sc, ST, false, false, s));
-  HIP_TRY("out_fwd", s, prism::launch_out_fwd<E>(d, w.Sc, w.Qt, w.Oloc, static_cast<E*>(o), s));
+          prism::launch_state_pass<E>(d, S0, w.Mt, w.HT, w.gC, keep ? w.Sc : nullptr, ST, false,
+                                      false, w.Qt, w.Oloc, static_cast<E*>(o), s));
   // after every read of hist, which hist_out may overwrite
   if (hist_out)
     HIP_TRY("conv_state", s, prism::launch_conv_state<E>(d, v_, hist_, static_cast<E*>(hist_out), s));
@@ -375,10 +377,12 @@ prism_status run_backward(const prism::Dims& d, const void* q, const void* k, co
             prism::launch_chunk_fwd<E>(d, q_, k_, v_, alpha, beta, w.Kl, w.Wl, dO_, w.Mt, w.HT,
                                        nullptr, nullptr, w.gC, w.ET, w.UT, w.WkT, s));
     HIP_TRY("state_fwd_recompute", s,
-            prism::launch_state_pass<E>(d, S0, w.Mt, w.HT, w.gC, w.Sc, nullptr, false, false, s));
+            prism::launch_state_pass<E>(d, S0, w.Mt, w.HT, w.gC, w.Sc, nullptr, false, false,
+                                        nullptr, nullptr, nullptr, s));
   }
   HIP_TRY("state_bwd", s,
-          prism::launch_state_pass<E>(d, dST, w.Mt, w.ET, w.gC, w.dSnT, dS0, true, true, s));
+          prism::launch_state_pass<E>(d, dST, w.Mt, w.ET, w.gC, w.dSnT, dS0, true, true, nullptr,
+                                      nullptr, nullptr, s));
   prism::ChunkBwdArgs<E> a;
   a.q = q_; a.k = k_; a.v = v_; a.dO = dO_; a.alpha = alpha; a.beta = beta;
   a.Kl = w.Kl; a.Wl = w.Wl; a.UT = w.UT; a.WkT = w.WkT; a.Sc = w.Sc; a.dSnT = w.dSnT;

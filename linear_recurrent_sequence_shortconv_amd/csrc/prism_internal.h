@@ -74,7 +74,7 @@ hipError_t launch_et(const Dims& d, const E* Qt, const E* dO, E* ET, hipStream_t
 template <typename E>
 hipError_t launch_state_pass(const Dims& d, const float* init, const E* Mt, const E* AddT,
                              const float* gC, E* Xc, float* fin, bool transposed, bool reverse,
-                             hipStream_t s);
+                             const E* Qt, const E* Oloc, E* o, hipStream_t s);
 
 // Arguments of the three chunk-parallel backward kernels (see chunk_bwd.hip).
 template <typename E>
@@ -142,9 +142,5 @@ hipError_t launch_step(const Dims& d, const E* q, const E* k, const E* v, const 
                        const float* beta, const E* Wk, const E* Wp, const E* wbeta, const E* conv,
                        float* S, E* cstate, E* o, E* Kl, E* Wl, int stage, hipStream_t s);
 
-// O = O_loc + Qt S_c^T, written to o [B, T, H, D].
-template <typename E>
-hipError_t launch_out_fwd(const Dims& d, const E* Sc, const E* Qt, const E* Oloc, E* o,
-                          hipStream_t s);
 
 }  // namespace prism

@@ -1,7 +1,7 @@
 // The only sequential part of the PRISM recurrence (summary §2.1, S_t =
 // S_{t-1} A_t + B_t): chunk after chunk, S_{c+1} = exp(gC_c) S_c - S_c M_c + H_c,
-// followed by the chunk-parallel readout O = O_loc + Qt S_c^T (the readout
-// o_t = S_t q_t, reading R7).  The same kernel runs the adjoint pass of the
+// and in the same step the chunk's readout O = O_loc + Qt S_c^T (the readout
+// o_t = S_t q_t with the post-update state).  The same kernel runs the adjoint pass of the
 // backward in reverse chunk order: dS_c = exp(gC_c) dS_{c+1} - dS_{c+1} M_c^T + E_c.
 //
 // Rows of S (the value index) never mix, so the pass is split over row
@@ -31,11 +31,17 @@ namespace prism {
 // double-buffered LDS tiles, and the next step's Bm, AddT block and decay are
 // fetched from global memory (L2: the row blocks of one sequence sit on the
 // same XCD) while the current step multiplies.
+// With RO (forward only) each step also forms its row block of the chunk's
+// readout, O[t][f] = O_loc[t][f] + sum_k Qt[t][k] S_c[f][k], from the operand
+// copy of S_c already in LDS: the chunk's Qt rows and O_loc block are fetched
+// two steps ahead with the other operands, and S_c goes to HBM only when a
+// caller keeps it (Xc non-null).  The readout reads no S_c from HBM and needs
+// no launch of its own.
 constexpr int SP_NW = 8;
 constexpr int SP_NT = SP_NW * WAVE;
 constexpr long SP_WIDE = 256;   // workgroups that fill the chip (one per CU)
 
-template <typename E, int D, int RB, bool REV>
+template <typename E, int D, int RB, bool REV, int C_RO>
 __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restrict__ init,
                                                            const E* __restrict__ Bm,
                                                            const E* __restrict__ AddT,
@@ -43,7 +49,14 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
                                                            E* __restrict__ Xc, float* __restrict__ fin,
                                                            int B, int H, int NC, int transposed,
                                                            int reverse, int T, int C,
-                                                           const int* __restrict__ cu) {
+                                                           const int* __restrict__ cu,
+                                                           const E* __restrict__ Qt,
+                                                           const E* __restrict__ Oloc,
+                                                           E* __restrict__ o) {
+  // C_RO > 0: fused readout for chunks of C_RO tokens (forward only)
+  constexpr bool RO = C_RO > 0;
+  constexpr int CR = RO ? C_RO : 16;
+  static_assert(!(RO && REV), "the readout belongs to the forward pass");
   constexpr int LS = ldpad<E>(D);
   constexpr int VN = 16 / sizeof(E);
   constexpr int NV = D * D / VN;                       // 16-byte vectors of Bm_c
@@ -53,6 +66,10 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
   typedef Tiling<RB, D, SP_NW> TL;
   __shared__ __attribute__((aligned(16))) E Mb[2][D * LS];
   __shared__ __attribute__((aligned(16))) E Ss[2][RB * LS];
+  __shared__ __attribute__((aligned(16))) E Qb[RO ? 2 : 1][RO ? CR * LS : 8];   // Qt rows of a step
+  constexpr int NVQ = CR * D / VN;                     // 16-byte vectors of Qt_c
+  constexpr int PERQ = (NVQ + SP_NT - 1) / SP_NT;
+  typedef Tiling<RB, CR, SP_NW> TLO;                   // readout tiles [f][t]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nblk = B * H * NRB;
   const int bid = xcd_swizzle(blockIdx.x, nblk);
@@ -81,6 +98,8 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
   // register sets, indexed by the step's parity at compile time): a step
   // then stages into LDS only data that has had a whole step to arrive.
   uint4 mst[2][PER];                    // Bm of a coming step, staged through registers
+  uint4 qst[2][RO ? PERQ : 1];          // Qt rows of a coming step (readout)
+  typename Raw4Of<E>::type oln[2][RO ? TLO::RM : 1][RO ? TLO::RN : 1];   // its O_loc block (raw)
   typename Raw4Of<E>::type addn[2][TL::RM][TL::RN];   // AddT^T block of a coming step (raw)
   float egn[2] = {0.f, 0.f};            // decay of a coming step
   auto fetch = [&](int step, auto setc) {
@@ -101,6 +120,24 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
           addn[Z][i][j] = ld_raw4(ac + (long)(n0 + 16 * j + cl) * D + m0 + 16 * i + rl);
     }
     egn[Z] = expf(gC[cidx]);
+    if constexpr (RO) {
+      const E* qc = Qt + cidx * CR * D;
+#pragma unroll
+      for (int p = 0; p < PERQ; ++p) {
+        const int e = tid + p * SP_NT;
+        if (e < NVQ) qst[Z][p] = ld16(qc + (long)e * VN);
+      }
+      if (TLO::active(wave)) {
+        const E* oc = Oloc + cidx * CR * D + rb0;
+#pragma unroll
+        for (int i = 0; i < TLO::RM; ++i)
+#pragma unroll
+          for (int j = 0; j < TLO::RN; ++j) {
+            const int f0 = TLO::m0(wave) + 16 * i + 4 * (lane >> 4), t = TLO::n0(wave) + 16 * j + (lane & 15);
+            oln[Z][i][j] = ld_raw4(oc + (long)t * D + f0);
+          }
+      }
+    }
   };
   auto stage = [&](E* dst, auto setc) {
     constexpr int Z = decltype(setc)::value;
@@ -110,6 +147,16 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
       if (e < NV) {
         const int r = e / (D / VN), c = (e % (D / VN)) * VN;
         st16(dst + r * LS + c, mst[Z][p]);
+      }
+    }
+    if constexpr (RO) {
+#pragma unroll
+      for (int p = 0; p < PERQ; ++p) {
+        const int e = tid + p * SP_NT;
+        if (e < NVQ) {
+          const int r = e / (D / VN), c = (e % (D / VN)) * VN;
+          st16(Qb[Z] + r * LS + c, qst[Z][p]);
+        }
       }
     }
   };
@@ -125,6 +172,14 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
 #pragma unroll
       for (int j = 0; j < TL::RN; ++j) addc[i][j] = raw4_to_f(addn[Z][i][j]);
     const float egc = egn[Z];
+    // this step's O_loc block: set Z is refilled with step + 2's below
+    typename Raw4Of<E>::type olc[RO ? TLO::RM : 1][RO ? TLO::RN : 1];
+    if constexpr (RO) {
+#pragma unroll
+      for (int i = 0; i < TLO::RM; ++i)
+#pragma unroll
+        for (int j = 0; j < TLO::RN; ++j) olc[i][j] = oln[Z][i][j];
+    }
     if (act) {   // state -> operand copy
 #pragma unroll
       for (int i = 0; i < TL::RM; ++i)
@@ -138,13 +193,16 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
     // other buffers are free to refill
     __syncthreads();
     if (step + 2 < ncb) fetch(step + 2, setc);
-    E* Xcc = Xc + cidx * D * D;
-    if (!transposed) {
+    if (!Xc) {
+      // the chunk-entry states are not kept (readout fused, inference)
+    } else if (!transposed) {
+      E* Xcc = Xc + cidx * D * D;
       for (int e = tid; e < NVR; e += SP_NT) {
         const int r = e / (D / VN), c = (e % (D / VN)) * VN;
         st16(Xcc + (long)(rb0 + r) * D + c, ld16(Ss[Z] + r * LS + c));
       }
     } else {
+      E* Xcc = Xc + cidx * D * D;
       for (int e = tid; e < NVR; e += SP_NT) {
         const int kk = e / (RB / VN), r0 = (e % (RB / VN)) * VN;
         E tmp[VN];
@@ -163,6 +221,23 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
       for (int i = 0; i < TL::RM; ++i)
 #pragma unroll
         for (int j = 0; j < TL::RN; ++j) S.v[i][j] = egc * S.v[i][j] - P.v[i][j] + addc[i][j];
+    }
+    if constexpr (RO) {
+      // readout rows f = rb0 .. rb0 + RB - 1 of chunk cidx: [f][t] = S_c[f] . Qt[t]
+      Acc<RB, CR, SP_NW> R;
+      R.zero();
+      gemm_acc<E, RB, CR, D, SP_NW, true, true>(R, Ss[Z], LS, Qb[Z], LS, wave, lane);
+      const int b = bh / H, h = bh % H;
+      const int c0 = chunk_of(step) * CR;
+      const int nval = min(CR, seq_len(cu, b, T) - c0);
+      E* oc = o + ((seq_start(cu, b, T) + c0) * H + h) * D + rb0;
+      for_tiles_ij(R, wave, lane, [&](int i, int j, int f0, int t, const f32x4& x) {
+        if (t < nval) {
+          const f32x4 lo = raw4_to_f(olc[i][j]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) oc[(long)t * H * D + f0 + r] = to_t<E>(lo[r] + x[r]);
+        }
+      });
     }
     if (step + 1 < ncb) stage(Mb[Z ^ 1], std::integral_constant<int, Z ^ 1>{});
   };
@@ -189,7 +264,7 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
 template <typename E, int D>
 static hipError_t state_launch_d(const Dims& d, const float* init, const E* Bm, const E* AddT,
                                  const float* gC, E* Xc, float* fin, bool tr, bool rev,
-                                 hipStream_t s) {
+                                 const E* Qt, const E* Oloc, E* o, hipStream_t s) {
   // Row blocks: the whole state below D = 128; at D = 128 blocks of 64 rows
   // (two workgroups per sequence), or of 32 or 16 rows when there are too few
   // sequence-heads to give every CU a workgroup (long sequences, small
@@ -197,14 +272,35 @@ static hipError_t state_launch_d(const Dims& d, const float* init, const E* Bm, 
   // parallelism it has).
   auto go = [&](auto rbc) {
     constexpr int RB = decltype(rbc)::value;
-    if (rev)
-      hipLaunchKernelGGL((state_pass_kernel<E, D, RB, true>), dim3(d.B * d.H * (D / RB)), dim3(SP_NT),
-                         0, s, init, Bm, AddT, gC, Xc, fin, d.B, d.H, d.NC, tr ? 1 : 0, 1, d.T, d.C,
-                         d.cu);
-    else
-      hipLaunchKernelGGL((state_pass_kernel<E, D, RB, false>), dim3(d.B * d.H * (D / RB)), dim3(SP_NT),
-                         0, s, init, Bm, AddT, gC, Xc, fin, d.B, d.H, d.NC, tr ? 1 : 0, 0, d.T, d.C,
-                         d.cu);
+    const dim3 grid(d.B * d.H * (D / RB));
+    if (rev) {
+      hipLaunchKernelGGL((state_pass_kernel<E, D, RB, true, 0>), grid, dim3(SP_NT), 0, s, init, Bm,
+                         AddT, gC, Xc, fin, d.B, d.H, d.NC, tr ? 1 : 0, 1, d.T, d.C, d.cu, nullptr,
+                         nullptr, nullptr);
+    } else if (!o) {
+      hipLaunchKernelGGL((state_pass_kernel<E, D, RB, false, 0>), grid, dim3(SP_NT), 0, s, init, Bm,
+                         AddT, gC, Xc, fin, d.B, d.H, d.NC, tr ? 1 : 0, 0, d.T, d.C, d.cu, nullptr,
+                         nullptr, nullptr);
+    } else {
+      auto ro = [&](auto cc) -> hipError_t {
+        constexpr int CC = decltype(cc)::value;
+        if constexpr (sizeof(E) == 4 && D * CC > 2048) {
+          return hipErrorInvalidValue;   // outside the fp32 envelope
+        } else {
+          hipLaunchKernelGGL((state_pass_kernel<E, D, RB, false, CC>), grid, dim3(SP_NT), 0, s, init,
+                             Bm, AddT, gC, Xc, fin, d.B, d.H, d.NC, tr ? 1 : 0, 0, d.T, d.C, d.cu,
+                             Qt, Oloc, o);
+          return hipSuccess;
+        }
+      };
+      hipError_t e = hipErrorInvalidValue;
+      switch (d.C) {
+        case 16: e = ro(std::integral_constant<int, 16>{}); break;
+        case 32: e = ro(std::integral_constant<int, 32>{}); break;
+        case 64: e = ro(std::integral_constant<int, 64>{}); break;
+      }
+      if (e != hipSuccess) return e;
+    }
     return hipGetLastError();
   };
   if constexpr (D > 64) {
@@ -220,113 +316,25 @@ static hipError_t state_launch_d(const Dims& d, const float* init, const E* Bm, 
 template <typename E>
 hipError_t launch_state_pass(const Dims& d, const float* init, const E* Bm, const E* AddT,
                              const float* gC, E* Xc, float* fin, bool transposed, bool reverse,
+                             const E* Qt, const E* Oloc, E* o,
                              hipStream_t s) {
   switch (d.D) {
-    case 16: return state_launch_d<E, 16>(d, init, Bm, AddT, gC, Xc, fin, transposed, reverse, s);
-    case 32: return state_launch_d<E, 32>(d, init, Bm, AddT, gC, Xc, fin, transposed, reverse, s);
-    case 64: return state_launch_d<E, 64>(d, init, Bm, AddT, gC, Xc, fin, transposed, reverse, s);
+    case 16: return state_launch_d<E, 16>(d, init, Bm, AddT, gC, Xc, fin, transposed, reverse, Qt, Oloc, o, s);
+    case 32: return state_launch_d<E, 32>(d, init, Bm, AddT, gC, Xc, fin, transposed, reverse, Qt, Oloc, o, s);
+    case 64: return state_launch_d<E, 64>(d, init, Bm, AddT, gC, Xc, fin, transposed, reverse, Qt, Oloc, o, s);
     case 128:
       if constexpr (sizeof(E) == 2)
-        return state_launch_d<E, 128>(d, init, Bm, AddT, gC, Xc, fin, transposed, reverse, s);
-      break;
-  }
-  return hipErrorInvalidValue;
-}
-
-// ---------------------------------------------------------------------------
-// readout: O[t][f] = O_loc[t][f] + sum_k Qt[t][k] S_c[f][k]
-// ---------------------------------------------------------------------------
-constexpr int OF_NW = 4;
-constexpr int OF_NT = OF_NW * WAVE;
-
-template <typename E, int D, int C>
-__global__ __launch_bounds__(OF_NT) void out_fwd_kernel(const E* __restrict__ Sc,
-                                                        const E* __restrict__ Qt,
-                                                        const E* __restrict__ Oloc,
-                                                        E* __restrict__ o, int B, int T, int H,
-                                                        int NC, const int* __restrict__ cu) {
-  constexpr int LR = ldpad<E>(D);
-  __shared__ __attribute__((aligned(16))) E Ss[D * LR];
-  __shared__ __attribute__((aligned(16))) E Qs[C * LR];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nblk = B * H * NC;
-  const int bid = xcd_swizzle(blockIdx.x, nblk);
-  const int c = bid % NC, bh = bid / NC;
-  const int h = bh % H, b = bh / H;
-  const int nval = min(C, seq_len(cu, b, T) - c * C);
-  if (nval <= 0) return;   // past the end of a packed sequence: S_c was never written
-  const long cidx = (long)bh * NC + c;
-  g2s_rows<E, D, D, OF_NT>(Ss, LR, Sc + cidx * D * D, D, D, tid);
-  g2s_rows<E, C, D, OF_NT>(Qs, LR, Qt + cidx * C * D, D, C, tid);
-  // O_loc in the accumulator layout, requested before the product so that
-  // its latency overlaps it: tile (i, j) holds features f0 .. f0 + 3 of token t
-  typedef Tiling<D, C, OF_NW> TL;
-  const E* Oc = Oloc + cidx * C * D;
-  typename Raw4Of<E>::type ol[TL::RM][TL::RN];
-  if (TL::active(wave)) {
-#pragma unroll
-    for (int i = 0; i < TL::RM; ++i)
-#pragma unroll
-      for (int j = 0; j < TL::RN; ++j) {
-        const int f0 = TL::m0(wave) + 16 * i + 4 * (lane >> 4), t = TL::n0(wave) + 16 * j + (lane & 15);
-        ol[i][j] = t < nval ? ld_raw4(Oc + (long)t * D + f0) : typename Raw4Of<E>::type{};
-      }
-  }
-  __syncthreads();
-  Acc<D, C, OF_NW> a;   // [f][t] = S[f] . Qt[t]
-  a.zero();
-  gemm_acc<E, D, C, D, OF_NW, true, true>(a, Ss, LR, Qs, LR, wave, lane);
-  E* oc = o + ((seq_start(cu, b, T) + c * C) * H + h) * D;
-  for_tiles_ij(a, wave, lane, [&](int i, int j, int f0, int t, const f32x4& x) {
-    if (t < nval) {
-      const f32x4 lo = raw4_to_f(ol[i][j]);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) oc[(long)t * H * D + f0 + r] = to_t<E>(lo[r] + x[r]);
-    }
-  });
-}
-
-template <typename E, int D, int C>
-static hipError_t out_launch_dc(const Dims& d, const E* Sc, const E* Qt, const E* Oloc, E* o,
-                                hipStream_t s) {
-  if constexpr (sizeof(E) == 4 && D * C > 2048) return hipErrorInvalidValue;   // fp32 envelope
-  hipLaunchKernelGGL((out_fwd_kernel<E, D, C>), dim3(d.B * d.H * d.NC), dim3(OF_NT), 0, s, Sc, Qt,
-                     Oloc, o, d.B, d.T, d.H, d.NC, d.cu);
-  return hipGetLastError();
-}
-
-template <typename E, int D>
-static hipError_t out_launch_d(const Dims& d, const E* Sc, const E* Qt, const E* Oloc, E* o,
-                               hipStream_t s) {
-  switch (d.C) {
-    case 16: return out_launch_dc<E, D, 16>(d, Sc, Qt, Oloc, o, s);
-    case 32: return out_launch_dc<E, D, 32>(d, Sc, Qt, Oloc, o, s);
-    case 64: return out_launch_dc<E, D, 64>(d, Sc, Qt, Oloc, o, s);
-  }
-  return hipErrorInvalidValue;
-}
-
-template <typename E>
-hipError_t launch_out_fwd(const Dims& d, const E* Sc, const E* Qt, const E* Oloc, E* o,
-                          hipStream_t s) {
-  switch (d.D) {
-    case 16: return out_launch_d<E, 16>(d, Sc, Qt, Oloc, o, s);
-    case 32: return out_launch_d<E, 32>(d, Sc, Qt, Oloc, o, s);
-    case 64: return out_launch_d<E, 64>(d, Sc, Qt, Oloc, o, s);
-    case 128:
-      if constexpr (sizeof(E) == 2) return out_launch_d<E, 128>(d, Sc, Qt, Oloc, o, s);
+        return state_launch_d<E, 128>(d, init, Bm, AddT, gC, Xc, fin, transposed, reverse, Qt, Oloc,
+                                      o, s);
       break;
   }
   return hipErrorInvalidValue;
 }
 
 template hipError_t launch_state_pass<bf16>(const Dims&, const float*, const bf16*, const bf16*,
-                                            const float*, bf16*, float*, bool, bool, hipStream_t);
+                                            const float*, bf16*, float*, bool, bool, const bf16*,
+                                            const bf16*, bf16*, hipStream_t);
 template hipError_t launch_state_pass<float>(const Dims&, const float*, const float*, const float*,
-                                             const float*, float*, float*, bool, bool, hipStream_t);
-template hipError_t launch_out_fwd<bf16>(const Dims&, const bf16*, const bf16*, const bf16*,
-                                         bf16*, hipStream_t);
-template hipError_t launch_out_fwd<float>(const Dims&, const float*, const float*, const float*,
-                                          float*, hipStream_t);
-
+                                             const float*, float*, float*, bool, bool, const float*,
+                                             const float*, float*, hipStream_t);
 }  // namespace prism

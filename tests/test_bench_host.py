@@ -62,7 +62,7 @@ def _write_csv(path, header, rows):
 
 def test_summarize_profiles_scales_counters_by_the_copy(tmp_path, monkeypatch):
     d = str(tmp_path)
-    k = "_ZN5prism14out_fwd_kernelIDF16bLi128ELi64EEEv"
+    k = "_ZN5prism9et_kernelIDF16bLi128ELi64EEEvPKT_S3_PS1_iiiiPKi"
     # copy: FETCH reads half of 1 GiB (KiB), WRITE all of it
     _write_csv(os.path.join(d, "cfetch", "run_counter_collection.csv"),
                ["Kernel_Name", "Counter_Value"], [["copy", (1 << 30) / 1024 / 2]])
@@ -82,7 +82,7 @@ def test_summarize_profiles_scales_counters_by_the_copy(tmp_path, monkeypatch):
     rec = json.load(open(out / "profiles" / "hbm_traffic.json"))
     assert abs(rec["calibration"]["fetch_factor"] - 2.0) < 1e-9
     assert abs(rec["calibration"]["write_factor"] - 1.0) < 1e-9
-    t = rec["kernels"]["out_fwd"]
+    t = rec["kernels"]["et_chunks"]
     assert t["fetch_bytes"] == 2 * 1000 * 1024 and t["write_bytes"] == 500 * 1024
     md = open(out / "profiles" / "lm-T2048_kernels.md").read()
-    assert "| out_fwd | 4 | 100.0 |" in md
+    assert "| et_chunks | 4 | 100.0 |" in md
