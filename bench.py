@@ -139,7 +139,6 @@ def measured_traffic():
 # rocprofv3 kernel names -> the timer names used by the library and above
 _FAMILIES = [("refine_fwd_kernel", ["refine_fwd", "refine_fwd_recompute"]),
              ("et_kernel", ["et_chunks"]),
-             ("state_pass_kernel", ["state_fwd", "state_fwd_recompute", "state_bwd"]),
              ("chunk_bwd_state_kernel", ["chunk_bwd_state"]),
              ("chunk_bwd_solve_kernel", ["chunk_bwd_solve"]),
              ("chunk_bwd_pairs_kernel", ["chunk_bwd_pairs"]),
@@ -153,6 +152,20 @@ _FAMILIES = [("refine_fwd_kernel", ["refine_fwd", "refine_fwd_recompute"]),
 
 
 def _family(kernel_name):
+    if "state_pass_kernel" in kernel_name:
+        # template <E, D, RB, REV, C_RO>: reverse pass, forward with the fused
+        # readout (C_RO > 0), or the backward's forward recompute
+        m = re.search(r"ELb([01])ELi(\d+)E", kernel_name)
+        if m is None:
+            m = re.search(r"\b(true|false), (\d+)>", kernel_name)
+            rev = m is not None and m.group(1) == "true"
+        else:
+            rev = m.group(1) == "1"
+        if m is None:
+            return ["state_fwd", "state_fwd_recompute", "state_bwd"]
+        if rev:
+            return ["state_bwd"]
+        return ["state_fwd"] if int(m.group(2)) > 0 else ["state_fwd_recompute"]
     if "chunk_fwd_kernel" in kernel_name:
         # template flags <E, D, C, BWD, FUSE, ...>: mangled Lb0/Lb1, or demangled false/true
         flags = re.findall(r"Lb([01])E", kernel_name) or [

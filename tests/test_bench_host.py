@@ -40,6 +40,10 @@ def test_algorithmic_counts_cover_every_timed_kernel():
 
 def test_kernel_names_map_to_timer_names():
     assert bench._family("_ZN5prism17refine_bwd_kernelIDF16bLi128ELi4ELi0ELi0EEEv") == ["refine_bwd"]
+    assert bench._family("_ZN5prism17state_pass_kernelIDF16bLi128ELi64ELb0ELi64EEEvPKf") == ["state_fwd"]
+    assert bench._family("_ZN5prism17state_pass_kernelIDF16bLi128ELi64ELb0ELi0EEEvPKf") == ["state_fwd_recompute"]
+    assert bench._family("_ZN5prism17state_pass_kernelIDF16bLi128ELi16ELb1ELi0EEEvPKf") == ["state_bwd"]
+    assert bench._family("void prism::state_pass_kernel<__bf16, 128, 64, false, 64>(float const*)") == ["state_fwd"]
     cf = "_ZN5prism16chunk_fwd_kernelIDF16bLi128ELi64ELb{}ELb{}ELi0ELi1EEEvPKT_S3_"
     assert bench._family(cf.format(1, 0)) == ["chunk_fwd_bwdmode"]
     assert bench._family(cf.format(0, 0)) == ["chunk_fwd"]
