@@ -68,13 +68,16 @@ def algorithmic_counts(w):
     c["chunk_fwd_bwdmode"] = (th * (4 * D * e + 8) + ntp * 2 * L * D * e
                               + nch * (4 * D * D * e + 2 * C * D * e + 4),
                               nch * (2 * C * C * D * (2 * L + 5) + 2 * C * D * D * (L + 4)))
-    c["et_chunks"] = (nch * (2 * C * D * e + D * D * e), nch * 2 * C * D * D)
     # state pass: read M^T, H^T, write S_c (kept by the training forward), S0 /
     # S_T; the forward pass also forms the readout: read Qt, O_loc, write o
     st = (nch * D * D * 3 * e + bh * D * D * 4, nch * 2 * D ** 3)
     c["state_fwd"] = (st[0] + nch * C * D * 2 * e + th * D * e, st[1] + nch * 2 * C * D * D)
     c["state_fwd_recompute"] = st
-    c["state_bwd"] = (st[0] + bh * D * D * 4, st[1])
+    # reverse pass: read M, write dS_c^T, dS_T / dS_0; after a training forward
+    # it forms E_c = dO^T Qt itself (read dO, Qt), otherwise it reads E^T
+    c["state_bwd_stateless"] = (st[0] + bh * D * D * 4, st[1])
+    c["state_bwd"] = (nch * D * D * 2 * e + bh * D * D * 8 + nch * C * D * e + th * D * e,
+                      st[1] + nch * 2 * C * D * D)
     c["chunk_bwd_state"] = (th * (2 * D * e + 4) + nch * (2 * C * D * e + 2 * D * D * e + 4 * e * C * D + 4 * C)
                             + ntp * L * D * (3 * e + 4),  # read K_l, W_l; write dK_l, dW_l (fp32) partials
                             nch * (2 * C * D * D * (6 + 2 * L) + 2 * D ** 3))
@@ -138,7 +141,6 @@ def measured_traffic():
 
 # rocprofv3 kernel names -> the timer names used by the library and above
 _FAMILIES = [("refine_fwd_kernel", ["refine_fwd", "refine_fwd_recompute"]),
-             ("et_kernel", ["et_chunks"]),
              ("chunk_bwd_state_kernel", ["chunk_bwd_state"]),
              ("chunk_bwd_solve_kernel", ["chunk_bwd_solve"]),
              ("chunk_bwd_pairs_kernel", ["chunk_bwd_pairs"]),
@@ -164,7 +166,7 @@ def _family(kernel_name):
         if m is None:
             return ["state_fwd", "state_fwd_recompute", "state_bwd"]
         if rev:
-            return ["state_bwd"]
+            return ["state_bwd"] if int(m.group(2)) > 0 else ["state_bwd_stateless"]
         return ["state_fwd"] if int(m.group(2)) > 0 else ["state_fwd_recompute"]
     if "chunk_fwd_kernel" in kernel_name:
         # template flags <E, D, C, BWD, FUSE, ...>: mangled Lb0/Lb1, or demangled false/true

@@ -23,7 +23,7 @@
 //   (training forward) U^T, Wk^T [D][C] for the reverse chunk kernels.
 // In backward mode (dO given) the kernel instead stores Mt, HT, gC,
 // ET = (dO^T Qt)^T fp32 (for the reverse state pass) and U^T, Wk^T.
-// et_kernel forms ET from a saved Qt when the forward was kept.
+// After a training forward the reverse state pass forms E from the kept Qt.
 //
 // Fused form (FUSE): the refinement pairs K_l, W_l are formed inside the
 // kernel from the chunk's v rows (and the 3 or 4 rows before it that the

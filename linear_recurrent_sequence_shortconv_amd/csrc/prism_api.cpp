@@ -331,7 +331,7 @@ prism_status run_forward(const prism::Dims& d, const void* q, const void* k, con
   // when the training forward keeps them
   HIP_TRY("state_fwd", s,
           prism::launch_state_pass<E>(d, S0, w.Mt, w.HT, w.gC, keep ? w.Sc : nullptr, ST, false,
-                                      false, w.Qt, w.Oloc, static_cast<E*>(o), s));
+                                      false, w.Qt, w.Oloc, static_cast<E*>(o), nullptr, s));
   // after every read of hist, which hist_out may overwrite
   if (hist_out)
     HIP_TRY("conv_state", s, prism::launch_conv_state<E>(d, v_, hist_, static_cast<E*>(hist_out), s));
@@ -366,7 +366,6 @@ prism_status run_backward(const prism::Dims& d, const void* q, const void* k, co
     w.UT = kp.UT;
     w.WkT = kp.WkT;
     w.gC = kp.gC;
-    HIP_TRY("et_chunks", s, prism::launch_et<E>(d, kp.Qt, dO_, w.ET, s));
   } else {
     if (d.L > 0)
       HIP_TRY("refine_fwd_recompute", s,
@@ -378,11 +377,24 @@ prism_status run_backward(const prism::Dims& d, const void* q, const void* k, co
                                        nullptr, nullptr, w.gC, w.ET, w.UT, w.WkT, s));
     HIP_TRY("state_fwd_recompute", s,
             prism::launch_state_pass<E>(d, S0, w.Mt, w.HT, w.gC, w.Sc, nullptr, false, false,
-                                        nullptr, nullptr, nullptr, s));
+                                        nullptr, nullptr, nullptr, nullptr, s));
   }
-  HIP_TRY("state_bwd", s,
-          prism::launch_state_pass<E>(d, dST, w.Mt, w.ET, w.gC, w.dSnT, dS0, true, true, nullptr,
-                                      nullptr, nullptr, s));
+  // reverse state pass; after a training forward it forms E_c = dO^T Qt from
+  // the kept Qt itself, otherwise it adds the E^T of the backward-mode chunk kernel
+  const E* Qk = nullptr;
+  if (kept) {
+    Carve ck;
+    ck.base = static_cast<char*>(const_cast<void*>(kept));
+    Qk = carve_kept<E>(d, ck).Qt;
+  }
+  if (kept)
+    HIP_TRY("state_bwd", s,
+            prism::launch_state_pass<E>(d, dST, w.Mt, nullptr, w.gC, w.dSnT, dS0, true, true, Qk,
+                                        nullptr, nullptr, dO_, s));
+  else
+    HIP_TRY("state_bwd_stateless", s,
+            prism::launch_state_pass<E>(d, dST, w.Mt, w.ET, w.gC, w.dSnT, dS0, true, true, nullptr,
+                                        nullptr, nullptr, nullptr, s));
   prism::ChunkBwdArgs<E> a;
   a.q = q_; a.k = k_; a.v = v_; a.dO = dO_; a.alpha = alpha; a.beta = beta;
   a.Kl = w.Kl; a.Wl = w.Wl; a.UT = w.UT; a.WkT = w.WkT; a.Sc = w.Sc; a.dSnT = w.dSnT;

@@ -63,9 +63,6 @@ hipError_t launch_chunk_fwd_fused(const Dims& d, const E* q, const E* k, const E
                                   E* Mt, E* HT, E* Qt, E* Oloc, float* gC,
                                   hipStream_t s);
 
-// ET per chunk from a kept Qt and dO (the backward of a training forward).
-template <typename E>
-hipError_t launch_et(const Dims& d, const E* Qt, const E* dO, E* ET, hipStream_t s);
 
 // Sequential pass over chunks, forward (X <- exp(gC) X - X M + H, from S0) or
 // reverse (X <- exp(gC) X - X M^T + E, from dS_T).  Both read Mt = M^T; AddT
@@ -74,7 +71,7 @@ hipError_t launch_et(const Dims& d, const E* Qt, const E* dO, E* ET, hipStream_t
 template <typename E>
 hipError_t launch_state_pass(const Dims& d, const float* init, const E* Mt, const E* AddT,
                              const float* gC, E* Xc, float* fin, bool transposed, bool reverse,
-                             const E* Qt, const E* Oloc, E* o, hipStream_t s);
+                             const E* Qt, const E* Oloc, E* o, const E* dO, hipStream_t s);
 
 // Arguments of the three chunk-parallel backward kernels (see chunk_bwd.hip).
 template <typename E>

@@ -37,11 +37,15 @@ namespace prism {
 // two steps ahead with the other operands, and S_c goes to HBM only when a
 // caller keeps it (Xc non-null).  The readout reads no S_c from HBM and needs
 // no launch of its own.
+// With FE (reverse only) each step forms its row block of the additive term
+// E_c = dO_c^T Qt_c itself, from the dO rows of the block and the Qt rows a
+// training forward kept (fetched two steps ahead, staged in LDS), and adds it
+// to the adjoint state in fp32: no E_c round trip through HBM.
 constexpr int SP_NW = 8;
 constexpr int SP_NT = SP_NW * WAVE;
 constexpr long SP_WIDE = 256;   // workgroups that fill the chip (one per CU)
 
-template <typename E, int D, int RB, bool REV, int C_RO>
+template <typename E, int D, int RB, bool REV, int C_X>
 __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restrict__ init,
                                                            const E* __restrict__ Bm,
                                                            const E* __restrict__ AddT,
@@ -52,11 +56,13 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
                                                            const int* __restrict__ cu,
                                                            const E* __restrict__ Qt,
                                                            const E* __restrict__ Oloc,
-                                                           E* __restrict__ o) {
-  // C_RO > 0: fused readout for chunks of C_RO tokens (forward only)
-  constexpr bool RO = C_RO > 0;
-  constexpr int CR = RO ? C_RO : 16;
-  static_assert(!(RO && REV), "the readout belongs to the forward pass");
+                                                           E* __restrict__ o,
+                                                           const E* __restrict__ dOg) {
+  // C_X > 0: chunks of C_X tokens, with the readout fused (forward, RO) or the
+  // additive term E_c formed in the pass (reverse, FE)
+  constexpr bool RO = !REV && C_X > 0;
+  constexpr bool FE = REV && C_X > 0;
+  constexpr int CR = C_X > 0 ? C_X : 16;
   constexpr int LS = ldpad<E>(D);
   constexpr int VN = 16 / sizeof(E);
   constexpr int NV = D * D / VN;                       // 16-byte vectors of Bm_c
@@ -66,10 +72,14 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
   typedef Tiling<RB, D, SP_NW> TL;
   __shared__ __attribute__((aligned(16))) E Mb[2][D * LS];
   __shared__ __attribute__((aligned(16))) E Ss[2][RB * LS];
-  __shared__ __attribute__((aligned(16))) E Qb[RO ? 2 : 1][RO ? CR * LS : 8];   // Qt rows of a step
+  __shared__ __attribute__((aligned(16))) E Qb[C_X > 0 ? 2 : 1][C_X > 0 ? CR * LS : 8];   // Qt rows of a step
+  constexpr int LO = ldpad<E>(RB);
+  __shared__ __attribute__((aligned(16))) E Ob[FE ? 2 : 1][FE ? CR * LO : 8];   // dO rows of the block
   constexpr int NVQ = CR * D / VN;                     // 16-byte vectors of Qt_c
   constexpr int PERQ = (NVQ + SP_NT - 1) / SP_NT;
   typedef Tiling<RB, CR, SP_NW> TLO;                   // readout tiles [f][t]
+  constexpr int NVO = CR * RB / VN;                    // 16-byte vectors of the dO block
+  constexpr int PERO = (NVO + SP_NT - 1) / SP_NT;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nblk = B * H * NRB;
   const int bid = xcd_swizzle(blockIdx.x, nblk);
@@ -98,7 +108,9 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
   // register sets, indexed by the step's parity at compile time): a step
   // then stages into LDS only data that has had a whole step to arrive.
   uint4 mst[2][PER];                    // Bm of a coming step, staged through registers
-  uint4 qst[2][RO ? PERQ : 1];          // Qt rows of a coming step (readout)
+  uint4 qst[2][C_X > 0 ? PERQ : 1];     // Qt rows of a coming step (readout, E_c)
+  uint4 dost[2][FE ? PERO : 1];         // dO block of a coming step (E_c)
+  int nvn[2] = {0, 0};                  // its valid rows (E_c)
   typename Raw4Of<E>::type oln[2][RO ? TLO::RM : 1][RO ? TLO::RN : 1];   // its O_loc block (raw)
   typename Raw4Of<E>::type addn[2][TL::RM][TL::RN];   // AddT^T block of a coming step (raw)
   float egn[2] = {0.f, 0.f};            // decay of a coming step
@@ -111,7 +123,7 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
       const int e = tid + p * SP_NT;
       if (e < NV) mst[Z][p] = ld16(bm + (long)e * VN);
     }
-    if (act) {
+    if (act && !FE) {
       const E* ac = AddT + cidx * D * D + rb0;
 #pragma unroll
       for (int i = 0; i < TL::RM; ++i)
@@ -120,13 +132,32 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
           addn[Z][i][j] = ld_raw4(ac + (long)(n0 + 16 * j + cl) * D + m0 + 16 * i + rl);
     }
     egn[Z] = expf(gC[cidx]);
-    if constexpr (RO) {
+    if constexpr (C_X > 0) {
       const E* qc = Qt + cidx * CR * D;
 #pragma unroll
       for (int p = 0; p < PERQ; ++p) {
         const int e = tid + p * SP_NT;
         if (e < NVQ) qst[Z][p] = ld16(qc + (long)e * VN);
       }
+    }
+    if constexpr (FE) {
+      // rows past the sequence end read the last valid row and are zeroed
+      // when staged (no load depends on a branch)
+      const int b = bh / H, h = bh % H;
+      const int c0 = chunk_of(step) * CR;
+      const int nval = min(CR, seq_len(cu, b, T) - c0);
+      nvn[Z] = nval;
+      const E* dc = dOg + ((seq_start(cu, b, T) + c0) * H + h) * D + rb0;
+#pragma unroll
+      for (int p = 0; p < PERO; ++p) {
+        const int e = tid + p * SP_NT;
+        if (e < NVO) {
+          const int t = min(e / (RB / VN), nval - 1), c = (e % (RB / VN)) * VN;
+          dost[Z][p] = ld16(dc + (long)t * H * D + c);
+        }
+      }
+    }
+    if constexpr (RO) {
       if (TLO::active(wave)) {
         const E* oc = Oloc + cidx * CR * D + rb0;
 #pragma unroll
@@ -149,13 +180,26 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
         st16(dst + r * LS + c, mst[Z][p]);
       }
     }
-    if constexpr (RO) {
+    if constexpr (C_X > 0) {
 #pragma unroll
       for (int p = 0; p < PERQ; ++p) {
         const int e = tid + p * SP_NT;
         if (e < NVQ) {
           const int r = e / (D / VN), c = (e % (D / VN)) * VN;
           st16(Qb[Z] + r * LS + c, qst[Z][p]);
+        }
+      }
+    }
+    if constexpr (FE) {
+#pragma unroll
+      for (int p = 0; p < PERO; ++p) {
+        const int e = tid + p * SP_NT;
+        if (e < NVO) {
+          const int r = e / (RB / VN), c = (e % (RB / VN)) * VN;
+          uint4 w = dost[Z][p];
+          asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
+          if (r >= nvn[Z]) w = uint4{0u, 0u, 0u, 0u};
+          st16(Ob[Z] + r * LO + c, w);
         }
       }
     }
@@ -167,10 +211,12 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
     constexpr int Z = decltype(setc)::value;
     const long cidx = (long)bh * NC + chunk_of(step);
     f32x4 addc[TL::RM][TL::RN];
+    if constexpr (!FE) {
 #pragma unroll
-    for (int i = 0; i < TL::RM; ++i)
+      for (int i = 0; i < TL::RM; ++i)
 #pragma unroll
-      for (int j = 0; j < TL::RN; ++j) addc[i][j] = raw4_to_f(addn[Z][i][j]);
+        for (int j = 0; j < TL::RN; ++j) addc[i][j] = raw4_to_f(addn[Z][i][j]);
+    }
     const float egc = egn[Z];
     // this step's O_loc block: set Z is refilled with step + 2's below
     typename Raw4Of<E>::type olc[RO ? TLO::RM : 1][RO ? TLO::RN : 1];
@@ -216,6 +262,19 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
     Acc<RB, D, SP_NW> P;
     P.zero();
     gemm_acc<E, RB, D, D, SP_NW, true, !REV>(P, Ss[Z], LS, Mb[Z], LS, wave, lane);
+    if constexpr (FE) {
+      // E_c rows of the block: [r][n] = sum_t dO[t][rb0 + r] Qt[t][n] (both
+      // operands k-strided in LDS), added in fp32
+      Acc<RB, D, SP_NW> Ea;
+      Ea.zero();
+      gemm_acc<E, RB, D, CR, SP_NW, false, false>(Ea, Ob[Z], LO, Qb[Z], LS, wave, lane);
+      if (act) {
+#pragma unroll
+        for (int i = 0; i < TL::RM; ++i)
+#pragma unroll
+          for (int j = 0; j < TL::RN; ++j) addc[i][j] = Ea.v[i][j];
+      }
+    }
     if (act) {
 #pragma unroll
       for (int i = 0; i < TL::RM; ++i)
@@ -264,7 +323,7 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
 template <typename E, int D>
 static hipError_t state_launch_d(const Dims& d, const float* init, const E* Bm, const E* AddT,
                                  const float* gC, E* Xc, float* fin, bool tr, bool rev,
-                                 const E* Qt, const E* Oloc, E* o, hipStream_t s) {
+                                 const E* Qt, const E* Oloc, E* o, const E* dO, hipStream_t s) {
   // Row blocks: the whole state below D = 128; at D = 128 blocks of 64 rows
   // (two workgroups per sequence), or of 32 or 16 rows when there are too few
   // sequence-heads to give every CU a workgroup (long sequences, small
@@ -273,23 +332,29 @@ static hipError_t state_launch_d(const Dims& d, const float* init, const E* Bm, 
   auto go = [&](auto rbc) {
     constexpr int RB = decltype(rbc)::value;
     const dim3 grid(d.B * d.H * (D / RB));
-    if (rev) {
+    if (rev && !dO) {
       hipLaunchKernelGGL((state_pass_kernel<E, D, RB, true, 0>), grid, dim3(SP_NT), 0, s, init, Bm,
                          AddT, gC, Xc, fin, d.B, d.H, d.NC, tr ? 1 : 0, 1, d.T, d.C, d.cu, nullptr,
-                         nullptr, nullptr);
-    } else if (!o) {
+                         nullptr, nullptr, nullptr);
+    } else if (!rev && !o) {
       hipLaunchKernelGGL((state_pass_kernel<E, D, RB, false, 0>), grid, dim3(SP_NT), 0, s, init, Bm,
                          AddT, gC, Xc, fin, d.B, d.H, d.NC, tr ? 1 : 0, 0, d.T, d.C, d.cu, nullptr,
-                         nullptr, nullptr);
+                         nullptr, nullptr, nullptr);
     } else {
+      // forward with the readout, or reverse with E_c formed in the pass
       auto ro = [&](auto cc) -> hipError_t {
         constexpr int CC = decltype(cc)::value;
         if constexpr (sizeof(E) == 4 && D * CC > 2048) {
           return hipErrorInvalidValue;   // outside the fp32 envelope
         } else {
-          hipLaunchKernelGGL((state_pass_kernel<E, D, RB, false, CC>), grid, dim3(SP_NT), 0, s, init,
-                             Bm, AddT, gC, Xc, fin, d.B, d.H, d.NC, tr ? 1 : 0, 0, d.T, d.C, d.cu,
-                             Qt, Oloc, o);
+          if (rev)
+            hipLaunchKernelGGL((state_pass_kernel<E, D, RB, true, CC>), grid, dim3(SP_NT), 0, s,
+                               init, Bm, AddT, gC, Xc, fin, d.B, d.H, d.NC, tr ? 1 : 0, 1, d.T, d.C,
+                               d.cu, Qt, nullptr, nullptr, dO);
+          else
+            hipLaunchKernelGGL((state_pass_kernel<E, D, RB, false, CC>), grid, dim3(SP_NT), 0, s,
+                               init, Bm, AddT, gC, Xc, fin, d.B, d.H, d.NC, tr ? 1 : 0, 0, d.T, d.C,
+                               d.cu, Qt, Oloc, o, nullptr);
           return hipSuccess;
         }
       };
@@ -316,16 +381,16 @@ static hipError_t state_launch_d(const Dims& d, const float* init, const E* Bm, 
 template <typename E>
 hipError_t launch_state_pass(const Dims& d, const float* init, const E* Bm, const E* AddT,
                              const float* gC, E* Xc, float* fin, bool transposed, bool reverse,
-                             const E* Qt, const E* Oloc, E* o,
+                             const E* Qt, const E* Oloc, E* o, const E* dO,
                              hipStream_t s) {
   switch (d.D) {
-    case 16: return state_launch_d<E, 16>(d, init, Bm, AddT, gC, Xc, fin, transposed, reverse, Qt, Oloc, o, s);
-    case 32: return state_launch_d<E, 32>(d, init, Bm, AddT, gC, Xc, fin, transposed, reverse, Qt, Oloc, o, s);
-    case 64: return state_launch_d<E, 64>(d, init, Bm, AddT, gC, Xc, fin, transposed, reverse, Qt, Oloc, o, s);
+    case 16: return state_launch_d<E, 16>(d, init, Bm, AddT, gC, Xc, fin, transposed, reverse, Qt, Oloc, o, dO, s);
+    case 32: return state_launch_d<E, 32>(d, init, Bm, AddT, gC, Xc, fin, transposed, reverse, Qt, Oloc, o, dO, s);
+    case 64: return state_launch_d<E, 64>(d, init, Bm, AddT, gC, Xc, fin, transposed, reverse, Qt, Oloc, o, dO, s);
     case 128:
       if constexpr (sizeof(E) == 2)
         return state_launch_d<E, 128>(d, init, Bm, AddT, gC, Xc, fin, transposed, reverse, Qt, Oloc,
-                                      o, s);
+                                      o, dO, s);
       break;
   }
   return hipErrorInvalidValue;
@@ -333,8 +398,8 @@ hipError_t launch_state_pass(const Dims& d, const float* init, const E* Bm, cons
 
 template hipError_t launch_state_pass<bf16>(const Dims&, const float*, const bf16*, const bf16*,
                                             const float*, bf16*, float*, bool, bool, const bf16*,
-                                            const bf16*, bf16*, hipStream_t);
+                                            const bf16*, bf16*, const bf16*, hipStream_t);
 template hipError_t launch_state_pass<float>(const Dims&, const float*, const float*, const float*,
                                              const float*, float*, float*, bool, bool, const float*,
-                                             const float*, float*, hipStream_t);
+                                             const float*, float*, const float*, hipStream_t);
 }  // namespace prism

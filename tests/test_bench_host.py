@@ -42,7 +42,8 @@ def test_kernel_names_map_to_timer_names():
     assert bench._family("_ZN5prism17refine_bwd_kernelIDF16bLi128ELi4ELi0ELi0EEEv") == ["refine_bwd"]
     assert bench._family("_ZN5prism17state_pass_kernelIDF16bLi128ELi64ELb0ELi64EEEvPKf") == ["state_fwd"]
     assert bench._family("_ZN5prism17state_pass_kernelIDF16bLi128ELi64ELb0ELi0EEEvPKf") == ["state_fwd_recompute"]
-    assert bench._family("_ZN5prism17state_pass_kernelIDF16bLi128ELi16ELb1ELi0EEEvPKf") == ["state_bwd"]
+    assert bench._family("_ZN5prism17state_pass_kernelIDF16bLi128ELi16ELb1ELi0EEEvPKf") == ["state_bwd_stateless"]
+    assert bench._family("_ZN5prism17state_pass_kernelIDF16bLi128ELi64ELb1ELi64EEEvPKf") == ["state_bwd"]
     assert bench._family("void prism::state_pass_kernel<__bf16, 128, 64, false, 64>(float const*)") == ["state_fwd"]
     cf = "_ZN5prism16chunk_fwd_kernelIDF16bLi128ELi64ELb{}ELb{}ELi0ELi1EEEvPKT_S3_"
     assert bench._family(cf.format(1, 0)) == ["chunk_fwd_bwdmode"]
@@ -66,7 +67,7 @@ def _write_csv(path, header, rows):
 
 def test_summarize_profiles_scales_counters_by_the_copy(tmp_path, monkeypatch):
     d = str(tmp_path)
-    k = "_ZN5prism9et_kernelIDF16bLi128ELi64EEEvPKT_S3_PS1_iiiiPKi"
+    k = "_ZN5prism19wgrad_reduce_kernelEPKfPfS2_iiii"
     # copy: FETCH reads half of 1 GiB (KiB), WRITE all of it
     _write_csv(os.path.join(d, "cfetch", "run_counter_collection.csv"),
                ["Kernel_Name", "Counter_Value"], [["copy", (1 << 30) / 1024 / 2]])
@@ -86,7 +87,7 @@ def test_summarize_profiles_scales_counters_by_the_copy(tmp_path, monkeypatch):
     rec = json.load(open(out / "profiles" / "hbm_traffic.json"))
     assert abs(rec["calibration"]["fetch_factor"] - 2.0) < 1e-9
     assert abs(rec["calibration"]["write_factor"] - 1.0) < 1e-9
-    t = rec["kernels"]["et_chunks"]
+    t = rec["kernels"]["wgrad_reduce"]
     assert t["fetch_bytes"] == 2 * 1000 * 1024 and t["write_bytes"] == 500 * 1024
     md = open(out / "profiles" / "lm-T2048_kernels.md").read()
-    assert "| et_chunks | 4 | 100.0 |" in md
+    assert "| wgrad_reduce | 4 | 100.0 |" in md
