@@ -405,7 +405,9 @@ __device__ inline void g2s_rows_transposed(T* s, int ld, const T* g, long gstrid
 // A ROWS x COLS tile of T held in registers as 16-byte vectors spread over
 // NT threads: load() issues the global reads early (software prefetch);
 // store_rows / store_transposed later write it into LDS.  Rows >= nvalid are
-// zeros.
+// zeros: load() reads the last valid row in their place (no load sits in a
+// per-lane branch, whose merge would make the prefetch wait for its data at
+// issue) and the stores write zeros for them.
 // TR = false: consecutive threads take consecutive vectors of a row (fully
 //   coalesced reads; for row stores).
 // TR = true: consecutive threads take consecutive row groups of one 16-byte
@@ -422,6 +424,7 @@ struct RegTile {
   static constexpr int PER = (NU + NT - 1) / NT;
   static_assert(ROWS % RG == 0, "row pairs");
   uint4 v[PER][RG];
+  int nv = ROWS;   // rows >= nv are zeros
   __device__ static inline void unit(int u, int& r0, int& c) {
     if constexpr (TR) {
       r0 = (u % NG) * RG;
@@ -432,17 +435,26 @@ struct RegTile {
     }
   }
   __device__ inline void load(const T* g, long gstride, int nvalid, int tid) {
+    nv = nvalid;
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const int u = tid + p * NT;
+      // threads past the last unit read it again (the stores skip them)
+      const int u = min(tid + p * NT, NU - 1);
       int r0, c;
       unit(u, r0, c);
 #pragma unroll
       for (int q = 0; q < RG; ++q) {
         v[p][q] = uint4{0u, 0u, 0u, 0u};
-        if (u < NU && r0 + q < nvalid) v[p][q] = ld16(g + (r0 + q) * gstride + c);
+        if (nvalid > 0) v[p][q] = ld16(g + min(r0 + q, nvalid - 1) * gstride + c);
       }
     }
+  }
+  // vector (p, q) of row r: zeros past the valid rows.  The empty asm keeps
+  // this select here, not next to the load.
+  __device__ inline uint4 get(int p, int q, int r) const {
+    uint4 w = v[p][q];
+    asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
+    return r < nv ? w : uint4{0u, 0u, 0u, 0u};
   }
   __device__ inline void store_rows(T* s, int ld, int tid) const {
 #pragma unroll
@@ -452,7 +464,7 @@ struct RegTile {
       unit(u, r0, c);
       if (u < NU) {
 #pragma unroll
-        for (int q = 0; q < RG; ++q) st16(s + (r0 + q) * ld + c, v[p][q]);
+        for (int q = 0; q < RG; ++q) st16(s + (r0 + q) * ld + c, get(p, q, r0 + q));
       }
     }
   }
@@ -468,8 +480,7 @@ struct RegTile {
       if (u < NU) {
 #pragma unroll
         for (int q = 0; q < RG; ++q) {
-          uint4 w = v[p][q];
-          asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
+          const uint4 w = get(p, q, r0 + q);
           const T* x = reinterpret_cast<const T*>(&w);
 #pragma unroll
           for (int j = 0; j < VN; j += 4)
@@ -488,8 +499,9 @@ struct RegTile {
       unit(u, r0, c);
       if (u < NU) {
         if constexpr (RG == 2) {
-          const T* x0 = reinterpret_cast<const T*>(&v[p][0]);
-          const T* x1 = reinterpret_cast<const T*>(&v[p][1]);
+          const uint4 w0 = get(p, 0, r0), w1 = get(p, 1, r0 + 1);
+          const T* x0 = reinterpret_cast<const T*>(&w0);
+          const T* x1 = reinterpret_cast<const T*>(&w1);
           const float s0 = scale ? scale[r0] : 1.0f, s1 = scale ? scale[r0 + 1] : 1.0f;
 #pragma unroll
           for (int j = 0; j < VN; ++j) {
@@ -501,7 +513,8 @@ struct RegTile {
         } else {
 #pragma unroll
           for (int q = 0; q < RG; ++q) {
-            const T* x = reinterpret_cast<const T*>(&v[p][q]);
+            const uint4 w = get(p, q, r0 + q);
+            const T* x = reinterpret_cast<const T*>(&w);
             const float sc = scale ? scale[r0 + q] : 1.0f;
 #pragma unroll
             for (int j = 0; j < VN; ++j) s[(c + j) * ld + r0 + q] = to_t<T>(to_f(x[j]) * sc);

@@ -37,30 +37,6 @@ constexpr int RB_NW = 4;                // one wave per feature group
 constexpr int RB_NT = RB_NW * WAVE;
 constexpr int rb_own(int off) { return RB_TT - 3 - off; }
 
-// MFMA A-operand fragment of bf16 (or fp32) values read from an fp32 LDS
-// row tile X[row][k] (k contiguous), rounded to the operand type.
-template <typename E, int K>
-__device__ inline typename MfmaK<E, K>::frag frag_from_f32(const float* X, int ld, int row0, int k0, int lane) {
-  if constexpr (sizeof(E) == 4) {
-    return load_frag<float, true>(X, ld, row0, k0, lane);
-  } else {
-    constexpr int KPL = MfmaK<E, K>::KPL;
-    const float* p = X + (row0 + (lane & 15)) * ld + k0 + KPL * (lane >> 4);
-    typename MfmaK<E, K>::frag f;
-#pragma unroll
-    for (int h = 0; h < KPL / 4; ++h) {
-      const f32x4 x = *reinterpret_cast<const f32x4*>(p + 4 * h);
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const bf16 y = (bf16)x[j];
-        if constexpr (KPL == 4) f[4 * h + j] = __builtin_bit_cast(short, y);
-        else f[4 * h + j] = y;
-      }
-    }
-    return f;
-  }
-}
-
 template <typename E, int D, int LMAX, int ACT, int OFF>
 __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
     const E* __restrict__ v, const E* __restrict__ hist, const E* __restrict__ conv,
@@ -86,7 +62,8 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
   __shared__ __attribute__((aligned(16))) E ubuf[RB_TT * LD];
   __shared__ __attribute__((aligned(16))) E ulo[sizeof(E) == 2 ? RB_TT * LD : 16];   // u - bf16(u)
   __shared__ __attribute__((aligned(16))) E dpbuf[RB_TT * LD];        // dp rows; at the end dv rows
-  __shared__ __attribute__((aligned(16))) float gk[2 * RB_TT * LW];   // dW_l, dK_l rows; at the end du
+  __shared__ __attribute__((aligned(16))) float gk[RB_TT * LW];       // dW_l rows (fp32); at the end du
+  __shared__ __attribute__((aligned(16))) E gkk[RB_TT * LD];          // dK_l rows (the product's operand type)
   __shared__ float gate[LMAX][RB_TT];
   __shared__ float gsum[4][RB_TT];
   __shared__ float dlog[RB_TT];
@@ -94,7 +71,6 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
   __shared__ float ctp[D * 4];                                        // conv taps of this head
   __shared__ float red[RB_NT * 4];                                    // dconv partials per thread
   float* gw = gk;
-  float* gkk = gk + RB_TT * LW;
 
   const int tid = threadIdx.x, lane = tid & 63, fq = tid >> 6;   // wave = feature group
   const int nblk = ntiles * B * H;
@@ -194,7 +170,7 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
     }
   }
   pw.store_rows_f32(gw, LW, tid);
-  pk.store_rows_f32(gkk, LW, tid);
+  pk.store_rows(gkk, LD, tid);
   __syncthreads();
 
   // Weight fragments (B operands) of this wave's feature tiles.  Every
@@ -238,19 +214,14 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
       }
     }
   };
-  // acc += X W  where X holds rows [t][i] (operand type in LDS, or fp32 in
-  // LDS when XF) and bws holds the fragments of WT[j][i] = W[i][j]
-  auto project_t = [&](auto xf, const void* X, int ldx, const Frag (&bws)[FPW][D / KS],
-                       f32x4 (&acc)[2][FPW]) {
-    constexpr bool XF = decltype(xf)::value;
+  // acc += X W  where X holds rows [t][i] in LDS (operand type) and bws holds
+  // the fragments of WT[j][i] = W[i][j]
+  auto project_t = [&](const E* X, int ldx, const Frag (&bws)[FPW][D / KS], f32x4 (&acc)[2][FPW]) {
 #pragma unroll
     for (int k0 = 0; k0 < D; k0 += KS) {
       typename MK::frag a[2];
 #pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        if constexpr (XF) a[m] = frag_from_f32<E, D>(static_cast<const float*>(X), ldx, 16 * m, k0, lane);
-        else a[m] = load_fragK<E, D>(static_cast<const E*>(X), ldx, 16 * m, k0, lane);
-      }
+      for (int m = 0; m < 2; ++m) a[m] = load_fragK<E, D>(X, ldx, 16 * m, k0, lane);
 #pragma unroll
       for (int nn = 0; nn < FPW; ++nn) {
         const int n = fq + 4 * nn;
@@ -449,9 +420,9 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
     }
     const long lrow = (bh * L + l) * Tp + t0;
     s2g_rows<E, RB_TT, D, RB_NT>(dPo + lrow * D, D, dpbuf, LD, own, tid);
-    project_t(std::false_type{}, dpbuf, LD, bpt, du);
+    project_t(dpbuf, LD, bpt, du);
     if constexpr (!EARLY_W) load_w(WkT + ((long)h * L + l) * D * D, bkt);
-    project_t(std::true_type{}, gkk, LW, bkt, du);
+    project_t(gkk, LD, bkt, du);
     // du += dlogit w_beta; dw_beta partial = sum over owned t of dlogit_t u_t
     const E* wb = wbl + l * D;
 #pragma unroll
@@ -476,7 +447,7 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
     __syncthreads();   // every read of gw, gkk, dpbuf and dlog is done
     if (l > 0) {
       pw.store_rows_f32(gw, LW, tid);
-      pk.store_rows_f32(gkk, LW, tid);
+      pk.store_rows(gkk, LD, tid);
       __syncthreads();
     }
   }
