@@ -253,14 +253,15 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
     Acc<C, D, NW> u;    // K dS_n^T: [t][r] = sum_n K[t][n] dS_n[r][n]
     u.zero();
     gemm_acc<E, C, D, D, NW, true, true>(u, R1, LR, X1, LD2, wave, lane);
-    E* out = dUs + cidx * C * D;
+    E* out = dUs + cidx * C * D;   // stored transposed, [r][t]
     for_tiles_ij(u, wave, lane, [&](int i, int j, int t0, int rr, const f32x4& x) {
-      f32x4 pu;
+      f32x4 pu, y;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        out[(long)(t0 + r) * D + rr] = to_t<E>(Dv[t0 + r] * x[r]);
+        y[r] = Dv[t0 + r] * x[r];
         pu[r] = x[r] * to_f(R2[(t0 + r) * LR + rr]);
       }
+      st_f4(out + (long)rr * C + t0, y);
       dds.add(i, j, pu, true, false);
     });
   }
@@ -313,20 +314,21 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
     Acc<C, D, NW> a;    // K dM^T: [t][k] = sum_n K[t][n] dM[k][n]
     a.zero();
     gemm_acc<E, C, D, D, NW, true, true>(a, R1, LR, X1, LD2, wave, lane);
-    E* out = dWks + cidx * C * D;
+    E* out = dWks + cidx * C * D;   // stored transposed, [k][t]
     for_tiles_ij(a, wave, lane, [&](int i, int j, int t0, int kk, const f32x4& x) {
-      f32x4 pw;
+      f32x4 pw, y;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        out[(long)(t0 + r) * D + kk] = to_t<E>(Dv[t0 + r] * x[r]);
+        y[r] = Dv[t0 + r] * x[r];
         pw[r] = x[r] * to_f(R3[(t0 + r) * LR + kk]);
       }
+      st_f4(out + (long)kk * C + t0, y);
       dds.add(i, j, pw, true, false);
     });
     Acc<C, D, NW> bb;   // Wk dM: [t][n] = sum_k Wk[t][k] dM^T[n][k]
     bb.zero();
     gemm_acc<E, C, D, D, NW, true, true>(bb, R3, LR, X2, LD2, wave, lane);
-    E* ok = dKs + cidx * C * D;
+    E* ok = dKs + cidx * C * D;   // stored transposed, [n][t]
     typedef Tiling<C, D, NW> TL;
     if (TL::active(wave)) {
 #pragma unroll
@@ -335,9 +337,10 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
         for (int j = 0; j < TL::RN; ++j) {
           const int t0 = TL::m0(wave) + 16 * i + 4 * (lane >> 4);
           const int n = TL::n0(wave) + 16 * j + (lane & 15);
+          f32x4 y;
 #pragma unroll
-          for (int r = 0; r < 4; ++r)
-            ok[(long)(t0 + r) * D + n] = to_t<E>(dk.v[i][j][r] + Dv[t0 + r] * bb.v[i][j][r]);
+          for (int r = 0; r < 4; ++r) y[r] = dk.v[i][j][r] + Dv[t0 + r] * bb.v[i][j][r];
+          st_f4(ok + (long)n * C + t0, y);
         }
     }
   }
@@ -606,7 +609,11 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
   const E* dUc = dUs + cidx * C * D;
   const E* dWc = dWks + cidx * C * D;
   const E* dKc = dKs + cidx * C * D;
-  f32x4 pU[TLD::RM][TLD::RN], pW[TLD::RM][TLD::RN], pK[TLD::RM][TLD::RN], pQ[TLD::RM][TLD::RN];
+  // (dU_s, dWk_s, dK_s stored transposed: a lane's four tokens are contiguous,
+  // kept as raw bits until used)
+  typedef typename Raw4Of<E>::type R4;
+  R4 pU[TLD::RM][TLD::RN], pW[TLD::RM][TLD::RN], pK[TLD::RM][TLD::RN];
+  f32x4 pQ[TLD::RM][TLD::RN];
   if (actD) {
 #pragma unroll
     for (int i = 0; i < TLD::RM; ++i)
@@ -614,14 +621,12 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
       for (int j = 0; j < TLD::RN; ++j) {
         const int t0 = TLD::m0(wave) + 16 * i + 4 * (lane >> 4);
         const int f = TLD::n0(wave) + 16 * j + (lane & 15);
+        const long ot = (long)f * C + t0;
+        pU[i][j] = ld_raw4(dUc + ot);
+        pW[i][j] = ld_raw4(dWc + ot);
+        pK[i][j] = ld_raw4(dKc + ot);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const long o = (long)(t0 + r) * D + f;
-          pU[i][j][r] = to_f(dUc[o]);
-          pW[i][j][r] = to_f(dWc[o]);
-          pK[i][j][r] = to_f(dKc[o]);
-          pQ[i][j][r] = to_f(dQtc[o]);
-        }
+        for (int r = 0; r < 4; ++r) pQ[i][j][r] = to_f(dQtc[(long)(t0 + r) * D + f]);
       }
   }
 
@@ -682,13 +687,14 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
       for (int j = 0; j < TLD::RN; ++j) {
         const int t0 = TLD::m0(wave) + 16 * i + 4 * (lane >> 4);
         const int f = TLD::n0(wave) + 16 * j + (lane & 15);
+        const f32x4 u4 = raw4_to_f(pU[i][j]), w4 = raw4_to_f(pW[i][j]), k4 = raw4_to_f(pK[i][j]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           const int t = t0 + r;
-          Ur[t * LR + f] = to_t<E>(du.v[i][j][r] + pU[i][j][r]);
-          Wkr[t * LR + f] = to_t<E>(dw.v[i][j][r] + pW[i][j][r]);
+          Ur[t * LR + f] = to_t<E>(du.v[i][j][r] + u4[r]);
+          Wkr[t * LR + f] = to_t<E>(dw.v[i][j][r] + w4[r]);
           dq.v[i][j][r] += ev[t] * pQ[i][j][r];
-          dk.v[i][j][r] += pK[i][j][r];
+          dk.v[i][j][r] += k4[r];
         }
       }
   }
