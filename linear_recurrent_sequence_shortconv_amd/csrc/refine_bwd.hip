@@ -44,23 +44,33 @@ struct RowChunk {
   static constexpr int NG = WG_ROWS / RG;
   static constexpr int NU = NG * VPR;
   static constexpr int PER = (NU + WG_NT - 1) / WG_NT;
+  static_assert(PER * RG <= 32, "validity bits");
   uint4 v[PER][RG];
+  unsigned ok = 0;   // bit p * RG + q: the row of v[p][q] exists (else it reads as zeros)
+  // Rows past the split or the sequence end read a row inside the tensor in
+  // their place and are zeroed by store_t: no load sits in a per-lane branch
+  // (its merge would make the prefetch wait for its data at issue).
   __device__ inline void load(const X* base, long rowstride_b, int Tp, int T, const int* cu, long n0,
                               long nend, int tid) {
+    ok = 0;
 #pragma unroll
     for (int p = 0; p < PER; ++p) {
-      const int u = tid + p * WG_NT;
+      const int u = min(tid + p * WG_NT, NU - 1);   // threads past the last unit read it again
       const int r0 = (u % NG) * RG, c = (u / NG) * VN;
 #pragma unroll
       for (int q = 0; q < RG; ++q) {
-        v[p][q] = uint4{0u, 0u, 0u, 0u};
         const long n = n0 + r0 + q;
-        if (u < NU && n < nend) {
-          const long bb = n / Tp, t = n % Tp;
-          if (t < seq_len(cu, (int)bb, T)) v[p][q] = ld16(base + bb * rowstride_b + t * D + c);
-        }
+        const long nc = n < nend ? n : nend - 1;
+        const long bb = nc / Tp, t = nc % Tp;
+        if (n < nend && t < seq_len(cu, (int)bb, T)) ok |= 1u << (p * RG + q);
+        v[p][q] = ld16(base + bb * rowstride_b + t * D + c);
       }
     }
+  }
+  __device__ inline uint4 get(int p, int q) const {
+    uint4 w = v[p][q];
+    asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
+    return (ok >> (p * RG + q)) & 1u ? w : uint4{0u, 0u, 0u, 0u};
   }
   __device__ inline void store_t(E* s, int ld, int tid) const {
 #pragma unroll
@@ -69,8 +79,9 @@ struct RowChunk {
       if (u >= NU) continue;
       const int r0 = (u % NG) * RG, c = (u / NG) * VN;
       if constexpr (RG == 2) {
-        const X* x0 = reinterpret_cast<const X*>(&v[p][0]);
-        const X* x1 = reinterpret_cast<const X*>(&v[p][1]);
+        const uint4 w0 = get(p, 0), w1 = get(p, 1);
+        const X* x0 = reinterpret_cast<const X*>(&w0);
+        const X* x1 = reinterpret_cast<const X*>(&w1);
 #pragma unroll
         for (int j = 0; j < VN; ++j) {
           E pr[2] = {to_t<E>(to_f(x0[j])), to_t<E>(to_f(x1[j]))};
@@ -79,7 +90,8 @@ struct RowChunk {
           *reinterpret_cast<uint32_t*>(s + (c + j) * ld + r0) = w;
         }
       } else {
-        const X* x = reinterpret_cast<const X*>(&v[p][0]);
+        const uint4 w = get(p, 0);
+        const X* x = reinterpret_cast<const X*>(&w);
 #pragma unroll
         for (int j = 0; j < VN; ++j) s[(c + j) * ld + r0] = to_t<E>(to_f(x[j]));
       }
