@@ -19,9 +19,12 @@
 //   chunk_bwd_pairs : the refinement-pair terms (R_l, F_l), final dq, dk, dK_l,
 //                     dW_l, dv and dalpha (reverse cumulative sum of dg).
 //
-// All products are MFMA (bf16 or fp32 operands, fp32 accumulation).  Row and
-// column sums needed for the decay gradient are reduced per wave in fixed
-// order (no atomics), so results are bitwise reproducible.
+// All products are MFMA (bf16 or fp32 operands, fp32 accumulation).  The
+// partials handed from one kernel to the next are stored in the element type
+// E (dU, dWk, dK transposed, [D][C] per chunk), except dW_l, which stays fp32
+// (the refinement backward subtracts from it).  Row and column sums needed for
+// the decay gradient are reduced per wave in fixed order (no atomics), so
+// results are bitwise reproducible.
 #include "prism_common.h"
 #include "prism_internal.h"
 
