@@ -9,17 +9,41 @@ namespace prism {
 
 int refine_bwd_tiles(const Dims& d) { return (d.T + rb_own(d.off) - 1) / rb_own(d.off); }
 
-// WT[h][l][j][i] = W[h][l][i][j] for W in {Wk, Wp}
-template <typename E>
-__global__ void transpose_weights_kernel(const E* __restrict__ Wk, const E* __restrict__ Wp,
-                                         E* __restrict__ WkT, E* __restrict__ WpT, int HL, int D) {
-  const long n = (long)HL * D * D;
-  for (long e = blockIdx.x * (long)blockDim.x + threadIdx.x; e < n; e += (long)gridDim.x * blockDim.x) {
-    const long m = e / ((long)D * D);
-    const int i = (int)((e / D) % D), j = (int)(e % D);
-    const long dst = (m * D + j) * D + i;
-    WkT[dst] = Wk[e];
-    WpT[dst] = Wp[e];
+// WT[h][l][j][i] = W[h][l][i][j] for W in {Wk, Wp}: one workgroup per TS x TS
+// tile of one matrix; rows are read as 16-byte vectors, transposed through LDS
+// and written as 16-byte vectors.
+constexpr int TW_NT = 256;
+template <typename E, int D>
+__global__ __launch_bounds__(TW_NT) void transpose_weights_kernel(const E* __restrict__ Wk,
+                                                                  const E* __restrict__ Wp,
+                                                                  E* __restrict__ WkT,
+                                                                  E* __restrict__ WpT) {
+  constexpr int TS = D < 64 ? D : 64;    // tile side
+  constexpr int NTL = D / TS;            // tiles per side
+  constexpr int VN = 16 / (int)sizeof(E);
+  constexpr int VPR = TS / VN;           // vectors per tile row
+  constexpr int NV = TS * VPR;
+  constexpr int LT = TS + VN;            // padded LDS row
+  __shared__ __attribute__((aligned(16))) E tl[TS * LT];
+  const int tile = blockIdx.x % (NTL * NTL);
+  const int mw = blockIdx.x / (NTL * NTL);   // 2 * matrix + (0: W_k, 1: W_p)
+  const long m = mw >> 1;
+  const E* W = ((mw & 1) ? Wp : Wk) + m * D * D;
+  E* WT = ((mw & 1) ? WpT : WkT) + m * D * D;
+  const int ti = tile / NTL, tj = tile % NTL;   // rows ti TS.., columns tj TS.. of W
+  for (int v = threadIdx.x; v < NV; v += TW_NT) {
+    const int r = v / VPR, c = (v % VPR) * VN;
+    st16(tl + r * LT + c, ld16(W + (long)(ti * TS + r) * D + tj * TS + c));
+  }
+  __syncthreads();
+  for (int v = threadIdx.x; v < NV; v += TW_NT) {
+    const int r = v / VPR, c = (v % VPR) * VN;   // row tj TS + r of WT, columns ti TS + c ..
+    E o[VN];
+#pragma unroll
+    for (int k = 0; k < VN; ++k) o[k] = tl[(c + k) * LT + r];
+    uint4 w;
+    __builtin_memcpy(&w, o, 16);
+    st16(WT + (long)(tj * TS + r) * D + ti * TS + c, w);
   }
 }
 
@@ -149,18 +173,23 @@ __global__ __launch_bounds__(WG_NT) void wgrad_gemm_kernel(const E* __restrict__
   });
 }
 
-// Fixed-order reduction of the split-K partial products into dW_k, dW_p.
+// Fixed-order reduction of the split-K partial products into dW_k, dW_p: each
+// thread sums four consecutive entries over the splits in split order.
 __global__ void wgrad_reduce_kernel(const float* __restrict__ part, float* __restrict__ dWk,
                                     float* __restrict__ dWp, int H, int L, int D, int NS) {
-  const long nW = (long)H * L * D * D;
-  for (long e = blockIdx.x * (long)blockDim.x + threadIdx.x; e < 2 * nW; e += (long)gridDim.x * blockDim.x) {
-    const int which = e < nW ? 0 : 1;
-    const long x = e - which * nW;
+  const long nW4 = (long)H * L * D * D / 4;
+  for (long e = blockIdx.x * (long)blockDim.x + threadIdx.x; e < 2 * nW4; e += (long)gridDim.x * blockDim.x) {
+    const int which = e < nW4 ? 0 : 1;
+    const long x = (e - which * nW4) * 4;
     const long hl = x / ((long)D * D), ij = x % ((long)D * D);
     const float* p = part + ((hl * 2 + which) * NS) * (long)D * D + ij;
-    float s = 0.f;
-    for (int k = 0; k < NS; ++k) s += p[(long)k * D * D];
-    (which == 0 ? dWk : dWp)[x] = s;
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < NS; ++k) {
+      const f32x4 y = *reinterpret_cast<const f32x4*>(p + (long)k * D * D);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) s[c] += y[c];
+    }
+    *reinterpret_cast<f32x4*>((which == 0 ? dWk : dWp) + x) = s;
   }
 }
 
@@ -212,9 +241,9 @@ static hipError_t refine_bwd_d(const Dims& d, const RefineBwdArgs<E>& a, int NS,
   const long nw = (long)d.H * d.L * D * D;
   switch (stage) {
     case 0:
-      hipLaunchKernelGGL((transpose_weights_kernel<E>),
-                         dim3((unsigned)((nw + 255) / 256 < 4096 ? (nw + 255) / 256 : 4096)), dim3(256),
-                         0, s, a.Wk, a.Wp, a.WkT, a.WpT, d.H * d.L, D);
+      hipLaunchKernelGGL((transpose_weights_kernel<E, D>),
+                         dim3(2 * d.H * d.L * (D < 64 ? 1 : (D / 64) * (D / 64))), dim3(TW_NT), 0, s,
+                         a.Wk, a.Wp, a.WkT, a.WpT);
       break;
     case 1:
       if (d.act == ACT_IDENTITY)
@@ -227,7 +256,8 @@ static hipError_t refine_bwd_d(const Dims& d, const RefineBwdArgs<E>& a, int NS,
                          a.dKl, a.dP, a.u, a.part, d.B, d.H, d.L, d.T, d.Tp, NS, d.cu);
       break;
     case 3: {
-      const unsigned grid = (unsigned)((2 * nw + 255) / 256 < 8192 ? (2 * nw + 255) / 256 : 8192);
+      const long n4 = 2 * nw / 4;
+      const unsigned grid = (unsigned)((n4 + 255) / 256 < 8192 ? (n4 + 255) / 256 : 8192);
       hipLaunchKernelGGL(wgrad_reduce_kernel, dim3(grid), dim3(256), 0, s, a.part, a.dWk_o, a.dWp_o,
                          d.H, d.L, D, NS);
       break;
