@@ -65,9 +65,11 @@ def algorithmic_counts(w):
                             + nch * (2 * D * D * e + 2 * C * D * e + 4),
                             nch * (2 * C * C * D * (4 * L + 6) + 2 * C * D * D * (L + 2))
                             + th * 4 * L * D * D)
+    # products per chunk: C x C x D ones K K^T, K Q^T, T V, T K, R0 Wk^T and,
+    # per step, K_l K^T and F W_l; D x D x C ones H, M, E and, per step, H's W_l part
     c["chunk_fwd_bwdmode"] = (th * (4 * D * e + 8) + ntp * 2 * L * D * e
                               + nch * (4 * D * D * e + 2 * C * D * e + 4),
-                              nch * (2 * C * C * D * (2 * L + 5) + 2 * C * D * D * (L + 4)))
+                              nch * (2 * C * C * D * (2 * L + 5) + 2 * C * D * D * (L + 3)))
     # state pass: read M^T, H^T, write S_c (kept by the training forward), S0 /
     # S_T; the forward pass also forms the readout: read Qt, O_loc, write o
     st = (nch * D * D * 3 * e + bh * D * D * 4, nch * 2 * D ** 3)
@@ -80,7 +82,9 @@ def algorithmic_counts(w):
                       st[1] + nch * 2 * C * D * D)
     c["chunk_bwd_state"] = (th * (2 * D * e + 4) + nch * (2 * C * D * e + 2 * D * D * e + 4 * e * C * D + 4 * C)
                             + ntp * L * D * (3 * e + 4),  # read K_l, W_l; write dK_l, dW_l (fp32) partials
-                            nch * (2 * C * D * D * (6 + 2 * L) + 2 * D ** 3))
+                            # C x D x D products dQt, U dS_n, K dS_n^T, K dM^T, Wk dM and
+                            # two per step; the D x D x D one dM
+                            nch * (2 * C * D * D * (5 + 2 * L) + 2 * D ** 3))
     c["chunk_bwd_solve"] = (th * (4 * D * e + 12) + ntp * 2 * L * D * e + nch * (7 * e * C * D + 8 * C),
                             nch * (2 * C * C * D * (2 * L + 16) + 4 * C ** 3))
     c["chunk_bwd_pairs"] = (th * (5 * D * e + 8) + ntp * 2 * L * D * e + nch * 3 * e * C * D
@@ -193,8 +197,9 @@ def _sources_sha256():
 
 def summarize_profiles(d, workload):
     """Turn the rocprofv3 runs under directory d (trace/, fetch/, write/,
-    cfetch/, cwrite/: the commands are listed in the written summary) into
-    profiles/hbm_traffic.json and profiles/<workload>_kernels.md."""
+    cfetch/, cwrite/ and, if present, mfma/: the commands are listed in the
+    written summary) into profiles/hbm_traffic.json and
+    profiles/<workload>_kernels.md."""
     import csv
     import collections
     from linear_recurrent_sequence_shortconv_amd.workloads import workloads
@@ -242,6 +247,7 @@ def summarize_profiles(d, workload):
         "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/write -o run -- python -u $R/bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-varlen",
         "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/cfetch -o run -- python -u $R/bench.py --calibrate-copy",
         "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/cwrite -o run -- python -u $R/bench.py --calibrate-copy",
+        f"cd /tmp && rocprofv3 --pmc {' '.join(MFMA_COUNTERS)} --output-format csv -d $OUT/mfma -o run -- python -u $R/bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-varlen",
         f"python bench.py --summarize-profiles $OUT --workload {workload}",
     ]
     rec = {"workload": workload, "sources_sha256": _sources_sha256(),
@@ -275,9 +281,65 @@ def summarize_profiles(d, workload):
                           f"{(meas / 1e6) if meas else float('nan'):.1f} | "
                           f"{(meas / c['bytes']) if meas else float('nan'):.2f} | {gbs:.0f} | {gbs / HBM_PEAK_GBS:.3f} |"))
     lines += [r for _, r in sorted(rows, reverse=True)]
+    mfma_csv = os.path.join(d, "mfma", "run_counter_collection.csv")
+    if os.path.exists(mfma_csv):
+        lines += _mfma_table(mfma_csv, times, names_of, counts)
     with open(os.path.join(ROOT, "profiles", f"{workload}_kernels.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+# Matrix-core counters (gfx950): SQ_INSTS_VALU_MFMA_MOPS_* count multiply and
+# add operations / 512, summed over the shader engines; SQ_VALU_MFMA_BUSY_CYCLES
+# sums the cycles each SIMD's matrix unit is busy; GRBM_GUI_ACTIVE reads once
+# per XCD, so the per-dispatch value is the XCDs' sum of the active cycles.
+MFMA_COUNTERS = ["SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_INSTS_VALU_MFMA_MOPS_F32",
+                 "SQ_VALU_MFMA_BUSY_CYCLES", "GRBM_GUI_ACTIVE"]
+N_XCD = 8
+N_SIMD = 256 * 4
+
+
+def _mfma_table(path, times, names_of, counts):
+    """Markdown lines: matrix-core FLOPs and busy time per kernel, from one
+    rocprofv3 --pmc run with MFMA_COUNTERS (one row per dispatch and counter).
+    TFLOP/s divide the counted FLOPs by the kernel-trace average duration;
+    `pipe frac` is the time the counted FLOPs need at the dense peaks
+    (bf16 2.5 PFLOP/s, fp32 157.3 TFLOP/s) over that duration; `busy` is the
+    matrix units' busy cycles over the SIMDs' active cycles."""
+    import csv
+    import collections
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    for r in csv.DictReader(open(path)):
+        fam = _family(r["Kernel_Name"])
+        if fam:
+            names_of.setdefault(fam[0], fam)
+            per[fam[0]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    out = ["", "Matrix cores (MFMA), one rocprofv3 --pmc run with " + ", ".join(MFMA_COUNTERS) + ": "
+           "counted FLOP = 512 x the MOPS counters; TFLOP/s over the kernel-trace average duration; "
+           "`pipe frac` = time the counted FLOPs need at the dense peaks (bf16 2.5 PFLOP/s, fp32 "
+           "157.3 TFLOP/s) / duration; `busy` = SQ_VALU_MFMA_BUSY_CYCLES / (GRBM_GUI_ACTIVE / "
+           f"{N_XCD} XCDs x {N_SIMD} SIMDs).  `algorithmic GFLOP` is the products the algorithm "
+           "needs (bench.py, algorithmic_counts).", "",
+           "| kernel | counted GFLOP bf16 | counted GFLOP fp32 | algorithmic GFLOP | TFLOP/s (bf16) | "
+           "pipe frac | busy |",
+           "|---|---:|---:|---:|---:|---:|---:|"]
+    rows = []
+    for first, v in per.items():
+        def avg(c):
+            x = v.get(c, [])
+            return sum(x) / len(x) if x else 0.0
+        fb, ff = avg(MFMA_COUNTERS[0]) * 512, avg(MFMA_COUNTERS[1]) * 512
+        if fb + ff <= 0 or first not in times:
+            continue
+        calls, tot = times[first]
+        sec = tot / calls * 1e-9
+        pipe = (fb / (MFMA_BF16_PEAK_TFLOPS * 1e12) + ff / (MFMA_F32_PEAK_TFLOPS * 1e12)) / sec
+        gui = avg(MFMA_COUNTERS[3])
+        busy = avg(MFMA_COUNTERS[2]) / (gui / N_XCD * N_SIMD) if gui > 0 else float("nan")
+        alg = counts.get(first, {}).get("flops", 0)
+        rows.append((tot, f"| {' / '.join(names_of[first])} | {fb / 1e9:.1f} | {ff / 1e9:.2f} | {alg / 1e9:.1f} | "
+                          f"{fb / sec / 1e12:.0f} | {pipe:.3f} | {busy:.3f} |"))
+    return out + [r for _, r in sorted(rows, reverse=True)]
 
 
 def roofline_for(name, counts, avg_ms, dtype, traffic=None):

@@ -79,6 +79,12 @@ def test_summarize_profiles_scales_counters_by_the_copy(tmp_path, monkeypatch):
                ["Kernel_Name", "Counter_Value"], [[k, 500.0]])
     _write_csv(os.path.join(d, "trace", "run_kernel_stats.csv"),
                ["Name", "Calls", "TotalDurationNs"], [[k, 4, 400000]])
+    # matrix-core pass: 1e6 MOPS = 512 MFLOP in 100 us; busy 1000 cycles per
+    # SIMD out of 4000 active cycles per XCD
+    mc = ["Kernel_Name", "Counter_Name", "Counter_Value"]
+    _write_csv(os.path.join(d, "mfma", "run_counter_collection.csv"), mc,
+               [[k, "SQ_INSTS_VALU_MFMA_MOPS_BF16", 1e6], [k, "SQ_INSTS_VALU_MFMA_MOPS_F32", 0.0],
+                [k, "SQ_VALU_MFMA_BUSY_CYCLES", 1000.0 * 1024], [k, "GRBM_GUI_ACTIVE", 8 * 4000.0]])
     out = tmp_path / "repo"
     (out / "profiles").mkdir(parents=True)
     monkeypatch.setattr(bench, "ROOT", str(out))
@@ -91,3 +97,5 @@ def test_summarize_profiles_scales_counters_by_the_copy(tmp_path, monkeypatch):
     assert t["fetch_bytes"] == 2 * 1000 * 1024 and t["write_bytes"] == 500 * 1024
     md = open(out / "profiles" / "lm-T2048_kernels.md").read()
     assert "| wgrad_reduce | 4 | 100.0 |" in md
+    # 0.512 GFLOP; 5.12 TFLOP/s; 0.512e9 / 2.5e15 / 1e-4 s = 0.002048 of the bf16 pipe
+    assert "| wgrad_reduce | 0.5 | 0.00 |" in md and "| 5 | 0.002 | 0.250 |" in md
