@@ -284,6 +284,13 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
   float a_[2][FPW][4];
   E dvd[2][FPW][4];         // direct v-gradient (fetched during the last step; converted at use)
   f32x4 du[2][FPW];
+  // Four steps: r^(l-1), kept from the replay of reverse step l for step
+  // l - 1 (steps 3 and 1 replay the chain, step 2 takes the kept rows; 4
+  // replayed GELUs instead of 6).  The launcher runs this kernel at L == 4
+  // only.  With three steps the kept rows would spill registers, which
+  // costs what the one saved GELU gains.
+  constexpr bool KEEP = LMAX == 4;
+  float rkeep[KEEP ? 2 : 1][FPW][4];
 #pragma unroll
   for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -306,27 +313,48 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
     f32x4 p[2][FPW];
     float rl[2][FPW][4];
     if constexpr (REPLAY) {
-      // r^(l) by replaying the chain from r^(1): l steps of VALU work
 #pragma unroll
       for (int m = 0; m < 2; ++m)
 #pragma unroll
-        for (int nn = 0; nn < FPW; ++nn) {
-          p[m][nn] = ps[l][m][nn];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) rl[m][nn][i] = r[m][nn][i];
-        }
-#pragma unroll
-      for (int j = 0; j < l; ++j)
+        for (int nn = 0; nn < FPW; ++nn) p[m][nn] = ps[l][m][nn];
+      if (KEEP && l >= 1 && ((LMAX - 1 - l) & 1)) {
+        // the previous reverse step replayed through r^(l)
 #pragma unroll
         for (int m = 0; m < 2; ++m)
 #pragma unroll
           for (int nn = 0; nn < FPW; ++nn)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float z = ps[j][m][nn][i] * rl[m][nn][i];
-              if constexpr (ACT == ACT_IDENTITY) rl[m][nn][i] -= z;
-              else rl[m][nn][i] -= gelu_erf(z);
-            }
+            for (int i = 0; i < 4; ++i) rl[m][nn][i] = rkeep[m][nn][i];
+      } else {
+        // r^(l) by replaying the chain from r^(1): l steps of VALU work
+#pragma unroll
+        for (int m = 0; m < 2; ++m)
+#pragma unroll
+          for (int nn = 0; nn < FPW; ++nn)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) rl[m][nn][i] = r[m][nn][i];
+#pragma unroll
+        for (int j = 0; j < l; ++j) {
+          if (KEEP && j + 1 == l) {   // rl holds r^(l-1) before this last replay step
+#pragma unroll
+            for (int m = 0; m < 2; ++m)
+#pragma unroll
+              for (int nn = 0; nn < FPW; ++nn)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) rkeep[m][nn][i] = rl[m][nn][i];
+          }
+#pragma unroll
+          for (int m = 0; m < 2; ++m)
+#pragma unroll
+            for (int nn = 0; nn < FPW; ++nn)
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const float z = ps[j][m][nn][i] * rl[m][nn][i];
+                if constexpr (ACT == ACT_IDENTITY) rl[m][nn][i] -= z;
+                else rl[m][nn][i] -= gelu_erf(z);
+              }
+        }
+      }
     } else {
       Frag bw[FPW][D / KS];
       load_w(Wp + ((long)h * L + l) * D * D, bw);
