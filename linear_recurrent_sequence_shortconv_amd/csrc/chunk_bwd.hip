@@ -302,6 +302,12 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
     __syncthreads();
   }
 
+  // The lane's offsets of the last phases are formed again from an opaque copy
+  // of the thread index: kept live across the refinement loop they spill.
+  int tid_o = threadIdx.x;
+  asm volatile("" : "+v"(tid_o));
+  {
+  const int tid = tid_o, lane = tid_o & 63;
   // ---- dM (row-major into X1, transposed into X2); Wk rows ----
   __syncthreads();   // every read of dS_n / dS_n^T (X1, X2) is done
   for_tiles(dm, wave, lane, [&](int k0, int n, const f32x4& x) {
@@ -362,6 +368,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
     for (int w = 0; w < NW; ++w) ssum += sdw[w];
     const float dgC = expf(g[C - 1]) * ssum + tot;
     if (lane < C) dgs[cidx * C + lane] = -Dd + (lane == C - 1 ? dgC : 0.f);
+  }
   }
 }
 
@@ -1051,6 +1058,12 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
     __syncthreads();
   }
 
+  // The lane's offsets of the last phases are formed again from an opaque copy
+  // of the thread index: kept live across the refinement loop they spill.
+  int tid_o = threadIdx.x;
+  asm volatile("" : "+v"(tid_o));
+  {
+  const int tid = tid_o, lane = tid_o & 63;
   // ---- final dq, dk (and dv when L = 0) ----
   if (actC) {
     dgs_.flush_rows(rs + wave * C, TLC::m0(wave), lane);
@@ -1128,6 +1141,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
       if (lane + off < 64) s += y;
     }
     if (lane < nval) dalpha[row0 + (long)lane * H] = s / al[lane];
+  }
   }
 }
 
