@@ -73,7 +73,7 @@ def test_fp32_backward_ragged(d, chunk, L):
     _check_full(x, "f32", chunk, L)
 
 
-@pytest.mark.parametrize("L", [1, 3, 5, 8])
+@pytest.mark.parametrize("L", [1, 3, 4, 5, 8])
 def test_fp32_backward_depths(L):
     x = make_inputs(1, 40, 2, 16, L, "f32", seed=70 + L, random_S0=True, with_dST=True)
     print(f"\n[fp32 bwd d=16 chunk=16 T=40 L={L}]", flush=True)
@@ -92,6 +92,14 @@ def test_bf16_d128_backward(chunk):
     x = make_inputs(2, 150, 2, 128, 3, "bf16", seed=5 + chunk, random_S0=True, with_dST=True)
     print(f"\n[bf16 bwd d=128 chunk={chunk} T=150 L=3]", flush=True)
     _check_full(x, "bf16", chunk, 3)
+
+
+def test_bf16_d128_backward_four_steps():
+    # the four-step refinement backward keeps one replayed residual for the
+    # next reverse step (a kernel instance of its own)
+    x = make_inputs(2, 150, 2, 128, 4, "bf16", seed=44, random_S0=True, with_dST=True)
+    print("\n[bf16 bwd d=128 chunk=64 T=150 L=4]", flush=True)
+    _check_full(x, "bf16", 64, 4)
 
 
 def test_bf16_backward_long_memory():
