@@ -143,6 +143,18 @@ def measured_traffic():
     return {k: v["bytes_per_launch"] for k, v in rec.get("kernels", {}).items()}
 
 
+def measured_mfma():
+    """Matrix-core FLOPs and busy fraction per kernel from the committed
+    counter summary, if it was taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return {}
+    rec = json.load(open(path))
+    if rec.get("sources_sha256") != _sources_sha256():
+        return {}
+    return rec.get("mfma", {})
+
+
 # rocprofv3 kernel names -> the timer names used by the library and above
 _FAMILIES = [("refine_fwd_kernel", ["refine_fwd", "refine_fwd_recompute"]),
              ("chunk_bwd_state_kernel", ["chunk_bwd_state"]),
@@ -250,10 +262,13 @@ def summarize_profiles(d, workload):
         f"cd /tmp && rocprofv3 --pmc {' '.join(MFMA_COUNTERS)} --output-format csv -d $OUT/mfma -o run -- python -u $R/bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-varlen",
         f"python bench.py --summarize-profiles $OUT --workload {workload}",
     ]
+    mfma_csv = os.path.join(d, "mfma", "run_counter_collection.csv")
+    mfma_lines, mfma_rec = (_mfma_table(mfma_csv, times, names_of, counts)
+                            if os.path.exists(mfma_csv) else ([], {}))
     rec = {"workload": workload, "sources_sha256": _sources_sha256(),
            "calibration": {"fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4),
                            "copy_bytes": 1 << 30},
-           "commands": cmds, "kernels": traffic}
+           "commands": cmds, "kernels": traffic, "mfma": mfma_rec}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(os.path.join(ROOT, "profiles", "hbm_traffic.json"), "w") as f:
         json.dump(rec, f, indent=1)
@@ -281,9 +296,7 @@ def summarize_profiles(d, workload):
                           f"{(meas / 1e6) if meas else float('nan'):.1f} | "
                           f"{(meas / c['bytes']) if meas else float('nan'):.2f} | {gbs:.0f} | {gbs / HBM_PEAK_GBS:.3f} |"))
     lines += [r for _, r in sorted(rows, reverse=True)]
-    mfma_csv = os.path.join(d, "mfma", "run_counter_collection.csv")
-    if os.path.exists(mfma_csv):
-        lines += _mfma_table(mfma_csv, times, names_of, counts)
+    lines += mfma_lines
     with open(os.path.join(ROOT, "profiles", f"{workload}_kernels.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -305,7 +318,8 @@ def _mfma_table(path, times, names_of, counts):
     TFLOP/s divide the counted FLOPs by the kernel-trace average duration;
     `pipe frac` is the time the counted FLOPs need at the dense peaks
     (bf16 2.5 PFLOP/s, fp32 157.3 TFLOP/s) over that duration; `busy` is the
-    matrix units' busy cycles over the SIMDs' active cycles."""
+    matrix units' busy cycles over the SIMDs' active cycles.  Returns the
+    lines and a per-timer-name record {counted flops, pipe frac, busy}."""
     import csv
     import collections
     per = collections.defaultdict(lambda: collections.defaultdict(list))
@@ -324,6 +338,7 @@ def _mfma_table(path, times, names_of, counts):
            "pipe frac | busy |",
            "|---|---:|---:|---:|---:|---:|---:|"]
     rows = []
+    rec = {}
     for first, v in per.items():
         def avg(c):
             x = v.get(c, [])
@@ -339,7 +354,10 @@ def _mfma_table(path, times, names_of, counts):
         alg = counts.get(first, {}).get("flops", 0)
         rows.append((tot, f"| {' / '.join(names_of[first])} | {fb / 1e9:.1f} | {ff / 1e9:.2f} | {alg / 1e9:.1f} | "
                           f"{fb / sec / 1e12:.0f} | {pipe:.3f} | {busy:.3f} |"))
-    return out + [r for _, r in sorted(rows, reverse=True)]
+        for n in names_of[first]:
+            rec[n] = {"flops_bf16": round(fb), "flops_f32": round(ff), "pipe_frac": round(pipe, 4),
+                      "busy": round(busy, 4)}
+    return out + [r for _, r in sorted(rows, reverse=True)], rec
 
 
 def roofline_for(name, counts, avg_ms, dtype, traffic=None):
@@ -361,30 +379,120 @@ def roofline_for(name, counts, avg_ms, dtype, traffic=None):
             "avg_launch_ms": round(avg_ms, 5), "roofline_floor_ms": round(c["floor_ms"], 5)}
 
 
-def cpu_baseline(w, x, budget_s=15.0, backward=False):
-    """The float64 oracle, as it stands, on a bounded sample of the workload:
-    whole (b, h) sequences of the same inputs, one thread.  Returns tokens/s
-    scaled to the workload's unit (a token spans all H heads)."""
+def _oracle_sequence(args):
+    """One (b, h) sequence through the float64 oracle (a CPU-baseline task):
+    forward, and the backward when asked.  Runs in a pool worker."""
     from threadpoolctl import threadpool_limits
     from oracle import prism_oracle as O
-    seqs, t_used = 0, 0.0
+    seq, W, backward = args
     with threadpool_limits(limits=1):
-        pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
-        for b, h in pairs:
-            t0 = time.perf_counter()
-            s = {n: x[n][b:b + 1, :, h:h + 1] for n in ("q", "k", "v", "alpha", "beta", "dO")}
-            W = [x[n][h:h + 1] for n in ("Wk", "Wp", "wbeta", "conv")] if w.L > 0 else [None] * 4
-            O.forward(s["q"], s["k"], s["v"], s["alpha"], s["beta"], *W)
-            if backward:
-                O.backward(s["q"], s["k"], s["v"], s["alpha"], s["beta"], *W, dO=s["dO"])
-            t_used += time.perf_counter() - t0
-            seqs += 1
-            if t_used >= budget_s:
-                break
-    tokens = seqs * w.T / w.H
-    return {"value": round(tokens / t_used, 2), "unit": "tokens/s", "cores": 1, "kind": "oracle",
+        O.forward(seq["q"], seq["k"], seq["v"], seq["alpha"], seq["beta"], *W)
+        if backward:
+            O.backward(seq["q"], seq["k"], seq["v"], seq["alpha"], seq["beta"], *W, dO=seq["dO"])
+    return seq["q"].shape[1]
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(w, x, budget_s=20.0, backward=False, max_workers=16):
+    """The float64 oracle, as it stands, on the host cores: whole (b, h)
+    sequences of the same inputs spread over a process pool (one BLAS thread
+    per worker, workers = the cores this process may use, at most
+    max_workers), submitted in order until the time budget is spent.  Workers
+    are started and warmed before the clock runs.  Returns tokens/s scaled to
+    the workload's unit (a token spans all H heads)."""
+    import multiprocessing as mp
+    from concurrent.futures import FIRST_COMPLETED, ProcessPoolExecutor, wait
+    workers = max(1, min(max_workers, len(os.sched_getaffinity(0))))
+    pairs = [(b, h) for b in range(w.B) for h in range(w.H)]
+
+    def task(b, h):
+        seq = {n: x[n][b:b + 1, :, h:h + 1] for n in ("q", "k", "v", "alpha", "beta", "dO")}
+        W = [x[n][h:h + 1] for n in ("Wk", "Wp", "wbeta", "conv")] if w.L > 0 else [None] * 4
+        return (seq, W, backward)
+
+    # spawned workers: a fresh interpreter each (this process has the GPU open)
+    with ProcessPoolExecutor(workers, mp_context=mp.get_context("spawn")) as ex:
+        tiny = {n: x[n][:1, :2, :1] for n in ("q", "k", "v", "alpha", "beta", "dO")}
+        Wt = [x[n][:1] for n in ("Wk", "Wp", "wbeta", "conv")] if w.L > 0 else [None] * 4
+        list(ex.map(_oracle_sequence, [(tiny, Wt, backward)] * workers))   # warm-up
+        t0 = time.perf_counter()
+        it = iter(pairs)
+        pending, done_tokens, seqs = set(), 0, 0
+        for _ in range(workers):
+            nxt = next(it, None)
+            if nxt is not None:
+                pending.add(ex.submit(_oracle_sequence, task(*nxt)))
+        while pending:
+            finished, pending = wait(pending, return_when=FIRST_COMPLETED)
+            for f in finished:
+                done_tokens += f.result()
+                seqs += 1
+            if time.perf_counter() - t0 < budget_s:
+                for _ in finished:
+                    nxt = next(it, None)
+                    if nxt is not None:
+                        pending.add(ex.submit(_oracle_sequence, task(*nxt)))
+        wall = time.perf_counter() - t0
+    tokens = done_tokens / w.H
+    return {"value": round(tokens / wall, 2), "unit": "tokens/s", "cores": workers, "kind": "oracle",
+            "cpu_model": _cpu_model(),
             "sample": f"{seqs} of {w.B * w.H} (b,h) sequences x T={w.T}, "
-                      f"{'fwd+bwd' if backward else 'fwd'}, float64, {t_used:.1f} s"}
+                      f"{'fwd+bwd' if backward else 'fwd'}, float64, {workers} worker processes "
+                      f"with one thread each, {wall:.1f} s wall"}
+
+
+# The two stages the targets are stated for: the chunked scan (chunk-local
+# solve and products, the state passes, and their backward) against the bf16
+# MFMA peak, and the refinement / ShortConv stage (its forward, its backward
+# with the ShortConv adjoint, and the weight-gradient kernels) against HBM.
+SCAN_KERNELS = ("chunk_fwd", "state_fwd", "state_bwd", "chunk_bwd_state", "chunk_bwd_solve",
+                "chunk_bwd_pairs")
+REFINE_KERNELS = ("refine_fwd", "refine_bwd", "wgrad_gemm", "wgrad_reduce", "bias_reduce",
+                  "transpose_weights")
+
+
+def stage_fractions(kernels, counts, dtype):
+    """Aggregate rates of the two stages over one training step: scan
+    sum(FLOP) / sum(t) against the dense MFMA peak (and its sum(bytes) /
+    sum(t) against HBM), refinement sum(bytes) / sum(t) against HBM; with the
+    counter-measured MFMA busy fraction of the scan kernels (time-weighted)
+    when the committed counter summary matches the current sources."""
+    peak_f = MFMA_BF16_PEAK_TFLOPS if dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
+    mf = measured_mfma()
+
+    def agg(names):
+        t = sum(kernels[n]["total_ms"] for n in names if n in kernels) * 1e-3
+        by = sum(counts[n]["bytes"] * kernels[n]["launches_per_step"] for n in names if n in kernels)
+        fl = sum(counts[n]["flops"] * kernels[n]["launches_per_step"] for n in names if n in kernels)
+        return t, by, fl
+
+    t, by, fl = agg(SCAN_KERNELS)
+    scan = None
+    if t > 0:
+        busy = None
+        if all(n in mf for n in SCAN_KERNELS if n in kernels):
+            busy = round(sum(mf[n]["busy"] * kernels[n]["total_ms"] for n in SCAN_KERNELS if n in kernels)
+                         / (t * 1e3), 4)
+        scan = {"kernels": [n for n in SCAN_KERNELS if n in kernels], "ms": round(t * 1e3, 4),
+                "tflops": round(fl / t / 1e12, 1), "mfma_frac": round(fl / t / 1e12 / peak_f, 4),
+                "mfma_busy_counted": busy, "target_mfma_frac": 0.40,
+                "hbm_frac": round(by / t / 1e9 / HBM_PEAK_GBS, 4)}
+    t, by, fl = agg(REFINE_KERNELS)
+    refine = None
+    if t > 0:
+        refine = {"kernels": [n for n in REFINE_KERNELS if n in kernels], "ms": round(t * 1e3, 4),
+                  "gbs": round(by / t / 1e9, 1), "hbm_frac": round(by / t / 1e9 / HBM_PEAK_GBS, 4),
+                  "target_hbm_frac": 0.60}
+    return {"scan": scan, "refinement": refine}
 
 
 def decode_bench(w, steps, batch=DECODE_BATCH):
@@ -513,12 +621,13 @@ def sweep(steps, names=SWEEP):
         del x
         desc = P.make_desc(w.B, w.T, w.H, w.d, w.d, w.L, w.chunk, P.PRISM_BF16)
         ws_f = P._workspace(P.forward_workspace_bytes(desc), a[0].device)[1]
-        ws_b = P._workspace(P.backward_workspace_bytes(desc), a[0].device)[1]
+        ws_ft = P._workspace(P.forward_train_workspace_bytes(desc), a[0].device)[1]
+        ws_bt = P._workspace(P.backward_train_workspace_bytes(desc), a[0].device)[1]
         saved = P._workspace(P.saved_bytes(desc), a[0].device)[1]
 
         def train():
-            P.forward(*a, chunk=w.chunk, workspace=ws_f, saved=saved)
-            P.backward(*a, dO=dO, chunk=w.chunk, workspace=ws_b, saved=saved)
+            P.forward(*a, chunk=w.chunk, workspace=ws_ft, saved=saved)
+            P.backward(*a, dO=dO, chunk=w.chunk, workspace=ws_bt, saved=saved)
 
         def fwd():
             P.forward(*a, chunk=w.chunk, workspace=ws_f)
@@ -539,7 +648,7 @@ def sweep(steps, names=SWEEP):
             res[f"tokens_per_s_{key}"] = round(w.B * w.T / (ms * 1e-3), 1)
         rows.append(res)
         print(json.dumps(res), file=sys.stderr, flush=True)
-        del a, dO, ws_f, ws_b, saved
+        del a, dO, ws_f, ws_ft, ws_bt, saved
         torch.cuda.empty_cache()
     print(json.dumps({"sweep": rows, "dtype": "bf16", "data": "synthetic", "steps": steps}))
 
@@ -611,15 +720,19 @@ def main():
         backward = False
     ws_f = P._workspace(P.forward_workspace_bytes(desc), q.device)[1]
     ws_b = P._workspace(P.backward_workspace_bytes(desc), q.device)[1] if backward else None
+    ws_ft = P._workspace(P.forward_train_workspace_bytes(desc), q.device)[1] if backward else None
+    ws_bt = P._workspace(P.backward_train_workspace_bytes(desc), q.device)[1] if backward else None
     saved = P._workspace(P.saved_bytes(desc), q.device)[1] if backward else None
 
     def step():
         # a training step: the forward keeps what the backward needs
-        P.forward(q, k, v, alpha, beta, Wk, Wp, wbeta, conv, chunk=w.chunk, workspace=ws_f,
-                  saved=saved)
         if backward:
+            P.forward(q, k, v, alpha, beta, Wk, Wp, wbeta, conv, chunk=w.chunk, workspace=ws_ft,
+                      saved=saved)
             P.backward(q, k, v, alpha, beta, Wk, Wp, wbeta, conv, dO=dO, chunk=w.chunk,
-                       workspace=ws_b, saved=saved)
+                       workspace=ws_bt, saved=saved)
+        else:
+            P.forward(q, k, v, alpha, beta, Wk, Wp, wbeta, conv, chunk=w.chunk, workspace=ws_f)
 
     def stateless_step():
         P.forward(q, k, v, alpha, beta, Wk, Wp, wbeta, conv, chunk=w.chunk, workspace=ws_f)
@@ -724,6 +837,7 @@ def main():
                            {"ms_per_step": round(ms_stateless, 4),
                             "tokens_per_s": round(tokens / (ms_stateless * 1e-3), 1)}),
         "roofline": roof,
+        "stages": stage_fractions(kernels, counts, w.dtype) if backward else None,
         "cpu_baseline": cpu,
         "kernels": kernels,
         "decode": decode,

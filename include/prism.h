@@ -85,12 +85,16 @@ typedef enum {
  *              current token and the three before it), 1 = tap j multiplies
  *              v_{t-1-j} (strictly past tokens, the ones the state S_{t-1}
  *              has seen; summary §2.2 Stage 1)
+ *   packed_tokens  with cu_seqlens (packed batch, below): N, the number of
+ *              token rows in the packed tensors; must be >= 0.  Ignored for
+ *              a dense batch.
  * A zero-initialised tail (activation = conv_offset = 0) is the method as
- * described.  Both fields are ignored when L = 0.                          */
+ * described.  activation and conv_offset are ignored when L = 0.           */
 typedef struct {
   int B, T, H, dk, dv, L, chunk, conv_width;
   prism_dtype dtype;
   int activation, conv_offset;
+  int packed_tokens;
 } prism_desc;
 
 /* Tensor layouts (element type "dt" = desc->dtype; f32 = float32):
@@ -115,12 +119,16 @@ typedef struct {
  * Packed batches (variable lengths).  With cu_seqlens (a device array of
  * B + 1 int32 offsets, 4-byte aligned; NULL = dense) the token tensors q, k,
  * v, o, dO, dq, dk, dv are [N, H, d] and alpha, beta, dalpha, dbeta [N, H],
- * N = cu_seqlens[B], sequence b being tokens cu_seqlens[b] ..
+ * N = desc->packed_tokens, sequence b being tokens cu_seqlens[b] ..
  * cu_seqlens[b+1] - 1; desc->T is then the longest length (it sizes the
- * workspaces).  Required: cu_seqlens[0] = 0, non-decreasing, every length
- * <= desc->T (lengths of 0 are allowed: S_T = S0).  The offsets are read on
- * the device only, so these conditions are the caller's to meet; longer
- * sequences are cut at T.  conv_hist, S0, ST and their gradients stay per
+ * workspaces).  Meant: cu_seqlens[0] = 0, non-decreasing, cu_seqlens[B] = N,
+ * every length <= desc->T (lengths of 0 are allowed: S_T = S0).  The offsets
+ * are read on the device only: before any kernel uses them, a sanitising
+ * pass replaces them by c'_i = max_{j <= i} min(max(cu_seqlens[j], 0), N),
+ * and sequences longer than T are cut at T.  Offsets outside the contract
+ * therefore give results for those clamped sequences (rows of o and of the
+ * gradients outside every clamped sequence are not written), but no access
+ * outside the N rows.  conv_hist, S0, ST and their gradients stay per
  * sequence.  A packed batch computes exactly what each sequence would
  * compute alone.
  *
@@ -130,9 +138,13 @@ typedef struct {
  * carries the past; §2.2 Stage 1: the ShortConv reads the last few values).
  * NULL conv_hist means zeros before the sequence. */
 
-/* Workspace sizes in bytes for a descriptor; *bytes = 0 on error. */
+/* Workspace sizes in bytes for a descriptor; *bytes = 0 on error.  The
+ * training pair (below) keeps most intermediates in its saved buffer, so its
+ * entry points need the (smaller) sizes of the *_train_workspace queries. */
 prism_status prism_forward_workspace(const prism_desc* desc, size_t* bytes);
 prism_status prism_backward_workspace(const prism_desc* desc, size_t* bytes);
+prism_status prism_forward_train_workspace(const prism_desc* desc, size_t* bytes);
+prism_status prism_backward_train_workspace(const prism_desc* desc, size_t* bytes);
 
 /* Forward pass: o = readout of S_1..S_T, ST = S_T (ST may be NULL).
  * S0 may be NULL (zero initial state); conv_hist may be NULL (zeros).
@@ -174,7 +186,8 @@ prism_status prism_backward(const prism_desc* desc, const void* q, const void* k
  *              the caller keeps it unchanged in between (same desc, same
  *              inputs, the same conv_hist contents, so not one that
  *              conv_hist_out overwrote; the backward does not check this).
- *   workspace: as for prism_forward / prism_backward (same sizes).
+ *   workspace: 256-byte aligned, prism_forward_train_workspace() /
+ *              prism_backward_train_workspace() bytes.
  * Errors: as for the plain entry points; a NULL, misaligned or too small
  * `saved` buffer gives PRISM_ERR_WORKSPACE / PRISM_ERR_ALIGN before any HIP
  * call. */

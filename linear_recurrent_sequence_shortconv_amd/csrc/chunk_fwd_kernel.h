@@ -17,12 +17,13 @@
 //     Qt  = diag(e^g) Q - R0 Wk,   O_loc = R0 U + sum_l R_l W_l
 //
 // All products are bf16 (or fp32) MFMA with fp32 accumulation; T, the decays
-// and the accumulators stay fp32.  Stored (global, per chunk):
+// and the accumulators stay fp32.  Stored (global, per chunk, in the storage
+// type E unless noted):
 //   Mt [D][D] = M^T (MFMA B operand of the state pass, both directions),
-//   HT [D][D] = H^T fp32, Qt [C][D], O_loc [C][D] fp32, gC, and when asked
+//   HT [D][D] = H^T, Qt [C][D], O_loc [C][D], gC (fp32), and when asked
 //   (training forward) U^T, Wk^T [D][C] for the reverse chunk kernels.
 // In backward mode (dO given) the kernel instead stores Mt, HT, gC,
-// ET = (dO^T Qt)^T fp32 (for the reverse state pass) and U^T, Wk^T.
+// ET = (dO^T Qt)^T (for the reverse state pass) and U^T, Wk^T.
 // After a training forward the reverse state pass forms E from the kept Qt.
 //
 // Fused form (FUSE): the refinement pairs K_l, W_l are formed inside the

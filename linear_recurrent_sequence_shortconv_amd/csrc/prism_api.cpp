@@ -77,6 +77,7 @@ struct FwdWs {
   E *Kl, *Wl, *Mt, *Qt, *Sc, *UT, *WkT;
   E *HT, *Oloc;   // H^T and O_loc per chunk (storage type)
   float* gC;
+  int* cu;        // sanitised packed-batch offsets (packed batches only)
 };
 
 // What a training forward keeps for its backward (caller-owned buffer).
@@ -104,20 +105,22 @@ Kept<E> carve_kept(const prism::Dims& d, Carve& cv) {
 }
 
 template <typename E>
-FwdWs<E> carve_fwd(const prism::Dims& d, Carve& cv) {
+FwdWs<E> carve_fwd(const prism::Dims& d, Carve& cv, bool train) {
   const size_t bh = (size_t)d.B * d.H;
   const size_t es = sizeof(E);
   FwdWs<E> w;
-  // no room for the refinement pairs: the inference forward forms them
-  // inside the chunk kernel, the training forward keeps them in its buffer
+  // No room for the refinement pairs: the inference forward forms them inside
+  // the chunk kernel, the training forward keeps them in its buffer.  The
+  // training forward also keeps M^T, Qt, gC, S_c, U^T, W_k^T there; the
+  // inference forward stores no S_c at all.
   w.Kl = w.Wl = nullptr;
-  w.Mt = cv.take<E>(bh * d.NC * d.D * d.D * es);
+  w.Sc = w.UT = w.WkT = nullptr;
+  w.Mt = train ? nullptr : cv.take<E>(bh * d.NC * d.D * d.D * es);
   w.HT = cv.take<E>(bh * d.NC * d.D * d.D * sizeof(E));
-  w.Qt = cv.take<E>(bh * d.NC * d.C * d.D * es);
+  w.Qt = train ? nullptr : cv.take<E>(bh * d.NC * d.C * d.D * es);
   w.Oloc = cv.take<E>(bh * d.NC * d.C * d.D * sizeof(E));
-  w.gC = cv.take<float>(bh * d.NC * 4);
-  w.Sc = cv.take<E>(bh * d.NC * d.D * d.D * es);
-  w.UT = w.WkT = nullptr;
+  w.gC = train ? nullptr : cv.take<float>(bh * d.NC * 4);
+  w.cu = cv.take<int>(((size_t)d.B + 1) * 4);
   return w;
 }
 
@@ -173,12 +176,17 @@ prism_status check_ptr(const void* p, const char* name, bool required) {
   return PRISM_OK;
 }
 
-// Packed batches: the offsets must be a 4-byte aligned device array; their
-// values are the caller's contract (read on the device only).
-prism_status check_cu(const int* cu, prism::Dims* d) {
+// Packed batches: the offsets must be a 4-byte aligned device array and the
+// packed tensors' row count N must be given; the offsets themselves are read
+// on the device only, where a sanitising pass clamps them into [0, N] before
+// any kernel uses them (prism::launch_cu_sanitize).
+prism_status check_cu(const int* cu, const prism_desc* desc, prism::Dims* d) {
   if (cu && (reinterpret_cast<uintptr_t>(cu) & 3u))
     return fail(PRISM_ERR_ALIGN, "cu_seqlens is not 4-byte aligned");
+  if (cu && desc->packed_tokens < 0)
+    return fail(PRISM_ERR_SHAPE, "packed_tokens must be >= 0 with cu_seqlens");
   d->cu = cu;
+  d->N = cu ? desc->packed_tokens : 0;
   return PRISM_OK;
 }
 
@@ -203,25 +211,33 @@ struct BwdWs {
   E *HT, *ET;     // H^T, E^T per chunk (storage type)
   float *gC, *dgs, *dgp;
   float *dwbp, *dcp, *part;
+  int* cu;        // sanitised packed-batch offsets (packed batches only)
 };
 
 template <typename E>
-BwdWs<E> carve_bwd(const prism::Dims& d, Carve& cv) {
+BwdWs<E> carve_bwd(const prism::Dims& d, Carve& cv, bool train) {
   const size_t bh = (size_t)d.B * d.H;
   const size_t es = sizeof(E);
   const size_t DD = (size_t)d.D * d.D, CD = (size_t)d.C * d.D;
   const size_t ntiles = (size_t)prism::refine_bwd_tiles(d);
   const size_t L1 = d.L > 0 ? d.L : 1;
   BwdWs<E> w;
-  w.Kl = cv.take<E>(bh * d.L * d.Tp * d.D * es);
-  w.Wl = cv.take<E>(bh * d.L * d.Tp * d.D * es);
-  w.Mt = cv.take<E>(bh * d.NC * DD * es);
-  w.HT = cv.take<E>(bh * d.NC * DD * es);
-  w.ET = cv.take<E>(bh * d.NC * DD * es);
-  w.gC = cv.take<float>(bh * d.NC * 4);
-  w.UT = cv.take<E>(bh * d.NC * CD * es);
-  w.WkT = cv.take<E>(bh * d.NC * CD * es);
-  w.Sc = cv.take<E>(bh * d.NC * DD * es);
+  // the forward intermediates: recomputed by the stateless backward, read
+  // from the saved buffer by the training backward (which forms E itself and
+  // needs no H^T)
+  w.Kl = w.Wl = w.Mt = w.HT = w.ET = w.UT = w.WkT = w.Sc = nullptr;
+  w.gC = nullptr;
+  if (!train) {
+    w.Kl = cv.take<E>(bh * d.L * d.Tp * d.D * es);
+    w.Wl = cv.take<E>(bh * d.L * d.Tp * d.D * es);
+    w.Mt = cv.take<E>(bh * d.NC * DD * es);
+    w.HT = cv.take<E>(bh * d.NC * DD * es);
+    w.ET = cv.take<E>(bh * d.NC * DD * es);
+    w.gC = cv.take<float>(bh * d.NC * 4);
+    w.UT = cv.take<E>(bh * d.NC * CD * es);
+    w.WkT = cv.take<E>(bh * d.NC * CD * es);
+    w.Sc = cv.take<E>(bh * d.NC * DD * es);
+  }
   w.dSnT = cv.take<E>(bh * d.NC * DD * es);
   w.dQt = cv.take<E>(bh * d.NC * CD * es);
   w.dUs = cv.take<E>(bh * d.NC * CD * es);
@@ -241,15 +257,16 @@ BwdWs<E> carve_bwd(const prism::Dims& d, Carve& cv) {
   w.part = cv.take<float>((size_t)d.H * L1 * 2 * prism::refine_bwd_splits(d) * DD * 4);
   w.WkW = cv.take<E>((size_t)d.H * d.L * DD * es);
   w.WpW = cv.take<E>((size_t)d.H * d.L * DD * es);
+  w.cu = cv.take<int>(((size_t)d.B + 1) * 4);
   return w;
 }
 
-size_t bwd_ws_bytes(const prism::Dims& d, prism_dtype dt) {
+size_t bwd_ws_bytes(const prism::Dims& d, prism_dtype dt, bool train) {
   Carve cv;
   if (dt == PRISM_BF16)
-    carve_bwd<prism::bf16>(d, cv);
+    carve_bwd<prism::bf16>(d, cv, train);
   else
-    carve_bwd<float>(d, cv);
+    carve_bwd<float>(d, cv, train);
   return cv.off;
 }
 
@@ -270,23 +287,29 @@ size_t step_ws_bytes(const prism::Dims& d, prism_dtype dt) {
   return 2 * one;
 }
 
-size_t fwd_ws_bytes(const prism::Dims& d, prism_dtype dt) {
+size_t fwd_ws_bytes(const prism::Dims& d, prism_dtype dt, bool train) {
   Carve cv;
   if (dt == PRISM_BF16)
-    carve_fwd<prism::bf16>(d, cv);
+    carve_fwd<prism::bf16>(d, cv, train);
   else
-    carve_fwd<float>(d, cv);
+    carve_fwd<float>(d, cv, train);
   return cv.off;
 }
 
 template <typename E>
-prism_status run_forward(const prism::Dims& d, const void* q, const void* k, const void* v,
+prism_status run_forward(const prism::Dims& d0, const void* q, const void* k, const void* v,
                          const float* alpha, const float* beta, const void* Wk, const void* Wp,
                          const void* wbeta, const void* conv, const float* S0, const void* hist,
                          void* o, float* ST, void* hist_out, void* ws, void* keep, hipStream_t s) {
   Carve cv;
   cv.base = static_cast<char*>(ws);
-  FwdWs<E> w = carve_fwd<E>(d, cv);
+  FwdWs<E> w = carve_fwd<E>(d0, cv, keep != nullptr);
+  // packed batch: every kernel reads the sanitised copy of the offsets
+  prism::Dims d = d0;
+  if (d0.cu) {
+    HIP_TRY("cu_sanitize", s, prism::launch_cu_sanitize(d0, w.cu, s));
+    d.cu = w.cu;
+  }
   if (keep) {   // training forward: what the backward reads lives in the kept buffer
     Carve ck;
     ck.base = static_cast<char*>(keep);
@@ -339,7 +362,7 @@ prism_status run_forward(const prism::Dims& d, const void* q, const void* k, con
 }
 
 template <typename E>
-prism_status run_backward(const prism::Dims& d, const void* q, const void* k, const void* v,
+prism_status run_backward(const prism::Dims& d0, const void* q, const void* k, const void* v,
                           const float* alpha, const float* beta, const void* Wk, const void* Wp,
                           const void* wbeta, const void* conv, const float* S0, const void* hist,
                           const void* dO, const float* dST, void* dq, void* dk, void* dv,
@@ -348,7 +371,12 @@ prism_status run_backward(const prism::Dims& d, const void* q, const void* k, co
                           hipStream_t s) {
   Carve cv;
   cv.base = static_cast<char*>(ws);
-  BwdWs<E> w = carve_bwd<E>(d, cv);
+  BwdWs<E> w = carve_bwd<E>(d0, cv, kept != nullptr);
+  prism::Dims d = d0;
+  if (d0.cu) {
+    HIP_TRY("cu_sanitize", s, prism::launch_cu_sanitize(d0, w.cu, s));
+    d.cu = w.cu;
+  }
   const E* q_ = static_cast<const E*>(q);
   const E* k_ = static_cast<const E*>(k);
   const E* v_ = static_cast<const E*>(v);
@@ -469,7 +497,7 @@ prism_status prism_forward_workspace(const prism_desc* desc, size_t* bytes) {
   prism::Dims d;
   prism_status st = check_desc(desc, &d);
   if (st != PRISM_OK) return st;
-  *bytes = fwd_ws_bytes(d, desc->dtype);
+  *bytes = fwd_ws_bytes(d, desc->dtype, false);
   return PRISM_OK;
 }
 
@@ -479,7 +507,27 @@ prism_status prism_backward_workspace(const prism_desc* desc, size_t* bytes) {
   prism::Dims d;
   prism_status st = check_desc(desc, &d);
   if (st != PRISM_OK) return st;
-  *bytes = bwd_ws_bytes(d, desc->dtype);
+  *bytes = bwd_ws_bytes(d, desc->dtype, false);
+  return PRISM_OK;
+}
+
+prism_status prism_forward_train_workspace(const prism_desc* desc, size_t* bytes) {
+  if (bytes) *bytes = 0;
+  if (!bytes) return fail(PRISM_ERR_NULL, "bytes is NULL");
+  prism::Dims d;
+  prism_status st = check_desc(desc, &d);
+  if (st != PRISM_OK) return st;
+  *bytes = fwd_ws_bytes(d, desc->dtype, true);
+  return PRISM_OK;
+}
+
+prism_status prism_backward_train_workspace(const prism_desc* desc, size_t* bytes) {
+  if (bytes) *bytes = 0;
+  if (!bytes) return fail(PRISM_ERR_NULL, "bytes is NULL");
+  prism::Dims d;
+  prism_status st = check_desc(desc, &d);
+  if (st != PRISM_OK) return st;
+  *bytes = bwd_ws_bytes(d, desc->dtype, true);
   return PRISM_OK;
 }
 
@@ -518,7 +566,7 @@ prism_status forward_entry(const prism_desc* desc, const void* q, const void* k,
     prism::Dims d;
     prism_status st = check_desc(desc, &d);
     if (st != PRISM_OK) return st;
-    st = check_cu(cu_seqlens, &d);
+    st = check_cu(cu_seqlens, desc, &d);
     if (st != PRISM_OK) return st;
     const bool refine = d.L > 0;
     CHECK_PTR(q, true);
@@ -539,7 +587,7 @@ prism_status forward_entry(const prism_desc* desc, const void* q, const void* k,
       st = check_buffer(saved, saved_bytes, kept_bytes(d, desc->dtype), "saved");
       if (st != PRISM_OK) return st;
     }
-    st = check_buffer(workspace, workspace_bytes, fwd_ws_bytes(d, desc->dtype), "workspace");
+    st = check_buffer(workspace, workspace_bytes, fwd_ws_bytes(d, desc->dtype, train), "workspace");
     if (st != PRISM_OK) return st;
     void* keep = train ? saved : nullptr;
     if (desc->dtype == PRISM_BF16)
@@ -566,7 +614,7 @@ prism_status backward_entry(const prism_desc* desc, const void* q, const void* k
     prism::Dims d;
     prism_status st = check_desc(desc, &d);
     if (st != PRISM_OK) return st;
-    st = check_cu(cu_seqlens, &d);
+    st = check_cu(cu_seqlens, desc, &d);
     if (st != PRISM_OK) return st;
     const bool refine = d.L > 0;
     CHECK_PTR(q, true);
@@ -597,7 +645,7 @@ prism_status backward_entry(const prism_desc* desc, const void* q, const void* k
       st = check_buffer(saved, saved_bytes, kept_bytes(d, desc->dtype), "saved");
       if (st != PRISM_OK) return st;
     }
-    st = check_buffer(workspace, workspace_bytes, bwd_ws_bytes(d, desc->dtype), "workspace");
+    st = check_buffer(workspace, workspace_bytes, bwd_ws_bytes(d, desc->dtype, train), "workspace");
     if (st != PRISM_OK) return st;
     const void* kept = train ? saved : nullptr;
     if (desc->dtype == PRISM_BF16)

@@ -18,11 +18,18 @@ constexpr int ACT_GELU = 0, ACT_IDENTITY = 1;
 struct Dims {
   int B, T, H, D, L, C, NC, Tp;
   int act, off;
-  // packed batch: sequence b is tokens cu[b] .. cu[b+1]-1 of the [*, H, D]
+  // packed batch: sequence b is tokens cu[b] .. cu[b+1]-1 of the [N, H, D]
   // token tensors (device array of B + 1 offsets, at most T tokens each);
-  // nullptr: dense [B, T, H, D]
+  // nullptr: dense [B, T, H, D].  The kernels read the sanitised copy (every
+  // offset in [0, N], non-decreasing), never the caller's array.
   const int* cu = nullptr;
+  int N = 0;
 };
+
+// Sanitised copy of the packed-batch offsets: out[i] = max_{j <= i}
+// clamp(d.cu[j], 0, d.N), i = 0..B.  Every sequence then lies inside the N
+// rows of the packed tensors and no two overlap, whatever the caller passed.
+hipError_t launch_cu_sanitize(const Dims& d, int* out, hipStream_t s);
 
 // Every launcher enqueues on `stream` and returns hipGetLastError().
 // Element type E is __bf16 or float.

@@ -286,10 +286,13 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
   f32x4 du[2][FPW];
   // Four steps: r^(l-1), kept from the replay of reverse step l for step
   // l - 1 (steps 3 and 1 replay the chain, step 2 takes the kept rows; 4
-  // replayed GELUs instead of 6).  The launcher runs this kernel at L == 4
-  // only.  With three steps the kept rows would spill registers, which
-  // costs what the one saved GELU gains.
+  // replayed GELUs instead of 6).  Only when the instance's step count is
+  // the runtime one (a uniform test): with fewer steps the first reverse
+  // step is not step 3 and the kept rows would be read unwritten.  With
+  // three steps the kept rows would spill registers, which costs what the
+  // one saved GELU gains.
   constexpr bool KEEP = LMAX == 4;
+  const bool keep = KEEP && L == LMAX;
   float rkeep[KEEP ? 2 : 1][FPW][4];
 #pragma unroll
   for (int m = 0; m < 2; ++m)
@@ -317,7 +320,7 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
       for (int m = 0; m < 2; ++m)
 #pragma unroll
         for (int nn = 0; nn < FPW; ++nn) p[m][nn] = ps[l][m][nn];
-      if (KEEP && l >= 1 && ((LMAX - 1 - l) & 1)) {
+      if (keep && l >= 1 && ((LMAX - 1 - l) & 1)) {
         // the previous reverse step replayed through r^(l)
 #pragma unroll
         for (int m = 0; m < 2; ++m)
@@ -335,7 +338,7 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
             for (int i = 0; i < 4; ++i) rl[m][nn][i] = r[m][nn][i];
 #pragma unroll
         for (int j = 0; j < l; ++j) {
-          if (KEEP && j + 1 == l) {   // rl holds r^(l-1) before this last replay step
+          if (keep && j + 1 == l) {   // rl holds r^(l-1) before this last replay step
 #pragma unroll
             for (int m = 0; m < 2; ++m)
 #pragma unroll
@@ -599,6 +602,8 @@ hipError_t launch_refine_bwd_main(const Dims& d, const RefineBwdArgs<E>& a, hipS
   };
   auto by_l = [&](auto dd) {
     constexpr int D = decltype(dd)::value;
+    // L = 3 has its own instance; the LMAX = 4 instance keeps replayed
+    // residuals only when its runtime L is 4 (it also serves no other L here)
     if (d.L <= 2) return go(refine_bwd_kernel<E, D, 2, ACT, OFF>);
     if (d.L == 3) return go(refine_bwd_kernel<E, D, 3, ACT, OFF>);
     if (d.L <= 4) return go(refine_bwd_kernel<E, D, 4, ACT, OFF>);

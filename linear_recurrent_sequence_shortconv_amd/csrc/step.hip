@@ -335,6 +335,36 @@ __global__ void zero_kernel(float* p, long n) {
     p[e] = 0.f;
 }
 
+// One workgroup walks the B + 1 offsets in tiles of 256: clamp into [0, N],
+// then a running maximum (inclusive max-scan in LDS, carried across tiles).
+__global__ __launch_bounds__(256) void cu_sanitize_kernel(const int* __restrict__ cu,
+                                                          int* __restrict__ out, int n, int N) {
+  __shared__ int sm[256];
+  const int tid = threadIdx.x;
+  int carry = 0;
+  for (int base = 0; base < n; base += 256) {
+    const int i = base + tid;
+    int x = i < n ? min(max(cu[i], 0), N) : 0;
+    sm[tid] = x;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+      const int y = tid >= off ? sm[tid - off] : 0;
+      __syncthreads();
+      x = max(x, y);
+      sm[tid] = x;
+      __syncthreads();
+    }
+    if (i < n) out[i] = max(x, carry);
+    carry = max(carry, sm[255]);
+    __syncthreads();
+  }
+}
+
+hipError_t launch_cu_sanitize(const Dims& d, int* out, hipStream_t s) {
+  hipLaunchKernelGGL(cu_sanitize_kernel, dim3(1), dim3(256), 0, s, d.cu, out, d.B + 1, d.N);
+  return hipGetLastError();
+}
+
 static unsigned grid_for(long n) {
   const long g = (n + 255) / 256;
   return (unsigned)(g < 4096 ? (g > 0 ? g : 1) : 4096);

@@ -18,7 +18,8 @@ PRISM_BF16 = 1
 STATUS = {0: "PRISM_OK", 1: "PRISM_ERR_NULL", 2: "PRISM_ERR_SHAPE", 3: "PRISM_ERR_UNSUPPORTED",
           4: "PRISM_ERR_ALIGN", 5: "PRISM_ERR_WORKSPACE", 6: "PRISM_ERR_HIP"}
 
-EXPORTS = ("prism_forward_workspace", "prism_backward_workspace", "prism_forward",
+EXPORTS = ("prism_forward_workspace", "prism_backward_workspace",
+           "prism_forward_train_workspace", "prism_backward_train_workspace", "prism_forward",
            "prism_backward", "prism_saved_bytes", "prism_forward_train", "prism_backward_train",
            "prism_step_workspace", "prism_step", "prism_status_string", "prism_last_error", "prism_timing_begin",
            "prism_timing_end")
@@ -28,7 +29,8 @@ class Desc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int), ("T", ctypes.c_int), ("H", ctypes.c_int),
                 ("dk", ctypes.c_int), ("dv", ctypes.c_int), ("L", ctypes.c_int),
                 ("chunk", ctypes.c_int), ("conv_width", ctypes.c_int), ("dtype", ctypes.c_int),
-                ("activation", ctypes.c_int), ("conv_offset", ctypes.c_int)]
+                ("activation", ctypes.c_int), ("conv_offset", ctypes.c_int),
+                ("packed_tokens", ctypes.c_int)]
 
 
 _lib = None
@@ -46,6 +48,10 @@ def lib():
         L = ctypes.CDLL(LIB_PATH)
         L.prism_forward_workspace.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(ctypes.c_size_t)]
         L.prism_backward_workspace.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(ctypes.c_size_t)]
+        L.prism_forward_train_workspace.argtypes = [ctypes.POINTER(Desc),
+                                                    ctypes.POINTER(ctypes.c_size_t)]
+        L.prism_backward_train_workspace.argtypes = [ctypes.POINTER(Desc),
+                                                     ctypes.POINTER(ctypes.c_size_t)]
         # inputs q..conv, S0, conv_hist, cu_seqlens (12); forward outputs o, ST,
         # conv_hist_out (3); backward: dO, dST, then 11 gradients (dq..dconv, dS0, dconv_hist)
         L.prism_forward.argtypes = [ctypes.POINTER(Desc)] + [_P] * 15 + [_P, ctypes.c_size_t, _P]
@@ -57,7 +63,8 @@ def lib():
                                            + [_P] * 13 + [_P, ctypes.c_size_t, _P])
         L.prism_step_workspace.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(ctypes.c_size_t)]
         L.prism_step.argtypes = [ctypes.POINTER(Desc)] + [_P] * 12 + [_P, ctypes.c_size_t, _P]
-        for f in ("prism_forward_workspace", "prism_backward_workspace", "prism_forward",
+        for f in ("prism_forward_workspace", "prism_backward_workspace",
+                  "prism_forward_train_workspace", "prism_backward_train_workspace", "prism_forward",
                   "prism_backward", "prism_saved_bytes", "prism_forward_train",
                   "prism_backward_train", "prism_step_workspace", "prism_step"):
             getattr(L, f).restype = ctypes.c_int
@@ -74,11 +81,12 @@ def lib():
 ACTIVATIONS = {"gelu": 0, "identity": 1}
 
 
-def make_desc(B, T, H, dk, dv, L, chunk, dtype, conv_width=4, activation="gelu", conv_offset=0):
+def make_desc(B, T, H, dk, dv, L, chunk, dtype, conv_width=4, activation="gelu", conv_offset=0,
+              packed_tokens=0):
     if activation not in ACTIVATIONS:
         raise ValueError(f"activation must be one of {sorted(ACTIVATIONS)}, got {activation!r}")
     return Desc(B, T, H, dk, dv, L, chunk, conv_width, dtype, ACTIVATIONS[activation],
-                int(conv_offset))
+                int(conv_offset), int(packed_tokens))
 
 
 def _check(status):
@@ -111,18 +119,52 @@ def _req(t, name, dtype, device):
 def _desc_from(q, v, Wk, chunk, activation="gelu", conv_offset=0, cu_seqlens=None,
                max_seqlen=None):
     """Descriptor of a dense batch (q [B,T,H,dk]) or, with cu_seqlens, of a
-    packed one (q [N,H,dk], B = len(cu_seqlens) - 1, T = max_seqlen)."""
+    packed one (q [N,H,dk], B = len(cu_seqlens) - 1, T = max_seqlen, N rows)."""
+    N = 0
     if cu_seqlens is None:
+        if q.dim() != 4:
+            raise ValueError(f"q: expected [B, T, H, dk], got shape {tuple(q.shape)}")
         B, T, H, dk = q.shape
     else:
         if max_seqlen is None:
             raise ValueError("max_seqlen is required with cu_seqlens")
-        _, H, dk = q.shape
+        N, H, dk = q.shape
         B, T = cu_seqlens.numel() - 1, int(max_seqlen)
     dv = v.shape[-1]
     L = 0 if Wk is None else Wk.shape[1]
     return make_desc(B, T, H, dk, dv, L, chunk, _dtype_code(q), activation=activation,
-                     conv_offset=conv_offset)
+                     conv_offset=conv_offset, packed_tokens=N)
+
+
+def _shape(t, name, shape):
+    if t is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+def _check_shapes(desc, packed, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0, extra=(),
+                  state_name="S0"):
+    """Every tensor's shape against the descriptor, on the host, before the
+    library sees a pointer: the C ABI cannot see shapes, and a wrong one
+    would make the kernels read or write outside the tensor."""
+    B, T, H, d, L = desc.B, desc.T, desc.H, desc.dk, desc.L
+    tok = (desc.packed_tokens, H) if packed else (B, T, H)
+    _shape(k, "k", tok + (d,))
+    _shape(v, "v", tok + (d,))
+    _shape(alpha, "alpha", tok)
+    _shape(beta, "beta", tok)
+    if L > 0:
+        _shape(Wk, "Wk", (H, L, d, d))
+        _shape(Wp, "Wp", (H, L, d, d))
+        _shape(wbeta, "wbeta", (H, L, d))
+        _shape(conv, "conv", (H, d, 4))
+    _shape(S0, state_name, (B, H, d, d))
+    for name, t, kind in extra:
+        _shape(t, name, tok + (d,) if kind == "tok" else (B, H, d, d))
+
+
+def _on_gpu(q):
+    if q.device.type != "cuda":
+        raise ValueError(f"tensors must be on a GPU device, got {q.device}")
 
 
 def _req_cu(cu, q):
@@ -149,6 +191,18 @@ def forward_workspace_bytes(desc):
 def backward_workspace_bytes(desc):
     n = ctypes.c_size_t(0)
     _check(lib().prism_backward_workspace(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def forward_train_workspace_bytes(desc):
+    n = ctypes.c_size_t(0)
+    _check(lib().prism_forward_train_workspace(ctypes.byref(desc), ctypes.byref(n)))
+    return n.value
+
+
+def backward_train_workspace_bytes(desc):
+    n = ctypes.c_size_t(0)
+    _check(lib().prism_backward_train_workspace(ctypes.byref(desc), ctypes.byref(n)))
     return n.value
 
 
@@ -203,13 +257,15 @@ def forward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None, S0=No
     _validate_inputs(q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0)
     _req_cu(cu_seqlens, q)
     desc = _desc_from(q, v, Wk, chunk, activation, conv_offset, cu_seqlens, max_seqlen)
+    _check_shapes(desc, cu_seqlens is not None, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0)
     B, H, dk, dv = desc.B, desc.H, desc.dk, desc.dv
     for name, h in (("conv_hist", conv_hist), ("conv_hist_out", conv_hist_out)):
         if h is not None:
             _req_hist(h, name, q, v, B)
+    _on_gpu(q)
     o = torch.empty_like(v)
     ST = torch.empty((B, H, dv, dk), dtype=torch.float32, device=q.device)
-    need = forward_workspace_bytes(desc)
+    need = forward_workspace_bytes(desc) if saved is None else forward_train_workspace_bytes(desc)
     if workspace is None:
         _, ws = _workspace(need, q.device)
     else:
@@ -258,11 +314,14 @@ def backward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None, S0=N
     _req(dO, "dO", q.dtype, q.device)
     _req_cu(cu_seqlens, q)
     desc = _desc_from(q, v, Wk, chunk, activation, conv_offset, cu_seqlens, max_seqlen)
+    if dST is not None:
+        _req(dST, "dST", torch.float32, q.device)
+    _check_shapes(desc, cu_seqlens is not None, k, v, alpha, beta, Wk, Wp, wbeta, conv, S0,
+                  extra=(("dO", dO, "tok"), ("dST", dST, "state")))
     B, H, dk, dv_ = desc.B, desc.H, desc.dk, desc.dv
     if conv_hist is not None:
         _req_hist(conv_hist, "conv_hist", q, v, B)
-    if dST is not None:
-        _req(dST, "dST", torch.float32, q.device)
+    _on_gpu(q)
     dev = q.device
     g = {"dq": torch.empty_like(q), "dk": torch.empty_like(k), "dv": torch.empty_like(v),
          "dalpha": torch.empty_like(alpha), "dbeta": torch.empty_like(beta)}
@@ -275,7 +334,7 @@ def backward(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None, S0=N
         g["dS0"] = torch.empty((B, H, dv_, dk), dtype=torch.float32, device=dev)
     if need_dconv_hist:
         g["dconv_hist"] = torch.empty((B, 4, H, dv_), dtype=torch.float32, device=dev)
-    need = backward_workspace_bytes(desc)
+    need = backward_workspace_bytes(desc) if saved is None else backward_train_workspace_bytes(desc)
     if workspace is None:
         _, ws = _workspace(need, dev)
     else:
@@ -313,12 +372,11 @@ def step(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None, S=None, 
     _validate_inputs(q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S)
     if S is None:
         raise ValueError("S is required")
-    B, T, H, dk = q.shape
-    if tuple(S.shape) != (B, H, v.shape[-1], dk):
-        raise ValueError(f"S: expected shape {(B, H, v.shape[-1], dk)}, got {tuple(S.shape)}")
+    desc = _desc_from(q, v, Wk, 16, activation, conv_offset)
+    _check_shapes(desc, False, k, v, alpha, beta, Wk, Wp, wbeta, conv, S, state_name="S")
     if conv_state is not None:
         _req_hist(conv_state, "conv_state", q, v)
-    desc = _desc_from(q, v, Wk, 16, activation, conv_offset)
+    _on_gpu(q)
     o = torch.empty_like(v)
     if workspace is None:
         _, workspace = _workspace(step_workspace_bytes(desc), q.device)

@@ -240,3 +240,40 @@ def test_step_checks():
     assert L.prism_step(ctypes.byref(d), *([fake] * 12), fake, ctypes.c_size_t(need - 1),
                         None) == E_WS
     assert P.step_workspace_bytes(good_desc(T=1, L=0)) == 0
+
+
+def test_train_workspaces():
+    """The training pair keeps the forward intermediates in its saved buffer,
+    so its workspaces are smaller than the stateless ones; the train entry
+    points accept exactly their own size."""
+    L = P.lib()
+    d = good_desc(T=2048, dk=128, dv=128, L=3)
+    f, b = P.forward_workspace_bytes(d), P.backward_workspace_bytes(d)
+    ft, bt = P.forward_train_workspace_bytes(d), P.backward_train_workspace_bytes(d)
+    assert 0 < ft < f and 0 < bt < b
+    fake = ctypes.c_void_p(0x10000)
+    need = P.saved_bytes(d)
+    p15 = [fake] * 15
+    assert L.prism_forward_train(ctypes.byref(d), *p15, fake, ctypes.c_size_t(need), fake,
+                                 ctypes.c_size_t(ft - 1), None) == E_WS
+    assert str(ft) in _err()
+    p12, p13 = [fake] * 12, [fake] * 13
+    assert L.prism_backward_train(ctypes.byref(d), *p12, fake, ctypes.c_size_t(need), *p13, fake,
+                                  ctypes.c_size_t(bt - 1), None) == E_WS
+    assert str(bt) in _err()
+    n = ctypes.c_size_t(7)
+    assert L.prism_forward_train_workspace(ctypes.byref(good_desc(B=0)), ctypes.byref(n)) == E_SHAPE
+    assert n.value == 0
+    assert L.prism_backward_train_workspace(ctypes.byref(d), None) == E_NULL
+
+
+def test_packed_tokens_checked():
+    """With cu_seqlens the packed row count N (packed_tokens) must be >= 0;
+    without offsets the field is ignored."""
+    fake = ctypes.c_void_p(0x10000)
+    d = good_desc()
+    d.packed_tokens = -1
+    p = [fake] * 15
+    assert _fwd(d, p) == E_SHAPE and "packed_tokens" in _err()
+    p[11] = None                     # dense batch: the field is not used
+    assert _fwd(d, p, nbytes=0) == E_WS

@@ -99,3 +99,33 @@ def test_summarize_profiles_scales_counters_by_the_copy(tmp_path, monkeypatch):
     assert "| wgrad_reduce | 4 | 100.0 |" in md
     # 0.512 GFLOP; 5.12 TFLOP/s; 0.512e9 / 2.5e15 / 1e-4 s = 0.002048 of the bf16 pipe
     assert "| wgrad_reduce | 0.5 | 0.00 |" in md and "| 5 | 0.002 | 0.250 |" in md
+
+
+def test_cpu_baseline_process_pool():
+    """The oracle baseline runs whole sequences in a pool of spawned worker
+    processes and reports the workers it used and the CPU model."""
+    import bench
+    from linear_recurrent_sequence_shortconv_amd.workloads import make_workload_inputs, workloads
+    w = workloads()["tiny-fp32"]
+    x = make_workload_inputs(w, seed=0)
+    r = bench.cpu_baseline(w, x, budget_s=0.5, backward=True, max_workers=2)
+    assert r["kind"] == "oracle" and r["unit"] == "tokens/s" and r["value"] > 0
+    assert 1 <= r["cores"] <= 2 and isinstance(r["cpu_model"], str) and r["cpu_model"]
+    assert "1 of 1 (b,h) sequences" in r["sample"]
+
+
+def test_stage_fractions():
+    import bench
+    from linear_recurrent_sequence_shortconv_amd.workloads import workloads
+    w = workloads()["lm-T2048"]
+    counts = bench.algorithmic_counts(w)
+    kernels = {n: {"total_ms": 0.5, "launches_per_step": 1} for n in
+               bench.SCAN_KERNELS + bench.REFINE_KERNELS}
+    st = bench.stage_fractions(kernels, counts, "bf16")
+    fl = sum(counts[n]["flops"] for n in bench.SCAN_KERNELS)
+    t = 0.5e-3 * len(bench.SCAN_KERNELS)
+    assert abs(st["scan"]["mfma_frac"] - fl / t / 2.5e15) < 1e-4
+    by = sum(counts[n]["bytes"] for n in bench.REFINE_KERNELS)
+    t = 0.5e-3 * len(bench.REFINE_KERNELS)
+    assert abs(st["refinement"]["hbm_frac"] - by / t / 8e12) < 1e-4
+    assert st["scan"]["target_mfma_frac"] == 0.40 and st["refinement"]["target_hbm_frac"] == 0.60

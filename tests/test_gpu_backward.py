@@ -13,6 +13,7 @@ import torch
 
 from oracle import prism_oracle as O
 from linear_recurrent_sequence_shortconv_amd.workloads import make_inputs, workloads
+from tests.parity import relerr
 
 pytestmark = pytest.mark.gpu
 
@@ -44,10 +45,6 @@ def oracle_backward(x, L, sl_b=slice(None), sl_h=slice(None)):
     dst = None if x["dST"] is None else x["dST"][sl_b, sl_h]
     return O.backward(s("q"), s("k"), s("v"), s("alpha"), s("beta"), *W, S0=s0, dO=s("dO"),
                       dST=dst, segment=64)
-
-
-def relerr(x, y):
-    return float(np.max(np.abs(x - y)) / max(np.max(np.abs(y)), 1e-30))
 
 
 def _compare(gg, go, names, tol, tag=""):
@@ -136,9 +133,20 @@ def test_lm_workload_backward():
     _check_workload("lm-T2048", [(0, 0), (5, 9)], weight_head=3)
 
 
-@pytest.mark.parametrize("L", [0, 8])
+@pytest.mark.parametrize("L", [0, 1, 2, 4, 8])
 def test_depth_backward(L):
+    """Refinement-depth sweep at its own shape (B = 4, T = 4096, d = 128):
+    every refinement-backward instance (two, three, four and eight steps)."""
     _check_workload(f"depth-L{L}", [(1, 2)], weight_head=14)
+
+
+@pytest.mark.parametrize("T", [4096, 8192, 16384])
+def test_long_context_backward(T):
+    """Long-context sweep (B = 16384 / T): the reverse state pass runs over
+    up to 256 chunks with 16-row state blocks (B H = 16 at T = 16384); the
+    last sequence's gradients and dS0, one head's weight and tap gradients."""
+    B = 16384 // T
+    _check_workload(f"long-T{T}", [(B - 1, 5)], weight_head=9)
 
 
 def test_backward_deterministic():

@@ -13,6 +13,7 @@ import torch
 
 from oracle import prism_oracle as O
 from linear_recurrent_sequence_shortconv_amd.workloads import make_inputs, workloads
+from tests.parity import relerr
 
 pytestmark = pytest.mark.gpu
 
@@ -51,10 +52,6 @@ def oracle_forward(x, L, b=None, h=None):
         outs.append(o[0, :, 0])
         states.append(s[0, 0])
     return np.stack(outs), np.stack(states)
-
-
-def relerr(x, y):
-    return float(np.max(np.abs(x - y)) / max(np.max(np.abs(y)), 1e-30))
 
 
 def _check_full(x, dtype, chunk, L, tol=None):
@@ -146,10 +143,16 @@ def test_lm_workload_sampled():
     _check_sampled("lm-T2048", [(0, 0), (3, 7), (7, 15)])
 
 
-def test_long_T16384_sampled():
-    _check_sampled("long-T16384", [(0, 0), (0, 11)])
+@pytest.mark.parametrize("T", [4096, 8192, 16384])
+def test_long_context_sampled(T):
+    """Long-context sweep (B = 16384 / T, H = 16, d = 128, L = 3): the first
+    and the last sequence of the batch."""
+    B = 16384 // T
+    _check_sampled(f"long-T{T}", [(0, 0), (B - 1, 11)])
 
 
-@pytest.mark.parametrize("L", [0, 8])
+@pytest.mark.parametrize("L", [0, 1, 2, 4, 8])
 def test_depth_sampled(L):
+    """Refinement-depth sweep (B = 4, T = 4096, H = 16, d = 128); L = 0 is the
+    Gated-DeltaNet path."""
     _check_sampled(f"depth-L{L}", [(0, 3), (3, 12)])

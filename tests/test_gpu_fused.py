@@ -18,6 +18,7 @@ import torch
 
 from oracle import prism_oracle as O
 from linear_recurrent_sequence_shortconv_amd.workloads import make_inputs
+from tests.parity import relerr
 
 pytestmark = pytest.mark.gpu
 
@@ -27,10 +28,6 @@ WN = ("Wk", "Wp", "wbeta", "conv")
 
 def _dev(a, dtype):
     return torch.from_numpy(np.ascontiguousarray(a)).to("cuda").to(dtype)
-
-
-def relerr(x, y):
-    return float(np.max(np.abs(x - y)) / max(np.max(np.abs(y)), 1e-30))
 
 
 def _args(x, dtype):

@@ -13,6 +13,7 @@ import torch
 
 from oracle import prism_oracle as O
 from linear_recurrent_sequence_shortconv_amd.workloads import make_inputs
+from tests.parity import relerr
 
 pytestmark = pytest.mark.gpu
 
@@ -27,10 +28,6 @@ def _dev(a, dtype):
 
 def _np(t):
     return t.double().cpu().numpy()
-
-
-def relerr(x, y):
-    return float(np.max(np.abs(x - y)) / max(np.max(np.abs(y)), 1e-30))
 
 
 def _hist(B, H, d, dtype, seed):

@@ -12,6 +12,7 @@ import torch
 
 from oracle import prism_oracle as O
 from linear_recurrent_sequence_shortconv_amd.workloads import make_inputs, workloads
+from tests.parity import relerr
 
 pytestmark = pytest.mark.gpu
 
@@ -42,10 +43,6 @@ def train_pair(x, dtype, chunk, L):
                    chunk=chunk, need_dS0=True, saved=saved)
     torch.cuda.synchronize()
     return o, ST, g
-
-
-def relerr(x, y):
-    return float(np.max(np.abs(x - y)) / max(np.max(np.abs(y)), 1e-30))
 
 
 @pytest.mark.parametrize("dtype,d,chunk", [("f32", 32, 32), ("bf16", 128, 64), ("bf16", 64, 16)])
@@ -80,19 +77,31 @@ def test_train_backward_matches_oracle(dtype, d, chunk, L):
 
 
 def test_train_pair_lm_workload_sampled():
+    """The timed training pair at its full size (B=8, H=16, T=2048, d=128,
+    L=3): two sequences' gradients and dS0, and one head's weight and tap
+    gradients (sums over all eight sequences of that head)."""
     w = workloads()["lm-T2048"]
     x = make_inputs(w.B, w.T, w.H, w.d, w.L, w.dtype, seed=0)
-    print(f"\n[{w.name} train pair, sequences (3,7), (6,12)]", flush=True)
+    print(f"\n[{w.name} train pair, sequences (3,7), (6,12), weights of head 12]", flush=True)
     _, _, g = train_pair(x, w.dtype, w.chunk, w.L)
-    for n in SEQ_GRADS:
-        assert np.all(np.isfinite(g[n].float().cpu().numpy())), n
+    g = {n: t.double().cpu().numpy() for n, t in g.items()}
+    for n in SEQ_GRADS + W_GRADS + ("dS0",):
+        assert np.all(np.isfinite(g[n])), n
     for b, h in [(3, 7), (6, 12)]:
         s = lambda n: x[n][b:b + 1, :, h:h + 1]
         Wn = [x[n][h:h + 1] for n in ("Wk", "Wp", "wbeta", "conv")]
         go = O.backward(s("q"), s("k"), s("v"), s("alpha"), s("beta"), *Wn, dO=s("dO"))
-        errs = {n: relerr(g[n][b:b + 1, :, h:h + 1].double().cpu().numpy(), go[n]) for n in SEQ_GRADS}
+        errs = {n: relerr(g[n][b:b + 1, :, h:h + 1], go[n]) for n in SEQ_GRADS}
+        errs["dS0"] = relerr(g["dS0"][b:b + 1, h:h + 1], go["dS0"])
         print(f"  (b={b},h={h}) " + "  ".join(f"{n} {e:.2e}" for n, e in errs.items()), flush=True)
         assert all(e <= TOL[w.dtype] for e in errs.values()), errs
+    hh = 12
+    s = lambda n: x[n][:, :, hh:hh + 1]
+    Wn = [x[n][hh:hh + 1] for n in ("Wk", "Wp", "wbeta", "conv")]
+    go = O.backward(s("q"), s("k"), s("v"), s("alpha"), s("beta"), *Wn, dO=s("dO"))
+    errs = {n: relerr(g[n][hh:hh + 1], go[n]) for n in W_GRADS}
+    print(f"  (weights, h={hh}) " + "  ".join(f"{n} {e:.2e}" for n, e in errs.items()), flush=True)
+    assert all(e <= TOL[w.dtype] for e in errs.values()), errs
 
 
 @pytest.mark.parametrize("B,H", [(1, 4), (4, 16), (8, 16)], ids=["rows16", "rows32", "rows64"])

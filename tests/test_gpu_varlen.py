@@ -15,6 +15,7 @@ import torch
 
 from oracle import prism_oracle as O
 from linear_recurrent_sequence_shortconv_amd.workloads import make_inputs
+from tests.parity import relerr
 
 pytestmark = pytest.mark.gpu
 
@@ -30,10 +31,6 @@ def _dev(a, dtype):
 
 def _np(t):
     return t.double().cpu().numpy()
-
-
-def relerr(x, y):
-    return float(np.max(np.abs(x - y)) / max(np.max(np.abs(y)), 1e-30))
 
 
 def _packed(lengths, H, d, L, dtype, seed):
@@ -138,3 +135,29 @@ def test_equal_lengths_packed_is_dense_bitwise():
     for n in g1:
         a, b = g1[n], g2[n]
         assert torch.equal(a.reshape(b.shape), b), n
+
+
+def test_out_of_contract_offsets_are_clamped():
+    """Offsets outside the contract (negative, decreasing, past the N packed
+    rows) are sanitised on the device into [0, N] and made non-decreasing
+    before any kernel reads them: the call gives exactly the results of the
+    clamped offsets, and nothing is read or written outside the N rows."""
+    from linear_recurrent_sequence_shortconv_amd import prism as P
+    N, H, d, L, Tmax = 150, 2, 64, 2, 100
+    x = make_inputs(1, N, H, d, L, "bf16", seed=77, with_dST=False)
+    t, f = torch.bfloat16, torch.float32
+    tok = lambda n, ty: _dev(x[n][0], ty)
+    args = (tok("q", t), tok("k", t), tok("v", t), tok("alpha", f), tok("beta", f)) + tuple(
+        _dev(x[n], t) for n in WN)
+    dO = tok("dO", t)
+    bad = torch.tensor([-5, 70, 40, 500], dtype=torch.int32, device="cuda")
+    good = torch.tensor([0, 70, 70, 150], dtype=torch.int32, device="cuda")
+    out = {}
+    for name, cu in (("bad", bad), ("good", good)):
+        kw = dict(chunk=32, cu_seqlens=cu, max_seqlen=Tmax)
+        o, ST = P.forward(*args, **kw)
+        g = P.backward(*args, dO=dO, need_dS0=True, **kw)
+        out[name] = dict(o=o, ST=ST, **g)
+    torch.cuda.synchronize()
+    for n in out["good"]:
+        assert torch.equal(out["bad"][n], out["good"][n]), n
