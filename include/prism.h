@@ -233,6 +233,28 @@ prism_status prism_step(const prism_desc* desc, const void* q, const void* k, co
                         const void* wbeta, const void* conv, float* S, void* conv_state, void* o,
                         void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/* prism_step without a workspace, for callers that cannot allocate device
+ * memory (code under graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same arguments, results and errors as prism_step,
+ * except that the refinement pairs of the tokens go to a fixed device array
+ * inside the library instead of a caller workspace:
+ *   - the array holds 16 MiB per GPU (2 * B * H * L * T * dv elements of dt,
+ *     each half rounded up to 256 bytes, must fit; e.g. B = 512, H = 16,
+ *     L = 3, T = 1, dv = 128 in bf16); a larger call returns
+ *     PRISM_ERR_WORKSPACE before any HIP call;
+ *   - each GPU the library runs on keeps its own copy until the process
+ *     ends; the call uses the copy of the device `stream` belongs to;
+ *   - nothing is allocated or freed (no hipMalloc, hipFree or allocating
+ *     library call): every pair the state kernel reads is written first by
+ *     the same call, so the array needs no clearing between calls;
+ *   - calls that overlap in time on one GPU (different streams, or several
+ *     threads) share the array and race: serialise them. */
+prism_status prism_step_noalloc(const prism_desc* desc, const void* q, const void* k,
+                                const void* v, const float* alpha, const float* beta,
+                                const void* Wk, const void* Wp, const void* wbeta,
+                                const void* conv, float* S, void* conv_state, void* o,
+                                hipStream_t stream);
+
 /* Human-readable name of a status code (static string). */
 const char* prism_status_string(prism_status status);
 

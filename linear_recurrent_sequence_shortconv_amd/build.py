@@ -32,6 +32,7 @@ SOURCES = [
     "state.hip",
     "step.hip",
     "refine_bwd.hip",
+    "noalloc.hip",
     "prism_api.cpp",
 ]
 

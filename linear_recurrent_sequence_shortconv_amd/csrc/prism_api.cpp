@@ -724,10 +724,18 @@ prism_status prism_step_workspace(const prism_desc* desc, size_t* bytes) {
   return PRISM_OK;
 }
 
-prism_status prism_step(const prism_desc* desc, const void* q, const void* k, const void* v,
+}  // extern "C"
+
+namespace {
+
+// prism_step and prism_step_noalloc: the same checks and kernels; the
+// refinement pairs go to the caller's workspace or (noalloc) to the fixed
+// device array of noalloc.hip.
+prism_status step_entry(const prism_desc* desc, const void* q, const void* k, const void* v,
                         const float* alpha, const float* beta, const void* Wk, const void* Wp,
                         const void* wbeta, const void* conv, float* S, void* conv_state, void* o,
-                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+                        void* workspace, size_t workspace_bytes, bool noalloc,
+                        hipStream_t stream) {
   try {
     g_err.clear();
     prism::Dims d;
@@ -747,7 +755,19 @@ prism_status prism_step(const prism_desc* desc, const void* q, const void* k, co
     CHECK_PTR(conv_state, false);
     CHECK_PTR(o, true);
     const size_t need = step_ws_bytes(d, desc->dtype);
-    if (need > 0) {
+    if (noalloc) {
+      if (need > prism::NOALLOC_SCRATCH_BYTES)
+        return fail(PRISM_ERR_WORKSPACE,
+                    "prism_step_noalloc: the refinement pairs of B * H * L * T * D elements need " +
+                        std::to_string(need) + " bytes; its fixed device array holds " +
+                        std::to_string(prism::NOALLOC_SCRATCH_BYTES) + " (use prism_step)");
+      if (need > 0) {
+        const hipError_t e = prism::noalloc_scratch(stream, &workspace);
+        if (e != hipSuccess)
+          return fail(PRISM_ERR_HIP, std::string("prism_step_noalloc: device array address: ") +
+                                         hipGetErrorString(e));
+      }
+    } else if (need > 0) {
       st = check_buffer(workspace, workspace_bytes, need, "workspace");
       if (st != PRISM_OK) return st;
     }
@@ -762,6 +782,27 @@ prism_status prism_step(const prism_desc* desc, const void* q, const void* k, co
   } catch (...) {
     return fail(PRISM_ERR_HIP, "unexpected host exception");
   }
+}
+
+}  // namespace
+
+extern "C" {
+
+prism_status prism_step(const prism_desc* desc, const void* q, const void* k, const void* v,
+                        const float* alpha, const float* beta, const void* Wk, const void* Wp,
+                        const void* wbeta, const void* conv, float* S, void* conv_state, void* o,
+                        void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return step_entry(desc, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S, conv_state, o, workspace,
+                    workspace_bytes, false, stream);
+}
+
+prism_status prism_step_noalloc(const prism_desc* desc, const void* q, const void* k,
+                                const void* v, const float* alpha, const float* beta,
+                                const void* Wk, const void* Wp, const void* wbeta,
+                                const void* conv, float* S, void* conv_state, void* o,
+                                hipStream_t stream) {
+  return step_entry(desc, q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S, conv_state, o, nullptr, 0,
+                    true, stream);
 }
 
 void prism_timing_begin(void) {

@@ -133,6 +133,12 @@ int refine_bwd_tiles(const Dims& d);    // token tiles per sequence (rows of the
 template <typename E>
 hipError_t launch_conv_state(const Dims& d, const E* v, const E* hist, E* out, hipStream_t s);
 
+// Bytes of the fixed device array behind prism_step_noalloc (the refinement
+// pairs of the recurrent step), and its device address on the device of
+// `stream` (looked up once per device; see noalloc.hip).
+constexpr size_t NOALLOC_SCRATCH_BYTES = size_t(16) << 20;
+hipError_t noalloc_scratch(hipStream_t stream, void** ptr);
+
 // Zero n floats (a kernel, so that the call may be captured in a graph).
 hipError_t launch_zero(float* p, long n, hipStream_t s);
 

@@ -21,7 +21,7 @@ STATUS = {0: "PRISM_OK", 1: "PRISM_ERR_NULL", 2: "PRISM_ERR_SHAPE", 3: "PRISM_ER
 EXPORTS = ("prism_forward_workspace", "prism_backward_workspace",
            "prism_forward_train_workspace", "prism_backward_train_workspace", "prism_forward",
            "prism_backward", "prism_saved_bytes", "prism_forward_train", "prism_backward_train",
-           "prism_step_workspace", "prism_step", "prism_status_string", "prism_last_error", "prism_timing_begin",
+           "prism_step_workspace", "prism_step", "prism_step_noalloc", "prism_status_string", "prism_last_error", "prism_timing_begin",
            "prism_timing_end")
 
 
@@ -63,10 +63,12 @@ def lib():
                                            + [_P] * 13 + [_P, ctypes.c_size_t, _P])
         L.prism_step_workspace.argtypes = [ctypes.POINTER(Desc), ctypes.POINTER(ctypes.c_size_t)]
         L.prism_step.argtypes = [ctypes.POINTER(Desc)] + [_P] * 12 + [_P, ctypes.c_size_t, _P]
+        L.prism_step_noalloc.argtypes = [ctypes.POINTER(Desc)] + [_P] * 12 + [_P]
         for f in ("prism_forward_workspace", "prism_backward_workspace",
                   "prism_forward_train_workspace", "prism_backward_train_workspace", "prism_forward",
                   "prism_backward", "prism_saved_bytes", "prism_forward_train",
-                  "prism_backward_train", "prism_step_workspace", "prism_step"):
+                  "prism_backward_train", "prism_step_workspace", "prism_step",
+                  "prism_step_noalloc"):
             getattr(L, f).restype = ctypes.c_int
         L.prism_status_string.argtypes = [ctypes.c_int]
         L.prism_status_string.restype = ctypes.c_char_p
@@ -363,12 +365,14 @@ def step_workspace_bytes(desc):
 
 
 def step(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None, S=None, conv_state=None,
-         activation="gelu", conv_offset=0, workspace=None):
+         activation="gelu", conv_offset=0, workspace=None, noalloc=False):
     """Recurrent form (prism_step): the T tokens of each sequence in order,
     token by token.  S [B,H,dv,dk] fp32 is required and updated in place
     (S_0 in, S_T out); conv_state [B,4,H,dv] (v's dtype) likewise, or None
     for a zero history that is not kept.  Returns o [B,T,H,dv].  With T = 1
-    this is one decode step."""
+    this is one decode step.  noalloc=True calls prism_step_noalloc (the
+    pairs go to the library's fixed device array; no workspace, nothing
+    allocated but the output)."""
     _validate_inputs(q, k, v, alpha, beta, Wk, Wp, wbeta, conv, S)
     if S is None:
         raise ValueError("S is required")
@@ -378,9 +382,14 @@ def step(q, k, v, alpha, beta, Wk=None, Wp=None, wbeta=None, conv=None, S=None, 
         _req_hist(conv_state, "conv_state", q, v)
     _on_gpu(q)
     o = torch.empty_like(v)
+    stream = torch.cuda.current_stream(q.device).cuda_stream
+    if noalloc:
+        _check(lib().prism_step_noalloc(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
+                                        _ptr(beta), _ptr(Wk), _ptr(Wp), _ptr(wbeta), _ptr(conv),
+                                        _ptr(S), _ptr(conv_state), _ptr(o), ctypes.c_void_p(stream)))
+        return o
     if workspace is None:
         _, workspace = _workspace(step_workspace_bytes(desc), q.device)
-    stream = torch.cuda.current_stream(q.device).cuda_stream
     _check(lib().prism_step(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(alpha),
                             _ptr(beta), _ptr(Wk), _ptr(Wp), _ptr(wbeta), _ptr(conv), _ptr(S),
                             _ptr(conv_state), _ptr(o), _ptr(workspace),

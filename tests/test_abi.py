@@ -277,3 +277,18 @@ def test_packed_tokens_checked():
     assert _fwd(d, p) == E_SHAPE and "packed_tokens" in _err()
     p[11] = None                     # dense batch: the field is not used
     assert _fwd(d, p, nbytes=0) == E_WS
+
+
+def test_step_noalloc_checks():
+    """prism_step_noalloc validates like prism_step and refuses, before any
+    HIP call, a call whose refinement pairs exceed its fixed 16 MiB array."""
+    L = P.lib()
+    fake = ctypes.c_void_p(0x10000)
+    d = P.make_desc(4096, 1, 16, 128, 128, 8, 16, P.PRISM_BF16)
+    assert P.step_workspace_bytes(d) > (16 << 20)
+    assert L.prism_step_noalloc(ctypes.byref(d), *([fake] * 12), None) == E_WS
+    assert "fixed device array" in _err()
+    p = [fake] * 12
+    p[9] = None
+    assert L.prism_step_noalloc(ctypes.byref(good_desc(T=1)), *p, None) == E_NULL and "S" in _err()
+    assert L.prism_step_noalloc(ctypes.byref(good_desc(T=1, L=9)), *([fake] * 12), None) == E_UNSUP
