@@ -260,15 +260,21 @@ def summarize_profiles(d, workload):
         "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/cfetch -o run -- python -u $R/bench.py --calibrate-copy",
         "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/cwrite -o run -- python -u $R/bench.py --calibrate-copy",
         f"cd /tmp && rocprofv3 --pmc {' '.join(MFMA_COUNTERS)} --output-format csv -d $OUT/mfma -o run -- python -u $R/bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-varlen",
+        f"cd /tmp && rocprofv3 --pmc {' '.join(ISSUE_COUNTERS)} --output-format csv -d $OUT/issue -o run -- python -u $R/bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-varlen",
+        f"cd /tmp && rocprofv3 --pmc {' '.join(LDS_COUNTERS)} --output-format csv -d $OUT/ldsq -o run -- python -u $R/bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-varlen",
         f"python bench.py --summarize-profiles $OUT --workload {workload}",
     ]
     mfma_csv = os.path.join(d, "mfma", "run_counter_collection.csv")
     mfma_lines, mfma_rec = (_mfma_table(mfma_csv, times, names_of, counts)
                             if os.path.exists(mfma_csv) else ([], {}))
+    ia = os.path.join(d, "issue", "run_counter_collection.csv")
+    ib = os.path.join(d, "ldsq", "run_counter_collection.csv")
+    issue_lines, issue_rec = (_issue_table(ia, ib, times, names_of)
+                              if os.path.exists(ia) else ([], {}))
     rec = {"workload": workload, "sources_sha256": _sources_sha256(),
            "calibration": {"fetch_factor": round(f_factor, 4), "write_factor": round(w_factor, 4),
                            "copy_bytes": 1 << 30},
-           "commands": cmds, "kernels": traffic, "mfma": mfma_rec}
+           "commands": cmds, "kernels": traffic, "mfma": mfma_rec, "issue": issue_rec}
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     with open(os.path.join(ROOT, "profiles", "hbm_traffic.json"), "w") as f:
         json.dump(rec, f, indent=1)
@@ -297,9 +303,80 @@ def summarize_profiles(d, workload):
                           f"{(meas / c['bytes']) if meas else float('nan'):.2f} | {gbs:.0f} | {gbs / HBM_PEAK_GBS:.3f} |"))
     lines += [r for _, r in sorted(rows, reverse=True)]
     lines += mfma_lines
+    lines += issue_lines
     with open(os.path.join(ROOT, "profiles", f"{workload}_kernels.md"), "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+# Issue and LDS counters (gfx950), two rocprofv3 --pmc runs (at most 8 SQ
+# counters each).  SQ_WAVE_CYCLES, SQ_WAIT_ANY and SQ_WAIT_INST_ANY are in
+# quad-cycles; instruction counts are summed over the shader engines.
+ISSUE_COUNTERS = ["SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_INSTS_VALU",
+                  "SQ_INSTS_LDS", "SQ_INSTS_SALU", "SQ_INSTS_VMEM"]
+LDS_COUNTERS = ["SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_VALU",
+                "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_ANY", "GRBM_GUI_ACTIVE"]
+CLOCK_GHZ = 2.4
+
+
+def _issue_table(path_a, path_b, times, names_of):
+    """Markdown lines and a per-timer-name record from the issue / LDS counter
+    runs: VALU, LDS, SALU, VMEM instructions per wave; the fraction of wave
+    time spent waiting for anything (SQ_WAIT_ANY / SQ_WAVE_CYCLES) and for an
+    instruction to issue (SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES); `VALU issue` =
+    SQ_INSTS_VALU x 4 cycles (a wave64 instruction on a 16-lane SIMD) over
+    the kernel-trace duration x 1024 SIMDs x 2.4 GHz; `LDS conflict` =
+    SQ_LDS_BANK_CONFLICT / SQ_LDS_IDX_ACTIVE (LDS busy cycles lost to bank
+    conflicts)."""
+    import csv
+    import collections
+    per = collections.defaultdict(lambda: collections.defaultdict(list))
+    for path in (path_a, path_b):
+        if not os.path.exists(path):
+            continue
+        for r in csv.DictReader(open(path)):
+            fam = _family(r["Kernel_Name"])
+            if fam:
+                names_of.setdefault(fam[0], fam)
+                per[fam[0]][r["Counter_Name"]].append(float(r["Counter_Value"]))
+    out = ["", "Issue and LDS, two rocprofv3 --pmc runs with " + ", ".join(ISSUE_COUNTERS) + " and "
+           + ", ".join(LDS_COUNTERS) + ": per-wave instruction counts (SQ_INSTS_* / SQ_WAVES); "
+           "`wait` = SQ_WAIT_ANY / SQ_WAVE_CYCLES (wave time waiting on anything: memory, "
+           "dependencies, barriers); `issue wait` = SQ_WAIT_INST_ANY / SQ_WAVE_CYCLES; `VALU issue` "
+           "= SQ_INSTS_VALU x 4 cycles / (kernel-trace duration x 1024 SIMDs x 2.4 GHz), the share "
+           "of the chip's VALU issue slots used; `LDS conflict` = SQ_LDS_BANK_CONFLICT / "
+           "SQ_LDS_IDX_ACTIVE.", "",
+           "| kernel | waves | VALU / wave | LDS / wave | SALU / wave | VMEM / wave | wait | issue wait | "
+           "VALU issue | LDS conflict |",
+           "|---|---:|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    rows, rec = [], {}
+    for first, v in per.items():
+        def avg(c):
+            x = v.get(c, [])
+            return sum(x) / len(x) if x else 0.0
+        waves = avg("SQ_WAVES")
+        if waves <= 0 or first not in times:
+            continue
+        calls, tot = times[first]
+        sec = tot / calls * 1e-9
+        wc = avg("SQ_WAVE_CYCLES")
+        wait = avg("SQ_WAIT_ANY") / wc if wc > 0 else float("nan")
+        iwait = avg("SQ_WAIT_INST_ANY") / wc if wc > 0 else float("nan")
+        valu_issue = avg("SQ_INSTS_VALU") * 4 / (sec * N_SIMD * CLOCK_GHZ * 1e9)
+        lds_act = avg("SQ_LDS_IDX_ACTIVE")
+        confl = avg("SQ_LDS_BANK_CONFLICT") / lds_act if lds_act > 0 else float("nan")
+        r = {"waves": round(waves), "valu_per_wave": round(avg("SQ_INSTS_VALU") / waves, 1),
+             "lds_per_wave": round(avg("SQ_INSTS_LDS") / waves, 1),
+             "salu_per_wave": round(avg("SQ_INSTS_SALU") / waves, 1),
+             "vmem_per_wave": round(avg("SQ_INSTS_VMEM") / waves, 1),
+             "wait": round(wait, 3), "issue_wait": round(iwait, 3), "valu_issue": round(valu_issue, 3),
+             "lds_conflict": round(confl, 3)}
+        rows.append((tot, f"| {' / '.join(names_of[first])} | {r['waves']} | {r['valu_per_wave']:.0f} | "
+                          f"{r['lds_per_wave']:.0f} | {r['salu_per_wave']:.0f} | {r['vmem_per_wave']:.0f} | "
+                          f"{wait:.2f} | {iwait:.2f} | {valu_issue:.3f} | {confl:.3f} |"))
+        for n in names_of[first]:
+            rec[n] = r
+    return out + [r for _, r in sorted(rows, reverse=True)], rec
 
 
 # Matrix-core counters (gfx950): SQ_INSTS_VALU_MFMA_MOPS_* count multiply and

@@ -560,9 +560,26 @@ __device__ inline void s2g_rows(T* g, long gstride, const T* s, int ld, int nval
   }
 }
 
-// Padded LDS leading dimension for a row of n elements of T (16-byte pad:
-// staggers rows across banks for 16-byte fragment reads).
-template <typename T> constexpr int ldpad(int n) { return n + 16 / (int)sizeof(T); }
+// Padded LDS leading dimension for a row of n elements of T.  Measured on
+// gfx950 with the LDS bank-conflict counters, for the access patterns of
+// these kernels over 16 consecutive rows: 16-byte fragment reads are
+// conflict-free when the row stride is 8 (mod 16) dwords and take twice the
+// LDS cycles at 4 (mod 8) dwords (e.g. 136 bf16); the transposed 8-byte
+// reads (ds_read_b64_tr_b16) cost the same at either; 4-byte reads of fp32
+// rows are best at 4 (mod 8) dwords.  So 2-byte rows of 32 or more elements
+// get the smallest stride >= n + 8 that is 8 (mod 16) dwords (e.g. 128 ->
+// 144, 64 -> 80); shorter rows and 4-byte rows keep a 16-byte pad.
+template <typename T> constexpr int ldpad(int n) {
+  if (sizeof(T) != 2 || n < 32) return n + 16 / (int)sizeof(T);
+  int m = n + 8;
+  while ((m / 2) % 16 != 8) m += 8;
+  return m;
+}
+// The smallest padding (16 bytes), where LDS space is tighter than bandwidth.
+template <typename T> constexpr int ldpad_min(int n) { return n + 16 / (int)sizeof(T); }
+static_assert(ldpad<__bf16>(128) == 144 && ldpad<__bf16>(64) == 80 && ldpad<__bf16>(32) == 48 &&
+                  ldpad<__bf16>(16) == 24 && ldpad<float>(64) == 68,
+              "row strides");
 
 // --------------------------------------------------------------------------
 // math

@@ -63,7 +63,8 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
   constexpr bool RO = !REV && C_X > 0;
   constexpr bool FE = REV && C_X > 0;
   constexpr int CR = C_X > 0 ? C_X : 16;
-  constexpr int LS = ldpad<E>(D);
+  // (the smallest padding: the 64-row blocks fill the LDS with it already)
+  constexpr int LS = ldpad_min<E>(D);
   constexpr int VN = 16 / sizeof(E);
   constexpr int NV = D * D / VN;                       // 16-byte vectors of Bm_c
   constexpr int PER = (NV + SP_NT - 1) / SP_NT;
@@ -73,7 +74,7 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
   __shared__ __attribute__((aligned(16))) E Mb[2][D * LS];
   __shared__ __attribute__((aligned(16))) E Ss[2][RB * LS];
   __shared__ __attribute__((aligned(16))) E Qb[C_X > 0 ? 2 : 1][C_X > 0 ? CR * LS : 8];   // Qt rows of a step
-  constexpr int LO = ldpad<E>(RB);
+  constexpr int LO = ldpad_min<E>(RB);
   __shared__ __attribute__((aligned(16))) E Ob[FE ? 2 : 1][FE ? CR * LO : 8];   // dO rows of the block
   constexpr int NVQ = CR * D / VN;                     // 16-byte vectors of Qt_c
   constexpr int PERQ = (NVQ + SP_NT - 1) / SP_NT;
