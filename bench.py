@@ -99,7 +99,9 @@ def algorithmic_counts(w):
     c["wgrad_reduce"] = (H * L * 2 * ns * D * D * 4 + H * L * 2 * D * D * 4, H * L * 2 * ns * D * D)
     ntiles = -(-T // 29)
     c["bias_reduce"] = (bh * ntiles * (L * D + 4 * D) * 4 + H * (L * D + 4 * D) * 4, 0)
-    c["transpose_weights"] = (H * L * 4 * D * D * e, 0)
+    # weights in MFMA fragment order for the refinement backward: read W_k,
+    # W_p, write W_p, W_p^T, W_k^T
+    c["weight_frags"] = (H * L * 5 * D * D * e, 0)
     c["refine_fwd_recompute"] = c["refine_fwd"]
     c.update(decode_counts(w))
     peak_f = MFMA_BF16_PEAK_TFLOPS if w.dtype == "bf16" else MFMA_F32_PEAK_TFLOPS
@@ -164,7 +166,7 @@ _FAMILIES = [("refine_fwd_kernel", ["refine_fwd", "refine_fwd_recompute"]),
              ("wgrad_gemm_kernel", ["wgrad_gemm"]),
              ("wgrad_reduce_kernel", ["wgrad_reduce"]),
              ("bias_reduce_kernel", ["bias_reduce"]),
-             ("transpose_weights_kernel", ["transpose_weights"]),
+             ("weight_frags_kernel", ["weight_frags"]),
              ("decode_refine_kernel", ["step_refine"]),
              ("step_state_kernel", ["step_state"])]
 
@@ -534,7 +536,7 @@ def cpu_baseline(w, x, budget_s=20.0, backward=False, max_workers=16):
 SCAN_KERNELS = ("chunk_fwd", "state_fwd", "state_bwd", "chunk_bwd_state", "chunk_bwd_solve",
                 "chunk_bwd_pairs")
 REFINE_KERNELS = ("refine_fwd", "refine_bwd", "wgrad_gemm", "wgrad_reduce", "bias_reduce",
-                  "transpose_weights")
+                  "weight_frags")
 
 
 def stage_fractions(kernels, counts, dtype):

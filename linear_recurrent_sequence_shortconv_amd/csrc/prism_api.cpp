@@ -205,7 +205,7 @@ prism_status check_cu(const int* cu, const prism_desc* desc, prism::Dims* d) {
 
 template <typename E>
 struct BwdWs {
-  E *Kl, *Wl, *Mt, *UT, *WkT, *Sc, *dSnT, *u, *dP, *WkW, *WpW, *dKl;
+  E *Kl, *Wl, *Mt, *UT, *WkT, *Sc, *dSnT, *u, *dP, *WkW, *WpW, *WpF, *dKl;
   float* dWl;
   E *dQt, *dUs, *dWks, *dKs, *dVp, *dqp, *dkp;
   E *HT, *ET;     // H^T, E^T per chunk (storage type)
@@ -257,6 +257,7 @@ BwdWs<E> carve_bwd(const prism::Dims& d, Carve& cv, bool train) {
   w.part = cv.take<float>((size_t)d.H * L1 * 2 * prism::refine_bwd_splits(d) * DD * 4);
   w.WkW = cv.take<E>((size_t)d.H * d.L * DD * es);
   w.WpW = cv.take<E>((size_t)d.H * d.L * DD * es);
+  w.WpF = cv.take<E>((size_t)d.H * d.L * DD * es);
   w.cu = cv.take<int>(((size_t)d.B + 1) * 4);
   return w;
 }
@@ -437,13 +438,13 @@ prism_status run_backward(const prism::Dims& d0, const void* q, const void* k, c
     prism::RefineBwdArgs<E> r;
     r.v = v_; r.conv = static_cast<const E*>(conv); r.Wk = static_cast<const E*>(Wk);
     r.Wp = static_cast<const E*>(Wp); r.wbeta = static_cast<const E*>(wbeta);
-    r.WkT = w.WkW; r.WpT = w.WpW; r.dKl = w.dKl; r.dWl = w.dWl; r.dvdir = w.dVp; r.u = w.u;
+    r.WkT = w.WkW; r.WpT = w.WpW; r.WpF = w.WpF; r.dKl = w.dKl; r.dWl = w.dWl; r.dvdir = w.dVp; r.u = w.u;
     r.dP = w.dP; r.dwbp = w.dwbp; r.dcp = w.dcp; r.part = w.part;
     r.dv = static_cast<E*>(dv); r.dWk_o = dWk; r.dWp_o = dWp; r.dwbeta_o = dwbeta;
     r.dconv_o = dconv;
     r.hist = hist_;
     r.dhist = dhist;
-    HIP_TRY("transpose_weights", s, prism::launch_refine_bwd<E>(d, r, 0, s));
+    HIP_TRY("weight_frags", s, prism::launch_refine_bwd<E>(d, r, 0, s));
     HIP_TRY("refine_bwd", s, prism::launch_refine_bwd<E>(d, r, 1, s));
     HIP_TRY("wgrad_gemm", s, prism::launch_refine_bwd<E>(d, r, 2, s));
     HIP_TRY("wgrad_reduce", s, prism::launch_refine_bwd<E>(d, r, 3, s));

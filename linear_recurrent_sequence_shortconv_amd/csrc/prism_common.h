@@ -138,6 +138,26 @@ __device__ inline typename MfmaK<T, K>::frag load_fragK(const T* p, int ld, int 
   return *reinterpret_cast<const typename MK::frag*>(p + r * ld + k);
 }
 
+// Fragment order of a D x D matrix W that serves as a k-contiguous MfmaK<T, D>
+// operand (rows in 16-row tiles): fragment (tile nt, k step kk) holds, for lane
+// l, row 16 nt + (l & 15) and k = kk KSTEP + KPL (l >> 4) .. + KPL - 1, and is
+// stored contiguously at ((nt NK + kk) 64 + l) KPL.  A wave then reads a whole
+// fragment as one contiguous piece (1 KB for bf16), where the row-major layout
+// spreads it over 16 rows in 64-byte pieces.
+template <typename T, int D>
+__device__ inline long frag_order_offset(int row, int k) {
+  typedef MfmaK<T, D> MK;
+  constexpr int NK = D / MK::KSTEP;
+  const int nt = row >> 4, kk = k / MK::KSTEP, q = (k % MK::KSTEP) / MK::KPL, e = k % MK::KPL;
+  return ((long)(nt * NK + kk) * 64 + (row & 15) + 16 * q) * MK::KPL + e;
+}
+template <typename T, int D>
+__device__ inline typename MfmaK<T, D>::frag load_frag_fo(const T* W, int nt, int kk, int lane) {
+  typedef MfmaK<T, D> MK;
+  constexpr int NK = D / MK::KSTEP;
+  return *reinterpret_cast<const typename MK::frag*>(W + ((long)(nt * NK + kk) * 64 + lane) * MK::KPL);
+}
+
 // --------------------------------------------------------------------------
 // wave-grid tiling of an M x N output over NW waves
 // --------------------------------------------------------------------------

@@ -34,6 +34,12 @@ hipError_t launch_cu_sanitize(const Dims& d, int* out, hipStream_t s);
 // Every launcher enqueues on `stream` and returns hipGetLastError().
 // Element type E is __bf16 or float.
 
+// Weight matrices [H, L, D, D] in MFMA fragment order (frag_order_offset in
+// prism_common.h): each non-null output receives W_p, W_k, W_p^T or W_k^T.
+template <typename E>
+hipError_t launch_weight_frags(const Dims& d, const E* Wk, const E* Wp, E* WpF, E* WkF, E* WpTF,
+                               E* WkTF, hipStream_t s);
+
 // Stage 1 + Stage 2: ShortConv anchor and the L refinement steps.
 // Writes Kl, Wl [B, H, L, Tp, D] (rows t >= T are zero).  hist [B, 4, H, D]
 // holds the four v values before the sequence (nullptr: zeros).
@@ -110,7 +116,8 @@ struct RefineBwdArgs {
   const E *v, *conv, *Wk, *Wp, *wbeta;
   const E* hist;                // v before the sequence [B, 4, H, D] (nullptr: zeros)
   float* dhist;                 // its gradient (nullptr: not wanted)
-  E *WkT, *WpT;                 // transposed weights (workspace)
+  // W_p, W_p^T and W_k^T in MFMA fragment order (workspace; frag_order_offset)
+  E *WpF, *WpT, *WkT;
   const E* dKl;                 // gradient of the directions k^(l) (storage type)
   const float* dWl;             // gradient of the values w^(l) (fp32)
   const E* dvdir;               // direct v-gradient of the recurrence ([bh][Tp][D])
@@ -121,7 +128,7 @@ struct RefineBwdArgs {
   float *dWk_o, *dWp_o, *dwbeta_o, *dconv_o;
 };
 template <typename E>
-// stage 0: transpose weights, 1: refinement + ShortConv backward (dv, per-tile
+// stage 0: weights in fragment order, 1: refinement + ShortConv backward (dv, per-tile
 // dw_beta and tap partials), 2: weight-gradient GEMM, 3: its reduction,
 // 4: reduction of the dw_beta and tap partials
 hipError_t launch_refine_bwd(const Dims& d, const RefineBwdArgs<E>& a, int stage, hipStream_t s);

@@ -9,43 +9,85 @@ namespace prism {
 
 int refine_bwd_tiles(const Dims& d) { return (d.T + rb_own(d.off) - 1) / rb_own(d.off); }
 
-// WT[h][l][j][i] = W[h][l][i][j] for W in {Wk, Wp}: one workgroup per TS x TS
-// tile of one matrix; rows are read as 16-byte vectors, transposed through LDS
-// and written as 16-byte vectors.
+// Weight matrices in fragment order (frag_order_offset) for the projection
+// kernels: up to four outputs, each a copy of W_p or W_k, or of a transpose.
+// The forward takes W_p, W_k (p = W_p u, k = W_k u); the refinement backward
+// W_p, W_p^T, W_k^T (du = W_p^T dp + W_k^T dk).  One thread per KPL-element
+// piece of a fragment: it gathers the piece's KPL values (one 16-byte read
+// from a row, or KPL strided reads for a transpose, where consecutive threads
+// read consecutive columns) and writes them as one piece.
 constexpr int TW_NT = 256;
+template <typename E>
+struct FragJobs {
+  const E* src[4];
+  E* dst[4];
+  int trans[4];
+};
 template <typename E, int D>
-__global__ __launch_bounds__(TW_NT) void transpose_weights_kernel(const E* __restrict__ Wk,
-                                                                  const E* __restrict__ Wp,
-                                                                  E* __restrict__ WkT,
-                                                                  E* __restrict__ WpT) {
-  constexpr int TS = D < 64 ? D : 64;    // tile side
-  constexpr int NTL = D / TS;            // tiles per side
-  constexpr int VN = 16 / (int)sizeof(E);
-  constexpr int VPR = TS / VN;           // vectors per tile row
-  constexpr int NV = TS * VPR;
-  constexpr int LT = TS + VN;            // padded LDS row
-  __shared__ __attribute__((aligned(16))) E tl[TS * LT];
-  const int tile = blockIdx.x % (NTL * NTL);
-  const int mw = blockIdx.x / (NTL * NTL);   // 2 * matrix + (0: W_k, 1: W_p)
-  const long m = mw >> 1;
-  const E* W = ((mw & 1) ? Wp : Wk) + m * D * D;
-  E* WT = ((mw & 1) ? WpT : WkT) + m * D * D;
-  const int ti = tile / NTL, tj = tile % NTL;   // rows ti TS.., columns tj TS.. of W
-  for (int v = threadIdx.x; v < NV; v += TW_NT) {
-    const int r = v / VPR, c = (v % VPR) * VN;
-    st16(tl + r * LT + c, ld16(W + (long)(ti * TS + r) * D + tj * TS + c));
-  }
-  __syncthreads();
-  for (int v = threadIdx.x; v < NV; v += TW_NT) {
-    const int r = v / VPR, c = (v % VPR) * VN;   // row tj TS + r of WT, columns ti TS + c ..
-    E o[VN];
+__global__ __launch_bounds__(TW_NT) void weight_frags_kernel(FragJobs<E> jobs, int nout, int nmat) {
+  typedef MfmaK<E, D> MK;
+  constexpr int KS = MK::KSTEP, KPL = MK::KPL, NK = D / KS;
+  constexpr int PIECES = D * D / KPL;
+  const long gid = (long)blockIdx.x * TW_NT + threadIdx.x;
+  if (gid >= (long)nout * nmat * PIECES) return;
+  const int which = (int)(gid / ((long)nmat * PIECES));
+  const long rem = gid % ((long)nmat * PIECES);
+  const long m = rem / PIECES;
+  const int c = (int)(rem % PIECES);
+  const int l = c % 64, f = c / 64;
+  const int nt = f / NK, kk = f % NK;
+  const int row = 16 * nt + (l & 15), k0 = kk * KS + KPL * (l >> 4);
+  const E* src = jobs.src[which] + m * D * D;
+  const bool tr = jobs.trans[which] != 0;
+  E x[KPL];
 #pragma unroll
-    for (int k = 0; k < VN; ++k) o[k] = tl[(c + k) * LT + r];
-    uint4 w;
-    __builtin_memcpy(&w, o, 16);
-    st16(WT + (long)(tj * TS + r) * D + ti * TS + c, w);
-  }
+  for (int e = 0; e < KPL; ++e) x[e] = tr ? src[(long)(k0 + e) * D + row] : src[(long)row * D + k0 + e];
+  __builtin_memcpy(jobs.dst[which] + m * D * D + (long)c * KPL, x, KPL * sizeof(E));
 }
+
+template <typename E, int D>
+static hipError_t weight_frags_d(const Dims& d, const FragJobs<E>& j, int nout, hipStream_t s) {
+  typedef MfmaK<E, D> MK;
+  const long total = (long)nout * d.H * d.L * (D * D / MK::KPL);
+  hipLaunchKernelGGL((weight_frags_kernel<E, D>), dim3((unsigned)((total + TW_NT - 1) / TW_NT)),
+                     dim3(TW_NT), 0, s, j, nout, d.H * d.L);
+  return hipGetLastError();
+}
+
+template <typename E>
+hipError_t launch_weight_frags(const Dims& d, const E* Wk, const E* Wp, E* WpF, E* WkF, E* WpTF,
+                               E* WkTF, hipStream_t s) {
+  if (d.L == 0) return hipSuccess;
+  FragJobs<E> j{};
+  int n = 0;
+  auto add = [&](const E* src, E* dst, int tr) {
+    if (dst) {
+      j.src[n] = src;
+      j.dst[n] = dst;
+      j.trans[n] = tr;
+      ++n;
+    }
+  };
+  add(Wp, WpF, 0);
+  add(Wk, WkF, 0);
+  add(Wp, WpTF, 1);
+  add(Wk, WkTF, 1);
+  if (n == 0) return hipSuccess;
+  if (n > 4) return hipErrorInvalidValue;
+  switch (d.D) {
+    case 16: return weight_frags_d<E, 16>(d, j, n, s);
+    case 32: return weight_frags_d<E, 32>(d, j, n, s);
+    case 64: return weight_frags_d<E, 64>(d, j, n, s);
+    case 128:
+      if constexpr (sizeof(E) == 2) return weight_frags_d<E, 128>(d, j, n, s);
+      break;
+  }
+  return hipErrorInvalidValue;
+}
+template hipError_t launch_weight_frags<bf16>(const Dims&, const bf16*, const bf16*, bf16*, bf16*,
+                                              bf16*, bf16*, hipStream_t);
+template hipError_t launch_weight_frags<float>(const Dims&, const float*, const float*, float*,
+                                               float*, float*, float*, hipStream_t);
 
 // Split-K weight-gradient GEMM: for (h, l, which, split):
 //   P[i][j] = sum_{n in split} X[n][i] u[n][j],  X = dK_l (fp32, which = 0)
@@ -240,11 +282,8 @@ static hipError_t refine_bwd_d(const Dims& d, const RefineBwdArgs<E>& a, int NS,
   const int ntiles = refine_bwd_tiles(d);
   const long nw = (long)d.H * d.L * D * D;
   switch (stage) {
-    case 0:
-      hipLaunchKernelGGL((transpose_weights_kernel<E, D>),
-                         dim3(2 * d.H * d.L * (D < 64 ? 1 : (D / 64) * (D / 64))), dim3(TW_NT), 0, s,
-                         a.Wk, a.Wp, a.WkT, a.WpT);
-      break;
+    case 0:   // (the caller may instead have formed them with launch_weight_frags)
+      return launch_weight_frags<E>(d, a.Wk, a.Wp, a.WpF, nullptr, a.WpT, a.WkT, s);
     case 1:
       if (d.act == ACT_IDENTITY)
         return d.off ? launch_refine_bwd_main<E, ACT_IDENTITY, 1>(d, a, s)

@@ -40,7 +40,7 @@ constexpr int rb_own(int off) { return RB_TT - 3 - off; }
 template <typename E, int D, int LMAX, int ACT, int OFF>
 __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
     const E* __restrict__ v, const E* __restrict__ hist, const E* __restrict__ conv,
-    const E* __restrict__ Wp,
+    const E* __restrict__ Wp,   // W_p, W_k^T, W_p^T in fragment order (frag_order_offset)
     const E* __restrict__ WkT, const E* __restrict__ WpT, const E* __restrict__ wbeta,
     const E* __restrict__ dKl, const float* __restrict__ dWl, const E* __restrict__ dvdir,
     E* __restrict__ uo, E* __restrict__ dPo, E* __restrict__ dv, float* __restrict__ dwbp,
@@ -179,12 +179,14 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
   // issuing it before the row prefetches and stores of a step keeps the
   // product's wait (vmcnt counts in issue order) from covering those.
   typedef typename MK::frag Frag;
+  // (the weights come in fragment order: each fragment is one contiguous
+  // 64-lane piece)
   auto load_w = [&](const E* W, Frag (&bw)[FPW][D / KS]) {
 #pragma unroll
     for (int nn = 0; nn < FPW; ++nn)
 #pragma unroll
       for (int kk = 0; kk < D / KS; ++kk)
-        if (FT_OK(fq + 4 * nn)) bw[nn][kk] = load_fragK<E, D>(W, D, 16 * (fq + 4 * nn), kk * KS, lane);
+        if (FT_OK(fq + 4 * nn)) bw[nn][kk] = load_frag_fo<E, D>(W, fq + 4 * nn, kk, lane);
   };
   // p^(l) = W_p^(l) (u_hi + u_lo) for this wave's tiles (same as the forward)
   auto project = [&](const Frag (&bws)[FPW][D / KS], f32x4 (&acc)[2][FPW]) {
@@ -595,7 +597,7 @@ template <typename E, int ACT, int OFF>
 hipError_t launch_refine_bwd_main(const Dims& d, const RefineBwdArgs<E>& a, hipStream_t s) {
   const int ntiles = refine_bwd_tiles(d);
   auto go = [&](auto kern) {
-    hipLaunchKernelGGL(kern, dim3(ntiles * d.B * d.H), dim3(RB_NT), 0, s, a.v, a.hist, a.conv, a.Wp,
+    hipLaunchKernelGGL(kern, dim3(ntiles * d.B * d.H), dim3(RB_NT), 0, s, a.v, a.hist, a.conv, a.WpF,
                        a.WkT, a.WpT, a.wbeta, a.dKl, a.dWl, a.dvdir, a.u, a.dP, a.dv, a.dwbp, a.dcp,
                        a.dhist, d.B, d.T, d.H, d.L, d.Tp, ntiles, d.cu);
     return hipGetLastError();
