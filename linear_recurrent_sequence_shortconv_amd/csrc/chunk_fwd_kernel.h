@@ -19,7 +19,8 @@
 // All products are bf16 (or fp32) MFMA with fp32 accumulation; T, the decays
 // and the accumulators stay fp32.  Stored (global, per chunk, in the storage
 // type E unless noted):
-//   Mt [D][D] = M^T (MFMA B operand of the state pass, both directions),
+//   Mt [D][D] = M^T (MFMA B operand of the state pass, both directions; in
+//              fragment order for bf16 at D >= 32, see mt_frag_order),
 //   HT [D][D] = H^T, Qt [C][D], O_loc [C][D], gC (fp32), and when asked
 //   (training forward) U^T, Wk^T [D][C] for the reverse chunk kernels.
 // In backward mode (dO given) the kernel instead stores Mt, HT, gC,
@@ -552,8 +553,16 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
     gemm_acc<E, D, D, C, NW, true, true>(ma, Wkt, LT, KtD, LT, wave, lane);
     E* Mtc = Mt + cidx * D * D;
     for_tiles(ma, wave, lane, [&](int k0, int n, const f32x4& x) {
+      if constexpr (mt_frag_order<E, D>()) {
+        // fragment order: k0 .. k0 + 3 are adjacent in one 16-byte piece
+        E w[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) Mtc[(long)n * D + k0 + r] = to_t<E>(x[r]);
+        for (int r = 0; r < 4; ++r) w[r] = to_t<E>(x[r]);
+        st4(Mtc + frag_order_offset<E, D>(n, k0), w);
+      } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Mtc[(long)n * D + k0 + r] = to_t<E>(x[r]);
+      }
     });
   }
   {

@@ -158,6 +158,22 @@ __device__ inline typename MfmaK<T, D>::frag load_frag_fo(const T* W, int nt, in
   return *reinterpret_cast<const typename MK::frag*>(W + ((long)(nt * NK + kk) * 64 + lane) * MK::KPL);
 }
 
+// The chunk kernels store the per-chunk matrix M^T ([D][D], rows = the column
+// of the state product) in fragment order where one lane's fragment is a
+// whole 16-byte piece (bf16, D >= 32: 8 consecutive k); elsewhere row-major.
+template <typename T, int D> constexpr bool mt_frag_order() {
+  return sizeof(T) == 2 && D >= 32;
+}
+// Row and first k of the 16-byte piece e of a matrix in that fragment order
+// (8 consecutive k of one row).
+template <int D>
+__device__ inline void fo_piece_rc(int e, int& row, int& k) {
+  constexpr int NK = D / 32;
+  const int ln = e & 63, f = e >> 6;
+  row = 16 * (f / NK) + (ln & 15);
+  k = 32 * (f % NK) + 8 * (ln >> 4);
+}
+
 // --------------------------------------------------------------------------
 // wave-grid tiling of an M x N output over NW waves
 // --------------------------------------------------------------------------

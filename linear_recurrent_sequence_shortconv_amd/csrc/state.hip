@@ -15,7 +15,8 @@
 
 namespace prism {
 
-// Both directions take Mt_c = M_c^T (row-major in HBM and LDS):
+// Both directions take Mt_c = M_c^T (in HBM in the MFMA fragment order of a
+// k-contiguous B operand for bf16 at D >= 32, else row-major; row-major in LDS):
 // Forward (reverse = 0): X_0 = init (S0, or 0), per chunk c = 0..NC-1 store
 //   X_c, then X <- exp(gC_c) X - X Mt_c^T + AddT_c^T (X Mt_c^T = X M_c), with
 //   AddT_c = H_c^T.  Final X -> fin (S_T).
@@ -30,7 +31,10 @@ namespace prism {
 // barrier: the chunk matrix Bm_c and the operand copy of the state live in
 // double-buffered LDS tiles, and the next step's Bm, AddT block and decay are
 // fetched from global memory (L2: the row blocks of one sequence sit on the
-// same XCD) while the current step multiplies.
+// same XCD) while the current step multiplies.  In the forward direction
+// with Bm_c in fragment order no LDS copy of it is made: each wave loads the
+// B fragments of its output columns (contiguous 1 KB pieces) into registers,
+// two steps ahead, right after the step that used the previous set.
 // With RO (forward only) each step also forms its row block of the chunk's
 // readout, O[t][f] = O_loc[t][f] + sum_k Qt[t][k] S_c[f][k], from the operand
 // copy of S_c already in LDS: the chunk's Qt rows and O_loc block are fetched
@@ -63,15 +67,23 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
   constexpr bool RO = !REV && C_X > 0;
   constexpr bool FE = REV && C_X > 0;
   constexpr int CR = C_X > 0 ? C_X : 16;
-  // (the smallest padding: the 64-row blocks fill the LDS with it already)
-  constexpr int LS = ldpad_min<E>(D);
+  // Bm_c in fragment order (bf16, D >= 32): the forward reads each wave's B
+  // fragments of the product straight into registers, and Bm needs no LDS
+  // copy; the reverse pass reads Bm transposed and stages it in LDS
+  constexpr bool MFO = mt_frag_order<E, D>();
+  constexpr bool FO = MFO && !REV;
+  typedef MfmaK<E, D> MK;
+  constexpr int NKS = D / MK::KSTEP;
+  // (with Bm in LDS the smallest padding: the 64-row blocks fill the LDS with
+  // it already)
+  constexpr int LS = FO ? ldpad<E>(D) : ldpad_min<E>(D);
   constexpr int VN = 16 / sizeof(E);
   constexpr int NV = D * D / VN;                       // 16-byte vectors of Bm_c
   constexpr int PER = (NV + SP_NT - 1) / SP_NT;
   constexpr int NVR = RB * D / VN;                     // 16-byte vectors of the row block
   constexpr int NRB = D / RB;
   typedef Tiling<RB, D, SP_NW> TL;
-  __shared__ __attribute__((aligned(16))) E Mb[2][D * LS];
+  __shared__ __attribute__((aligned(16))) E Mb[FO ? 1 : 2][FO ? 8 : D * LS];
   __shared__ __attribute__((aligned(16))) E Ss[2][RB * LS];
   __shared__ __attribute__((aligned(16))) E Qb[C_X > 0 ? 2 : 1][C_X > 0 ? CR * LS : 8];   // Qt rows of a step
   constexpr int LO = ldpad_min<E>(RB);
@@ -100,39 +112,48 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
         for (int r = 0; r < 4; ++r)
           S.v[i][j][r] = init[((long)bh * D + rb0 + m0 + 16 * i + rl + r) * D + n0 + 16 * j + cl];
   }
+  // the initial state is complete before the loop: otherwise the compiler
+  // keeps its loads pending at the loop head and waits there, every step,
+  // for all memory operations in flight (the prefetches too)
+  __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   (void)reverse;   // the direction is the template parameter REV
   // chunks of this sequence (all NC in a dense batch; a packed sequence stops
   // at its own end, and the chunks after it are never read)
-  const int ncb = (seq_len(cu, bh / H, T) + C - 1) / C;
+  // (the sequence's bounds are read once: a scalar load inside the loop
+  // would hold up the LDS waits that follow it)
+  const int slen = seq_len(cu, bh / H, T);
+  const long sbeg = seq_start(cu, bh / H, T);
+  const int ncb = (slen + C - 1) / C;
   auto chunk_of = [&](int step) { return REV ? ncb - 1 - step : step; };
-  // The operands of step s + 2 are requested at the start of step s (two
-  // register sets, indexed by the step's parity at compile time): a step
-  // then stages into LDS only data that has had a whole step to arrive.
-  uint4 mst[2][PER];                    // Bm of a coming step, staged through registers
+  // The operands of step s + 2 are requested during step s (two register
+  // sets, indexed by the step's parity at compile time), each as soon as
+  // step s has used the set's previous contents: a step then stages into LDS
+  // only data that has had a whole step to arrive.
+  uint4 mst[2][FO ? 1 : PER];           // Bm of a coming step, staged through registers
+  typename MK::frag bfr[2][FO ? TL::RN : 1][FO ? NKS : 1];   // or its B fragments (FO)
   uint4 qst[2][C_X > 0 ? PERQ : 1];     // Qt rows of a coming step (readout, E_c)
   uint4 dost[2][FE ? PERO : 1];         // dO block of a coming step (E_c)
   int nvn[2] = {0, 0};                  // its valid rows (E_c)
   typename Raw4Of<E>::type oln[2][RO ? TLO::RM : 1][RO ? TLO::RN : 1];   // its O_loc block (raw)
   typename Raw4Of<E>::type addn[2][TL::RM][TL::RN];   // AddT^T block of a coming step (raw)
-  float egn[2] = {0.f, 0.f};            // decay of a coming step
+  float egn[2] = {0.f, 0.f};            // log decay gC of a coming step
   auto fetch = [&](int step, auto setc) {
     constexpr int Z = decltype(setc)::value;
     const long cidx = (long)bh * NC + chunk_of(step);
-    const E* bm = Bm + cidx * D * D;
+    if constexpr (!FO) {
+      const E* bm = Bm + cidx * D * D;
 #pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int e = tid + p * SP_NT;
-      if (e < NV) mst[Z][p] = ld16(bm + (long)e * VN);
+      for (int p = 0; p < PER; ++p) {
+        const int e = tid + p * SP_NT;
+        if (e < NV) mst[Z][p] = ld16(bm + (long)e * VN);
+      }
     }
-    if (act && !FE) {
-      const E* ac = AddT + cidx * D * D + rb0;
-#pragma unroll
-      for (int i = 0; i < TL::RM; ++i)
-#pragma unroll
-        for (int j = 0; j < TL::RN; ++j)
-          addn[Z][i][j] = ld_raw4(ac + (long)(n0 + 16 * j + cl) * D + m0 + 16 * i + rl);
-    }
-    egn[Z] = expf(gC[cidx]);
+    // a vector load (its offset made opaque to the compiler): a scalar load
+    // shares its wait counter with the LDS operations and may return out of
+    // order, so every LDS wait after it would wait for it as well
+    int zoff;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(zoff));
+    egn[Z] = gC[cidx + zoff];
     if constexpr (C_X > 0) {
       const E* qc = Qt + cidx * CR * D;
 #pragma unroll
@@ -144,11 +165,11 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
     if constexpr (FE) {
       // rows past the sequence end read the last valid row and are zeroed
       // when staged (no load depends on a branch)
-      const int b = bh / H, h = bh % H;
+      const int h = bh % H;
       const int c0 = chunk_of(step) * CR;
-      const int nval = min(CR, seq_len(cu, b, T) - c0);
+      const int nval = min(CR, slen - c0);
       nvn[Z] = nval;
-      const E* dc = dOg + ((seq_start(cu, b, T) + c0) * H + h) * D + rb0;
+      const E* dc = dOg + ((sbeg + c0) * H + h) * D + rb0;
 #pragma unroll
       for (int p = 0; p < PERO; ++p) {
         const int e = tid + p * SP_NT;
@@ -158,9 +179,28 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
         }
       }
     }
+  };
+  // the AddT^T block of a coming step, requested once the state update has
+  // used the set's previous block (a register set still in use when its
+  // refill is issued costs a copy, and a wait, at the loop's end)
+  auto fetch_add = [&](int step, auto setc) {
+    constexpr int Z = decltype(setc)::value;
+    if (act && !FE) {
+      const E* ac = AddT + ((long)bh * NC + chunk_of(step)) * D * D + rb0;
+#pragma unroll
+      for (int i = 0; i < TL::RM; ++i)
+#pragma unroll
+        for (int j = 0; j < TL::RN; ++j)
+          addn[Z][i][j] = ld_raw4(ac + (long)(n0 + 16 * j + cl) * D + m0 + 16 * i + rl);
+    }
+  };
+  // the O_loc block of a coming step (RO), requested once the readout has
+  // used the set's previous block
+  auto fetch_ol = [&](int step, auto setc) {
+    constexpr int Z = decltype(setc)::value;
     if constexpr (RO) {
       if (TLO::active(wave)) {
-        const E* oc = Oloc + cidx * CR * D + rb0;
+        const E* oc = Oloc + ((long)bh * NC + chunk_of(step)) * CR * D + rb0;
 #pragma unroll
         for (int i = 0; i < TLO::RM; ++i)
 #pragma unroll
@@ -171,14 +211,35 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
       }
     }
   };
+  // FO: this wave's B fragments of Bm_c (output columns n0 .. n0 + 16 RN - 1)
+  auto fetch_m = [&](int step, auto setc) {
+    constexpr int Z = decltype(setc)::value;
+    if constexpr (FO) {
+      if (act) {
+        const E* bm = Bm + ((long)bh * NC + chunk_of(step)) * D * D;
+#pragma unroll
+        for (int j = 0; j < TL::RN; ++j)
+#pragma unroll
+          for (int kk = 0; kk < NKS; ++kk) bfr[Z][j][kk] = load_frag_fo<E, D>(bm, (n0 >> 4) + j, kk, lane);
+      }
+    }
+  };
   auto stage = [&](E* dst, auto setc) {
     constexpr int Z = decltype(setc)::value;
+    if constexpr (!FO) {
 #pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int e = tid + p * SP_NT;
-      if (e < NV) {
-        const int r = e / (D / VN), c = (e % (D / VN)) * VN;
-        st16(dst + r * LS + c, mst[Z][p]);
+      for (int p = 0; p < PER; ++p) {
+        const int e = tid + p * SP_NT;
+        if (e < NV) {
+          int r, c;
+          if constexpr (MFO) {
+            fo_piece_rc<D>(e, r, c);
+          } else {
+            r = e / (D / VN);
+            c = (e % (D / VN)) * VN;
+          }
+          st16(dst + r * LS + c, mst[Z][p]);
+        }
       }
     }
     if constexpr (C_X > 0) {
@@ -218,15 +279,10 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
 #pragma unroll
         for (int j = 0; j < TL::RN; ++j) addc[i][j] = raw4_to_f(addn[Z][i][j]);
     }
-    const float egc = egn[Z];
-    // this step's O_loc block: set Z is refilled with step + 2's below
-    typename Raw4Of<E>::type olc[RO ? TLO::RM : 1][RO ? TLO::RN : 1];
-    if constexpr (RO) {
-#pragma unroll
-      for (int i = 0; i < TLO::RM; ++i)
-#pragma unroll
-        for (int j = 0; j < TLO::RN; ++j) olc[i][j] = oln[Z][i][j];
-    }
+    // (computed here, before the refill of set Z below, which it then
+    // cannot share registers with)
+    float egc = expf(egn[Z]);
+    asm volatile("" : "+v"(egc));
     if (act) {   // state -> operand copy
 #pragma unroll
       for (int i = 0; i < TL::RM; ++i)
@@ -239,7 +295,10 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
     // Ss[Z] and Mb[Z] complete; every wave is past the previous step, so the
     // other buffers are free to refill
     __syncthreads();
-    if (step + 2 < ncb) fetch(step + 2, setc);
+    // (unconditional, the last chunk again past the end: a load under a
+    // condition leaves a merge of old and new registers that the compiler
+    // resolves with copies, which wait for the load at the loop's end)
+    fetch(min(step + 2, ncb - 1), setc);
     if (!Xc) {
       // the chunk-entry states are not kept (readout fused, inference)
     } else if (!transposed) {
@@ -262,7 +321,24 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
     }
     Acc<RB, D, SP_NW> P;
     P.zero();
-    gemm_acc<E, RB, D, D, SP_NW, true, !REV>(P, Ss[Z], LS, Mb[Z], LS, wave, lane);
+    if constexpr (FO) {
+      if (act) {
+#pragma unroll
+        for (int kk = 0; kk < NKS; ++kk) {
+          typename MK::frag a[TL::RM];
+#pragma unroll
+          for (int i = 0; i < TL::RM; ++i) a[i] = load_fragK<E, D>(Ss[Z], LS, m0 + 16 * i, kk * MK::KSTEP, lane);
+#pragma unroll
+          for (int i = 0; i < TL::RM; ++i)
+#pragma unroll
+            for (int j = 0; j < TL::RN; ++j) P.v[i][j] = MK::mma(a[i], bfr[Z][j][kk], P.v[i][j]);
+        }
+      }
+      // set Z's fragments are consumed: refill it with step + 2's
+      fetch_m(min(step + 2, ncb - 1), setc);
+    } else {
+      gemm_acc<E, RB, D, D, SP_NW, true, !REV>(P, Ss[Z], LS, Mb[Z], LS, wave, lane);
+    }
     if constexpr (FE) {
       // E_c rows of the block: [r][n] = sum_t dO[t][rb0 + r] Qt[t][n] (both
       // operands k-strided in LDS), added in fp32
@@ -282,34 +358,51 @@ __global__ __launch_bounds__(SP_NT) void state_pass_kernel(const float* __restri
 #pragma unroll
         for (int j = 0; j < TL::RN; ++j) S.v[i][j] = egc * S.v[i][j] - P.v[i][j] + addc[i][j];
     }
+    // the update is done (and the AddT block it read is dead) before the
+    // refill below is issued: the compiler may not move either across this
+#pragma unroll
+    for (int i = 0; i < TL::RM; ++i)
+#pragma unroll
+      for (int j = 0; j < TL::RN; ++j) asm volatile("" : "+v"(S.v[i][j])::"memory");
+    fetch_add(min(step + 2, ncb - 1), setc);
     if constexpr (RO) {
       // readout rows f = rb0 .. rb0 + RB - 1 of chunk cidx: [f][t] = S_c[f] . Qt[t]
       Acc<RB, CR, SP_NW> R;
       R.zero();
       gemm_acc<E, RB, CR, D, SP_NW, true, true>(R, Ss[Z], LS, Qb[Z], LS, wave, lane);
-      const int b = bh / H, h = bh % H;
+      const int h = bh % H;
       const int c0 = chunk_of(step) * CR;
-      const int nval = min(CR, seq_len(cu, b, T) - c0);
-      E* oc = o + ((seq_start(cu, b, T) + c0) * H + h) * D + rb0;
+      const int nval = min(CR, slen - c0);
+      E* oc = o + ((sbeg + c0) * H + h) * D + rb0;
       for_tiles_ij(R, wave, lane, [&](int i, int j, int f0, int t, const f32x4& x) {
         if (t < nval) {
-          const f32x4 lo = raw4_to_f(olc[i][j]);
+          const f32x4 lo = raw4_to_f(oln[Z][i][j]);
 #pragma unroll
           for (int r = 0; r < 4; ++r) oc[(long)t * H * D + f0 + r] = to_t<E>(lo[r] + x[r]);
         }
       });
+      fetch_ol(min(step + 2, ncb - 1), setc);
     }
-    if (step + 1 < ncb) stage(Mb[Z ^ 1], std::integral_constant<int, Z ^ 1>{});
+    if (step + 1 < ncb) stage(Mb[FO ? 0 : Z ^ 1], std::integral_constant<int, Z ^ 1>{});
   };
   if (ncb > 0) {
     fetch(0, Z0{});
+    fetch_m(0, Z0{});
+    fetch_add(0, Z0{});
+    fetch_ol(0, Z0{});
     stage(Mb[0], Z0{});
-    if (ncb > 1) fetch(1, Z1{});
+    fetch(min(1, ncb - 1), Z1{});
+    fetch_m(min(1, ncb - 1), Z1{});
+    fetch_add(min(1, ncb - 1), Z1{});
+    fetch_ol(min(1, ncb - 1), Z1{});
   }
-  for (int step = 0; step < ncb; step += 2) {
+  // two steps per iteration (register sets 0 and 1), no condition inside
+  int step = 0;
+  for (; step + 1 < ncb; step += 2) {
     body(step, Z0{});
-    if (step + 1 < ncb) body(step + 1, Z1{});
+    body(step + 1, Z1{});
   }
+  if (step < ncb) body(step, Z0{});
   if (fin && act) {
 #pragma unroll
     for (int i = 0; i < TL::RM; ++i)
