@@ -209,6 +209,54 @@ def _sources_sha256():
     return h.hexdigest()
 
 
+def summarize_trace(d, workload):
+    """Kernel times of one rocprofv3 --kernel-trace --stats run (directory
+    d/trace) against the algorithmic bytes and FLOPs of workload: written to
+    profiles/<workload>_kernels.md (no counters; profiles/hbm_traffic.json is
+    left as it is)."""
+    import csv
+    from linear_recurrent_sequence_shortconv_amd.workloads import workloads
+    w = workloads()[workload]
+    counts = algorithmic_counts(w)
+    times, names_of = {}, {}
+    for r in csv.DictReader(open(os.path.join(d, "trace", "run_kernel_stats.csv"))):
+        fam = _family(r["Name"])
+        if fam:
+            names_of[fam[0]] = fam
+            t = times.setdefault(fam[0], [0, 0.0])
+            t[0] += int(r["Calls"])
+            t[1] += float(r["TotalDurationNs"])
+    cmd = ("cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/trace -o run -- "
+           f"python -u $R/bench.py --workload {workload} --steps 3 --warmup 1 --no-cpu-baseline "
+           "--no-varlen --no-decode")
+    lines = [f"# Kernel time, workload {workload}", "",
+             f"B={w.B} T={w.T} H={w.H} d_k=d_v={w.d} L={w.L} chunk={w.chunk} {w.dtype}; one forward + "
+             "backward step (the training pair) and the forward alone.",
+             "Made with (R = repository root, OUT = an output directory):", "", "```", cmd,
+             f"python bench.py --summarize-profiles $OUT --workload {workload}", "```", "",
+             "`algorithmic` bytes and FLOPs are what each kernel must move and compute "
+             "(bench.py, algorithmic_counts).", "",
+             "| kernel | launches | avg us (rocprofv3) | algorithmic MB | GB/s | frac of 8 TB/s | "
+             "algorithmic GFLOP | TFLOP/s |",
+             "|---|---:|---:|---:|---:|---:|---:|---:|"]
+    rows = []
+    for first, (calls, tot) in times.items():
+        c = counts.get(first)
+        if not c:
+            continue
+        avg_us = tot / calls / 1e3
+        gbs = c["bytes"] / (avg_us * 1e-6) / 1e9
+        tfl = c["flops"] / (avg_us * 1e-6) / 1e12
+        rows.append((tot, f"| {' / '.join(names_of[first])} | {calls} | {avg_us:.1f} | "
+                          f"{c['bytes'] / 1e6:.1f} | {gbs:.0f} | {gbs / HBM_PEAK_GBS:.3f} | "
+                          f"{c['flops'] / 1e9:.1f} | {tfl:.0f} |"))
+    lines += [r for _, r in sorted(rows, reverse=True)]
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    with open(os.path.join(ROOT, "profiles", f"{workload}_kernels.md"), "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def summarize_profiles(d, workload):
     """Turn the rocprofv3 runs under directory d (trace/, fetch/, write/,
     cfetch/, cwrite/ and, if present, mfma/: the commands are listed in the
@@ -750,7 +798,10 @@ def main():
     args = ap.parse_args()
 
     if args.summarize_profiles:
-        summarize_profiles(args.summarize_profiles, args.workload)
+        if os.path.isdir(os.path.join(args.summarize_profiles, "cfetch")):
+            summarize_profiles(args.summarize_profiles, args.workload)
+        else:   # a kernel trace only
+            summarize_trace(args.summarize_profiles, args.workload)
         return
 
     if args.gpus != 1:
