@@ -175,10 +175,20 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
   typedef Tiling<C, D, NW> TLS;
   TileSums<TLS::RM, TLS::RN> dds;   // row sums of the dD terms, over all products
   dds.zero();
-  if (wave == 0) chunk_decays<C>(alpha, nullptr, row0, H, nval, g, ev, Dv, nullptr, nullptr, nullptr, lane);
-  g2s_rows<E, C, D, NT>(R1, LR, dO + row0 * D, ts, nval, tid);
-  g2s_rows<E, D, D, NT>(X1, LD2, Sc + cidx * D * D, D, D, tid);   // S_c row-major
-  g2s_rows<E, D, D, NT>(X2, LD2, dSnT + cidx * D * D, D, D, tid);
+  // the first phase's tiles (dO rows, S_c and dS_n^T, both row-major), all
+  // requested before the first is stored (one memory round trip, which the
+  // decays' reads share)
+  {
+    RegTile<E, C, D, NT> t_do;
+    RegTile<E, D, D, NT> t_sc, t_dsnt;
+    t_do.load(dO + row0 * D, ts, nval, tid);
+    t_sc.load(Sc + cidx * D * D, D, D, tid);
+    t_dsnt.load(dSnT + cidx * D * D, D, D, tid);
+    if (wave == 0) chunk_decays<C>(alpha, nullptr, row0, H, nval, g, ev, Dv, nullptr, nullptr, nullptr, lane);
+    t_do.store_rows(R1, LR, tid);
+    t_sc.store_rows(X1, LD2, tid);
+    t_dsnt.store_rows(X2, LD2, tid);
+  }
   // tiles of the next phase, in flight during the first products: dS_n^T
   // again (stored transposed, i.e. dS_n row-major), K rows, U^T
   RegTile<E, D, D, NT, true> dsn;
@@ -274,9 +284,14 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
     kl.store_rows(R3, LR, tid);
     wl.store_rows(R4, LR, tid);
     __syncthreads();
-    if (l + 1 < L) {
-      kl.load(Kl + (lrow + Tp) * D, D, C, tid);
-      wl.load(Wl + (lrow + Tp) * D, D, C, tid);
+    {
+      // (the last step reads its own rows again: a load under a condition
+      // leaves a merge of old and new registers that the compiler resolves
+      // with copies at the loop head, which wait for every memory operation
+      // in flight, the previous step's gradient stores included)
+      const long nrow = l + 1 < L ? lrow + Tp : lrow;
+      kl.load(Kl + nrow * D, D, C, tid);
+      wl.load(Wl + nrow * D, D, C, tid);
     }
     Acc<C, D, NW> a;
     a.zero();
@@ -478,8 +493,13 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
   }
   vn.load(v + row0 * D, ts, nval, tid);
   for (int e = tid; e < 4 * NW * C; e += NT) rs[e] = 0.f;
-  if (wave == 0) chunk_decays<C>(alpha, beta, row0, H, nval, g, ev, Dv, bt, be, nullptr, lane);
-  g2s_rows<E, C, D, NT>(Kr, LR, k + row0 * D, ts, nval, tid);
+  {
+    // K rows requested before the decays' reads wait (one round trip)
+    RegTile<E, C, D, NT> t_k;
+    t_k.load(k + row0 * D, ts, nval, tid);
+    if (wave == 0) chunk_decays<C>(alpha, beta, row0, H, nval, g, ev, Dv, bt, be, nullptr, lane);
+    t_k.store_rows(Kr, LR, tid);
+  }
   __syncthreads();
 
   // ---- fold: V' = V - sum_l (Gam * K K_l^T)_{i<t} W_l  (kept in registers) ----
@@ -495,9 +515,10 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
       kl.store_rows(Klr, LR, tid);
       wl.store_rows(Wlr, LR, tid);
       __syncthreads();
-      if (l + 1 < L) {
-        kl.load(Kl + (lrow + Tp) * D, D, C, tid);
-        wl.load(Wl + (lrow + Tp) * D, D, C, tid);
+      {
+        const long nrow = l + 1 < L ? lrow + Tp : lrow;   // (unconditional, as above)
+        kl.load(Kl + nrow * D, D, C, tid);
+        wl.load(Wl + nrow * D, D, C, tid);
       }
       Acc<C, C, NW> f;    // [t][i] = K_t . K_l,i
       f.zero();
@@ -925,14 +946,23 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
   const bool actC = TLC::active(wave);
 
   for (int e = tid; e < 2 * NW * C; e += NT) rs[e] = 0.f;
-  if (wave == 0) {
-    __shared__ float dummy[3 * C];
-    chunk_decays<C>(alpha, nullptr, row0, H, nval, g, dummy, dummy + C, nullptr, nullptr, al, lane);
+  {
+    // the four row tiles, all requested before the first is stored (one
+    // memory round trip, which the decays' reads share)
+    RegTile<E, C, D, NT> t_q, t_k, t_do, t_dv;
+    t_q.load(q + row0 * D, ts, nval, tid);
+    t_k.load(k + row0 * D, ts, nval, tid);
+    t_do.load(dO + row0 * D, ts, nval, tid);
+    t_dv.load(dVp + cidx * C * D, D, C, tid);
+    if (wave == 0) {
+      __shared__ float dummy[3 * C];
+      chunk_decays<C>(alpha, nullptr, row0, H, nval, g, dummy, dummy + C, nullptr, nullptr, al, lane);
+    }
+    t_q.store_rows(Qr, LR, tid);
+    t_k.store_rows(Kr, LR, tid);
+    t_do.store_rows(dOr, LR, tid);
+    t_dv.store_rows(dVr, LR, tid);
   }
-  g2s_rows<E, C, D, NT>(Qr, LR, q + row0 * D, ts, nval, tid);
-  g2s_rows<E, C, D, NT>(Kr, LR, k + row0 * D, ts, nval, tid);
-  g2s_rows<E, C, D, NT>(dOr, LR, dO + row0 * D, ts, nval, tid);
-  g2s_rows<E, C, D, NT>(dVr, LR, dVp + cidx * C * D, D, C, tid);
   __syncthreads();
 
   Acc<C, D, NW> dqa, dka;
@@ -952,13 +982,21 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
     kl.store_rows(Klr, LR, tid);
     wl.store_rows(Wlr, LR, tid);
     __syncthreads();
-    if (l + 1 < L) {
-      kl.load(Kl + (lrow + Tp) * D, D, C, tid);
-      wl.load(Wl + (lrow + Tp) * D, D, C, tid);
+    {
+      // (the last step reads its own rows again: a load under a condition
+      // leaves a merge of old and new registers that the compiler resolves
+      // with copies at the loop head, which wait for every memory operation
+      // in flight, the previous step's gradient stores included)
+      const long nrow = l + 1 < L ? lrow + Tp : lrow;
+      kl.load(Kl + nrow * D, D, C, tid);
+      wl.load(Wl + nrow * D, D, C, tid);
     }
     // the partial dK_l, dW_l of the state-gradient kernel (accumulator
-    // layout), in flight during the products of this step
-    f32x4 pkl[TLD::RM][TLD::RN], pwl[TLD::RM][TLD::RN];
+    // layout), in flight during the products of this step; kept raw and
+    // converted where they are added (a conversion next to the load would
+    // make the wave wait for these scattered loads right after issuing them)
+    typename Raw1Of<E>::type pkl[TLD::RM][TLD::RN][4];
+    float pwl[TLD::RM][TLD::RN][4];
     if (TLD::active(wave)) {
 #pragma unroll
       for (int i = 0; i < TLD::RM; ++i)
@@ -968,7 +1006,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
           const int f = TLD::n0(wave) + 16 * j + (lane & 15);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            pkl[i][j][r] = to_f(dKl[(lrow + t0 + r) * D + f]);
+            pkl[i][j][r] = ld_raw1(dKl + (lrow + t0 + r) * D + f);
             pwl[i][j][r] = dWl[(lrow + t0 + r) * D + f];
           }
         }
@@ -1050,8 +1088,8 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
           const int f = TLD::n0(wave) + 16 * j + (lane & 15);
 #pragma unroll
           for (int r = 0; r < 4; ++r) {
-            dKl[(lrow + t0 + r) * D + f] = to_t<E>(pkl[i][j][r] + dkl.v[i][j][r]);
-            dWl[(lrow + t0 + r) * D + f] = pwl[i][j][r] + dwl.v[i][j][r];
+            dKl[(lrow + t0 + r) * D + f] = to_t<E>(raw1_to_f(pkl[i][j][r]) + dkl.v[i][j][r]);
+            dWl[(lrow + t0 + r) * D + f] = raw1_to_f(pwl[i][j][r]) + dwl.v[i][j][r];
           }
         }
     }

@@ -421,9 +421,12 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
       }
       __syncthreads();
       if constexpr (!FUSE) {
-        if (l + 1 < L) {   // next step's tiles are in flight during this step's products
-          kn.load(Klb + (long)(l + 1) * Tp * D, D, C, tid);
-          wn.load(Wlb + (long)(l + 1) * Tp * D, D, C, tid);
+        {   // next step's tiles are in flight during this step's products (the
+            // last step reads its own again: unconditional loads leave no
+            // register merge, whose copies would wait for every load in flight)
+          const long nl = l + 1 < L ? l + 1 : l;
+          kn.load(Klb + nl * Tp * D, D, C, tid);
+          wn.load(Wlb + nl * Tp * D, D, C, tid);
         }
       }
       {

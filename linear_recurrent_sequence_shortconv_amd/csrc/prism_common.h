@@ -406,38 +406,6 @@ __device__ __attribute__((always_inline)) inline void invert_unit_lower(const fl
 // --------------------------------------------------------------------------
 // cooperative global <-> LDS tile copies (16-byte vectors)
 // --------------------------------------------------------------------------
-// rows x cols tile of T; global row r at g + r * gstride; LDS row r at s + r * ld.
-// Rows >= nvalid are filled with zeros (ragged tails).
-template <typename T, int ROWS, int COLS, int NT>
-__device__ inline void g2s_rows(T* s, int ld, const T* g, long gstride, int nvalid, int tid) {
-  constexpr int VN = 16 / sizeof(T);
-  constexpr int VPR = COLS / VN;
-  for (int e = tid; e < ROWS * VPR; e += NT) {
-    const int r = e / VPR, c = (e % VPR) * VN;
-    uint4 v = {0u, 0u, 0u, 0u};
-    if (r < nvalid) v = ld16(g + r * gstride + c);
-    st16(s + r * ld + c, v);
-  }
-}
-
-// Same source, stored transposed in LDS: element (r, c) -> s[c * ld + r],
-// each value multiplied by scale[r] (nullptr = 1).
-template <typename T, int ROWS, int COLS, int NT>
-__device__ inline void g2s_rows_transposed(T* s, int ld, const T* g, long gstride, int nvalid,
-                                           const float* scale, int tid) {
-  constexpr int VN = 16 / sizeof(T);
-  constexpr int VPR = COLS / VN;
-  for (int e = tid; e < ROWS * VPR; e += NT) {
-    const int r = e / VPR, c = (e % VPR) * VN;
-    uint4 v = {0u, 0u, 0u, 0u};
-    if (r < nvalid) v = ld16(g + r * gstride + c);
-    const T* x = reinterpret_cast<const T*>(&v);
-    const float sc = scale ? scale[r] : 1.0f;
-#pragma unroll
-    for (int j = 0; j < VN; ++j) s[(c + j) * ld + r] = to_t<T>(to_f(x[j]) * sc);
-  }
-}
-
 // A ROWS x COLS tile of T held in registers as 16-byte vectors spread over
 // NT threads: load() issues the global reads early (software prefetch);
 // store_rows / store_transposed later write it into LDS.  Rows >= nvalid are
@@ -561,6 +529,16 @@ struct RegTile {
   }
 };
 
+// Global rows -> LDS rows (rows >= nvalid are zeros), all loads of the tile
+// issued before the first store: one memory round trip, where a copy loop
+// that stores each vector as it arrives waits once per iteration.
+template <typename T, int ROWS, int COLS, int NT>
+__device__ inline void g2s_rows(T* s, int ld, const T* g, long gstride, int nvalid, int tid) {
+  RegTile<T, ROWS, COLS, NT> t;
+  t.load(g, gstride, nvalid, tid);
+  t.store_rows(s, ld, tid);
+}
+
 // Four consecutive values of T to global memory, converted from fp32.
 __device__ inline void st_f4(float* p, const f32x4& x) { *reinterpret_cast<f32x4*>(p) = x; }
 __device__ inline void st_f4(bf16* p, const f32x4& x) {
@@ -583,6 +561,20 @@ __device__ inline f32x4 raw4_to_f(uint2 w) {
   asm volatile("" : "+v"(w.x), "+v"(w.y));
   return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u),
                __uint_as_float(w.y << 16), __uint_as_float(w.y & 0xffff0000u)};
+}
+
+// One storage-type value kept raw in a register until its use, the same way.
+template <typename T> struct Raw1Of { typedef float type; };
+template <> struct Raw1Of<bf16> { typedef unsigned int type; };
+__device__ inline float ld_raw1(const float* p) { return *p; }
+__device__ inline unsigned int ld_raw1(const bf16* p) { return *reinterpret_cast<const unsigned short*>(p); }
+__device__ inline float raw1_to_f(float x) {
+  asm volatile("" : "+v"(x));
+  return x;
+}
+__device__ inline float raw1_to_f(unsigned int w) {
+  asm volatile("" : "+v"(w));
+  return __uint_as_float(w << 16);
 }
 
 // LDS tile -> global rows (first nvalid rows only)
