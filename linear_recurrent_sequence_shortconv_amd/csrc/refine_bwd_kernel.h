@@ -99,16 +99,36 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
   const E* ch = conv + (long)h * D * 4;
   const int tile_id = (int)(bh * ntiles + tile);
 
-  for (int e = tid; e < L * (D / VN); e += RB_NT)
-    st16(wbl + e * VN, ld16(wbeta + (long)h * L * D + e * VN));
-  for (int e = tid; e < D * 4; e += RB_NT) ctp[e] = to_f(ch[e]);
-  for (int e = tid; e < (RB_TT + HL) * (D / VN); e += RB_NT) {
+  // The set-up's reads (w_beta rows, taps, the v rows of the tile and its
+  // halo) are all issued before the first is stored: one memory round trip,
+  // where copy loops that store each value as it arrives wait once per
+  // iteration.  No load sits in a per-lane branch (its merge would make the
+  // wave wait for it at issue): out-of-range v rows read row 0 and are zeroed
+  // at the store.
+  constexpr int NWB = LMAX * (D / VN), PWB = (NWB + RB_NT - 1) / RB_NT;
+  constexpr int NCT = 4 * D, PCT = (NCT + RB_NT - 1) / RB_NT;
+  constexpr int NVB = (RB_TT + HL) * (D / VN), PVB = (NVB + RB_NT - 1) / RB_NT;
+  const int nwb = L * (D / VN);
+  uint4 wbv[PWB], vbv[PVB];
+  E ctv[PCT];
+  bool vz[PVB];
+  if (nwb > 0) {   // (uniform: no refinement, no w_beta)
+#pragma unroll
+    for (int p = 0; p < PWB; ++p)
+      wbv[p] = ld16(wbeta + (long)h * L * D + (long)min(tid + p * RB_NT, nwb - 1) * VN);
+  }
+#pragma unroll
+  for (int p = 0; p < PCT; ++p) ctv[p] = ch[min(tid + p * RB_NT, NCT - 1)];
+#pragma unroll
+  for (int p = 0; p < PVB; ++p) {
+    const int e = min(tid + p * RB_NT, NVB - 1);
     const int r = e / (D / VN), c = (e % (D / VN)) * VN;
     const int t = t0 - HL + r;
-    uint4 x = {0u, 0u, 0u, 0u};
-    if (t >= 0 && t < Tb) x = ld16(vseq + t * tok_stride + c);
-    else if (t < 0 && hist) x = ld16(hist + (((long)b * 4 + 4 + t) * H + h) * D + c);
-    st16(vbuf + r * D + c, x);
+    const bool in_seq = t >= 0 && t < Tb, in_hist = t < 0 && hist;
+    vz[p] = !in_seq && !in_hist;
+    const E* src = in_seq ? vseq + t * tok_stride + c
+                 : in_hist ? hist + (((long)b * 4 + 4 + t) * H + h) * D + c : vseq + c;
+    vbv[p] = ld16(src);
   }
   // dW, dK rows of the first reverse step, in flight during the set-up
   RegTile<float, RB_TT, D, RB_NT> pw;   // dW_l rows (fp32)
@@ -117,6 +137,23 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
     const long lrow = (bh * L + (L - 1)) * Tp + t0;
     pw.load(dWl + lrow * D, D, nrow, tid);
     pk.load(dKl + lrow * D, D, nrow, tid);
+  }
+#pragma unroll
+  for (int p = 0; p < PWB; ++p)
+    if (tid + p * RB_NT < nwb) st16(wbl + (tid + p * RB_NT) * VN, wbv[p]);
+#pragma unroll
+  for (int p = 0; p < PCT; ++p)
+    if (tid + p * RB_NT < NCT) ctp[tid + p * RB_NT] = to_f(ctv[p]);
+#pragma unroll
+  for (int p = 0; p < PVB; ++p) {
+    const int e = tid + p * RB_NT;
+    if (e < NVB) {
+      uint4 x = vbv[p];
+      asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w));
+      if (vz[p]) x = uint4{0u, 0u, 0u, 0u};
+      const int r = e / (D / VN), c = (e % (D / VN)) * VN;
+      st16(vbuf + r * D + c, x);
+    }
   }
   __syncthreads();
   // anchor u (fp32; to LDS as the MFMA operand, hi and lo parts) and residual

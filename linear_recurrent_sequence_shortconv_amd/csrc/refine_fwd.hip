@@ -77,18 +77,48 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
   // batch, whose tiles all start before T.
   if (t0 >= Tb) return;
 
-  // ---- w_beta rows of this head (L x D) ----
-  for (int e = tid; e < L * (D / VN); e += RF_NT)
-    st16(wbs + e * VN, ld16(wbeta + (long)h * L * D + e * VN));
-  // ---- v rows t0-HL .. t0+63 (zeros past T; before 0 the history rows
-  //      [B, 4, H, D], or zeros without a history) ----
-  for (int e = tid; e < (RF_TT + HL) * (D / VN); e += RF_NT) {
-    const int r = e / (D / VN), c = (e % (D / VN)) * VN;
-    const int t = t0 - HL + r;
-    uint4 x = {0u, 0u, 0u, 0u};
-    if (t >= 0 && t < Tb) x = ld16(vseq + t * tok_stride + c);
-    else if (t < 0 && hist) x = ld16(hist + (((long)b * 4 + 4 + t) * H + h) * D + c);
-    st16(vbuf + r * D + c, x);
+  // ---- w_beta rows of this head (L x D) and the v rows t0-HL .. t0+63
+  //      (zeros past T; before 0 the history rows [B, 4, H, D], or zeros
+  //      without a history): every read issued before the first store (one
+  //      memory round trip, where a copy loop that stores each vector as it
+  //      arrives waits once per iteration), none in a per-lane branch
+  //      (out-of-range rows read row 0 and are zeroed at the store) ----
+  {
+    constexpr int NWB = 8 * (D / VN), PWB = (NWB + RF_NT - 1) / RF_NT;
+    constexpr int NVB = (RF_TT + HL) * (D / VN), PVB = (NVB + RF_NT - 1) / RF_NT;
+    const int nwb = L * (D / VN);
+    uint4 wbv[PWB], vbv[PVB];
+    bool vz[PVB];
+    if (nwb > 0) {   // (uniform: no refinement, no w_beta)
+#pragma unroll
+      for (int p = 0; p < PWB; ++p)
+        wbv[p] = ld16(wbeta + (long)h * L * D + (long)min(tid + p * RF_NT, nwb - 1) * VN);
+    }
+#pragma unroll
+    for (int p = 0; p < PVB; ++p) {
+      const int e = min(tid + p * RF_NT, NVB - 1);
+      const int r = e / (D / VN), c = (e % (D / VN)) * VN;
+      const int t = t0 - HL + r;
+      const bool in_seq = t >= 0 && t < Tb, in_hist = t < 0 && hist;
+      vz[p] = !in_seq && !in_hist;
+      const E* src = in_seq ? vseq + t * tok_stride + c
+                   : in_hist ? hist + (((long)b * 4 + 4 + t) * H + h) * D + c : vseq + c;
+      vbv[p] = ld16(src);
+    }
+#pragma unroll
+    for (int p = 0; p < PWB; ++p)
+      if (tid + p * RF_NT < nwb) st16(wbs + (tid + p * RF_NT) * VN, wbv[p]);
+#pragma unroll
+    for (int p = 0; p < PVB; ++p) {
+      const int e = tid + p * RF_NT;
+      if (e < NVB) {
+        uint4 x = vbv[p];
+        asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w));
+        if (vz[p]) x = uint4{0u, 0u, 0u, 0u};
+        const int r = e / (D / VN), c = (e % (D / VN)) * VN;
+        st16(vbuf + r * D + c, x);
+      }
+    }
   }
   typedef typename MK::frag Frag;
   auto load_w = [&](const E* W, Frag (&bw)[FPW][NK]) {
