@@ -215,12 +215,13 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
   dm.zero();
   gemm_acc<E, D, D, D, NW, false, true>(dm, X1, LD2, X2, LD2, wave, lane);
   {
-    // sum over all entries of S (.) dS_n = sum_{r,c} S[r][c] dS_n^T[c][r]
+    // sum over all entries of S (.) dS_n = sum_{r,c} S[r][c] dS_n[r][c]: the
+    // trace of dm, taken from the diagonal of the accumulator tiles
     float s = 0.f;
-    for (int e = tid; e < D * D; e += NT) {
-      const int r = e / D, cc = e % D;
-      s += to_f(X1[r * LD2 + cc]) * to_f(X2[cc * LD2 + r]);
-    }
+    for_tiles(dm, wave, lane, [&](int k0, int n, const f32x4& x) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s += k0 + r == n ? x[r] : 0.f;
+    });
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
     if (lane == 0) sdw[wave] = s;
