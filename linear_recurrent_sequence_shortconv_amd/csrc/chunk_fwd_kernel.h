@@ -493,11 +493,15 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
   E* Vt = reinterpret_cast<E*>(smem + LY::C_VT);       // (beta V')^T, later U^T / Qt^T
   E* R0 = reinterpret_cast<E*>(smem + LY::C_R0);
   E* Vr = reinterpret_cast<E*>(smem + LY::C_V);        // V rows, later dO^T
-  for (int e = tid; e < C * D; e += NT) {
-    const int t = e / D, f = e % D;
-    const float kv = to_f(Kr[t * LR + f]);
-    Ktbe[f * LT + t] = to_t<E>(be[t] * kv);
-    KtD[f * LT + t] = to_t<E>(Dv[t] * kv);
+  {
+    // (beta e K)^T and (D K)^T from the K rows: row pairs read as 16-byte
+    // pieces, written transposed as one 32-bit word per column (no bank
+    // conflicts; an element-wise transposition wrote 2 bytes at a time to
+    // addresses 8 banks apart)
+    RegTile<E, C, D, NT, true> kt;
+    kt.load(Kr, LR, C, tid);
+    kt.store_transposed(Ktbe, LT, be, tid);
+    kt.store_transposed(KtD, LT, Dv, tid);
   }
   vn.store_rows(Vr, LR, tid);
   RegTile<E, C, D, NT, true> on;   // dO rows (backward mode), in flight during the products below
