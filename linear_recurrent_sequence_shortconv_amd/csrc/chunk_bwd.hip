@@ -328,10 +328,8 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
   __syncthreads();   // every read of dS_n / dS_n^T (X1, X2) is done
   for_tiles(dm, wave, lane, [&](int k0, int n, const f32x4& x) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      X1[(k0 + r) * LD2 + n] = to_t<E>(-x[r]);
-      X2[n * LD2 + k0 + r] = to_t<E>(-x[r]);
-    }
+    for (int r = 0; r < 4; ++r) X1[(k0 + r) * LD2 + n] = to_t<E>(-x[r]);
+    st4f(X2 + n * LD2 + k0, -x);   // four consecutive k: one write
   });
   wkt.store_transposed(R3, LR, nullptr, tid);
   __syncthreads();

@@ -42,20 +42,6 @@
 
 namespace prism {
 
-// four consecutive elements (8 or 16 bytes, aligned) to LDS
-template <typename E>
-__device__ inline void st4(E* p, const E (&x)[4]) {
-  if constexpr (sizeof(E) == 2) {
-    uint2 w;
-    __builtin_memcpy(&w, x, 8);
-    *reinterpret_cast<uint2*>(p) = w;
-  } else {
-    uint4 w;
-    __builtin_memcpy(&w, x, 16);
-    *reinterpret_cast<uint4*>(p) = w;
-  }
-}
-
 constexpr int CF_NW = 8;
 constexpr int CF_NT = CF_NW * WAVE;
 constexpr int FUSE_LMAX = 8;   // refinement steps the fused kernel's LDS is sized for
@@ -514,11 +500,13 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
   }
   __syncthreads();
   for_tiles(vacc, wave, lane, [&](int t0, int f, const f32x4& x) {
+    E w[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = t0 + r;
-      Vt[f * LT + t] = to_t<E>(bt[t] * (to_f(Vr[t * LR + f]) - x[r]));
+      w[r] = to_t<E>(bt[t] * (to_f(Vr[t * LR + f]) - x[r]));
     }
+    st4(Vt + f * LT + t0, w);   // four consecutive tokens: one 8-byte write
   });
   __syncthreads();
   {
@@ -528,14 +516,8 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
     gemm_acc<E, C, D, C, NW, true, true>(ua, Tb, LT, Vt, LT, wave, lane);
     gemm_acc<E, C, D, C, NW, true, true>(wa, Tb, LT, Ktbe, LT, wave, lane);
     __syncthreads();
-    for_tiles(ua, wave, lane, [&](int t0, int f, const f32x4& x) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Vt[f * LT + t0 + r] = to_t<E>(x[r]);
-    });
-    for_tiles(wa, wave, lane, [&](int t0, int f, const f32x4& x) {
-#pragma unroll
-      for (int r = 0; r < 4; ++r) Ktbe[f * LT + t0 + r] = to_t<E>(x[r]);
-    });
+    for_tiles(ua, wave, lane, [&](int t0, int f, const f32x4& x) { st4f(Vt + f * LT + t0, x); });
+    for_tiles(wa, wave, lane, [&](int t0, int f, const f32x4& x) { st4f(Ktbe + f * LT + t0, x); });
   }
   __syncthreads();
   E* Ut = Vt;
@@ -606,11 +588,13 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
     gemm_acc<E, C, D, C, NW, true, true>(qa, R0, LT, Wkt, LT, wave, lane);
     E* Qtt = Vt;        // U^T is dead in backward mode once H is done
     for_tiles(qa, wave, lane, [&](int t0, int f, const f32x4& x) {
+      E w[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int t = t0 + r;
-        Qtt[f * LT + t] = to_t<E>(ev[t] * to_f(Qr[t * LR + f]) - x[r]);
+        w[r] = to_t<E>(ev[t] * to_f(Qr[t * LR + f]) - x[r]);
       }
+      st4(Qtt + f * LT + t0, w);
     });
     E* dOt = Vr;
     on.store_transposed(dOt, LT, nullptr, tid);

@@ -403,6 +403,27 @@ __device__ __attribute__((always_inline)) inline void invert_unit_lower(const fl
   if constexpr (C >= 64) invert_double_level<C, 32, NW>(A, Tm, Xs, wave, lane);
 }
 
+// four consecutive elements (8 or 16 bytes, aligned) to LDS or global memory
+template <typename E>
+__device__ inline void st4(E* p, const E (&x)[4]) {
+  if constexpr (sizeof(E) == 2) {
+    uint2 w;
+    __builtin_memcpy(&w, x, 8);
+    *reinterpret_cast<uint2*>(p) = w;
+  } else {
+    uint4 w;
+    __builtin_memcpy(&w, x, 16);
+    *reinterpret_cast<uint4*>(p) = w;
+  }
+}
+
+// four consecutive fp32 accumulator values, converted, as one st4
+template <typename E>
+__device__ inline void st4f(E* p, const f32x4& x) {
+  const E w[4] = {to_t<E>(x[0]), to_t<E>(x[1]), to_t<E>(x[2]), to_t<E>(x[3])};
+  st4(p, w);
+}
+
 // --------------------------------------------------------------------------
 // cooperative global <-> LDS tile copies (16-byte vectors)
 // --------------------------------------------------------------------------
