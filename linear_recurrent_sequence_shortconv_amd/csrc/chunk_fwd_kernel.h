@@ -346,6 +346,29 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
     }
   };
 
+  // Decays Gam_ti = exp(g_t - g_i) (i <= t, else 0) at this wave's positions
+  // of the C x C products that are rows i, column t (F_l, R_l of every step
+  // and R0): formed once per chunk and kept in registers by the separate-pair
+  // kernel; the fused kernel, at its register limit, forms them per product.
+  typedef Tiling<C, C, NW> TLC;
+  constexpr bool GAMC = !FUSE;
+  f32x4 gamc[GAMC ? TLC::RM : 1][GAMC ? TLC::RN : 1];
+  if constexpr (GAMC) {
+    if (TLC::active(wave)) {
+#pragma unroll
+      for (int i = 0; i < TLC::RM; ++i)
+#pragma unroll
+        for (int j = 0; j < TLC::RN; ++j) {
+          const int i0 = TLC::m0(wave) + 16 * i + 4 * (lane >> 4), t = TLC::n0(wave) + 16 * j + (lane & 15);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) gamc[i][j][r] = i0 + r <= t ? __expf(g[t] - g[i0 + r]) : 0.f;
+        }
+    }
+  }
+  auto gam_at = [&](int i, int j, int i0, int t, int r) -> float {
+    if constexpr (GAMC) return gamc[i][j][r];
+    else return i0 + r <= t ? __expf(g[t] - g[i0 + r]) : 0.f;
+  };
   // ---- phase B: refinement pairs, one step l at a time ----
   Acc<C, D, NW> vacc;    // sum_l (Gam * K K_l^T)_{i<t} W_l       [t][f]
   Acc<D, C, NW> oacc;    // O_loc^T                              [f][t]
@@ -420,24 +443,22 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
         a.zero();
         if constexpr (FUSE) gemm_acc<E, C, C, D, NW, false, true>(a, Klr, LT, Kr, LR, wave, lane);
         else gemm_acc<E, C, C, D, NW, true, true>(a, Klr, LR, Kr, LR, wave, lane);
-        for_tiles(a, wave, lane, [&](int i0, int t, const f32x4& x) {
+        for_tiles_ij(a, wave, lane, [&](int i, int j, int i0, int t, const f32x4& x) {
+          E w[4];
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int i = i0 + r;
-            F[t * LT + i] = to_t<E>(i < t ? __expf(g[t] - g[i]) * x[r] : 0.f);
-          }
+          for (int r = 0; r < 4; ++r) w[r] = to_t<E>(i0 + r < t ? gam_at(i, j, i0, t, r) * x[r] : 0.f);
+          st4(F + t * LT + i0, w);
         });
         if constexpr (!BWD) {
           Acc<C, C, NW> p;   // [i][t] = K_l,i . Q_t  ->  R_l[t][i], i <= t
           p.zero();
           if constexpr (FUSE) gemm_acc<E, C, C, D, NW, false, true>(p, Klr, LT, Qr, LR, wave, lane);
           else gemm_acc<E, C, C, D, NW, true, true>(p, Klr, LR, Qr, LR, wave, lane);
-          for_tiles(p, wave, lane, [&](int i0, int t, const f32x4& x) {
+          for_tiles_ij(p, wave, lane, [&](int i, int j, int i0, int t, const f32x4& x) {
+            E w[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-              const int i = i0 + r;
-              Rl[t * LT + i] = to_t<E>(i <= t ? __expf(g[t] - g[i]) * x[r] : 0.f);
-            }
+            for (int r = 0; r < 4; ++r) w[r] = to_t<E>(gam_at(i, j, i0, t, r) * x[r]);
+            st4(Rl + t * LT + i0, w);
           });
         }
       }
@@ -558,12 +579,11 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
     Acc<C, C, NW> a;   // [i][t] = K_i . Q_t  ->  R0[t][i], i <= t
     a.zero();
     gemm_acc<E, C, C, D, NW, true, true>(a, Kr, LR, Qr, LR, wave, lane);
-    for_tiles(a, wave, lane, [&](int i0, int t, const f32x4& x) {
+    for_tiles_ij(a, wave, lane, [&](int i, int j, int i0, int t, const f32x4& x) {
+      E w[4];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int i = i0 + r;
-        R0[t * LT + i] = to_t<E>(i <= t ? __expf(g[t] - g[i]) * x[r] : 0.f);
-      }
+      for (int r = 0; r < 4; ++r) w[r] = to_t<E>(gam_at(i, j, i0, t, r) * x[r]);
+      st4(R0 + t * LT + i0, w);
     });
   }
   __syncthreads();
