@@ -114,6 +114,24 @@ struct TileSums {
   }
 };
 
+// Decays Gam_ti = exp(g_t - g_i) for i <= t (else 0) at this wave's positions
+// of a C x C product held as rows t, column i (Tiling<C, C, NW>): formed once
+// per chunk for the products that share those positions.
+template <int C, int NW, int RM, int RN>
+__device__ inline void decays_ti(f32x4 (&gm)[RM][RN], const float* g, int wave, int lane) {
+  typedef Tiling<C, C, NW> TL;
+  static_assert(RM == TL::RM && RN == TL::RN, "tiles of a C x C product");
+  if (!TL::active(wave)) return;
+#pragma unroll
+  for (int i = 0; i < TL::RM; ++i)
+#pragma unroll
+    for (int j = 0; j < TL::RN; ++j) {
+      const int t0 = TL::m0(wave) + 16 * i + 4 * (lane >> 4), ii = TL::n0(wave) + 16 * j + (lane & 15);
+#pragma unroll
+      for (int r = 0; r < 4; ++r) gm[i][j][r] = ii <= t0 + r ? __expf(g[t0 + r] - g[ii]) : 0.f;
+    }
+}
+
 // ===========================================================================
 // chunk_bwd_state
 // ===========================================================================
@@ -500,6 +518,8 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
     t_k.store_rows(Kr, LR, tid);
   }
   __syncthreads();
+  f32x4 gamc[TLC::RM][TLC::RN];   // the decays of F_l (every fold step), R0 and dR0
+  decays_ti<C, NW>(gamc, g, wave, lane);
 
   // ---- fold: V' = V - sum_l (Gam * K K_l^T)_{i<t} W_l  (kept in registers) ----
   Acc<C, D, NW> vp;
@@ -522,12 +542,9 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
       Acc<C, C, NW> f;    // [t][i] = K_t . K_l,i
       f.zero();
       gemm_acc<E, C, C, D, NW, true, true>(f, Kr, LR, Klr, LR, wave, lane);
-      for_tiles(f, wave, lane, [&](int t0, int i, const f32x4& x) {
+      for_tiles_ij(f, wave, lane, [&](int i, int j, int t0, int ii, const f32x4& x) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int t = t0 + r;
-          Fb[t * LT + i] = to_t<E>(i < t ? __expf(g[t] - g[i]) * x[r] : 0.f);
-        }
+        for (int r = 0; r < 4; ++r) Fb[(t0 + r) * LT + ii] = to_t<E>(ii < t0 + r ? gamc[i][j][r] * x[r] : 0.f);
       });
       __syncthreads();
       gemm_acc<E, C, D, C, NW, true, false>(vp, Fb, LT, Wlr, LR, wave, lane);
@@ -664,14 +681,19 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
   Acc<C, C, NW> r0;   // [t][i] = Gam * Q_t . K_i, i <= t
   r0.zero();
   gemm_acc<E, C, C, D, NW, true, true>(r0, Qr, LR, Kr, LR, wave, lane);
-  for_tiles_mut(r0, wave, lane, [&](int t0, int i, f32x4& x) {
+  if (actC) {
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = t0 + r;
-      x[r] = i <= t ? __expf(g[t] - g[i]) * x[r] : 0.f;
-      R0b[t * LT + i] = to_t<E>(x[r]);
-    }
-  });
+    for (int i = 0; i < TLC::RM; ++i)
+#pragma unroll
+      for (int j = 0; j < TLC::RN; ++j) {
+        const int t0 = TLC::m0(wave) + 16 * i + 4 * (lane >> 4), ii = TLC::n0(wave) + 16 * j + (lane & 15);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          r0.v[i][j][r] = gamc[i][j][r] * r0.v[i][j][r];
+          R0b[(t0 + r) * LT + ii] = to_t<E>(r0.v[i][j][r]);
+        }
+      }
+  }
   {
     Acc<C, C, NW> dr;   // dR0 = dO U^T - dQt Wk^T
     dr.zero();
@@ -690,7 +712,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
             const int t = t0 + r;
             const float d_ = ii <= t ? dr.v[i][j][r] : 0.f;
             pr[r] = d_ * r0.v[i][j][r];
-            Xb[t * LT + ii] = to_t<E>(ii <= t ? __expf(g[t] - g[ii]) * d_ : 0.f);
+            Xb[t * LT + ii] = to_t<E>(gamc[i][j][r] * d_);
           }
           sgc.add(i, j, pr);
         }
@@ -1010,6 +1032,10 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
           }
         }
     }
+    // the decays of R_l and F_l (formed per step: kept across the steps they
+    // would push the kernel past its registers)
+    f32x4 gamc[TLC::RM][TLC::RN];
+    decays_ti<C, NW>(gamc, g, wave, lane);
     // R_l = (Gam * Q K_l^T)_{i<=t}, dR_l = dO W_l^T  -> Rb, Xb = Gam * dR_l
     {
       Acc<C, C, NW> r, dr;
@@ -1028,7 +1054,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
               const int t = t0 + rr;
-              const float gam = ii <= t ? __expf(g[t] - g[ii]) : 0.f;
+              const float gam = gamc[i][j][rr];
               const float rv = gam * r.v[i][j][rr];
               const float drv = ii <= t ? dr.v[i][j][rr] : 0.f;
               p[rr] = drv * rv;
@@ -1057,7 +1083,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
 #pragma unroll
             for (int rr = 0; rr < 4; ++rr) {
               const int t = t0 + rr;
-              const float gam = ii < t ? __expf(g[t] - g[ii]) : 0.f;
+              const float gam = ii < t ? gamc[i][j][rr] : 0.f;
               const float fv = gam * f.v[i][j][rr];
               const float dfv = ii < t ? -df.v[i][j][rr] : 0.f;
               p[rr] = dfv * fv;
