@@ -1041,8 +1041,8 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
       Acc<C, C, NW> r, dr;
       r.zero();
       dr.zero();
-      gemm_acc<E, C, C, D, NW, true, true>(r, Qr, LR, Klr, LR, wave, lane);
-      gemm_acc<E, C, C, D, NW, true, true>(dr, dOr, LR, Wlr, LR, wave, lane);
+      gemm_acc<E, C, C, D, NW, true, true, true>(r, Qr, LR, Klr, LR, wave, lane);
+      gemm_acc<E, C, C, D, NW, true, true, true>(dr, dOr, LR, Wlr, LR, wave, lane);
       if (actC) {
 #pragma unroll
         for (int i = 0; i < TLC::RM; ++i)
@@ -1070,8 +1070,8 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
       Acc<C, C, NW> f, df;
       f.zero();
       df.zero();
-      gemm_acc<E, C, C, D, NW, true, true>(f, Kr, LR, Klr, LR, wave, lane);
-      gemm_acc<E, C, C, D, NW, true, true>(df, dVr, LR, Wlr, LR, wave, lane);
+      gemm_acc<E, C, C, D, NW, true, true, true>(f, Kr, LR, Klr, LR, wave, lane);
+      gemm_acc<E, C, C, D, NW, true, true, true>(df, dVr, LR, Wlr, LR, wave, lane);
       if (actC) {
 #pragma unroll
         for (int i = 0; i < TLC::RM; ++i)
@@ -1098,12 +1098,12 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
     Acc<C, D, NW> dkl, dwl;
     dkl.zero();
     dwl.zero();
-    gemm_acc<E, C, D, C, NW, false, false>(dkl, Xb, LT, Qr, LR, wave, lane);    // X_l^T Q
-    gemm_acc<E, C, D, C, NW, false, false>(dkl, Gb, LT, Kr, LR, wave, lane);    // dG_l^T K
-    gemm_acc<E, C, D, C, NW, false, false>(dwl, Rb, LT, dOr, LR, wave, lane);   // R_l^T dO
-    gemm_acc<E, C, D, C, NW, false, false>(dwl, NFb, LT, dVr, LR, wave, lane);  // -F_l^T dV'
-    gemm_acc<E, C, D, C, NW, true, false>(dqa, Xb, LT, Klr, LR, wave, lane);    // X_l K_l
-    gemm_acc<E, C, D, C, NW, true, false>(dka, Gb, LT, Klr, LR, wave, lane);    // dG_l K_l
+    gemm_acc<E, C, D, C, NW, false, false, true>(dkl, Xb, LT, Qr, LR, wave, lane);    // X_l^T Q
+    gemm_acc<E, C, D, C, NW, false, false, true>(dkl, Gb, LT, Kr, LR, wave, lane);    // dG_l^T K
+    gemm_acc<E, C, D, C, NW, false, false, true>(dwl, Rb, LT, dOr, LR, wave, lane);   // R_l^T dO
+    gemm_acc<E, C, D, C, NW, false, false, true>(dwl, NFb, LT, dVr, LR, wave, lane);  // -F_l^T dV'
+    gemm_acc<E, C, D, C, NW, true, false, true>(dqa, Xb, LT, Klr, LR, wave, lane);    // X_l K_l
+    gemm_acc<E, C, D, C, NW, true, false, true>(dka, Gb, LT, Klr, LR, wave, lane);    // dG_l K_l
     if (TLD::active(wave)) {
 #pragma unroll
       for (int i = 0; i < TLD::RM; ++i)

@@ -441,8 +441,8 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
       {
         Acc<C, C, NW> a;   // [i][t] = K_l,i . K_t  ->  F[t][i], i < t
         a.zero();
-        if constexpr (FUSE) gemm_acc<E, C, C, D, NW, false, true>(a, Klr, LT, Kr, LR, wave, lane);
-        else gemm_acc<E, C, C, D, NW, true, true>(a, Klr, LR, Kr, LR, wave, lane);
+        if constexpr (FUSE) gemm_acc<E, C, C, D, NW, false, true, !FUSE>(a, Klr, LT, Kr, LR, wave, lane);
+        else gemm_acc<E, C, C, D, NW, true, true, !FUSE>(a, Klr, LR, Kr, LR, wave, lane);
         for_tiles_ij(a, wave, lane, [&](int i, int j, int i0, int t, const f32x4& x) {
           E w[4];
 #pragma unroll
@@ -452,8 +452,8 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
         if constexpr (!BWD) {
           Acc<C, C, NW> p;   // [i][t] = K_l,i . Q_t  ->  R_l[t][i], i <= t
           p.zero();
-          if constexpr (FUSE) gemm_acc<E, C, C, D, NW, false, true>(p, Klr, LT, Qr, LR, wave, lane);
-          else gemm_acc<E, C, C, D, NW, true, true>(p, Klr, LR, Qr, LR, wave, lane);
+          if constexpr (FUSE) gemm_acc<E, C, C, D, NW, false, true, !FUSE>(p, Klr, LT, Qr, LR, wave, lane);
+          else gemm_acc<E, C, C, D, NW, true, true, !FUSE>(p, Klr, LR, Qr, LR, wave, lane);
           for_tiles_ij(p, wave, lane, [&](int i, int j, int i0, int t, const f32x4& x) {
             E w[4];
 #pragma unroll
@@ -463,9 +463,9 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
         }
       }
       __syncthreads();
-      gemm_acc<E, C, D, C, NW, true, true>(vacc, F, LT, Wlt, LT, wave, lane);
-      if constexpr (!BWD) gemm_acc<E, D, C, C, NW, true, true>(oacc, Wlt, LT, Rl, LT, wave, lane);
-      gemm_acc<E, D, D, C, NW, true, true>(hacc, Wlt, LT, KltD, LT, wave, lane);
+      gemm_acc<E, C, D, C, NW, true, true, !FUSE>(vacc, F, LT, Wlt, LT, wave, lane);
+      if constexpr (!BWD) gemm_acc<E, D, C, C, NW, true, true, !FUSE>(oacc, Wlt, LT, Rl, LT, wave, lane);
+      gemm_acc<E, D, D, C, NW, true, true, !FUSE>(hacc, Wlt, LT, KltD, LT, wave, lane);
       __syncthreads();
     }
   }
@@ -480,7 +480,7 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
     float* Xs = reinterpret_cast<float*>(smem + LY::T_XS);
     Acc<C, C, NW> a;   // [t][i] = K_t . K_i
     a.zero();
-    gemm_acc<E, C, C, D, NW, true, true>(a, Kr, LR, Kr, LR, wave, lane);
+    gemm_acc<E, C, C, D, NW, true, true, !FUSE>(a, Kr, LR, Kr, LR, wave, lane);
     for_tiles(a, wave, lane, [&](int t0, int i, const f32x4& x) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
@@ -489,7 +489,7 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
       }
     });
     __syncthreads();
-    invert_unit_lower<C, NW>(Af, Tf, Xs, tid);
+    invert_unit_lower<C, NW, !FUSE>(Af, Tf, Xs, tid);
     for (int e = tid; e < C * C; e += NT) Tb[(e / C) * LT + (e % C)] = to_t<E>(Tf[(e / C) * LA + (e % C)]);
     __syncthreads();
   }
@@ -534,8 +534,8 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
     Acc<C, D, NW> ua, wa;   // U[t][f], Wk[t][f]
     ua.zero();
     wa.zero();
-    gemm_acc<E, C, D, C, NW, true, true>(ua, Tb, LT, Vt, LT, wave, lane);
-    gemm_acc<E, C, D, C, NW, true, true>(wa, Tb, LT, Ktbe, LT, wave, lane);
+    gemm_acc<E, C, D, C, NW, true, true, !FUSE>(ua, Tb, LT, Vt, LT, wave, lane);
+    gemm_acc<E, C, D, C, NW, true, true, !FUSE>(wa, Tb, LT, Ktbe, LT, wave, lane);
     __syncthreads();
     for_tiles(ua, wave, lane, [&](int t0, int f, const f32x4& x) { st4f(Vt + f * LT + t0, x); });
     for_tiles(wa, wave, lane, [&](int t0, int f, const f32x4& x) { st4f(Ktbe + f * LT + t0, x); });
@@ -550,7 +550,7 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
   }
 
   // H += U^T diag(D) K;  stored transposed (HT[n][r])
-  gemm_acc<E, D, D, C, NW, true, true>(hacc, Ut, LT, KtD, LT, wave, lane);
+  gemm_acc<E, D, D, C, NW, true, true, !FUSE>(hacc, Ut, LT, KtD, LT, wave, lane);
   {
     E* HTc = HT + cidx * D * D;
     for_tiles(hacc, wave, lane, [&](int r0, int n, const f32x4& x) {
@@ -560,7 +560,7 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
   {
     Acc<D, D, NW> ma;   // [k][n] = sum_t Wk[t][k] D_t K[t][n] = M[k][n]  -> stored as Mt[n][k]
     ma.zero();
-    gemm_acc<E, D, D, C, NW, true, true>(ma, Wkt, LT, KtD, LT, wave, lane);
+    gemm_acc<E, D, D, C, NW, true, true, !FUSE>(ma, Wkt, LT, KtD, LT, wave, lane);
     E* Mtc = Mt + cidx * D * D;
     for_tiles(ma, wave, lane, [&](int k0, int n, const f32x4& x) {
       if constexpr (mt_frag_order<E, D>()) {
@@ -578,7 +578,7 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
   {
     Acc<C, C, NW> a;   // [i][t] = K_i . Q_t  ->  R0[t][i], i <= t
     a.zero();
-    gemm_acc<E, C, C, D, NW, true, true>(a, Kr, LR, Qr, LR, wave, lane);
+    gemm_acc<E, C, C, D, NW, true, true, !FUSE>(a, Kr, LR, Qr, LR, wave, lane);
     for_tiles_ij(a, wave, lane, [&](int i, int j, int i0, int t, const f32x4& x) {
       E w[4];
 #pragma unroll
@@ -590,14 +590,14 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
   if constexpr (!BWD) {
     Acc<D, C, NW> qa;   // [f][t] = sum_i Wk[i][f] R0[t][i]
     qa.zero();
-    gemm_acc<E, D, C, C, NW, true, true>(qa, Wkt, LT, R0, LT, wave, lane);
+    gemm_acc<E, D, C, C, NW, true, true, !FUSE>(qa, Wkt, LT, R0, LT, wave, lane);
     E* Qtc = Qt + cidx * C * D;
     for_tiles(qa, wave, lane, [&](int f0, int t, const f32x4& x) {
 #pragma unroll
       for (int r = 0; r < 4; ++r)
         Qtc[(long)t * D + f0 + r] = to_t<E>(ev[t] * to_f(Qr[t * LR + f0 + r]) - x[r]);
     });
-    gemm_acc<E, D, C, C, NW, true, true>(oacc, Ut, LT, R0, LT, wave, lane);
+    gemm_acc<E, D, C, C, NW, true, true, !FUSE>(oacc, Ut, LT, R0, LT, wave, lane);
     E* Oc = Oloc + cidx * C * D;
     for_tiles(oacc, wave, lane, [&](int f0, int t, const f32x4& x) {
       st_f4(Oc + (long)t * D + f0, x);
@@ -605,7 +605,7 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
   } else {
     Acc<C, D, NW> qa;   // [t][f] = sum_i R0[t][i] Wk[i][f]  ->  Qt^T[f][t]
     qa.zero();
-    gemm_acc<E, C, D, C, NW, true, true>(qa, R0, LT, Wkt, LT, wave, lane);
+    gemm_acc<E, C, D, C, NW, true, true, !FUSE>(qa, R0, LT, Wkt, LT, wave, lane);
     E* Qtt = Vt;        // U^T is dead in backward mode once H is done
     for_tiles(qa, wave, lane, [&](int t0, int f, const f32x4& x) {
       E w[4];
@@ -621,7 +621,7 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
     __syncthreads();
     Acc<D, D, NW> ea;   // E[r][n] = sum_t dO[t][r] Qt[t][n]  -> stored as ET[n][r]
     ea.zero();
-    gemm_acc<E, D, D, C, NW, true, true>(ea, dOt, LT, Qtt, LT, wave, lane);
+    gemm_acc<E, D, D, C, NW, true, true, !FUSE>(ea, dOt, LT, Qtt, LT, wave, lane);
     E* ETc = ET + cidx * D * D;
     for_tiles(ea, wave, lane, [&](int r0, int n, const f32x4& x) {
       st_f4(ETc + (long)n * D + r0, x);

@@ -235,8 +235,11 @@ __device__ inline s16x4 load_frag4(const bf16* p, int ld, int row0, int k0, int 
   return f;
 }
 
-// acc += A * B^T over k in [0, K): A is M x K, B is N x K (both as LDS views)
-template <typename T, int M, int N, int K, int NW, bool AKC, bool BKC>
+// acc += A * B^T over k in [0, K): A is M x K, B is N x K (both as LDS views).
+// The k steps are unrolled fully (every fragment read of the product is issued
+// before the products that wait for it) unless KU2 asks for pairs of steps, for
+// a kernel at its register limit.
+template <typename T, int M, int N, int K, int NW, bool AKC, bool BKC, bool KU2 = false>
 __device__ inline void gemm_acc(Acc<M, N, NW>& acc, const T* A, int lda, const T* B, int ldb,
                                 int wave, int lane) {
   typedef Tiling<M, N, NW> TL;
@@ -260,17 +263,33 @@ __device__ inline void gemm_acc(Acc<M, N, NW>& acc, const T* A, int lda, const T
     }
   } else {
     static_assert(K % KS == 0, "k multiple");
+    if constexpr (KU2) {
 #pragma unroll 2
-    for (int k0 = 0; k0 < K; k0 += KS) {
-      typename Mfma<T>::frag a[TL::RM], b[TL::RN];
+      for (int k0 = 0; k0 < K; k0 += KS) {
+        typename Mfma<T>::frag a[TL::RM], b[TL::RN];
 #pragma unroll
-      for (int i = 0; i < TL::RM; ++i) a[i] = load_frag<T, AKC>(A, lda, m0 + 16 * i, k0, lane);
+        for (int i = 0; i < TL::RM; ++i) a[i] = load_frag<T, AKC>(A, lda, m0 + 16 * i, k0, lane);
 #pragma unroll
-      for (int j = 0; j < TL::RN; ++j) b[j] = load_frag<T, BKC>(B, ldb, n0 + 16 * j, k0, lane);
+        for (int j = 0; j < TL::RN; ++j) b[j] = load_frag<T, BKC>(B, ldb, n0 + 16 * j, k0, lane);
 #pragma unroll
-      for (int i = 0; i < TL::RM; ++i)
+        for (int i = 0; i < TL::RM; ++i)
 #pragma unroll
-        for (int j = 0; j < TL::RN; ++j) acc.v[i][j] = Mfma<T>::mma(a[i], b[j], acc.v[i][j]);
+          for (int j = 0; j < TL::RN; ++j) acc.v[i][j] = Mfma<T>::mma(a[i], b[j], acc.v[i][j]);
+      }
+    } else {
+      auto kstep = [&](int k0) {
+        typename Mfma<T>::frag a[TL::RM], b[TL::RN];
+  #pragma unroll
+        for (int i = 0; i < TL::RM; ++i) a[i] = load_frag<T, AKC>(A, lda, m0 + 16 * i, k0, lane);
+  #pragma unroll
+        for (int j = 0; j < TL::RN; ++j) b[j] = load_frag<T, BKC>(B, ldb, n0 + 16 * j, k0, lane);
+  #pragma unroll
+        for (int i = 0; i < TL::RM; ++i)
+  #pragma unroll
+          for (int j = 0; j < TL::RN; ++j) acc.v[i][j] = Mfma<T>::mma(a[i], b[j], acc.v[i][j]);
+      };
+#pragma unroll
+      for (int k0 = 0; k0 < K; k0 += KS) kstep(k0);
     }
   }
 }
@@ -330,7 +349,7 @@ __device__ inline void for_tiles_mut(Acc<M, N, NW>& acc, int wave, int lane, F&&
 // --------------------------------------------------------------------------
 constexpr int inv_scratch_floats(int C) { return C >= 32 ? ((C / 2) * (C / 2 + 1) + 3) / 4 * 4 : 4; }
 
-template <int C, int S, int NW>
+template <int C, int S, int NW, bool KU2>
 __device__ __attribute__((always_inline)) inline void invert_double_level(const float* A, float* Tm, float* Xs, int wave, int lane) {
   constexpr int LA = C + 1, P = C / (2 * S), LX = S + 1;
   static_assert(NW % P == 0, "waves per block pair");
@@ -341,7 +360,7 @@ __device__ __attribute__((always_inline)) inline void invert_double_level(const 
   {
     Acc<S, S, NWP> x;   // X = A21 T11
     x.zero();
-    gemm_acc<float, S, S, S, NWP, true, false>(x, A + (o + S) * LA + o, LA, Tm + o * LA + o, LA, w, lane);
+    gemm_acc<float, S, S, S, NWP, true, false, KU2>(x, A + (o + S) * LA + o, LA, Tm + o * LA + o, LA, w, lane);
     for_tiles(x, w, lane, [&](int r0, int cc, const f32x4& v) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) X[(r0 + r) * LX + cc] = v[r];
@@ -351,7 +370,7 @@ __device__ __attribute__((always_inline)) inline void invert_double_level(const 
   {
     Acc<S, S, NWP> y;   // T21 = -T22 X
     y.zero();
-    gemm_acc<float, S, S, S, NWP, true, false>(y, Tm + (o + S) * LA + o + S, LA, X, LX, w, lane);
+    gemm_acc<float, S, S, S, NWP, true, false, KU2>(y, Tm + (o + S) * LA + o + S, LA, X, LX, w, lane);
     for_tiles(y, w, lane, [&](int r0, int cc, const f32x4& v) {
 #pragma unroll
       for (int r = 0; r < 4; ++r) Tm[(o + S + r0 + r) * LA + o + cc] = -v[r];
@@ -361,8 +380,9 @@ __device__ __attribute__((always_inline)) inline void invert_double_level(const 
 }
 
 // Always inlined: as a call it would make the caller wait for every load in
-// flight (its prefetches of the next phase) and spill around the call.
-template <int C, int NW>
+// flight (its prefetches of the next phase) and spill around the call.  KU2 as
+// for gemm_acc.
+template <int C, int NW, bool KU2 = false>
 __device__ __attribute__((always_inline)) inline void invert_unit_lower(const float* A, float* Tm,
                                                                        float* Xs, int tid) {
   constexpr int NB = C / 16, LA = C + 1;
@@ -399,8 +419,8 @@ __device__ __attribute__((always_inline)) inline void invert_unit_lower(const fl
       if (r >= col) Tm[(base + r) * LA + base + col] = t[r];
   }
   __syncthreads();
-  if constexpr (C >= 32) invert_double_level<C, 16, NW>(A, Tm, Xs, wave, lane);
-  if constexpr (C >= 64) invert_double_level<C, 32, NW>(A, Tm, Xs, wave, lane);
+  if constexpr (C >= 32) invert_double_level<C, 16, NW, KU2>(A, Tm, Xs, wave, lane);
+  if constexpr (C >= 64) invert_double_level<C, 32, NW, KU2>(A, Tm, Xs, wave, lane);
 }
 
 // four consecutive elements (8 or 16 bytes, aligned) to LDS or global memory
