@@ -20,7 +20,9 @@ LIB = os.path.join(HERE, "libprism.so")
 
 # slowest first, so the parallel compile finishes early
 SOURCES = [
-    "chunk_bwd.hip",
+    "chunk_bwd_solve.hip",
+    "chunk_bwd_pairs.hip",
+    "chunk_bwd_state.hip",
     "chunk_fwd.hip",
     "chunk_fused_gelu.hip",
     "chunk_fused_identity.hip",
@@ -33,6 +35,7 @@ SOURCES = [
     "step.hip",
     "refine_bwd.hip",
     "noalloc.hip",
+    "chunk_bwd.hip",
     "prism_api.cpp",
 ]
 
