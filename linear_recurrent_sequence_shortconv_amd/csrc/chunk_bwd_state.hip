@@ -35,18 +35,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
   typedef CB1Lds<E, D, C> LY;
   constexpr int NW = CB_NW, NT = CB_NT;
   constexpr int LR = LY::LR, LD2 = LY::LD2;
-  __shared__ __attribute__((aligned(16))) unsigned char smem[LY::TOTAL];
-  float* g = reinterpret_cast<float*>(smem + LY::O_VEC);
-  float* ev = g + C;
-  float* Dv = g + 2 * C;
-  float* ddw = g + 3 * C;            // [NW][C] per-wave row sums of dD
-  float* sdw = ddw + NW * C;         // [NW] per-wave sums of S (.) dS_n
-  E* X1 = reinterpret_cast<E*>(smem + LY::O_X1);
-  E* X2 = reinterpret_cast<E*>(smem + LY::O_X2);
-  E* R1 = reinterpret_cast<E*>(smem + LY::O_R1);
-  E* R2 = reinterpret_cast<E*>(smem + LY::O_R2);
-  E* R3 = reinterpret_cast<E*>(smem + LY::O_R3);
-  E* R4 = reinterpret_cast<E*>(smem + LY::O_R4);
+  __shared__ __attribute__((aligned(16))) unsigned char smem_[LY::TOTAL];
 
   int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nblk = B * H * NC;
@@ -95,6 +84,18 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
   const bool more = PERSIST && vid + vstride < nblk;
   // past the end of a packed sequence: nothing to do (one workgroup per chunk)
   if (nval <= 0) return;
+  unsigned char* smem = PERSIST ? lds_opaque(smem_) : smem_;
+  float* g = reinterpret_cast<float*>(smem + LY::O_VEC);
+  float* ev = g + C;
+  float* Dv = g + 2 * C;
+  float* ddw = g + 3 * C;            // [NW][C] per-wave row sums of dD
+  float* sdw = ddw + NW * C;         // [NW] per-wave sums of S (.) dS_n
+  E* X1 = reinterpret_cast<E*>(smem + LY::O_X1);
+  E* X2 = reinterpret_cast<E*>(smem + LY::O_X2);
+  E* R1 = reinterpret_cast<E*>(smem + LY::O_R1);
+  E* R2 = reinterpret_cast<E*>(smem + LY::O_R2);
+  E* R3 = reinterpret_cast<E*>(smem + LY::O_R3);
+  E* R4 = reinterpret_cast<E*>(smem + LY::O_R4);
 
   for (int e = tid; e < NW * C + NW; e += NT) ddw[e] = 0.f;
   typedef Tiling<C, D, NW> TLS;

@@ -67,6 +67,18 @@ template <typename T> struct Vec16 {
 };
 
 __device__ inline uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// The LDS array's address as a value the compiler cannot see through.  Taken
+// at the head of a persistent workgroup's loop, the LDS addresses formed from
+// it are computed in the loop body; formed from the array itself they are
+// constants, which the compiler materializes once before the loop and keeps in
+// registers across all of it.
+__device__ inline unsigned char* lds_opaque(unsigned char* p) {
+  typedef __attribute__((address_space(3))) unsigned char L;
+  L* q = (L*)p;
+  asm volatile("" : "+s"(q));
+  return (unsigned char*)__builtin_assume_aligned((unsigned char*)q, 16);
+}
 __device__ inline void st16(void* p, const uint4& v) { *reinterpret_cast<uint4*>(p) = v; }
 
 // --------------------------------------------------------------------------
