@@ -91,6 +91,21 @@ def test_bf16_d128_backward(chunk):
     _check_full(x, "bf16", chunk, 3)
 
 
+@pytest.mark.parametrize("chunk", [16, 32])
+def test_bf16_d128_backward_many_chunks(chunk):
+    """More chunks than resident workgroups at d = 128 (B H NC = 520), so
+    the persistent chunk-backward workgroups each take several chunks, with a
+    ragged last chunk: one sequence's gradients and dS0 against the oracle."""
+    T = 64 * chunk + 7
+    x = make_inputs(2, T, 4, 128, 3, "bf16", seed=70 + chunk, random_S0=True, with_dST=True)
+    print(f"\n[bf16 bwd d=128 chunk={chunk} T={T} H=4 L=3, sequence (1, 2)]", flush=True)
+    gg = gpu_backward(x, "bf16", chunk, 3)
+    go = oracle_backward(x, 3, slice(1, 2), slice(2, 3))
+    gs = {n: gg[n][1:2, :, 2:3] for n in SEQ_GRADS}
+    gs["dS0"] = gg["dS0"][1:2, 2:3]
+    _compare(gs, go, SEQ_GRADS + ("dS0",), TOL["bf16"], tag="(b=1,h=2)")
+
+
 def test_bf16_d128_backward_four_steps():
     # the four-step refinement backward keeps one replayed residual for the
     # next reverse step (a kernel instance of its own)
