@@ -227,7 +227,7 @@ def summarize_trace(d, workload):
             t[0] += int(r["Calls"])
             t[1] += float(r["TotalDurationNs"])
     cmd = ("cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/trace -o run -- "
-           f"python -u $R/bench.py --workload {workload} --steps 3 --warmup 1 --no-cpu-baseline "
+           f"python -u $R/bench.py --workload {workload} --steps 10 --warmup 3 --no-cpu-baseline "
            "--no-varlen --no-decode")
     lines = [f"# Kernel time, workload {workload}", "",
              f"B={w.B} T={w.T} H={w.H} d_k=d_v={w.d} L={w.L} chunk={w.chunk} {w.dtype}; one forward + "
@@ -304,7 +304,7 @@ def summarize_profiles(d, workload):
             t[1] += float(r["TotalDurationNs"])
     counts = algorithmic_counts(w)
     cmds = [
-        "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/trace -o run -- python -u $R/bench.py --steps 3 --warmup 1 --no-cpu-baseline --no-varlen",
+        "cd /tmp && rocprofv3 --kernel-trace --stats --output-format csv -d $OUT/trace -o run -- python -u $R/bench.py --steps 10 --warmup 3 --no-cpu-baseline --no-varlen",
         "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/fetch -o run -- python -u $R/bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-varlen",
         "cd /tmp && rocprofv3 --pmc WRITE_SIZE --output-format csv -d $OUT/write -o run -- python -u $R/bench.py --steps 1 --warmup 1 --no-cpu-baseline --no-varlen",
         "cd /tmp && rocprofv3 --pmc FETCH_SIZE --output-format csv -d $OUT/cfetch -o run -- python -u $R/bench.py --calibrate-copy",
