@@ -86,7 +86,7 @@ hipError_t launch_state_pass(const Dims& d, const float* init, const E* Mt, cons
                              const float* gC, E* Xc, float* fin, bool transposed, bool reverse,
                              const E* Qt, const E* Oloc, E* o, const E* dO, hipStream_t s);
 
-// Arguments of the three chunk-parallel backward kernels (see chunk_bwd.hip).
+// Arguments of the three chunk-parallel backward kernels (see chunk_bwd_common.h).
 template <typename E>
 struct ChunkBwdArgs {
   const E *q, *k, *v, *dO;
