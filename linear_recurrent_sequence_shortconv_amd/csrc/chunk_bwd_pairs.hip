@@ -94,11 +94,15 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
   typedef Tiling<C, D, NW> TLD;
   TileSums<TLC::RM, TLC::RN> dgs_;   // decay-gradient row / column sums over all steps
   dgs_.zero();
-  RegTile<E, C, D, NT> kl, wl;   // next step's K_l, W_l rows (software prefetch)
-  if (L > 0) {
+  // next step's K_l, W_l rows (software prefetch); after the last step, the
+  // solve kernel's parts of dq and dk (rows), which the last phase adds to
+  const E* dqc = dqp + cidx * C * D;
+  const E* dkc = dkp + cidx * C * D;
+  RegTile<E, C, D, NT> kl, wl;
+  {
     const long lrow = (long)bh * L * Tp + tb;
-    kl.load(Kl + lrow * D, D, C, tid);
-    wl.load(Wl + lrow * D, D, C, tid);
+    kl.load(L > 0 ? Kl + lrow * D : dqc, D, C, tid);
+    wl.load(L > 0 ? Wl + lrow * D : dkc, D, C, tid);
   }
   for (int l = 0; l < L; ++l) {
     const long lrow = ((long)bh * L + l) * Tp + tb;
@@ -106,13 +110,14 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
     wl.store_rows(Wlr, LR, tid);
     __syncthreads();
     {
-      // (the last step reads its own rows again: a load under a condition
-      // leaves a merge of old and new registers that the compiler resolves
-      // with copies at the loop head, which wait for every memory operation
-      // in flight, the previous step's gradient stores included)
-      const long nrow = l + 1 < L ? lrow + Tp : lrow;
-      kl.load(Kl + nrow * D, D, C, tid);
-      wl.load(Wl + nrow * D, D, C, tid);
+      // (unconditional loads into the same registers, the last step's being
+      // the dq, dk parts: a load under a condition leaves a merge of old and
+      // new registers that the compiler resolves with copies at the loop head,
+      // which wait for every memory operation in flight, the previous step's
+      // gradient stores included)
+      const bool nx = l + 1 < L;
+      kl.load(nx ? Kl + (lrow + Tp) * D : dqc, D, C, tid);
+      wl.load(nx ? Wl + (lrow + Tp) * D : dkc, D, C, tid);
     }
     // the partial dK_l, dW_l of the state-gradient kernel (accumulator
     // layout), in flight during the products of this step; kept raw and
@@ -236,12 +241,12 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
   }
   // fp32 products staged in LDS (every tile buffer is free now), then added
   // to the solve kernel's parts and stored as full rows
-  const E* dqc = dqp + cidx * C * D;
-  const E* dkc = dkp + cidx * C * D;
   const E* dvc = dVp + cidx * C * D;
-  RegTile<E, C, D, NT> rq, rk;
-  rq.load(dqc, D, C, tid);
-  rk.load(dkc, D, C, tid);
+  const RegTile<E, C, D, NT>& rq = kl;   // the dq, dk parts, fetched during the last step
+  const RegTile<E, C, D, NT>& rk = wl;
+  // the decay gradient of the other kernels, requested ahead of the output
+  // stores (requested after them, its wait would cover every one of them)
+  const float dgp_t = dgp[cidx * C + (lane & (C - 1))];
   constexpr int LF = D + 4;
   float* Sq = reinterpret_cast<float*>(smem + LY::O_Q);
   float* Sk = Sq + C * LF;
@@ -283,11 +288,17 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
   // with L > 0 the direct v-gradient dV' (chunk rows [bh][c][t] = token rows
   // [bh][c C + t]) is completed by the refinement backward; at L = 0 it is dv
   if (L == 0) {
-    constexpr int VN = 16 / (int)sizeof(E);
+    // (every row requested before the first is stored: one round trip)
+    typedef RegTile<E, C, D, NT> VT;
+    VT tv;
+    tv.load(dvc, D, C, tid);
     E* dvo = dv + row0 * D;
-    for (int e = tid; e < C * D / VN; e += NT) {
-      const int t = e / (D / VN), f = (e % (D / VN)) * VN;
-      if (t < nval) st16(dvo + (long)t * ts + f, ld16(dvc + (long)t * D + f));
+#pragma unroll
+    for (int p = 0; p < VT::PER; ++p) {
+      const int u = tid + p * NT;
+      int t, f;
+      VT::unit(u, t, f);
+      if (u < VT::NU && t < nval) st16(dvo + (long)t * ts + f, tv.v[p][0]);
     }
   }
   __syncthreads();
@@ -295,7 +306,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_pairs_kernel(
   if (wave == 0) {
     float dg = 0.f;
     if (lane < C) {
-      dg = dgp[cidx * C + lane];
+      dg = dgp_t;
       for (int w = 0; w < NW; ++w) dg += rs[w * C + lane] - cs[w * C + lane];
     }
     // reverse inclusive scan over lanes 0..C-1

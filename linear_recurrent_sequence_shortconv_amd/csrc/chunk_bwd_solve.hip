@@ -464,6 +464,10 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
   __syncthreads();
   gemm_acc<E, C, D, C, NW, true, false>(dk, Zb, LT, Kr, LR, wave, lane);   // (dG0 + dG0^T) K
 
+  // the state kernel's part of the decay gradient, requested ahead of the
+  // output stores (loads and stores retire in issue order: requested after
+  // them, its wait would cover every one of them)
+  const float dgs_t = dgs[cidx * C + (tid & (C - 1))];
   // ---- outputs ----
   E* dqc = dqp + cidx * C * D;
   E* dkc = dkp + cidx * C * D;
@@ -495,7 +499,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
     }
     // de: from Qt (Q . dQt) and from Wk (beta K . X2); e_t = exp(g_t)
     const float det = de[t] + bt[t] * se;
-    dgp[cidx * C + t] = dgs[cidx * C + t] + sr + ev[t] * det;
+    dgp[cidx * C + t] = dgs_t + sr + ev[t] * det;
     if (t < nval) dbeta[row0 + (long)t * H] = sb + ev[t] * se;
   }
 }

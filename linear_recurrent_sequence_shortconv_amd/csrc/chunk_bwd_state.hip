@@ -71,6 +71,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
   // live across it
   if constexpr (PERSIST) {
     asm volatile("" : "+v"(tid));
+    tid &= NT - 1;   // (its range: tile loops over exactly NT units need no guard)
     lane = tid & 63;
     wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   }
@@ -251,7 +252,11 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
   wkt.store_transposed(R3, LR, nullptr, tid);
   // the next chunk's first tiles are fetched during the rest of this one
   // (issued after every load this chunk still waits for: loads complete in
-  // order)
+  // order).  Everything in flight before them is a phase old; waiting for it
+  // here costs little, and otherwise the compiler's bookkeeping at the
+  // refinement loop's exit has a later register reuse wait for the prefetch
+  // too (the last step's unconditional K_l, W_l reads are never used).
+  if constexpr (PERSIST) __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   if (more) prefetch(vid + vstride);
   __syncthreads();
   {
