@@ -92,6 +92,17 @@ __device__ __attribute__((always_inline)) inline void chunk_decays(const float* 
   }
 }
 
+// Sum of v over the 16 lanes of each row of the wave (lanes 16k .. 16k + 15),
+// left in lane 16k + 15: an inclusive prefix sum by DPP row shifts with zero
+// fill (row_shr 1, 2, 4, 8).
+__device__ inline float row16_sum(float v) {
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x111, 0xf, 0xf, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x112, 0xf, 0xf, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x114, 0xf, 0xf, true));
+  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x118, 0xf, 0xf, true));
+  return v;
+}
+
 // Row and column sums of products over all of a wave's accumulator tiles,
 // kept in registers and reduced across lanes once (flush_*), instead of per
 // tile: r[i][q] is row m0 + 16 i + 4 (lane >> 4) + q summed over this lane's
@@ -115,27 +126,26 @@ struct TileSums {
     }
     if (cols) c[j] += v[0] + v[1] + v[2] + v[3];
   }
-  // slot[row] += row sums (one wave's private slots)
+  // slot[row] = row sums (one wave's private slots, each written by one
+  // flush only): a row of 16 lanes summed by DPP row shifts, not by LDS
+  // shuffles, and stored, not added (no read-modify-write of LDS)
   __device__ inline void flush_rows(float* slot, int m0, int lane) const {
 #pragma unroll
     for (int i = 0; i < RM; ++i)
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        float s = r[i][q];
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        s += __shfl_xor(s, 4);
-        s += __shfl_xor(s, 8);
-        if ((lane & 15) == 0) slot[m0 + 16 * i + 4 * (lane >> 4) + q] += s;
+        const float s = row16_sum(r[i][q]);
+        if ((lane & 15) == 15) slot[m0 + 16 * i + 4 * (lane >> 4) + q] = s;
       }
   }
+  // slot[col] = column sums (as above)
   __device__ inline void flush_cols(float* slot, int n0, int lane) const {
 #pragma unroll
     for (int j = 0; j < RN; ++j) {
       float s = c[j];
       s += __shfl_xor(s, 16);
       s += __shfl_xor(s, 32);
-      if (lane < 16) slot[n0 + 16 * j + lane] += s;
+      if (lane < 16) slot[n0 + 16 * j + lane] = s;
     }
   }
 };

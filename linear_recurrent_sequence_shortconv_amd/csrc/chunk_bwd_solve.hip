@@ -14,8 +14,8 @@ struct CB2Lds {
   static constexpr int SZ_R = C * LR * (int)sizeof(E);
   static constexpr int SZ_CC = C * LT * (int)sizeof(E);
   static constexpr int SZ_F = C * LA * 4;
-  // vectors: g, e, Dv, bt, be, de (6C) + slots rs, cs, bs, es [NW][C]
-  static constexpr int SZ_VEC = (6 * C + 4 * CB_NW * C) * 4;
+  // vectors: g, e, Dv, bt, be, de (6C) + slots rs, cs, bs, es, bs2 [NW][C]
+  static constexpr int SZ_VEC = (6 * C + 5 * CB_NW * C) * 4;
   static constexpr int O_K = (SZ_VEC + 15) / 16 * 16;
   static constexpr int O_TB = O_K + SZ_R;
   static constexpr int O_X = O_TB + SZ_CC;
@@ -73,6 +73,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
   float* cs = rs + NW * C;          // [NW][C] column sums for dg
   float* bs = cs + NW * C;          // [NW][C] dbeta
   float* es = bs + NW * C;          // [NW][C] de
+  float* bs2 = es + NW * C;         // [NW][C] dbeta, C x D products
   E* Kr = reinterpret_cast<E*>(smem + LY::O_K);
   E* Tb = reinterpret_cast<E*>(smem + LY::O_TB);
 
@@ -108,7 +109,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
     wl.load(Wl + lrow * D, D, C, tid);
   }
   vn.load(v + row0 * D, ts, nval, tid);
-  for (int e = tid; e < 4 * NW * C; e += NT) rs[e] = 0.f;
+  for (int e = tid; e < 5 * NW * C; e += NT) rs[e] = 0.f;
   {
     // K rows requested before the decays' reads wait (one round trip)
     RegTile<E, C, D, NT> t_k;
@@ -485,7 +486,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
     sbc.flush_rows(bs + wave * C, TLC::m0(wave), lane);
   }
   if (actD) {
-    sbd.flush_rows(bs + wave * C, TLD::m0(wave), lane);
+    sbd.flush_rows(bs2 + wave * C, TLD::m0(wave), lane);
     sed.flush_rows(es + wave * C, TLD::m0(wave), lane);
   }
   __syncthreads();
@@ -494,7 +495,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
     float sr = 0.f, sb = 0.f, se = 0.f;
     for (int w = 0; w < NW; ++w) {
       sr += rs[w * C + t] - cs[w * C + t];
-      sb += bs[w * C + t];
+      sb += bs[w * C + t] + bs2[w * C + t];
       se += es[w * C + t];
     }
     // de: from Qt (Q . dQt) and from Wk (beta K . X2); e_t = exp(g_t)
