@@ -47,12 +47,8 @@ template <int C>
 __device__ __attribute__((always_inline)) inline void chunk_decays_of(float a, float bv, float* g, float* ev, float* Dv,
                                        float* bt, float* be, float* ai, int lane) {
   float s = logf(a);
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float y = __shfl_up(s, off);
-    if (lane >= off) s += y;
-  }
-  const float gC = __shfl(s, C - 1);
+  s = wave_scan(s);
+  const float gC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), C - 1));
   if (lane < C) {
     const float e = expf(s);
     g[lane] = s;
@@ -75,12 +71,8 @@ __device__ __attribute__((always_inline)) inline void chunk_decays(const float* 
     if (beta) bv = beta[row0 + (long)lane * H];
   }
   float s = lg;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const float y = __shfl_up(s, off);
-    if (lane >= off) s += y;
-  }
-  const float gC = __shfl(s, C - 1);
+  s = wave_scan(s);
+  const float gC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), C - 1));
   if (lane < C) {
     const float e = expf(s);
     g[lane] = s;
@@ -90,17 +82,6 @@ __device__ __attribute__((always_inline)) inline void chunk_decays(const float* 
     if (be) be[lane] = bv * e;
     if (ai) ai[lane] = a;
   }
-}
-
-// Sum of v over the 16 lanes of each row of the wave (lanes 16k .. 16k + 15),
-// left in lane 16k + 15: an inclusive prefix sum by DPP row shifts with zero
-// fill (row_shr 1, 2, 4, 8).
-__device__ inline float row16_sum(float v) {
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x111, 0xf, 0xf, true));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x112, 0xf, 0xf, true));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x114, 0xf, 0xf, true));
-  v += __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x118, 0xf, 0xf, true));
-  return v;
 }
 
 // Row and column sums of products over all of a wave's accumulator tiles,

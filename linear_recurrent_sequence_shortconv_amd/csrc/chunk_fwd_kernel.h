@@ -237,13 +237,8 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
   // ---- phase A: decays and gates; Q, K tiles ----
   if (wave == 0) {
     const float lg = logf(pa), bv = pb;   // alpha = 1, beta = 0 past the end
-    float s = lg;
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-      const float y = __shfl_up(s, off);
-      if (lane >= off) s += y;
-    }
-    const float gC = __shfl(s, C - 1);
+    const float s = wave_scan(lg);
+    const float gC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), C - 1));
     if (lane < C) {
       const float e = expf(s);
       g[lane] = s;
@@ -313,8 +308,7 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
           for (int jj = 0; jj < VN; ++jj) s += to_f(we[jj]) * to_f(ue[jj]);
         }
       }
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
+      s = quad_sum(s);
       if (part == 0) Gt[l * C + t] = sigmoidf(s);
     }
   }

@@ -701,6 +701,40 @@ __device__ inline void gelu_and_grad(float z, float& g, float& dg) {
   g = z * c;
   dg = c + z * 0.39894228040143268f * e;
 }
+// --------------------------------------------------------------------------
+// cross-lane sums by DPP (VALU operations with a lane-shifted source) instead
+// of LDS shuffles (ds_bpermute, an LDS round trip each)
+// --------------------------------------------------------------------------
+#define PRISM_DPP(v, ctrl, rowm, bc) \
+  __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, (v)), (ctrl), (rowm), 0xf, (bc)))
+// Sum over each quad of lanes (4k .. 4k + 3), in every lane of the quad:
+// quad_perm [1,0,3,2], then [2,3,0,1] (the pairing of an xor 1, 2 butterfly).
+__device__ inline float quad_sum(float v) {
+  v += PRISM_DPP(v, 0xB1, 0xf, false);
+  v += PRISM_DPP(v, 0x4E, 0xf, false);
+  return v;
+}
+// Sum over each row of 16 lanes (16k .. 16k + 15), left in lane 16k + 15: an
+// inclusive prefix sum by row shifts 1, 2, 4, 8 with zero fill (the pairing
+// tree of an xor 1, 2, 4, 8 butterfly).
+__device__ inline float row16_sum(float v) {
+  v += PRISM_DPP(v, 0x111, 0xf, true);
+  v += PRISM_DPP(v, 0x112, 0xf, true);
+  v += PRISM_DPP(v, 0x114, 0xf, true);
+  v += PRISM_DPP(v, 0x118, 0xf, true);
+  return v;
+}
+// Inclusive prefix sum over the 64 lanes of the wave: row scans by row shifts,
+// then each row's carry from the rows before it by row broadcasts (lane 15 to
+// rows 1 and 3, then lane 31 to rows 2 and 3).
+__device__ inline float wave_scan(float v) {
+  v = row16_sum(v);
+  v += PRISM_DPP(v, 0x142, 0xa, false);
+  v += PRISM_DPP(v, 0x143, 0xc, false);
+  return v;
+}
+#undef PRISM_DPP
+
 __device__ inline float sigmoidf(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 
 // Sequence b of a batch: its first token and its length.  A dense batch

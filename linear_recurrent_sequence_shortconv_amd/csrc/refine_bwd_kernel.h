@@ -201,8 +201,7 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
 #pragma unroll
         for (int j = 0; j < VN; ++j) s += to_f(we[j]) * to_f(ue[j]);
       }
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
+      s = quad_sum(s);
       if (part == 0) gate[l][t] = sigmoidf(s);
     }
   }
@@ -433,12 +432,8 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        float s = part[i];
-        s += __shfl_xor(s, 1);
-        s += __shfl_xor(s, 2);
-        s += __shfl_xor(s, 4);
-        s += __shfl_xor(s, 8);
-        if ((lane & 15) == 0) gsum[fq][16 * m + 4 * (lane >> 4) + i] = s;
+        const float s = row16_sum(part[i]);
+        if ((lane & 15) == 15) gsum[fq][16 * m + 4 * (lane >> 4) + i] = s;
       }
     }
     __syncthreads();

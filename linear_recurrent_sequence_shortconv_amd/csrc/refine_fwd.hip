@@ -194,8 +194,7 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
 #pragma unroll
         for (int j = 0; j < VN; ++j) s += to_f(we[j]) * to_f(ue[j]);
       }
-      s += __shfl_xor(s, 1);
-      s += __shfl_xor(s, 2);
+      s = quad_sum(s);
       if (part == 0) gate[l][t] = sigmoidf(s);
     }
   }
