@@ -140,8 +140,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
 #pragma unroll
       for (int r = 0; r < 4; ++r) s += k0 + r == n ? x[r] : 0.f;
     });
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+    s = wave_sum(s);
     if (lane == 0) sdw[wave] = s;
   }
   __syncthreads();
@@ -301,9 +300,7 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_state_kernel(
     if (lane < C)
       for (int w = 0; w < NW; ++w) dd += ddw[w * C + lane];
     const float Dd = lane < C ? Dv[lane] * dd : 0.f;
-    float tot = Dd;
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) tot += __shfl_xor(tot, off);
+    const float tot = wave_sum(Dd);
     float ssum = 0.f;
     for (int w = 0; w < NW; ++w) ssum += sdw[w];
     const float dgC = expf(g[C - 1]) * ssum + tot;

@@ -724,6 +724,17 @@ __device__ inline float row16_sum(float v) {
   v += PRISM_DPP(v, 0x118, 0xf, true);
   return v;
 }
+// Sum over the 64 lanes of the wave, in every lane: the row sums, then the four
+// row totals read from lanes 15, 31, 47 and 63.
+__device__ inline float wave_sum(float v) {
+  v = row16_sum(v);
+  const int b = __builtin_bit_cast(int, v);
+  const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 15));
+  const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 31));
+  const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 47));
+  const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(b, 63));
+  return (r0 + r1) + (r2 + r3);
+}
 // Inclusive prefix sum over the 64 lanes of the wave: row scans by row shifts,
 // then each row's carry from the rows before it by row broadcasts (lane 15 to
 // rows 1 and 3, then lane 31 to rows 2 and 3).
