@@ -187,12 +187,19 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
     });
     __syncthreads();
     invert_unit_lower<C, NW>(Af, Tf, Xs, tid);
-    for (int e = tid; e < C * C; e += NT) {
-      const int t = e / C, i = e % C;
-      const float tv = Tf[t * LA + i];
-      Tb[t * LT + i] = to_t<E>(tv);
-      Tbb[t * LT + i] = to_t<E>(tv * bt[i]);
-      Tbe[t * LT + i] = to_t<E>(tv * be[i]);
+    // T, T diag(beta), T diag(beta e) in the operand type: column pairs, one
+    // 2-element store each, all of a thread's reads issued together
+    constexpr int NPR = C * C / 2, PPR = (NPR + NT - 1) / NT;
+#pragma unroll
+    for (int k = 0; k < PPR; ++k) {
+      const int e = tid + k * NT;
+      if (NPR % NT == 0 || e < NPR) {
+        const int t = e / (C / 2), i = 2 * (e % (C / 2));
+        const float t0 = Tf[t * LA + i], t1 = Tf[t * LA + i + 1];
+        st2f(Tb + t * LT + i, t0, t1);
+        st2f(Tbb + t * LT + i, t0 * bt[i], t1 * bt[i + 1]);
+        st2f(Tbe + t * LT + i, t0 * be[i], t1 * be[i + 1]);
+      }
     }
     __syncthreads();
   }

@@ -484,7 +484,16 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
     });
     __syncthreads();
     invert_unit_lower<C, NW, !FUSE>(Af, Tf, Xs, tid);
-    for (int e = tid; e < C * C; e += NT) Tb[(e / C) * LT + (e % C)] = to_t<E>(Tf[(e / C) * LA + (e % C)]);
+    // T in the operand type: column pairs, one 2-element store each
+    constexpr int NPR = C * C / 2, PPR = (NPR + NT - 1) / NT;
+#pragma unroll
+    for (int k = 0; k < PPR; ++k) {
+      const int e = tid + k * NT;
+      if (NPR % NT == 0 || e < NPR) {
+        const int t = e / (C / 2), i = 2 * (e % (C / 2));
+        st2f(Tb + t * LT + i, Tf[t * LA + i], Tf[t * LA + i + 1]);
+      }
+    }
     __syncthreads();
   }
 

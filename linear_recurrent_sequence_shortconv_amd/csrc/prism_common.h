@@ -435,6 +435,19 @@ __device__ __attribute__((always_inline)) inline void invert_unit_lower(const fl
   if constexpr (C >= 64) invert_double_level<C, 32, NW, KU2>(A, Tm, Xs, wave, lane);
 }
 
+// two consecutive elements from fp32 values (one 4- or 8-byte store, aligned)
+template <typename E>
+__device__ inline void st2f(E* p, float a, float b) {
+  if constexpr (sizeof(E) == 2) {
+    const E x[2] = {to_t<E>(a), to_t<E>(b)};
+    uint32_t w;
+    __builtin_memcpy(&w, x, 4);
+    *reinterpret_cast<uint32_t*>(p) = w;
+  } else {
+    *reinterpret_cast<float2*>(p) = make_float2(a, b);
+  }
+}
+
 // four consecutive elements (8 or 16 bytes, aligned) to LDS or global memory
 template <typename E>
 __device__ inline void st4(E* p, const E (&x)[4]) {
