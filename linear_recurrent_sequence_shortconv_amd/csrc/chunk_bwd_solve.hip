@@ -465,9 +465,18 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
     }
   }
   __syncthreads();
-  for (int e = tid; e < C * C; e += NT) {
-    const int t = e / C, i = e % C;
-    Zb[t * LT + i] = to_t<E>(Zf[t * LA + i] + Zf[i * LA + t]);
+  {
+    // dG0 + dG0^T in the operand type: column pairs, all of a thread's reads
+    // issued together, one 2-element store each
+    constexpr int NPR = C * C / 2, PPR = (NPR + NT - 1) / NT;
+#pragma unroll
+    for (int k = 0; k < PPR; ++k) {
+      const int e = tid + k * NT;
+      if (NPR % NT == 0 || e < NPR) {
+        const int t = e / (C / 2), i = 2 * (e % (C / 2));
+        st2f(Zb + t * LT + i, Zf[t * LA + i] + Zf[i * LA + t], Zf[t * LA + i + 1] + Zf[(i + 1) * LA + t]);
+      }
+    }
   }
   __syncthreads();
   gemm_acc<E, C, D, C, NW, true, false>(dk, Zb, LT, Kr, LR, wave, lane);   // (dG0 + dG0^T) K
