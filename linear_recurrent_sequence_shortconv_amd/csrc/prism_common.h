@@ -678,41 +678,38 @@ static_assert(ldpad<__bf16>(128) == 144 && ldpad<__bf16>(64) == 80 && ldpad<__bf
 // --------------------------------------------------------------------------
 // math
 // --------------------------------------------------------------------------
-// Standard normal CDF Phi(z) = (1 + erf(z / sqrt 2)) / 2, with erf from
-// Abramowitz & Stegun, Handbook of Mathematical Functions, formula 7.1.26:
-//   erf(x) = 1 - (a1 t + a2 t^2 + a3 t^3 + a4 t^4 + a5 t^5) exp(-x^2),
-//   t = 1 / (1 + p x), x >= 0, |error| <= 1.5e-7;  erf(-x) = -erf(x).
-// One exp and one hardware reciprocal (v_rcp_f32, 1 ulp: far below the
-// formula's own error); e = exp(-z^2 / 2) is returned for reuse.
-__device__ inline float normal_cdf(float z, float& e) {
-  const float x = fabsf(z) * 0.70710678118654752f;
-  const float t = __builtin_amdgcn_rcpf(fmaf(0.3275911f, x, 1.0f));   // v_rcp_f32 (1 ulp)
-  float poly = fmaf(1.061405429f, t, -1.453152027f);
-  poly = fmaf(poly, t, 1.421413741f);
-  poly = fmaf(poly, t, -0.284496736f);
-  poly = fmaf(poly, t, 0.254829592f);
-  poly *= t;
-  e = __expf(-x * x);
-  const float erf_abs = 1.0f - poly * e;
-  return 0.5f + copysignf(0.5f * erf_abs, z);
+// Standard normal tail q(x) = Phi(-x) = erfc(x / sqrt 2) / 2 for x >= 0, with
+// erfc from Abramowitz & Stegun, Handbook of Mathematical Functions, formula
+// 7.1.26:
+//   erfc(y) = (a1 s + a2 s^2 + a3 s^3 + a4 s^4 + a5 s^5) exp(-y^2),
+//   s = 1 / (1 + p y), y >= 0, |error| <= 1.5e-7.
+// With y = x / sqrt 2 the 1 / sqrt 2 goes into p and the halving into the
+// coefficients (exact: a power of two); exp(-x^2 / 2) is one v_exp_f32 of
+// -x^2 log2(e) / 2 and is returned for reuse; s is one v_rcp_f32 (1 ulp, far
+// below the formula's own error).
+__device__ inline float normal_tail(float x, float& e) {
+  const float s = __builtin_amdgcn_rcpf(fmaf(0.3275911f * 0.70710678118654752f, x, 1.0f));
+  float poly = fmaf(0.5f * 1.061405429f, s, 0.5f * -1.453152027f);
+  poly = fmaf(poly, s, 0.5f * 1.421413741f);
+  poly = fmaf(poly, s, 0.5f * -0.284496736f);
+  poly = fmaf(poly, s, 0.5f * 0.254829592f);
+  e = __builtin_amdgcn_exp2f((x * -0.72134752044448170f) * x);   // 2^(-x^2 log2(e) / 2)
+  return poly * s * e;
 }
-// GELU(z) = z Phi(z) (exact-erf form, to the accuracy above)
+// GELU(z) = z Phi(z) (exact-erf form, to the accuracy above): Phi(z) = 1 - q(|z|)
+// for z >= 0 and q(|z|) below, so z Phi(z) = max(z, 0) - |z| q(|z|) either way.
 __device__ inline float gelu_erf(float z) {
+  const float x = fabsf(z);
   float e;
-  return z * normal_cdf(z, e);
+  return fmaf(-x, normal_tail(x, e), fmaxf(z, 0.f));
 }
-// d/dz GELU = Phi(z) + z phi(z), phi(z) = exp(-z^2/2) / sqrt(2 pi)
-__device__ inline float gelu_erf_grad(float z) {
-  float e;
-  const float c = normal_cdf(z, e);
-  return c + z * 0.39894228040143268f * e;
-}
-// both at once
+// GELU and its derivative d/dz GELU = Phi(z) + z phi(z), phi(z) = exp(-z^2/2) / sqrt(2 pi)
 __device__ inline void gelu_and_grad(float z, float& g, float& dg) {
   float e;
-  const float c = normal_cdf(z, e);
+  const float q = normal_tail(fabsf(z), e);
+  const float c = z >= 0.f ? 1.f - q : q;
   g = z * c;
-  dg = c + z * 0.39894228040143268f * e;
+  dg = fmaf(z * 0.39894228040143268f, e, c);
 }
 // --------------------------------------------------------------------------
 // cross-lane sums by DPP (VALU operations with a lane-shifted source) instead
