@@ -167,7 +167,11 @@ template <typename T, int D>
 __device__ inline typename MfmaK<T, D>::frag load_frag_fo(const T* W, int nt, int kk, int lane) {
   typedef MfmaK<T, D> MK;
   constexpr int NK = D / MK::KSTEP;
-  return *reinterpret_cast<const typename MK::frag*>(W + ((long)(nt * NK + kk) * 64 + lane) * MK::KPL);
+  // (the fragment's base, then the lane's 32-bit unsigned byte offset: with a
+  // wave-uniform matrix and tile the load takes the scalar-base form, no 64-bit
+  // address arithmetic per fragment)
+  const char* b = reinterpret_cast<const char*>(W) + (long)(nt * NK + kk) * (64 * MK::KPL * (int)sizeof(T));
+  return *reinterpret_cast<const typename MK::frag*>(b + (unsigned)lane * (unsigned)(MK::KPL * sizeof(T)));
 }
 
 // The chunk kernels store the per-chunk matrix M^T ([D][D], rows = the column

@@ -72,7 +72,12 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
   __shared__ float red[RB_NT * 4];                                    // dconv partials per thread
   float* gw = gk;
 
-  const int tid = threadIdx.x, lane = tid & 63, fq = tid >> 6;   // wave = feature group
+  const int tid = threadIdx.x, lane = tid & 63;
+  // wave = feature group; at D = 128 taken as wave-uniform, so that the
+  // weight fragments' bases are scalar (the registers that frees hold the
+  // kept residual rows below; the smaller instances use fewer registers
+  // without it)
+  const int fq = D >= 128 ? __builtin_amdgcn_readfirstlane(tid >> 6) : tid >> 6;
   const int nblk = ntiles * B * H;
   const int bid = xcd_swizzle(blockIdx.x, nblk);
   const int h = bid / (B * ntiles);
@@ -322,14 +327,15 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
   float a_[2][FPW][4];
   E dvd[2][FPW][4];         // direct v-gradient (fetched during the last step; converted at use)
   f32x4 du[2][FPW];
-  // Four steps: r^(l-1), kept from the replay of reverse step l for step
-  // l - 1 (steps 3 and 1 replay the chain, step 2 takes the kept rows; 4
-  // replayed GELUs instead of 6).  Only when the instance's step count is
-  // the runtime one (a uniform test): with fewer steps the first reverse
-  // step is not step 3 and the kept rows would be read unwritten.  With
-  // three steps the kept rows would spill registers, which costs what the
-  // one saved GELU gains.
-  constexpr bool KEEP = LMAX == 4;
+  // Three or four steps: r^(l-1), kept from the replay of reverse step l for
+  // step l - 1 (four steps: steps 3 and 1 replay the chain, step 2 takes the
+  // kept rows, 4 replayed GELUs instead of 6; three steps: step 2 replays,
+  // step 1 takes the kept rows, 2 instead of 3).  Only when the instance's
+  // step count is the runtime one (a uniform test): with fewer steps the
+  // first reverse step is not the last step and the kept rows would be read
+  // unwritten.  (Three fp32 steps: the kept rows would cost the D = 64
+  // instance a wave per SIMD.)
+  constexpr bool KEEP = LMAX == 4 || (LMAX == 3 && sizeof(E) == 2);
   const bool keep = KEEP && L == LMAX;
   float rkeep[KEEP ? 2 : 1][FPW][4];
 #pragma unroll
