@@ -70,7 +70,8 @@ typedef enum {
 } prism_activation;
 
 /* Problem descriptor.
- *   B, T, H    batch, sequence length, heads            (each >= 1)
+ *   B, T, H    batch, sequence length, heads            (each >= 1;
+ *              H * dk <= 4194304)
  *   dk, dv     key / value head dimension; must be equal, in {16, 32, 64, 128}
  *              for PRISM_BF16 and {16, 32, 64} for PRISM_F32
  *   L          refinement steps, 0 <= L <= 8

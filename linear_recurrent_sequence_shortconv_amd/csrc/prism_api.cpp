@@ -150,6 +150,10 @@ prism_status check_desc(const prism_desc* desc, prism::Dims* out) {
     return fail(PRISM_ERR_UNSUPPORTED, "activation must be PRISM_ACT_GELU or PRISM_ACT_IDENTITY");
   if (d.conv_offset != 0 && d.conv_offset != 1)
     return fail(PRISM_ERR_UNSUPPORTED, "conv_offset must be 0 or 1");
+  // a token row is H * dk elements apart: the kernels address a tile of up to
+  // 64 rows by 32-bit byte offsets from its base
+  if ((long long)d.H * d.dk > (1LL << 22))
+    return fail(PRISM_ERR_SHAPE, "H * dk must be <= 4194304 (got " + std::to_string((long long)d.H * d.dk) + ")");
   const double elems = (double)d.B * d.T * d.H * d.dk * (d.L + 1);
   if (elems > 4.0e12) return fail(PRISM_ERR_SHAPE, "problem too large");
   if ((long long)d.B * d.H * ((d.T + d.chunk - 1) / d.chunk) > 0x7fffffffLL)

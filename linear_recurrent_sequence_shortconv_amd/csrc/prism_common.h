@@ -519,7 +519,11 @@ struct RegTile {
 #pragma unroll
       for (int q = 0; q < RG; ++q) {
         v[p][q] = uint4{0u, 0u, 0u, 0u};
-        if (nvalid > 0) v[p][q] = ld16(g + min(r0 + q, nvalid - 1) * gstride + c);
+        // (a 32-bit unsigned byte offset from the tile's base: no 64-bit
+        // address arithmetic per vector)
+        if (nvalid > 0)
+          v[p][q] = ld16(reinterpret_cast<const char*>(g) +
+                         ((unsigned)min(r0 + q, nvalid - 1) * (unsigned)gstride + (unsigned)c) * (unsigned)sizeof(T));
       }
     }
   }
@@ -654,7 +658,9 @@ __device__ inline void s2g_rows(T* g, long gstride, const T* s, int ld, int nval
   constexpr int VPR = COLS / VN;
   for (int e = tid; e < ROWS * VPR; e += NT) {
     const int r = e / VPR, c = (e % VPR) * VN;
-    if (r < nvalid) st16(g + r * gstride + c, ld16(s + r * ld + c));
+    if (r < nvalid)
+      st16(reinterpret_cast<T*>(reinterpret_cast<char*>(g) + ((unsigned)r * (unsigned)gstride + (unsigned)c) * (unsigned)sizeof(T)),
+           ld16(s + r * ld + c));
   }
 }
 

@@ -70,6 +70,7 @@ def good_desc(**kw):
     ("B", 0, E_SHAPE), ("T", 0, E_SHAPE), ("H", -1, E_SHAPE),
     ("dk", 48, E_UNSUP), ("dv", 32, E_UNSUP), ("L", 9, E_UNSUP), ("L", -1, E_SHAPE),
     ("chunk", 128, E_UNSUP), ("chunk", 8, E_UNSUP), ("dtype", 7, E_UNSUP),
+    ("H", (1 << 22) // 64 + 1, E_SHAPE),
 ])
 def test_descriptor_checks(field, value, code):
     d = good_desc(**{field: value})
