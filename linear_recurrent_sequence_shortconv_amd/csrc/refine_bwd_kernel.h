@@ -143,6 +143,26 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
     pw.load(dWl + lrow * D, D, nrow, tid);
     pk.load(dKl + lrow * D, D, nrow, tid);
   }
+  // Weight fragments (B operands) of this wave's feature tiles.  Every
+  // product takes them preloaded: a fragment load issued ahead of the work
+  // that precedes its product keeps its L2 latency off the critical path, and
+  // issuing it before the row prefetches and stores of a step keeps the
+  // product's wait (vmcnt counts in issue order) from covering those.
+  typedef typename MK::frag Frag;
+  // (the weights come in fragment order: each fragment is one contiguous
+  // 64-lane piece)
+  auto load_w = [&](const E* W, Frag (&bw)[FPW][D / KS]) {
+#pragma unroll
+    for (int nn = 0; nn < FPW; ++nn)
+#pragma unroll
+      for (int kk = 0; kk < D / KS; ++kk)
+        if (FT_OK(fq + 4 * nn)) bw[nn][kk] = load_frag_fo<E, D>(W, fq + 4 * nn, kk, lane);
+  };
+  // Up to three steps (EARLY_W) the first projection's fragments are
+  // requested here, with the set-up's reads.
+  constexpr bool EARLY_W = LMAX <= 3;
+  Frag bwp[FPW][D / KS];   // W_p^(l) fragments
+  if (EARLY_W && L > 0) load_w(Wp + (long)h * L * D * D, bwp);
 #pragma unroll
   for (int p = 0; p < PWB; ++p)
     if (tid + p * RB_NT < nwb) st16(wbl + (tid + p * RB_NT) * VN, wbv[p]);
@@ -193,11 +213,14 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
   }
   __syncthreads();
   // owned u rows for the weight-gradient GEMM; gates (4 threads per token,
-  // 16-byte reads of u and w_beta)
+  // 16-byte reads of u and w_beta; the RB_NT / 4 RB_TT thread groups take
+  // the steps round robin)
   s2g_rows<E, RB_TT, D, RB_NT>(uo + (bh * Tp + t0) * D, D, ubuf, LD, own, tid);
-  if (tid < RB_TT * 4) {
-    const int t = tid >> 2, part = tid & 3;
-    for (int l = 0; l < L; ++l) {
+  {
+    constexpr int GG = RB_NT / (4 * RB_TT);
+    static_assert(GG >= 1, "a thread group per step");
+    const int grp = tid / (4 * RB_TT), t = (tid % (4 * RB_TT)) >> 2, part = tid & 3;
+    for (int l = grp; l < L; l += GG) {
       float s = 0.f;
       for (int c = part * VN; c < D; c += 4 * VN) {
         const uint4 ua = ld16(ubuf + t * LD + c), wa = ld16(wbl + l * D + c);
@@ -214,21 +237,6 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
   pk.store_rows(gkk, LD, tid);
   __syncthreads();
 
-  // Weight fragments (B operands) of this wave's feature tiles.  Every
-  // product takes them preloaded: a fragment load issued ahead of the work
-  // that precedes its product keeps its L2 latency off the critical path, and
-  // issuing it before the row prefetches and stores of a step keeps the
-  // product's wait (vmcnt counts in issue order) from covering those.
-  typedef typename MK::frag Frag;
-  // (the weights come in fragment order: each fragment is one contiguous
-  // 64-lane piece)
-  auto load_w = [&](const E* W, Frag (&bw)[FPW][D / KS]) {
-#pragma unroll
-    for (int nn = 0; nn < FPW; ++nn)
-#pragma unroll
-      for (int kk = 0; kk < D / KS; ++kk)
-        if (FT_OK(fq + 4 * nn)) bw[nn][kk] = load_frag_fo<E, D>(W, fq + 4 * nn, kk, lane);
-  };
   // p^(l) = W_p^(l) (u_hi + u_lo) for this wave's tiles (same as the forward)
   auto project = [&](const Frag (&bws)[FPW][D / KS], f32x4 (&acc)[2][FPW]) {
 #pragma unroll
@@ -289,9 +297,6 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
   // step's fragments are requested before this step's product, and each
   // reverse step requests its first product's fragments before the chain
   // replay.  More steps keep one set, requested just before its product.
-  constexpr bool EARLY_W = LMAX <= 3;
-  Frag bwp[FPW][D / KS];   // W_p^(l) fragments
-  if (EARLY_W && L > 0) load_w(Wp + (long)h * L * D * D, bwp);
 #pragma unroll
   for (int l = 0; l < LMAX; ++l) {
     if (l >= L) break;
