@@ -186,7 +186,9 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
       }
     });
     __syncthreads();
-    invert_unit_lower<C, NW>(Af, Tf, Xs, tid);
+    // (the wide instance reads the diagonal blocks' rows further ahead: its
+    // registers peak elsewhere)
+    invert_unit_lower<C, NW, false, (D >= 128 && C >= 64) ? INV_PD : 1>(Af, Tf, Xs, tid);
     // T, T diag(beta), T diag(beta e) in the operand type: column pairs, one
     // 2-element store each, all of a thread's reads issued together
     constexpr int NPR = C * C / 2, PPR = (NPR + NT - 1) / NT;
@@ -254,9 +256,16 @@ __global__ __launch_bounds__(CB_NT) void chunk_bwd_solve_kernel(
 #pragma unroll
       for (int j = 0; j < DQT::VN; ++j) sdq += to_f(Qr[r * LR + c0 + j]) * to_f(x[j]);
     }
+    if constexpr (DQT::VPR == 16) {
+      // a row is one 16-lane DPP row: its total in the last lane (the same
+      // pairing as the xor butterfly, without LDS round trips)
+      sdq = row16_sum(sdq);
+      if (u < DQT::NU && (u % DQT::VPR) == DQT::VPR - 1) de[r] = sdq;
+    } else {
 #pragma unroll
-    for (int off = 1; off < DQT::VPR; off <<= 1) sdq += __shfl_xor(sdq, off);
-    if (u < DQT::NU && (u % DQT::VPR) == 0) de[r] = sdq;
+      for (int off = 1; off < DQT::VPR; off <<= 1) sdq += __shfl_xor(sdq, off);
+      if (u < DQT::NU && (u % DQT::VPR) == 0) de[r] = sdq;
+    }
   }
   // dU_s, dWk_s, dK_s and dQt in the accumulator layout, for the epilogue
   // of the R0 products (fetched while they run)

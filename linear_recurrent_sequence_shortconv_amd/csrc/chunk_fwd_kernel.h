@@ -483,7 +483,9 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
       }
     });
     __syncthreads();
-    invert_unit_lower<C, NW, !FUSE>(Af, Tf, Xs, tid);
+    // (the wide instances read the diagonal blocks' rows further ahead: their
+    // registers peak elsewhere)
+    invert_unit_lower<C, NW, !FUSE, (D >= 128 && C >= 64) ? INV_PD : 1>(Af, Tf, Xs, tid);
     // T in the operand type: column pairs, one 2-element store each
     constexpr int NPR = C * C / 2, PPR = (NPR + NT - 1) / NT;
 #pragma unroll

@@ -398,7 +398,12 @@ __device__ __attribute__((always_inline)) inline void invert_double_level(const 
 // Always inlined: as a call it would make the caller wait for every load in
 // flight (its prefetches of the next phase) and spill around the call.  KU2 as
 // for gemm_acc.
-template <int C, int NW, bool KU2 = false>
+// PD: rows of A read ahead of the one computed in the diagonal blocks (more
+// rows hide more LDS latency and hold more registers).
+#ifndef INV_PD
+#define INV_PD 3
+#endif
+template <int C, int NW, bool KU2 = false, int PD = 1>
 __device__ __attribute__((always_inline)) inline void invert_unit_lower(const float* A, float* Tm,
                                                                        float* Xs, int tid) {
   constexpr int NB = C / 16, LA = C + 1;
@@ -412,21 +417,26 @@ __device__ __attribute__((always_inline)) inline void invert_unit_lower(const fl
   if (wave == 0 && lane < NB * 16) {
     const int base = 16 * (lane >> 4), col = lane & 15;
     const float* Ab = A + base * LA + base;
-    // row r + 1 of A is read from LDS while row r is computed; the empty asm
-    // (which takes t[r] and clobbers memory) pins that order, so the reads
-    // are not all hoisted up front with 120 values held in registers
-    float t[16], an[16], ac[16];
+    // row r + PD of A is read from LDS while row r is computed (a ring of
+    // PD + 1 rows in registers: an LDS round trip is longer than the FMA chain
+    // of a short row); the empty asm (which takes t[r] and clobbers memory)
+    // pins that order, so the reads are not all hoisted up front with 120
+    // values held in registers
+    static_assert(PD >= 1 && PD < 16, "rows ahead");
+    float t[16], an[PD + 1][16];
+#pragma unroll
+    for (int k = 1; k < PD && k < 16; ++k)
+#pragma unroll
+      for (int m = 0; m < k; ++m) an[k % (PD + 1)][m] = Ab[k * LA + m];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
+      if (r + PD < 16) {
 #pragma unroll
-      for (int m = 0; m < r; ++m) ac[m] = an[m];
-      if (r + 1 < 16) {
-#pragma unroll
-        for (int m = 0; m <= r; ++m) an[m] = Ab[(r + 1) * LA + m];
+        for (int m = 0; m < r + PD; ++m) an[(r + PD) % (PD + 1)][m] = Ab[(r + PD) * LA + m];
       }
       float s = (r == col) ? 1.f : 0.f;
 #pragma unroll
-      for (int m = 0; m < r; ++m) s = fmaf(-ac[m], t[m], s);
+      for (int m = 0; m < r; ++m) s = fmaf(-an[r % (PD + 1)][m], t[m], s);
       t[r] = s;
       asm volatile("" : "+v"(t[r]) : : "memory");
     }
