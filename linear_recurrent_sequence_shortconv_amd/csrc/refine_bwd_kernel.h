@@ -339,8 +339,8 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
   // step count is the runtime one (a uniform test): with fewer steps the
   // first reverse step is not the last step and the kept rows would be read
   // unwritten.  (Three fp32 steps: the kept rows would cost the D = 64
-  // instance a wave per SIMD.)
-  constexpr bool KEEP = LMAX == 4 || (LMAX == 3 && sizeof(E) == 2);
+  // instance a wave per SIMD; three steps with past-only taps: they spill.)
+  constexpr bool KEEP = LMAX == 4 || (LMAX == 3 && sizeof(E) == 2 && OFF == 0);
   const bool keep = KEEP && L == LMAX;
   float rkeep[KEEP ? 2 : 1][FPW][4];
 #pragma unroll
