@@ -216,16 +216,21 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
   auto tile_ok = [&](int j) { return MT % WPF == 0 || mb + WPF * j < MT; };
   Frag bw[FUSE ? NK : 1];   // weight fragments of the next projection
   float tp[4];              // ShortConv taps of feature f
+  uint4 wbn;                // w_beta rows (a vector per thread below L D / VN)
   auto load_w = [&](const E* W) {
 #pragma unroll
     for (int kk = 0; kk < NK; ++kk) bw[kk] = load_fragK<E, D>(W, D, 16 * fn, kk * KS, lane);
   };
   if constexpr (FUSE) {
-    load_w(fz.Wp + (long)h * L * D * D);   // W_p^(1)
+    // Requested in the order they are waited for (vmcnt retires in issue
+    // order): the taps (before phase A's barrier), the w_beta rows (one
+    // vector per thread, clamped rather than conditional; stored after the
+    // anchor pass), then the W_p^(1) fragments (first used after the gates)
 #pragma unroll
     for (int j = 0; j < 4; ++j) tp[j] = to_f(fz.conv[((long)h * D + f) * 4 + j]);
-    E* wbs = reinterpret_cast<E*>(smem + LY::F_WB);
-    for (int e = tid; e < L * VPRW; e += NT) st16(wbs + e * VN, ld16(fz.wbeta + (long)h * L * D + e * VN));
+    static_assert(FUSE_LMAX * (D / VN) <= NT, "w_beta rows: one vector per thread");
+    wbn = ld16(fz.wbeta + (long)h * L * D + (long)min(tid, L * VPRW - 1) * VN);
+    load_w(fz.Wp + (long)h * L * D * D);   // W_p^(1)
     E* vb = reinterpret_cast<E*>(smem + LY::F_V);
 #pragma unroll
     for (int p = 0; p < VPER; ++p) {
@@ -286,6 +291,7 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
         }
       }
     }
+    if (tid < L * VPRW) st16(reinterpret_cast<E*>(smem + LY::F_WB) + tid * VN, wbn);
     __syncthreads();
     // four threads per token (16-byte reads of u and w_beta, each thread a
     // fixed set of feature blocks in order); NT / 4C groups take the steps
