@@ -145,6 +145,19 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
     const int tb = c * C;
     const int nval = min(C, seq_len(cu, b, T) - tb);
     const long row0 = (seq_start(cu, b, T) + tb) * H + h;
+    if (!FUSE && wave == 0) {
+      // separate-pair kernel: requested first (a wait for them then leaves
+      // the tiles below in flight: vmcnt retires in issue order) and not under
+      // a per-lane condition (lanes past the chunk's tokens read its last row
+      // and take alpha = 1, beta = 0 at the use).  Requested last, and per
+      // lane, their join waited for the whole prefetch; in the fused kernel
+      // this order measured slower.
+      if (nval > 0) {
+        const long ab = row0 + (long)min(lane, nval - 1) * H;
+        pa = alpha[ab];
+        pb = beta[ab];
+      }
+    }
     if constexpr (FUSE) {
       const int Tb = seq_len(cu, b, T);
       const E* vs = v + (seq_start(cu, b, T) * H + h) * D;
@@ -166,7 +179,7 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
     }
     qn.load(q + row0 * D, ts, nval, tid);
     kr.load(k + row0 * D, ts, nval, tid);
-    if (wave == 0) {
+    if (FUSE && wave == 0) {
       pa = lane < nval ? alpha[row0 + (long)lane * H] : 1.f;
       pb = lane < nval ? beta[row0 + (long)lane * H] : 0.f;
     }
@@ -241,7 +254,9 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
 
   // ---- phase A: decays and gates; Q, K tiles ----
   if (wave == 0) {
-    const float lg = logf(pa), bv = pb;   // alpha = 1, beta = 0 past the end
+    // alpha = 1, beta = 0 past the end
+    const float lg = FUSE ? logf(pa) : lane < nval ? logf(pa) : 0.f;
+    const float bv = FUSE ? pb : lane < nval ? pb : 0.f;
     const float s = wave_scan(lg);
     const float gC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), C - 1));
     if (lane < C) {
