@@ -161,27 +161,33 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
     if constexpr (FUSE) {
       const int Tb = seq_len(cu, b, T);
       const E* vs = v + (seq_start(cu, b, T) * H + h) * D;
+      // (no load under a per-lane condition, whose merge made the wave wait
+      // for it right after issue: rows outside the sequence and its history
+      // read the chunk's own H^T block, and the store writes zeros for them)
+      const E* fb = HT + ((long)bh * NC + c) * D * D;
 #pragma unroll
       for (int p = 0; p < VPER; ++p) {
-        const int u = tid + p * NT;
+        const int u = min(tid + p * NT, VUN - 1);
         const int r = u / VPRW, cc = (u % VPRW) * VN;
         const int t = tb - HL + r;
-        uint4 x = {0u, 0u, 0u, 0u};
-        if (u < VUN) {
-          if (t >= 0 && t < Tb) x = ld16(vs + t * ts + cc);
-          else if (t < 0 && fz.hist) x = ld16(fz.hist + (((long)b * 4 + 4 + t) * H + h) * D + cc);
-        }
-        vh[p] = x;
+        const bool in_seq = t >= 0 && t < Tb, in_hist = t < 0 && fz.hist;
+        const E* src = in_seq ? vs + t * ts + cc
+                     : in_hist ? fz.hist + (((long)b * 4 + 4 + t) * H + h) * D + cc : fb + cc;
+        vh[p] = ld16(src);
       }
     } else if (L > 0) {
       kn.load(Kl + (long)bh * L * Tp * D + (long)tb * D, D, C, tid);
       wn.load(Wl + (long)bh * L * Tp * D + (long)tb * D, D, C, tid);
     }
-    qn.load(q + row0 * D, ts, nval, tid);
-    kr.load(k + row0 * D, ts, nval, tid);
-    if (FUSE && wave == 0) {
-      pa = lane < nval ? alpha[row0 + (long)lane * H] : 1.f;
-      pb = lane < nval ? beta[row0 + (long)lane * H] : 0.f;
+    if constexpr (FUSE) {
+      // (branch-free, as the v rows above; a chunk past a sequence's end
+      // reads its H^T block, zeroed at the store)
+      const E* fb = HT + ((long)bh * NC + c) * D * D;
+      qn.load_nb(q + row0 * D, ts, nval, fb, tid);
+      kr.load_nb(k + row0 * D, ts, nval, fb, tid);
+    } else {
+      qn.load(q + row0 * D, ts, nval, tid);
+      kr.load(k + row0 * D, ts, nval, tid);
     }
   };
   if ((int)blockIdx.x < nblk) prefetch(blockIdx.x);
@@ -236,27 +242,44 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
   };
   if constexpr (FUSE) {
     // Requested in the order they are waited for (vmcnt retires in issue
-    // order): the taps (before phase A's barrier), the w_beta rows (one
+    // order): alpha and beta (wave 0; not prefetched with the next chunk's
+    // tiles, where they made the wave wait for that whole prefetch, and not
+    // under a per-lane condition: lanes past the chunk's tokens read its last
+    // row) and the taps (before phase A's barrier), the w_beta rows (one
     // vector per thread, clamped rather than conditional; stored after the
     // anchor pass), then the W_p^(1) fragments (first used after the gates)
+    if (wave == 0 && nval > 0) {
+      const long ab = row0 + (long)min(lane, nval - 1) * H;
+      pa = alpha[ab];
+      pb = beta[ab];
+    }
 #pragma unroll
     for (int j = 0; j < 4; ++j) tp[j] = to_f(fz.conv[((long)h * D + f) * 4 + j]);
     static_assert(FUSE_LMAX * (D / VN) <= NT, "w_beta rows: one vector per thread");
     wbn = ld16(fz.wbeta + (long)h * L * D + (long)min(tid, L * VPRW - 1) * VN);
     load_w(fz.Wp + (long)h * L * D * D);   // W_p^(1)
     E* vb = reinterpret_cast<E*>(smem + LY::F_V);
+    const int Tb = seq_len(cu, b, T);
 #pragma unroll
     for (int p = 0; p < VPER; ++p) {
       const int u = tid + p * NT;
-      if (u < VUN) st16(vb + (u / VPRW) * D + (u % VPRW) * VN, vh[p]);
+      if (u < VUN) {
+        // zeros for the rows outside the sequence and its history (the empty
+        // asm keeps the select here, not next to the load)
+        const int t = tb - HL + u / VPRW;
+        uint4 x = vh[p];
+        asm volatile("" : "+v"(x.x), "+v"(x.y), "+v"(x.z), "+v"(x.w));
+        if (!((t >= 0 && t < Tb) || (t < 0 && fz.hist))) x = uint4{0u, 0u, 0u, 0u};
+        st16(vb + (u / VPRW) * D + (u % VPRW) * VN, x);
+      }
     }
   }
 
   // ---- phase A: decays and gates; Q, K tiles ----
   if (wave == 0) {
     // alpha = 1, beta = 0 past the end
-    const float lg = FUSE ? logf(pa) : lane < nval ? logf(pa) : 0.f;
-    const float bv = FUSE ? pb : lane < nval ? pb : 0.f;
+    const float lg = lane < nval ? logf(pa) : 0.f;
+    const float bv = lane < nval ? pb : 0.f;
     const float s = wave_scan(lg);
     const float gC = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, s), C - 1));
     if (lane < C) {
@@ -543,7 +566,10 @@ __global__ __launch_bounds__(CF_NT) void chunk_fwd_kernel(
   // (issued after every load this chunk still waits for: loads complete in
   // order)
   if constexpr (PERSIST) {
-    if (vid + vstride < nblk) prefetch(vid + vstride);
+    // (the fused kernel prefetches unconditionally, the last chunk again past
+    // the end: the join of a conditional prefetch made the wave wait for it
+    // right after issue)
+    if (FUSE || vid + vstride < nblk) prefetch(FUSE ? min(vid + vstride, nblk - 1) : vid + vstride);
   }
   __syncthreads();
   for_tiles(vacc, wave, lane, [&](int t0, int f, const f32x4& x) {

@@ -537,6 +537,29 @@ struct RegTile {
       }
     }
   }
+  // load() without its branch on nvalid, whose join (registers zeroed on one
+  // side, loaded on the other) can make the wave wait for every load in
+  // flight right after issuing these: with nvalid <= 0 every lane reads the
+  // first 16 bytes at fallback (any valid address) instead, and the rows are
+  // zeros at the store as with load()
+  __device__ inline void load_nb(const T* g, long gstride, int nvalid, const T* fallback, int tid) {
+    nv = nvalid;
+    const bool any = nvalid > 0;   // (uniform: scalar selects below)
+    const T* base = any ? g : fallback;
+    const unsigned st = any ? (unsigned)gstride : 0u;
+    const int last = any ? nvalid - 1 : 0;
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int u = min(tid + p * NT, NU - 1);
+      int r0, c;
+      unit(u, r0, c);
+      if (!any) c = 0;
+#pragma unroll
+      for (int q = 0; q < RG; ++q)
+        v[p][q] = ld16(reinterpret_cast<const char*>(base) +
+                       ((unsigned)min(r0 + q, last) * st + (unsigned)c) * (unsigned)sizeof(T));
+    }
+  }
   // vector (p, q) of row r: zeros past the valid rows.  The empty asm keeps
   // this select here, not next to the load.
   __device__ inline uint4 get(int p, int q, int r) const {
