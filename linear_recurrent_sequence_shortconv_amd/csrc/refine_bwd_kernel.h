@@ -361,6 +361,14 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
     // during the chain replay and the gate gradient when EARLY_W)
     Frag bpt[FPW][D / KS], bkt[FPW][D / KS];
     if constexpr (EARLY_W) load_w(WpT + ((long)h * L + l) * D * D, bpt);
+    // (up to three steps) the next step's dW, dK rows right after: the
+    // registers are free (this step's rows are in LDS), and the GELU and
+    // gate-gradient phases hide their latency
+    if (EARLY_W && l > 0) {
+      const long lrow = (bh * L + (l - 1)) * Tp + t0;
+      pw.load(dWl + lrow * D, D, nrow, tid);
+      pk.load(dKl + lrow * D, D, nrow, tid);
+    }
     // p^(l) and r^(l) of this step
     f32x4 p[2][FPW];
     float rl[2][FPW][4];
@@ -475,11 +483,11 @@ __global__ __launch_bounds__(RB_NT, 2) void refine_bwd_kernel(
     // products below
     if constexpr (!EARLY_W) load_w(WpT + ((long)h * L + l) * D * D, bpt);
     else load_w(WkT + ((long)h * L + l) * D * D, bkt);
-    if (l > 0) {
+    if (!EARLY_W && l > 0) {
       const long lrow = (bh * L + (l - 1)) * Tp + t0;
       pw.load(dWl + lrow * D, D, nrow, tid);
       pk.load(dKl + lrow * D, D, nrow, tid);
-    } else {
+    } else if (l == 0) {
       const E* dvs = dvdir + (bh * Tp + t0) * D;
 #pragma unroll
       for (int m = 0; m < 2; ++m)
