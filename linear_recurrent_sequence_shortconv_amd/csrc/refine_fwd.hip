@@ -89,11 +89,9 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
     const int nwb = L * (D / VN);
     uint4 wbv[PWB], vbv[PVB];
     bool vz[PVB];
-    if (nwb > 0) {   // (uniform: no refinement, no w_beta)
 #pragma unroll
-      for (int p = 0; p < PWB; ++p)
-        wbv[p] = ld16(wbeta + (long)h * L * D + (long)min(tid + p * RF_NT, nwb - 1) * VN);
-    }
+    for (int p = 0; p < PWB; ++p)   // (L >= 1: nwb > 0)
+      wbv[p] = ld16(wbeta + (long)h * L * D + (long)min(tid + p * RF_NT, nwb - 1) * VN);
 #pragma unroll
     for (int p = 0; p < PVB; ++p) {
       const int e = min(tid + p * RF_NT, NVB - 1);
@@ -130,9 +128,9 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
         if (FT_OK(n)) bw[nn][kk] = load_fragK<E, D>(W, D, 16 * n, kk * KS, lane);
     }
   };
-  Frag bw[FPW][NK];   // weight fragments of the next projection (W_p^(1) now)
-  if (L > 0) load_w(Wp + (long)h * L * D * D, bw);
   // taps of the lane's features, requested with the v rows (one round trip)
+  // and before the W_p^(1) fragments: their wait (at the set-up's barrier)
+  // then leaves the fragments, first used after the gates, in flight
   const E* ch = conv + (long)h * D * 4;
   float taps[FPW][4];
 #pragma unroll
@@ -142,6 +140,10 @@ __global__ __launch_bounds__(RF_NT) void refine_fwd_kernel(
 #pragma unroll
     for (int j = 0; j < 4; ++j) taps[nn][j] = (FT_OK(n)) ? to_f(ch[f * 4 + j]) : 0.f;
   }
+  Frag bw[FPW][NK];   // weight fragments of the next projection (W_p^(1) now)
+  // (unconditional: the kernel runs only with L >= 1, and a branch here made
+  // the taps' wait cover these fragments at its join)
+  load_w(Wp + (long)h * L * D * D, bw);
   __syncthreads();
 
   // ---- anchor u (fp32; to LDS as the MFMA operand, hi and lo parts) and
